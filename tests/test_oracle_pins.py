@@ -1,0 +1,455 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix.
+
+Each test ties one oracle function to something other than itself: a worked
+example printed on the pages (tests/golden/*.json, each citing its source),
+a closed form, an invariant, brute force on tiny inputs, or an independent
+library routine (CPU torch in float64).
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+import workloads as W
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+# --------------------------------------------------------------------------
+# router / top-k / weights
+# --------------------------------------------------------------------------
+def test_router_worked_example():
+    g = gold("router_worked_example.json")
+    p = np.array([g["router_probs"]])
+    s = np.log(p)                       # softmax(log p) = p exactly up to rounding
+    q = O.selection_key(s, O.SOFTMAX_TOPK, None)
+    np.testing.assert_allclose(q, p, rtol=1e-15)
+    idx = O.topk(q, g["top_k"])
+    assert idx.tolist() == [g["topk_indices"]]
+    raw = O.gate_weights(s, idx, O.SOFTMAX_TOPK, renormalize=0)
+    np.testing.assert_allclose(raw, [g["topk_weights"]], rtol=1e-14)
+    ren = O.gate_weights(s, idx, O.SOFTMAX_TOPK, renormalize=1)
+    np.testing.assert_allclose(ren, [g["renormalized"]], rtol=1e-14)
+    # tie reading: 0.10 at experts 0 and 3 -> expert 0
+    assert O.topk(q, 3).tolist() == [g["top3_indices"]]
+
+
+def _brute_topk(qrow, k):
+    """Max-sum subset of size k; among equal sums the lexicographically smallest
+    index tuple; then slots ordered by (value desc, index asc)."""
+    best, best_sum = None, None
+    for comb in itertools.combinations(range(len(qrow)), k):
+        ssum = sum(qrow[i] for i in comb)
+        if best is None or ssum > best_sum or (ssum == best_sum and comb < best):
+            best, best_sum = comb, ssum
+    return sorted(best, key=lambda i: (-qrow[i], i))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_brute_force_random_and_ties(seed):
+    rng = np.random.default_rng(100 + seed)
+    for _ in range(20):
+        T = int(rng.integers(1, 17))
+        E = int(rng.integers(1, 9))
+        k = int(rng.integers(1, min(E, 4) + 1))
+        if seed % 2 == 0:
+            q = rng.integers(0, 3, size=(T, E)).astype(np.float64)   # many exact ties, exact sums
+        else:
+            q = rng.standard_normal((T, E)).round(1)                   # ties after rounding
+            q = np.round(q * 10).astype(np.float64)                    # integers: exact subset sums
+        idx = O.topk(q, k)
+        for t in range(T):
+            assert idx[t].tolist() == _brute_topk(q[t].tolist(), k)
+
+
+def test_topk_values_match_torch():
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal((50, 33))
+    idx = O.topk(q, 5)
+    vals = np.take_along_axis(q, idx, axis=1)
+    tv, _ = torch.topk(torch.from_numpy(q), 5, dim=-1, sorted=True)
+    np.testing.assert_array_equal(vals, tv.numpy())
+
+
+def test_softmax_matches_torch_and_sums_to_one():
+    rng = np.random.default_rng(8)
+    s = rng.standard_normal((40, 17)) * 3
+    p = O.softmax(s)
+    np.testing.assert_allclose(p, torch.softmax(torch.from_numpy(s), -1).numpy(), rtol=1e-13, atol=0)
+    np.testing.assert_allclose(p.sum(-1), 1.0, rtol=1e-14)
+
+
+def test_renormalised_weights_sum_to_one():
+    rng = np.random.default_rng(9)
+    s = rng.standard_normal((64, 16))
+    b = rng.uniform(-0.1, 0.1, 16)
+    for scoring, ren in [(O.SOFTMAX_TOPK, 1), (O.TOPK_SOFTMAX, 0), (O.SIGMOID_BIAS, 1)]:
+        idx = O.topk(O.selection_key(s, scoring, b), 4)
+        w = O.gate_weights(s, idx, scoring, ren)
+        np.testing.assert_allclose(w.sum(-1), 1.0, rtol=1e-14)
+        assert (w > 0).all()
+
+
+def test_topk_softmax_equals_renormalised_softmax_topk():
+    """exp(s_i)/sum_K exp(s_j) = p_i / sum_K p_j: the two softmax orders agree once
+    the selected probabilities are renormalised (closed form)."""
+    rng = np.random.default_rng(10)
+    s = rng.standard_normal((80, 12)) * 2
+    i1 = O.topk(O.selection_key(s, O.TOPK_SOFTMAX, None), 3)
+    i2 = O.topk(O.selection_key(s, O.SOFTMAX_TOPK, None), 3)
+    np.testing.assert_array_equal(i1, i2)
+    w1 = O.gate_weights(s, i1, O.TOPK_SOFTMAX, 0)
+    w2 = O.gate_weights(s, i2, O.SOFTMAX_TOPK, 1)
+    np.testing.assert_allclose(w1, w2, rtol=1e-13)
+    # and TOPK_SOFTMAX's weight is the k-way softmax of the selected logits, checked with torch
+    sel = np.take_along_axis(s, i1, 1)
+    np.testing.assert_allclose(w1, torch.softmax(torch.from_numpy(sel), -1).numpy(), rtol=1e-13)
+
+
+def test_switch_top1_weight_is_raw_probability():
+    rng = np.random.default_rng(11)
+    s = rng.standard_normal((100, 128)) * 0.5
+    idx = O.topk(O.selection_key(s, O.SOFTMAX_TOPK, None), 1)
+    w = O.gate_weights(s, idx, O.SOFTMAX_TOPK, renormalize=0)
+    p = torch.softmax(torch.from_numpy(s), -1).numpy()
+    np.testing.assert_allclose(w[:, 0], p.max(-1), rtol=1e-13)
+    assert (w[:, 0] >= 1.0 / 128).all() and (w[:, 0] < 1).all()
+
+
+def test_sigmoid_bias_selection_only():
+    rng = np.random.default_rng(12)
+    s = rng.standard_normal((60, 32))
+    # b = 0: sigmoid is monotone, so selection = top-k of the logits
+    i0 = O.topk(O.selection_key(s, O.SIGMOID_BIAS, np.zeros(32)), 8)
+    np.testing.assert_array_equal(i0, O.topk(s, 8))
+    # a large bias on a chosen set forces that set; the weights ignore the bias
+    forced = np.array([3, 5, 7, 11, 13, 17, 19, 23])
+    b = np.zeros(32)
+    b[forced] = 10.0
+    i1 = O.topk(O.selection_key(s, O.SIGMOID_BIAS, b), 8)
+    assert all(sorted(r) == sorted(forced.tolist()) for r in i1.tolist())
+    w = O.gate_weights(s, i1, O.SIGMOID_BIAS, 1)
+    a = 1.0 / (1.0 + np.exp(-np.take_along_axis(s, i1, 1)))
+    np.testing.assert_allclose(w, a / a.sum(1, keepdims=True), rtol=1e-14)
+    # torch's sigmoid as an independent routine for the affinity
+    np.testing.assert_allclose(O.sigmoid(s), torch.sigmoid(torch.from_numpy(s)).numpy(), rtol=1e-14)
+
+
+def test_near_tie_mask():
+    key = np.array([[0.5, 0.3, 0.3, 0.1],            # boundary tie at k=2
+                    [0.4, 0.4, 0.1, 0.1],            # slot tie only
+                    [0.5, 0.3, 0.3 - 1e-3, 0.1]])    # clear gap
+    bnd, sw = O.near_tie_mask(key, 2)
+    assert bnd.tolist() == [True, False, False]
+    assert sw[:, 0].tolist() == [False, True, False]
+
+
+# --------------------------------------------------------------------------
+# dispatch and capacity
+# --------------------------------------------------------------------------
+def test_dispatch_worked_example():
+    g = gold("dispatch_worked_example.json")
+    idx = np.array(g["topk_indices"])
+    d = O.dispatch(idx, 4, None)
+    e = g["expert"]
+    rows = range(d["offsets"][e], d["offsets"][e + 1])
+    toks = [int(d["token_of_row"][r]) for r in rows]
+    assert toks == g["token_indices"]
+    slots = [int(np.nonzero(d["row_of"][t] == r)[0][0]) for t, r in zip(toks, rows)]
+    assert slots == g["route_slots"]
+    assert d["counts"].tolist() == g["counts"]
+    assert d["offsets"].tolist() == g["offsets"]
+    assert d["token_of_row"].tolist() == g["token_of_row"]
+    assert d["row_of"].tolist() == g["row_of"]
+    c = g["capacity_2"]
+    d2 = O.dispatch(idx, 4, 2)
+    assert d2["counts"].tolist() == g["counts"]
+    assert d2["kept"].tolist() == c["kept"]
+    assert d2["offsets"].tolist() == c["offsets"]
+    assert d2["row_of"].tolist() == c["row_of"]
+    assert d2["token_of_row"].tolist() == c["token_of_row"]
+    assert d2["dropped"] == c["dropped"]
+
+
+@pytest.mark.parametrize("cap", [None, 1, 3, 7])
+def test_dispatch_invariants(cap):
+    rng = np.random.default_rng(13)
+    T, E, k = 37, 9, 3
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+    d = O.dispatch(idx, E, cap)
+    assert d["counts"].sum() == T * k
+    # counts by an independent route: bincount
+    np.testing.assert_array_equal(d["counts"], np.bincount(idx.ravel(), minlength=E))
+    A = int(d["offsets"][-1])
+    kept_rows = d["row_of"][d["row_of"] >= 0]
+    assert sorted(kept_rows.tolist()) == list(range(A))          # bijection onto [0, A)
+    for (t, j), r in np.ndenumerate(d["row_of"]):
+        if r >= 0:
+            assert d["token_of_row"][r] == t
+            assert d["offsets"][idx[t, j]] <= r < d["offsets"][idx[t, j] + 1]
+    for e in range(E):
+        seg = d["token_of_row"][d["offsets"][e]:d["offsets"][e + 1]]
+        assert (np.diff(seg) > 0).all()                            # ascending tokens
+        allt = sorted(t for t in range(T) if e in idx[t])
+        n = len(allt) if cap is None else min(cap, len(allt))
+        assert seg.tolist() == allt[:n]                           # first C by token order kept
+    assert d["dropped"] == T * k - A
+
+
+def test_capacity_every_token_on_one_expert():
+    T, E, C = 50, 4, 12
+    idx = np.zeros((T, 1), dtype=np.int64)
+    d = O.dispatch(idx, E, C)
+    assert d["token_of_row"].tolist() == list(range(C))
+    assert (d["row_of"][:C, 0] == np.arange(C)).all() and (d["row_of"][C:, 0] == -1).all()
+    assert d["dropped"] == T - C
+
+
+def test_capacity_formula():
+    for c in gold("capacity_examples.json")["cases"]:
+        assert O.capacity(c["capacity_factor"], c["num_tokens"], c["top_k"], c["num_experts"]) == c["capacity"]
+    assert O.capacity(0.0, 10, 1, 2) is None
+
+
+# --------------------------------------------------------------------------
+# experts
+# --------------------------------------------------------------------------
+def test_parameter_counts():
+    g = gold("parameter_counts.json")
+    D, F, E, k = g["d_model"], g["d_ff"], g["num_experts"], g["top_k"]
+    assert O.num_parameters_swiglu(D, F) == g["per_expert"]
+    assert E * O.num_parameters_swiglu(D, F) == g["all_experts"]
+    assert D * E == g["router"]
+    assert D * E + k * O.num_parameters_swiglu(D, F) == g["active_per_token"]
+    assert O.num_parameters_swiglu(D, g["dense_ff"]) == g["dense_swiglu"]
+    # and the generated Tiny workload has exactly these shapes
+    w13, w2 = W.make_expert(W.TINY, 0)
+    assert w13.size + w2.size == g["per_expert"]
+
+
+def test_activation_closed_forms():
+    assert O.silu(np.array([0.0]))[0] == 0.0
+    np.testing.assert_allclose(O.silu(np.array([1.0])), [1.0 / (1.0 + math.exp(-1.0))], rtol=1e-15)
+    # Phi(1) = 0.8413447460685429 (standard normal CDF); gelu(1) = Phi(1)
+    np.testing.assert_allclose(O.gelu(np.array([1.0])), [0.8413447460685429], rtol=1e-14)
+    np.testing.assert_allclose(O.gelu(np.array([-1.0])), [-(1 - 0.8413447460685429)], rtol=1e-13)
+    z = np.linspace(-8, 8, 101)
+    tz = torch.from_numpy(z)
+    np.testing.assert_allclose(O.gelu(z), torch.nn.functional.gelu(tz).numpy(), rtol=1e-13, atol=1e-300)
+    np.testing.assert_allclose(O.silu(z), torch.nn.functional.silu(tz).numpy(), rtol=1e-13, atol=1e-300)
+
+
+def test_swiglu_expert_matches_torch_module():
+    rng = np.random.default_rng(14)
+    D, F = 24, 40
+    x = rng.standard_normal((7, D))
+    g, u, d = (rng.standard_normal(s) * 0.1 for s in [(F, D), (F, D), (D, F)])
+    lin = lambda w: torch.nn.Linear(w.shape[1], w.shape[0], bias=False).double()
+    G, U, Dn = lin(g), lin(u), lin(d)
+    with torch.no_grad():
+        G.weight.copy_(torch.from_numpy(g)); U.weight.copy_(torch.from_numpy(u)); Dn.weight.copy_(torch.from_numpy(d))
+        tx = torch.from_numpy(x)
+        ref = Dn(torch.nn.functional.silu(G(tx)) * U(tx)).numpy()
+    np.testing.assert_allclose(O.swiglu_expert(x, g, u, d), ref, rtol=1e-12, atol=1e-15)
+    w13 = np.concatenate([g, u])
+    np.testing.assert_allclose(O.expert_apply(x, w13, d, O.SWIGLU, F), ref, rtol=1e-12, atol=1e-15)
+
+
+def test_gelu_expert_matches_torch():
+    rng = np.random.default_rng(15)
+    D, F = 16, 20
+    x = rng.standard_normal((5, D))
+    wi, wo = rng.standard_normal((F, D)), rng.standard_normal((D, F)) * 0.1
+    tx = torch.from_numpy(x)
+    ref = (torch.nn.functional.gelu(tx @ torch.from_numpy(wi).T) @ torch.from_numpy(wo).T).numpy()
+    np.testing.assert_allclose(O.expert_apply(x, wi, wo, O.GELU, F), ref, rtol=1e-12, atol=1e-15)
+
+
+def test_shared_concatenation_equals_sum():
+    """S shared experts summed == one expert of width S*F_s on the packed layout."""
+    cfg = W.MoEConfig("t", 9, 16, 2, 1, 8, num_shared=3, d_ff_shared=12, act_dtype=W.F32, router_dtype=W.F32)
+    shared = [W.make_shared_expert(cfg, i) for i in range(3)]
+    ws13, ws2 = W.pack_shared(cfg, shared)
+    x = W.make_tokens(cfg)
+    ys = O.shared_experts(x, shared)
+    SF = 3 * 12
+    one = O.swiglu_expert(x, ws13[:SF], ws13[SF:], ws2)
+    np.testing.assert_allclose(ys, one, rtol=1e-12, atol=1e-15)
+
+
+# --------------------------------------------------------------------------
+# combine
+# --------------------------------------------------------------------------
+def _rand_experts(rng, E, D, F):
+    return [(rng.standard_normal((2 * F, D)) * 0.3, rng.standard_normal((D, F)) * 0.3) for _ in range(E)]
+
+
+def test_combine_worked_example():
+    g = gold("combine_worked_example.json")
+    rng = np.random.default_rng(16)
+    T, D, F, E = 4, 6, 5, 4
+    x = rng.standard_normal((T, D))
+    ex = _rand_experts(rng, E, D, F)
+    idx = np.array(g["topk_indices"])
+    w = np.full(idx.shape, 0.5)
+    w[g["token"]] = g["token0_weights"]
+    d = O.dispatch(idx, E, None)
+    Y = O.expert_outputs(x, d, lambda e: ex[e], O.SWIGLU, F, E)
+    y = O.combine(Y, d, w, T)
+    e2 = O.expert_apply(x[:1], *ex[2], O.SWIGLU, F)[0]
+    e0 = O.expert_apply(x[:1], *ex[0], O.SWIGLU, F)[0]
+    np.testing.assert_allclose(y[0], 0.75 * e2 + 0.25 * e0, rtol=1e-13, atol=1e-15)
+
+
+def test_combine_accumulates_identical_experts():
+    """Identical experts + renormalised weights give y = E(x) for any routing
+    (an assigning combine would give only the last route's share)."""
+    rng = np.random.default_rng(17)
+    T, D, F, E, k = 20, 8, 6, 5, 2
+    x = rng.standard_normal((T, D))
+    one = _rand_experts(rng, 1, D, F)[0]
+    s = rng.standard_normal((T, E))
+    idx = O.topk(O.selection_key(s, O.SOFTMAX_TOPK, None), k)
+    w = O.gate_weights(s, idx, O.SOFTMAX_TOPK, 1)
+    d = O.dispatch(idx, E, None)
+    Y = O.expert_outputs(x, d, lambda e: one, O.SWIGLU, F, E)
+    y = O.combine(Y, d, w, T)
+    np.testing.assert_allclose(y, O.expert_apply(x, *one, O.SWIGLU, F), rtol=1e-12, atol=1e-14)
+
+
+def test_soft_routing_k_equals_e_is_dense_weighted_sum():
+    """k = E routes every token to every expert: the layer is the dense
+    weighted sum over all experts of softmax(s)_e * E_e(x) (soft routing)."""
+    rng = np.random.default_rng(18)
+    T, D, F, E = 11, 8, 6, 5
+    x = rng.standard_normal((T, D))
+    wr = rng.standard_normal((E, D))
+    ex = _rand_experts(rng, E, D, F)
+    cfg = W.MoEConfig("soft", T, D, E, E, F, act_dtype=W.F32, router_dtype=W.F32)
+    out = O.forward(cfg, x, wr, None, lambda e: ex[e])
+    p = torch.softmax(torch.from_numpy(x @ wr.T), -1).numpy()
+    dense = np.zeros((T, D))
+    for e in range(E):
+        dense += p[:, e:e + 1] * O.expert_apply(x, *ex[e], O.SWIGLU, F)
+    np.testing.assert_allclose(out["y"], dense, rtol=1e-12, atol=1e-14)
+
+
+def test_dropped_assignment_contributes_zero():
+    rng = np.random.default_rng(19)
+    T, D, F, E = 6, 4, 3, 2
+    x = rng.standard_normal((T, D))
+    ex = _rand_experts(rng, E, D, F)
+    idx = np.zeros((T, 1), dtype=np.int64)
+    w = np.ones((T, 1))
+    d = O.dispatch(idx, E, 2)
+    Y = O.expert_outputs(x, d, lambda e: ex[e], O.SWIGLU, F, E)
+    y = O.combine(Y, d, w, T)
+    np.testing.assert_allclose(y[:2], O.expert_apply(x[:2], *ex[0], O.SWIGLU, F), rtol=1e-13)
+    assert (y[2:] == 0).all()
+
+
+# --------------------------------------------------------------------------
+# load statistics
+# --------------------------------------------------------------------------
+def test_assignment_example_9_4_2_1():
+    g = gold("load_examples.json")["assignment_example"]
+    c = np.array(g["counts"])
+    st = O.load_stats(c, np.full((4, 4), 0.25), 4, 0.01)
+    assert c.sum() == g["total"] and c.sum() / 4 == g["ideal_mean"]
+    assert st["imbalance"] == pytest.approx(g["imbalance_e0"], rel=1e-15)
+    np.testing.assert_allclose(st["f"].sum(), 1.0)
+
+
+def test_importance_vs_load_cases():
+    g = gold("load_examples.json")["importance_vs_load"]
+    for case in ("case_A", "case_B"):
+        c = g[case]
+        probs = np.array(c["router_probs"])
+        s = np.log(probs)
+        idx = O.topk(O.selection_key(s, O.SOFTMAX_TOPK, None), 1)
+        assert idx.tolist() == c["topk_indices"]
+        counts = O.expert_counts(idx, 2)
+        st = O.load_stats(counts, O.importance_probs(s, O.SOFTMAX_TOPK), 1, alpha=1.0)
+        np.testing.assert_allclose(st["P"], c["importance"], rtol=1e-14)
+        np.testing.assert_allclose(st["f"], c["load"], rtol=1e-15)
+        assert st["aux_loss"] == pytest.approx(c["loss_over_alpha"], rel=1e-14)
+
+
+@pytest.mark.parametrize("E,k", [(4, 2), (8, 1), (64, 6)])
+def test_uniform_routing_loss_equals_alpha(E, k):
+    alpha = 0.01
+    T = E * 3
+    idx = np.array([[(t + j) % E for j in range(k)] for t in range(T)])   # every expert k*3 times
+    counts = O.expert_counts(idx, E)
+    assert (counts == counts[0]).all()
+    probs = np.full((T, E), 1.0 / E)
+    st = O.load_stats(counts, probs, k, alpha)
+    assert st["aux_loss"] == pytest.approx(alpha, rel=1e-14)
+    assert st["imbalance"] == pytest.approx(1.0, rel=1e-15)
+
+
+def test_sigmoid_importance_sums_to_one():
+    rng = np.random.default_rng(20)
+    s = rng.standard_normal((30, 16))
+    P = O.importance_probs(s, O.SIGMOID_BIAS)
+    np.testing.assert_allclose(P.sum(-1), 1.0, rtol=1e-14)
+    a = 1 / (1 + np.exp(-s))
+    np.testing.assert_allclose(P * a.sum(-1, keepdims=True), a, rtol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# whole layer against a token-by-token evaluation (no dispatch, no permutation)
+# --------------------------------------------------------------------------
+def _per_token_reference(cfg, inp, out):
+    X = O.widen(inp.x)
+    y = np.zeros_like(X)
+    for t in range(cfg.num_tokens):
+        for j in range(cfg.top_k):
+            if out["row_of"][t, j] < 0:
+                continue
+            e = int(out["idx"][t, j])
+            y[t] += out["w"][t, j] * O.expert_apply(X[t:t + 1], inp.w13[e], inp.w2[e], cfg.activation, cfg.d_ff)[0]
+        for g, u, d in inp.shared:
+            y[t] += O.swiglu_expert(X[t:t + 1], g, u, d)[0]
+    return y
+
+
+@pytest.mark.parametrize("cfg", [
+    W.TINY,
+    W.TINY.replace(name="tiny_cap", capacity_factor=0.75),
+    W.MoEConfig("tiny_shared_sigmoid", 40, 32, 8, 3, 24, num_shared=2, d_ff_shared=16,
+                scoring=W.SIGMOID_BIAS, act_dtype=W.BF16, router_dtype=W.BF16, zipf_s=1.0),
+    W.MoEConfig("tiny_gelu_switch", 48, 16, 6, 1, 20, scoring=W.SOFTMAX_TOPK, renormalize=0,
+                activation=W.GELU, act_dtype=W.BF16, router_dtype=W.F32, capacity_factor=1.0),
+    W.MoEConfig("tiny_topk_softmax", 32, 16, 8, 2, 12, scoring=W.TOPK_SOFTMAX),
+], ids=lambda c: c.name)
+def test_forward_matches_per_token_evaluation(cfg):
+    inp = W.make_inputs(cfg)
+    out = O.forward(cfg, inp.x, inp.w_router, inp.sel_bias, lambda e: (inp.w13[e], inp.w2[e]), inp.shared)
+    assert out["counts"].sum() == cfg.num_tokens * cfg.top_k
+    ref = _per_token_reference(cfg, inp, out)
+    np.testing.assert_allclose(out["y"], ref, rtol=1e-12, atol=1e-14)
+    if cfg.capacity_factor <= 0:
+        assert out["dropped"] == 0 and (out["row_of"] >= 0).all()
+    else:
+        assert out["dropped"] == int((out["row_of"] < 0).sum())
+
+
+def test_tiny_workload_routes_every_assignment():
+    cfg = W.TINY
+    inp = W.make_inputs(cfg)
+    out = O.forward(cfg, inp.x, inp.w_router, None, lambda e: (inp.w13[e], inp.w2[e]))
+    assert out["counts"].sum() == 128                      # N * K = 64 * 2
+    np.testing.assert_allclose(out["w"].sum(1), 1.0, rtol=1e-14)
+    np.testing.assert_allclose(out["P"].sum(), 1.0, rtol=1e-14)
+    assert out["aux_loss"] > 0
