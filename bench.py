@@ -1,0 +1,235 @@
+"""Benchmark of the sparse-MoE layer forward on one MI355X.
+
+One step = one moe_layer_forward over a batch of seeded synthetic tokens that
+is already resident in HBM: router logits, scoring / top-k, permute, grouped
+expert FFN (routed and shared), combine and the load statistics.
+
+Prints ONE JSON line: MoE-layer tokens/s, the roofline of the dominant kernel
+(timed live with HIP events on the library's stream over the timed steps) and
+the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+# MI355X published peaks
+HBM_GBPS = 8000.0
+MFMA_BF16_TFLOPS = 2500.0
+VALU_F32_TFLOPS = 78.6       # FMA without packed-FP32 instructions: 256 CU x 64 lanes x 2 x 2.4 GHz
+
+DEFAULT_CPU_SAMPLE = {"tiny": 64, "switch": 1024, "mixtral": 64, "deepseekmoe": 256, "deepseekv3": 32}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def stage_work(cfg, stage, A, E_act, T):
+    """Algorithmic (flops, bytes) of one launch of a stage; A = kept rows."""
+    b = 2 if cfg.act_dtype == W.BF16 else 4
+    br = 2 if cfg.router_dtype == W.BF16 else 4
+    D, F, E, k = cfg.d_model, cfg.d_ff, cfg.num_experts, cfg.top_k
+    nm = cfg.n_mat
+    SF = cfg.num_shared * cfg.d_ff_shared
+    if stage == "router_logits":
+        return 2.0 * T * D * E, T * D * b + E * D * br + T * E * 4
+    if stage == "route_select":
+        return 0.0, T * E * 4 * 2 + T * k * 8
+    if stage == "permute":
+        return 0.0, T * k * 4 * 3 + A * 4 + (E + 1) * 8
+    if stage == "expert_gate_up":
+        return 2.0 * A * D * F * nm, E_act * nm * F * D * b + A * D * b + A * F * b
+    if stage == "expert_down":
+        return 2.0 * A * F * D, E_act * D * F * b + A * F * b + A * D * b
+    if stage == "shared_gate_up":
+        return 2.0 * T * D * 2 * SF, 2 * SF * D * b + T * D * b + T * SF * b
+    if stage == "shared_down":
+        return 2.0 * T * SF * D, D * SF * b + T * SF * b + T * D * b
+    if stage == "combine":
+        return 0.0, A * D * b + T * k * 8 + (T * D * b if SF else 0) + T * D * b
+    if stage == "load_stats":
+        return 0.0, T * E * 4 + E * 4
+    raise KeyError(stage)
+
+
+def roofline_of(cfg, stage, flops, nbytes, ms):
+    t = ms * 1e-3
+    gemm = flops > 0
+    f32 = (cfg.act_dtype == W.F32) or (stage == "router_logits" and cfg.router_dtype == W.F32)
+    if gemm and f32:
+        peak_f, unit_bound = VALU_F32_TFLOPS, "alu"
+    else:
+        peak_f, unit_bound = MFMA_BF16_TFLOPS, "mfma"
+    if gemm and flops / max(nbytes, 1) > peak_f * 1e12 / (HBM_GBPS * 1e9):
+        achieved = flops / t / 1e12
+        return dict(bound=unit_bound, achieved=round(achieved, 2), peak=peak_f, unit="TFLOP/s",
+                    frac=round(achieved / peak_f, 4))
+    achieved = nbytes / t / 1e9
+    return dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_GBPS, unit="GB/s",
+                frac=round(achieved / HBM_GBPS, 4))
+
+
+def cpu_baseline(cfg, inp, sample_tokens):
+    """The oracle as it stands, on the first `sample_tokens` tokens."""
+    from oracle import moe_oracle as O
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        cores = 1
+    Ts = min(sample_tokens, cfg.num_tokens)
+    scfg = cfg.replace(num_tokens=Ts)
+    x = inp.x[:Ts]
+    t0 = time.perf_counter()
+    O.forward(scfg, x, inp.w_router, inp.sel_bias, lambda e: (inp.w13[e], inp.w2[e]), inp.shared)
+    dt = time.perf_counter() - t0
+    return dict(value=round(Ts / dt, 2), unit="tokens/s", cores=int(cores), kind="oracle",
+                sample=f"first {Ts} of {cfg.num_tokens} tokens, all {cfg.num_experts} experts"
+                       + (", capacity recomputed for the sample" if cfg.capacity_factor > 0 else "")
+                       + f"; {dt:.1f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="switch", choices=sorted(W.CONFIGS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=None)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import top_routing_dispatch_amd as M
+    from workloads.torch_io import act_torch_dtype, to_torch, upload_experts
+
+    cfg = W.CONFIGS[args.config]
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    t_setup = time.perf_counter()
+    inp = W.make_inputs(cfg, with_experts=False)
+    x = to_torch(inp.x, dev)
+    w13, w2, host = upload_experts(cfg, dev, keep_host=not args.no_cpu_baseline)
+    if host is not None:
+        inp.w13 = _Stack(host, 0)
+        inp.w2 = _Stack(host, 1)
+    weights = dict(w_router=to_torch(inp.w_router, dev), sel_bias=to_torch(inp.sel_bias, dev), w13=w13, w2=w2,
+                   ws13=to_torch(inp.ws13, dev), ws2=to_torch(inp.ws2, dev))
+    T, E, k = cfg.num_tokens, cfg.num_experts, cfg.top_k
+    y = torch.empty((T, cfg.d_model), dtype=act_torch_dtype(cfg), device=dev)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    tw = torch.empty((T, k), dtype=torch.float32, device=dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    stats = torch.empty(2 * E + 2, dtype=torch.float32, device=dev)
+    dropped = torch.empty(1, dtype=torch.int32, device=dev)
+    ws = M.workspace(cfg, M.MOE_OP_LAYER, dev)
+    torch.cuda.synchronize()
+    log(f"[bench] {cfg.name}: setup {time.perf_counter() - t_setup:.1f} s, workspace {ws.numel() / 1e6:.1f} MB")
+
+    nst = len(M.STAGES)
+
+    def new_events():
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * nst)]
+        for e in evs:
+            e.record()          # creates the HIP event handle
+        return evs
+
+    def step(evs=None):
+        M.moe_layer_forward_timed(cfg, weights, x, y, idx, tw, counts, cfg.alpha, stats, dropped, ws,
+                                  stage_events=evs)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [new_events() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    log(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step")
+
+    # per-stage averages over the timed steps (HIP events on the library's stream)
+    stage_ms = {}
+    c_host = counts.cpu().numpy()
+    for si, name in enumerate(M.STAGES):
+        vals = []
+        for evs in events:
+            try:
+                vals.append(evs[2 * si].elapsed_time(evs[2 * si + 1]))
+            except RuntimeError:
+                vals = []
+                break
+        if vals and max(vals) > 0:
+            stage_ms[name] = float(np.mean(vals))
+    cap, rows_cap = M.moe_capacity(cfg)
+    kept = np.minimum(c_host, cap)
+    A = int(kept.sum())
+    E_act = int((kept > 0).sum())
+    stage_info = {}
+    for name, ms in stage_ms.items():
+        fl, by = stage_work(cfg, name, A, E_act, T)
+        stage_info[name] = dict(ms=round(ms, 4), **roofline_of(cfg, name, fl, by, ms))
+    dominant = max(stage_ms, key=stage_ms.get)
+    fl, by = stage_work(cfg, dominant, A, E_act, T)
+    roof = roofline_of(cfg, dominant, fl, by, stage_ms[dominant])
+    roof["kernel"] = dominant
+    roof["traffic"] = None
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        n = args.cpu_sample_tokens or DEFAULT_CPU_SAMPLE.get(cfg.name, 64)
+        log(f"[bench] timing the CPU oracle on {n} tokens")
+        cpu = cpu_baseline(cfg, inp, n)
+
+    value = T / (ms_per_step * 1e-3)
+    line = {
+        "metric": "MoE-layer tokens/sec at 1 GPU; % HBM roofline (route/permute) and % MFMA peak",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg.act_dtype == W.BF16 else "f32", "data": "synthetic",
+        "config": {"workload": cfg.name, "tokens": T, "d_model": cfg.d_model, "experts": E, "top_k": k,
+                   "d_ff": cfg.d_ff, "shared": cfg.num_shared, "d_ff_shared": cfg.d_ff_shared,
+                   "scoring": ["softmax_topk", "topk_softmax", "sigmoid_bias"][cfg.scoring],
+                   "activation": ["swiglu", "gelu"][cfg.activation], "capacity_factor": cfg.capacity_factor,
+                   "kept_rows": A, "active_experts": E_act, "max_expert_rows": int(kept.max())},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "stages": stage_info,
+    }
+    print(json.dumps(line), flush=True)
+
+
+class _Stack:
+    """Indexable view of per-expert host weights kept by upload_experts."""
+
+    def __init__(self, host, i):
+        self.host, self.i = host, i
+
+    def __getitem__(self, e):
+        return self.host[e][self.i]
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,125 @@
+"""Host-side tests of the C ABI (no GPU): the library loads, exports every
+symbol include/moe.h declares, sizes workspaces, and rejects bad arguments
+before enqueuing anything (so no HIP call is reached)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import top_routing_dispatch_amd as M
+import workloads as W
+from top_routing_dispatch_amd import binding as B
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:moe_status|const char\*)\s+(moe_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 10
+    L = M.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(B.EXPORTED)
+
+
+def test_status_strings():
+    L = M.lib()
+    for st in range(5):
+        assert L.moe_status_string(st).decode().startswith("MOE_")
+
+
+def test_capacity_matches_formula():
+    assert M.moe_capacity(W.SWITCH) == (80, 8192)                  # 1.25 * 8192 * 1 / 128
+    cap, rows = M.moe_capacity(W.DEEPSEEKV3)
+    assert cap == 2**31 - 1 and rows == 8192 * 8                    # dropless
+    c = W.MoEConfig("c", 10, 8, 4, 1, 8, capacity_factor=1.5)       # 3.75 -> 4
+    assert M.moe_capacity(c) == (4, 10)
+    c = W.MoEConfig("c", 10, 8, 4, 2, 8, capacity_factor=0.01)      # ceil(0.05) = 1
+    assert M.moe_capacity(c) == (1, 4)
+
+
+def test_capacity_agrees_with_oracle():
+    from oracle import moe_oracle as O
+    for cf in (0.3, 0.75, 1.0, 1.1, 1.25, 1.7, 2.0):
+        for T, k, E in ((8192, 1, 128), (777, 8, 64), (10, 3, 7)):
+            c = W.MoEConfig("c", T, 8, E, k, 8, capacity_factor=cf)
+            assert M.moe_capacity(c)[0] == O.capacity(cf, T, k, E), (cf, T, k, E)
+
+
+def test_workspace_sizes_cover_buffers():
+    c = W.DEEPSEEKV3
+    layer = M.moe_workspace_size(c, M.MOE_OP_LAYER)
+    A = 8192 * 8
+    assert layer >= A * 7168 * 2 + A * 2048 * 2        # y_perm + hidden
+    assert M.moe_workspace_size(c, M.MOE_OP_ROUTE) >= 8192 * 256 * 4
+    for op in range(6):
+        assert M.moe_workspace_size(c, op) % 256 == 0
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("top_k", 0, M.MOE_ERR_INVALID_ARGUMENT),
+    ("top_k", 5, M.MOE_ERR_INVALID_ARGUMENT),          # k > E
+    ("num_experts", 2000, M.MOE_ERR_UNSUPPORTED),
+    ("d_model", 30, M.MOE_ERR_UNSUPPORTED),            # bf16 rows must be 16-byte multiples
+    ("scoring", 7, M.MOE_ERR_INVALID_ARGUMENT),
+    ("num_tokens", -1, M.MOE_ERR_INVALID_ARGUMENT),
+    ("router_dtype", W.BF16, None),
+])
+def test_config_validation(field, value, status):
+    cfg = W.MoEConfig("v", 16, 64, 4, 2, 32).replace(**{field: value})
+    if field == "router_dtype":
+        cfg = cfg.replace(act_dtype=W.F32)            # f32 activations with bf16 router: unsupported
+        status = M.MOE_ERR_UNSUPPORTED
+    with pytest.raises(M.MoEError) as ei:
+        M.moe_workspace_size(cfg, M.MOE_OP_LAYER)
+    assert ei.value.status == status
+
+
+def _raw(fn, *args):
+    return getattr(M.lib(), fn)(*args)
+
+
+def test_null_and_misaligned_pointers_rejected_before_launch():
+    cfg = W.MoEConfig("v", 16, 64, 4, 2, 32)
+    c = B.make_config(cfg)
+    p = ctypes.c_void_p(0x100000)           # aligned, never dereferenced: validation fails first
+    mis = ctypes.c_void_p(0x100004)
+    ws_n = M.moe_workspace_size(cfg, M.MOE_OP_ROUTE)
+    # missing outputs
+    assert _raw("moe_route", ctypes.byref(c), p, p, None, None, p, None, p, ws_n, None) == M.MOE_ERR_INVALID_ARGUMENT
+    # misaligned input
+    assert _raw("moe_route", ctypes.byref(c), mis, p, None, p, p, None, p, ws_n, None) == M.MOE_ERR_INVALID_ARGUMENT
+    # workspace too small
+    assert _raw("moe_route", ctypes.byref(c), p, p, None, p, p, None, p, ws_n - 256, None) == \
+        M.MOE_ERR_WORKSPACE_TOO_SMALL
+    # permute: x without x_perm
+    assert _raw("moe_permute", ctypes.byref(c), p, p, p, p, p, p, None, p, 1 << 20, None) == \
+        M.MOE_ERR_INVALID_ARGUMENT
+    # expert ffn: bad activation / group count
+    assert _raw("moe_expert_ffn", ctypes.byref(c), 4, 32, 9, 8, p, None, p, p, p, p, p, 1 << 20, None) == \
+        M.MOE_ERR_INVALID_ARGUMENT
+    assert _raw("moe_expert_ffn", ctypes.byref(c), 0, 32, 0, 8, p, None, p, p, p, p, p, 1 << 20, None) == \
+        M.MOE_ERR_INVALID_ARGUMENT
+    # layer: missing weights struct
+    assert _raw("moe_layer_forward", ctypes.byref(c), None, p, p, None, None, None, ctypes.c_float(0.01), None,
+                None, p, 1 << 30, None) == M.MOE_ERR_INVALID_ARGUMENT
+    # layer: shared experts declared but weights missing
+    cs = B.make_config(cfg.replace(num_shared=1, d_ff_shared=16))
+    w = B.moe_weights(p.value, None, p.value, p.value, None, None)
+    assert _raw("moe_layer_forward", ctypes.byref(cs), ctypes.byref(w), p, p, None, None, None, ctypes.c_float(0.01),
+                None, None, p, 1 << 30, None) == M.MOE_ERR_INVALID_ARGUMENT
+    # null config
+    assert _raw("moe_combine", None, p, p, p, None, p, None) == M.MOE_ERR_INVALID_ARGUMENT
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(B, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        B.lib()

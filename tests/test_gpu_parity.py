@@ -1,0 +1,299 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, on seeded
+inputs at sizes the oracle finishes in seconds (several tiles, ragged tails).
+"""
+import numpy as np
+import pytest
+import torch
+
+import top_routing_dispatch_amd as M
+import workloads as W
+from oracle import moe_oracle as O
+from workloads.torch_io import act_torch_dtype, to_numpy, to_torch
+
+from parity import (BF16_TOL, W_TOL, DeviceLayer, check_layer, oracle_forward, out_tol, rel_err,
+                    route_differences, row_rel_err)
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    W.TINY,
+    W.MoEConfig("switch_small", 700, 136, 16, 1, 200, scoring=W.SOFTMAX_TOPK, renormalize=0,
+                activation=W.GELU, act_dtype=W.BF16, router_dtype=W.F32, capacity_factor=1.25),
+    W.MoEConfig("mixtral_small", 520, 264, 8, 2, 328, scoring=W.TOPK_SOFTMAX, zipf_s=1.0),
+    W.MoEConfig("deepseekmoe_small", 600, 200, 32, 6, 136, num_shared=2, d_ff_shared=72,
+                scoring=W.SOFTMAX_TOPK, renormalize=1),
+    W.MoEConfig("deepseekv3_small", 777, 320, 64, 8, 256, num_shared=1, d_ff_shared=128,
+                scoring=W.SIGMOID_BIAS, renormalize=1, zipf_s=1.2),
+    W.MoEConfig("fp32_shared_gelu", 150, 96, 12, 3, 100, num_shared=3, d_ff_shared=20,
+                activation=W.GELU, act_dtype=W.F32, router_dtype=W.F32, capacity_factor=0.8),
+    W.MoEConfig("bf16_x_f32_router_swiglu", 300, 64, 24, 4, 72, act_dtype=W.BF16, router_dtype=W.F32),
+]
+
+EDGE = [
+    W.MoEConfig("one_token", 1, 64, 4, 2, 64),
+    W.MoEConfig("one_expert", 130, 64, 1, 1, 48),
+    W.MoEConfig("k_equals_e_soft", 90, 64, 8, 8, 40, renormalize=1),
+    W.MoEConfig("mostly_empty_experts", 20, 72, 64, 2, 56, scoring=W.SIGMOID_BIAS),
+    W.MoEConfig("max_experts_max_k", 70, 64, 1024, 32, 16, scoring=W.SOFTMAX_TOPK),
+    W.MoEConfig("ragged_everything", 259, 8, 5, 3, 8, num_shared=1, d_ff_shared=8, capacity_factor=0.6),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL + EDGE, ids=lambda c: c.name)
+def test_layer_forward_matches_oracle(cfg):
+    print(f"[layer parity] {cfg.name}", flush=True)
+    inp = W.make_inputs(cfg)
+    ref = oracle_forward(cfg, inp)
+    dl = DeviceLayer(cfg, inp)
+    got = dl.layer()
+    diff, err = check_layer(cfg, inp, ref, got)
+    print(f"  max rel err {err:.3e}, near-tie tokens {len(diff)}")
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+def test_route_matches_oracle(cfg):
+    print(f"[route parity] {cfg.name}", flush=True)
+    inp = W.make_inputs(cfg, with_experts=False)
+    ref = O.route(inp.x, inp.w_router, inp.sel_bias, cfg.top_k, cfg.scoring, cfg.renormalize)
+    dl = DeviceLayer(cfg, inp)
+    got = dl.route()
+    diff = route_differences(cfg, ref, got["idx"], inp.sel_bias)
+    same = np.setdiff1d(np.arange(cfg.num_tokens), diff)
+    assert rel_err(got["w"][same], ref["w"][same]) <= W_TOL
+    assert rel_err(got["probs"], ref["probs"]) <= W_TOL
+
+
+def _permute_gpu(cfg, idx, x_host):
+    T, k, E = cfg.num_tokens, cfg.top_k, cfg.num_experts
+    cap, rows_cap = M.moe_capacity(cfg)
+    dev = "cuda"
+    idx_d = to_torch(idx.astype(np.int32), dev)
+    x_d = to_torch(x_host, dev) if x_host is not None else None
+    counts = torch.full((E,), -7, dtype=torch.int32, device=dev)
+    offsets = torch.full((E + 1,), -7, dtype=torch.int32, device=dev)
+    row_of = torch.full((T, k), -7, dtype=torch.int32, device=dev)
+    tor = torch.full((max(rows_cap, 1),), -7, dtype=torch.int32, device=dev)
+    xp = None
+    if x_d is not None:
+        xp = torch.zeros((max(rows_cap, 1), cfg.d_model), dtype=act_torch_dtype(cfg), device=dev)
+    ws = M.workspace(cfg, M.MOE_OP_PERMUTE, dev)
+    M.moe_permute(cfg, idx_d, x_d, counts, offsets, row_of, tor, xp, ws)
+    torch.cuda.synchronize()
+    return (to_numpy(counts), to_numpy(offsets), to_numpy(row_of), to_numpy(tor)[:rows_cap],
+            None if xp is None else to_numpy(xp)[:rows_cap])
+
+
+@pytest.mark.parametrize("cfg", SMALL + EDGE[:4], ids=lambda c: c.name)
+def test_permute_bit_exact(cfg):
+    """Dispatch of the oracle's own selection: counts, offsets, permutation, drops
+    and the gathered rows are bit-exact."""
+    print(f"[permute parity] {cfg.name}", flush=True)
+    inp = W.make_inputs(cfg, with_experts=False)
+    ref = O.route(inp.x, inp.w_router, inp.sel_bias, cfg.top_k, cfg.scoring, cfg.renormalize)
+    disp = O.dispatch(ref["idx"], cfg.num_experts, O.capacity(cfg.capacity_factor, cfg.num_tokens, cfg.top_k,
+                                                              cfg.num_experts))
+    counts, offsets, row_of, tor, xp = _permute_gpu(cfg, ref["idx"], inp.x)
+    np.testing.assert_array_equal(counts, disp["counts"])
+    np.testing.assert_array_equal(offsets, disp["offsets"])
+    np.testing.assert_array_equal(row_of, disp["row_of"])
+    A = int(disp["offsets"][-1])
+    np.testing.assert_array_equal(tor[:A], disp["token_of_row"])
+    assert (tor[A:] == -1).all()
+    np.testing.assert_array_equal(xp[:A], inp.x[disp["token_of_row"]])
+
+
+def test_permute_worked_example_and_capacity():
+    """The Tiny-MoE dispatch example (4 tokens, top-2), dropless and with C = 2."""
+    idx = np.array([[2, 0], [1, 2], [3, 0], [2, 1]])
+    cfg = W.MoEConfig("ex", 4, 8, 4, 2, 8, act_dtype=W.F32, router_dtype=W.F32)
+    counts, offsets, row_of, tor, _ = _permute_gpu(cfg, idx, None)
+    assert counts.tolist() == [2, 2, 3, 1] and offsets.tolist() == [0, 2, 4, 7, 8]
+    assert tor.tolist() == [0, 2, 1, 3, 0, 1, 3, 2]
+    assert row_of.tolist() == [[4, 0], [2, 5], [7, 1], [6, 3]]
+    cfg2 = cfg.replace(capacity_factor=1.0)          # C = ceil(1.0 * 4 * 2 / 4) = 2
+    counts, offsets, row_of, tor, _ = _permute_gpu(cfg2, idx, None)
+    assert offsets.tolist() == [0, 2, 4, 6, 7]
+    assert row_of.tolist() == [[4, 0], [2, 5], [6, 1], [-1, 3]]
+    assert tor.tolist() == [0, 2, 1, 3, 0, 1, 2]
+
+
+def test_permute_every_token_on_one_expert_with_capacity():
+    T, E = 1000, 8
+    cfg = W.MoEConfig("one_hot", T, 8, E, 1, 8, act_dtype=W.F32, router_dtype=W.F32, capacity_factor=2.0)
+    C = O.capacity(2.0, T, 1, E)     # 250
+    idx = np.full((T, 1), 5)
+    counts, offsets, row_of, tor, _ = _permute_gpu(cfg, idx, None)
+    assert counts.tolist() == [0] * 5 + [T] + [0] * 2
+    assert offsets[-1] == C
+    assert tor.tolist() == list(range(C))
+    assert (row_of[:C, 0] == np.arange(C)).all() and (row_of[C:, 0] == -1).all()
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+def test_expert_ffn_matches_oracle(cfg):
+    """Grouped expert FFN on the oracle's expert batches (x_perm, offsets)."""
+    print(f"[expert ffn parity] {cfg.name}", flush=True)
+    inp = W.make_inputs(cfg)
+    ref = oracle_forward(cfg, inp)
+    A = int(ref["offsets"][-1])
+    dev = "cuda"
+    xp = to_torch(inp.x[ref["token_of_row"]], dev) if A else torch.empty((0, cfg.d_model), device=dev)
+    off = to_torch(ref["offsets"].astype(np.int32), dev)
+    y = torch.zeros((max(A, 1), cfg.d_model), dtype=act_torch_dtype(cfg), device=dev)
+    ws = torch.empty(max(M.moe_workspace_size(cfg, M.MOE_OP_EXPERT_FFN), 256), dtype=torch.uint8, device=dev)
+    M.moe_expert_ffn(cfg, cfg.num_experts, cfg.d_ff, cfg.activation, A, xp, None, off,
+                     to_torch(inp.w13, dev), to_torch(inp.w2, dev), y, ws)
+    torch.cuda.synchronize()
+    err = row_rel_err(to_numpy(y)[:A], ref["y_perm"])
+    assert err <= out_tol(cfg), err
+    if cfg.num_shared:
+        ys = torch.zeros((cfg.num_tokens, cfg.d_model), dtype=act_torch_dtype(cfg), device=dev)
+        ws2 = M.workspace(cfg, M.MOE_OP_SHARED_FFN, dev)
+        M.moe_expert_ffn(cfg, 1, cfg.num_shared * cfg.d_ff_shared, W.SWIGLU, cfg.num_tokens, to_torch(inp.x, dev),
+                         None, None, to_torch(inp.ws13, dev), to_torch(inp.ws2, dev), ys, ws2)
+        torch.cuda.synchronize()
+        err = row_rel_err(to_numpy(ys), ref["y_shared"])
+        assert err <= out_tol(cfg), err
+
+
+@pytest.mark.parametrize("cfg", [SMALL[0], SMALL[3]], ids=lambda c: c.name)
+def test_expert_ffn_gathered_rows(cfg):
+    """Same grouped FFN reading token rows through the permutation (gather_rows)."""
+    inp = W.make_inputs(cfg)
+    ref = oracle_forward(cfg, inp)
+    A = int(ref["offsets"][-1])
+    dev = "cuda"
+    y = torch.zeros((A, cfg.d_model), dtype=act_torch_dtype(cfg), device=dev)
+    ws = M.workspace(cfg, M.MOE_OP_EXPERT_FFN, dev)
+    M.moe_expert_ffn(cfg, cfg.num_experts, cfg.d_ff, cfg.activation, A, to_torch(inp.x, dev),
+                     to_torch(ref["token_of_row"].astype(np.int32), dev), to_torch(ref["offsets"].astype(np.int32), dev),
+                     to_torch(inp.w13, dev), to_torch(inp.w2, dev), y, ws)
+    torch.cuda.synchronize()
+    assert row_rel_err(to_numpy(y), ref["y_perm"]) <= out_tol(cfg)
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+def test_combine_matches_oracle(cfg):
+    """Combine on oracle-supplied expert outputs (rounded to the activation type)."""
+    inp = W.make_inputs(cfg)
+    ref = oracle_forward(cfg, inp)
+    dev = "cuda"
+    enc = (lambda a: W.f32_to_bf16_bits(a.astype(np.float32))) if cfg.act_dtype == W.BF16 else \
+        (lambda a: a.astype(np.float32))
+    yp_h = enc(ref["y_perm"]) if ref["y_perm"].size else enc(np.zeros((1, cfg.d_model)))
+    yp = to_torch(yp_h, dev)
+    ys = to_torch(enc(ref["y_shared"]), dev) if ref["y_shared"] is not None else None
+    y = torch.empty((cfg.num_tokens, cfg.d_model), dtype=act_torch_dtype(cfg), device=dev)
+    M.moe_combine(cfg, yp, to_torch(ref["row_of"].astype(np.int32), dev), to_torch(ref["w"].astype(np.float32), dev),
+                  ys, y)
+    torch.cuda.synchronize()
+    # expected from the same rounded operands, in float64
+    Yr = O.widen(yp_h)
+    ysr = O.widen(enc(ref["y_shared"])) if ref["y_shared"] is not None else None
+    exp = O.combine(Yr[:int(ref["offsets"][-1])], ref, ref["w"].astype(np.float32).astype(np.float64),
+                    cfg.num_tokens, ysr)
+    assert row_rel_err(to_numpy(y), exp) <= out_tol(cfg)
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+def test_load_stats_matches_oracle(cfg):
+    inp = W.make_inputs(cfg, with_experts=False)
+    r = O.route(inp.x, inp.w_router, inp.sel_bias, cfg.top_k, cfg.scoring, cfg.renormalize)
+    cap = O.capacity(cfg.capacity_factor, cfg.num_tokens, cfg.top_k, cfg.num_experts)
+    d = O.dispatch(r["idx"], cfg.num_experts, cap)
+    st = O.load_stats(d["counts"], r["probs"], cfg.top_k, cfg.alpha, d["kept"])
+    dev = "cuda"
+    E = cfg.num_experts
+    f = torch.empty(E, device=dev)
+    P = torch.empty(E, device=dev)
+    out = torch.empty(2, device=dev)
+    dropped = torch.empty(1, dtype=torch.int32, device=dev)
+    ws = M.workspace(cfg, M.MOE_OP_LOAD_STATS, dev)
+    M.moe_load_stats(cfg, to_torch(d["counts"].astype(np.int32), dev), to_torch(r["probs"].astype(np.float32), dev),
+                     cfg.alpha, f, P, out[0:1], out[1:2], dropped, ws)
+    torch.cuda.synchronize()
+    assert rel_err(to_numpy(f), st["f"]) <= W_TOL
+    assert rel_err(to_numpy(P), st["P"]) <= W_TOL
+    o = to_numpy(out)
+    assert abs(o[0] - st["aux_loss"]) <= W_TOL * st["aux_loss"]
+    assert abs(o[1] - st["imbalance"]) <= W_TOL * st["imbalance"]
+    assert int(to_numpy(dropped)[0]) == st["dropped"]
+
+
+def test_load_stats_worked_examples():
+    """[9,4,2,1] -> imbalance 2.25; uniform routing -> loss = alpha."""
+    dev = "cuda"
+    cfg = W.MoEConfig("ex", 8, 8, 4, 2, 8, act_dtype=W.F32, router_dtype=W.F32)
+    probs = torch.full((8, 4), 0.25, device=dev)
+    f = torch.empty(4, device=dev); P = torch.empty(4, device=dev); o = torch.empty(2, device=dev)
+    dr = torch.empty(1, dtype=torch.int32, device=dev)
+    ws = M.workspace(cfg, M.MOE_OP_LOAD_STATS, dev)
+    M.moe_load_stats(cfg, torch.tensor([9, 4, 2, 1], dtype=torch.int32, device=dev), probs, 0.01, f, P,
+                     o[0:1], o[1:2], dr, ws)
+    torch.cuda.synchronize()
+    assert abs(o[1].item() - 2.25) < 1e-6
+    M.moe_load_stats(cfg, torch.tensor([4, 4, 4, 4], dtype=torch.int32, device=dev), probs, 0.01, f, P,
+                     o[0:1], o[1:2], dr, ws)
+    torch.cuda.synchronize()
+    assert abs(o[0].item() - 0.01) < 1e-8 and int(dr.item()) == 0
+
+
+def test_forced_expert_with_capacity_drops_to_residual():
+    """A huge selection bias sends every token to expert 3; with capacity C only
+    the first C tokens get expert output, the rest get exactly zero (the
+    residual carries them)."""
+    cfg = W.MoEConfig("forced", 300, 64, 8, 1, 32, scoring=W.SIGMOID_BIAS, renormalize=0, capacity_factor=2.0)
+    inp = W.make_inputs(cfg)
+    b = np.zeros(8, dtype=np.float32)
+    b[3] = 100.0
+    ref = oracle_forward(cfg, inp, sel_bias=b)
+    assert (ref["idx"][:, 0] == 3).all()
+    C = O.capacity(2.0, 300, 1, 8)
+    dl = DeviceLayer(cfg, inp, sel_bias=b)
+    got = dl.layer()
+    check_layer(cfg, inp, ref, got, sel_bias=b)
+    y = O.widen(got["y"])
+    assert (y[C:] == 0).all() and got["dropped"] == 300 - C
+
+
+def test_empty_batch():
+    cfg = W.MoEConfig("empty", 0, 64, 8, 2, 32)
+    inp = W.make_inputs(cfg)
+    dl = DeviceLayer(cfg, inp)
+    got = dl.layer()
+    assert got["y"].shape == (0, 64)
+    assert (got["counts"] == 0).all() and got["dropped"] == 0
+
+
+@pytest.mark.parametrize("cfg", [SMALL[2], SMALL[4], SMALL[1]], ids=lambda c: c.name)
+def test_deterministic(cfg):
+    inp = W.make_inputs(cfg)
+    dl = DeviceLayer(cfg, inp)
+    a, b = dl.layer(), dl.layer()
+    for key in ("y", "idx", "w", "counts", "stats"):
+        np.testing.assert_array_equal(a[key], b[key])
+
+
+def test_near_tie_refinement_decides_in_double_precision():
+    """Two experts whose logits differ by far less than float32 can resolve:
+    the library must still pick the one the exact logits rank higher."""
+    T, D, E = 64, 64, 16
+    cfg = W.MoEConfig("ties", T, D, E, 2, 16, act_dtype=W.F32, router_dtype=W.F32, scoring=W.TOPK_SOFTMAX)
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((T, D)).astype(np.float32)
+    wr = (rng.standard_normal((E, D)) * 0.02).astype(np.float32)
+    # expert 9 = expert 4 plus a tiny perturbation on one coordinate: logits of 4 and 9
+    # differ by ~x[:, 0] * 2^-20, below float32 resolution of a D-long sum
+    wr[4] = wr[2] * 3
+    wr[9] = wr[4]
+    wr[9, 0] = np.nextafter(wr[9, 0], np.float32(1.0))
+    inp = W.HostInputs(cfg, x, wr, None, np.zeros((E, 32, D), np.float32), np.zeros((E, D, 16), np.float32),
+                       [], None, None)
+    ref = O.route(x, wr, None, 2, cfg.scoring, 0)
+    dl = DeviceLayer(cfg, inp)
+    got = dl.route()
+    diff = route_differences(cfg, ref, got["idx"], None)
+    # the exact logits of 4 and 9 are distinct (gap ~1e-9 relative: exempt by the 1e-6 rule),
+    # yet the refinement orders them like the float64 oracle
+    np.testing.assert_array_equal(got["idx"], ref["idx"])
+    assert len(diff) == 0

@@ -1,0 +1,448 @@
+// C ABI of the MoE layer library: argument validation, workspace carving and
+// the launch sequence of each entry point.  Declarations and the contract of
+// every function are in include/moe.h.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "common.h"
+#include "moe.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+void set_error(const char* where, hipError_t e) {
+  snprintf(g_last_error, sizeof(g_last_error), "%s: %s", where, hipGetErrorString(e));
+}
+
+moe_status hip_status(const char* where, hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  set_error(where, e);
+  (void)hipGetLastError();   // clear the sticky launch error
+  return MOE_ERR_HIP;
+}
+
+#define MOE_TRY_HIP(where, expr)                        \
+  do {                                                  \
+    const moe_status _st = hip_status(where, (expr));   \
+    if (_st != MOE_OK) return _st;                      \
+  } while (0)
+#define MOE_TRY(expr)                                   \
+  do {                                                  \
+    const moe_status _st = (expr);                      \
+    if (_st != MOE_OK) return _st;                      \
+  } while (0)
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool opt_aligned(const void* p) { return p == nullptr || aligned16(p); }
+inline size_t esize(int dt) { return dt == BF16 ? 2 : 4; }
+inline size_t carve(size_t bytes) { return round_up(bytes, 256); }
+
+struct Derived {
+  int capacity;     // INT32_MAX when dropless
+  int rows_cap;     // A_cap
+};
+
+moe_status derive(const moe_config* c, Derived* d) {
+  const long long A = (long long)c->num_tokens * c->top_k;
+  if (c->capacity_factor > 0.0f) {
+    const double C = ceil((double)c->capacity_factor * (double)A / (double)c->num_experts);
+    d->capacity = C >= 2147483647.0 ? INT32_MAX : (int)C;
+    const long long ec = (long long)c->num_experts * d->capacity;
+    d->rows_cap = (int)(A < ec ? A : ec);
+  } else {
+    d->capacity = INT32_MAX;
+    d->rows_cap = (int)A;
+  }
+  return MOE_OK;
+}
+
+moe_status validate_config(const moe_config* c) {
+  if (c == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+  if (c->num_tokens < 0 || c->d_model <= 0 || c->num_experts <= 0 || c->top_k <= 0 || c->d_ff <= 0)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (c->top_k > c->num_experts) return MOE_ERR_INVALID_ARGUMENT;
+  if (c->num_shared < 0 || (c->num_shared > 0 && c->d_ff_shared <= 0)) return MOE_ERR_INVALID_ARGUMENT;
+  if (c->scoring < 0 || c->scoring > 2) return MOE_ERR_INVALID_ARGUMENT;
+  if (c->activation < 0 || c->activation > 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (c->act_dtype < 0 || c->act_dtype > 1 || c->router_dtype < 0 || c->router_dtype > 1)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!(c->capacity_factor == c->capacity_factor)) return MOE_ERR_INVALID_ARGUMENT;   // NaN
+  if (c->num_experts > kMaxExperts || c->top_k > kMaxTopK) return MOE_ERR_UNSUPPORTED;
+  if (c->act_dtype == F32 && c->router_dtype == BF16) return MOE_ERR_UNSUPPORTED;
+  const int vec = c->act_dtype == BF16 ? 8 : 4;
+  if (c->d_model % vec || c->d_ff % vec) return MOE_ERR_UNSUPPORTED;
+  if (c->num_shared > 0 && (((long long)c->num_shared * c->d_ff_shared) % vec)) return MOE_ERR_UNSUPPORTED;
+  const long long T = c->num_tokens;
+  if (T * c->num_experts > INT32_MAX / 2 || T * c->top_k > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
+  if ((long long)c->num_shared * c->d_ff_shared > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// Workspace pieces ---------------------------------------------------------
+size_t ws_route(const moe_config* c) { return carve((size_t)c->num_tokens * c->num_experts * 4); }
+size_t ws_permute(const moe_config* c) {
+  return carve((size_t)ceil_div(c->num_tokens, kPermuteTile) * c->num_experts * 4);
+}
+size_t ws_ffn(const moe_config*, int G, int F, int max_rows, int act) {
+  return carve((size_t)max_rows * F * esize(act)) + carve((size_t)(G + 1) * 4);
+}
+size_t ws_stats(const moe_config* c) {
+  return carve((size_t)ceil_div(c->num_tokens, kStatsChunk) * c->num_experts * 4);
+}
+
+struct Layout {
+  size_t logits, probs, idx, w, tile_counts, counts, offsets, tile_prefix, row_of, tor, h, yperm,
+      partial, total;
+};
+
+Layout layer_layout(const moe_config* c, const Derived& d) {
+  Layout L{};
+  const size_t T = c->num_tokens, E = c->num_experts, k = c->top_k;
+  const size_t es = esize(c->act_dtype);
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o += carve(bytes); return at; };
+  L.logits = take(T * E * 4);
+  L.probs = take(T * E * 4);
+  L.idx = take(T * k * 4);
+  L.w = take(T * k * 4);
+  L.tile_counts = take((size_t)ceil_div(c->num_tokens, kPermuteTile) * E * 4);
+  L.counts = take(E * 4);
+  L.offsets = take((E + 1) * 4);
+  L.tile_prefix = take((E + 1) * 4);
+  L.row_of = take(T * k * 4);
+  L.tor = take((size_t)d.rows_cap * 4);
+  const size_t h_routed = (size_t)d.rows_cap * c->d_ff * es;
+  const size_t h_shared = (size_t)T * c->num_shared * c->d_ff_shared * es;
+  L.h = take(h_routed > h_shared ? h_routed : h_shared);
+  L.yperm = take((size_t)d.rows_cap * c->d_model * es);
+  L.partial = take((size_t)ceil_div(c->num_tokens, kStatsChunk) * E * 4);
+  L.total = o;
+  return L;
+}
+
+template <typename P>
+P* at(void* ws, size_t off) { return reinterpret_cast<P*>(static_cast<char*>(ws) + off); }
+
+// Launch helpers -----------------------------------------------------------
+moe_status run_router_logits(const moe_config* c, const void* x, const void* w_router, float* logits,
+                             hipStream_t s) {
+  GroupedGemm g{};
+  g.A = x; g.a_rows = nullptr; g.lda = c->d_model;
+  g.B = w_router; g.b_group_stride = 0;
+  g.C = logits; g.ldc = c->num_experts;
+  g.M_max = c->num_tokens; g.N = c->num_experts; g.K = c->d_model;
+  g.G = 1; g.offsets = nullptr; g.tile_prefix = nullptr;
+  g.epilogue = EPI_STORE_F32;
+  if (c->router_dtype == BF16) MOE_TRY_HIP("router logits (bf16)", launch_gemm_bf16(g, s));
+  else MOE_TRY_HIP("router logits (f32)", launch_gemm_f32(g, c->act_dtype, F32, s));
+  return MOE_OK;
+}
+
+moe_status run_select(const moe_config* c, const float* logits, const void* x, const void* w_router,
+                      const float* sel_bias, int32_t* idx, float* w, float* probs, hipStream_t s) {
+  RouteArgs a{};
+  a.logits = logits; a.x = x; a.w_router = w_router;
+  a.sel_bias = c->scoring == SIGMOID_BIAS ? sel_bias : nullptr;
+  a.topk_idx = idx; a.topk_w = w; a.probs = probs;
+  a.T = c->num_tokens; a.D = c->d_model; a.E = c->num_experts; a.k = c->top_k;
+  a.scoring = c->scoring; a.renormalize = c->renormalize;
+  a.act_dtype = c->act_dtype; a.router_dtype = c->router_dtype;
+  MOE_TRY_HIP("route select", launch_route_select(a, s));
+  return MOE_OK;
+}
+
+int ffn_bm(int act) {
+  GroupedGemm dummy{};
+  return act == BF16 ? gemm_bf16_bm(dummy) : kF32GemmBM;
+}
+
+// gate/up (+activation) then down projection for G groups.
+// Records stage event `which` (0 = start, 1 = stop) when timing is requested.
+moe_status mark(void* const* ev, int stage, int which, hipStream_t s) {
+  if (ev == nullptr || ev[2 * stage + which] == nullptr) return MOE_OK;
+  MOE_TRY_HIP("stage event", hipEventRecord(static_cast<hipEvent_t>(ev[2 * stage + which]), s));
+  return MOE_OK;
+}
+
+moe_status run_ffn(int act, int activation, int G, int D, int F, int max_rows, const void* x_in,
+                   const int32_t* gather, const int32_t* offsets, const int32_t* tile_prefix,
+                   const void* w13, const void* w2, void* h, void* y_out, hipStream_t s,
+                   void* const* ev = nullptr, int stage_up = 0, int stage_down = 0) {
+  const int n_mat = activation == SWIGLU ? 2 : 1;
+  GroupedGemm g1{};
+  g1.A = x_in; g1.a_rows = gather; g1.lda = D;
+  g1.B = w13; g1.b_group_stride = (long long)n_mat * F * D;
+  g1.C = h; g1.ldc = F;
+  g1.M_max = max_rows; g1.N = F; g1.K = D;
+  g1.G = G; g1.offsets = offsets; g1.tile_prefix = tile_prefix;
+  g1.epilogue = activation == SWIGLU ? EPI_SWIGLU : EPI_GELU;
+  GroupedGemm g2{};
+  g2.A = h; g2.a_rows = nullptr; g2.lda = F;
+  g2.B = w2; g2.b_group_stride = (long long)D * F;
+  g2.C = y_out; g2.ldc = D;
+  g2.M_max = max_rows; g2.N = D; g2.K = F;
+  g2.G = G; g2.offsets = offsets; g2.tile_prefix = tile_prefix;
+  g2.epilogue = EPI_STORE_ACT;
+  MOE_TRY(mark(ev, stage_up, 0, s));
+  if (act == BF16) MOE_TRY_HIP("expert gate/up", launch_gemm_bf16(g1, s));
+  else MOE_TRY_HIP("expert gate/up", launch_gemm_f32(g1, F32, F32, s));
+  MOE_TRY(mark(ev, stage_up, 1, s));
+  MOE_TRY(mark(ev, stage_down, 0, s));
+  if (act == BF16) MOE_TRY_HIP("expert down", launch_gemm_bf16(g2, s));
+  else MOE_TRY_HIP("expert down", launch_gemm_f32(g2, F32, F32, s));
+  MOE_TRY(mark(ev, stage_down, 1, s));
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status st) {
+  switch (st) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "unknown moe_status";
+}
+
+const char* moe_last_error(void) { return g_last_error; }
+
+moe_status moe_capacity(const moe_config* cfg, int32_t* capacity, int32_t* rows_cap) {
+  MOE_TRY(validate_config(cfg));
+  Derived d;
+  derive(cfg, &d);
+  if (capacity) *capacity = d.capacity;
+  if (rows_cap) *rows_cap = d.rows_cap;
+  return MOE_OK;
+}
+
+moe_status moe_workspace_size(const moe_config* cfg, int32_t op, size_t* bytes) {
+  MOE_TRY(validate_config(cfg));
+  if (bytes == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+  Derived d;
+  derive(cfg, &d);
+  switch (op) {
+    case MOE_OP_ROUTE: *bytes = ws_route(cfg); break;
+    case MOE_OP_PERMUTE: *bytes = ws_permute(cfg); break;
+    case MOE_OP_EXPERT_FFN:
+      *bytes = ws_ffn(cfg, cfg->num_experts, cfg->d_ff, d.rows_cap, cfg->act_dtype);
+      break;
+    case MOE_OP_SHARED_FFN:
+      *bytes = ws_ffn(cfg, 1, cfg->num_shared * cfg->d_ff_shared, cfg->num_tokens, cfg->act_dtype);
+      break;
+    case MOE_OP_LOAD_STATS: *bytes = ws_stats(cfg); break;
+    case MOE_OP_LAYER: *bytes = layer_layout(cfg, d).total; break;
+    default: return MOE_ERR_INVALID_ARGUMENT;
+  }
+  return MOE_OK;
+}
+
+moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
+                     const float* sel_bias, int32_t* topk_idx, float* topk_w, float* probs,
+                     void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(validate_config(cfg));
+  if (cfg->num_tokens > 0 && (x == nullptr || topk_idx == nullptr || topk_w == nullptr || ws == nullptr))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (w_router == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+  if (!opt_aligned(x) || !aligned16(w_router) || !opt_aligned(sel_bias) || !opt_aligned(topk_idx) ||
+      !opt_aligned(topk_w) || !opt_aligned(probs) || !opt_aligned(ws))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < ws_route(cfg)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (cfg->num_tokens == 0) return MOE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* logits = static_cast<float*>(ws);
+  MOE_TRY(run_router_logits(cfg, x, w_router, logits, s));
+  return run_select(cfg, logits, x, w_router, sel_bias, topk_idx, topk_w, probs, s);
+}
+
+moe_status moe_permute(const moe_config* cfg, const int32_t* topk_idx, const void* x,
+                       int32_t* counts, int32_t* offsets, int32_t* row_of, int32_t* token_of_row,
+                       void* x_perm, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(validate_config(cfg));
+  Derived d;
+  derive(cfg, &d);
+  const bool any = cfg->num_tokens > 0;
+  if (counts == nullptr || offsets == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+  if (any && (topk_idx == nullptr || row_of == nullptr || ws == nullptr)) return MOE_ERR_INVALID_ARGUMENT;
+  if (d.rows_cap > 0 && token_of_row == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+  if ((x == nullptr) != (x_perm == nullptr)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!opt_aligned(topk_idx) || !opt_aligned(x) || !aligned16(counts) || !aligned16(offsets) ||
+      !opt_aligned(row_of) || !opt_aligned(token_of_row) || !opt_aligned(x_perm) || !opt_aligned(ws))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < ws_permute(cfg)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  PermuteArgs a{};
+  a.topk_idx = topk_idx; a.T = cfg->num_tokens; a.k = cfg->top_k; a.E = cfg->num_experts;
+  a.capacity = d.capacity; a.rows_cap = d.rows_cap;
+  a.tile_counts = static_cast<int32_t*>(ws);
+  a.counts = counts; a.offsets = offsets; a.row_of = row_of; a.token_of_row = token_of_row;
+  a.tile_prefix = nullptr; a.bm = 1;
+  MOE_TRY_HIP("permute", launch_permute(a, s));
+  if (x != nullptr)
+    MOE_TRY_HIP("gather rows", launch_gather_rows(x, token_of_row, offsets, cfg->num_experts, d.rows_cap,
+                                                  cfg->d_model, (int)esize(cfg->act_dtype), x_perm, s));
+  return MOE_OK;
+}
+
+moe_status moe_expert_ffn(const moe_config* cfg, int32_t num_groups, int32_t d_ff, int32_t activation,
+                          int32_t max_rows, const void* x_in, const int32_t* gather_rows,
+                          const int32_t* offsets, const void* w13, const void* w2, void* y_out,
+                          void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(validate_config(cfg));
+  if (num_groups <= 0 || d_ff <= 0 || max_rows < 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (activation != SWIGLU && activation != GELU) return MOE_ERR_INVALID_ARGUMENT;
+  if (num_groups > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  const int vec = cfg->act_dtype == BF16 ? 8 : 4;
+  if (d_ff % vec) return MOE_ERR_UNSUPPORTED;
+  if (max_rows > 0 && (x_in == nullptr || w13 == nullptr || w2 == nullptr || y_out == nullptr || ws == nullptr))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!opt_aligned(x_in) || !opt_aligned(gather_rows) || !opt_aligned(offsets) || !opt_aligned(w13) ||
+      !opt_aligned(w2) || !opt_aligned(y_out) || !opt_aligned(ws))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < ws_ffn(cfg, num_groups, d_ff, max_rows, cfg->act_dtype)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (max_rows == 0) return MOE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* h = ws;
+  int32_t* tile_prefix = nullptr;
+  if (offsets != nullptr) {
+    tile_prefix = at<int32_t>(ws, carve((size_t)max_rows * d_ff * esize(cfg->act_dtype)));
+    MOE_TRY_HIP("tile prefix", launch_tile_prefix(offsets, num_groups, ffn_bm(cfg->act_dtype), tile_prefix, s));
+  }
+  return run_ffn(cfg->act_dtype, activation, num_groups, cfg->d_model, d_ff, max_rows, x_in, gather_rows,
+                 offsets, tile_prefix, w13, w2, h, y_out, s);
+}
+
+moe_status moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* row_of,
+                       const float* topk_w, const void* y_shared, void* y, void* stream) {
+  MOE_TRY(validate_config(cfg));
+  Derived d;
+  derive(cfg, &d);
+  if (cfg->num_tokens > 0 && (row_of == nullptr || topk_w == nullptr || y == nullptr))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (d.rows_cap > 0 && cfg->num_tokens > 0 && y_perm == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+  if (!opt_aligned(y_perm) || !opt_aligned(row_of) || !opt_aligned(topk_w) || !opt_aligned(y_shared) ||
+      !opt_aligned(y))
+    return MOE_ERR_INVALID_ARGUMENT;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  MOE_TRY_HIP("combine", launch_combine(y_perm, row_of, topk_w, y_shared, y, cfg->num_tokens, cfg->top_k,
+                                        cfg->d_model, cfg->act_dtype, s));
+  return MOE_OK;
+}
+
+moe_status moe_load_stats(const moe_config* cfg, const int32_t* counts, const float* probs, float alpha,
+                          float* f, float* P, float* aux_loss, float* imbalance, int32_t* dropped,
+                          void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(validate_config(cfg));
+  Derived d;
+  derive(cfg, &d);
+  if (counts == nullptr || (cfg->num_tokens > 0 && (probs == nullptr || ws == nullptr)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(counts) || !opt_aligned(probs) || !opt_aligned(ws)) return MOE_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < ws_stats(cfg)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  StatsArgs a{};
+  a.counts = counts; a.probs = probs; a.partial = static_cast<float*>(ws);
+  a.T = cfg->num_tokens; a.E = cfg->num_experts; a.k = cfg->top_k; a.capacity = d.capacity;
+  a.alpha = alpha; a.f = f; a.P = P; a.aux_loss = aux_loss; a.imbalance = imbalance; a.dropped = dropped;
+  MOE_TRY_HIP("load stats", launch_load_stats(a, static_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
+moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* wt, const void* x, void* y,
+                             int32_t* topk_idx, float* topk_w, int32_t* counts, float alpha, float* stats,
+                             int32_t* dropped, void* ws, size_t ws_bytes, void* stream) {
+  return moe_layer_forward_timed(cfg, wt, x, y, topk_idx, topk_w, counts, alpha, stats, dropped, ws, ws_bytes,
+                                 stream, nullptr);
+}
+
+moe_status moe_layer_forward_timed(const moe_config* cfg, const moe_weights* wt, const void* x, void* y,
+                                   int32_t* topk_idx, float* topk_w, int32_t* counts, float alpha, float* stats,
+                                   int32_t* dropped, void* ws, size_t ws_bytes, void* stream,
+                                   void* const* ev) {
+  MOE_TRY(validate_config(cfg));
+  if (wt == nullptr || wt->w_router == nullptr || wt->w13 == nullptr || wt->w2 == nullptr)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (cfg->num_shared > 0 && (wt->ws13 == nullptr || wt->ws2 == nullptr)) return MOE_ERR_INVALID_ARGUMENT;
+  const bool any = cfg->num_tokens > 0;
+  if (any && (x == nullptr || y == nullptr || ws == nullptr)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!opt_aligned(x) || !opt_aligned(y) || !opt_aligned(topk_idx) || !opt_aligned(topk_w) ||
+      !opt_aligned(counts) || !opt_aligned(stats) || !opt_aligned(dropped) || !opt_aligned(ws) ||
+      !aligned16(wt->w_router) || !opt_aligned(wt->sel_bias) || !aligned16(wt->w13) || !aligned16(wt->w2) ||
+      !opt_aligned(wt->ws13) || !opt_aligned(wt->ws2))
+    return MOE_ERR_INVALID_ARGUMENT;
+  Derived d;
+  derive(cfg, &d);
+  const Layout L = layer_layout(cfg, d);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int T = cfg->num_tokens, E = cfg->num_experts, D = cfg->d_model;
+  const bool want_stats = stats != nullptr || dropped != nullptr;
+
+  int32_t* idx = topk_idx ? topk_idx : at<int32_t>(ws, L.idx);
+  float* w = topk_w ? topk_w : at<float>(ws, L.w);
+  int32_t* cnt = counts ? counts : at<int32_t>(ws, L.counts);
+  int32_t* off = at<int32_t>(ws, L.offsets);
+  int32_t* tp = at<int32_t>(ws, L.tile_prefix);
+  int32_t* row_of = at<int32_t>(ws, L.row_of);
+  int32_t* tor = at<int32_t>(ws, L.tor);
+  float* probs = want_stats ? at<float>(ws, L.probs) : nullptr;
+
+  if (any) {
+    float* logits = at<float>(ws, L.logits);
+    MOE_TRY(mark(ev, MOE_STAGE_ROUTER_LOGITS, 0, s));
+    MOE_TRY(run_router_logits(cfg, x, wt->w_router, logits, s));
+    MOE_TRY(mark(ev, MOE_STAGE_ROUTER_LOGITS, 1, s));
+    MOE_TRY(mark(ev, MOE_STAGE_ROUTE_SELECT, 0, s));
+    MOE_TRY(run_select(cfg, logits, x, wt->w_router, wt->sel_bias, idx, w, probs, s));
+    MOE_TRY(mark(ev, MOE_STAGE_ROUTE_SELECT, 1, s));
+  }
+
+  PermuteArgs pa{};
+  pa.topk_idx = idx; pa.T = T; pa.k = cfg->top_k; pa.E = E;
+  pa.capacity = d.capacity; pa.rows_cap = d.rows_cap;
+  pa.tile_counts = at<int32_t>(ws, L.tile_counts);
+  pa.counts = cnt; pa.offsets = off; pa.row_of = row_of; pa.token_of_row = tor;
+  pa.tile_prefix = tp; pa.bm = ffn_bm(cfg->act_dtype);
+  MOE_TRY(mark(ev, MOE_STAGE_PERMUTE, 0, s));
+  MOE_TRY_HIP("permute", launch_permute(pa, s));
+  MOE_TRY(mark(ev, MOE_STAGE_PERMUTE, 1, s));
+
+  if (any) {
+    void* h = at<void>(ws, L.h);
+    void* yperm = at<void>(ws, L.yperm);
+    if (d.rows_cap > 0)
+      MOE_TRY(run_ffn(cfg->act_dtype, cfg->activation, E, D, cfg->d_ff, d.rows_cap, x, tor, off, tp, wt->w13,
+                      wt->w2, h, yperm, s, ev, MOE_STAGE_EXPERT_GATE_UP, MOE_STAGE_EXPERT_DOWN));
+    const void* y_shared = nullptr;
+    if (cfg->num_shared > 0) {
+      const int SF = cfg->num_shared * cfg->d_ff_shared;
+      MOE_TRY(run_ffn(cfg->act_dtype, SWIGLU, 1, D, SF, T, x, nullptr, nullptr, nullptr, wt->ws13, wt->ws2, h,
+                      y, s, ev, MOE_STAGE_SHARED_GATE_UP, MOE_STAGE_SHARED_DOWN));
+      y_shared = y;
+    }
+    MOE_TRY(mark(ev, MOE_STAGE_COMBINE, 0, s));
+    MOE_TRY_HIP("combine", launch_combine(yperm, row_of, w, y_shared, y, T, cfg->top_k, D, cfg->act_dtype, s));
+    MOE_TRY(mark(ev, MOE_STAGE_COMBINE, 1, s));
+  }
+
+  if (want_stats) {
+    StatsArgs sa{};
+    sa.counts = cnt; sa.probs = probs; sa.partial = at<float>(ws, L.partial);
+    sa.T = T; sa.E = E; sa.k = cfg->top_k; sa.capacity = d.capacity; sa.alpha = alpha;
+    if (stats) { sa.f = stats; sa.P = stats + E; sa.aux_loss = stats + 2 * E; sa.imbalance = stats + 2 * E + 1; }
+    sa.dropped = dropped;
+    MOE_TRY(mark(ev, MOE_STAGE_LOAD_STATS, 0, s));
+    MOE_TRY_HIP("load stats", launch_load_stats(sa, s));
+    MOE_TRY(mark(ev, MOE_STAGE_LOAD_STATS, 1, s));
+  }
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,148 @@
+// Internal helpers shared by the HIP sources of the MoE layer library.
+// Not part of the C ABI (see include/moe.h for that).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace moe {
+
+constexpr int kWave = 64;          // CDNA wavefront width
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 32;
+constexpr int kNumXcd = 8;         // MI355X: 8 accelerator complex dies, one L2 each
+
+enum Dtype { F32 = 0, BF16 = 1 };
+enum Scoring { SOFTMAX_TOPK = 0, TOPK_SOFTMAX = 1, SIGMOID_BIAS = 2 };
+enum Activation { SWIGLU = 0, GELU = 1 };
+
+typedef uint16_t bf16_t;   // bfloat16 bit pattern
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
+
+__host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+__host__ __device__ inline size_t round_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float32 -> bfloat16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float to_f32(T v);
+template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f32<bf16_t>(bf16_t v) { return bf16_to_f32(v); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return f32_to_bf16(v); }
+
+// Workgroups are dealt to the XCDs round-robin (workgroup i runs on XCD i % 8).
+// Renumber them so that each XCD works on one contiguous range of logical
+// tiles, which then share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  const int xcd = bid % kNumXcd;
+  const int local = bid / kNumXcd;
+  const int per = nblocks / kNumXcd;
+  const int rem = nblocks % kNumXcd;
+  return xcd * per + (xcd < rem ? xcd : rem) + local;
+}
+
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+__device__ __forceinline__ float gelu_erf_f32(float z) {
+  return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
+}
+
+// ---------------------------------------------------------------------------
+// Launchers implemented in the .hip files (all enqueue on `stream`).
+// ---------------------------------------------------------------------------
+
+// Epilogue kinds of the grouped GEMM C[r, n] = sum_k A[r, k] * B_g[n, k].
+enum Epilogue {
+  EPI_STORE_F32 = 0,   // C float32
+  EPI_STORE_ACT = 1,   // C in the activation type
+  EPI_SWIGLU = 2,      // B rows n and F+n are gate and up: H = silu(g) * u
+  EPI_GELU = 3,        // H = gelu(C)
+};
+
+struct GroupedGemm {
+  const void* A;              // rows of K elements (act type)
+  const int32_t* a_rows;      // [M_max] gather map or nullptr
+  int lda;
+  const void* B;              // [G][rows_b][K]
+  long long b_group_stride;   // elements
+  void* C;                    // [M_max][ldc]
+  int ldc;
+  int M_max, N, K;            // N = output columns (SwiGLU: F)
+  int G;
+  const int32_t* offsets;     // [G+1] or nullptr (one group of M_max rows)
+  const int32_t* tile_prefix; // [G+1] m-tile prefix for the kernel's BM (grouped case)
+  int epilogue;
+};
+
+// m-tile prefix for grouped GEMMs: prefix[g] = sum_{h<g} ceil((off[h+1]-off[h]) / bm).
+hipError_t launch_tile_prefix(const int32_t* offsets, int G, int bm, int32_t* prefix, hipStream_t s);
+
+// bf16 MFMA grouped GEMM; returns the BM its tiles use via bm_out when non-null.
+hipError_t launch_gemm_bf16(const GroupedGemm& g, hipStream_t s);
+int gemm_bf16_bm(const GroupedGemm& g);
+// float32 SIMT grouped GEMM.  a_dtype / b_dtype select float32 or bf16 operands.
+hipError_t launch_gemm_f32(const GroupedGemm& g, int a_dtype, int b_dtype, hipStream_t s);
+constexpr int kF32GemmBM = 64;
+
+struct RouteArgs {
+  const float* logits;        // [T, E]
+  const void* x;              // [T, D] act type (near-tie refinement)
+  const void* w_router;       // [E, D] router type
+  const float* sel_bias;      // [E] or nullptr
+  int32_t* topk_idx;          // [T, k]
+  float* topk_w;              // [T, k]
+  float* probs;               // [T, E] or nullptr
+  int T, D, E, k;
+  int scoring, renormalize, act_dtype, router_dtype;
+};
+hipError_t launch_route_select(const RouteArgs& a, hipStream_t s);
+
+struct PermuteArgs {
+  const int32_t* topk_idx;    // [T, k]
+  int T, k, E;
+  int capacity;               // INT32_MAX when dropless
+  int rows_cap;               // A_cap
+  int32_t* tile_counts;       // ws [ntiles][E]
+  int32_t* counts;            // [E]
+  int32_t* offsets;           // [E+1]
+  int32_t* row_of;            // [T, k]
+  int32_t* token_of_row;      // [A_cap]
+  int32_t* tile_prefix;       // [E+1] m-tile prefix for bm (or nullptr)
+  int bm;
+};
+constexpr int kPermuteTile = 256;   // tokens per histogram / scatter block
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
+hipError_t launch_gather_rows(const void* x, const int32_t* token_of_row, const int32_t* offsets,
+                              int E, int rows_cap, int D, int elem_bytes, void* x_perm,
+                              hipStream_t s);
+
+hipError_t launch_combine(const void* y_perm, const int32_t* row_of, const float* topk_w,
+                          const void* y_shared, void* y, int T, int k, int D, int act_dtype,
+                          hipStream_t s);
+
+struct StatsArgs {
+  const int32_t* counts;      // [E]
+  const float* probs;         // [T, E]
+  float* partial;             // ws [nchunks][E]
+  int T, E, k, capacity;
+  float alpha;
+  float* f; float* P; float* aux_loss; float* imbalance; int32_t* dropped;
+};
+constexpr int kStatsChunk = 256;    // tokens per partial-sum block
+hipError_t launch_load_stats(const StatsArgs& a, hipStream_t s);
+
+}  // namespace moe

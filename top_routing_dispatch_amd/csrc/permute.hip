@@ -1,0 +1,314 @@
+// Dispatch (permute), combine (unpermute) and load statistics.
+//
+// Dispatch groups the (token, slot) assignments by expert the way the
+// Tiny-MoE walk-through's torch.where does ("从 Dense FFN 到 MoE" §5): experts
+// in ascending id, and inside one expert the assignments in row-major
+// (token, slot) order.  With a capacity C ("Top-k 路由" 容量因子 section) an
+// expert keeps its first C assignments in that order; the rest are dropped
+// and the residual path carries them ("别只比较 Top-k" mechanism table).
+//
+// Three small kernels, all deterministic (integer atomics only, whose result
+// does not depend on their order):
+//   histogram  per 256-token tile, per expert: a bit mask of the tile's tokens
+//              that chose the expert (LDS atomicOr), popcounted;
+//   scan       per expert over tiles -> tile bases and nominal counts; kept =
+//              min(count, C); exclusive scan over experts -> offsets; m-tile
+//              prefix for the grouped GEMM; unused row slots set to -1;
+//   scatter    rank of a token inside its tile = popcount of the expert's mask
+//              below it; row = offsets[e] + tile base + rank, kept if the
+//              expert-local rank is below C.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kWordsPerTile = kPermuteTile / 32;
+
+// Build the per-expert token masks of one tile.  Returns, for the calling
+// thread's token, a bit per slot that is set for slots to skip (expert id
+// out of range, or an id already used by an earlier slot of the same token).
+__device__ uint32_t build_masks(const PermuteArgs& a, uint32_t* mask) {
+  const int tid = threadIdx.x;
+  for (int w = tid; w < a.E * kWordsPerTile; w += blockDim.x) mask[w] = 0u;
+  __syncthreads();
+  const int t = blockIdx.x * kPermuteTile + tid;
+  uint32_t skip = 0u;
+  if (t < a.T) {
+    const uint32_t bit = 1u << (tid & 31);
+    const int word = tid >> 5;
+    for (int j = 0; j < a.k; ++j) {
+      const int e = a.topk_idx[(long long)t * a.k + j];
+      if ((unsigned)e >= (unsigned)a.E) { skip |= 1u << j; continue; }
+      const uint32_t old = atomicOr(&mask[e * kWordsPerTile + word], bit);
+      if (old & bit) skip |= 1u << j;
+    }
+  }
+  __syncthreads();
+  return skip;
+}
+
+__global__ __launch_bounds__(kPermuteTile) void hist_kernel(const PermuteArgs a) {
+  __shared__ uint32_t mask[kMaxExperts * kWordsPerTile];
+  build_masks(a, mask);
+  for (int e = threadIdx.x; e < a.E; e += blockDim.x) {
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < kWordsPerTile; ++w) c += __popc(mask[e * kWordsPerTile + w]);
+    a.tile_counts[(long long)blockIdx.x * a.E + e] = c;
+  }
+}
+
+__device__ int block_exclusive_scan(int v, int* s) {
+  const int i = threadIdx.x;
+  s[i] = v;
+  __syncthreads();
+  for (int d = 1; d < (int)blockDim.x; d <<= 1) {
+    const int u = (i >= d) ? s[i - d] : 0;
+    __syncthreads();
+    s[i] += u;
+    __syncthreads();
+  }
+  const int incl = s[i];
+  __syncthreads();
+  return incl - v;
+}
+
+__global__ __launch_bounds__(kMaxExperts) void scan_kernel(const PermuteArgs a, int ntiles) {
+  __shared__ int s[kMaxExperts];
+  __shared__ int s_total;
+  const int e = threadIdx.x;
+  int total = 0;
+  if (e < a.E) {
+    for (int tl = 0; tl < ntiles; ++tl) {
+      int* p = a.tile_counts + (long long)tl * a.E + e;
+      const int c = *p;
+      *p = total;                 // becomes the tile's base rank inside expert e
+      total += c;
+    }
+    a.counts[e] = total;
+  }
+  const int kept = (e < a.E) ? min(total, a.capacity) : 0;
+  const int off = block_exclusive_scan(kept, s);
+  if (e < a.E) a.offsets[e] = off;
+  if (e == a.E - 1) { a.offsets[a.E] = off + kept; s_total = off + kept; }
+  if (a.tile_prefix != nullptr) {
+    const int mt = (e < a.E) ? ceil_div(kept, a.bm) : 0;
+    const int mo = block_exclusive_scan(mt, s);
+    if (e < a.E) a.tile_prefix[e] = mo;
+    if (e == a.E - 1) a.tile_prefix[a.E] = mo + mt;
+  }
+  __syncthreads();
+  for (int r = s_total + e; r < a.rows_cap; r += blockDim.x) a.token_of_row[r] = -1;
+}
+
+__global__ __launch_bounds__(kPermuteTile) void scatter_kernel(const PermuteArgs a) {
+  __shared__ uint32_t mask[kMaxExperts * kWordsPerTile];
+  const uint32_t skip = build_masks(a, mask);
+  const int tid = threadIdx.x;
+  const int t = blockIdx.x * kPermuteTile + tid;
+  if (t >= a.T) return;
+  const int word = tid >> 5;
+  const uint32_t below = (1u << (tid & 31)) - 1u;
+  for (int j = 0; j < a.k; ++j) {
+    int row = -1;
+    if (!((skip >> j) & 1u)) {
+      const int e = a.topk_idx[(long long)t * a.k + j];
+      const uint32_t* m = mask + e * kWordsPerTile;
+      int rank = __popc(m[word] & below);
+      for (int w = 0; w < word; ++w) rank += __popc(m[w]);
+      const int r_in_e = a.tile_counts[(long long)blockIdx.x * a.E + e] + rank;
+      const int base = a.offsets[e];
+      if (r_in_e < a.offsets[e + 1] - base) {
+        row = base + r_in_e;
+        a.token_of_row[row] = t;
+      }
+    }
+    a.row_of[(long long)t * a.k + j] = row;
+  }
+}
+
+// x_perm[r] = x[token_of_row[r]] for rows with a token; 16-byte chunks.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restrict__ x,
+                                                          const int32_t* __restrict__ tor,
+                                                          uint4* __restrict__ xp, int chunks) {
+  const int r = blockIdx.x;
+  const int tok = tor[r];
+  if (tok < 0) return;
+  const uint4* src = x + (long long)tok * chunks;
+  uint4* dst = xp + (long long)r * chunks;
+  for (int c = threadIdx.x; c < chunks; c += blockDim.x) dst[c] = src[c];
+}
+
+// ---------------------------------------------------------------------------
+// combine: y[t] = sum_j w[t,j] * y_perm[row_of[t,j]] (+ y_shared[t])
+// ---------------------------------------------------------------------------
+template <typename T>
+struct Chunk;
+template <> struct Chunk<float> {
+  static constexpr int N = 4;
+  static __device__ __forceinline__ void load(const float* p, float v[4]) {
+    const float4 q = *reinterpret_cast<const float4*>(p);
+    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+  }
+  static __device__ __forceinline__ void store(float* p, const float v[4]) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+};
+template <> struct Chunk<bf16_t> {
+  static constexpr int N = 8;
+  static __device__ __forceinline__ void load(const bf16_t* p, float v[8]) {
+    const uint4 q = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  static __device__ __forceinline__ void store(bf16_t* p, const float v[8]) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = (uint32_t)f32_to_bf16(v[2 * i]) | ((uint32_t)f32_to_bf16(v[2 * i + 1]) << 16);
+    *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ yp, const int32_t* __restrict__ row_of,
+                                                      const float* __restrict__ tw, const T* ys, T* y,
+                                                      int k, int D) {
+  constexpr int N = Chunk<T>::N;
+  const int t = blockIdx.x;
+  const int chunks = D / N;
+  for (int c = threadIdx.x; c < chunks; c += blockDim.x) {
+    float acc[N];
+#pragma unroll
+    for (int q = 0; q < N; ++q) acc[q] = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      const int row = row_of[(long long)t * k + j];
+      if (row < 0) continue;
+      const float w = tw[(long long)t * k + j];
+      float v[N];
+      Chunk<T>::load(yp + (long long)row * D + c * N, v);
+#pragma unroll
+      for (int q = 0; q < N; ++q) acc[q] = fmaf(w, v[q], acc[q]);
+    }
+    if (ys != nullptr) {
+      float v[N];
+      Chunk<T>::load(ys + (long long)t * D + c * N, v);
+#pragma unroll
+      for (int q = 0; q < N; ++q) acc[q] += v[q];
+    }
+    Chunk<T>::store(y + (long long)t * D + c * N, acc);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// load statistics
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void stats_partial_kernel(const StatsArgs a) {
+  const int t0 = blockIdx.x * kStatsChunk;
+  const int t1 = min(a.T, t0 + kStatsChunk);
+  for (int e = threadIdx.x; e < a.E; e += blockDim.x) {
+    float s = 0.0f;
+    for (int t = t0; t < t1; ++t) s += a.probs[(long long)t * a.E + e];
+    a.partial[(long long)blockIdx.x * a.E + e] = s;
+  }
+}
+
+__global__ __launch_bounds__(kMaxExperts) void stats_final_kernel(const StatsArgs a, int nchunks) {
+  __shared__ float sf[kMaxExperts];
+  __shared__ int si[kMaxExperts];
+  __shared__ int sd[kMaxExperts];
+  const int e = threadIdx.x;
+  const float A = (float)a.T * (float)a.k;
+  float fe = 0.0f, pe = 0.0f;
+  int c = 0, drop = 0;
+  if (e < a.E) {
+    c = a.counts[e];
+    float s = 0.0f;
+    for (int b = 0; b < nchunks; ++b) s += a.partial[(long long)b * a.E + e];
+    pe = a.T > 0 ? s / (float)a.T : 0.0f;
+    fe = a.T > 0 ? (float)c / A : 0.0f;
+    drop = c - min(c, a.capacity);
+    if (a.f) a.f[e] = fe;
+    if (a.P) a.P[e] = pe;
+  }
+  sf[e] = fe * pe;
+  si[e] = c;
+  sd[e] = drop;
+  __syncthreads();
+  for (int d = kMaxExperts / 2; d >= 1; d >>= 1) {
+    if (e < d) {
+      sf[e] += sf[e + d];
+      si[e] = max(si[e], si[e + d]);
+      sd[e] += sd[e + d];
+    }
+    __syncthreads();
+  }
+  if (e == 0) {
+    if (a.aux_loss) *a.aux_loss = a.alpha * (float)a.E * sf[0];
+    if (a.imbalance) *a.imbalance = a.T > 0 ? (float)si[0] / (A / (float)a.E) : 0.0f;
+    if (a.dropped) *a.dropped = sd[0];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
+  const int ntiles = ceil_div(a.T, kPermuteTile);
+  if (ntiles > 0) {
+    hipLaunchKernelGGL(hist_kernel, dim3(ntiles), dim3(kPermuteTile), 0, s, a);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kMaxExperts), 0, s, a, ntiles);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || ntiles == 0) return err;
+  hipLaunchKernelGGL(scatter_kernel, dim3(ntiles), dim3(kPermuteTile), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const void* x, const int32_t* token_of_row, const int32_t*, int,
+                              int rows_cap, int D, int elem_bytes, void* x_perm, hipStream_t s) {
+  if (rows_cap == 0) return hipSuccess;
+  const int chunks = D * elem_bytes / 16;
+  const int threads = chunks >= 256 ? 256 : ((chunks + 63) / 64) * 64;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(rows_cap), dim3(threads), 0, s,
+                     static_cast<const uint4*>(x), token_of_row, static_cast<uint4*>(x_perm), chunks);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const void* y_perm, const int32_t* row_of, const float* topk_w,
+                          const void* y_shared, void* y, int T, int k, int D, int act_dtype,
+                          hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (act_dtype == BF16) {
+    const int chunks = D / 8;
+    const int threads = chunks >= 256 ? 256 : ((chunks + 63) / 64) * 64;
+    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(T), dim3(threads), 0, s,
+                       static_cast<const bf16_t*>(y_perm), row_of, topk_w,
+                       static_cast<const bf16_t*>(y_shared), static_cast<bf16_t*>(y), k, D);
+  } else {
+    const int chunks = D / 4;
+    const int threads = chunks >= 256 ? 256 : ((chunks + 63) / 64) * 64;
+    hipLaunchKernelGGL(combine_kernel<float>, dim3(T), dim3(threads), 0, s,
+                       static_cast<const float*>(y_perm), row_of, topk_w,
+                       static_cast<const float*>(y_shared), static_cast<float*>(y), k, D);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_load_stats(const StatsArgs& a, hipStream_t s) {
+  const int nchunks = ceil_div(a.T, kStatsChunk);
+  if (nchunks > 0) {
+    hipLaunchKernelGGL(stats_partial_kernel, dim3(nchunks), dim3(256), 0, s, a);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(stats_final_kernel, dim3(1), dim3(kMaxExperts), 0, s, a, nchunks);
+  return hipGetLastError();
+}
+
+}  // namespace moe
