@@ -29,7 +29,7 @@ HBM_GBPS = 8000.0
 MFMA_BF16_TFLOPS = 2500.0
 VALU_F32_TFLOPS = 78.6       # FMA without packed-FP32 instructions: 256 CU x 64 lanes x 2 x 2.4 GHz
 
-DEFAULT_CPU_SAMPLE = {"tiny": 64, "switch": 1024, "mixtral": 64, "deepseekmoe": 256, "deepseekv3": 32}
+DEFAULT_CPU_SAMPLE = {"tiny": 64, "switch": 8192, "mixtral": 256, "deepseekmoe": 1024, "deepseekv3": 64}
 
 
 def log(msg):
@@ -126,7 +126,8 @@ def main():
     t_setup = time.perf_counter()
     inp = W.make_inputs(cfg, with_experts=False)
     x = to_torch(inp.x, dev)
-    w13, w2, host = upload_experts(cfg, dev, keep_host=not args.no_cpu_baseline)
+    w13, w2, host = upload_experts(cfg, dev, keep_host=not args.no_cpu_baseline,
+                                   progress=lambda n: log(f"[bench] generated {n}/{cfg.num_experts} experts"))
     if host is not None:
         inp.w13 = _Stack(host, 0)
         inp.w2 = _Stack(host, 1)

@@ -1,0 +1,125 @@
+"""Full-size parity at the benchmark workloads (Switch, Mixtral, DeepSeekMoE,
+DeepSeek-V3 shapes), in the launch configuration bench.py times
+(moe_layer_forward on the whole batch):
+
+  * expert selection of every token against the float64 oracle (near-tie
+    exemption only), counts, and the full permutation of the oracle's own
+    selection, bit-exact;
+  * the float32 router logits the selection starts from, against float64:
+    the error must sit far inside the margin that triggers the float64
+    near-tie refinement;
+  * layer outputs on a seeded sample of tokens, each computed by the oracle
+    expert by expert (only the experts the sample uses are widened).
+"""
+import numpy as np
+import pytest
+import torch
+
+import top_routing_dispatch_amd as M
+import workloads as W
+from oracle import moe_oracle as O
+from workloads.torch_io import act_torch_dtype, to_numpy, to_torch, upload_experts
+
+from parity import W_TOL, out_tol, rel_err, route_differences, row_rel_err
+
+pytestmark = pytest.mark.gpu
+
+SAMPLE = {"switch": 32, "mixtral": 12, "deepseekmoe": 24, "deepseekv3": 8}
+
+
+def refinement_margin(s32: np.ndarray) -> np.ndarray:
+    """Per-token logit margin the route kernel trusts float32 within."""
+    return np.ldexp(1.0 + np.abs(s32).max(axis=1), -16)
+
+
+@pytest.mark.parametrize("name", ["switch", "mixtral", "deepseekmoe", "deepseekv3"])
+def test_full_size_layer(name):
+    cfg = W.CONFIGS[name]
+    T, E, k, D = cfg.num_tokens, cfg.num_experts, cfg.top_k, cfg.d_model
+    print(f"[full-size parity] {name}", flush=True)
+    dev = "cuda"
+    inp = W.make_inputs(cfg, with_experts=False)
+    w13, w2, host = upload_experts(cfg, dev, keep_host=True)
+    weights = dict(w_router=to_torch(inp.w_router, dev), sel_bias=to_torch(inp.sel_bias, dev), w13=w13, w2=w2,
+                   ws13=to_torch(inp.ws13, dev), ws2=to_torch(inp.ws2, dev))
+    x = to_torch(inp.x, dev)
+
+    # --- the benchmark's call
+    y = torch.empty((T, D), dtype=act_torch_dtype(cfg), device=dev)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    tw = torch.empty((T, k), dtype=torch.float32, device=dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    stats = torch.empty(2 * E + 2, dtype=torch.float32, device=dev)
+    dropped = torch.empty(1, dtype=torch.int32, device=dev)
+    ws = M.workspace(cfg, M.MOE_OP_LAYER, dev)
+    M.moe_layer_forward(cfg, weights, x, y, idx, tw, counts, cfg.alpha, stats, dropped, ws)
+    # float32 logits as the route kernel sees them
+    wsr = M.workspace(cfg, M.MOE_OP_ROUTE, dev)
+    idx2 = torch.empty_like(idx)
+    tw2 = torch.empty_like(tw)
+    M.moe_route(cfg, x, weights["w_router"], weights["sel_bias"], idx2, tw2, None, wsr)
+    torch.cuda.synchronize()
+    s32 = wsr[: T * E * 4].view(torch.float32).reshape(T, E).cpu().numpy().astype(np.float64)
+
+    # --- oracle routing of every token (float64)
+    ref = O.route(inp.x, inp.w_router, inp.sel_bias, k, cfg.scoring, cfg.renormalize)
+    err_s = np.abs(s32 - ref["logits"]).max(axis=1)
+    margin = refinement_margin(s32)
+    print(f"  float32 logit error max {err_s.max():.3e}; smallest margin/error {np.min(margin / np.maximum(err_s, 1e-30)):.1f}")
+    assert (err_s * 16 < margin).all(), "float32 logits too far from exact for the refinement margin"
+
+    gi, gw = to_numpy(idx), to_numpy(tw)
+    np.testing.assert_array_equal(gi, to_numpy(idx2))
+    diff = route_differences(cfg, ref, gi, inp.sel_bias)
+    same = np.setdiff1d(np.arange(T), diff)
+    assert rel_err(gw[same], ref["w"][same]) <= W_TOL
+    print(f"  near-tie tokens {len(diff)}")
+
+    cap = O.capacity(cfg.capacity_factor, T, k, E)
+    disp = O.dispatch(ref["idx"], E, cap)
+    ref_counts = disp["counts"].copy()
+    for t in diff:
+        np.subtract.at(ref_counts, ref["idx"][t], 1)
+        np.add.at(ref_counts, gi[t], 1)
+    np.testing.assert_array_equal(to_numpy(counts), ref_counts)
+    if len(diff) == 0:
+        st = O.load_stats(disp["counts"], ref["probs"], k, cfg.alpha, disp["kept"])
+        g = to_numpy(stats)
+        assert rel_err(g[:E], st["f"]) <= W_TOL and rel_err(g[E:2 * E], st["P"]) <= W_TOL
+        assert int(to_numpy(dropped)[0]) == st["dropped"]
+
+    # --- permutation of the oracle's selection, bit-exact at full size
+    cap_c, rows_cap = M.moe_capacity(cfg)
+    c2 = torch.empty(E, dtype=torch.int32, device=dev)
+    off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    row_of = torch.empty((T, k), dtype=torch.int32, device=dev)
+    tor = torch.empty(rows_cap, dtype=torch.int32, device=dev)
+    M.moe_permute(cfg, to_torch(ref["idx"].astype(np.int32), dev), None, c2, off, row_of, tor, None,
+                  M.workspace(cfg, M.MOE_OP_PERMUTE, dev))
+    torch.cuda.synchronize()
+    A = int(disp["offsets"][-1])
+    np.testing.assert_array_equal(to_numpy(off), disp["offsets"])
+    np.testing.assert_array_equal(to_numpy(row_of), disp["row_of"])
+    np.testing.assert_array_equal(to_numpy(tor)[:A], disp["token_of_row"])
+
+    # --- sampled outputs, oracle expert by expert
+    rng = np.random.default_rng(1234)
+    cand = same if cfg.capacity_factor <= 0 or len(diff) == 0 else np.array([], dtype=np.int64)
+    sample = np.sort(rng.choice(cand, size=min(SAMPLE[name], len(cand)), replace=False))
+    X = O.widen(inp.x[sample])
+    y_ref = np.zeros((len(sample), D))
+    users = {}
+    for i, t in enumerate(sample):
+        for j in range(k):
+            if disp["row_of"][t, j] >= 0:
+                users.setdefault(int(ref["idx"][t, j]), []).append((i, j))
+    for e, lst in users.items():
+        rows = [i for i, _ in lst]
+        out = O.expert_apply(X[rows], host[e][0], host[e][1], cfg.activation, cfg.d_ff)
+        for (i, j), o in zip(lst, out):
+            y_ref[i] += ref["w"][sample[i], j] * o
+    if cfg.num_shared:
+        y_ref += O.shared_experts(inp.x[sample], inp.shared)
+    err = row_rel_err(to_numpy(y)[sample], y_ref)
+    print(f"  sampled {len(sample)} tokens over {len(users)} experts: max rel err {err:.3e}")
+    assert err <= out_tol(cfg)

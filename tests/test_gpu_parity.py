@@ -114,7 +114,7 @@ def test_permute_worked_example_and_capacity():
     counts, offsets, row_of, tor, _ = _permute_gpu(cfg2, idx, None)
     assert offsets.tolist() == [0, 2, 4, 6, 7]
     assert row_of.tolist() == [[4, 0], [2, 5], [6, 1], [-1, 3]]
-    assert tor.tolist() == [0, 2, 1, 3, 0, 1, 2]
+    assert tor.tolist() == [0, 2, 1, 3, 0, 1, 2, -1]      # A_cap = min(T*k, E*C) = 8 rows, 7 kept
 
 
 def test_permute_every_token_on_one_expert_with_capacity():
@@ -125,7 +125,7 @@ def test_permute_every_token_on_one_expert_with_capacity():
     counts, offsets, row_of, tor, _ = _permute_gpu(cfg, idx, None)
     assert counts.tolist() == [0] * 5 + [T] + [0] * 2
     assert offsets[-1] == C
-    assert tor.tolist() == list(range(C))
+    assert tor.tolist() == list(range(C)) + [-1] * (T - C)
     assert (row_of[:C, 0] == np.arange(C)).all() and (row_of[C:, 0] == -1).all()
 
 
@@ -297,3 +297,26 @@ def test_near_tie_refinement_decides_in_double_precision():
     # yet the refinement orders them like the float64 oracle
     np.testing.assert_array_equal(got["idx"], ref["idx"])
     assert len(diff) == 0
+
+
+V2_SHAPES = [
+    W.MoEConfig("v2_swiglu_shared", 700, 256, 8, 2, 320, num_shared=1, d_ff_shared=128),
+    W.MoEConfig("v2_gelu_capacity", 900, 192, 16, 1, 384, scoring=W.SOFTMAX_TOPK, renormalize=0,
+                activation=W.GELU, router_dtype=W.F32, capacity_factor=1.25),
+    W.MoEConfig("v2_sigmoid_many", 333, 128, 64, 6, 128, num_shared=2, d_ff_shared=64, scoring=W.SIGMOID_BIAS,
+                zipf_s=1.2),
+]
+
+
+@pytest.mark.parametrize("gemm_cfg", [str(c) for c in range(-1, 10)])
+@pytest.mark.parametrize("cfg", V2_SHAPES, ids=lambda c: c.name)
+def test_every_gemm_tile_config(cfg, gemm_cfg, monkeypatch):
+    """Each tile configuration of the pipelined expert GEMM (K a multiple of 64)
+    against the oracle, through the whole layer; -1 is the general kernel."""
+    monkeypatch.setenv("MOE_GEMM_CFG", gemm_cfg)
+    print(f"[tile config {gemm_cfg}] {cfg.name}", flush=True)
+    inp = W.make_inputs(cfg)
+    ref = oracle_forward(cfg, inp)
+    got = DeviceLayer(cfg, inp).layer()
+    diff, err = check_layer(cfg, inp, ref, got)
+    print(f"  max rel err {err:.3e}")

@@ -3,6 +3,7 @@
 // every function are in include/moe.h.
 #include <math.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "common.h"
@@ -88,15 +89,15 @@ size_t ws_permute(const moe_config* c) {
   return carve((size_t)ceil_div(c->num_tokens, kPermuteTile) * c->num_experts * 4);
 }
 size_t ws_ffn(const moe_config*, int G, int F, int max_rows, int act) {
-  return carve((size_t)max_rows * F * esize(act)) + carve((size_t)(G + 1) * 4);
+  return carve((size_t)max_rows * F * esize(act)) + 2 * carve((size_t)(G + 1) * 4);
 }
 size_t ws_stats(const moe_config* c) {
   return carve((size_t)ceil_div(c->num_tokens, kStatsChunk) * c->num_experts * 4);
 }
 
 struct Layout {
-  size_t logits, probs, idx, w, tile_counts, counts, offsets, tile_prefix, row_of, tor, h, yperm,
-      partial, total;
+  size_t logits, probs, idx, w, tile_counts, counts, offsets, tile_prefix, tile_prefix2, row_of, tor, h,
+      yperm, partial, total;
 };
 
 Layout layer_layout(const moe_config* c, const Derived& d) {
@@ -113,6 +114,7 @@ Layout layer_layout(const moe_config* c, const Derived& d) {
   L.counts = take(E * 4);
   L.offsets = take((E + 1) * 4);
   L.tile_prefix = take((E + 1) * 4);
+  L.tile_prefix2 = take((E + 1) * 4);
   L.row_of = take(T * k * 4);
   L.tor = take((size_t)d.rows_cap * 4);
   const size_t h_routed = (size_t)d.rows_cap * c->d_ff * es;
@@ -155,12 +157,6 @@ moe_status run_select(const moe_config* c, const float* logits, const void* x, c
   return MOE_OK;
 }
 
-int ffn_bm(int act) {
-  GroupedGemm dummy{};
-  return act == BF16 ? gemm_bf16_bm(dummy) : kF32GemmBM;
-}
-
-// gate/up (+activation) then down projection for G groups.
 // Records stage event `which` (0 = start, 1 = stop) when timing is requested.
 moe_status mark(void* const* ev, int stage, int which, hipStream_t s) {
   if (ev == nullptr || ev[2 * stage + which] == nullptr) return MOE_OK;
@@ -168,32 +164,85 @@ moe_status mark(void* const* ev, int stage, int which, hipStream_t s) {
   return MOE_OK;
 }
 
+// Kernel choice for one projection: -1 = the general kernels (any K), else a
+// tile configuration of the pipelined bf16 kernel (K a multiple of 64).  The
+// tile height follows the average rows per group; MOE_GEMM_CFG=<n> overrides
+// the choice (tuning aid; -1 forces the general kernels).
+int pick_cfg(int act, int K, int max_rows, int G) {
+  if (act != BF16 || K % 64 != 0) return -1;
+  const char* env = getenv("MOE_GEMM_CFG");
+  if (env != nullptr && *env != '\0') {
+    const int c = atoi(env);
+    return (c >= -1 && c < kGemmV2Configs) ? c : -1;
+  }
+  // measured on MI355X at the Switch / Mixtral / DeepSeekMoE / DeepSeek-V3
+  // shapes: 256x256 tiles on 8 waves once groups are a few hundred rows deep,
+  // 128x128 tiles with two workgroups per CU for shallow (weight-streaming)
+  // groups
+  const int avg = G > 0 ? max_rows / G : max_rows;
+  return avg >= 160 ? 4 : 7;
+}
+
+int cfg_bm(int act, int cfg) {
+  if (act != BF16) return kF32GemmBM;
+  if (cfg < 0) {
+    GroupedGemm dummy{};
+    return gemm_bf16_bm(dummy);
+  }
+  return gemm_v2_bm(cfg);
+}
+
+struct FfnPlan {
+  int cfg_up, cfg_dn, bm_up, bm_dn;
+};
+
+FfnPlan plan_ffn(int act, int D, int F, int max_rows, int G) {
+  FfnPlan pl;
+  pl.cfg_up = pick_cfg(act, D, max_rows, G);
+  pl.cfg_dn = pick_cfg(act, F, max_rows, G);
+  pl.bm_up = cfg_bm(act, pl.cfg_up);
+  pl.bm_dn = cfg_bm(act, pl.cfg_dn);
+  return pl;
+}
+
+hipError_t launch_gemm(int act, int cfg, const GroupedGemm& g, hipStream_t s) {
+  if (act != BF16) return launch_gemm_f32(g, F32, F32, s);
+  if (cfg >= 0) return launch_gemm_v2(g, cfg, s);
+  return launch_gemm_bf16(g, s);
+}
+
+// gate/up (+activation) then down projection for G groups.  prefix_up holds
+// the m-tile prefix for plan.bm_up (computed by the caller when offsets are
+// given); prefix_dn is filled here when the down projection tiles differently.
 moe_status run_ffn(int act, int activation, int G, int D, int F, int max_rows, const void* x_in,
-                   const int32_t* gather, const int32_t* offsets, const int32_t* tile_prefix,
-                   const void* w13, const void* w2, void* h, void* y_out, hipStream_t s,
+                   const int32_t* gather, const int32_t* offsets, const int32_t* prefix_up,
+                   int32_t* prefix_dn, const void* w13, const void* w2, void* h, void* y_out, hipStream_t s,
                    void* const* ev = nullptr, int stage_up = 0, int stage_down = 0) {
+  const FfnPlan pl = plan_ffn(act, D, F, max_rows, G);
   const int n_mat = activation == SWIGLU ? 2 : 1;
   GroupedGemm g1{};
   g1.A = x_in; g1.a_rows = gather; g1.lda = D;
   g1.B = w13; g1.b_group_stride = (long long)n_mat * F * D;
   g1.C = h; g1.ldc = F;
   g1.M_max = max_rows; g1.N = F; g1.K = D;
-  g1.G = G; g1.offsets = offsets; g1.tile_prefix = tile_prefix;
+  g1.G = G; g1.offsets = offsets; g1.tile_prefix = prefix_up;
   g1.epilogue = activation == SWIGLU ? EPI_SWIGLU : EPI_GELU;
   GroupedGemm g2{};
   g2.A = h; g2.a_rows = nullptr; g2.lda = F;
   g2.B = w2; g2.b_group_stride = (long long)D * F;
   g2.C = y_out; g2.ldc = D;
   g2.M_max = max_rows; g2.N = D; g2.K = F;
-  g2.G = G; g2.offsets = offsets; g2.tile_prefix = tile_prefix;
+  g2.G = G; g2.offsets = offsets; g2.tile_prefix = prefix_up;
   g2.epilogue = EPI_STORE_ACT;
   MOE_TRY(mark(ev, stage_up, 0, s));
-  if (act == BF16) MOE_TRY_HIP("expert gate/up", launch_gemm_bf16(g1, s));
-  else MOE_TRY_HIP("expert gate/up", launch_gemm_f32(g1, F32, F32, s));
+  MOE_TRY_HIP("expert gate/up", launch_gemm(act, pl.cfg_up, g1, s));
   MOE_TRY(mark(ev, stage_up, 1, s));
   MOE_TRY(mark(ev, stage_down, 0, s));
-  if (act == BF16) MOE_TRY_HIP("expert down", launch_gemm_bf16(g2, s));
-  else MOE_TRY_HIP("expert down", launch_gemm_f32(g2, F32, F32, s));
+  if (offsets != nullptr && pl.bm_dn != pl.bm_up) {
+    MOE_TRY_HIP("tile prefix", launch_tile_prefix(offsets, G, pl.bm_dn, prefix_dn, s));
+    g2.tile_prefix = prefix_dn;
+  }
+  MOE_TRY_HIP("expert down", launch_gemm(act, pl.cfg_dn, g2, s));
   MOE_TRY(mark(ev, stage_down, 1, s));
   return MOE_OK;
 }
@@ -311,13 +360,17 @@ moe_status moe_expert_ffn(const moe_config* cfg, int32_t num_groups, int32_t d_f
   if (max_rows == 0) return MOE_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   void* h = ws;
-  int32_t* tile_prefix = nullptr;
+  int32_t* prefix_up = nullptr;
+  int32_t* prefix_dn = nullptr;
   if (offsets != nullptr) {
-    tile_prefix = at<int32_t>(ws, carve((size_t)max_rows * d_ff * esize(cfg->act_dtype)));
-    MOE_TRY_HIP("tile prefix", launch_tile_prefix(offsets, num_groups, ffn_bm(cfg->act_dtype), tile_prefix, s));
+    const size_t hb = carve((size_t)max_rows * d_ff * esize(cfg->act_dtype));
+    prefix_up = at<int32_t>(ws, hb);
+    prefix_dn = at<int32_t>(ws, hb + carve((size_t)(num_groups + 1) * 4));
+    const FfnPlan pl = plan_ffn(cfg->act_dtype, cfg->d_model, d_ff, max_rows, num_groups);
+    MOE_TRY_HIP("tile prefix", launch_tile_prefix(offsets, num_groups, pl.bm_up, prefix_up, s));
   }
   return run_ffn(cfg->act_dtype, activation, num_groups, cfg->d_model, d_ff, max_rows, x_in, gather_rows,
-                 offsets, tile_prefix, w13, w2, h, y_out, s);
+                 offsets, prefix_up, prefix_dn, w13, w2, h, y_out, s);
 }
 
 moe_status moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* row_of,
@@ -409,7 +462,8 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const moe_weights* wt,
   pa.capacity = d.capacity; pa.rows_cap = d.rows_cap;
   pa.tile_counts = at<int32_t>(ws, L.tile_counts);
   pa.counts = cnt; pa.offsets = off; pa.row_of = row_of; pa.token_of_row = tor;
-  pa.tile_prefix = tp; pa.bm = ffn_bm(cfg->act_dtype);
+  pa.tile_prefix = tp;
+  pa.bm = plan_ffn(cfg->act_dtype, D, cfg->d_ff, d.rows_cap, E).bm_up;
   MOE_TRY(mark(ev, MOE_STAGE_PERMUTE, 0, s));
   MOE_TRY_HIP("permute", launch_permute(pa, s));
   MOE_TRY(mark(ev, MOE_STAGE_PERMUTE, 1, s));
@@ -418,13 +472,14 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const moe_weights* wt,
     void* h = at<void>(ws, L.h);
     void* yperm = at<void>(ws, L.yperm);
     if (d.rows_cap > 0)
-      MOE_TRY(run_ffn(cfg->act_dtype, cfg->activation, E, D, cfg->d_ff, d.rows_cap, x, tor, off, tp, wt->w13,
-                      wt->w2, h, yperm, s, ev, MOE_STAGE_EXPERT_GATE_UP, MOE_STAGE_EXPERT_DOWN));
+      MOE_TRY(run_ffn(cfg->act_dtype, cfg->activation, E, D, cfg->d_ff, d.rows_cap, x, tor, off, tp,
+                      at<int32_t>(ws, L.tile_prefix2), wt->w13, wt->w2, h, yperm, s, ev, MOE_STAGE_EXPERT_GATE_UP,
+                      MOE_STAGE_EXPERT_DOWN));
     const void* y_shared = nullptr;
     if (cfg->num_shared > 0) {
       const int SF = cfg->num_shared * cfg->d_ff_shared;
-      MOE_TRY(run_ffn(cfg->act_dtype, SWIGLU, 1, D, SF, T, x, nullptr, nullptr, nullptr, wt->ws13, wt->ws2, h,
-                      y, s, ev, MOE_STAGE_SHARED_GATE_UP, MOE_STAGE_SHARED_DOWN));
+      MOE_TRY(run_ffn(cfg->act_dtype, SWIGLU, 1, D, SF, T, x, nullptr, nullptr, nullptr, nullptr, wt->ws13,
+                      wt->ws2, h, y, s, ev, MOE_STAGE_SHARED_GATE_UP, MOE_STAGE_SHARED_DOWN));
       y_shared = y;
     }
     MOE_TRY(mark(ev, MOE_STAGE_COMBINE, 0, s));

@@ -21,6 +21,7 @@ typedef uint16_t bf16_t;   // bfloat16 bit pattern
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 __host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 __host__ __device__ inline size_t round_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
@@ -88,12 +89,68 @@ struct GroupedGemm {
   int epilogue;
 };
 
+// Tile order of the grouped GEMMs.  The tiles that exist (known on the device
+// only) are numbered group by group; inside a group, runs of up to 8 m-tiles
+// sweep all n-tiles, so the blocks that run together share both the group's
+// weight tiles and its activation rows in L2.  Workgroup ids are then dealt so
+// that every XCD gets one contiguous, equally long stretch of that order.
+// Returns false for workgroups beyond the last tile (the grid is an upper
+// bound).  Outputs: group g, first row of the tile, rows in the tile, n-tile.
+template <int BM>
+__device__ __forceinline__ bool map_tile(const GroupedGemm& p, int n_tiles, int& g, int& row0, int& rows,
+                                         int& nt) {
+  constexpr int GM = 8;
+  const int bid = blockIdx.x;
+  if (p.offsets == nullptr) {
+    const int mt_all = ceil_div(p.M_max, BM);
+    const int total = mt_all * n_tiles;
+    if (bid >= total) return false;
+    const int L = xcd_remap(bid, total);
+    const int sub = L / (GM * n_tiles);
+    const int first = sub * GM;
+    const int gm = min(mt_all - first, GM);
+    const int loc = L - sub * GM * n_tiles;
+    const int mt = first + loc % gm;
+    nt = loc / gm;
+    g = 0;
+    row0 = mt * BM;
+    rows = min(BM, p.M_max - row0);
+    return true;
+  }
+  const int* tp = p.tile_prefix;
+  const int total = tp[p.G] * n_tiles;
+  if (bid >= total) return false;
+  const int L = xcd_remap(bid, total);
+  const int mtile = L / n_tiles;          // tiles of group g are [tp[g] n, tp[g+1] n)
+  int lo = 0, hi = p.G;                   // tp[lo] <= mtile < tp[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (tp[mid] <= mtile) lo = mid; else hi = mid;
+  }
+  g = lo;                                 // last group starting at or before: non-empty
+  const int mg = tp[g + 1] - tp[g];
+  const int local = L - tp[g] * n_tiles;
+  const int sub = local / (GM * n_tiles);
+  const int first = sub * GM;
+  const int gm = min(mg - first, GM);
+  const int loc = local - sub * GM * n_tiles;
+  const int m = first + loc % gm;
+  nt = loc / gm;
+  row0 = p.offsets[g] + m * BM;
+  rows = min(BM, p.offsets[g + 1] - row0);
+  return true;
+}
+
 // m-tile prefix for grouped GEMMs: prefix[g] = sum_{h<g} ceil((off[h+1]-off[h]) / bm).
 hipError_t launch_tile_prefix(const int32_t* offsets, int G, int bm, int32_t* prefix, hipStream_t s);
 
 // bf16 MFMA grouped GEMM; returns the BM its tiles use via bm_out when non-null.
 hipError_t launch_gemm_bf16(const GroupedGemm& g, hipStream_t s);
 int gemm_bf16_bm(const GroupedGemm& g);
+// Pipelined bf16 grouped GEMM (K % 64 == 0), tile configuration `cfg`.
+constexpr int kGemmV2Configs = 10;
+hipError_t launch_gemm_v2(const GroupedGemm& g, int cfg, hipStream_t s);
+int gemm_v2_bm(int cfg);
 // float32 SIMT grouped GEMM.  a_dtype / b_dtype select float32 or bf16 operands.
 hipError_t launch_gemm_f32(const GroupedGemm& g, int a_dtype, int b_dtype, hipStream_t s);
 constexpr int kF32GemmBM = 64;
@@ -142,7 +199,7 @@ struct StatsArgs {
   float alpha;
   float* f; float* P; float* aux_loss; float* imbalance; int32_t* dropped;
 };
-constexpr int kStatsChunk = 256;    // tokens per partial-sum block
+constexpr int kStatsChunk = 128;    // tokens per partial-sum block
 hipError_t launch_load_stats(const StatsArgs& a, hipStream_t s);
 
 }  // namespace moe

@@ -32,30 +32,6 @@ __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __rest
   if (g == 0) prefix[0] = 0;
 }
 
-// Locate the (group, first row, row count) of grouped m-tile `mt`.  Returns
-// false for m-tiles beyond the last one (the grid is sized by an upper bound).
-template <int BM>
-__device__ __forceinline__ bool locate_tile(const GroupedGemm& p, int mt, int& g, int& row0,
-                                            int& rows) {
-  if (p.offsets == nullptr) {
-    g = 0;
-    row0 = mt * BM;
-    rows = min(BM, p.M_max - row0);
-    return rows > 0;
-  }
-  const int* tp = p.tile_prefix;
-  if (mt >= tp[p.G]) return false;
-  int lo = 0, hi = p.G;                 // tp[lo] <= mt < tp[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (tp[mid] <= mt) lo = mid; else hi = mid;
-  }
-  g = lo;                               // last group starting at or before mt: non-empty
-  row0 = p.offsets[g] + (mt - tp[g]) * BM;
-  rows = min(BM, p.offsets[g + 1] - row0);
-  return true;
-}
-
 // Number of m-tiles that can exist: sum_g ceil(n_g / BM) <= floor(M / BM) + #non-empty groups.
 inline int m_tiles_bound(const GroupedGemm& p, int bm) {
   if (p.offsets == nullptr) return ceil_div(p.M_max, bm);
@@ -80,9 +56,11 @@ struct Tile {
   static_assert(BM % RPP == 0 && BN % RPP == 0, "tile/load mismatch");
 };
 
-template <int BM, int BN, int BK, int EPI, typename OutT>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(const GroupedGemm p, int m_tiles,
-                                                        int n_tiles) {
+// PRECISE: every BK-deep slice is summed by the MFMAs in float32 and then
+// added into float64 accumulators, so rounding error does not grow with K
+// (used for the router logits, which decide the expert selection).
+template <int BM, int BN, int BK, int EPI, typename OutT, bool PRECISE = false>
+__global__ __launch_bounds__(256) void gemm_bf16_kernel(const GroupedGemm p, int n_tiles) {
   using C = Tile<BM, BN, BK>;
   __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * C::LDS];
   __shared__ __attribute__((aligned(16))) bf16_t sB[2][BN * C::LDS];
@@ -92,19 +70,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GroupedGemm p, int
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // Tile order: XCD-contiguous ranges, then groups of 8 m-tiles sweeping the
-  // n-tiles so that A rows and B rows are reused out of L2.
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  constexpr int GM = 8;
-  const int grp = bid / (GM * n_tiles);
-  const int first_m = grp * GM;
-  const int gm = min(m_tiles - first_m, GM);
-  const int local = bid - grp * GM * n_tiles;
-  const int mt = first_m + local % gm;
-  const int nt = local / gm;
-
-  int g, row0, rows;
-  if (!locate_tile<BM>(p, mt, g, row0, rows)) return;
+  int g, row0, rows, nt;
+  if (!map_tile<BM>(p, n_tiles, g, row0, rows, nt)) return;
 
   const int K = p.K;
   const bf16_t* __restrict__ A = static_cast<const bf16_t*>(p.A);
@@ -172,6 +139,16 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GroupedGemm p, int
     for (int j = 0; j < C::TN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  constexpr int DM = PRECISE ? C::TM : 1, DN = PRECISE ? C::TN : 1, DR = PRECISE ? 16 : 1;
+  double dacc[DM][DN][DR];
+  if constexpr (PRECISE) {
+#pragma unroll
+    for (int i = 0; i < DM; ++i)
+#pragma unroll
+      for (int j = 0; j < DN; ++j)
+#pragma unroll
+        for (int r = 0; r < DR; ++r) dacc[i][j][r] = 0.0;
+  }
 
   const int nk = ceil_div(K, BK);
   gload(0);
@@ -200,6 +177,17 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GroupedGemm p, int
         for (int j = 0; j < C::TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfv[j], acc[i][j], 0, 0, 0);
     }
+    if constexpr (PRECISE) {
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            dacc[i][j][r] += (double)acc[i][j][r];
+            acc[i][j][r] = 0.0f;
+          }
+    }
     if (kt + 1 < nk) sstore(buf ^ 1);
     __syncthreads();
   }
@@ -225,7 +213,9 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GroupedGemm p, int
         for (int j = 0; j < C::TN; ++j) {
           const int n = nt * BN + wn * C::WN + j * 32 + (lane & 31);
           if (n < p.N) {
-            float v = acc[i][j][r];
+            float v;
+            if constexpr (PRECISE) v = (float)dacc[i][j][r];
+            else v = acc[i][j][r];
             if constexpr (EPI == EPI_GELU) v = gelu_erf_f32(v);
             crow[n] = from_f32<OutT>(v);
           }
@@ -255,16 +245,14 @@ template <> struct Vec4<bf16_t> {
 };
 
 template <typename TA, typename TB, int EPI, typename OutT>
-__global__ __launch_bounds__(256) void gemm_f32_kernel(const GroupedGemm p, int m_tiles, int n_tiles) {
+__global__ __launch_bounds__(256) void gemm_f32_kernel(const GroupedGemm p, int n_tiles) {
   constexpr int BM = kF32GemmBM, BN = 64, BK = 16;
   __shared__ float sA[BK][BM + 4];
   __shared__ float sB[BK][BN + 4];
   const int tid = threadIdx.x;
   const int tx = tid & 15, ty = tid >> 4;
-  const int mt = blockIdx.x % m_tiles;
-  const int nt = blockIdx.x / m_tiles;
-  int g, row0, rows;
-  if (!locate_tile<BM>(p, mt, g, row0, rows)) return;
+  int g, row0, rows, nt;
+  if (!map_tile<BM>(p, n_tiles, g, row0, rows, nt)) return;
 
   const int K = p.K;
   const TA* __restrict__ A = static_cast<const TA*>(p.A);
@@ -292,7 +280,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const GroupedGemm p, int 
     if (ok) b_ptr = B + (long long)brow * K + lk;
   }
 
+  // Each 16-deep slice is accumulated in float32, then added in float64.
   float acc[4][4] = {};
+  double dacc[4][4] = {};
   for (int k0 = 0; k0 < K; k0 += BK) {
     float va[4] = {0, 0, 0, 0}, vb[4] = {0, 0, 0, 0};
     if (a_ptr && k0 + lk < K) Vec4<TA>::load(a_ptr + k0, va);
@@ -312,6 +302,13 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const GroupedGemm p, int 
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        dacc[i][j] += (double)acc[i][j];
+        acc[i][j] = 0.0f;
+      }
     __syncthreads();
   }
 
@@ -325,14 +322,14 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const GroupedGemm p, int 
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int h = nt * (BN / 2) + tx + 16 * j;
-        if (h < p.N) crow[h] = from_f32<OutT>(silu_f32(acc[i][j]) * acc[i][j + 2]);
+        if (h < p.N) crow[h] = from_f32<OutT>(silu_f32((float)dacc[i][j]) * (float)dacc[i][j + 2]);
       }
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int n = nt * BN + tx + 16 * j;
         if (n < p.N) {
-          float v = acc[i][j];
+          float v = (float)dacc[i][j];
           if constexpr (EPI == EPI_GELU) v = gelu_erf_f32(v);
           crow[n] = from_f32<OutT>(v);
         }
@@ -343,16 +340,16 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const GroupedGemm p, int 
 
 constexpr int kBM = 128, kBN = 128, kBK = 64;
 
-template <int EPI, typename OutT>
+template <int EPI, typename OutT, int BM = kBM, int BN = kBN, bool PRECISE = false>
 hipError_t launch_bf16_epi(const GroupedGemm& p, hipStream_t s) {
-  const int cols = (EPI == EPI_SWIGLU) ? kBN / 2 : kBN;
+  const int cols = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
   const int n_tiles = ceil_div(p.N, cols);
-  const int m_tiles = m_tiles_bound(p, kBM);
+  const int m_tiles = m_tiles_bound(p, BM);
   if (m_tiles == 0 || n_tiles == 0) return hipSuccess;
   const long long blocks = (long long)m_tiles * n_tiles;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_bf16_kernel<kBM, kBN, kBK, EPI, OutT>), dim3((unsigned)blocks), dim3(256),
-                     0, s, p, m_tiles, n_tiles);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, kBK, EPI, OutT, PRECISE>), dim3((unsigned)blocks), dim3(256),
+                     0, s, p, n_tiles);
   return hipGetLastError();
 }
 
@@ -365,7 +362,7 @@ hipError_t launch_f32_epi(const GroupedGemm& p, hipStream_t s) {
   const long long blocks = (long long)m_tiles * n_tiles;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((gemm_f32_kernel<TA, TB, EPI, OutT>), dim3((unsigned)blocks), dim3(256), 0, s,
-                     p, m_tiles, n_tiles);
+                     p, n_tiles);
   return hipGetLastError();
 }
 
@@ -380,7 +377,8 @@ int gemm_bf16_bm(const GroupedGemm&) { return kBM; }
 
 hipError_t launch_gemm_bf16(const GroupedGemm& p, hipStream_t s) {
   switch (p.epilogue) {
-    case EPI_STORE_F32: return launch_bf16_epi<EPI_STORE_F32, float>(p, s);
+    // float32 output is the router logits: small tiles, float64 slice accumulation
+    case EPI_STORE_F32: return launch_bf16_epi<EPI_STORE_F32, float, 64, 64, true>(p, s);
     case EPI_STORE_ACT: return launch_bf16_epi<EPI_STORE_ACT, bf16_t>(p, s);
     case EPI_SWIGLU: return launch_bf16_epi<EPI_SWIGLU, bf16_t>(p, s);
     case EPI_GELU: return launch_bf16_epi<EPI_GELU, bf16_t>(p, s);

@@ -210,10 +210,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ yp, 
 __global__ __launch_bounds__(256) void stats_partial_kernel(const StatsArgs a) {
   const int t0 = blockIdx.x * kStatsChunk;
   const int t1 = min(a.T, t0 + kStatsChunk);
+  // four independent partial sums (fixed assignment t % 4) keep several
+  // loads in flight per thread
   for (int e = threadIdx.x; e < a.E; e += blockDim.x) {
-    float s = 0.0f;
-    for (int t = t0; t < t1; ++t) s += a.probs[(long long)t * a.E + e];
-    a.partial[(long long)blockIdx.x * a.E + e] = s;
+    float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    int t = t0;
+    for (; t + 4 <= t1; t += 4) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) s[q] += a.probs[(long long)(t + q) * a.E + e];
+    }
+    for (; t < t1; ++t) s[t & 3] += a.probs[(long long)t * a.E + e];
+    a.partial[(long long)blockIdx.x * a.E + e] = (s[0] + s[1]) + (s[2] + s[3]);
   }
 }
 
@@ -227,8 +234,9 @@ __global__ __launch_bounds__(kMaxExperts) void stats_final_kernel(const StatsArg
   int c = 0, drop = 0;
   if (e < a.E) {
     c = a.counts[e];
-    float s = 0.0f;
-    for (int b = 0; b < nchunks; ++b) s += a.partial[(long long)b * a.E + e];
+    float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int b = 0; b < nchunks; ++b) s4[b & 3] += a.partial[(long long)b * a.E + e];
+    const float s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     pe = a.T > 0 ? s / (float)a.T : 0.0f;
     fe = a.T > 0 ? (float)c / A : 0.0f;
     drop = c - min(c, a.capacity);

@@ -34,7 +34,7 @@ def device_weights(inp: HostInputs, device="cuda") -> dict:
                 ws13=to_torch(inp.ws13, device), ws2=to_torch(inp.ws2, device))
 
 
-def upload_experts(cfg: MoEConfig, device="cuda", keep_host: bool = False, workers: int = 16):
+def upload_experts(cfg: MoEConfig, device="cuda", keep_host: bool = False, workers: int = 16, progress=None):
     """Generate the routed expert weights expert by expert and copy them into
     device tensors w13 [E, n_mat*F, D], w2 [E, D, F] without holding all of them
     on the host (unless keep_host)."""
@@ -47,4 +47,6 @@ def upload_experts(cfg: MoEConfig, device="cuda", keep_host: bool = False, worke
         w2[e].copy_(to_torch(b, "cpu"))
         if keep_host:
             host[e] = (a, b)
+        if progress is not None and (e + 1) % 32 == 0:
+            progress(e + 1)
     return w13, w2, host
