@@ -84,7 +84,10 @@ moe_status validate_config(const moe_config* c) {
 }
 
 // Workspace pieces ---------------------------------------------------------
-size_t ws_route(const moe_config* c) { return carve((size_t)c->num_tokens * c->num_experts * 4); }
+size_t router_split_bytes(const moe_config* c);
+size_t ws_route(const moe_config* c) {
+  return carve((size_t)c->num_tokens * c->num_experts * 4) + router_split_bytes(c);
+}
 size_t ws_permute(const moe_config* c) {
   return carve((size_t)ceil_div(c->num_tokens, kPermuteTile) * c->num_experts * 4);
 }
@@ -96,7 +99,7 @@ size_t ws_stats(const moe_config* c) {
 }
 
 struct Layout {
-  size_t logits, probs, idx, w, tile_counts, counts, offsets, tile_prefix, tile_prefix2, row_of, tor, h,
+  size_t logits, wsplit, probs, idx, w, tile_counts, counts, offsets, tile_prefix, tile_prefix2, row_of, tor, h,
       yperm, partial, total;
 };
 
@@ -107,6 +110,7 @@ Layout layer_layout(const moe_config* c, const Derived& d) {
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o += carve(bytes); return at; };
   L.logits = take(T * E * 4);
+  L.wsplit = take(router_split_bytes(c));
   L.probs = take(T * E * 4);
   L.idx = take(T * k * 4);
   L.w = take(T * k * 4);
@@ -130,8 +134,18 @@ template <typename P>
 P* at(void* ws, size_t off) { return reinterpret_cast<P*>(static_cast<char*>(ws) + off); }
 
 // Launch helpers -----------------------------------------------------------
+// bf16 tokens with a float32 router weight run on the matrix cores: the weight
+// is split exactly into three bf16 planes and the GEMM runs over K = 3D with
+// the token columns wrapping (x . w = x . hi + x . mid + x . lo).
+inline bool router_split(const moe_config* c) {
+  return c->router_dtype == F32 && c->act_dtype == BF16 && c->d_model % 64 == 0;
+}
+size_t router_split_bytes(const moe_config* c) {
+  return router_split(c) ? carve((size_t)c->num_experts * 3 * c->d_model * 2) : 0;
+}
+
 moe_status run_router_logits(const moe_config* c, const void* x, const void* w_router, float* logits,
-                             hipStream_t s) {
+                             void* split_ws, hipStream_t s) {
   GroupedGemm g{};
   g.A = x; g.a_rows = nullptr; g.lda = c->d_model;
   g.B = w_router; g.b_group_stride = 0;
@@ -139,8 +153,20 @@ moe_status run_router_logits(const moe_config* c, const void* x, const void* w_r
   g.M_max = c->num_tokens; g.N = c->num_experts; g.K = c->d_model;
   g.G = 1; g.offsets = nullptr; g.tile_prefix = nullptr;
   g.epilogue = EPI_STORE_F32;
-  if (c->router_dtype == BF16) MOE_TRY_HIP("router logits (bf16)", launch_gemm_bf16(g, s));
-  else MOE_TRY_HIP("router logits (f32)", launch_gemm_f32(g, c->act_dtype, F32, s));
+  g.a_kwrap = 0;
+  if (c->router_dtype == BF16) {
+    MOE_TRY_HIP("router logits (bf16)", launch_gemm_bf16(g, s));
+  } else if (router_split(c)) {
+    bf16_t* planes = static_cast<bf16_t*>(split_ws);
+    MOE_TRY_HIP("router weight split", launch_split_bf16x3(static_cast<const float*>(w_router), c->num_experts,
+                                                           c->d_model, planes, s));
+    g.B = planes;
+    g.K = 3 * c->d_model;
+    g.a_kwrap = c->d_model;
+    MOE_TRY_HIP("router logits (bf16 x3)", launch_gemm_bf16(g, s));
+  } else {
+    MOE_TRY_HIP("router logits (f32)", launch_gemm_f32(g, c->act_dtype, F32, s));
+  }
   return MOE_OK;
 }
 
@@ -308,7 +334,8 @@ moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
   if (cfg->num_tokens == 0) return MOE_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* logits = static_cast<float*>(ws);
-  MOE_TRY(run_router_logits(cfg, x, w_router, logits, s));
+  MOE_TRY(run_router_logits(cfg, x, w_router, logits,
+                            at<void>(ws, carve((size_t)cfg->num_tokens * cfg->num_experts * 4)), s));
   return run_select(cfg, logits, x, w_router, sel_bias, topk_idx, topk_w, probs, s);
 }
 
@@ -450,7 +477,7 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const moe_weights* wt,
   if (any) {
     float* logits = at<float>(ws, L.logits);
     MOE_TRY(mark(ev, MOE_STAGE_ROUTER_LOGITS, 0, s));
-    MOE_TRY(run_router_logits(cfg, x, wt->w_router, logits, s));
+    MOE_TRY(run_router_logits(cfg, x, wt->w_router, logits, at<void>(ws, L.wsplit), s));
     MOE_TRY(mark(ev, MOE_STAGE_ROUTER_LOGITS, 1, s));
     MOE_TRY(mark(ev, MOE_STAGE_ROUTE_SELECT, 0, s));
     MOE_TRY(run_select(cfg, logits, x, wt->w_router, wt->sel_bias, idx, w, probs, s));

@@ -87,7 +87,12 @@ struct GroupedGemm {
   const int32_t* offsets;     // [G+1] or nullptr (one group of M_max rows)
   const int32_t* tile_prefix; // [G+1] m-tile prefix for the kernel's BM (grouped case)
   int epilogue;
+  int a_kwrap;                // 0, or: A column k is read at k % a_kwrap (a multiple of 64)
 };
+
+// Exact split of a float32 matrix into three bfloat16 planes, hi + mid + lo = w:
+// out[e][j][d] = plane j of w[e][d], out has [E][3][D] layout.
+hipError_t launch_split_bf16x3(const float* w, int E, int D, bf16_t* out, hipStream_t s);
 
 // Tile order of the grouped GEMMs.  The tiles that exist (known on the device
 // only) are numbered group by group; inside a group, runs of up to 8 m-tiles
@@ -199,7 +204,7 @@ struct StatsArgs {
   float alpha;
   float* f; float* P; float* aux_loss; float* imbalance; int32_t* dropped;
 };
-constexpr int kStatsChunk = 128;    // tokens per partial-sum block
+constexpr int kStatsChunk = 64;     // tokens per partial-sum block (multiple of 4)
 hipError_t launch_load_stats(const StatsArgs& a, hipStream_t s);
 
 }  // namespace moe

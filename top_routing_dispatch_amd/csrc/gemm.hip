@@ -112,9 +112,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GroupedGemm p, int
   uint4 ra[C::A_PASSES], rb[C::B_PASSES];
   auto gload = [&](int k0) {
     const bool kin = (k0 + kc) < K;
+    const int ka = p.a_kwrap ? k0 % p.a_kwrap : k0;
 #pragma unroll
     for (int i = 0; i < C::A_PASSES; ++i)
-      ra[i] = (a_ptr[i] && kin) ? *reinterpret_cast<const uint4*>(a_ptr[i] + k0) : make_uint4(0, 0, 0, 0);
+      ra[i] = (a_ptr[i] && kin) ? *reinterpret_cast<const uint4*>(a_ptr[i] + ka) : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < C::B_PASSES; ++i)
       rb[i] = (b_ptr[i] && kin) ? *reinterpret_cast<const uint4*>(b_ptr[i] + k0) : make_uint4(0, 0, 0, 0);

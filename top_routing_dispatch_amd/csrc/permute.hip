@@ -207,55 +207,89 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ yp, 
 // ---------------------------------------------------------------------------
 // load statistics
 // ---------------------------------------------------------------------------
+// Column sums of probs over chunks of kStatsChunk tokens.  A block covers 64
+// experts x one chunk: thread (e, rg) sums rows rg, rg + 4, ... of the chunk
+// (all loads issued before the adds), then the four row groups are added in
+// LDS in a fixed order.
 __global__ __launch_bounds__(256) void stats_partial_kernel(const StatsArgs a) {
+  __shared__ float sp[4][64];
+  const int el = threadIdx.x & 63, rg = threadIdx.x >> 6;
+  const int e = blockIdx.y * 64 + el;
   const int t0 = blockIdx.x * kStatsChunk;
-  const int t1 = min(a.T, t0 + kStatsChunk);
-  // four independent partial sums (fixed assignment t % 4) keep several
-  // loads in flight per thread
-  for (int e = threadIdx.x; e < a.E; e += blockDim.x) {
-    float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    int t = t0;
-    for (; t + 4 <= t1; t += 4) {
+  constexpr int PER = kStatsChunk / 4;
+  float v[PER];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) s[q] += a.probs[(long long)(t + q) * a.E + e];
-    }
-    for (; t < t1; ++t) s[t & 3] += a.probs[(long long)t * a.E + e];
-    a.partial[(long long)blockIdx.x * a.E + e] = (s[0] + s[1]) + (s[2] + s[3]);
+  for (int i = 0; i < PER; ++i) {
+    const int t = t0 + rg + 4 * i;
+    v[i] = (e < a.E && t < a.T) ? a.probs[(long long)t * a.E + e] : 0.0f;
   }
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) s += v[i];
+  sp[rg][el] = s;
+  __syncthreads();
+  if (rg == 0 && e < a.E)
+    a.partial[(long long)blockIdx.x * a.E + e] = (sp[0][el] + sp[1][el]) + (sp[2][el] + sp[3][el]);
 }
 
-__global__ __launch_bounds__(kMaxExperts) void stats_final_kernel(const StatsArgs a, int nchunks) {
+// f, P, loss, imbalance, dropped.  Thread (e, j) of the 1024 sums partial
+// chunks j, j + TPE, ... of expert e (TPE threads per expert), combined in LDS
+// in a fixed order; scalar results by a fixed-shape tree.
+__global__ __launch_bounds__(kMaxExperts) void stats_final_kernel(const StatsArgs a, int nchunks, int tpe) {
   __shared__ float sf[kMaxExperts];
   __shared__ int si[kMaxExperts];
   __shared__ int sd[kMaxExperts];
-  const int e = threadIdx.x;
-  const float A = (float)a.T * (float)a.k;
+  const int tid = threadIdx.x;
+  const int e = tid / tpe, j = tid % tpe;
+  float s = 0.0f;
+  if (e < a.E) {
+    float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    int b = j, q = 0;
+    for (; b < nchunks; b += tpe, q = (q + 1) & 3) v[q] += a.partial[(long long)b * a.E + e];
+    s = (v[0] + v[1]) + (v[2] + v[3]);
+  }
+  sf[tid] = s;
+  __syncthreads();
+  for (int d = tpe / 2; d >= 1; d >>= 1) {
+    if (j < d) sf[tid] += sf[tid + d];
+    __syncthreads();
+  }
+  const float psum = sf[e * tpe];
+  __syncthreads();
+  // one thread per expert from here on
+  const int ee = tid;
   float fe = 0.0f, pe = 0.0f;
   int c = 0, drop = 0;
-  if (e < a.E) {
-    c = a.counts[e];
-    float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int b = 0; b < nchunks; ++b) s4[b & 3] += a.partial[(long long)b * a.E + e];
-    const float s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
-    pe = a.T > 0 ? s / (float)a.T : 0.0f;
-    fe = a.T > 0 ? (float)c / A : 0.0f;
+  const float A = (float)a.T * (float)a.k;
+  if (ee < a.E) {
+    c = a.counts[ee];
     drop = c - min(c, a.capacity);
-    if (a.f) a.f[e] = fe;
-    if (a.P) a.P[e] = pe;
+    fe = a.T > 0 ? (float)c / A : 0.0f;
   }
-  sf[e] = fe * pe;
-  si[e] = c;
-  sd[e] = drop;
+  if (j == 0 && e < a.E) {
+    pe = a.T > 0 ? psum / (float)a.T : 0.0f;
+    if (a.P) a.P[e] = pe;
+    sf[e] = pe;            // stash P[e] (slot e was read by its owner thread already)
+  }
+  __syncthreads();
+  if (ee < a.E) {
+    pe = sf[ee];
+    if (a.f) a.f[ee] = fe;
+  }
+  __syncthreads();
+  sf[tid] = (ee < a.E) ? fe * pe : 0.0f;
+  si[tid] = c;
+  sd[tid] = drop;
   __syncthreads();
   for (int d = kMaxExperts / 2; d >= 1; d >>= 1) {
-    if (e < d) {
-      sf[e] += sf[e + d];
-      si[e] = max(si[e], si[e + d]);
-      sd[e] += sd[e + d];
+    if (tid < d) {
+      sf[tid] += sf[tid + d];
+      si[tid] = max(si[tid], si[tid + d]);
+      sd[tid] += sd[tid + d];
     }
     __syncthreads();
   }
-  if (e == 0) {
+  if (tid == 0) {
     if (a.aux_loss) *a.aux_loss = a.alpha * (float)a.E * sf[0];
     if (a.imbalance) *a.imbalance = a.T > 0 ? (float)si[0] / (A / (float)a.E) : 0.0f;
     if (a.dropped) *a.dropped = sd[0];
@@ -311,11 +345,13 @@ hipError_t launch_combine(const void* y_perm, const int32_t* row_of, const float
 hipError_t launch_load_stats(const StatsArgs& a, hipStream_t s) {
   const int nchunks = ceil_div(a.T, kStatsChunk);
   if (nchunks > 0) {
-    hipLaunchKernelGGL(stats_partial_kernel, dim3(nchunks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(stats_partial_kernel, dim3(nchunks, ceil_div(a.E, 64)), dim3(256), 0, s, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(stats_final_kernel, dim3(1), dim3(kMaxExperts), 0, s, a, nchunks);
+  int tpe = 1;                          // threads per expert: largest power of two with E * tpe <= 1024
+  while (a.E * tpe * 2 <= kMaxExperts) tpe *= 2;
+  hipLaunchKernelGGL(stats_final_kernel, dim3(1), dim3(kMaxExperts), 0, s, a, nchunks, tpe);
   return hipGetLastError();
 }
 

@@ -63,20 +63,6 @@ __device__ __forceinline__ void load4(const void* p, int dt, long long i, float 
   }
 }
 
-// float64 dot product of token row t with router row e, reduced over the wave.
-__device__ double logit_f64(const RouteArgs& a, int t, int e, int lane) {
-  double acc = 0.0;
-  const long long xo = (long long)t * a.D, wo = (long long)e * a.D;
-  for (int d = lane * 4; d < a.D; d += kWave * 4) {
-    float xv[4], wv[4];
-    load4(a.x, a.act_dtype, xo + d, xv);
-    load4(a.w_router, a.router_dtype, wo + d, wv);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) acc = fma((double)xv[q], (double)wv[q], acc);
-  }
-  return wave_sum_f64(acc);
-}
-
 __device__ __forceinline__ float sigmoid_f32(float s) { return 1.0f / (1.0f + expf(-s)); }
 
 template <int EPL>
@@ -128,28 +114,87 @@ __global__ __launch_bounds__(256) void route_select_kernel(const RouteArgs a) {
   }
 
   // ---- near-tie refinement in float64
+  // Among the k+1 best keys, pick r is "close" to pick r+1 when their float32
+  // keys are within 2 tau.  Exactly the picks in a close run get float64
+  // keys; when the run reaches the k-th/(k+1)-th boundary, so does every
+  // other expert whose key lies within 2 tau below the k-th.  Ranking refined
+  // experts by their float64 key and all others by their float32 key then
+  // gives the order of the exact keys: any pair with an unrefined member is
+  // more than 2 tau apart, far beyond the error of either key.
   const float next_key = __shfl_down(my_key, 1);
   const bool close = (lane + 1 < nsel) && (my_key - next_key <= 2.0f * tau);
-  if (__ballot(close) != 0) {
+  const unsigned long long close_mask = __ballot(close);
+  if (close_mask != 0) {
+    // pick r needs float64 when it is close to a neighbour
+    const bool prev_close = lane > 0 && ((close_mask >> (lane - 1)) & 1ull);
+    const bool pick_ref = lane < nsel && (close || prev_close);
+    const bool boundary = k < nsel && ((close_mask >> (k - 1)) & 1ull);
     const float thr = __shfl(my_key, k - 1) - 2.0f * tau;
-    double k64[EPL];
-    bool cand[EPL];
+    // per-expert flags: candidate (ranked at all) and refined (float64 key)
+    bool cand[EPL], ref[EPL];
+    double m64[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
-      const int e = lane + kWave * i;
-      cand[i] = e < E && key[i] >= thr;
-      k64[i] = -INFINITY;
-      unsigned long long m = __ballot(cand[i]);
+      cand[i] = false;
+      ref[i] = false;
+      m64[i] = (double)key[i];
+    }
+    // the k+1 picks are candidates; publish which of them are refined
+    for (int r = 0; r < nsel; ++r) {
+      const int pe_r = __shfl(my_e, r);
+      const bool pr = __shfl((int)pick_ref, r) != 0;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (lane + kWave * i == pe_r) { cand[i] = true; ref[i] = pr; }
+    }
+    if (boundary) {
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (lane + kWave * i < E && !cand[i] && key[i] >= thr) { cand[i] = true; ref[i] = true; }
+    }
+    // float64 logits of the refined experts, up to eight per pass over the
+    // token row (the loop is unrolled so several rows' loads are in flight)
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      unsigned long long m = __ballot(ref[i]);
       while (m) {
-        const int l = __builtin_ctzll(m);
-        m &= m - 1;
-        const int ce = l + kWave * i;
-        const double s64 = logit_f64(a, t, ce, lane);
-        double q64 = s64;
-        if (sig) q64 = 1.0 / (1.0 + exp(-s64)) + (a.sel_bias ? (double)a.sel_bias[ce] : 0.0);
-        if (lane == l) k64[i] = q64;
+        constexpr int NB = 4;
+        int ce[NB];
+        int nb = 0;
+        for (; nb < NB && m; ++nb) {
+          const int l = __builtin_ctzll(m);
+          m &= m - 1;
+          ce[nb] = l + kWave * i;
+        }
+        for (int c = nb; c < NB; ++c) ce[c] = ce[0];
+        double acc[NB];
+#pragma unroll
+        for (int c = 0; c < NB; ++c) acc[c] = 0.0;
+        const long long xo = (long long)t * a.D;
+
+        for (int d = lane * 4; d < a.D; d += kWave * 4) {
+          float xv[4];
+          load4(a.x, a.act_dtype, xo + d, xv);
+#pragma unroll
+          for (int c = 0; c < NB; ++c) {
+            float wv[4];
+            load4(a.w_router, a.router_dtype, (long long)ce[c] * a.D + d, wv);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[c] = fma((double)xv[q], (double)wv[q], acc[c]);
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < NB; ++c) {
+          if (c < nb) {
+            const double s64 = wave_sum_f64(acc[c]);
+            double q64 = s64;
+            if (sig) q64 = 1.0 / (1.0 + exp(-s64)) + (a.sel_bias ? (double)a.sel_bias[ce[c]] : 0.0);
+            if (lane == (ce[c] & 63)) m64[i] = q64;
+          }
+        }
       }
     }
+    // rank the candidates: k rounds of (key desc, expert asc)
     bool tk[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) tk[i] = !cand[i];
@@ -158,7 +203,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(const RouteArgs a) {
       int be = INT_MAX;
 #pragma unroll
       for (int i = 0; i < EPL; ++i)
-        if (!tk[i] && (be == INT_MAX || k64[i] > bv)) { bv = k64[i]; be = lane + kWave * i; }
+        if (!tk[i] && (be == INT_MAX || m64[i] > bv)) { bv = m64[i]; be = lane + kWave * i; }
       wave_argmax(bv, be);
 #pragma unroll
       for (int i = 0; i < EPL; ++i)
@@ -257,6 +302,40 @@ hipError_t launch_route_select(const RouteArgs& a, hipStream_t s) {
   if (epl <= 4) return launch_epl<4>(a, s);
   if (epl <= 8) return launch_epl<8>(a, s);
   return launch_epl<16>(a, s);
+}
+
+}  // namespace moe
+
+namespace moe {
+namespace {
+
+// hi = rne(w), mid = rne(w - hi), lo = w - hi - mid: every difference is exact
+// in float32 and lo has at most 8 significant bits, so hi + mid + lo == w.
+__global__ __launch_bounds__(256) void split_bf16x3_kernel(const float* __restrict__ w, int E, int D,
+                                                           bf16_t* __restrict__ out) {
+  const long long n = (long long)E * D;
+  for (long long i = blockIdx.x * 256LL + threadIdx.x; i < n; i += (long long)gridDim.x * 256) {
+    const int e = (int)(i / D), d = (int)(i % D);
+    const float v = w[i];
+    const bf16_t hi = f32_to_bf16(v);
+    const float r1 = v - bf16_to_f32(hi);
+    const bf16_t mid = f32_to_bf16(r1);
+    const float r2 = r1 - bf16_to_f32(mid);
+    const bf16_t lo = f32_to_bf16(r2);
+    bf16_t* o = out + (long long)e * 3 * D + d;
+    o[0] = hi;
+    o[D] = mid;
+    o[2 * D] = lo;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_split_bf16x3(const float* w, int E, int D, bf16_t* out, hipStream_t s) {
+  const long long n = (long long)E * D;
+  const int blocks = (int)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
+  hipLaunchKernelGGL(split_bf16x3_kernel, dim3(blocks), dim3(256), 0, s, w, E, D, out);
+  return hipGetLastError();
 }
 
 }  // namespace moe
