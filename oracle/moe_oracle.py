@@ -14,7 +14,7 @@ step; the steps and their sources:
                                                     Tiny-MoE page ("从 Dense FFN 到 MoE") §4 Router
   scores       softmax / sigmoid + selection bias   "Top-k 路由" Step 2 note (a)/(b);
                                                     "别只比较 Top-k" page, Score / Select / Merge steps
-  top-k        k best experts per token             Tiny-MoE §4 (torch.topk); "Top-K Routing (MoE)"
+  top-k        k best experts per token             Tiny-MoE §4 (top-k of the probabilities); "Top-K Routing (MoE)"
                                                     glossary, Implementation Router MoE
   weights      renormalised / k-way softmax / raw   same places
   dispatch     per-expert (token, slot) lists       Tiny-MoE §5 (torch.where, row-major order)
@@ -29,7 +29,7 @@ step; the steps and their sources:
 Readings taken where the pages are silent (each is also listed with its reason
 in the design notes):
   * top-k ties go to the lower expert index; slots are ordered by descending
-    score (torch.topk sorted order);
+    score (sorted top-k order);
   * SOFTMAX_TOPK ranks on p = softmax(s); TOPK_SOFTMAX ranks on s, the
     pages' Top-k(s) (same order as p); SIGMOID_BIAS ranks on sigmoid(s) + b;
   * rows inside an expert are in ascending token order, experts in ascending
@@ -80,7 +80,7 @@ def router_logits(x: np.ndarray, w_router: np.ndarray) -> np.ndarray:
 
 
 def softmax(s: np.ndarray) -> np.ndarray:
-    """Row softmax over experts (Tiny-MoE §4 router_probs)."""
+    """Row softmax over experts (Tiny-MoE §4 routing probabilities)."""
     z = np.exp(s - s.max(axis=-1, keepdims=True))
     return z / z.sum(axis=-1, keepdims=True)
 
@@ -145,7 +145,7 @@ def gate_weights(s: np.ndarray, idx: np.ndarray, scoring: int, renormalize: int)
 
 def importance_probs(s: np.ndarray, scoring: int) -> np.ndarray:
     """Per-token soft probability over all experts used for P_e: the full
-    softmax (Tiny-MoE §8 importance = router_probs.mean); for sigmoid scoring
+    softmax (Tiny-MoE §8: importance is its token mean); for sigmoid scoring
     the affinities normalised to sum 1 per token."""
     if scoring == SIGMOID_BIAS:
         a = sigmoid(s)
@@ -269,7 +269,7 @@ def shared_experts(x, shared: Sequence) -> np.ndarray:
 def expert_outputs(x, disp, expert_weights: Callable[[int], tuple], activation: int,
                    d_ff: int, num_experts: int) -> np.ndarray:
     """Y [A_kept, D]: expert e applied to its batch x[token_of_row[off_e:off_e+1]]
-    (Tiny-MoE §5 expert_input = tokens[token_indices]).  Expert weights are
+    (Tiny-MoE §5: an expert's batch is its tokens' rows).  Expert weights are
     fetched lazily so only experts with rows are materialised."""
     X = widen(x)
     off, tor = disp["offsets"], disp["token_of_row"]

@@ -30,7 +30,7 @@ def gold(name):
 # --------------------------------------------------------------------------
 def test_router_worked_example():
     g = gold("router_worked_example.json")
-    p = np.array([g["router_probs"]])
+    p = np.array([g["probabilities"]])
     s = np.log(p)                       # softmax(log p) = p exactly up to rounding
     q = O.selection_key(s, O.SOFTMAX_TOPK, None)
     np.testing.assert_allclose(q, p, rtol=1e-15)
@@ -374,7 +374,7 @@ def test_importance_vs_load_cases():
     g = gold("load_examples.json")["importance_vs_load"]
     for case in ("case_A", "case_B"):
         c = g[case]
-        probs = np.array(c["router_probs"])
+        probs = np.array(c["probabilities"])
         s = np.log(probs)
         idx = O.topk(O.selection_key(s, O.SOFTMAX_TOPK, None), 1)
         assert idx.tolist() == c["topk_indices"]
