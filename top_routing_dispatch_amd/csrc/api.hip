@@ -85,8 +85,10 @@ moe_status validate_config(const moe_config* c) {
 
 // Workspace pieces ---------------------------------------------------------
 size_t router_split_bytes(const moe_config* c);
+// route workspace: logits [T, E] f32 | refinement flags [T] | router weight planes
 size_t ws_route(const moe_config* c) {
-  return carve((size_t)c->num_tokens * c->num_experts * 4) + router_split_bytes(c);
+  return carve((size_t)c->num_tokens * c->num_experts * 4) + carve((size_t)c->num_tokens * 4) +
+         router_split_bytes(c);
 }
 size_t ws_permute(const moe_config* c) {
   return carve((size_t)ceil_div(c->num_tokens, kPermuteTile) * c->num_experts * 4);
@@ -99,7 +101,7 @@ size_t ws_stats(const moe_config* c) {
 }
 
 struct Layout {
-  size_t logits, wsplit, probs, idx, w, tile_counts, counts, offsets, tile_prefix, tile_prefix2, row_of, tor, h,
+  size_t logits, flags, wsplit, probs, idx, w, tile_counts, counts, offsets, tile_prefix, tile_prefix2, row_of, tor, h,
       yperm, partial, total;
 };
 
@@ -110,6 +112,7 @@ Layout layer_layout(const moe_config* c, const Derived& d) {
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o += carve(bytes); return at; };
   L.logits = take(T * E * 4);
+  L.flags = take(T * 4);
   L.wsplit = take(router_split_bytes(c));
   L.probs = take(T * E * 4);
   L.idx = take(T * k * 4);
@@ -171,7 +174,8 @@ moe_status run_router_logits(const moe_config* c, const void* x, const void* w_r
 }
 
 moe_status run_select(const moe_config* c, const float* logits, const void* x, const void* w_router,
-                      const float* sel_bias, int32_t* idx, float* w, float* probs, hipStream_t s) {
+                      const float* sel_bias, int32_t* idx, float* w, float* probs, int32_t* flags,
+                      hipStream_t s) {
   RouteArgs a{};
   a.logits = logits; a.x = x; a.w_router = w_router;
   a.sel_bias = c->scoring == SIGMOID_BIAS ? sel_bias : nullptr;
@@ -179,7 +183,7 @@ moe_status run_select(const moe_config* c, const float* logits, const void* x, c
   a.T = c->num_tokens; a.D = c->d_model; a.E = c->num_experts; a.k = c->top_k;
   a.scoring = c->scoring; a.renormalize = c->renormalize;
   a.act_dtype = c->act_dtype; a.router_dtype = c->router_dtype;
-  MOE_TRY_HIP("route select", launch_route_select(a, s));
+  MOE_TRY_HIP("route select", launch_route_select(a, flags, s));
   return MOE_OK;
 }
 
@@ -334,9 +338,10 @@ moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
   if (cfg->num_tokens == 0) return MOE_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* logits = static_cast<float*>(ws);
-  MOE_TRY(run_router_logits(cfg, x, w_router, logits,
-                            at<void>(ws, carve((size_t)cfg->num_tokens * cfg->num_experts * 4)), s));
-  return run_select(cfg, logits, x, w_router, sel_bias, topk_idx, topk_w, probs, s);
+  const size_t lb = carve((size_t)cfg->num_tokens * cfg->num_experts * 4);
+  int32_t* flags = at<int32_t>(ws, lb);
+  MOE_TRY(run_router_logits(cfg, x, w_router, logits, at<void>(ws, lb + carve((size_t)cfg->num_tokens * 4)), s));
+  return run_select(cfg, logits, x, w_router, sel_bias, topk_idx, topk_w, probs, flags, s);
 }
 
 moe_status moe_permute(const moe_config* cfg, const int32_t* topk_idx, const void* x,
@@ -480,7 +485,7 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const moe_weights* wt,
     MOE_TRY(run_router_logits(cfg, x, wt->w_router, logits, at<void>(ws, L.wsplit), s));
     MOE_TRY(mark(ev, MOE_STAGE_ROUTER_LOGITS, 1, s));
     MOE_TRY(mark(ev, MOE_STAGE_ROUTE_SELECT, 0, s));
-    MOE_TRY(run_select(cfg, logits, x, wt->w_router, wt->sel_bias, idx, w, probs, s));
+    MOE_TRY(run_select(cfg, logits, x, wt->w_router, wt->sel_bias, idx, w, probs, at<int32_t>(ws, L.flags), s));
     MOE_TRY(mark(ev, MOE_STAGE_ROUTE_SELECT, 1, s));
   }
 

@@ -171,7 +171,8 @@ struct RouteArgs {
   int T, D, E, k;
   int scoring, renormalize, act_dtype, router_dtype;
 };
-hipError_t launch_route_select(const RouteArgs& a, hipStream_t s);
+// flags: [T] int32 scratch (tokens that need the float64 refinement pass).
+hipError_t launch_route_select(const RouteArgs& a, int32_t* flags, hipStream_t s);
 
 struct PermuteArgs {
   const int32_t* topk_idx;    // [T, k]

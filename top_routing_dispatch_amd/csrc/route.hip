@@ -11,12 +11,15 @@
 // k (+1) best are found by k (+1) rounds of a wave-wide arg-max with ties to
 // the lower expert index, and lane r keeps the r-th pick in a register.
 //
-// Near-tie refinement: the logits arrive in float32.  Wherever two of the
-// k+1 best keys of a token are closer than twice a bound on the float32 error,
-// every expert within that distance of the k-th key has its logit recomputed
-// as a float64 dot product, and the selection is redone in float64 on those
-// candidates.  Every expert outside the candidate set is provably below the
-// k-th selected one, so the result equals the selection on exact logits.
+// Near-tie refinement: the logits arrive in float32.  Among the k+1 best keys,
+// pick r is "close" to pick r+1 when their float32 keys are within 2 tau (tau
+// bounds the float32 error).  The picks in a close run get float64 logits;
+// when the run reaches the k-th/(k+1)-th boundary, so does every other expert
+// whose key lies within 2 tau below the k-th.  Ranking refined experts by their
+// float64 key and all others by their float32 key gives the order of the exact
+// keys: any pair with an unrefined member is more than 2 tau apart.  The first
+// pass flags such tokens; a second pass (one wavefront per flagged token)
+// redoes only those.
 #include <float.h>
 #include <limits.h>
 
@@ -65,190 +68,101 @@ __device__ __forceinline__ void load4(const void* p, int dt, long long i, float 
 
 __device__ __forceinline__ float sigmoid_f32(float s) { return 1.0f / (1.0f + expf(-s)); }
 
+
+// Float32 selection state of one token, held by one wave.
 template <int EPL>
-__global__ __launch_bounds__(256) void route_select_kernel(const RouteArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= a.T) return;                        // uniform per wave
+struct TokenSel {
+  float s[EPL], key[EPL];
+  bool taken[EPL];
+  int my_e;          // lane r < nsel: the r-th pick
+  float my_key;
+  float tau;
+  int nsel;
+};
+
+template <int EPL>
+__device__ __forceinline__ void select_f32(const RouteArgs& a, int t, int lane, TokenSel<EPL>& st) {
   const int E = a.E, k = a.k;
   const bool sig = a.scoring == SIGMOID_BIAS;
   const float* srow = a.logits + (long long)t * E;
-
-  float s[EPL], key[EPL];
-  bool taken[EPL];
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     const int e = lane + kWave * i;
     const bool valid = e < E;
-    s[i] = valid ? srow[e] : 0.0f;
+    st.s[i] = valid ? srow[e] : 0.0f;
     float q = -INFINITY;
-    if (valid) q = sig ? sigmoid_f32(s[i]) + (a.sel_bias ? a.sel_bias[e] : 0.0f) : s[i];
-    key[i] = q;
-    taken[i] = !valid;
-    amax = fmaxf(amax, fabsf(s[i]));
+    if (valid) q = sig ? sigmoid_f32(st.s[i]) + (a.sel_bias ? a.sel_bias[e] : 0.0f) : st.s[i];
+    st.key[i] = q;
+    st.taken[i] = !valid;
+    amax = fmaxf(amax, fabsf(st.s[i]));
   }
   amax = wave_max_f32(amax);
   // Margin on |float32 logit - exact logit|.  The logits come from float32
-  // sums of 64-deep slices added in float64, whose error is ~1e-7 at
+  // sums of 64-deep slices added in float64, whose error is ~1e-6 at
   // D = 7168; the margin is about two orders of magnitude above that.  It is
   // mapped onto the ranking key (sigmoid slope <= 1/4).
   const float eps_s = ldexpf(1.0f + amax, -16);
-  const float tau = sig ? 0.25f * eps_s + 1e-6f : eps_s;
-
-  // ---- k (+1) best keys; lane r keeps pick r.
-  const int nsel = min(k + 1, E);
-  int my_e = -1;
-  float my_key = -INFINITY;
-  for (int r = 0; r < nsel; ++r) {
+  st.tau = sig ? 0.25f * eps_s + 1e-6f : eps_s;
+  st.nsel = min(k + 1, E);
+  st.my_e = -1;
+  st.my_key = -INFINITY;
+  for (int r = 0; r < st.nsel; ++r) {
     float bv = -INFINITY;
     int be = INT_MAX;
 #pragma unroll
     for (int i = 0; i < EPL; ++i)
-      if (!taken[i] && (be == INT_MAX || key[i] > bv)) { bv = key[i]; be = lane + kWave * i; }
+      if (!st.taken[i] && (be == INT_MAX || st.key[i] > bv)) { bv = st.key[i]; be = lane + kWave * i; }
     wave_argmax(bv, be);
 #pragma unroll
     for (int i = 0; i < EPL; ++i)
-      if (lane + kWave * i == be) taken[i] = true;
-    if (lane == r) { my_e = be; my_key = bv; }
+      if (lane + kWave * i == be) st.taken[i] = true;
+    if (lane == r) { st.my_e = be; st.my_key = bv; }
   }
+}
 
-  // ---- near-tie refinement in float64
-  // Among the k+1 best keys, pick r is "close" to pick r+1 when their float32
-  // keys are within 2 tau.  Exactly the picks in a close run get float64
-  // keys; when the run reaches the k-th/(k+1)-th boundary, so does every
-  // other expert whose key lies within 2 tau below the k-th.  Ranking refined
-  // experts by their float64 key and all others by their float32 key then
-  // gives the order of the exact keys: any pair with an unrefined member is
-  // more than 2 tau apart, far beyond the error of either key.
-  const float next_key = __shfl_down(my_key, 1);
-  const bool close = (lane + 1 < nsel) && (my_key - next_key <= 2.0f * tau);
-  const unsigned long long close_mask = __ballot(close);
-  if (close_mask != 0) {
-    // pick r needs float64 when it is close to a neighbour
-    const bool prev_close = lane > 0 && ((close_mask >> (lane - 1)) & 1ull);
-    const bool pick_ref = lane < nsel && (close || prev_close);
-    const bool boundary = k < nsel && ((close_mask >> (k - 1)) & 1ull);
-    const float thr = __shfl(my_key, k - 1) - 2.0f * tau;
-    // per-expert flags: candidate (ranked at all) and refined (float64 key)
-    bool cand[EPL], ref[EPL];
-    double m64[EPL];
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      cand[i] = false;
-      ref[i] = false;
-      m64[i] = (double)key[i];
-    }
-    // the k+1 picks are candidates; publish which of them are refined
-    for (int r = 0; r < nsel; ++r) {
-      const int pe_r = __shfl(my_e, r);
-      const bool pr = __shfl((int)pick_ref, r) != 0;
-#pragma unroll
-      for (int i = 0; i < EPL; ++i)
-        if (lane + kWave * i == pe_r) { cand[i] = true; ref[i] = pr; }
-    }
-    if (boundary) {
-#pragma unroll
-      for (int i = 0; i < EPL; ++i)
-        if (lane + kWave * i < E && !cand[i] && key[i] >= thr) { cand[i] = true; ref[i] = true; }
-    }
-    // float64 logits of the refined experts, up to eight per pass over the
-    // token row (the loop is unrolled so several rows' loads are in flight)
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      unsigned long long m = __ballot(ref[i]);
-      while (m) {
-        constexpr int NB = 4;
-        int ce[NB];
-        int nb = 0;
-        for (; nb < NB && m; ++nb) {
-          const int l = __builtin_ctzll(m);
-          m &= m - 1;
-          ce[nb] = l + kWave * i;
-        }
-        for (int c = nb; c < NB; ++c) ce[c] = ce[0];
-        double acc[NB];
-#pragma unroll
-        for (int c = 0; c < NB; ++c) acc[c] = 0.0;
-        const long long xo = (long long)t * a.D;
+// Bit r set: picks r and r+1 are within 2 tau.
+template <int EPL>
+__device__ __forceinline__ unsigned long long close_mask(const TokenSel<EPL>& st, int lane) {
+  const float next_key = __shfl_down(st.my_key, 1);
+  return __ballot((lane + 1 < st.nsel) && (st.my_key - next_key <= 2.0f * st.tau));
+}
 
-        for (int d = lane * 4; d < a.D; d += kWave * 4) {
-          float xv[4];
-          load4(a.x, a.act_dtype, xo + d, xv);
-#pragma unroll
-          for (int c = 0; c < NB; ++c) {
-            float wv[4];
-            load4(a.w_router, a.router_dtype, (long long)ce[c] * a.D + d, wv);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) acc[c] = fma((double)xv[q], (double)wv[q], acc[c]);
-          }
-        }
-#pragma unroll
-        for (int c = 0; c < NB; ++c) {
-          if (c < nb) {
-            const double s64 = wave_sum_f64(acc[c]);
-            double q64 = s64;
-            if (sig) q64 = 1.0 / (1.0 + exp(-s64)) + (a.sel_bias ? (double)a.sel_bias[ce[c]] : 0.0);
-            if (lane == (ce[c] & 63)) m64[i] = q64;
-          }
-        }
-      }
-    }
-    // rank the candidates: k rounds of (key desc, expert asc)
-    bool tk[EPL];
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) tk[i] = !cand[i];
-    for (int r = 0; r < k; ++r) {
-      double bv = -INFINITY;
-      int be = INT_MAX;
-#pragma unroll
-      for (int i = 0; i < EPL; ++i)
-        if (!tk[i] && (be == INT_MAX || m64[i] > bv)) { bv = m64[i]; be = lane + kWave * i; }
-      wave_argmax(bv, be);
-#pragma unroll
-      for (int i = 0; i < EPL; ++i)
-        if (lane + kWave * i == be) tk[i] = true;
-      if (lane == r) my_e = be;
-    }
-  }
-
-  // ---- weights from the float32 logits
-  // s of this lane's pick (lanes r < k): fetch from the owner lane.
+// Combine weights from the float32 logits for the picks my_e of lanes < k,
+// written with the expert ids.
+template <int EPL>
+__device__ __forceinline__ void write_selection(const RouteArgs& a, int t, int lane, const TokenSel<EPL>& st,
+                                                int my_e) {
+  const int E = a.E, k = a.k;
+  const bool sig = a.scoring == SIGMOID_BIAS;
   const int pe = (lane < k) ? my_e : 0;
   float s_pick = 0.0f;
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
-    const float v = __shfl(s[i], pe & 63);
+    const float v = __shfl(st.s[i], pe & 63);
     if ((pe >> 6) == i) s_pick = v;
   }
   const bool slot = lane < k;
   float w = 0.0f;
-  float smax = -INFINITY, z = 0.0f;
-  if (a.scoring == SOFTMAX_TOPK || a.probs != nullptr) {
+  if (a.scoring == SOFTMAX_TOPK) {
     float m = -INFINITY;
 #pragma unroll
     for (int i = 0; i < EPL; ++i)
-      if (lane + kWave * i < E) m = fmaxf(m, sig ? -INFINITY : s[i]);
-    smax = wave_max_f32(m);
-  }
-  if (a.scoring == SOFTMAX_TOPK) {
+      if (lane + kWave * i < E) m = fmaxf(m, st.s[i]);
+    const float smax = wave_max_f32(m);
     float zz = 0.0f;
 #pragma unroll
     for (int i = 0; i < EPL; ++i)
-      if (lane + kWave * i < E) zz += expf(s[i] - smax);
-    z = wave_sum_f32(zz);
+      if (lane + kWave * i < E) zz += expf(st.s[i] - smax);
+    const float z = wave_sum_f32(zz);
     const float p = slot ? expf(s_pick - smax) / z : 0.0f;
-    if (a.renormalize) {
-      const float ps = wave_sum_f32(p);
-      w = p / ps;
-    } else {
-      w = p;
-    }
+    w = a.renormalize ? p / wave_sum_f32(p) : p;
   } else if (a.scoring == TOPK_SOFTMAX) {
     const float msel = wave_max_f32(slot ? s_pick : -INFINITY);
     const float ex = slot ? expf(s_pick - msel) : 0.0f;
     w = ex / wave_sum_f32(ex);
   } else {
+    (void)sig;
     const float af = slot ? sigmoid_f32(s_pick) : 0.0f;
     w = a.renormalize ? af / wave_sum_f32(af) : af;
   }
@@ -256,15 +170,29 @@ __global__ __launch_bounds__(256) void route_select_kernel(const RouteArgs a) {
     a.topk_idx[(long long)t * k + lane] = my_e;
     a.topk_w[(long long)t * k + lane] = w;
   }
+}
 
-  // ---- per-token soft probabilities for the balance loss
+// Pass 1: float32 selection of every token, the per-token probabilities, and
+// a flag for the tokens that need float64 (rewritten by pass 2).
+template <int EPL>
+__global__ __launch_bounds__(256) void route_select_kernel(const RouteArgs a, int32_t* __restrict__ flags) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;                        // uniform per wave
+  const int E = a.E;
+  TokenSel<EPL> st;
+  select_f32(a, t, lane, st);
+  const unsigned long long cm = close_mask(st, lane);
+  if (lane == 0) flags[t] = cm != 0;
+  write_selection(a, t, lane, st, st.my_e);
+
   if (a.probs != nullptr) {
     float* prow = a.probs + (long long)t * E;
-    if (sig) {
+    if (a.scoring == SIGMOID_BIAS) {
       float av[EPL], as = 0.0f;
 #pragma unroll
       for (int i = 0; i < EPL; ++i) {
-        av[i] = (lane + kWave * i < E) ? sigmoid_f32(s[i]) : 0.0f;
+        av[i] = (lane + kWave * i < E) ? sigmoid_f32(st.s[i]) : 0.0f;
         as += av[i];
       }
       as = wave_sum_f32(as);
@@ -272,36 +200,122 @@ __global__ __launch_bounds__(256) void route_select_kernel(const RouteArgs a) {
       for (int i = 0; i < EPL; ++i)
         if (lane + kWave * i < E) prow[lane + kWave * i] = av[i] / as;
     } else {
-      if (a.scoring != SOFTMAX_TOPK) {
-        float zz = 0.0f;
-#pragma unroll
-        for (int i = 0; i < EPL; ++i)
-          if (lane + kWave * i < E) zz += expf(s[i] - smax);
-        z = wave_sum_f32(zz);
-      }
+      float m = -INFINITY;
 #pragma unroll
       for (int i = 0; i < EPL; ++i)
-        if (lane + kWave * i < E) prow[lane + kWave * i] = expf(s[i] - smax) / z;
+        if (lane + kWave * i < E) m = fmaxf(m, st.s[i]);
+      const float smax = wave_max_f32(m);
+      float zz = 0.0f;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (lane + kWave * i < E) zz += expf(st.s[i] - smax);
+      const float z = wave_sum_f32(zz);
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (lane + kWave * i < E) prow[lane + kWave * i] = expf(st.s[i] - smax) / z;
     }
   }
 }
 
+// Pass 2: one wavefront per flagged token (all other waves exit at once).  It
+// redoes the float32 selection, computes float64 logits for the experts that
+// need them (a D-long dot product of the stored inputs each, loads unrolled
+// ahead), ranks the candidates and rewrites the token's selection.
 template <int EPL>
-hipError_t launch_epl(const RouteArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(route_select_kernel<EPL>, dim3(ceil_div(a.T, 4)), dim3(256), 0, s, a);
+__global__ __launch_bounds__(256) void route_refine_kernel(const RouteArgs a, const int32_t* __restrict__ flags) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.T || flags[t] == 0) return;       // uniform per wave
+  const bool sig = a.scoring == SIGMOID_BIAS;
+  TokenSel<EPL> st;
+  select_f32(a, t, lane, st);
+  const unsigned long long cm = close_mask(st, lane);
+  const bool cl = (cm >> lane) & 1ull;
+  const bool prev_close = lane > 0 && ((cm >> (lane - 1)) & 1ull);
+  const bool pick_ref = lane < st.nsel && (cl || prev_close);
+  const bool boundary = a.k < st.nsel && ((cm >> (a.k - 1)) & 1ull);
+  const float thr = __shfl(st.my_key, a.k - 1) - 2.0f * st.tau;
+  bool cand[EPL], ref[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) { cand[i] = false; ref[i] = false; }
+  for (int r = 0; r < st.nsel; ++r) {
+    const int pe_r = __shfl(st.my_e, r);
+    const bool pr = __shfl((int)pick_ref, r) != 0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (lane + kWave * i == pe_r) { cand[i] = true; ref[i] = pr; }
+  }
+  if (boundary) {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (lane + kWave * i < a.E && !cand[i] && st.key[i] >= thr) { cand[i] = true; ref[i] = true; }
+  }
+  double m64[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) m64[i] = (double)st.key[i];
+  const long long xo = (long long)t * a.D;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    unsigned long long m = __ballot(ref[i]);
+    while (m) {
+      const int l = __builtin_ctzll(m);
+      m &= m - 1;
+      const int e = l + kWave * i;
+      const long long wo = (long long)e * a.D;
+      double acc = 0.0;
+#pragma unroll 8
+      for (int d = lane * 4; d < a.D; d += kWave * 4) {
+        float xv[4], wv[4];
+        load4(a.x, a.act_dtype, xo + d, xv);
+        load4(a.w_router, a.router_dtype, wo + d, wv);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = fma((double)xv[j], (double)wv[j], acc);
+      }
+      const double s64 = wave_sum_f64(acc);
+      double q64 = s64;
+      if (sig) q64 = 1.0 / (1.0 + exp(-s64)) + (a.sel_bias ? (double)a.sel_bias[e] : 0.0);
+      if (lane == l) m64[i] = q64;
+    }
+  }
+  bool tk[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) tk[i] = !cand[i];
+  int my_e = -1;
+  for (int r = 0; r < a.k; ++r) {
+    double bv = -INFINITY;
+    int be = INT_MAX;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (!tk[i] && (be == INT_MAX || m64[i] > bv)) { bv = m64[i]; be = lane + kWave * i; }
+    wave_argmax(bv, be);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (lane + kWave * i == be) tk[i] = true;
+    if (lane == r) my_e = be;
+  }
+  write_selection(a, t, lane, st, my_e);
+}
+
+template <int EPL>
+hipError_t launch_epl(const RouteArgs& a, int32_t* flags, hipStream_t s) {
+  hipLaunchKernelGGL(route_select_kernel<EPL>, dim3(ceil_div(a.T, 4)), dim3(256), 0, s, a, flags);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(route_refine_kernel<EPL>, dim3(ceil_div(a.T, 4)), dim3(256), 0, s, a,
+                     (const int32_t*)flags);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_route_select(const RouteArgs& a, hipStream_t s) {
+hipError_t launch_route_select(const RouteArgs& a, int32_t* flags, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   const int epl = ceil_div(a.E, kWave);
-  if (epl <= 1) return launch_epl<1>(a, s);
-  if (epl <= 2) return launch_epl<2>(a, s);
-  if (epl <= 4) return launch_epl<4>(a, s);
-  if (epl <= 8) return launch_epl<8>(a, s);
-  return launch_epl<16>(a, s);
+  if (epl <= 1) return launch_epl<1>(a, flags, s);
+  if (epl <= 2) return launch_epl<2>(a, flags, s);
+  if (epl <= 4) return launch_epl<4>(a, flags, s);
+  if (epl <= 8) return launch_epl<8>(a, flags, s);
+  return launch_epl<16>(a, flags, s);
 }
 
 }  // namespace moe
