@@ -11,6 +11,7 @@ the CPU oracle timed on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -28,6 +29,12 @@ import workloads as W  # noqa: E402
 HBM_GBPS = 8000.0
 MFMA_BF16_TFLOPS = 2500.0
 VALU_F32_TFLOPS = 78.6       # FMA without packed-FP32 instructions: 256 CU x 64 lanes x 2 x 2.4 GHz
+
+# Files whose change invalidates HBM-traffic counters taken earlier: the GEMM
+# kernels, their launch planning and the synthetic workload recipe.
+TRAFFIC_SOURCES = ("top_routing_dispatch_amd/csrc/common.h", "top_routing_dispatch_amd/csrc/gemm_v2.hip",
+                   "top_routing_dispatch_amd/csrc/gemm.hip", "top_routing_dispatch_amd/csrc/api.hip",
+                   "workloads/__init__.py")
 
 DEFAULT_CPU_SAMPLE = {"tiny": 64, "switch": 8192, "mixtral": 256, "deepseekmoe": 1024, "deepseekv3": 64}
 
@@ -81,6 +88,55 @@ def roofline_of(cfg, stage, flops, nbytes, ms):
                 frac=round(achieved / HBM_GBPS, 4))
 
 
+def sources_digest():
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(workload, stage):
+    return os.path.join(ROOT, "profiles", f"{stage}_{workload}_hbm_traffic.md")
+
+
+def measured_traffic(workload, stage):
+    """HBM bytes per launch of `stage`'s kernel from the committed FETCH_SIZE /
+    WRITE_SIZE summary, or None when there is none or the kernel sources have
+    changed since the counters were taken."""
+    path = traffic_file(workload, stage)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for ln in f:
+            if ":" in ln and not ln.startswith(("#", "|", " ", "`")):
+                key, val = ln.split(":", 1)
+                kv[key.strip()] = val.strip()
+    if kv.get("sources_digest") != sources_digest():
+        log(f"[bench] {os.path.basename(path)} is stale (kernel sources changed): traffic = null")
+        return None
+    try:
+        return int(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(mib, reps):
+    """A plain streaming copy of known size (torch.neg on float32, out of place)
+    for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "kernel": "torch.neg float32", "bytes_read": 4 * n,
+                      "bytes_written": 4 * n, "launches": reps}), flush=True)
+
+
 def cpu_baseline(cfg, inp, sample_tokens):
     """The oracle as it stands, on the first `sample_tokens` tokens."""
     from oracle import moe_oracle as O
@@ -110,11 +166,17 @@ def main():
     ap.add_argument("--config", default="switch", choices=sorted(W.CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=None)
+    ap.add_argument("--copy-calibration", type=int, default=None, metavar="MIB",
+                    help="only run a plain copy of MIB MiB --steps times (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, args.steps)
+        return
 
     import torch
     import top_routing_dispatch_amd as M
@@ -174,6 +236,8 @@ def main():
     stage_ms = {}
     c_host = counts.cpu().numpy()
     for si, name in enumerate(M.STAGES):
+        if name.startswith("shared") and cfg.num_shared == 0:
+            continue            # no kernels: the events only hold their creation-time records
         vals = []
         for evs in events:
             try:
@@ -195,7 +259,7 @@ def main():
     fl, by = stage_work(cfg, dominant, A, E_act, T)
     roof = roofline_of(cfg, dominant, fl, by, stage_ms[dominant])
     roof["kernel"] = dominant
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(cfg.name, dominant)
 
     cpu = None
     if not args.no_cpu_baseline:
