@@ -308,7 +308,11 @@ V2_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("gemm_cfg", [str(c) for c in range(-1, 10)])
+# -1: general kernel; 0-9: pipelined 8-wave kernel; 10-24: kernel with 32- or 64-deep slices
+GEMM_TILE_CONFIGS = range(-1, 25)
+
+
+@pytest.mark.parametrize("gemm_cfg", [str(c) for c in GEMM_TILE_CONFIGS])
 @pytest.mark.parametrize("cfg", V2_SHAPES, ids=lambda c: c.name)
 def test_every_gemm_tile_config(cfg, gemm_cfg, monkeypatch):
     """Each tile configuration of the pipelined expert GEMM (K a multiple of 64)

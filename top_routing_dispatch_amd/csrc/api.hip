@@ -203,14 +203,14 @@ int pick_cfg(int act, int K, int max_rows, int G) {
   const char* env = getenv("MOE_GEMM_CFG");
   if (env != nullptr && *env != '\0') {
     const int c = atoi(env);
-    return (c >= -1 && c < kGemmV2Configs) ? c : -1;
+    return (c >= -1 && c < kGemmConfigs) ? c : -1;
   }
   // measured on MI355X at the Switch / Mixtral / DeepSeekMoE / DeepSeek-V3
-  // shapes: 256x256 tiles on 8 waves once groups are a few hundred rows deep,
-  // 128x128 tiles with two workgroups per CU for shallow (weight-streaming)
-  // groups
+  // shapes: 256x256 tiles on 8 waves (64-deep slices, interleaved schedule)
+  // once groups are a few hundred rows deep, 128x128 tiles with 32-deep
+  // slices and two workgroups per CU for shallow (weight-streaming) groups
   const int avg = G > 0 ? max_rows / G : max_rows;
-  return avg >= 160 ? 4 : 7;
+  return kGemmV2Configs + (avg >= 160 ? 6 : 12);
 }
 
 int cfg_bm(int act, int cfg) {
@@ -219,7 +219,7 @@ int cfg_bm(int act, int cfg) {
     GroupedGemm dummy{};
     return gemm_bf16_bm(dummy);
   }
-  return gemm_v2_bm(cfg);
+  return cfg < kGemmV2Configs ? gemm_v2_bm(cfg) : gemm_v3_bm(cfg - kGemmV2Configs);
 }
 
 struct FfnPlan {
@@ -237,6 +237,7 @@ FfnPlan plan_ffn(int act, int D, int F, int max_rows, int G) {
 
 hipError_t launch_gemm(int act, int cfg, const GroupedGemm& g, hipStream_t s) {
   if (act != BF16) return launch_gemm_f32(g, F32, F32, s);
+  if (cfg >= kGemmV2Configs) return launch_gemm_v3(g, cfg - kGemmV2Configs, s);
   if (cfg >= 0) return launch_gemm_v2(g, cfg, s);
   return launch_gemm_bf16(g, s);
 }

@@ -57,7 +57,9 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   return xcd * per + (xcd < rem ? xcd : rem) + local;
 }
 
-__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+// silu(z) = z * sigmoid(z); the reciprocal is the hardware one (1 ulp), which
+// keeps the result within a few ulp of the float32 quotient.
+__device__ __forceinline__ float silu_f32(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 __device__ __forceinline__ float gelu_erf_f32(float z) {
   return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
 }
@@ -156,6 +158,13 @@ int gemm_bf16_bm(const GroupedGemm& g);
 constexpr int kGemmV2Configs = 10;
 hipError_t launch_gemm_v2(const GroupedGemm& g, int cfg, hipStream_t s);
 int gemm_v2_bm(int cfg);
+// bf16 grouped GEMM with 128x128 wave tiles, one wave per SIMD (K % 32 == 0,
+// K % 64 == 0 for the 64-deep configuration).  Its tile configurations follow
+// the pipelined kernel's in one numbering: kGemmV2Configs + cfg.
+constexpr int kGemmV3Configs = 15;
+constexpr int kGemmConfigs = kGemmV2Configs + kGemmV3Configs;
+hipError_t launch_gemm_v3(const GroupedGemm& g, int cfg, hipStream_t s);
+int gemm_v3_bm(int cfg);
 // float32 SIMT grouped GEMM.  a_dtype / b_dtype select float32 or bf16 operands.
 hipError_t launch_gemm_f32(const GroupedGemm& g, int a_dtype, int b_dtype, hipStream_t s);
 constexpr int kF32GemmBM = 64;

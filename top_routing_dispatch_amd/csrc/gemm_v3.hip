@@ -1,0 +1,401 @@
+// bf16 grouped GEMM with one wavefront per SIMD and 128x128 wave tiles, for
+// the deep expert FFN shapes (K a multiple of BK).
+//
+// C[r, n] = sum_k A[r, k] * B_g[n, k] for the rows r of group g, with the tile
+// scheduler and epilogues of gemm.hip.  Differences from the 8-wave kernel:
+//   * four waves per workgroup, each owning a 128x128 block of C (4x4 MFMA
+//     32x32x16 blocks, accumulators in the AGPR half of the register file):
+//     every fragment read from LDS feeds four MFMAs, which keeps LDS traffic
+//     (fragment reads plus the DMA writes) below what the LDS port delivers
+//     while the matrix cores run at full rate;
+//   * K-slices of BK (32 or 64) elements in an NST-deep LDS ring: with BK=32
+//     the ring holds four or five slices of a 256x256 tile, so three or four
+//     refills are in flight behind the slice being multiplied;
+//   * a wave skips the MFMAs and fragment reads of 32-row blocks that lie past
+//     the tile's last row (groups of a few rows pay only for the weight
+//     stream, not for MFMAs on padding).
+// LDS rows are BK*2 bytes; the 16-byte chunk c of row r sits in slot
+// c ^ ((r / (16 / CPR)) % CPR) (CPR chunks per row), so that the 16 rows read
+// by one pass of a fragment load cover all 64 banks once.
+#include "common.h"
+
+#include <type_traits>
+
+namespace moe {
+namespace {
+
+template <int BM, int BN, int WGM, int WGN, int BK, int NST>
+struct Cfg3 {
+  static constexpr int THREADS = 64 * WGM * WGN;
+  static constexpr int NWAVES = WGM * WGN;
+  static constexpr int WM = BM / WGM, WN = BN / WGN;     // wave tile
+  static constexpr int TM = WM / 32, TN = WN / 32;       // 32x32 MFMA blocks per wave
+  static constexpr int RB = BK * 2;                      // bytes per LDS row
+  static constexpr int CPR = BK / 8;                     // 16-byte chunks per row
+  static constexpr int RPI = 1024 / RB;                  // rows per 1 KB load instruction
+  static constexpr int KK = BK / 16;                     // MFMA k-steps per slice
+  static constexpr int A_BYTES = BM * RB, B_BYTES = BN * RB;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int A_INS = BM / RPI / NWAVES;        // load instructions per wave per slice
+  static constexpr int B_INS = BN / RPI / NWAVES;
+  static constexpr int INS = A_INS + B_INS;
+  static_assert(BK == 32 || BK == 64, "slice depth");
+  static_assert(KK % 2 == 0, "fragment double buffering alternates per k-step");
+  static_assert(BM % (RPI * NWAVES) == 0 && BN % (RPI * NWAVES) == 0, "load split");
+  static_assert(TM >= 1 && TN >= 1, "wave tile");
+  static_assert(STAGE * NST <= 160 * 1024, "LDS");
+  static_assert(INS * (NST - 2) <= 63, "vmcnt range");
+};
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc3(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// 16 bytes per lane, buffer -> LDS: lane i lands at lds + 16 * i.
+__device__ __forceinline__ void dma16_3(__amdgpu_buffer_rsrc_t r, unsigned voff, char* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int CPR>
+__device__ __forceinline__ int swz3(int r, int c) {
+  return r * (CPR * 16) + ((c ^ ((r / (16 / CPR)) & (CPR - 1))) << 4);
+}
+
+template <int BM, int BN, int WGM, int WGN, int BK, int NST, int SP, int OCC, int EPI, typename OutT>
+__global__ __launch_bounds__(64 * WGM * WGN)
+__attribute__((amdgpu_waves_per_eu(WGM * WGN / 4 * OCC, WGM * WGN / 4 * OCC)))
+void gemm_v3_kernel(const GroupedGemm p, int n_tiles) {
+  using C = Cfg3<BM, BN, WGM, WGN, BK, NST>;
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / WGN, wn = wave % WGN;
+
+  int g, row0, rows, nt;
+  if (!map_tile<BM>(p, n_tiles, g, row0, rows, nt)) return;
+  // 32-row blocks of this wave that hold at least one row of the tile
+  const int act_i = min(C::TM, max(0, ceil_div(rows - wm * C::WM, 32)));
+
+  const int K = p.K;
+  const bf16_t* __restrict__ A = static_cast<const bf16_t*>(p.A);
+  const bf16_t* __restrict__ B = static_cast<const bf16_t*>(p.B) + (long long)g * p.b_group_stride;
+
+  // Byte offsets of this wave's load instructions (rows past the tile end
+  // clamped to a valid row: their outputs are never stored).
+  const int lrow = lane / C::CPR;
+  const int lslot = lane % C::CPR;
+  const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc3(A, 0xffffffffu);
+  const int b_rows = (EPI == EPI_SWIGLU) ? 2 * p.N : p.N;
+  const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc3(B, (unsigned)b_rows * (unsigned)K * 2u);
+  unsigned a_off[C::A_INS], b_off[C::B_INS];
+#pragma unroll
+  for (int q = 0; q < C::A_INS; ++q) {
+    const int r = (wave * C::A_INS + q) * C::RPI + lrow;
+    const int rr = r < rows ? r : rows - 1;
+    const unsigned src = p.a_rows ? (unsigned)p.a_rows[row0 + rr] : (unsigned)(row0 + rr);
+    const int c = lslot ^ ((r / (16 / C::CPR)) & (C::CPR - 1));
+    a_off[q] = (src * (unsigned)p.lda + c * 8) * 2u;
+  }
+#pragma unroll
+  for (int q = 0; q < C::B_INS; ++q) {
+    const int r = (wave * C::B_INS + q) * C::RPI + lrow;
+    int brow;
+    if constexpr (EPI == EPI_SWIGLU) {
+      // 32-row sub-tiles alternate gate / up rows of the same hidden columns
+      const int s = r >> 5, wc = s / C::TN, ls = s % C::TN;
+      int h = nt * (BN / 2) + (wc * (C::TN / 2) + (ls >> 1)) * 32 + (r & 31);
+      h = h < p.N ? h : p.N - 1;
+      brow = (ls & 1) ? p.N + h : h;
+    } else {
+      const int n = nt * BN + r;
+      brow = n < p.N ? n : p.N - 1;
+    }
+    const int c = lslot ^ ((r / (16 / C::CPR)) & (C::CPR - 1));
+    b_off[q] = ((unsigned)brow * (unsigned)K + c * 8) * 2u;
+  }
+
+  // Load instruction q of a refill (A rows first, then B rows).
+  auto dma_one = [&](int q, char* st, unsigned kb) __attribute__((always_inline)) {
+    if (q < C::A_INS) dma16_3(a_rsrc, a_off[q] + kb, st + (wave * C::A_INS + q) * 1024);
+    else dma16_3(b_rsrc, b_off[q - C::A_INS] + kb, st + C::A_BYTES + (wave * C::B_INS + q - C::A_INS) * 1024);
+  };
+
+  floatx16_t acc[C::TM][C::TN];
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // The ring always advances by one slice per slice consumed: past the last
+  // slice, a refill loads the last slice again into the slot just released,
+  // which no remaining slice uses.  Every wait then leaves exactly the loads
+  // of the NST-2 younger slices outstanding.
+  const int nk = K / BK;
+#pragma unroll
+  for (int st = 0; st < NST - 1; ++st) {
+#pragma unroll
+    for (int q = 0; q < C::INS; ++q) dma_one(q, smem + st * C::STAGE, min(st, nk - 1) * (unsigned)C::RB);
+  }
+  // Slice kt has landed for every wave, and every wave is done with the slot
+  // refilled next.
+  auto slice_ready = [&]() __attribute__((always_inline)) {
+    wait_vm<C::INS * (NST - 2)>();
+    __builtin_amdgcn_s_barrier();
+  };
+
+  const int fr = lane & 31;              // fragment row inside a 32-row block
+  const int fc = lane >> 5;              // which 8-wide half of a 16-deep step
+  bf16x8_t af[2][C::TM], bfv[2][C::TN];
+
+  // With SP > 0 a refill's load instructions are spread between the MFMAs of
+  // the slice's first SP steps (load q follows MFMA block `at`), otherwise
+  // they are issued together at the start of the slice.
+  static_assert(SP >= 0 && SP <= C::KK - 1, "refill loads go out before the next slice's wait");
+  constexpr int MF = C::TM * C::TN;
+  constexpr int SPAN = (SP > 0 ? SP : 1) * MF;
+
+  // FULL: every 32-row block of the wave holds rows of the tile.  Its steps
+  // are straight-line code, and each step's fragment reads for the next step
+  // (and its refill loads) are placed one after each MFMA, so that they issue
+  // while the matrix core works instead of in a burst that leaves it idle.
+  auto k_loop = [&](auto full_c) __attribute__((always_inline)) {
+    constexpr bool FULL = decltype(full_c)::value;
+    // Fragment reads in the order of first use by the MFMAs (block row i,
+    // then column j): A0, B0..B(TN-1), A1, ..., A(TM-1).
+    auto load_frags = [&](int buf, int slot, int kk) __attribute__((always_inline)) {
+      const char* sa = smem + slot * C::STAGE;
+      const char* sb = sa + C::A_BYTES;
+      const int ch = kk * 2 + fc;
+      af[buf][0] = *reinterpret_cast<const bf16x8_t*>(sa + swz3<C::CPR>(wm * C::WM + fr, ch));
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j)
+        bfv[buf][j] = *reinterpret_cast<const bf16x8_t*>(sb + swz3<C::CPR>(wn * C::WN + j * 32 + fr, ch));
+#pragma unroll
+      for (int i = 1; i < C::TM; ++i)
+        if (FULL || i < act_i)
+          af[buf][i] = *reinterpret_cast<const bf16x8_t*>(sa + swz3<C::CPR>(wm * C::WM + i * 32 + fr, ch));
+    };
+    // MFMAs of one 16-deep step on fragment buffer `buf`, with the refill
+    // loads that belong to step kk.
+    auto mfma_step = [&](int buf, int kk, char* st, unsigned kb) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i) {
+        if (FULL || i < act_i) {
+#pragma unroll
+          for (int j = 0; j < C::TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][i], bfv[buf][j], acc[i][j], 0, 0, 0);
+        }
+        if (SP > 0 && kk < SP) {
+#pragma unroll
+          for (int q = 0; q < C::INS; ++q)
+            if ((q * SPAN / C::INS) / C::TN == kk * C::TM + i) dma_one(q, st, kb);
+        }
+      }
+    };
+    // Instruction order of one straight-line step: MFMA m is followed by the
+    // reads r with r * MF / NR == m and the loads d with d * MF / ND == m.
+    auto interleave = [&](int kk, bool reads, bool refill_here) __attribute__((always_inline)) {
+      if constexpr (FULL) {
+        constexpr int NR = C::TM + C::TN;
+        int nd = 0;
+        if (refill_here) {
+          if (SP == 0) nd = C::INS;
+          else {
+#pragma unroll
+            for (int q = 0; q < C::INS; ++q)
+              if ((q * SPAN / C::INS) / MF == kk) ++nd;
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < MF; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
+          if (reads) {
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+              if (r * MF / NR == m) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+          }
+#pragma unroll
+          for (int d = 0; d < C::INS; ++d)
+            if (d < nd && d * MF / nd == m) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one VMEM load
+        }
+      }
+    };
+    // One slice: refill, KK-1 steps that also read the next step's fragments,
+    // then (unless it is the last slice) the hand-over to the next slice and
+    // the last step.
+    auto slice = [&](int kt, bool last) __attribute__((always_inline)) {
+      const int slot = kt % NST;
+      char* rst = smem + ((kt + NST - 1) % NST) * C::STAGE;
+      const unsigned rkb = min(kt + NST - 1, nk - 1) * (unsigned)C::RB;
+      if (SP == 0) {
+#pragma unroll
+        for (int q = 0; q < C::INS; ++q) dma_one(q, rst, rkb);
+      }
+#pragma unroll
+      for (int kk = 0; kk < C::KK - 1; ++kk) {
+        load_frags((kk + 1) & 1, slot, kk + 1);
+        mfma_step(kk & 1, kk, rst, rkb);
+        interleave(kk, true, kk == 0 || SP > 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // the last step's fragments are in registers before the slot is handed
+      // back; the next slice's first fragments are read while this slice's
+      // last MFMAs run
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (!last) {
+        slice_ready();
+        load_frags(0, (kt + 1) % NST, 0);
+      }
+      mfma_step(1, C::KK - 1, rst, rkb);
+      interleave(C::KK - 1, !last, false);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    slice_ready();
+    load_frags(0, 0, 0);
+    for (int kt = 0; kt < nk - 1; ++kt) slice(kt, false);
+    slice(nk - 1, true);
+  };
+  if (act_i == C::TM) k_loop(std::true_type{});
+  else k_loop(std::false_type{});
+  wait_vm<0>();   // the ring's last loads land before the workgroup's LDS is released
+
+  // Epilogue: the activation is applied in registers, each wave's output
+  // block goes to its own LDS region and is read back as 16-byte row chunks
+  // for full-width global stores.  One LDS write instruction covers rows r and
+  // r+4; they land on different banks through a 16-byte row pad, or, where the
+  // padded block does not fit, by swapping the 64-byte halves of rows with
+  // bit 2 of the row index set.
+  static_assert(sizeof(OutT) == 2, "16-bit outputs");
+  constexpr int OC = (EPI == EPI_SWIGLU) ? C::WN / 2 : C::WN;   // output columns per wave
+  constexpr bool PAD = C::NWAVES * C::WM * (OC * 2 + 16) <= C::STAGE * NST;
+  constexpr int PITCH = OC * 2 + (PAD ? 16 : 0);
+  static_assert(C::NWAVES * C::WM * PITCH <= C::STAGE * NST, "output staging fits in the ring");
+  static_assert(PAD || (OC * 2) % 128 == 0, "half swap needs rows of whole 128-byte pairs");
+  auto sbyte = [](int row, int byte) { return PAD ? byte : (byte ^ (((row >> 2) & 1) << 6)); };
+  __builtin_amdgcn_s_barrier();          // every wave is done with the ring
+  char* stg = smem + wave * (C::WM * PITCH);
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i) {
+    if (i >= act_i) continue;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      char* srow = stg + row * PITCH;
+      if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+        for (int q = 0; q < C::TN / 2; ++q)
+          *reinterpret_cast<bf16_t*>(srow + sbyte(row, q * 64 + (lane & 31) * 2)) =
+              f32_to_bf16(silu_f32(acc[i][2 * q][r]) * acc[i][2 * q + 1][r]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) {
+          float v = acc[i][j][r];
+          if constexpr (EPI == EPI_GELU) v = gelu_erf_f32(v);
+          *reinterpret_cast<bf16_t*>(srow + sbyte(row, j * 64 + (lane & 31) * 2)) = f32_to_bf16(v);
+        }
+      }
+    }
+  }
+  constexpr int CPO = OC / 8;            // 16-byte chunks per output row
+  constexpr int RPO = 64 / CPO;          // rows per pass of the wave
+  static_assert(64 % CPO == 0 && C::WM % RPO == 0, "store passes");
+  OutT* __restrict__ Cout = static_cast<OutT*>(p.C);
+  const int col0 = (EPI == EPI_SWIGLU) ? nt * (BN / 2) + wn * OC : nt * BN + wn * OC;
+  const int rows_w = min(C::WM, rows - wm * C::WM);   // this wave's rows inside the tile
+  const bool vec = (p.ldc % 8 == 0) && ((reinterpret_cast<uintptr_t>(p.C) & 15) == 0);
+  const int ch = lane % CPO;
+  const int n = col0 + ch * 8;
+#pragma unroll
+  for (int ps = 0; ps < C::WM / RPO; ++ps) {
+    const int rr = ps * RPO + lane / CPO;
+    if (rr < rows_w) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + rr * PITCH + sbyte(rr, ch * 16));
+      OutT* dst = Cout + (long long)(row0 + wm * C::WM + rr) * p.ldc + n;
+      if (vec && n + 8 <= p.N) {
+        *reinterpret_cast<u32x4_t*>(dst) = v;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (n + e < p.N) dst[e] = static_cast<OutT>((v[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+      }
+    }
+  }
+}
+
+inline int m_bound3(const GroupedGemm& p, int bm) {
+  if (p.offsets == nullptr) return ceil_div(p.M_max, bm);
+  return p.M_max / bm + (p.G < p.M_max ? p.G : p.M_max);
+}
+
+template <int BM, int BN, int WGM, int WGN, int BK, int NST, int SP, int OCC, int EPI>
+hipError_t launch_cfg3(const GroupedGemm& p, hipStream_t s) {
+  using C = Cfg3<BM, BN, WGM, WGN, BK, NST>;
+  if (p.K % BK != 0) return hipErrorInvalidValue;
+  const int cols = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
+  const int n_tiles = ceil_div(p.N, cols);
+  const int m_tiles = m_bound3(p, BM);
+  if (m_tiles == 0 || n_tiles == 0) return hipSuccess;
+  const long long blocks = (long long)m_tiles * n_tiles;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  // dynamic LDS above 64 KB has to be allowed explicitly
+  hipError_t e = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&gemm_v3_kernel<BM, BN, WGM, WGN, BK, NST, SP, OCC, EPI, bf16_t>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, C::STAGE * NST);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((gemm_v3_kernel<BM, BN, WGM, WGN, BK, NST, SP, OCC, EPI, bf16_t>), dim3((unsigned)blocks),
+                     dim3(C::THREADS), C::STAGE * NST, s, p, n_tiles);
+  return hipGetLastError();
+}
+
+template <int EPI>
+hipError_t launch_v3_epi(const GroupedGemm& p, int cfg, hipStream_t s) {
+  switch (cfg) {
+    // one workgroup per CU
+    case 0: return launch_cfg3<256, 256, 2, 2, 32, 4, 0, 1, EPI>(p, s);
+    case 1: return launch_cfg3<256, 256, 2, 2, 32, 5, 0, 1, EPI>(p, s);
+    case 2: return launch_cfg3<256, 256, 2, 2, 64, 2, 0, 1, EPI>(p, s);
+    case 3: return launch_cfg3<128, 256, 1, 4, 32, 4, 0, 1, EPI>(p, s);
+    case 4: return launch_cfg3<256, 256, 2, 4, 32, 4, 0, 1, EPI>(p, s);
+    case 5: return launch_cfg3<256, 256, 2, 4, 32, 5, 0, 1, EPI>(p, s);
+    case 6: return launch_cfg3<256, 256, 2, 4, 64, 2, 0, 1, EPI>(p, s);
+    case 7: return launch_cfg3<256, 256, 2, 4, 32, 4, 1, 1, EPI>(p, s);
+    case 8: return launch_cfg3<256, 256, 2, 2, 32, 4, 1, 1, EPI>(p, s);
+    case 9: return launch_cfg3<256, 256, 2, 4, 64, 2, 1, 1, EPI>(p, s);
+    case 10: return launch_cfg3<256, 256, 2, 4, 64, 2, 3, 1, EPI>(p, s);
+    // two workgroups per CU (<= 80 KB of LDS each)
+    case 11: return launch_cfg3<128, 128, 2, 2, 64, 2, 0, 2, EPI>(p, s);
+    case 12: return launch_cfg3<128, 128, 2, 2, 32, 4, 0, 2, EPI>(p, s);
+    case 13: return launch_cfg3<128, 256, 2, 2, 32, 3, 0, 2, EPI>(p, s);
+    case 14: return launch_cfg3<64, 256, 1, 4, 32, 4, 0, 2, EPI>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int gemm_v3_bm(int cfg) {
+  static const int bm[] = {256, 256, 256, 128, 256, 256, 256, 256, 256, 256, 256, 128, 128, 128, 64};
+  return (cfg >= 0 && cfg < kGemmV3Configs) ? bm[cfg] : 0;
+}
+
+hipError_t launch_gemm_v3(const GroupedGemm& p, int cfg, hipStream_t s) {
+  switch (p.epilogue) {
+    case EPI_STORE_ACT: return launch_v3_epi<EPI_STORE_ACT>(p, cfg, s);
+    case EPI_SWIGLU: return launch_v3_epi<EPI_SWIGLU>(p, cfg, s);
+    case EPI_GELU: return launch_v3_epi<EPI_GELU>(p, cfg, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moe
