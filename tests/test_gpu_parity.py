@@ -308,8 +308,9 @@ V2_SHAPES = [
 ]
 
 
-# -1: general kernel; 0-9: pipelined 8-wave kernel; 10-24: kernel with 32- or 64-deep slices
-GEMM_TILE_CONFIGS = range(-1, 25)
+# -1: general kernel; 0-9: pipelined 8-wave kernel; 10-29: kernel with 32- or 64-deep slices
+# (25-29: persistent weight-streaming tiles)
+GEMM_TILE_CONFIGS = range(-1, 30)
 
 
 @pytest.mark.parametrize("gemm_cfg", [str(c) for c in GEMM_TILE_CONFIGS])
@@ -321,6 +322,30 @@ def test_every_gemm_tile_config(cfg, gemm_cfg, monkeypatch):
     print(f"[tile config {gemm_cfg}] {cfg.name}", flush=True)
     inp = W.make_inputs(cfg)
     ref = oracle_forward(cfg, inp)
+    got = DeviceLayer(cfg, inp).layer()
+    diff, err = check_layer(cfg, inp, ref, got)
+    print(f"  max rel err {err:.3e}")
+
+
+SPLIT_SHAPES = [
+    # shallow (<= 64 rows) and deep groups side by side
+    W.MoEConfig("split_sigmoid_zipf", 1500, 256, 32, 4, 192, num_shared=1, d_ff_shared=128,
+                scoring=W.SIGMOID_BIAS, zipf_s=1.4),
+    W.MoEConfig("split_softmax_ragged", 777, 320, 16, 2, 448, zipf_s=1.2),
+]
+
+
+@pytest.mark.parametrize("split", ["0", "1"])
+@pytest.mark.parametrize("cfg", SPLIT_SHAPES + V2_SHAPES, ids=lambda c: c.name)
+def test_shallow_group_split(cfg, split, monkeypatch):
+    """Expert FFN with shallow groups split off to the persistent
+    weight-streaming kernel (and without), against the oracle."""
+    monkeypatch.setenv("MOE_GEMM_SPLIT", split)
+    print(f"[split {split}] {cfg.name}", flush=True)
+    inp = W.make_inputs(cfg)
+    ref = oracle_forward(cfg, inp)
+    counts = np.bincount(ref["idx"].ravel(), minlength=cfg.num_experts)
+    print(f"  group rows: min {counts.min()} max {counts.max()}, <= 64: {(counts <= 64).sum()}")
     got = DeviceLayer(cfg, inp).layer()
     diff, err = check_layer(cfg, inp, ref, got)
     print(f"  max rel err {err:.3e}")

@@ -1,6 +1,7 @@
 // C ABI of the MoE layer library: argument validation, workspace carving and
 // the launch sequence of each entry point.  Declarations and the contract of
 // every function are in include/moe.h.
+#include <limits.h>
 #include <math.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -94,7 +95,7 @@ size_t ws_permute(const moe_config* c) {
   return carve((size_t)ceil_div(c->num_tokens, kPermuteTile) * c->num_experts * 4);
 }
 size_t ws_ffn(const moe_config*, int G, int F, int max_rows, int act) {
-  return carve((size_t)max_rows * F * esize(act)) + 2 * carve((size_t)(G + 1) * 4);
+  return carve((size_t)max_rows * F * esize(act)) + 4 * carve((size_t)(G + 1) * 4);
 }
 size_t ws_stats(const moe_config* c) {
   return carve((size_t)ceil_div(c->num_tokens, kStatsChunk) * c->num_experts * 4);
@@ -121,7 +122,7 @@ Layout layer_layout(const moe_config* c, const Derived& d) {
   L.counts = take(E * 4);
   L.offsets = take((E + 1) * 4);
   L.tile_prefix = take((E + 1) * 4);
-  L.tile_prefix2 = take((E + 1) * 4);
+  L.tile_prefix2 = take(3 * (E + 1) * 4);
   L.row_of = take(T * k * 4);
   L.tor = take((size_t)d.rows_cap * 4);
   const size_t h_routed = (size_t)d.rows_cap * c->d_ff * es;
@@ -224,14 +225,31 @@ int cfg_bm(int act, int cfg) {
 
 struct FfnPlan {
   int cfg_up, cfg_dn, bm_up, bm_dn;
+  // split: groups of at most sh_rows rows go to the persistent weight-streaming
+  // configuration cfg_sh (one m-tile each), deeper groups to cfg_up / cfg_dn
+  bool split;
+  int cfg_sh, sh_rows;
 };
 
-FfnPlan plan_ffn(int act, int D, int F, int max_rows, int G) {
+// Shallow groups are split off when both contractions are long (the
+// weight stream of a tile then dwarfs its start-up) and groups are shallow on
+// average.  MOE_GEMM_SPLIT=0 / 1 overrides the choice (tuning aid).
+FfnPlan plan_ffn(int act, int D, int F, int max_rows, int G, bool grouped) {
   FfnPlan pl;
   pl.cfg_up = pick_cfg(act, D, max_rows, G);
   pl.cfg_dn = pick_cfg(act, F, max_rows, G);
   pl.bm_up = cfg_bm(act, pl.cfg_up);
   pl.bm_dn = cfg_bm(act, pl.cfg_dn);
+  int sh = 15;
+  const char* sh_env = getenv("MOE_GEMM_SHCFG");       // tuning aid: persistent configuration 15-19
+  if (sh_env != nullptr && *sh_env != '\0' && atoi(sh_env) >= 15 && atoi(sh_env) < kGemmV3Configs) sh = atoi(sh_env);
+  pl.cfg_sh = kGemmV2Configs + sh;
+  pl.sh_rows = gemm_v3_bm(sh);
+  const bool able = grouped && pl.cfg_up >= 0 && pl.cfg_dn >= 0 && D % 64 == 0 && F % 64 == 0;
+  const int avg = G > 0 ? max_rows / G : max_rows;
+  pl.split = able && D >= 1024 && F >= 1024 && avg < 320;
+  const char* env = getenv("MOE_GEMM_SPLIT");
+  if (able && env != nullptr && *env != '\0') pl.split = atoi(env) != 0;
   return pl;
 }
 
@@ -243,13 +261,15 @@ hipError_t launch_gemm(int act, int cfg, const GroupedGemm& g, hipStream_t s) {
 }
 
 // gate/up (+activation) then down projection for G groups.  prefix_up holds
-// the m-tile prefix for plan.bm_up (computed by the caller when offsets are
-// given); prefix_dn is filled here when the down projection tiles differently.
+// the m-tile prefix for the plan's bm_up over all groups (computed by the
+// caller when offsets are given); prefix_ws has room for three more prefixes
+// of G+1 entries (the down projection's when it tiles differently, or the
+// class prefixes of a split).
 moe_status run_ffn(int act, int activation, int G, int D, int F, int max_rows, const void* x_in,
                    const int32_t* gather, const int32_t* offsets, const int32_t* prefix_up,
-                   int32_t* prefix_dn, const void* w13, const void* w2, void* h, void* y_out, hipStream_t s,
+                   int32_t* prefix_ws, const void* w13, const void* w2, void* h, void* y_out, hipStream_t s,
                    void* const* ev = nullptr, int stage_up = 0, int stage_down = 0) {
-  const FfnPlan pl = plan_ffn(act, D, F, max_rows, G);
+  const FfnPlan pl = plan_ffn(act, D, F, max_rows, G, offsets != nullptr);
   const int n_mat = activation == SWIGLU ? 2 : 1;
   GroupedGemm g1{};
   g1.A = x_in; g1.a_rows = gather; g1.lda = D;
@@ -265,15 +285,30 @@ moe_status run_ffn(int act, int activation, int G, int D, int F, int max_rows, c
   g2.M_max = max_rows; g2.N = D; g2.K = F;
   g2.G = G; g2.offsets = offsets; g2.tile_prefix = prefix_up;
   g2.epilogue = EPI_STORE_ACT;
+  GroupedGemm g1s = g1, g2s = g2;       // shallow groups of a split
+  if (pl.split) {
+    int32_t* deep_up = prefix_ws;
+    int32_t* deep_dn = pl.bm_dn != pl.bm_up ? prefix_ws + (G + 1) : deep_up;
+    int32_t* shallow = prefix_ws + 2 * (G + 1);
+    const TilePrefixReq r0{deep_up, pl.bm_up, pl.sh_rows, INT_MAX};
+    const TilePrefixReq r1{deep_dn != deep_up ? deep_dn : nullptr, pl.bm_dn, pl.sh_rows, INT_MAX};
+    const TilePrefixReq r2{shallow, pl.sh_rows, 0, pl.sh_rows};
+    MOE_TRY_HIP("tile prefix", launch_tile_prefix_classes(offsets, G, r0, r1, r2, s));
+    g1.tile_prefix = deep_up;
+    g2.tile_prefix = deep_dn;
+    g1s.tile_prefix = shallow;
+    g2s.tile_prefix = shallow;
+  } else if (offsets != nullptr && pl.bm_dn != pl.bm_up) {
+    MOE_TRY_HIP("tile prefix", launch_tile_prefix(offsets, G, pl.bm_dn, prefix_ws, s));
+    g2.tile_prefix = prefix_ws;
+  }
   MOE_TRY(mark(ev, stage_up, 0, s));
   MOE_TRY_HIP("expert gate/up", launch_gemm(act, pl.cfg_up, g1, s));
+  if (pl.split) MOE_TRY_HIP("expert gate/up (shallow groups)", launch_gemm(act, pl.cfg_sh, g1s, s));
   MOE_TRY(mark(ev, stage_up, 1, s));
   MOE_TRY(mark(ev, stage_down, 0, s));
-  if (offsets != nullptr && pl.bm_dn != pl.bm_up) {
-    MOE_TRY_HIP("tile prefix", launch_tile_prefix(offsets, G, pl.bm_dn, prefix_dn, s));
-    g2.tile_prefix = prefix_dn;
-  }
   MOE_TRY_HIP("expert down", launch_gemm(act, pl.cfg_dn, g2, s));
+  if (pl.split) MOE_TRY_HIP("expert down (shallow groups)", launch_gemm(act, pl.cfg_sh, g2s, s));
   MOE_TRY(mark(ev, stage_down, 1, s));
   return MOE_OK;
 }
@@ -399,8 +434,8 @@ moe_status moe_expert_ffn(const moe_config* cfg, int32_t num_groups, int32_t d_f
     const size_t hb = carve((size_t)max_rows * d_ff * esize(cfg->act_dtype));
     prefix_up = at<int32_t>(ws, hb);
     prefix_dn = at<int32_t>(ws, hb + carve((size_t)(num_groups + 1) * 4));
-    const FfnPlan pl = plan_ffn(cfg->act_dtype, cfg->d_model, d_ff, max_rows, num_groups);
-    MOE_TRY_HIP("tile prefix", launch_tile_prefix(offsets, num_groups, pl.bm_up, prefix_up, s));
+    const FfnPlan pl = plan_ffn(cfg->act_dtype, cfg->d_model, d_ff, max_rows, num_groups, true);
+    if (!pl.split) MOE_TRY_HIP("tile prefix", launch_tile_prefix(offsets, num_groups, pl.bm_up, prefix_up, s));
   }
   return run_ffn(cfg->act_dtype, activation, num_groups, cfg->d_model, d_ff, max_rows, x_in, gather_rows,
                  offsets, prefix_up, prefix_dn, w13, w2, h, y_out, s);
@@ -496,7 +531,7 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const moe_weights* wt,
   pa.tile_counts = at<int32_t>(ws, L.tile_counts);
   pa.counts = cnt; pa.offsets = off; pa.row_of = row_of; pa.token_of_row = tor;
   pa.tile_prefix = tp;
-  pa.bm = plan_ffn(cfg->act_dtype, D, cfg->d_ff, d.rows_cap, E).bm_up;
+  pa.bm = plan_ffn(cfg->act_dtype, D, cfg->d_ff, d.rows_cap, E, true).bm_up;
   MOE_TRY(mark(ev, MOE_STAGE_PERMUTE, 0, s));
   MOE_TRY_HIP("permute", launch_permute(pa, s));
   MOE_TRY(mark(ev, MOE_STAGE_PERMUTE, 1, s));

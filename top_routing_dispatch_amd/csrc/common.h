@@ -99,20 +99,20 @@ hipError_t launch_split_bf16x3(const float* w, int E, int D, bf16_t* out, hipStr
 // Tile order of the grouped GEMMs.  The tiles that exist (known on the device
 // only) are numbered group by group; inside a group, runs of up to 8 m-tiles
 // sweep all n-tiles, so the blocks that run together share both the group's
-// weight tiles and its activation rows in L2.  Workgroup ids are then dealt so
-// that every XCD gets one contiguous, equally long stretch of that order.
-// Returns false for workgroups beyond the last tile (the grid is an upper
-// bound).  Outputs: group g, first row of the tile, rows in the tile, n-tile.
+// weight tiles and its activation rows in L2.  decode_tile maps logical tile L
+// (below tile_count) to group g, first row of the tile, rows in the tile and
+// n-tile.
 template <int BM>
-__device__ __forceinline__ bool map_tile(const GroupedGemm& p, int n_tiles, int& g, int& row0, int& rows,
-                                         int& nt) {
+__device__ __forceinline__ int tile_count(const GroupedGemm& p, int n_tiles) {
+  return (p.offsets == nullptr ? ceil_div(p.M_max, BM) : p.tile_prefix[p.G]) * n_tiles;
+}
+
+template <int BM>
+__device__ __forceinline__ void decode_tile(const GroupedGemm& p, int n_tiles, int L, int& g, int& row0, int& rows,
+                                            int& nt) {
   constexpr int GM = 8;
-  const int bid = blockIdx.x;
   if (p.offsets == nullptr) {
     const int mt_all = ceil_div(p.M_max, BM);
-    const int total = mt_all * n_tiles;
-    if (bid >= total) return false;
-    const int L = xcd_remap(bid, total);
     const int sub = L / (GM * n_tiles);
     const int first = sub * GM;
     const int gm = min(mt_all - first, GM);
@@ -122,12 +122,9 @@ __device__ __forceinline__ bool map_tile(const GroupedGemm& p, int n_tiles, int&
     g = 0;
     row0 = mt * BM;
     rows = min(BM, p.M_max - row0);
-    return true;
+    return;
   }
   const int* tp = p.tile_prefix;
-  const int total = tp[p.G] * n_tiles;
-  if (bid >= total) return false;
-  const int L = xcd_remap(bid, total);
   const int mtile = L / n_tiles;          // tiles of group g are [tp[g] n, tp[g+1] n)
   int lo = 0, hi = p.G;                   // tp[lo] <= mtile < tp[hi]
   while (hi - lo > 1) {
@@ -145,11 +142,32 @@ __device__ __forceinline__ bool map_tile(const GroupedGemm& p, int n_tiles, int&
   nt = loc / gm;
   row0 = p.offsets[g] + m * BM;
   rows = min(BM, p.offsets[g + 1] - row0);
+}
+
+// Tile of this workgroup in a grid sized for the upper bound of tiles:
+// workgroup ids are dealt so that every XCD gets one contiguous, equally long
+// stretch of the tile order.  Returns false for workgroups beyond the last
+// tile.
+template <int BM>
+__device__ __forceinline__ bool map_tile(const GroupedGemm& p, int n_tiles, int& g, int& row0, int& rows,
+                                         int& nt) {
+  const int total = tile_count<BM>(p, n_tiles);
+  if ((int)blockIdx.x >= total) return false;
+  decode_tile<BM>(p, n_tiles, xcd_remap(blockIdx.x, total), g, row0, rows, nt);
   return true;
 }
 
 // m-tile prefix for grouped GEMMs: prefix[g] = sum_{h<g} ceil((off[h+1]-off[h]) / bm).
 hipError_t launch_tile_prefix(const int32_t* offsets, int G, int bm, int32_t* prefix, hipStream_t s);
+// m-tile prefixes restricted to a class of groups: group h counts
+// ceil(n_h / bm) m-tiles when lo < n_h <= hi and none otherwise.  Up to three
+// prefixes in one launch (unused ones: out == nullptr).
+struct TilePrefixReq {
+  int32_t* out;
+  int bm, lo, hi;
+};
+hipError_t launch_tile_prefix_classes(const int32_t* offsets, int G, TilePrefixReq r0, TilePrefixReq r1,
+                                      TilePrefixReq r2, hipStream_t s);
 
 // bf16 MFMA grouped GEMM; returns the BM its tiles use via bm_out when non-null.
 hipError_t launch_gemm_bf16(const GroupedGemm& g, hipStream_t s);
@@ -161,7 +179,7 @@ int gemm_v2_bm(int cfg);
 // bf16 grouped GEMM with 128x128 wave tiles, one wave per SIMD (K % 32 == 0,
 // K % 64 == 0 for the 64-deep configuration).  Its tile configurations follow
 // the pipelined kernel's in one numbering: kGemmV2Configs + cfg.
-constexpr int kGemmV3Configs = 15;
+constexpr int kGemmV3Configs = 20;
 constexpr int kGemmConfigs = kGemmV2Configs + kGemmV3Configs;
 hipError_t launch_gemm_v3(const GroupedGemm& g, int cfg, hipStream_t s);
 int gemm_v3_bm(int cfg);

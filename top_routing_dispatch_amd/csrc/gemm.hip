@@ -32,6 +32,31 @@ __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __rest
   if (g == 0) prefix[0] = 0;
 }
 
+// Class-restricted prefixes (see launch_tile_prefix_classes): one inclusive
+// scan over the groups per requested prefix.
+__global__ __launch_bounds__(1024) void tile_prefix_classes_kernel(const int32_t* __restrict__ off, int G,
+                                                                   TilePrefixReq r0, TilePrefixReq r1,
+                                                                   TilePrefixReq r2) {
+  __shared__ int s[kMaxExperts];
+  const int g = threadIdx.x;
+  const int n = (g < G) ? off[g + 1] - off[g] : 0;
+  for (int q = 0; q < 3; ++q) {
+    const TilePrefixReq r = q == 0 ? r0 : (q == 1 ? r1 : r2);
+    if (r.out == nullptr) continue;     // uniform: the same request for every thread
+    s[g] = (n > r.lo && n <= r.hi) ? ceil_div(n, r.bm) : 0;
+    __syncthreads();
+    for (int d = 1; d < kMaxExperts; d <<= 1) {
+      const int v = (g >= d) ? s[g - d] : 0;
+      __syncthreads();
+      s[g] += v;
+      __syncthreads();
+    }
+    if (g < G) r.out[g + 1] = s[g];
+    if (g == 0) r.out[0] = 0;
+    __syncthreads();                    // s is rewritten by the next request
+  }
+}
+
 // Number of m-tiles that can exist: sum_g ceil(n_g / BM) <= floor(M / BM) + #non-empty groups.
 inline int m_tiles_bound(const GroupedGemm& p, int bm) {
   if (p.offsets == nullptr) return ceil_div(p.M_max, bm);
@@ -371,6 +396,13 @@ hipError_t launch_f32_epi(const GroupedGemm& p, hipStream_t s) {
 
 hipError_t launch_tile_prefix(const int32_t* offsets, int G, int bm, int32_t* prefix, hipStream_t s) {
   hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(kMaxExperts), 0, s, offsets, G, bm, prefix);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_prefix_classes(const int32_t* offsets, int G, TilePrefixReq r0, TilePrefixReq r1,
+                                      TilePrefixReq r2, hipStream_t s) {
+  if (G > kMaxExperts) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(tile_prefix_classes_kernel, dim3(1), dim3(kMaxExperts), 0, s, offsets, G, r0, r1, r2);
   return hipGetLastError();
 }
 

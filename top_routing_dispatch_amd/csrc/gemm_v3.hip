@@ -19,6 +19,7 @@
 // by one pass of a fragment load cover all 64 banks once.
 #include "common.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace moe {
@@ -69,7 +70,7 @@ __device__ __forceinline__ int swz3(int r, int c) {
   return r * (CPR * 16) + ((c ^ ((r / (16 / CPR)) & (CPR - 1))) << 4);
 }
 
-template <int BM, int BN, int WGM, int WGN, int BK, int NST, int SP, int OCC, int EPI, typename OutT>
+template <int BM, int BN, int WGM, int WGN, int BK, int NST, int SP, int OCC, bool PERS, int EPI, typename OutT>
 __global__ __launch_bounds__(64 * WGM * WGN)
 __attribute__((amdgpu_waves_per_eu(WGM * WGN / 4 * OCC, WGM * WGN / 4 * OCC)))
 void gemm_v3_kernel(const GroupedGemm p, int n_tiles) {
@@ -80,8 +81,17 @@ void gemm_v3_kernel(const GroupedGemm p, int n_tiles) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WGN, wn = wave % WGN;
 
+  // PERS: a grid of about one workgroup per CU slot walks the tiles that
+  // exist (tile, tile + gridDim.x, ...); otherwise one tile per workgroup.
+  const int total = PERS ? tile_count<BM>(p, n_tiles) : 0;
+  for (int tile = blockIdx.x;; tile += gridDim.x) {
   int g, row0, rows, nt;
-  if (!map_tile<BM>(p, n_tiles, g, row0, rows, nt)) return;
+  if constexpr (PERS) {
+    if (tile >= total) break;
+    decode_tile<BM>(p, n_tiles, tile, g, row0, rows, nt);
+  } else {
+    if (!map_tile<BM>(p, n_tiles, g, row0, rows, nt)) return;
+  }
   // 32-row blocks of this wave that hold at least one row of the tile
   const int act_i = min(C::TM, max(0, ceil_div(rows - wm * C::WM, 32)));
 
@@ -331,6 +341,22 @@ void gemm_v3_kernel(const GroupedGemm p, int n_tiles) {
       }
     }
   }
+  if constexpr (!PERS) break;
+  __builtin_amdgcn_s_barrier();          // the staging reads are done before the next tile's loads land
+  }
+}
+
+inline int num_cus() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      n = v;
+    else
+      n = 256;
+  }
+  return n;
 }
 
 inline int m_bound3(const GroupedGemm& p, int bm) {
@@ -338,7 +364,7 @@ inline int m_bound3(const GroupedGemm& p, int bm) {
   return p.M_max / bm + (p.G < p.M_max ? p.G : p.M_max);
 }
 
-template <int BM, int BN, int WGM, int WGN, int BK, int NST, int SP, int OCC, int EPI>
+template <int BM, int BN, int WGM, int WGN, int BK, int NST, int SP, int OCC, bool PERS, int EPI>
 hipError_t launch_cfg3(const GroupedGemm& p, hipStream_t s) {
   using C = Cfg3<BM, BN, WGM, WGN, BK, NST>;
   if (p.K % BK != 0) return hipErrorInvalidValue;
@@ -346,14 +372,15 @@ hipError_t launch_cfg3(const GroupedGemm& p, hipStream_t s) {
   const int n_tiles = ceil_div(p.N, cols);
   const int m_tiles = m_bound3(p, BM);
   if (m_tiles == 0 || n_tiles == 0) return hipSuccess;
-  const long long blocks = (long long)m_tiles * n_tiles;
+  long long blocks = (long long)m_tiles * n_tiles;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (PERS) blocks = std::min<long long>(blocks, (long long)num_cus() * OCC);
   // dynamic LDS above 64 KB has to be allowed explicitly
   hipError_t e = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&gemm_v3_kernel<BM, BN, WGM, WGN, BK, NST, SP, OCC, EPI, bf16_t>),
+      reinterpret_cast<const void*>(&gemm_v3_kernel<BM, BN, WGM, WGN, BK, NST, SP, OCC, PERS, EPI, bf16_t>),
       hipFuncAttributeMaxDynamicSharedMemorySize, C::STAGE * NST);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((gemm_v3_kernel<BM, BN, WGM, WGN, BK, NST, SP, OCC, EPI, bf16_t>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((gemm_v3_kernel<BM, BN, WGM, WGN, BK, NST, SP, OCC, PERS, EPI, bf16_t>), dim3((unsigned)blocks),
                      dim3(C::THREADS), C::STAGE * NST, s, p, n_tiles);
   return hipGetLastError();
 }
@@ -362,22 +389,28 @@ template <int EPI>
 hipError_t launch_v3_epi(const GroupedGemm& p, int cfg, hipStream_t s) {
   switch (cfg) {
     // one workgroup per CU
-    case 0: return launch_cfg3<256, 256, 2, 2, 32, 4, 0, 1, EPI>(p, s);
-    case 1: return launch_cfg3<256, 256, 2, 2, 32, 5, 0, 1, EPI>(p, s);
-    case 2: return launch_cfg3<256, 256, 2, 2, 64, 2, 0, 1, EPI>(p, s);
-    case 3: return launch_cfg3<128, 256, 1, 4, 32, 4, 0, 1, EPI>(p, s);
-    case 4: return launch_cfg3<256, 256, 2, 4, 32, 4, 0, 1, EPI>(p, s);
-    case 5: return launch_cfg3<256, 256, 2, 4, 32, 5, 0, 1, EPI>(p, s);
-    case 6: return launch_cfg3<256, 256, 2, 4, 64, 2, 0, 1, EPI>(p, s);
-    case 7: return launch_cfg3<256, 256, 2, 4, 32, 4, 1, 1, EPI>(p, s);
-    case 8: return launch_cfg3<256, 256, 2, 2, 32, 4, 1, 1, EPI>(p, s);
-    case 9: return launch_cfg3<256, 256, 2, 4, 64, 2, 1, 1, EPI>(p, s);
-    case 10: return launch_cfg3<256, 256, 2, 4, 64, 2, 3, 1, EPI>(p, s);
+    case 0: return launch_cfg3<256, 256, 2, 2, 32, 4, 0, 1, false, EPI>(p, s);
+    case 1: return launch_cfg3<256, 256, 2, 2, 32, 5, 0, 1, false, EPI>(p, s);
+    case 2: return launch_cfg3<256, 256, 2, 2, 64, 2, 0, 1, false, EPI>(p, s);
+    case 3: return launch_cfg3<128, 256, 1, 4, 32, 4, 0, 1, false, EPI>(p, s);
+    case 4: return launch_cfg3<256, 256, 2, 4, 32, 4, 0, 1, false, EPI>(p, s);
+    case 5: return launch_cfg3<256, 256, 2, 4, 32, 5, 0, 1, false, EPI>(p, s);
+    case 6: return launch_cfg3<256, 256, 2, 4, 64, 2, 0, 1, false, EPI>(p, s);
+    case 7: return launch_cfg3<256, 256, 2, 4, 32, 4, 1, 1, false, EPI>(p, s);
+    case 8: return launch_cfg3<256, 256, 2, 2, 32, 4, 1, 1, false, EPI>(p, s);
+    case 9: return launch_cfg3<256, 256, 2, 4, 64, 2, 1, 1, false, EPI>(p, s);
+    case 10: return launch_cfg3<256, 256, 2, 4, 64, 2, 3, 1, false, EPI>(p, s);
     // two workgroups per CU (<= 80 KB of LDS each)
-    case 11: return launch_cfg3<128, 128, 2, 2, 64, 2, 0, 2, EPI>(p, s);
-    case 12: return launch_cfg3<128, 128, 2, 2, 32, 4, 0, 2, EPI>(p, s);
-    case 13: return launch_cfg3<128, 256, 2, 2, 32, 3, 0, 2, EPI>(p, s);
-    case 14: return launch_cfg3<64, 256, 1, 4, 32, 4, 0, 2, EPI>(p, s);
+    case 11: return launch_cfg3<128, 128, 2, 2, 64, 2, 0, 2, false, EPI>(p, s);
+    case 12: return launch_cfg3<128, 128, 2, 2, 32, 4, 0, 2, false, EPI>(p, s);
+    case 13: return launch_cfg3<128, 256, 2, 2, 32, 3, 0, 2, false, EPI>(p, s);
+    case 14: return launch_cfg3<64, 256, 1, 4, 32, 4, 0, 2, false, EPI>(p, s);
+    // persistent weight streaming for shallow groups (one m-tile per group)
+    case 15: return launch_cfg3<64, 256, 1, 4, 64, 4, 0, 1, true, EPI>(p, s);
+    case 16: return launch_cfg3<64, 256, 1, 4, 64, 3, 0, 1, true, EPI>(p, s);
+    case 17: return launch_cfg3<64, 256, 1, 4, 32, 8, 0, 1, true, EPI>(p, s);
+    case 18: return launch_cfg3<32, 256, 1, 4, 64, 4, 0, 1, true, EPI>(p, s);
+    case 19: return launch_cfg3<64, 256, 1, 4, 32, 4, 0, 2, true, EPI>(p, s);
   }
   return hipErrorInvalidValue;
 }
@@ -385,7 +418,8 @@ hipError_t launch_v3_epi(const GroupedGemm& p, int cfg, hipStream_t s) {
 }  // namespace
 
 int gemm_v3_bm(int cfg) {
-  static const int bm[] = {256, 256, 256, 128, 256, 256, 256, 256, 256, 256, 256, 128, 128, 128, 64};
+  static const int bm[] = {256, 256, 256, 128, 256, 256, 256, 256, 256, 256, 256, 128, 128, 128, 64,
+                           64, 64, 64, 32, 64};
   return (cfg >= 0 && cfg < kGemmV3Configs) ? bm[cfg] : 0;
 }
 
