@@ -207,11 +207,12 @@ int pick_cfg(int act, int K, int max_rows, int G) {
     return (c >= -1 && c < kGemmConfigs) ? c : -1;
   }
   // measured on MI355X at the Switch / Mixtral / DeepSeekMoE / DeepSeek-V3
-  // shapes: 256x256 tiles on 8 waves (64-deep slices, interleaved schedule)
-  // once groups are a few hundred rows deep, 128x128 tiles with 32-deep
-  // slices and two workgroups per CU for shallow (weight-streaming) groups
+  // shapes: 256x256 tiles on 8 waves (64-deep slices, interleaved schedule,
+  // weights fetched two slices ahead) once groups are a few hundred rows
+  // deep, 128x128 tiles with 32-deep slices and two workgroups per CU for
+  // shallow (weight-streaming) groups
   const int avg = G > 0 ? max_rows / G : max_rows;
-  return kGemmV2Configs + (avg >= 160 ? 6 : 12);
+  return kGemmV2Configs + (avg >= 160 ? 20 : 12);
 }
 
 int cfg_bm(int act, int cfg) {

@@ -84,7 +84,10 @@ struct Tile {
 // PRECISE: every BK-deep slice is summed by the MFMAs in float32 and then
 // added into float64 accumulators, so rounding error does not grow with K
 // (used for the router logits, which decide the expert selection).
-template <int BM, int BN, int BK, int EPI, typename OutT, bool PRECISE = false>
+// NPF: K slices held in registers ahead of the one being multiplied (the
+// loads of NPF slices are in flight while the LDS copy of the next one is
+// written).
+template <int BM, int BN, int BK, int EPI, typename OutT, bool PRECISE = false, int NPF = 1>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GroupedGemm p, int n_tiles) {
   using C = Tile<BM, BN, BK>;
   __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * C::LDS];
@@ -134,27 +137,28 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GroupedGemm p, int
     b_ptr[i] = ok ? B + (long long)brow * K + kc : nullptr;
   }
 
-  uint4 ra[C::A_PASSES], rb[C::B_PASSES];
-  auto gload = [&](int k0) {
+  u32x4_t ra[NPF][C::A_PASSES], rb[NPF][C::B_PASSES];
+  auto gload = [&](int slot, int k0) __attribute__((always_inline)) {
     const bool kin = (k0 + kc) < K;
     const int ka = p.a_kwrap ? k0 % p.a_kwrap : k0;
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < C::A_PASSES; ++i)
-      ra[i] = (a_ptr[i] && kin) ? *reinterpret_cast<const uint4*>(a_ptr[i] + ka) : make_uint4(0, 0, 0, 0);
+      ra[slot][i] = (a_ptr[i] && kin) ? *reinterpret_cast<const u32x4_t*>(a_ptr[i] + ka) : zero;
 #pragma unroll
     for (int i = 0; i < C::B_PASSES; ++i)
-      rb[i] = (b_ptr[i] && kin) ? *reinterpret_cast<const uint4*>(b_ptr[i] + k0) : make_uint4(0, 0, 0, 0);
+      rb[slot][i] = (b_ptr[i] && kin) ? *reinterpret_cast<const u32x4_t*>(b_ptr[i] + k0) : zero;
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](int slot, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < C::A_PASSES; ++i) {
       const int r = tid / C::CPR + i * C::RPP;
-      *reinterpret_cast<uint4*>(&sA[buf][r * C::LDS + kc]) = ra[i];
+      *reinterpret_cast<u32x4_t*>(&sA[buf][r * C::LDS + kc]) = ra[slot][i];
     }
 #pragma unroll
     for (int i = 0; i < C::B_PASSES; ++i) {
       const int r = tid / C::CPR + i * C::RPP;
-      *reinterpret_cast<uint4*>(&sB[buf][r * C::LDS + kc]) = rb[i];
+      *reinterpret_cast<u32x4_t*>(&sB[buf][r * C::LDS + kc]) = rb[slot][i];
     }
   };
 
@@ -177,45 +181,54 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GroupedGemm p, int
   }
 
   const int nk = ceil_div(K, BK);
-  gload(0);
-  sstore(0);
+  // slice j lives in register slot j % NPF until it is copied to LDS
+#pragma unroll
+  for (int u = 0; u < NPF; ++u)
+    if (u < nk) gload(u, u * BK);
+  sstore(0, 0);
   __syncthreads();
   const int frag_k = (lane >> 5) * 8;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
+  for (int kb = 0; kb < nk; kb += NPF) {
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8_t af[C::TM], bfv[C::TN];
+    for (int u = 0; u < NPF; ++u) {
+      const int kt = kb + u;
+      if (kt >= nk) break;
+      const int buf = kt & 1;
+      // slot u is free (slice kt is in LDS): fetch slice kt + NPF into it
+      if (kt + NPF < nk) gload(u, (kt + NPF) * BK);
 #pragma unroll
-      for (int i = 0; i < C::TM; ++i) {
-        const int row = wm * C::WM + i * 32 + (lane & 31);
-        af[i] = *reinterpret_cast<const bf16x8_t*>(&sA[buf][row * C::LDS + kk * 16 + frag_k]);
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        bf16x8_t af[C::TM], bfv[C::TN];
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i) {
+          const int row = wm * C::WM + i * 32 + (lane & 31);
+          af[i] = *reinterpret_cast<const bf16x8_t*>(&sA[buf][row * C::LDS + kk * 16 + frag_k]);
+        }
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) {
+          const int row = wn * C::WN + j * 32 + (lane & 31);
+          bfv[j] = *reinterpret_cast<const bf16x8_t*>(&sB[buf][row * C::LDS + kk * 16 + frag_k]);
+        }
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfv[j], acc[i][j], 0, 0, 0);
       }
+      if constexpr (PRECISE) {
 #pragma unroll
-      for (int j = 0; j < C::TN; ++j) {
-        const int row = wn * C::WN + j * 32 + (lane & 31);
-        bfv[j] = *reinterpret_cast<const bf16x8_t*>(&sB[buf][row * C::LDS + kk * 16 + frag_k]);
+        for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              dacc[i][j][r] += (double)acc[i][j][r];
+              acc[i][j][r] = 0.0f;
+            }
       }
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfv[j], acc[i][j], 0, 0, 0);
+      if (kt + 1 < nk) sstore((u + 1) % NPF, buf ^ 1);
+      __syncthreads();
     }
-    if constexpr (PRECISE) {
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            dacc[i][j][r] += (double)acc[i][j][r];
-            acc[i][j][r] = 0.0f;
-          }
-    }
-    if (kt + 1 < nk) sstore(buf ^ 1);
-    __syncthreads();
   }
 
   // Epilogue.  MFMA 32x32 output: lane holds column (lane & 31) and rows
@@ -366,7 +379,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const GroupedGemm p, int 
 
 constexpr int kBM = 128, kBN = 128, kBK = 64;
 
-template <int EPI, typename OutT, int BM = kBM, int BN = kBN, bool PRECISE = false>
+template <int EPI, typename OutT, int BM = kBM, int BN = kBN, bool PRECISE = false, int NPF = 1>
 hipError_t launch_bf16_epi(const GroupedGemm& p, hipStream_t s) {
   const int cols = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
   const int n_tiles = ceil_div(p.N, cols);
@@ -374,7 +387,7 @@ hipError_t launch_bf16_epi(const GroupedGemm& p, hipStream_t s) {
   if (m_tiles == 0 || n_tiles == 0) return hipSuccess;
   const long long blocks = (long long)m_tiles * n_tiles;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, kBK, EPI, OutT, PRECISE>), dim3((unsigned)blocks), dim3(256),
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, kBK, EPI, OutT, PRECISE, NPF>), dim3((unsigned)blocks), dim3(256),
                      0, s, p, n_tiles);
   return hipGetLastError();
 }
@@ -411,7 +424,7 @@ int gemm_bf16_bm(const GroupedGemm&) { return kBM; }
 hipError_t launch_gemm_bf16(const GroupedGemm& p, hipStream_t s) {
   switch (p.epilogue) {
     // float32 output is the router logits: small tiles, float64 slice accumulation
-    case EPI_STORE_F32: return launch_bf16_epi<EPI_STORE_F32, float, 64, 64, true>(p, s);
+    case EPI_STORE_F32: return launch_bf16_epi<EPI_STORE_F32, float, 64, 64, true, 4>(p, s);
     case EPI_STORE_ACT: return launch_bf16_epi<EPI_STORE_ACT, bf16_t>(p, s);
     case EPI_SWIGLU: return launch_bf16_epi<EPI_SWIGLU, bf16_t>(p, s);
     case EPI_GELU: return launch_bf16_epi<EPI_GELU, bf16_t>(p, s);

@@ -25,7 +25,7 @@
 namespace moe {
 namespace {
 
-template <int BM, int BN, int WGM, int WGN, int BK, int NST>
+template <int BM, int BN, int WGM, int WGN, int BK, int NST, int NSTB>
 struct Cfg3 {
   static constexpr int THREADS = 64 * WGM * WGN;
   static constexpr int NWAVES = WGM * WGN;
@@ -36,7 +36,8 @@ struct Cfg3 {
   static constexpr int RPI = 1024 / RB;                  // rows per 1 KB load instruction
   static constexpr int KK = BK / 16;                     // MFMA k-steps per slice
   static constexpr int A_BYTES = BM * RB, B_BYTES = BN * RB;
-  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int B_RING = NST * A_BYTES;           // the B ring follows the A ring
+  static constexpr int LDS = NST * A_BYTES + NSTB * B_BYTES;
   static constexpr int A_INS = BM / RPI / NWAVES;        // load instructions per wave per slice
   static constexpr int B_INS = BN / RPI / NWAVES;
   static constexpr int INS = A_INS + B_INS;
@@ -44,8 +45,11 @@ struct Cfg3 {
   static_assert(KK % 2 == 0, "fragment double buffering alternates per k-step");
   static_assert(BM % (RPI * NWAVES) == 0 && BN % (RPI * NWAVES) == 0, "load split");
   static_assert(TM >= 1 && TN >= 1, "wave tile");
-  static_assert(STAGE * NST <= 160 * 1024, "LDS");
-  static_assert(INS * (NST - 2) <= 63, "vmcnt range");
+  static_assert(LDS <= 160 * 1024, "LDS");
+  static_assert(NSTB >= NST && NST >= 2, "B is fetched at least as far ahead as A");
+  // loads younger than the later of A(kt+1) / B(kt+1) when slice kt+1 is awaited
+  static constexpr int WAIT = (NSTB > NST ? B_INS : 0) + INS * (NST - 2);
+  static_assert(WAIT <= 63, "vmcnt range");
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -70,11 +74,12 @@ __device__ __forceinline__ int swz3(int r, int c) {
   return r * (CPR * 16) + ((c ^ ((r / (16 / CPR)) & (CPR - 1))) << 4);
 }
 
-template <int BM, int BN, int WGM, int WGN, int BK, int NST, int SP, int OCC, bool PERS, int EPI, typename OutT>
+template <int BM, int BN, int WGM, int WGN, int BK, int NST, int NSTB, int SP, int OCC, bool PERS, int EPI,
+          typename OutT>
 __global__ __launch_bounds__(64 * WGM * WGN)
 __attribute__((amdgpu_waves_per_eu(WGM * WGN / 4 * OCC, WGM * WGN / 4 * OCC)))
 void gemm_v3_kernel(const GroupedGemm p, int n_tiles) {
-  using C = Cfg3<BM, BN, WGM, WGN, BK, NST>;
+  using C = Cfg3<BM, BN, WGM, WGN, BK, NST, NSTB>;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
   const int lane = threadIdx.x & 63;
@@ -133,10 +138,21 @@ void gemm_v3_kernel(const GroupedGemm p, int n_tiles) {
     b_off[q] = ((unsigned)brow * (unsigned)K + c * 8) * 2u;
   }
 
-  // Load instruction q of a refill (A rows first, then B rows).
-  auto dma_one = [&](int q, char* st, unsigned kb) __attribute__((always_inline)) {
-    if (q < C::A_INS) dma16_3(a_rsrc, a_off[q] + kb, st + (wave * C::A_INS + q) * 1024);
-    else dma16_3(b_rsrc, b_off[q - C::A_INS] + kb, st + C::A_BYTES + (wave * C::B_INS + q - C::A_INS) * 1024);
+  // Slice j of A lives in A slot j % NST, slice j of B in B slot j % NSTB.
+  // Iteration it refills A with slice it + NST - 1 and B with slice
+  // it + NSTB - 1 (B runs further ahead); load instruction q of an iteration:
+  // A rows first, then B rows.
+  const int nk = K / BK;
+  auto dma_one = [&](int q, int it) __attribute__((always_inline)) {
+    if (q < C::A_INS) {
+      const int j = it + NST - 1;
+      dma16_3(a_rsrc, a_off[q] + min(j, nk - 1) * (unsigned)C::RB,
+              smem + (j % NST) * C::A_BYTES + (wave * C::A_INS + q) * 1024);
+    } else {
+      const int j = it + NSTB - 1;
+      dma16_3(b_rsrc, b_off[q - C::A_INS] + min(j, nk - 1) * (unsigned)C::RB,
+              smem + C::B_RING + (j % NSTB) * C::B_BYTES + (wave * C::B_INS + q - C::A_INS) * 1024);
+    }
   };
 
   floatx16_t acc[C::TM][C::TN];
@@ -147,20 +163,21 @@ void gemm_v3_kernel(const GroupedGemm p, int n_tiles) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // The ring always advances by one slice per slice consumed: past the last
+  // The rings always advance by one slice per slice consumed: past the last
   // slice, a refill loads the last slice again into the slot just released,
-  // which no remaining slice uses.  Every wait then leaves exactly the loads
-  // of the NST-2 younger slices outstanding.
-  const int nk = K / BK;
+  // which no remaining slice uses.  Every wait then leaves exactly C::WAIT
+  // younger loads outstanding.  The prologue runs iterations 1-NSTB .. -1 of
+  // the same schedule (loads of negative slices skipped).
 #pragma unroll
-  for (int st = 0; st < NST - 1; ++st) {
+  for (int it = 1 - NSTB; it < 0; ++it) {
 #pragma unroll
-    for (int q = 0; q < C::INS; ++q) dma_one(q, smem + st * C::STAGE, min(st, nk - 1) * (unsigned)C::RB);
+    for (int q = 0; q < C::INS; ++q)
+      if ((q < C::A_INS ? it + NST - 1 : it + NSTB - 1) >= 0) dma_one(q, it);
   }
-  // Slice kt has landed for every wave, and every wave is done with the slot
+  // Slice kt has landed for every wave, and every wave is done with the slots
   // refilled next.
   auto slice_ready = [&]() __attribute__((always_inline)) {
-    wait_vm<C::INS * (NST - 2)>();
+    wait_vm<C::WAIT>();
     __builtin_amdgcn_s_barrier();
   };
 
@@ -183,9 +200,9 @@ void gemm_v3_kernel(const GroupedGemm p, int n_tiles) {
     constexpr bool FULL = decltype(full_c)::value;
     // Fragment reads in the order of first use by the MFMAs (block row i,
     // then column j): A0, B0..B(TN-1), A1, ..., A(TM-1).
-    auto load_frags = [&](int buf, int slot, int kk) __attribute__((always_inline)) {
-      const char* sa = smem + slot * C::STAGE;
-      const char* sb = sa + C::A_BYTES;
+    auto load_frags = [&](int buf, int kt, int kk) __attribute__((always_inline)) {
+      const char* sa = smem + (kt % NST) * C::A_BYTES;
+      const char* sb = smem + C::B_RING + (kt % NSTB) * C::B_BYTES;
       const int ch = kk * 2 + fc;
       af[buf][0] = *reinterpret_cast<const bf16x8_t*>(sa + swz3<C::CPR>(wm * C::WM + fr, ch));
 #pragma unroll
@@ -198,7 +215,7 @@ void gemm_v3_kernel(const GroupedGemm p, int n_tiles) {
     };
     // MFMAs of one 16-deep step on fragment buffer `buf`, with the refill
     // loads that belong to step kk.
-    auto mfma_step = [&](int buf, int kk, char* st, unsigned kb) __attribute__((always_inline)) {
+    auto mfma_step = [&](int buf, int kk, int kt) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < C::TM; ++i) {
         if (FULL || i < act_i) {
@@ -209,7 +226,7 @@ void gemm_v3_kernel(const GroupedGemm p, int n_tiles) {
         if (SP > 0 && kk < SP) {
 #pragma unroll
           for (int q = 0; q < C::INS; ++q)
-            if ((q * SPAN / C::INS) / C::TN == kk * C::TM + i) dma_one(q, st, kb);
+            if ((q * SPAN / C::INS) / C::TN == kk * C::TM + i) dma_one(q, kt);
         }
       }
     };
@@ -245,17 +262,14 @@ void gemm_v3_kernel(const GroupedGemm p, int n_tiles) {
     // then (unless it is the last slice) the hand-over to the next slice and
     // the last step.
     auto slice = [&](int kt, bool last) __attribute__((always_inline)) {
-      const int slot = kt % NST;
-      char* rst = smem + ((kt + NST - 1) % NST) * C::STAGE;
-      const unsigned rkb = min(kt + NST - 1, nk - 1) * (unsigned)C::RB;
       if (SP == 0) {
 #pragma unroll
-        for (int q = 0; q < C::INS; ++q) dma_one(q, rst, rkb);
+        for (int q = 0; q < C::INS; ++q) dma_one(q, kt);
       }
 #pragma unroll
       for (int kk = 0; kk < C::KK - 1; ++kk) {
-        load_frags((kk + 1) & 1, slot, kk + 1);
-        mfma_step(kk & 1, kk, rst, rkb);
+        load_frags((kk + 1) & 1, kt, kk + 1);
+        mfma_step(kk & 1, kk, kt);
         interleave(kk, true, kk == 0 || SP > 0);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -265,9 +279,9 @@ void gemm_v3_kernel(const GroupedGemm p, int n_tiles) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       if (!last) {
         slice_ready();
-        load_frags(0, (kt + 1) % NST, 0);
+        load_frags(0, kt + 1, 0);
       }
-      mfma_step(1, C::KK - 1, rst, rkb);
+      mfma_step(1, C::KK - 1, kt);
       interleave(C::KK - 1, !last, false);
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -288,9 +302,9 @@ void gemm_v3_kernel(const GroupedGemm p, int n_tiles) {
   // bit 2 of the row index set.
   static_assert(sizeof(OutT) == 2, "16-bit outputs");
   constexpr int OC = (EPI == EPI_SWIGLU) ? C::WN / 2 : C::WN;   // output columns per wave
-  constexpr bool PAD = C::NWAVES * C::WM * (OC * 2 + 16) <= C::STAGE * NST;
+  constexpr bool PAD = C::NWAVES * C::WM * (OC * 2 + 16) <= C::LDS;
   constexpr int PITCH = OC * 2 + (PAD ? 16 : 0);
-  static_assert(C::NWAVES * C::WM * PITCH <= C::STAGE * NST, "output staging fits in the ring");
+  static_assert(C::NWAVES * C::WM * PITCH <= C::LDS, "output staging fits in the rings");
   static_assert(PAD || (OC * 2) % 128 == 0, "half swap needs rows of whole 128-byte pairs");
   auto sbyte = [](int row, int byte) { return PAD ? byte : (byte ^ (((row >> 2) & 1) << 6)); };
   __builtin_amdgcn_s_barrier();          // every wave is done with the ring
@@ -364,9 +378,9 @@ inline int m_bound3(const GroupedGemm& p, int bm) {
   return p.M_max / bm + (p.G < p.M_max ? p.G : p.M_max);
 }
 
-template <int BM, int BN, int WGM, int WGN, int BK, int NST, int SP, int OCC, bool PERS, int EPI>
+template <int BM, int BN, int WGM, int WGN, int BK, int NST, int SP, int OCC, bool PERS, int EPI, int NSTB = NST>
 hipError_t launch_cfg3(const GroupedGemm& p, hipStream_t s) {
-  using C = Cfg3<BM, BN, WGM, WGN, BK, NST>;
+  using C = Cfg3<BM, BN, WGM, WGN, BK, NST, NSTB>;
   if (p.K % BK != 0) return hipErrorInvalidValue;
   const int cols = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
   const int n_tiles = ceil_div(p.N, cols);
@@ -377,11 +391,11 @@ hipError_t launch_cfg3(const GroupedGemm& p, hipStream_t s) {
   if (PERS) blocks = std::min<long long>(blocks, (long long)num_cus() * OCC);
   // dynamic LDS above 64 KB has to be allowed explicitly
   hipError_t e = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&gemm_v3_kernel<BM, BN, WGM, WGN, BK, NST, SP, OCC, PERS, EPI, bf16_t>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, C::STAGE * NST);
+      reinterpret_cast<const void*>(&gemm_v3_kernel<BM, BN, WGM, WGN, BK, NST, NSTB, SP, OCC, PERS, EPI, bf16_t>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((gemm_v3_kernel<BM, BN, WGM, WGN, BK, NST, SP, OCC, PERS, EPI, bf16_t>), dim3((unsigned)blocks),
-                     dim3(C::THREADS), C::STAGE * NST, s, p, n_tiles);
+  hipLaunchKernelGGL((gemm_v3_kernel<BM, BN, WGM, WGN, BK, NST, NSTB, SP, OCC, PERS, EPI, bf16_t>), dim3((unsigned)blocks),
+                     dim3(C::THREADS), C::LDS, s, p, n_tiles);
   return hipGetLastError();
 }
 
@@ -411,6 +425,11 @@ hipError_t launch_v3_epi(const GroupedGemm& p, int cfg, hipStream_t s) {
     case 17: return launch_cfg3<64, 256, 1, 4, 32, 8, 0, 1, true, EPI>(p, s);
     case 18: return launch_cfg3<32, 256, 1, 4, 64, 4, 0, 1, true, EPI>(p, s);
     case 19: return launch_cfg3<64, 256, 1, 4, 32, 4, 0, 2, true, EPI>(p, s);
+    // weights (B) fetched one slice further ahead than the activations (A)
+    case 20: return launch_cfg3<256, 256, 2, 4, 64, 2, 0, 1, false, EPI, 3>(p, s);
+    case 21: return launch_cfg3<256, 256, 2, 2, 64, 2, 0, 1, false, EPI, 3>(p, s);
+    case 22: return launch_cfg3<256, 256, 2, 4, 64, 2, 1, 1, false, EPI, 3>(p, s);
+    case 23: return launch_cfg3<64, 256, 1, 4, 64, 2, 0, 1, true, EPI, 4>(p, s);
   }
   return hipErrorInvalidValue;
 }
@@ -419,7 +438,7 @@ hipError_t launch_v3_epi(const GroupedGemm& p, int cfg, hipStream_t s) {
 
 int gemm_v3_bm(int cfg) {
   static const int bm[] = {256, 256, 256, 128, 256, 256, 256, 256, 256, 256, 256, 128, 128, 128, 64,
-                           64, 64, 64, 32, 64};
+                           64, 64, 64, 32, 64, 256, 256, 256, 64};
   return (cfg >= 0 && cfg < kGemmV3Configs) ? bm[cfg] : 0;
 }
 

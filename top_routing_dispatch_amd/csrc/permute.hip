@@ -79,11 +79,19 @@ __global__ __launch_bounds__(kMaxExperts) void scan_kernel(const PermuteArgs a, 
   const int e = threadIdx.x;
   int total = 0;
   if (e < a.E) {
-    for (int tl = 0; tl < ntiles; ++tl) {
-      int* p = a.tile_counts + (long long)tl * a.E + e;
-      const int c = *p;
-      *p = total;                 // becomes the tile's base rank inside expert e
-      total += c;
+    // the counts of 16 tiles are fetched together, then turned into the
+    // tiles' base ranks inside expert e
+    constexpr int B = 16;
+    for (int t0 = 0; t0 < ntiles; t0 += B) {
+      int c[B];
+#pragma unroll
+      for (int u = 0; u < B; ++u)
+        c[u] = (t0 + u < ntiles) ? a.tile_counts[(long long)(t0 + u) * a.E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < B; ++u) {
+        if (t0 + u < ntiles) a.tile_counts[(long long)(t0 + u) * a.E + e] = total;
+        total += c[u];
+      }
     }
     a.counts[e] = total;
   }
