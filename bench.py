@@ -36,7 +36,8 @@ TRAFFIC_SOURCES = ("top_routing_dispatch_amd/csrc/common.h", "top_routing_dispat
                    "top_routing_dispatch_amd/csrc/gemm.hip", "top_routing_dispatch_amd/csrc/api.hip",
                    "workloads/__init__.py")
 
-DEFAULT_CPU_SAMPLE = {"tiny": 64, "switch": 8192, "mixtral": 256, "deepseekmoe": 1024, "deepseekv3": 64}
+DEFAULT_CPU_SAMPLE = {"tiny": 64, "switch": 8192, "mixtral": 1024, "deepseekmoe": 4096, "deepseekv3": 256}
+CPU_MIN_SECONDS = 10.0       # the oracle's sample is repeated until this much time has passed
 
 
 def log(msg):
@@ -149,13 +150,18 @@ def cpu_baseline(cfg, inp, sample_tokens):
     Ts = min(sample_tokens, cfg.num_tokens)
     scfg = cfg.replace(num_tokens=Ts)
     x = inp.x[:Ts]
+    passes = 0
     t0 = time.perf_counter()
-    O.forward(scfg, x, inp.w_router, inp.sel_bias, lambda e: (inp.w13[e], inp.w2[e]), inp.shared)
-    dt = time.perf_counter() - t0
-    return dict(value=round(Ts / dt, 2), unit="tokens/s", cores=int(cores), kind="oracle",
+    while True:
+        O.forward(scfg, x, inp.w_router, inp.sel_bias, lambda e: (inp.w13[e], inp.w2[e]), inp.shared)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= CPU_MIN_SECONDS:
+            break
+    return dict(value=round(Ts * passes / dt, 2), unit="tokens/s", cores=int(cores), kind="oracle",
                 sample=f"first {Ts} of {cfg.num_tokens} tokens, all {cfg.num_experts} experts"
                        + (", capacity recomputed for the sample" if cfg.capacity_factor > 0 else "")
-                       + f"; {dt:.1f} s")
+                       + f"; {passes} pass(es) in {dt:.1f} s")
 
 
 def main():
