@@ -4,9 +4,10 @@ One step = one moe_layer_forward over a batch of seeded synthetic tokens that
 is already resident in HBM: router logits, scoring / top-k, permute, grouped
 expert FFN (routed and shared), combine and the load statistics.
 
-Prints ONE JSON line: MoE-layer tokens/s, the roofline of the dominant kernel
-(timed live with HIP events on the library's stream over the timed steps) and
-the CPU oracle timed on a bounded sample of the same workload.
+Prints ONE JSON line: MoE-layer tokens/s, the roofline of the dominant stage
+(timed live with HIP events on the library's stream over the timed steps), the
+per-stage breakdown of an untimed pass with every stage bracketed by events,
+and the CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -214,20 +215,47 @@ def main():
 
     nst = len(M.STAGES)
 
-    def new_events():
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * nst)]
-        for e in evs:
-            e.record()          # creates the HIP event handle
+    def new_events(stages=None):
+        """Events for the given stage indices (all by default), None elsewhere."""
+        evs = [None] * (2 * nst)
+        for si in (range(nst) if stages is None else stages):
+            for w in (0, 1):
+                e = torch.cuda.Event(enable_timing=True)
+                e.record()      # creates the HIP event handle
+                evs[2 * si + w] = e
         return evs
 
     def step(evs=None):
         M.moe_layer_forward_timed(cfg, weights, x, y, idx, tw, counts, cfg.alpha, stats, dropped, ws,
                                   stage_events=evs)
 
+    def stage_times(events, stages):
+        out = {}
+        for si in stages:
+            name = M.STAGES[si]
+            if name.startswith("shared") and cfg.num_shared == 0:
+                continue        # no kernels: the events only hold their creation-time records
+            vals = [evs[2 * si].elapsed_time(evs[2 * si + 1]) for evs in events]
+            if vals and max(vals) > 0:
+                out[name] = float(np.mean(vals))
+        return out
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [new_events() for _ in range(args.steps)]
+    # Untimed breakdown pass: every stage bracketed by events, to find the
+    # slowest stage.  The timed steps below record only that stage's two
+    # events, so the per-step time carries no extra event packets.
+    n_prof = max(1, min(args.steps, 10))
+    prof_events = [new_events() for _ in range(n_prof)]
+    torch.cuda.synchronize()
+    for i in range(n_prof):
+        step(prof_events[i])
+    torch.cuda.synchronize()
+    stage_ms = stage_times(prof_events, range(nst))
+    dominant = max(stage_ms, key=stage_ms.get)
+    dom_i = M.STAGES.index(dominant)
+    events = [new_events([dom_i]) for _ in range(args.steps)]
     torch.cuda.synchronize()
 
     t0 = time.perf_counter()
@@ -237,22 +265,10 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
     log(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step")
+    # the dominant stage's time over the timed steps (HIP events on the library's stream)
+    dom_ms = stage_times(events, [dom_i])[dominant]
 
-    # per-stage averages over the timed steps (HIP events on the library's stream)
-    stage_ms = {}
     c_host = counts.cpu().numpy()
-    for si, name in enumerate(M.STAGES):
-        if name.startswith("shared") and cfg.num_shared == 0:
-            continue            # no kernels: the events only hold their creation-time records
-        vals = []
-        for evs in events:
-            try:
-                vals.append(evs[2 * si].elapsed_time(evs[2 * si + 1]))
-            except RuntimeError:
-                vals = []
-                break
-        if vals and max(vals) > 0:
-            stage_ms[name] = float(np.mean(vals))
     cap, rows_cap = M.moe_capacity(cfg)
     kept = np.minimum(c_host, cap)
     A = int(kept.sum())
@@ -261,10 +277,10 @@ def main():
     for name, ms in stage_ms.items():
         fl, by = stage_work(cfg, name, A, E_act, T)
         stage_info[name] = dict(ms=round(ms, 4), **roofline_of(cfg, name, fl, by, ms))
-    dominant = max(stage_ms, key=stage_ms.get)
     fl, by = stage_work(cfg, dominant, A, E_act, T)
-    roof = roofline_of(cfg, dominant, fl, by, stage_ms[dominant])
+    roof = roofline_of(cfg, dominant, fl, by, dom_ms)
     roof["kernel"] = dominant
+    roof["ms"] = round(dom_ms, 4)
     roof["traffic"] = measured_traffic(cfg.name, dominant)
 
     cpu = None

@@ -212,7 +212,7 @@ int pick_cfg(int act, int K, int max_rows, int G) {
   // deep, 128x128 tiles with 32-deep slices and two workgroups per CU for
   // shallow (weight-streaming) groups
   const int avg = G > 0 ? max_rows / G : max_rows;
-  return kGemmV2Configs + (avg >= 160 ? 20 : 12);
+  return kGemmV2Configs + (avg >= 160 ? 0 : 5);
 }
 
 int cfg_bm(int act, int cfg) {
@@ -241,9 +241,9 @@ FfnPlan plan_ffn(int act, int D, int F, int max_rows, int G, bool grouped) {
   pl.cfg_dn = pick_cfg(act, F, max_rows, G);
   pl.bm_up = cfg_bm(act, pl.cfg_up);
   pl.bm_dn = cfg_bm(act, pl.cfg_dn);
-  int sh = 15;
-  const char* sh_env = getenv("MOE_GEMM_SHCFG");       // tuning aid: persistent configuration 15-19
-  if (sh_env != nullptr && *sh_env != '\0' && atoi(sh_env) >= 15 && atoi(sh_env) < kGemmV3Configs) sh = atoi(sh_env);
+  int sh = 9;
+  const char* sh_env = getenv("MOE_GEMM_SHCFG");       // tuning aid: persistent configuration 9 or 10
+  if (sh_env != nullptr && *sh_env != '\0' && (atoi(sh_env) == 9 || atoi(sh_env) == 10)) sh = atoi(sh_env);
   pl.cfg_sh = kGemmV2Configs + sh;
   pl.sh_rows = gemm_v3_bm(sh);
   const bool able = grouped && pl.cfg_up >= 0 && pl.cfg_dn >= 0 && D % 64 == 0 && F % 64 == 0;

@@ -179,7 +179,7 @@ int gemm_v2_bm(int cfg);
 // bf16 grouped GEMM with 128x128 wave tiles, one wave per SIMD (K % 32 == 0,
 // K % 64 == 0 for the 64-deep configuration).  Its tile configurations follow
 // the pipelined kernel's in one numbering: kGemmV2Configs + cfg.
-constexpr int kGemmV3Configs = 24;
+constexpr int kGemmV3Configs = 12;
 constexpr int kGemmConfigs = kGemmV2Configs + kGemmV3Configs;
 hipError_t launch_gemm_v3(const GroupedGemm& g, int cfg, hipStream_t s);
 int gemm_v3_bm(int cfg);

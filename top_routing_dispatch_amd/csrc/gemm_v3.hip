@@ -47,9 +47,7 @@ struct Cfg3 {
   static_assert(TM >= 1 && TN >= 1, "wave tile");
   static_assert(LDS <= 160 * 1024, "LDS");
   static_assert(NSTB >= NST && NST >= 2, "B is fetched at least as far ahead as A");
-  // loads younger than the later of A(kt+1) / B(kt+1) when slice kt+1 is awaited
-  static constexpr int WAIT = (NSTB > NST ? B_INS : 0) + INS * (NST - 2);
-  static_assert(WAIT <= 63, "vmcnt range");
+
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -69,13 +67,26 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// gelu(z) = z * Phi(z) = z/2 * erfc(-z/sqrt(2)) for outputs rounded to bf16.
+// erfc(a), a >= 0, from Abramowitz & Stegun 7.1.26 (|error| <= 1.5e-7):
+// erfc(a) ~ t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-a^2), t = 1 / (1 + p a).
+// For z < 0 the result is z/2 * erfc(|x|) directly, so small values keep
+// their relative accuracy instead of coming out of 1 - erf.
+__device__ __forceinline__ float gelu_bf16out(float z) {
+  const float x = z * 0.70710678118654752f;
+  const float a = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * a);
+  const float poly = t * (0.254829592f + t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
+  const float c = poly * __expf(-a * a);                  // erfc(|x|)
+  return 0.5f * z * (x >= 0.0f ? 2.0f - c : c);
+}
+
 template <int CPR>
 __device__ __forceinline__ int swz3(int r, int c) {
   return r * (CPR * 16) + ((c ^ ((r / (16 / CPR)) & (CPR - 1))) << 4);
 }
 
-template <int BM, int BN, int WGM, int WGN, int BK, int NST, int NSTB, int SP, int OCC, bool PERS, int EPI,
-          typename OutT>
+template <int BM, int BN, int WGM, int WGN, int BK, int NST, int NSTB, int OCC, bool PERS, int EPI, typename OutT>
 __global__ __launch_bounds__(64 * WGM * WGN)
 __attribute__((amdgpu_waves_per_eu(WGM * WGN / 4 * OCC, WGM * WGN / 4 * OCC)))
 void gemm_v3_kernel(const GroupedGemm p, int n_tiles) {
@@ -146,11 +157,11 @@ void gemm_v3_kernel(const GroupedGemm p, int n_tiles) {
   auto dma_one = [&](int q, int it) __attribute__((always_inline)) {
     if (q < C::A_INS) {
       const int j = it + NST - 1;
-      dma16_3(a_rsrc, a_off[q] + min(j, nk - 1) * (unsigned)C::RB,
+      dma16_3(a_rsrc, a_off[q] + j * (unsigned)C::RB,
               smem + (j % NST) * C::A_BYTES + (wave * C::A_INS + q) * 1024);
     } else {
       const int j = it + NSTB - 1;
-      dma16_3(b_rsrc, b_off[q - C::A_INS] + min(j, nk - 1) * (unsigned)C::RB,
+      dma16_3(b_rsrc, b_off[q - C::A_INS] + j * (unsigned)C::RB,
               smem + C::B_RING + (j % NSTB) * C::B_BYTES + (wave * C::B_INS + q - C::A_INS) * 1024);
     }
   };
@@ -163,41 +174,52 @@ void gemm_v3_kernel(const GroupedGemm p, int n_tiles) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // The rings always advance by one slice per slice consumed: past the last
-  // slice, a refill loads the last slice again into the slot just released,
-  // which no remaining slice uses.  Every wait then leaves exactly C::WAIT
-  // younger loads outstanding.  The prologue runs iterations 1-NSTB .. -1 of
-  // the same schedule (loads of negative slices skipped).
-#pragma unroll
-  for (int it = 1 - NSTB; it < 0; ++it) {
-#pragma unroll
-    for (int q = 0; q < C::INS; ++q)
-      if ((q < C::A_INS ? it + NST - 1 : it + NSTB - 1) >= 0) dma_one(q, it);
-  }
-  // Slice kt has landed for every wave, and every wave is done with the slots
-  // refilled next.
-  auto slice_ready = [&]() __attribute__((always_inline)) {
-    wait_vm<C::WAIT>();
-    __builtin_amdgcn_s_barrier();
-  };
+  // A wave whose A rows all lie past the tile's last row loads no A (those
+  // LDS rows feed only 32-row blocks that no wave multiplies).
+  const bool a_live = wave * C::A_INS * C::RPI < rows;
 
   const int fr = lane & 31;              // fragment row inside a 32-row block
   const int fc = lane >> 5;              // which 8-wide half of a 16-deep step
   bf16x8_t af[2][C::TM], bfv[2][C::TN];
 
-  // With SP > 0 a refill's load instructions are spread between the MFMAs of
-  // the slice's first SP steps (load q follows MFMA block `at`), otherwise
-  // they are issued together at the start of the slice.
-  static_assert(SP >= 0 && SP <= C::KK - 1, "refill loads go out before the next slice's wait");
   constexpr int MF = C::TM * C::TN;
-  constexpr int SPAN = (SP > 0 ? SP : 1) * MF;
 
   // FULL: every 32-row block of the wave holds rows of the tile.  Its steps
   // are straight-line code, and each step's fragment reads for the next step
   // (and its refill loads) are placed one after each MFMA, so that they issue
   // while the matrix core works instead of in a burst that leaves it idle.
-  auto k_loop = [&](auto full_c) __attribute__((always_inline)) {
+  auto k_loop = [&](auto full_c, auto al_c) __attribute__((always_inline)) {
     constexpr bool FULL = decltype(full_c)::value;
+    constexpr bool AL = decltype(al_c)::value;          // this wave loads A rows
+    constexpr int WA = AL ? C::A_INS : 0;
+    // Loads younger than the later of this wave's A(kt+1) / B(kt+1) when
+    // slice kt+1 is awaited.
+    constexpr int WAIT = AL ? (NSTB > NST ? C::B_INS : 0) + (WA + C::B_INS) * (NST - 2)
+                            : C::B_INS * (NSTB - 2);
+    static_assert(WAIT <= 63, "vmcnt range");
+    // Load q of iteration it (iteration it refills A with slice it + NST - 1
+    // and B with slice it + NSTB - 1); `exists` skips the check that the
+    // slice exists, in the steady part of the loop where it always does.
+    auto load_q = [&](int q, int it, bool exists) __attribute__((always_inline)) {
+      const int j = q < C::A_INS ? it + NST - 1 : it + NSTB - 1;
+      if ((AL || q >= C::A_INS) && (exists || j < nk)) dma_one(q, it);
+    };
+    // Prologue: iterations 1-NSTB .. -1 of the same schedule.
+#pragma unroll
+    for (int it = 1 - NSTB; it < 0; ++it) {
+#pragma unroll
+      for (int q = 0; q < C::INS; ++q)
+        if ((q < C::A_INS ? it + NST - 1 : it + NSTB - 1) >= 0) load_q(q, it, false);
+    }
+    // Slice `next` has landed for every wave, and every wave is done with the
+    // slots refilled next.  While every refill so far was of an existing
+    // slice (next + NSTB - 2 < nk), exactly WAIT younger loads are
+    // outstanding; in the last iterations everything is awaited.
+    auto slice_ready = [&](bool exact) __attribute__((always_inline)) {
+      if (exact) wait_vm<WAIT>();
+      else wait_vm<0>();
+      __builtin_amdgcn_s_barrier();
+    };
     // Fragment reads in the order of first use by the MFMAs (block row i,
     // then column j): A0, B0..B(TN-1), A1, ..., A(TM-1).
     auto load_frags = [&](int buf, int kt, int kk) __attribute__((always_inline)) {
@@ -215,7 +237,7 @@ void gemm_v3_kernel(const GroupedGemm p, int n_tiles) {
     };
     // MFMAs of one 16-deep step on fragment buffer `buf`, with the refill
     // loads that belong to step kk.
-    auto mfma_step = [&](int buf, int kk, int kt) __attribute__((always_inline)) {
+    auto mfma_step = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < C::TM; ++i) {
         if (FULL || i < act_i) {
@@ -223,27 +245,14 @@ void gemm_v3_kernel(const GroupedGemm p, int n_tiles) {
           for (int j = 0; j < C::TN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][i], bfv[buf][j], acc[i][j], 0, 0, 0);
         }
-        if (SP > 0 && kk < SP) {
-#pragma unroll
-          for (int q = 0; q < C::INS; ++q)
-            if ((q * SPAN / C::INS) / C::TN == kk * C::TM + i) dma_one(q, kt);
-        }
       }
     };
     // Instruction order of one straight-line step: MFMA m is followed by the
     // reads r with r * MF / NR == m and the loads d with d * MF / ND == m.
-    auto interleave = [&](int kk, bool reads, bool refill_here) __attribute__((always_inline)) {
+    auto interleave = [&](bool reads, bool refill_here) __attribute__((always_inline)) {
       if constexpr (FULL) {
         constexpr int NR = C::TM + C::TN;
-        int nd = 0;
-        if (refill_here) {
-          if (SP == 0) nd = C::INS;
-          else {
-#pragma unroll
-            for (int q = 0; q < C::INS; ++q)
-              if ((q * SPAN / C::INS) / MF == kk) ++nd;
-          }
-        }
+        const int nd = refill_here ? (AL ? C::INS : C::B_INS) : 0;
 #pragma unroll
         for (int m = 0; m < MF; ++m) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
@@ -260,17 +269,15 @@ void gemm_v3_kernel(const GroupedGemm p, int n_tiles) {
     };
     // One slice: refill, KK-1 steps that also read the next step's fragments,
     // then (unless it is the last slice) the hand-over to the next slice and
-    // the last step.
-    auto slice = [&](int kt, bool last) __attribute__((always_inline)) {
-      if (SP == 0) {
+    // the last step.  steady: every refill of this iteration exists.
+    auto slice = [&](int kt, bool steady, bool last) __attribute__((always_inline)) {
 #pragma unroll
-        for (int q = 0; q < C::INS; ++q) dma_one(q, kt);
-      }
+      for (int q = 0; q < C::INS; ++q) load_q(q, kt, steady);
 #pragma unroll
       for (int kk = 0; kk < C::KK - 1; ++kk) {
         load_frags((kk + 1) & 1, kt, kk + 1);
-        mfma_step(kk & 1, kk, kt);
-        interleave(kk, true, kk == 0 || SP > 0);
+        mfma_step(kk & 1);
+        interleave(true, kk == 0 && steady);
         __builtin_amdgcn_sched_barrier(0);
       }
       // the last step's fragments are in registers before the slot is handed
@@ -278,21 +285,29 @@ void gemm_v3_kernel(const GroupedGemm p, int n_tiles) {
       // last MFMAs run
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       if (!last) {
-        slice_ready();
+        slice_ready(steady);
         load_frags(0, kt + 1, 0);
       }
-      mfma_step(1, C::KK - 1, kt);
-      interleave(C::KK - 1, !last, false);
+      mfma_step(1);
+      interleave(!last, false);
       __builtin_amdgcn_sched_barrier(0);
     };
-    slice_ready();
+    slice_ready(NSTB - 2 < nk);
     load_frags(0, 0, 0);
-    for (int kt = 0; kt < nk - 1; ++kt) slice(kt, false);
-    slice(nk - 1, true);
+    const int n_steady = max(0, nk - NSTB + 1);     // iterations whose refills all exist
+    int kt = 0;
+    for (; kt < n_steady && kt < nk - 1; ++kt) slice(kt, true, false);
+    for (; kt < nk - 1; ++kt) slice(kt, false, false);
+    slice(nk - 1, false, true);
   };
-  if (act_i == C::TM) k_loop(std::true_type{});
-  else k_loop(std::false_type{});
-  wait_vm<0>();   // the ring's last loads land before the workgroup's LDS is released
+  if (act_i == C::TM) {
+    if (a_live) k_loop(std::true_type{}, std::true_type{});
+    else k_loop(std::true_type{}, std::false_type{});
+  } else {
+    if (a_live) k_loop(std::false_type{}, std::true_type{});
+    else k_loop(std::false_type{}, std::false_type{});
+  }
+  wait_vm<0>();   // nothing is in flight into LDS when the staging below reuses it
 
   // Epilogue: the activation is applied in registers, each wave's output
   // block goes to its own LDS region and is read back as 16-byte row chunks
@@ -325,7 +340,7 @@ void gemm_v3_kernel(const GroupedGemm p, int n_tiles) {
 #pragma unroll
         for (int j = 0; j < C::TN; ++j) {
           float v = acc[i][j][r];
-          if constexpr (EPI == EPI_GELU) v = gelu_erf_f32(v);
+          if constexpr (EPI == EPI_GELU) v = gelu_bf16out(v);
           *reinterpret_cast<bf16_t*>(srow + sbyte(row, j * 64 + (lane & 31) * 2)) = f32_to_bf16(v);
         }
       }
@@ -378,7 +393,7 @@ inline int m_bound3(const GroupedGemm& p, int bm) {
   return p.M_max / bm + (p.G < p.M_max ? p.G : p.M_max);
 }
 
-template <int BM, int BN, int WGM, int WGN, int BK, int NST, int SP, int OCC, bool PERS, int EPI, int NSTB = NST>
+template <int BM, int BN, int WGM, int WGN, int BK, int NST, int NSTB, int OCC, bool PERS, int EPI>
 hipError_t launch_cfg3(const GroupedGemm& p, hipStream_t s) {
   using C = Cfg3<BM, BN, WGM, WGN, BK, NST, NSTB>;
   if (p.K % BK != 0) return hipErrorInvalidValue;
@@ -391,10 +406,10 @@ hipError_t launch_cfg3(const GroupedGemm& p, hipStream_t s) {
   if (PERS) blocks = std::min<long long>(blocks, (long long)num_cus() * OCC);
   // dynamic LDS above 64 KB has to be allowed explicitly
   hipError_t e = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&gemm_v3_kernel<BM, BN, WGM, WGN, BK, NST, NSTB, SP, OCC, PERS, EPI, bf16_t>),
+      reinterpret_cast<const void*>(&gemm_v3_kernel<BM, BN, WGM, WGN, BK, NST, NSTB, OCC, PERS, EPI, bf16_t>),
       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((gemm_v3_kernel<BM, BN, WGM, WGN, BK, NST, NSTB, SP, OCC, PERS, EPI, bf16_t>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((gemm_v3_kernel<BM, BN, WGM, WGN, BK, NST, NSTB, OCC, PERS, EPI, bf16_t>), dim3((unsigned)blocks),
                      dim3(C::THREADS), C::LDS, s, p, n_tiles);
   return hipGetLastError();
 }
@@ -402,34 +417,22 @@ hipError_t launch_cfg3(const GroupedGemm& p, hipStream_t s) {
 template <int EPI>
 hipError_t launch_v3_epi(const GroupedGemm& p, int cfg, hipStream_t s) {
   switch (cfg) {
+    //                       BM   BN WGM WGN  BK NST NSTB OCC   PERS
     // one workgroup per CU
-    case 0: return launch_cfg3<256, 256, 2, 2, 32, 4, 0, 1, false, EPI>(p, s);
-    case 1: return launch_cfg3<256, 256, 2, 2, 32, 5, 0, 1, false, EPI>(p, s);
-    case 2: return launch_cfg3<256, 256, 2, 2, 64, 2, 0, 1, false, EPI>(p, s);
-    case 3: return launch_cfg3<128, 256, 1, 4, 32, 4, 0, 1, false, EPI>(p, s);
-    case 4: return launch_cfg3<256, 256, 2, 4, 32, 4, 0, 1, false, EPI>(p, s);
-    case 5: return launch_cfg3<256, 256, 2, 4, 32, 5, 0, 1, false, EPI>(p, s);
-    case 6: return launch_cfg3<256, 256, 2, 4, 64, 2, 0, 1, false, EPI>(p, s);
-    case 7: return launch_cfg3<256, 256, 2, 4, 32, 4, 1, 1, false, EPI>(p, s);
-    case 8: return launch_cfg3<256, 256, 2, 2, 32, 4, 1, 1, false, EPI>(p, s);
-    case 9: return launch_cfg3<256, 256, 2, 4, 64, 2, 1, 1, false, EPI>(p, s);
-    case 10: return launch_cfg3<256, 256, 2, 4, 64, 2, 3, 1, false, EPI>(p, s);
+    case 0: return launch_cfg3<256, 256, 2, 4, 64, 2, 3, 1, false, EPI>(p, s);
+    case 1: return launch_cfg3<256, 256, 2, 4, 64, 2, 2, 1, false, EPI>(p, s);
+    case 2: return launch_cfg3<256, 256, 2, 2, 64, 2, 3, 1, false, EPI>(p, s);
+    case 3: return launch_cfg3<256, 256, 2, 2, 64, 2, 2, 1, false, EPI>(p, s);
+    case 4: return launch_cfg3<256, 256, 2, 4, 32, 4, 4, 1, false, EPI>(p, s);
+    case 11: return launch_cfg3<128, 256, 1, 4, 32, 4, 4, 1, false, EPI>(p, s);
     // two workgroups per CU (<= 80 KB of LDS each)
-    case 11: return launch_cfg3<128, 128, 2, 2, 64, 2, 0, 2, false, EPI>(p, s);
-    case 12: return launch_cfg3<128, 128, 2, 2, 32, 4, 0, 2, false, EPI>(p, s);
-    case 13: return launch_cfg3<128, 256, 2, 2, 32, 3, 0, 2, false, EPI>(p, s);
-    case 14: return launch_cfg3<64, 256, 1, 4, 32, 4, 0, 2, false, EPI>(p, s);
+    case 5: return launch_cfg3<128, 128, 2, 2, 32, 4, 4, 2, false, EPI>(p, s);
+    case 6: return launch_cfg3<128, 128, 2, 2, 64, 2, 2, 2, false, EPI>(p, s);
+    case 7: return launch_cfg3<128, 128, 2, 2, 64, 2, 3, 2, false, EPI>(p, s);
+    case 8: return launch_cfg3<128, 256, 2, 2, 32, 3, 3, 2, false, EPI>(p, s);
     // persistent weight streaming for shallow groups (one m-tile per group)
-    case 15: return launch_cfg3<64, 256, 1, 4, 64, 4, 0, 1, true, EPI>(p, s);
-    case 16: return launch_cfg3<64, 256, 1, 4, 64, 3, 0, 1, true, EPI>(p, s);
-    case 17: return launch_cfg3<64, 256, 1, 4, 32, 8, 0, 1, true, EPI>(p, s);
-    case 18: return launch_cfg3<32, 256, 1, 4, 64, 4, 0, 1, true, EPI>(p, s);
-    case 19: return launch_cfg3<64, 256, 1, 4, 32, 4, 0, 2, true, EPI>(p, s);
-    // weights (B) fetched one slice further ahead than the activations (A)
-    case 20: return launch_cfg3<256, 256, 2, 4, 64, 2, 0, 1, false, EPI, 3>(p, s);
-    case 21: return launch_cfg3<256, 256, 2, 2, 64, 2, 0, 1, false, EPI, 3>(p, s);
-    case 22: return launch_cfg3<256, 256, 2, 4, 64, 2, 1, 1, false, EPI, 3>(p, s);
-    case 23: return launch_cfg3<64, 256, 1, 4, 64, 2, 0, 1, true, EPI, 4>(p, s);
+    case 9: return launch_cfg3<64, 256, 1, 4, 64, 4, 4, 1, true, EPI>(p, s);
+    case 10: return launch_cfg3<64, 256, 1, 4, 32, 4, 4, 2, true, EPI>(p, s);
   }
   return hipErrorInvalidValue;
 }
@@ -437,8 +440,7 @@ hipError_t launch_v3_epi(const GroupedGemm& p, int cfg, hipStream_t s) {
 }  // namespace
 
 int gemm_v3_bm(int cfg) {
-  static const int bm[] = {256, 256, 256, 128, 256, 256, 256, 256, 256, 256, 256, 128, 128, 128, 64,
-                           64, 64, 64, 32, 64, 256, 256, 256, 64};
+  static const int bm[] = {256, 256, 256, 256, 256, 128, 128, 128, 128, 64, 64, 128};
   return (cfg >= 0 && cfg < kGemmV3Configs) ? bm[cfg] : 0;
 }
 
