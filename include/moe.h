@@ -15,7 +15,9 @@
  *     work enqueued on `stream` has completed.  Inputs are never written.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Every call only enqueues work on that stream: no host synchronisation,
- *     no device-to-host reads, no device allocation or free.
+ *     no device-to-host reads, no device allocation or free.  (The layer
+ *     forward also forks work onto a library-owned stream and joins it back;
+ *     see moe_layer_forward.)
  *   - Validation is synchronous and happens before anything is enqueued: when
  *     a call returns anything but MOE_OK, nothing was launched.  A launch
  *     failure returns MOE_ERR_HIP (the HIP error is cleared and its text is
@@ -217,7 +219,14 @@ typedef struct {
  *   stats [2E + 2] float32 optional: f[0..E), P[E..2E), aux_loss, imbalance
  *   dropped [1] int32 optional
  *   alpha: balance-loss coefficient (used with stats)
- *   ws: moe_workspace_size(MOE_OP_LAYER) bytes. */
+ *   ws: moe_workspace_size(MOE_OP_LAYER) bytes.
+ * Streams: with shared experts, their gate/up projection (which needs only x)
+ * runs on a stream the library creates once per device (default priority),
+ * forked from `stream` with an event at the start of the call and joined back
+ * to it before the routed experts, so every output is complete when `stream`
+ * passes the call.  Calls from several host threads are serialised around the
+ * fork and join.  If a call fails after enqueueing, work already enqueued on
+ * either stream may still run. */
 moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* weights,
                              const void* x, void* y, int32_t* topk_idx, float* topk_w,
                              int32_t* counts, float alpha, float* stats, int32_t* dropped,
@@ -238,8 +247,10 @@ typedef enum {
 } moe_stage;
 
 /* moe_layer_forward with stage timing: identical work, and for every stage s
- * that runs, hipEventRecord(stage_events[2s], stream) before its kernels and
- * hipEventRecord(stage_events[2s+1], stream) after them.  stage_events holds
+ * that runs, hipEventRecord(stage_events[2s], <its stream>) before its kernels
+ * and hipEventRecord(stage_events[2s+1], <its stream>) after them, where the
+ * shared gate/up stage runs on the library's auxiliary stream and the others
+ * on `stream`.  stage_events holds
  * 2 * MOE_NUM_STAGES caller-created hipEvent_t handles (entries may be NULL;
  * NULL array = no timing, i.e. moe_layer_forward).  For profiling tools. */
 moe_status moe_layer_forward_timed(const moe_config* cfg, const moe_weights* weights,

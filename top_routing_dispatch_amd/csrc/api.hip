@@ -7,6 +7,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "common.h"
 #include "moe.h"
 
@@ -103,7 +105,7 @@ size_t ws_stats(const moe_config* c) {
 
 struct Layout {
   size_t logits, flags, wsplit, probs, idx, w, tile_counts, counts, offsets, tile_prefix, tile_prefix2, row_of, tor, h,
-      yperm, partial, total;
+      h_shared, yperm, partial, total;
 };
 
 Layout layer_layout(const moe_config* c, const Derived& d) {
@@ -125,9 +127,9 @@ Layout layer_layout(const moe_config* c, const Derived& d) {
   L.tile_prefix2 = take(3 * (E + 1) * 4);
   L.row_of = take(T * k * 4);
   L.tor = take((size_t)d.rows_cap * 4);
-  const size_t h_routed = (size_t)d.rows_cap * c->d_ff * es;
-  const size_t h_shared = (size_t)T * c->num_shared * c->d_ff_shared * es;
-  L.h = take(h_routed > h_shared ? h_routed : h_shared);
+  // the shared experts run beside the routed ones: separate activations
+  L.h = take((size_t)d.rows_cap * c->d_ff * es);
+  L.h_shared = take((size_t)T * c->num_shared * c->d_ff_shared * es);
   L.yperm = take((size_t)d.rows_cap * c->d_model * es);
   L.partial = take((size_t)ceil_div(c->num_tokens, kStatsChunk) * E * 4);
   L.total = o;
@@ -311,6 +313,66 @@ moe_status run_ffn(int act, int activation, int G, int D, int F, int max_rows, c
   MOE_TRY_HIP("expert down", launch_gemm(act, pl.cfg_dn, g2, s));
   if (pl.split) MOE_TRY_HIP("expert down (shallow groups)", launch_gemm(act, pl.cfg_sh, g2s, s));
   MOE_TRY(mark(ev, stage_down, 1, s));
+  return MOE_OK;
+}
+
+// One projection of an ungrouped (shared-expert) FFN over `rows` rows:
+// gate/up with SwiGLU into h (up == true), or down from h into y_out.
+moe_status run_ffn_part(int act, int activation, int G, int D, int F, int rows, const void* x_in, const void* w13,
+                        const void* w2, void* h, void* y_out, hipStream_t s, void* const* ev, int stage, bool up) {
+  const FfnPlan pl = plan_ffn(act, D, F, rows, G, false);
+  GroupedGemm g{};
+  if (up) {
+    g.A = x_in; g.lda = D; g.B = w13; g.b_group_stride = (long long)(activation == SWIGLU ? 2 : 1) * F * D;
+    g.C = h; g.ldc = F; g.N = F; g.K = D;
+    g.epilogue = activation == SWIGLU ? EPI_SWIGLU : EPI_GELU;
+  } else {
+    g.A = h; g.lda = F; g.B = w2; g.b_group_stride = (long long)D * F;
+    g.C = y_out; g.ldc = D; g.N = D; g.K = F;
+    g.epilogue = EPI_STORE_ACT;
+  }
+  g.a_rows = nullptr; g.M_max = rows; g.G = G; g.offsets = nullptr; g.tile_prefix = nullptr;
+  MOE_TRY(mark(ev, stage, 0, s));
+  MOE_TRY_HIP(up ? "shared gate/up" : "shared down", launch_gemm(act, up ? pl.cfg_up : pl.cfg_dn, g, s));
+  MOE_TRY(mark(ev, stage, 1, s));
+  return MOE_OK;
+}
+
+// How the shared experts run beside the routed path: 0 = after the routed
+// experts on the caller's stream; 1 = gate/up on the auxiliary stream during
+// routing, joined before the routed experts; 2 = both projections on the
+// auxiliary stream, joined before the combine.  MOE_SHARED_OVERLAP overrides
+// (tuning aid).
+int shared_overlap() {
+  const char* env = getenv("MOE_SHARED_OVERLAP");
+  if (env != nullptr && *env != '\0' && atoi(env) >= 0 && atoi(env) <= 2) return atoi(env);
+  return 2;
+}
+
+// A library-owned stream per device for the layer's work that does not depend
+// on the routing (the shared experts' gate/up projection), forked from and
+// joined back to the caller's stream with events.  Default priority.  The
+// mutex keeps the fork / join sequences of concurrent host threads from
+// interleaving.
+struct AuxStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+AuxStream g_aux[kMaxDevices];
+std::mutex g_aux_mu;
+
+moe_status aux_stream(AuxStream** out) {
+  int dev = 0;
+  MOE_TRY_HIP("hipGetDevice", hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  AuxStream& a = g_aux[dev];
+  if (a.s == nullptr) {
+    MOE_TRY_HIP("auxiliary stream", hipStreamCreateWithFlags(&a.s, hipStreamNonBlocking));
+    MOE_TRY_HIP("fork event", hipEventCreateWithFlags(&a.fork, hipEventDisableTiming));
+    MOE_TRY_HIP("join event", hipEventCreateWithFlags(&a.join, hipEventDisableTiming));
+  }
+  *out = &a;
   return MOE_OK;
 }
 
@@ -516,6 +578,28 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const moe_weights* wt,
   int32_t* tor = at<int32_t>(ws, L.tor);
   float* probs = want_stats ? at<float>(ws, L.probs) : nullptr;
 
+  // The shared experts' gate/up projection needs only x: it runs on the
+  // auxiliary stream while routing and permutation (short, latency-bound
+  // kernels that leave most of the chip idle) run here, and is joined before
+  // the routed experts, which need the whole chip.
+  const bool shared = any && cfg->num_shared > 0;
+  const int SF = cfg->num_shared * cfg->d_ff_shared;
+  const int overlap = shared ? shared_overlap() : 0;
+  std::unique_lock<std::mutex> aux_lock(g_aux_mu, std::defer_lock);
+  AuxStream* aux = nullptr;
+  if (overlap > 0) {
+    aux_lock.lock();
+    MOE_TRY(aux_stream(&aux));
+    MOE_TRY_HIP("fork", hipEventRecord(aux->fork, s));
+    MOE_TRY_HIP("fork", hipStreamWaitEvent(aux->s, aux->fork, 0));
+    MOE_TRY(run_ffn_part(cfg->act_dtype, SWIGLU, 1, D, SF, T, x, wt->ws13, wt->ws2, at<void>(ws, L.h_shared), y,
+                         aux->s, ev, MOE_STAGE_SHARED_GATE_UP, true));
+    if (overlap == 2)
+      MOE_TRY(run_ffn_part(cfg->act_dtype, SWIGLU, 1, D, SF, T, x, wt->ws13, wt->ws2, at<void>(ws, L.h_shared), y,
+                           aux->s, ev, MOE_STAGE_SHARED_DOWN, false));
+    MOE_TRY_HIP("join", hipEventRecord(aux->join, aux->s));
+  }
+
   if (any) {
     float* logits = at<float>(ws, L.logits);
     MOE_TRY(mark(ev, MOE_STAGE_ROUTER_LOGITS, 0, s));
@@ -537,6 +621,8 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const moe_weights* wt,
   MOE_TRY_HIP("permute", launch_permute(pa, s));
   MOE_TRY(mark(ev, MOE_STAGE_PERMUTE, 1, s));
 
+  if (overlap == 1) MOE_TRY_HIP("join", hipStreamWaitEvent(s, aux->join, 0));
+
   if (any) {
     void* h = at<void>(ws, L.h);
     void* yperm = at<void>(ws, L.yperm);
@@ -544,13 +630,14 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const moe_weights* wt,
       MOE_TRY(run_ffn(cfg->act_dtype, cfg->activation, E, D, cfg->d_ff, d.rows_cap, x, tor, off, tp,
                       at<int32_t>(ws, L.tile_prefix2), wt->w13, wt->w2, h, yperm, s, ev, MOE_STAGE_EXPERT_GATE_UP,
                       MOE_STAGE_EXPERT_DOWN));
-    const void* y_shared = nullptr;
-    if (cfg->num_shared > 0) {
-      const int SF = cfg->num_shared * cfg->d_ff_shared;
-      MOE_TRY(run_ffn(cfg->act_dtype, SWIGLU, 1, D, SF, T, x, nullptr, nullptr, nullptr, nullptr, wt->ws13,
-                      wt->ws2, h, y, s, ev, MOE_STAGE_SHARED_GATE_UP, MOE_STAGE_SHARED_DOWN));
-      y_shared = y;
-    }
+    if (shared && overlap == 0)
+      MOE_TRY(run_ffn_part(cfg->act_dtype, SWIGLU, 1, D, SF, T, x, wt->ws13, wt->ws2, at<void>(ws, L.h_shared), y,
+                           s, ev, MOE_STAGE_SHARED_GATE_UP, true));
+    if (shared && overlap != 2)
+      MOE_TRY(run_ffn_part(cfg->act_dtype, SWIGLU, 1, D, SF, T, x, wt->ws13, wt->ws2, at<void>(ws, L.h_shared), y,
+                           s, ev, MOE_STAGE_SHARED_DOWN, false));
+    if (overlap == 2) MOE_TRY_HIP("join", hipStreamWaitEvent(s, aux->join, 0));
+    const void* y_shared = shared ? y : nullptr;
     MOE_TRY(mark(ev, MOE_STAGE_COMBINE, 0, s));
     MOE_TRY_HIP("combine", launch_combine(yperm, row_of, w, y_shared, y, T, cfg->top_k, D, cfg->act_dtype, s));
     MOE_TRY(mark(ev, MOE_STAGE_COMBINE, 1, s));
