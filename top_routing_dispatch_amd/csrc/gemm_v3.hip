@@ -46,7 +46,14 @@ struct Cfg3 {
   static_assert(BM % (RPI * NWAVES) == 0 && BN % (RPI * NWAVES) == 0, "load split");
   static_assert(TM >= 1 && TN >= 1, "wave tile");
   static_assert(LDS <= 160 * 1024, "LDS");
-  static_assert(NSTB >= NST && NST >= 2, "B is fetched at least as far ahead as A");
+  static_assert(NST >= 2 && NSTB >= 2, "ring depths");
+  static constexpr int NMAX = NST > NSTB ? NST : NSTB;
+  // Within one refill the shallower ring's loads are issued first.
+  static constexpr bool A_FIRST = NST <= NSTB;
+  __host__ __device__ static constexpr bool is_a(int q) { return A_FIRST ? q < A_INS : q >= B_INS; }
+  __host__ __device__ static constexpr int a_idx(int q) { return A_FIRST ? q : q - B_INS; }
+  __host__ __device__ static constexpr int b_idx(int q) { return A_FIRST ? q - A_INS : q; }
+  __host__ __device__ static constexpr int depth(int q) { return is_a(q) ? NST : NSTB; }
 
 };
 
@@ -151,18 +158,19 @@ void gemm_v3_kernel(const GroupedGemm p, int n_tiles) {
 
   // Slice j of A lives in A slot j % NST, slice j of B in B slot j % NSTB.
   // Iteration it refills A with slice it + NST - 1 and B with slice
-  // it + NSTB - 1 (B runs further ahead); load instruction q of an iteration:
-  // A rows first, then B rows.
+  // it + NSTB - 1; load instruction q of an iteration belongs to the
+  // shallower ring first, then to the deeper one.
   const int nk = K / BK;
   auto dma_one = [&](int q, int it) __attribute__((always_inline)) {
-    if (q < C::A_INS) {
-      const int j = it + NST - 1;
-      dma16_3(a_rsrc, a_off[q] + j * (unsigned)C::RB,
-              smem + (j % NST) * C::A_BYTES + (wave * C::A_INS + q) * 1024);
+    const int j = it + C::depth(q) - 1;
+    if (C::is_a(q)) {
+      const int qa = C::a_idx(q);
+      dma16_3(a_rsrc, a_off[qa] + j * (unsigned)C::RB,
+              smem + (j % NST) * C::A_BYTES + (wave * C::A_INS + qa) * 1024);
     } else {
-      const int j = it + NSTB - 1;
-      dma16_3(b_rsrc, b_off[q - C::A_INS] + j * (unsigned)C::RB,
-              smem + C::B_RING + (j % NSTB) * C::B_BYTES + (wave * C::B_INS + q - C::A_INS) * 1024);
+      const int qb = C::b_idx(q);
+      dma16_3(b_rsrc, b_off[qb] + j * (unsigned)C::RB,
+              smem + C::B_RING + (j % NSTB) * C::B_BYTES + (wave * C::B_INS + qb) * 1024);
     }
   };
 
@@ -193,27 +201,30 @@ void gemm_v3_kernel(const GroupedGemm p, int n_tiles) {
     constexpr bool AL = decltype(al_c)::value;          // this wave loads A rows
     constexpr int WA = AL ? C::A_INS : 0;
     // Loads younger than the later of this wave's A(kt+1) / B(kt+1) when
-    // slice kt+1 is awaited.
-    constexpr int WAIT = AL ? (NSTB > NST ? C::B_INS : 0) + (WA + C::B_INS) * (NST - 2)
-                            : C::B_INS * (NSTB - 2);
+    // slice kt+1 is awaited: the deeper ring's loads of the same refill, then
+    // the refills of the shallower depth minus two iterations.
+    constexpr int WAIT = !AL ? C::B_INS * (NSTB - 2)
+                         : NST == NSTB ? (WA + C::B_INS) * (NST - 2)
+                         : NSTB > NST ? C::B_INS + (WA + C::B_INS) * (NST - 2)
+                                      : WA + (WA + C::B_INS) * (NSTB - 2);
     static_assert(WAIT <= 63, "vmcnt range");
     // Load q of iteration it (iteration it refills A with slice it + NST - 1
     // and B with slice it + NSTB - 1); `exists` skips the check that the
     // slice exists, in the steady part of the loop where it always does.
     auto load_q = [&](int q, int it, bool exists) __attribute__((always_inline)) {
-      const int j = q < C::A_INS ? it + NST - 1 : it + NSTB - 1;
-      if ((AL || q >= C::A_INS) && (exists || j < nk)) dma_one(q, it);
+      const int j = it + C::depth(q) - 1;
+      if ((AL || !C::is_a(q)) && (exists || j < nk)) dma_one(q, it);
     };
-    // Prologue: iterations 1-NSTB .. -1 of the same schedule.
+    // Prologue: iterations 1-NMAX .. -1 of the same schedule.
 #pragma unroll
-    for (int it = 1 - NSTB; it < 0; ++it) {
+    for (int it = 1 - C::NMAX; it < 0; ++it) {
 #pragma unroll
       for (int q = 0; q < C::INS; ++q)
-        if ((q < C::A_INS ? it + NST - 1 : it + NSTB - 1) >= 0) load_q(q, it, false);
+        if (it + C::depth(q) - 1 >= 0) load_q(q, it, false);
     }
     // Slice `next` has landed for every wave, and every wave is done with the
     // slots refilled next.  While every refill so far was of an existing
-    // slice (next + NSTB - 2 < nk), exactly WAIT younger loads are
+    // slice (next + NMAX - 2 < nk), exactly WAIT younger loads are
     // outstanding; in the last iterations everything is awaited.
     auto slice_ready = [&](bool exact) __attribute__((always_inline)) {
       if (exact) wait_vm<WAIT>();
@@ -292,9 +303,9 @@ void gemm_v3_kernel(const GroupedGemm p, int n_tiles) {
       interleave(!last, false);
       __builtin_amdgcn_sched_barrier(0);
     };
-    slice_ready(NSTB - 2 < nk);
+    slice_ready(C::NMAX - 2 < nk);
     load_frags(0, 0, 0);
-    const int n_steady = max(0, nk - NSTB + 1);     // iterations whose refills all exist
+    const int n_steady = max(0, nk - C::NMAX + 1);  // iterations whose refills all exist
     int kt = 0;
     for (; kt < n_steady && kt < nk - 1; ++kt) slice(kt, true, false);
     for (; kt < nk - 1; ++kt) slice(kt, false, false);
