@@ -50,6 +50,12 @@ def oracle_forward(cfg, inp, sel_bias=None):
     return O.forward(cfg, inp.x, inp.w_router, b, lambda e: (inp.w13[e], inp.w2[e]), inp.shared)
 
 
+def refinement_margin(s32: np.ndarray) -> np.ndarray:
+    """Per-token logit margin within which the route kernel trusts its float32
+    logits (tokens with keys closer than that are refined in float64)."""
+    return np.ldexp(1.0 + np.abs(s32).max(axis=1), -16)
+
+
 def route_differences(cfg, ref, idx_gpu: np.ndarray, sel_bias) -> np.ndarray:
     """Tokens whose GPU selection differs from the oracle's; asserts that every
     such token is a near-tie the oracle itself cannot decide (1e-6 relative)."""

@@ -20,16 +20,11 @@ import workloads as W
 from oracle import moe_oracle as O
 from workloads.torch_io import act_torch_dtype, to_numpy, to_torch, upload_experts
 
-from parity import W_TOL, out_tol, rel_err, route_differences, row_rel_err
+from parity import W_TOL, out_tol, refinement_margin, rel_err, route_differences, row_rel_err
 
 pytestmark = pytest.mark.gpu
 
 SAMPLE = {"switch": 32, "mixtral": 12, "deepseekmoe": 24, "deepseekv3": 8}
-
-
-def refinement_margin(s32: np.ndarray) -> np.ndarray:
-    """Per-token logit margin the route kernel trusts float32 within."""
-    return np.ldexp(1.0 + np.abs(s32).max(axis=1), -16)
 
 
 @pytest.mark.parametrize("name", ["switch", "mixtral", "deepseekmoe", "deepseekv3"])

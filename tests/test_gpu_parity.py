@@ -10,7 +10,7 @@ import workloads as W
 from oracle import moe_oracle as O
 from workloads.torch_io import act_torch_dtype, to_numpy, to_torch
 
-from parity import (BF16_TOL, W_TOL, DeviceLayer, check_layer, oracle_forward, out_tol, rel_err,
+from parity import (BF16_TOL, W_TOL, DeviceLayer, check_layer, oracle_forward, out_tol, refinement_margin, rel_err,
                     route_differences, row_rel_err)
 
 pytestmark = pytest.mark.gpu
@@ -349,3 +349,43 @@ def test_shallow_group_split(cfg, split, monkeypatch):
     got = DeviceLayer(cfg, inp).layer()
     diff, err = check_layer(cfg, inp, ref, got)
     print(f"  max rel err {err:.3e}")
+
+
+ROUTER_SHAPES = [
+    # the router kernel's range (65 <= E <= 256, D % 64 == 0): float32 and bf16
+    # weights, a ragged expert count, a row count that is not a multiple of 32
+    W.MoEConfig("router_e128_f32w", 300, 256, 128, 2, 64, scoring=W.SOFTMAX_TOPK, renormalize=1,
+                router_dtype=W.F32),
+    W.MoEConfig("router_e200_bf16w", 257, 192, 200, 4, 64, scoring=W.SIGMOID_BIAS, zipf_s=1.2),
+    W.MoEConfig("router_e256_f32w", 129, 512, 256, 8, 64, scoring=W.TOPK_SOFTMAX, router_dtype=W.F32),
+]
+
+
+@pytest.mark.parametrize("kernel", ["1", "0"])
+@pytest.mark.parametrize("cfg", ROUTER_SHAPES, ids=lambda c: c.name)
+def test_router_logits_and_selection(cfg, kernel, monkeypatch):
+    """Router logits within the refinement margin of the float64 logits and the
+    selection equal to the oracle's, with the router kernel (1) and the general
+    GEMM path (0)."""
+    monkeypatch.setenv("MOE_ROUTER_KERNEL", kernel)
+    print(f"[router {kernel}] {cfg.name}", flush=True)
+    T, E, k = cfg.num_tokens, cfg.num_experts, cfg.top_k
+    inp = W.make_inputs(cfg, with_experts=False)
+    ref = O.route(inp.x, inp.w_router, inp.sel_bias, k, cfg.scoring, cfg.renormalize)
+    x = to_torch(inp.x, "cuda")
+    wr = to_torch(inp.w_router, "cuda")
+    bias = to_torch(inp.sel_bias, "cuda") if inp.sel_bias is not None else None
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    tw = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    ws = M.workspace(cfg, M.MOE_OP_ROUTE, "cuda")
+    M.moe_route(cfg, x, wr, bias, idx, tw, None, ws)
+    torch.cuda.synchronize()
+    s32 = ws[: T * E * 4].view(torch.float32).reshape(T, E).cpu().numpy().astype(np.float64)
+    err = np.abs(s32 - ref["logits"]).max(axis=1)
+    margin = refinement_margin(s32)
+    print(f"  logit error max {err.max():.3e}; smallest margin/error {np.min(margin / np.maximum(err, 1e-30)):.1f}")
+    assert (err * 16 < margin).all()
+    gi = to_numpy(idx)
+    diff = route_differences(cfg, ref, gi, inp.sel_bias)
+    same = np.setdiff1d(np.arange(T), diff)
+    assert rel_err(to_numpy(tw)[same], ref["w"][same]) <= W_TOL

@@ -150,6 +150,12 @@ size_t router_split_bytes(const moe_config* c) {
   return router_split(c) ? carve((size_t)c->num_experts * 3 * c->d_model * 2) : 0;
 }
 
+// MOE_ROUTER_KERNEL=0 keeps the router on the general GEMM (tuning aid).
+bool router_kernel_enabled() {
+  const char* env = getenv("MOE_ROUTER_KERNEL");
+  return env == nullptr || *env == '\0' || atoi(env) != 0;
+}
+
 moe_status run_router_logits(const moe_config* c, const void* x, const void* w_router, float* logits,
                              void* split_ws, hipStream_t s) {
   GroupedGemm g{};
@@ -160,7 +166,19 @@ moe_status run_router_logits(const moe_config* c, const void* x, const void* w_r
   g.G = 1; g.offsets = nullptr; g.tile_prefix = nullptr;
   g.epilogue = EPI_STORE_F32;
   g.a_kwrap = 0;
-  if (c->router_dtype == BF16) {
+  const int planes = c->router_dtype == BF16 ? 1 : 3;
+  if (c->act_dtype == BF16 && (planes == 1 || router_split(c)) &&
+      router_kernel_fits(c->num_tokens, c->num_experts, c->d_model, planes) && router_kernel_enabled()) {
+    const bf16_t* wp = static_cast<const bf16_t*>(w_router);
+    if (planes == 3) {
+      bf16_t* sp = static_cast<bf16_t*>(split_ws);
+      MOE_TRY_HIP("router weight split", launch_split_bf16x3(static_cast<const float*>(w_router), c->num_experts,
+                                                             c->d_model, sp, s));
+      wp = sp;
+    }
+    MOE_TRY_HIP("router logits", launch_router_logits(static_cast<const bf16_t*>(x), wp, planes, logits,
+                                                      c->num_tokens, c->num_experts, c->d_model, s));
+  } else if (c->router_dtype == BF16) {
     MOE_TRY_HIP("router logits (bf16)", launch_gemm_bf16(g, s));
   } else if (router_split(c)) {
     bf16_t* planes = static_cast<bf16_t*>(split_ws);

@@ -237,11 +237,17 @@ hipError_t launch_cfg(const GroupedGemm& p, hipStream_t s) {
   if (m_tiles == 0 || n_tiles == 0) return hipSuccess;
   const long long blocks = (long long)m_tiles * n_tiles;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  // dynamic LDS above 64 KB has to be allowed explicitly
-  hipError_t e = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&gemm_v2_kernel<BM, BN, WGM, WGN, NST, EPI, bf16_t>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, C::STAGE * NST);
+  // dynamic LDS above 64 KB has to be allowed explicitly, once per device
+  static bool allowed[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64 || !allowed[dev]) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_v2_kernel<BM, BN, WGM, WGN, NST, EPI, bf16_t>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, C::STAGE * NST);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < 64) allowed[dev] = true;
+  }
   hipLaunchKernelGGL((gemm_v2_kernel<BM, BN, WGM, WGN, NST, EPI, bf16_t>), dim3((unsigned)blocks),
                      dim3(C::THREADS), C::STAGE * NST, s, p, n_tiles);
   return hipGetLastError();

@@ -415,11 +415,17 @@ hipError_t launch_cfg3(const GroupedGemm& p, hipStream_t s) {
   long long blocks = (long long)m_tiles * n_tiles;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   if (PERS) blocks = std::min<long long>(blocks, (long long)num_cus() * OCC);
-  // dynamic LDS above 64 KB has to be allowed explicitly
-  hipError_t e = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&gemm_v3_kernel<BM, BN, WGM, WGN, BK, NST, NSTB, OCC, PERS, EPI, bf16_t>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+  // dynamic LDS above 64 KB has to be allowed explicitly, once per device
+  static bool allowed[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64 || !allowed[dev]) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_v3_kernel<BM, BN, WGM, WGN, BK, NST, NSTB, OCC, PERS, EPI, bf16_t>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < 64) allowed[dev] = true;
+  }
   hipLaunchKernelGGL((gemm_v3_kernel<BM, BN, WGM, WGN, BK, NST, NSTB, OCC, PERS, EPI, bf16_t>), dim3((unsigned)blocks),
                      dim3(C::THREADS), C::LDS, s, p, n_tiles);
   return hipGetLastError();

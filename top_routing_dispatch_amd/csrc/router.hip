@@ -1,0 +1,170 @@
+// Router logits s[t, e] = sum_d x[t, d] w[e, d] for bf16 tokens and bf16
+// weights given as NP planes (NP = 1: the weights; NP = 3: the exact split of
+// float32 weights into hi + mid + lo made by launch_split_bf16x3), for
+// 65 <= E <= 256 and D a multiple of 64 ("Top-k 路由" page, step 1 of the
+// gate: one bias-free linear layer).
+//
+// One workgroup owns 32 tokens and every expert, so each token row is read
+// once and each token fragment feeds NP MFMAs.  Operands stream through an
+// LDS ring (up to 4 deep) of 64-deep K slices (buffer loads with the LDS bit).
+// Every slice's MFMA sums are added into float64 accumulators, which keeps the
+// logits within a small multiple of float32 rounding of the exact sum, as the
+// selection's near-tie refinement requires.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_void_r;
+
+__device__ __forceinline__ void dma16_r(__amdgpu_buffer_rsrc_t r, unsigned voff, char* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_r*)lds, 16, voff, 0, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm_r() {
+  static_assert(N >= 0 && N <= 63, "vmcnt");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// 128-byte rows (64 bf16), chunk c of row r in slot c ^ ((r >> 1) & 7).
+__device__ __forceinline__ int swz_r(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
+
+template <int BN, int NP>
+struct RCfg {
+  static constexpr int BM = 32;                       // tokens per workgroup
+  static constexpr int XB = BM * 128, WB = NP * BN * 128;  // bytes per slice
+  static constexpr int STAGE = XB + WB;
+  static constexpr int NST = (160 * 1024) / STAGE < 4 ? (160 * 1024) / STAGE : 4;
+  static constexpr int X_INS = XB / 1024 / 4, W_INS = WB / 1024 / 4;   // per wave per slice
+  static constexpr int INS = X_INS + W_INS;
+  static constexpr int TN = BN / 4 / 32;              // 32-column blocks per wave
+  static_assert(XB % 4096 == 0 && WB % 4096 == 0, "load split");
+  static_assert(TN >= 1, "wave tile");
+  static_assert(NST >= 2 && STAGE * NST <= 160 * 1024, "LDS");
+  static_assert(INS * (NST - 2) <= 63, "vmcnt range");
+};
+
+template <int BN, int NP>
+__global__ __launch_bounds__(256) void router_logits_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ w,
+                                                            float* __restrict__ logits, int T, int E, int D) {
+  using C = RCfg<BN, NP>;
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row0 = blockIdx.x * C::BM;
+  const int rows = min(C::BM, T - row0);
+  const int nk = D / 64;
+
+  const __amdgpu_buffer_rsrc_t x_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(x), 0, 0x7fffffff, 0x00020000);
+  const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(w), 0, (int)((unsigned)E * NP * (unsigned)D * 2u), 0x00020000);
+  // byte offsets of this wave's loads at slice 0 (rows past the end clamped);
+  // the weight slice holds plane p of BN rows at LDS rows p*BN ..
+  unsigned x_off[C::X_INS], w_off[C::W_INS];
+#pragma unroll
+  for (int q = 0; q < C::X_INS; ++q) {
+    const int r = (wave * C::X_INS + q) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    x_off[q] = ((unsigned)(row0 + min(r, rows - 1)) * (unsigned)D + c * 8) * 2u;
+  }
+#pragma unroll
+  for (int q = 0; q < C::W_INS; ++q) {
+    const int r = (wave * C::W_INS + q) * 8 + (lane >> 3);     // LDS row: plane r / BN, expert r % BN
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    const unsigned e = (unsigned)min(r % BN, E - 1), pl = (unsigned)(r / BN);
+    w_off[q] = ((e * NP + pl) * (unsigned)D + c * 8) * 2u;
+  }
+  auto issue = [&](int kt) __attribute__((always_inline)) {
+    char* st = smem + (kt % C::NST) * C::STAGE;
+#pragma unroll
+    for (int q = 0; q < C::X_INS; ++q) dma16_r(x_rsrc, x_off[q] + kt * 128u, st + (wave * C::X_INS + q) * 1024);
+#pragma unroll
+    for (int q = 0; q < C::W_INS; ++q)
+      dma16_r(w_rsrc, w_off[q] + kt * 128u, st + C::XB + (wave * C::W_INS + q) * 1024);
+  };
+
+  floatx16_t acc[C::TN];
+  double dacc[C::TN][16];
+#pragma unroll
+  for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { acc[j][r] = 0.0f; dacc[j][r] = 0.0; }
+
+  for (int s = 0; s < C::NST - 1 && s < nk; ++s) issue(s);
+  const int fr = lane & 31, fh = lane >> 5;
+  for (int kt = 0; kt < nk; ++kt) {
+    // slice kt has landed: while the refills so far all existed, exactly the
+    // NST-2 younger slices' loads are outstanding
+    if (kt + C::NST - 2 < nk) wait_vm_r<C::INS * (C::NST - 2)>();
+    else wait_vm_r<0>();
+    __builtin_amdgcn_s_barrier();            // ... for every wave; slot kt-1 is free
+    if (kt + C::NST - 1 < nk) issue(kt + C::NST - 1);
+    const char* sx = smem + (kt % C::NST) * C::STAGE;
+    const char* sw = sx + C::XB;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(sx + swz_r(fr, kk * 2 + fh));
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) {
+        const int r = wave * (BN / 4) + j * 32 + fr;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+          const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(sw + swz_r(p * BN + r, kk * 2 + fh));
+          acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) { dacc[j][r] += (double)acc[j][r]; acc[j][r] = 0.0f; }
+  }
+
+  // lane holds column (lane & 31) and rows 8*(r/4) + 4*(lane/32) + (r%4)
+#pragma unroll
+  for (int j = 0; j < C::TN; ++j) {
+    const int e = wave * (BN / 4) + j * 32 + fr;
+    if (e >= E) continue;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int rl = 8 * (r >> 2) + 4 * fh + (r & 3);
+      if (rl < rows) logits[(long long)(row0 + rl) * E + e] = (float)dacc[j][r];
+    }
+  }
+}
+
+template <int BN, int NP>
+hipError_t launch_router_cfg(const bf16_t* x, const bf16_t* w, float* logits, int T, int E, int D, hipStream_t s) {
+  using C = RCfg<BN, NP>;
+  static bool allowed[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64 || !allowed[dev]) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&router_logits_kernel<BN, NP>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, C::STAGE * C::NST);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < 64) allowed[dev] = true;
+  }
+  hipLaunchKernelGGL((router_logits_kernel<BN, NP>), dim3(ceil_div(T, C::BM)), dim3(256), C::STAGE * C::NST, s, x, w,
+                     logits, T, E, D);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool router_kernel_fits(int T, int E, int D, int planes) {
+  return T > 0 && D > 0 && D % 64 == 0 && E > 64 && (planes == 1 ? E <= 256 : planes == 3 && E <= 128);
+}
+
+hipError_t launch_router_logits(const bf16_t* x, const bf16_t* w, int planes, float* logits, int T, int E, int D,
+                                hipStream_t s) {
+  if (!router_kernel_fits(T, E, D, planes)) return hipErrorInvalidValue;
+  if (planes == 3) return launch_router_cfg<128, 3>(x, w, logits, T, E, D, s);
+  if (E <= 128) return launch_router_cfg<128, 1>(x, w, logits, T, E, D, s);
+  return launch_router_cfg<256, 1>(x, w, logits, T, E, D, s);
+}
+
+}  // namespace moe
