@@ -18,8 +18,8 @@
 // whose key lies within 2 tau below the k-th.  Ranking refined experts by their
 // float64 key and all others by their float32 key gives the order of the exact
 // keys: any pair with an unrefined member is more than 2 tau apart.  The first
-// pass flags such tokens; a second pass (one wavefront per flagged token)
-// redoes only those.
+// pass refines such tokens in the same wavefront (up to 128 experts) or flags
+// them for a second pass (one wavefront per flagged token).
 #include <float.h>
 #include <limits.h>
 
@@ -172,60 +172,12 @@ __device__ __forceinline__ void write_selection(const RouteArgs& a, int t, int l
   }
 }
 
-// Pass 1: float32 selection of every token, the per-token probabilities, and
-// a flag for the tokens that need float64 (rewritten by pass 2).
+// Refinement of one token on one wavefront: redo the float32 selection,
+// compute float64 logits for the experts that need them (a D-long dot product
+// of the stored inputs each, loads unrolled ahead), rank the candidates and
+// rewrite the token's selection.
 template <int EPL>
-__global__ __launch_bounds__(256) void route_select_kernel(const RouteArgs a, int32_t* __restrict__ flags) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= a.T) return;                        // uniform per wave
-  const int E = a.E;
-  TokenSel<EPL> st;
-  select_f32(a, t, lane, st);
-  const unsigned long long cm = close_mask(st, lane);
-  if (lane == 0) flags[t] = cm != 0;
-  write_selection(a, t, lane, st, st.my_e);
-
-  if (a.probs != nullptr) {
-    float* prow = a.probs + (long long)t * E;
-    if (a.scoring == SIGMOID_BIAS) {
-      float av[EPL], as = 0.0f;
-#pragma unroll
-      for (int i = 0; i < EPL; ++i) {
-        av[i] = (lane + kWave * i < E) ? sigmoid_f32(st.s[i]) : 0.0f;
-        as += av[i];
-      }
-      as = wave_sum_f32(as);
-#pragma unroll
-      for (int i = 0; i < EPL; ++i)
-        if (lane + kWave * i < E) prow[lane + kWave * i] = av[i] / as;
-    } else {
-      float m = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < EPL; ++i)
-        if (lane + kWave * i < E) m = fmaxf(m, st.s[i]);
-      const float smax = wave_max_f32(m);
-      float zz = 0.0f;
-#pragma unroll
-      for (int i = 0; i < EPL; ++i)
-        if (lane + kWave * i < E) zz += expf(st.s[i] - smax);
-      const float z = wave_sum_f32(zz);
-#pragma unroll
-      for (int i = 0; i < EPL; ++i)
-        if (lane + kWave * i < E) prow[lane + kWave * i] = expf(st.s[i] - smax) / z;
-    }
-  }
-}
-
-// Pass 2: one wavefront per flagged token (all other waves exit at once).  It
-// redoes the float32 selection, computes float64 logits for the experts that
-// need them (a D-long dot product of the stored inputs each, loads unrolled
-// ahead), ranks the candidates and rewrites the token's selection.
-template <int EPL>
-__global__ __launch_bounds__(256) void route_refine_kernel(const RouteArgs a, const int32_t* __restrict__ flags) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= a.T || flags[t] == 0) return;       // uniform per wave
+__device__ __forceinline__ void refine_token(const RouteArgs& a, int t, int lane) {
   const bool sig = a.scoring == SIGMOID_BIAS;
   TokenSel<EPL> st;
   select_f32(a, t, lane, st);
@@ -296,9 +248,70 @@ __global__ __launch_bounds__(256) void route_refine_kernel(const RouteArgs a, co
   write_selection(a, t, lane, st, my_e);
 }
 
+// Pass 2 (more than 128 experts): one wavefront per flagged token, all other
+// waves exit at once.
+template <int EPL>
+__global__ __launch_bounds__(256) void route_refine_kernel(const RouteArgs a, const int32_t* __restrict__ flags) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.T || flags[t] == 0) return;       // uniform per wave
+  refine_token<EPL>(a, t, lane);
+}
+
+// Pass 1: float32 selection of every token, the per-token probabilities, and
+// either the refinement of the tokens that need float64 in the same wave
+// (FUSED, up to 128 experts) or a flag for pass 2.
+template <int EPL, bool FUSED>
+__global__ __launch_bounds__(256) void route_select_kernel(const RouteArgs a, int32_t* __restrict__ flags) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;                        // uniform per wave
+  const int E = a.E;
+  TokenSel<EPL> st;
+  select_f32(a, t, lane, st);
+  const unsigned long long cm = close_mask(st, lane);
+  if (!FUSED && lane == 0) flags[t] = cm != 0;
+  write_selection(a, t, lane, st, st.my_e);
+
+  if (a.probs != nullptr) {
+    float* prow = a.probs + (long long)t * E;
+    if (a.scoring == SIGMOID_BIAS) {
+      float av[EPL], as = 0.0f;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        av[i] = (lane + kWave * i < E) ? sigmoid_f32(st.s[i]) : 0.0f;
+        as += av[i];
+      }
+      as = wave_sum_f32(as);
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (lane + kWave * i < E) prow[lane + kWave * i] = av[i] / as;
+    } else {
+      float m = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (lane + kWave * i < E) m = fmaxf(m, st.s[i]);
+      const float smax = wave_max_f32(m);
+      float zz = 0.0f;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (lane + kWave * i < E) zz += expf(st.s[i] - smax);
+      const float z = wave_sum_f32(zz);
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (lane + kWave * i < E) prow[lane + kWave * i] = expf(st.s[i] - smax) / z;
+    }
+  }
+  if (FUSED && cm != 0) refine_token<EPL>(a, t, lane);   // rewrites the selection
+}
+
 template <int EPL>
 hipError_t launch_epl(const RouteArgs& a, int32_t* flags, hipStream_t s) {
-  hipLaunchKernelGGL(route_select_kernel<EPL>, dim3(ceil_div(a.T, 4)), dim3(256), 0, s, a, flags);
+  if constexpr (EPL <= 2) {
+    hipLaunchKernelGGL((route_select_kernel<EPL, true>), dim3(ceil_div(a.T, 4)), dim3(256), 0, s, a, flags);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((route_select_kernel<EPL, false>), dim3(ceil_div(a.T, 4)), dim3(256), 0, s, a, flags);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(route_refine_kernel<EPL>, dim3(ceil_div(a.T, 4)), dim3(256), 0, s, a,
