@@ -182,25 +182,45 @@ template <> struct Chunk<bf16_t> {
   }
 };
 
+// One workgroup per token.  The token's row indices and weights go to LDS
+// once; each chunk then issues the loads of up to 8 rows before the first
+// multiply-add, so they are in flight together.  The sum runs over the slots
+// in order, as a chain of fused multiply-adds.
 template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ yp, const int32_t* __restrict__ row_of,
                                                       const float* __restrict__ tw, const T* ys, T* y,
                                                       int k, int D) {
   constexpr int N = Chunk<T>::N;
+  constexpr int G = 8;                         // rows in flight per chunk
+  __shared__ int srow[kMaxTopK];
+  __shared__ float sw[kMaxTopK];
   const int t = blockIdx.x;
+  if ((int)threadIdx.x < k) {
+    srow[threadIdx.x] = row_of[(long long)t * k + threadIdx.x];
+    sw[threadIdx.x] = tw[(long long)t * k + threadIdx.x];
+  }
+  __syncthreads();
   const int chunks = D / N;
   for (int c = threadIdx.x; c < chunks; c += blockDim.x) {
     float acc[N];
 #pragma unroll
     for (int q = 0; q < N; ++q) acc[q] = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      const int row = row_of[(long long)t * k + j];
-      if (row < 0) continue;
-      const float w = tw[(long long)t * k + j];
-      float v[N];
-      Chunk<T>::load(yp + (long long)row * D + c * N, v);
+    for (int j0 = 0; j0 < k; j0 += G) {
+      float v[G][N];
 #pragma unroll
-      for (int q = 0; q < N; ++q) acc[q] = fmaf(w, v[q], acc[q]);
+      for (int g = 0; g < G; ++g) {
+        const int j = j0 + g;
+        if (j < k && srow[j] >= 0) Chunk<T>::load(yp + (long long)srow[j] * D + c * N, v[g]);
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int j = j0 + g;
+        if (j < k && srow[j] >= 0) {
+          const float w = sw[j];
+#pragma unroll
+          for (int q = 0; q < N; ++q) acc[q] = fmaf(w, v[g][q], acc[q]);
+        }
+      }
     }
     if (ys != nullptr) {
       float v[N];
@@ -240,15 +260,22 @@ __global__ __launch_bounds__(256) void stats_partial_kernel(const StatsArgs a) {
     a.partial[(long long)blockIdx.x * a.E + e] = (sp[0][el] + sp[1][el]) + (sp[2][el] + sp[3][el]);
 }
 
-// f, P, loss, imbalance, dropped.  Thread (e, j) of the 1024 sums partial
-// chunks j, j + TPE, ... of expert e (TPE threads per expert), combined in LDS
-// in a fixed order; scalar results by a fixed-shape tree.
+// f, P, loss, imbalance, dropped.  Thread (e, j) sums the partial chunks
+// j, j + TPE, ... of expert e (TPE <= 64 consecutive lanes per expert) and the
+// group is combined by a fixed shuffle tree; the scalar results use a fixed
+// shuffle tree per wave and then the waves in order.
 __global__ __launch_bounds__(kMaxExperts) void stats_final_kernel(const StatsArgs a, int nchunks, int tpe) {
-  __shared__ float sf[kMaxExperts];
-  __shared__ int si[kMaxExperts];
-  __shared__ int sd[kMaxExperts];
-  const int tid = threadIdx.x;
+  __shared__ float sP[kMaxExperts];
+  __shared__ float wf[kMaxExperts / 64];
+  __shared__ int wc[kMaxExperts / 64], wd[kMaxExperts / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int e = tid / tpe, j = tid % tpe;
+  // per-expert counts (issued before the partial sums' adds)
+  int c = 0, drop = 0;
+  if (tid < a.E) {
+    c = a.counts[tid];
+    drop = c - min(c, a.capacity);
+  }
   float s = 0.0f;
   if (e < a.E) {
     float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -256,51 +283,34 @@ __global__ __launch_bounds__(kMaxExperts) void stats_final_kernel(const StatsArg
     for (; b < nchunks; b += tpe, q = (q + 1) & 3) v[q] += a.partial[(long long)b * a.E + e];
     s = (v[0] + v[1]) + (v[2] + v[3]);
   }
-  sf[tid] = s;
-  __syncthreads();
-  for (int d = tpe / 2; d >= 1; d >>= 1) {
-    if (j < d) sf[tid] += sf[tid + d];
-    __syncthreads();
-  }
-  const float psum = sf[e * tpe];
-  __syncthreads();
-  // one thread per expert from here on
-  const int ee = tid;
-  float fe = 0.0f, pe = 0.0f;
-  int c = 0, drop = 0;
-  const float A = (float)a.T * (float)a.k;
-  if (ee < a.E) {
-    c = a.counts[ee];
-    drop = c - min(c, a.capacity);
-    fe = a.T > 0 ? (float)c / A : 0.0f;
-  }
+  for (int d = tpe / 2; d >= 1; d >>= 1) s += __shfl_down(s, d, tpe);
   if (j == 0 && e < a.E) {
-    pe = a.T > 0 ? psum / (float)a.T : 0.0f;
+    const float pe = a.T > 0 ? s / (float)a.T : 0.0f;
     if (a.P) a.P[e] = pe;
-    sf[e] = pe;            // stash P[e] (slot e was read by its owner thread already)
+    sP[e] = pe;
   }
   __syncthreads();
-  if (ee < a.E) {
-    pe = sf[ee];
-    if (a.f) a.f[ee] = fe;
+  const float A = (float)a.T * (float)a.k;
+  float fp = 0.0f;
+  if (tid < a.E) {
+    const float fe = a.T > 0 ? (float)c / A : 0.0f;
+    if (a.f) a.f[tid] = fe;
+    fp = fe * sP[tid];
   }
-  __syncthreads();
-  sf[tid] = (ee < a.E) ? fe * pe : 0.0f;
-  si[tid] = c;
-  sd[tid] = drop;
-  __syncthreads();
-  for (int d = kMaxExperts / 2; d >= 1; d >>= 1) {
-    if (tid < d) {
-      sf[tid] += sf[tid + d];
-      si[tid] = max(si[tid], si[tid + d]);
-      sd[tid] += sd[tid + d];
-    }
-    __syncthreads();
+  for (int d = 32; d >= 1; d >>= 1) {
+    fp += __shfl_down(fp, d);
+    c = max(c, __shfl_down(c, d));
+    drop += __shfl_down(drop, d);
   }
+  if (lane == 0) { wf[wave] = fp; wc[wave] = c; wd[wave] = drop; }
+  __syncthreads();
   if (tid == 0) {
-    if (a.aux_loss) *a.aux_loss = a.alpha * (float)a.E * sf[0];
-    if (a.imbalance) *a.imbalance = a.T > 0 ? (float)si[0] / (A / (float)a.E) : 0.0f;
-    if (a.dropped) *a.dropped = sd[0];
+    float sf = 0.0f;
+    int cm = 0, sd = 0;
+    for (int w = 0; w < kMaxExperts / 64; ++w) { sf += wf[w]; cm = max(cm, wc[w]); sd += wd[w]; }
+    if (a.aux_loss) *a.aux_loss = a.alpha * (float)a.E * sf;
+    if (a.imbalance) *a.imbalance = a.T > 0 ? (float)cm / (A / (float)a.E) : 0.0f;
+    if (a.dropped) *a.dropped = sd;
   }
 }
 
@@ -357,8 +367,8 @@ hipError_t launch_load_stats(const StatsArgs& a, hipStream_t s) {
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  int tpe = 1;                          // threads per expert: largest power of two with E * tpe <= 1024
-  while (a.E * tpe * 2 <= kMaxExperts) tpe *= 2;
+  int tpe = 1;                          // threads per expert: largest power of two <= 64 with E * tpe <= 1024
+  while (tpe < 64 && a.E * tpe * 2 <= kMaxExperts) tpe *= 2;
   hipLaunchKernelGGL(stats_final_kernel, dim3(1), dim3(kMaxExperts), 0, s, a, nchunks, tpe);
   return hipGetLastError();
 }
