@@ -143,7 +143,9 @@ moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
  *   x_perm       [A_cap, D] act_dtype out, or NULL: x_perm[r] = x[token_of_row[r]]
  *                           for r < offsets[E]; later rows are not written
  * Rows are grouped by ascending expert id and, inside an expert, by ascending
- * token.  Bit-exact and deterministic. */
+ * token.  Bit-exact and deterministic.  Ids outside [0, E) and repeats of an
+ * id already used by an earlier slot of the same token (neither is produced by
+ * moe_route) are skipped: their row_of is -1 and they are not counted. */
 moe_status moe_permute(const moe_config* cfg, const int32_t* topk_idx, const void* x,
                        int32_t* counts, int32_t* offsets, int32_t* row_of,
                        int32_t* token_of_row, void* x_perm,
