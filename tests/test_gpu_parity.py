@@ -309,8 +309,8 @@ V2_SHAPES = [
 
 
 # -1: general kernel; 0-9: pipelined 8-wave kernel; 10-21: kernel with 32- or 64-deep slices
-# (19, 20: persistent weight-streaming tiles)
-GEMM_TILE_CONFIGS = range(-1, 22)
+# (19, 20: persistent tiles); 22-29: persistent weight-streaming kernel
+GEMM_TILE_CONFIGS = range(-1, 30)
 
 
 @pytest.mark.parametrize("gemm_cfg", [str(c) for c in GEMM_TILE_CONFIGS])
@@ -346,6 +346,33 @@ def test_shallow_group_split(cfg, split, monkeypatch):
     ref = oracle_forward(cfg, inp)
     counts = np.bincount(ref["idx"].ravel(), minlength=cfg.num_experts)
     print(f"  group rows: min {counts.min()} max {counts.max()}, <= 64: {(counts <= 64).sum()}")
+    got = DeviceLayer(cfg, inp).layer()
+    diff, err = check_layer(cfg, inp, ref, got)
+    print(f"  max rel err {err:.3e}")
+
+
+WS_SHAPES = [
+    # more tiles than workgroups of the persistent weight-streaming kernel, so
+    # that its ring crosses tile boundaries: a 512-deep GELU contraction with
+    # capacity (8 slices per tile) and a 192-deep SwiGLU one (3 slices per
+    # tile: the loads run more than a whole tile ahead)
+    W.MoEConfig("ws_gelu_many_tiles", 2048, 512, 128, 1, 2048, scoring=W.SOFTMAX_TOPK, renormalize=0,
+                activation=W.GELU, router_dtype=W.F32, capacity_factor=1.25),
+    W.MoEConfig("ws_swiglu_many_tiles", 1024, 192, 96, 2, 1536, zipf_s=1.0),
+]
+
+
+@pytest.mark.parametrize("gemm_cfg", ["default"] + [str(c) for c in range(22, 30)])
+@pytest.mark.parametrize("cfg", WS_SHAPES, ids=lambda c: c.name)
+def test_weight_streaming_many_tiles(cfg, gemm_cfg, monkeypatch):
+    """The persistent weight-streaming GEMM (its configurations 22-29, and the
+    default choice for these shallow groups) against the oracle with several
+    tiles per workgroup."""
+    if gemm_cfg != "default":
+        monkeypatch.setenv("MOE_GEMM_CFG", gemm_cfg)
+    print(f"[ws {gemm_cfg}] {cfg.name}", flush=True)
+    inp = W.make_inputs(cfg)
+    ref = oracle_forward(cfg, inp)
     got = DeviceLayer(cfg, inp).layer()
     diff, err = check_layer(cfg, inp, ref, got)
     print(f"  max rel err {err:.3e}")

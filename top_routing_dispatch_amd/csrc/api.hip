@@ -218,10 +218,11 @@ moe_status mark(void* const* ev, int stage, int which, hipStream_t s) {
 // Kernel choice for one projection: -1 = the general kernels (any K), else a
 // tile configuration of the pipelined bf16 kernel (K a multiple of 64).  The
 // tile height follows the average rows per group; MOE_GEMM_CFG=<n> overrides
-// the choice (tuning aid; -1 forces the general kernels).
-int pick_cfg(int act, int K, int max_rows, int G) {
+// the choice (tuning aid; -1 forces the general kernels), MOE_GEMM_CFG_DOWN
+// that of the down projection alone.
+int pick_cfg(int act, int K, int max_rows, int G, bool down) {
   if (act != BF16 || K % 64 != 0) return -1;
-  const char* env = getenv("MOE_GEMM_CFG");
+  const char* env = down && getenv("MOE_GEMM_CFG_DOWN") != nullptr ? getenv("MOE_GEMM_CFG_DOWN") : getenv("MOE_GEMM_CFG");
   if (env != nullptr && *env != '\0') {
     const int c = atoi(env);
     return (c >= -1 && c < kGemmConfigs) ? c : -1;
@@ -229,10 +230,13 @@ int pick_cfg(int act, int K, int max_rows, int G) {
   // measured on MI355X at the Switch / Mixtral / DeepSeekMoE / DeepSeek-V3
   // shapes: 256x256 tiles on 8 waves (64-deep slices, interleaved schedule,
   // weights fetched two slices ahead) once groups are a few hundred rows
-  // deep, 128x128 tiles with 32-deep slices and two workgroups per CU for
-  // shallow (weight-streaming) groups
+  // deep; for shallow groups the persistent weight-streaming kernel with
+  // 128x128 tiles and waves side by side over the columns (gate/up: two
+  // workgroups per CU, so that one's activation epilogue overlaps the
+  // other's weight stream; down: one workgroup per CU, four slices deep)
   const int avg = G > 0 ? max_rows / G : max_rows;
-  return kGemmV2Configs + (avg >= 160 ? 0 : 5);
+  if (avg >= 160) return kGemmV2Configs;
+  return kGemmV2Configs + kGemmV3Configs + (down ? 5 : 6);
 }
 
 int cfg_bm(int act, int cfg) {
@@ -241,7 +245,9 @@ int cfg_bm(int act, int cfg) {
     GroupedGemm dummy{};
     return gemm_bf16_bm(dummy);
   }
-  return cfg < kGemmV2Configs ? gemm_v2_bm(cfg) : gemm_v3_bm(cfg - kGemmV2Configs);
+  if (cfg < kGemmV2Configs) return gemm_v2_bm(cfg);
+  if (cfg < kGemmV2Configs + kGemmV3Configs) return gemm_v3_bm(cfg - kGemmV2Configs);
+  return gemm_ws_bm(cfg - kGemmV2Configs - kGemmV3Configs);
 }
 
 struct FfnPlan {
@@ -257,15 +263,15 @@ struct FfnPlan {
 // average.  MOE_GEMM_SPLIT=0 / 1 overrides the choice (tuning aid).
 FfnPlan plan_ffn(int act, int D, int F, int max_rows, int G, bool grouped) {
   FfnPlan pl;
-  pl.cfg_up = pick_cfg(act, D, max_rows, G);
-  pl.cfg_dn = pick_cfg(act, F, max_rows, G);
+  pl.cfg_up = pick_cfg(act, D, max_rows, G, false);
+  pl.cfg_dn = pick_cfg(act, F, max_rows, G, true);
   pl.bm_up = cfg_bm(act, pl.cfg_up);
   pl.bm_dn = cfg_bm(act, pl.cfg_dn);
-  int sh = 9;
-  const char* sh_env = getenv("MOE_GEMM_SHCFG");       // tuning aid: persistent configuration 9 or 10
-  if (sh_env != nullptr && *sh_env != '\0' && (atoi(sh_env) == 9 || atoi(sh_env) == 10)) sh = atoi(sh_env);
-  pl.cfg_sh = kGemmV2Configs + sh;
-  pl.sh_rows = gemm_v3_bm(sh);
+  pl.cfg_sh = kGemmV2Configs + 9;
+  const char* sh_env = getenv("MOE_GEMM_SHCFG");       // tuning aid: a configuration index >= kGemmV2Configs
+  if (sh_env != nullptr && *sh_env != '\0' && atoi(sh_env) >= kGemmV2Configs && atoi(sh_env) < kGemmConfigs)
+    pl.cfg_sh = atoi(sh_env);
+  pl.sh_rows = cfg_bm(act, pl.cfg_sh);
   const bool able = grouped && pl.cfg_up >= 0 && pl.cfg_dn >= 0 && D % 64 == 0 && F % 64 == 0;
   const int avg = G > 0 ? max_rows / G : max_rows;
   pl.split = able && D >= 1024 && F >= 1024 && avg < 320;
@@ -276,6 +282,7 @@ FfnPlan plan_ffn(int act, int D, int F, int max_rows, int G, bool grouped) {
 
 hipError_t launch_gemm(int act, int cfg, const GroupedGemm& g, hipStream_t s) {
   if (act != BF16) return launch_gemm_f32(g, F32, F32, s);
+  if (cfg >= kGemmV2Configs + kGemmV3Configs) return launch_gemm_ws(g, cfg - kGemmV2Configs - kGemmV3Configs, s);
   if (cfg >= kGemmV2Configs) return launch_gemm_v3(g, cfg - kGemmV2Configs, s);
   if (cfg >= 0) return launch_gemm_v2(g, cfg, s);
   return launch_gemm_bf16(g, s);

@@ -57,6 +57,39 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   return xcd * per + (xcd < rem ? xcd : rem) + local;
 }
 
+// Compute units of the current device (cached after the first call).
+inline int num_cus() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      n = v;
+    else
+      n = 256;
+  }
+  return n;
+}
+
+// gelu(z) = z * Phi(z) = z/2 * erfc(-z/sqrt(2)) for outputs rounded to bf16.
+// erfc(a), a >= 0, from Abramowitz & Stegun 7.1.26 (|error| <= 1.5e-7):
+// erfc(a) ~ t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-a^2), t = 1 / (1 + p a).
+// For z < 0 the result is z/2 * erfc(|x|) directly, so small values keep
+// their relative accuracy instead of coming out of 1 - erf.  Evaluated on
+// y = x * sqrt(log2 e), so that exp(-x^2) = 2^(-y^2) is one hardware exp2 and
+// p a = (p / sqrt(log2 e)) |y|.
+__device__ __forceinline__ float gelu_bf16out(float z) {
+  const float y = z * 0.84932180028801907f;               // z / sqrt(2) * sqrt(log2 e)
+  const float t = __builtin_amdgcn_rcpf(1.0f + 0.27273748087922250f * fabsf(y));
+  const float poly = t * (0.254829592f + t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
+  const float c = poly * __builtin_amdgcn_exp2f(-y * y);  // erfc(|z| / sqrt(2))
+  return 0.5f * z * (y >= 0.0f ? 2.0f - c : c);
+}
+
+// float32 -> bfloat16 bit pattern by the hardware conversion (round to
+// nearest even), for kernel outputs.
+__device__ __forceinline__ bf16_t f32_to_bf16_rn(float f) { return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f)); }
+
 // silu(z) = z * sigmoid(z); the reciprocal is the hardware one (1 ulp), which
 // keeps the result within a few ulp of the float32 quotient.
 __device__ __forceinline__ float silu_f32(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
@@ -107,7 +140,18 @@ __device__ __forceinline__ int tile_count(const GroupedGemm& p, int n_tiles) {
   return (p.offsets == nullptr ? ceil_div(p.M_max, BM) : p.tile_prefix[p.G]) * n_tiles;
 }
 
-template <int BM>
+//
+// SCALAR: the tables are read through the constant address space, so that
+// (uniform) reads become scalar loads, which a kernel with vector loads in
+// flight can wait for without waiting for those.
+typedef const __attribute__((address_space(4))) int32_t const_i32;
+template <bool SCALAR>
+__device__ __forceinline__ int ld_table(const int32_t* t, int i) {
+  if constexpr (SCALAR) return ((const_i32*)t)[i];
+  else return t[i];
+}
+
+template <int BM, bool SCALAR = false>
 __device__ __forceinline__ void decode_tile(const GroupedGemm& p, int n_tiles, int L, int& g, int& row0, int& rows,
                                             int& nt) {
   constexpr int GM = 8;
@@ -129,19 +173,20 @@ __device__ __forceinline__ void decode_tile(const GroupedGemm& p, int n_tiles, i
   int lo = 0, hi = p.G;                   // tp[lo] <= mtile < tp[hi]
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (tp[mid] <= mtile) lo = mid; else hi = mid;
+    if (ld_table<SCALAR>(tp, mid) <= mtile) lo = mid; else hi = mid;
   }
   g = lo;                                 // last group starting at or before: non-empty
-  const int mg = tp[g + 1] - tp[g];
-  const int local = L - tp[g] * n_tiles;
+  const int tg = ld_table<SCALAR>(tp, g);
+  const int mg = ld_table<SCALAR>(tp, g + 1) - tg;
+  const int local = L - tg * n_tiles;
   const int sub = local / (GM * n_tiles);
   const int first = sub * GM;
   const int gm = min(mg - first, GM);
   const int loc = local - sub * GM * n_tiles;
   const int m = first + loc % gm;
   nt = loc / gm;
-  row0 = p.offsets[g] + m * BM;
-  rows = min(BM, p.offsets[g + 1] - row0);
+  row0 = ld_table<SCALAR>(p.offsets, g) + m * BM;
+  rows = min(BM, ld_table<SCALAR>(p.offsets, g + 1) - row0);
 }
 
 // Tile of this workgroup in a grid sized for the upper bound of tiles:
@@ -180,9 +225,15 @@ int gemm_v2_bm(int cfg);
 // K % 64 == 0 for the 64-deep configuration).  Its tile configurations follow
 // the pipelined kernel's in one numbering: kGemmV2Configs + cfg.
 constexpr int kGemmV3Configs = 12;
-constexpr int kGemmConfigs = kGemmV2Configs + kGemmV3Configs;
 hipError_t launch_gemm_v3(const GroupedGemm& g, int cfg, hipStream_t s);
 int gemm_v3_bm(int cfg);
+// Persistent weight-streaming bf16 grouped GEMM for shallow groups (K % 64 ==
+// 0); its tile configurations follow in the same numbering:
+// kGemmV2Configs + kGemmV3Configs + cfg.
+constexpr int kGemmWsConfigs = 8;
+hipError_t launch_gemm_ws(const GroupedGemm& g, int cfg, hipStream_t s);
+int gemm_ws_bm(int cfg);
+constexpr int kGemmConfigs = kGemmV2Configs + kGemmV3Configs + kGemmWsConfigs;
 // float32 SIMT grouped GEMM.  a_dtype / b_dtype select float32 or bf16 operands.
 hipError_t launch_gemm_f32(const GroupedGemm& g, int a_dtype, int b_dtype, hipStream_t s);
 constexpr int kF32GemmBM = 64;

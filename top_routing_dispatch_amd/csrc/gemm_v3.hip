@@ -74,20 +74,6 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// gelu(z) = z * Phi(z) = z/2 * erfc(-z/sqrt(2)) for outputs rounded to bf16.
-// erfc(a), a >= 0, from Abramowitz & Stegun 7.1.26 (|error| <= 1.5e-7):
-// erfc(a) ~ t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-a^2), t = 1 / (1 + p a).
-// For z < 0 the result is z/2 * erfc(|x|) directly, so small values keep
-// their relative accuracy instead of coming out of 1 - erf.
-__device__ __forceinline__ float gelu_bf16out(float z) {
-  const float x = z * 0.70710678118654752f;
-  const float a = fabsf(x);
-  const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * a);
-  const float poly = t * (0.254829592f + t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
-  const float c = poly * __expf(-a * a);                  // erfc(|x|)
-  return 0.5f * z * (x >= 0.0f ? 2.0f - c : c);
-}
-
 template <int CPR>
 __device__ __forceinline__ int swz3(int r, int c) {
   return r * (CPR * 16) + ((c ^ ((r / (16 / CPR)) & (CPR - 1))) << 4);
@@ -346,13 +332,13 @@ void gemm_v3_kernel(const GroupedGemm p, int n_tiles) {
 #pragma unroll
         for (int q = 0; q < C::TN / 2; ++q)
           *reinterpret_cast<bf16_t*>(srow + sbyte(row, q * 64 + (lane & 31) * 2)) =
-              f32_to_bf16(silu_f32(acc[i][2 * q][r]) * acc[i][2 * q + 1][r]);
+              f32_to_bf16_rn(silu_f32(acc[i][2 * q][r]) * acc[i][2 * q + 1][r]);
       } else {
 #pragma unroll
         for (int j = 0; j < C::TN; ++j) {
           float v = acc[i][j][r];
           if constexpr (EPI == EPI_GELU) v = gelu_bf16out(v);
-          *reinterpret_cast<bf16_t*>(srow + sbyte(row, j * 64 + (lane & 31) * 2)) = f32_to_bf16(v);
+          *reinterpret_cast<bf16_t*>(srow + sbyte(row, j * 64 + (lane & 31) * 2)) = f32_to_bf16_rn(v);
         }
       }
     }
@@ -384,19 +370,6 @@ void gemm_v3_kernel(const GroupedGemm p, int n_tiles) {
   if constexpr (!PERS) break;
   __builtin_amdgcn_s_barrier();          // the staging reads are done before the next tile's loads land
   }
-}
-
-inline int num_cus() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      n = v;
-    else
-      n = 256;
-  }
-  return n;
 }
 
 inline int m_bound3(const GroupedGemm& p, int bm) {

@@ -177,7 +177,7 @@ template <> struct Chunk<bf16_t> {
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      w[i] = (uint32_t)f32_to_bf16(v[2 * i]) | ((uint32_t)f32_to_bf16(v[2 * i + 1]) << 16);
+      w[i] = (uint32_t)f32_to_bf16_rn(v[2 * i]) | ((uint32_t)f32_to_bf16_rn(v[2 * i + 1]) << 16);
     *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 };
