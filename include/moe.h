@@ -222,13 +222,15 @@ typedef struct {
  *   dropped [1] int32 optional
  *   alpha: balance-loss coefficient (used with stats)
  *   ws: moe_workspace_size(MOE_OP_LAYER) bytes.
- * Streams: with shared experts, their gate/up projection (which needs only x)
- * runs on a stream the library creates once per device (default priority),
- * forked from `stream` with an event at the start of the call and joined back
- * to it before the routed experts, so every output is complete when `stream`
- * passes the call.  Calls from several host threads are serialised around the
- * fork and join.  If a call fails after enqueueing, work already enqueued on
- * either stream may still run. */
+ * Streams: work that does not lie on the routed path runs on a stream the
+ * library creates once per device (default priority), forked from `stream`
+ * with events and joined back to it: the shared experts' projections (they
+ * need only x) from the start of the call, joined before the combine, and the
+ * load statistics (they need the probabilities and counts) from the end of
+ * the permutation, joined at the end of the call.  Every output is complete
+ * when `stream` passes the call.  Calls from several host threads are
+ * serialised around the forks and joins.  If a call fails after enqueueing,
+ * work already enqueued on either stream may still run. */
 moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* weights,
                              const void* x, void* y, int32_t* topk_idx, float* topk_w,
                              int32_t* counts, float alpha, float* stats, int32_t* dropped,
@@ -251,8 +253,8 @@ typedef enum {
 /* moe_layer_forward with stage timing: identical work, and for every stage s
  * that runs, hipEventRecord(stage_events[2s], <its stream>) before its kernels
  * and hipEventRecord(stage_events[2s+1], <its stream>) after them, where the
- * shared gate/up stage runs on the library's auxiliary stream and the others
- * on `stream`.  stage_events holds
+ * shared expert and load statistics stages run on the library's auxiliary
+ * stream and the others on `stream`.  stage_events holds
  * 2 * MOE_NUM_STAGES caller-created hipEvent_t handles (entries may be NULL;
  * NULL array = no timing, i.e. moe_layer_forward).  For profiling tools. */
 moe_status moe_layer_forward_timed(const moe_config* cfg, const moe_weights* weights,

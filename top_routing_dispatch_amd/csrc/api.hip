@@ -382,6 +382,7 @@ int shared_overlap() {
 struct AuxStream {
   hipStream_t s = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
+  hipEvent_t stats_fork = nullptr, stats_join = nullptr;   // load statistics beside the experts
 };
 constexpr int kMaxDevices = 64;
 AuxStream g_aux[kMaxDevices];
@@ -396,6 +397,8 @@ moe_status aux_stream(AuxStream** out) {
     MOE_TRY_HIP("auxiliary stream", hipStreamCreateWithFlags(&a.s, hipStreamNonBlocking));
     MOE_TRY_HIP("fork event", hipEventCreateWithFlags(&a.fork, hipEventDisableTiming));
     MOE_TRY_HIP("join event", hipEventCreateWithFlags(&a.join, hipEventDisableTiming));
+    MOE_TRY_HIP("fork event", hipEventCreateWithFlags(&a.stats_fork, hipEventDisableTiming));
+    MOE_TRY_HIP("join event", hipEventCreateWithFlags(&a.stats_join, hipEventDisableTiming));
   }
   *out = &a;
   return MOE_OK;
@@ -610,11 +613,16 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const moe_weights* wt,
   const bool shared = any && cfg->num_shared > 0;
   const int SF = cfg->num_shared * cfg->d_ff_shared;
   const int overlap = shared ? shared_overlap() : 0;
+  // The load statistics need only the probabilities and the counts: they run
+  // on the auxiliary stream beside the expert GEMMs, joined at the end.
+  const bool stats_aside = any && want_stats;
   std::unique_lock<std::mutex> aux_lock(g_aux_mu, std::defer_lock);
   AuxStream* aux = nullptr;
-  if (overlap > 0) {
+  if (overlap > 0 || stats_aside) {
     aux_lock.lock();
     MOE_TRY(aux_stream(&aux));
+  }
+  if (overlap > 0) {
     MOE_TRY_HIP("fork", hipEventRecord(aux->fork, s));
     MOE_TRY_HIP("fork", hipStreamWaitEvent(aux->s, aux->fork, 0));
     MOE_TRY(run_ffn_part(cfg->act_dtype, SWIGLU, 1, D, SF, T, x, wt->ws13, wt->ws2, at<void>(ws, L.h_shared), y,
@@ -646,6 +654,22 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const moe_weights* wt,
   MOE_TRY_HIP("permute", launch_permute(pa, s));
   MOE_TRY(mark(ev, MOE_STAGE_PERMUTE, 1, s));
 
+  StatsArgs sa{};
+  if (want_stats) {
+    sa.counts = cnt; sa.probs = probs; sa.partial = at<float>(ws, L.partial);
+    sa.T = T; sa.E = E; sa.k = cfg->top_k; sa.capacity = d.capacity; sa.alpha = alpha;
+    if (stats) { sa.f = stats; sa.P = stats + E; sa.aux_loss = stats + 2 * E; sa.imbalance = stats + 2 * E + 1; }
+    sa.dropped = dropped;
+  }
+  if (stats_aside) {
+    MOE_TRY_HIP("fork", hipEventRecord(aux->stats_fork, s));
+    MOE_TRY_HIP("fork", hipStreamWaitEvent(aux->s, aux->stats_fork, 0));
+    MOE_TRY(mark(ev, MOE_STAGE_LOAD_STATS, 0, aux->s));
+    MOE_TRY_HIP("load stats", launch_load_stats(sa, aux->s));
+    MOE_TRY(mark(ev, MOE_STAGE_LOAD_STATS, 1, aux->s));
+    MOE_TRY_HIP("join", hipEventRecord(aux->stats_join, aux->s));
+  }
+
   if (overlap == 1) MOE_TRY_HIP("join", hipStreamWaitEvent(s, aux->join, 0));
 
   if (any) {
@@ -668,12 +692,9 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const moe_weights* wt,
     MOE_TRY(mark(ev, MOE_STAGE_COMBINE, 1, s));
   }
 
-  if (want_stats) {
-    StatsArgs sa{};
-    sa.counts = cnt; sa.probs = probs; sa.partial = at<float>(ws, L.partial);
-    sa.T = T; sa.E = E; sa.k = cfg->top_k; sa.capacity = d.capacity; sa.alpha = alpha;
-    if (stats) { sa.f = stats; sa.P = stats + E; sa.aux_loss = stats + 2 * E; sa.imbalance = stats + 2 * E + 1; }
-    sa.dropped = dropped;
+  if (stats_aside) {
+    MOE_TRY_HIP("join", hipStreamWaitEvent(s, aux->stats_join, 0));
+  } else if (want_stats) {
     MOE_TRY(mark(ev, MOE_STAGE_LOAD_STATS, 0, s));
     MOE_TRY_HIP("load stats", launch_load_stats(sa, s));
     MOE_TRY(mark(ev, MOE_STAGE_LOAD_STATS, 1, s));

@@ -9,7 +9,9 @@
 //
 // One wavefront per token.  Lane l holds experts l, l+64, l+128, ...; the
 // k (+1) best are found by k (+1) rounds of a wave-wide arg-max with ties to
-// the lower expert index, and lane r keeps the r-th pick in a register.
+// the lower expert index (the maximum by DPP moves across the lanes, then the
+// first slot and lane holding it by ballots), and lane r keeps the r-th pick
+// in a register.
 //
 // Near-tie refinement: the logits arrive in float32.  Among the k+1 best keys,
 // pick r is "close" to pick r+1 when their float32 keys are within 2 tau (tau
@@ -17,9 +19,9 @@
 // when the run reaches the k-th/(k+1)-th boundary, so does every other expert
 // whose key lies within 2 tau below the k-th.  Ranking refined experts by their
 // float64 key and all others by their float32 key gives the order of the exact
-// keys: any pair with an unrefined member is more than 2 tau apart.  The first
-// pass refines such tokens in the same wavefront (up to 128 experts) or flags
-// them for a second pass (one wavefront per flagged token).
+// keys: any pair with an unrefined member is more than 2 tau apart.  Such
+// tokens are refined in their own wavefront, in the selection kernel (up to
+// 128 experts) or in a second pass (one wavefront per flagged token).
 #include <float.h>
 #include <limits.h>
 
@@ -28,27 +30,42 @@
 namespace moe {
 namespace {
 
-__device__ __forceinline__ float wave_max_f32(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  return v;
+// ---- wave-wide reductions ----
+// Float max / sum over the 64 lanes by DPP moves (row-local butterflies, then
+// the row broadcasts), in a fixed order; the result is read from lane 63 and
+// is wave-uniform.  `id` is the identity, which lanes outside a row mask take.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_f32(float v, float id) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(id), __float_as_int(v), CTRL, ROWS, 0xf, false));
 }
-__device__ __forceinline__ float wave_sum_f32(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+__device__ __forceinline__ float wave_max_u(float v) {
+  v = fmaxf(v, dpp_f32<0xb1, 0xf>(v, -INFINITY));    // lane ^ 1
+  v = fmaxf(v, dpp_f32<0x4e, 0xf>(v, -INFINITY));    // lane ^ 2
+  v = fmaxf(v, dpp_f32<0x141, 0xf>(v, -INFINITY));   // mirror inside 8 lanes
+  v = fmaxf(v, dpp_f32<0x140, 0xf>(v, -INFINITY));   // mirror inside 16 lanes
+  v = fmaxf(v, dpp_f32<0x142, 0xa>(v, -INFINITY));   // lane 15 of a row into the next
+  v = fmaxf(v, dpp_f32<0x143, 0xc>(v, -INFINITY));   // lane 31 into rows 2, 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ float wave_sum_u(float v) {
+  v += dpp_f32<0xb1, 0xf>(v, 0.0f);
+  v += dpp_f32<0x4e, 0xf>(v, 0.0f);
+  v += dpp_f32<0x141, 0xf>(v, 0.0f);
+  v += dpp_f32<0x140, 0xf>(v, 0.0f);
+  v += dpp_f32<0x142, 0xa>(v, 0.0f);
+  v += dpp_f32<0x143, 0xc>(v, 0.0f);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
   return v;
 }
-// Wave-wide arg-max over (value desc, expert asc); every lane gets the result.
-template <typename V>
-__device__ __forceinline__ void wave_argmax(V& v, int& e) {
+// Wave-wide arg-max over (value desc, expert asc) for the refinement.
+__device__ __forceinline__ void wave_argmax_f64(double& v, int& e) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
-    const V ov = __shfl_xor(v, off);
+    const double ov = __shfl_xor(v, off);
     const int oe = __shfl_xor(e, off);
     if (ov > v || (ov == v && oe < e)) { v = ov; e = oe; }
   }
@@ -68,7 +85,6 @@ __device__ __forceinline__ void load4(const void* p, int dt, long long i, float 
 
 __device__ __forceinline__ float sigmoid_f32(float s) { return 1.0f / (1.0f + expf(-s)); }
 
-
 // Float32 selection state of one token, held by one wave.
 template <int EPL>
 struct TokenSel {
@@ -79,6 +95,25 @@ struct TokenSel {
   float tau;
   int nsel;
 };
+
+// Pick with the largest key among the experts not yet taken, ties to the lower
+// expert index: the wave maximum of the per-lane maxima, then the first slot
+// and lane that hold it (expert lane + 64 i grows with i, then with the lane).
+template <int EPL>
+__device__ __forceinline__ int wave_pick(const float key[EPL], const bool taken[EPL], float& best) {
+  float bv = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i)
+    if (!taken[i]) bv = fmaxf(bv, key[i]);
+  best = wave_max_u(bv);
+  int be = INT_MAX;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const unsigned long long m = __ballot(!taken[i] && key[i] == best);
+    if (be == INT_MAX && m != 0ull) be = __builtin_ctzll(m) + kWave * i;
+  }
+  return be;
+}
 
 template <int EPL>
 __device__ __forceinline__ void select_f32(const RouteArgs& a, int t, int lane, TokenSel<EPL>& st) {
@@ -97,7 +132,7 @@ __device__ __forceinline__ void select_f32(const RouteArgs& a, int t, int lane, 
     st.taken[i] = !valid;
     amax = fmaxf(amax, fabsf(st.s[i]));
   }
-  amax = wave_max_f32(amax);
+  amax = wave_max_u(amax);
   // Margin on |float32 logit - exact logit|.  The logits come from float32
   // sums of 64-deep slices added in float64, whose error is ~1e-6 at
   // D = 7168; the margin is about two orders of magnitude above that.  It is
@@ -108,12 +143,8 @@ __device__ __forceinline__ void select_f32(const RouteArgs& a, int t, int lane, 
   st.my_e = -1;
   st.my_key = -INFINITY;
   for (int r = 0; r < st.nsel; ++r) {
-    float bv = -INFINITY;
-    int be = INT_MAX;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i)
-      if (!st.taken[i] && (be == INT_MAX || st.key[i] > bv)) { bv = st.key[i]; be = lane + kWave * i; }
-    wave_argmax(bv, be);
+    float bv;
+    const int be = wave_pick<EPL>(st.key, st.taken, bv);
 #pragma unroll
     for (int i = 0; i < EPL; ++i)
       if (lane + kWave * i == be) st.taken[i] = true;
@@ -128,13 +159,28 @@ __device__ __forceinline__ unsigned long long close_mask(const TokenSel<EPL>& st
   return __ballot((lane + 1 < st.nsel) && (st.my_key - next_key <= 2.0f * st.tau));
 }
 
+// Softmax statistics of one token's logits over the E experts: the maximum
+// and the sum of exp(s - max) (wave-uniform).
+template <int EPL>
+__device__ __forceinline__ void softmax_stats(const TokenSel<EPL>& st, int lane, int E, float& smax, float& z) {
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i)
+    if (lane + kWave * i < E) m = fmaxf(m, st.s[i]);
+  smax = wave_max_u(m);
+  float zz = 0.0f;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i)
+    if (lane + kWave * i < E) zz += expf(st.s[i] - smax);
+  z = wave_sum_u(zz);
+}
+
 // Combine weights from the float32 logits for the picks my_e of lanes < k,
-// written with the expert ids.
+// written with the expert ids.  smax, z: softmax_stats (SOFTMAX_TOPK only).
 template <int EPL>
 __device__ __forceinline__ void write_selection(const RouteArgs& a, int t, int lane, const TokenSel<EPL>& st,
-                                                int my_e) {
-  const int E = a.E, k = a.k;
-  const bool sig = a.scoring == SIGMOID_BIAS;
+                                                int my_e, float smax, float z) {
+  const int k = a.k;
   const int pe = (lane < k) ? my_e : 0;
   float s_pick = 0.0f;
 #pragma unroll
@@ -145,26 +191,15 @@ __device__ __forceinline__ void write_selection(const RouteArgs& a, int t, int l
   const bool slot = lane < k;
   float w = 0.0f;
   if (a.scoring == SOFTMAX_TOPK) {
-    float m = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i)
-      if (lane + kWave * i < E) m = fmaxf(m, st.s[i]);
-    const float smax = wave_max_f32(m);
-    float zz = 0.0f;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i)
-      if (lane + kWave * i < E) zz += expf(st.s[i] - smax);
-    const float z = wave_sum_f32(zz);
     const float p = slot ? expf(s_pick - smax) / z : 0.0f;
-    w = a.renormalize ? p / wave_sum_f32(p) : p;
+    w = a.renormalize ? p / wave_sum_u(p) : p;
   } else if (a.scoring == TOPK_SOFTMAX) {
-    const float msel = wave_max_f32(slot ? s_pick : -INFINITY);
+    const float msel = wave_max_u(slot ? s_pick : -INFINITY);
     const float ex = slot ? expf(s_pick - msel) : 0.0f;
-    w = ex / wave_sum_f32(ex);
+    w = ex / wave_sum_u(ex);
   } else {
-    (void)sig;
     const float af = slot ? sigmoid_f32(s_pick) : 0.0f;
-    w = a.renormalize ? af / wave_sum_f32(af) : af;
+    w = a.renormalize ? af / wave_sum_u(af) : af;
   }
   if (slot) {
     a.topk_idx[(long long)t * k + lane] = my_e;
@@ -172,16 +207,15 @@ __device__ __forceinline__ void write_selection(const RouteArgs& a, int t, int l
   }
 }
 
-// Refinement of one token on one wavefront: redo the float32 selection,
-// compute float64 logits for the experts that need them (a D-long dot product
-// of the stored inputs each, loads unrolled ahead), rank the candidates and
-// rewrite the token's selection.
-template <int EPL>
-__device__ __forceinline__ void refine_token(const RouteArgs& a, int t, int lane) {
+// Refinement of one token on its wavefront, from the float32 state st and its
+// close mask cm: float64 logits for the experts that need them (D-long dot
+// products of the stored inputs, two experts per pass over the token's row,
+// UNROLL iterations of loads in flight), then the candidates ranked and the
+// token's selection written.
+template <int EPL, int UNROLL>
+__device__ __forceinline__ void refine_token(const RouteArgs& a, int t, int lane, const TokenSel<EPL>& st,
+                                          unsigned long long cm, float smax, float z) {
   const bool sig = a.scoring == SIGMOID_BIAS;
-  TokenSel<EPL> st;
-  select_f32(a, t, lane, st);
-  const unsigned long long cm = close_mask(st, lane);
   const bool cl = (cm >> lane) & 1ull;
   const bool prev_close = lane > 0 && ((cm >> (lane - 1)) & 1ull);
   const bool pick_ref = lane < st.nsel && (cl || prev_close);
@@ -206,27 +240,59 @@ __device__ __forceinline__ void refine_token(const RouteArgs& a, int t, int lane
 #pragma unroll
   for (int i = 0; i < EPL; ++i) m64[i] = (double)st.key[i];
   const long long xo = (long long)t * a.D;
+  // the refined experts, in expert order, four per pass over x
+  unsigned long long rm[EPL];
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    unsigned long long m = __ballot(ref[i]);
-    while (m) {
-      const int l = __builtin_ctzll(m);
-      m &= m - 1;
-      const int e = l + kWave * i;
-      const long long wo = (long long)e * a.D;
-      double acc = 0.0;
-#pragma unroll 8
-      for (int d = lane * 4; d < a.D; d += kWave * 4) {
-        float xv[4], wv[4];
-        load4(a.x, a.act_dtype, xo + d, xv);
-        load4(a.w_router, a.router_dtype, wo + d, wv);
+  for (int i = 0; i < EPL; ++i) rm[i] = __ballot(ref[i]);
+  int slot_i = 0;
+  auto next_ref = [&]() -> int {      // next refined expert id, -1 when done (uniform)
+    while (slot_i < EPL) {
+      unsigned long long m = 0ull;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc = fma((double)xv[j], (double)wv[j], acc);
+      for (int i = 0; i < EPL; ++i)
+        if (i == slot_i) m = rm[i];
+      if (m != 0ull) {
+        const int l = __builtin_ctzll(m);
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+          if (i == slot_i) rm[i] &= rm[i] - 1;
+        return l + kWave * slot_i;
       }
-      const double s64 = wave_sum_f64(acc);
+      ++slot_i;
+    }
+    return -1;
+  };
+  for (;;) {
+    int ex[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) ex[j] = next_ref();
+    if (ex[0] < 0) break;
+    // branch-free body (a missing second expert repeats the first, its sum is
+    // dropped), unrolled so that several slices' loads are in flight at once
+    long long wo[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) wo[j] = (long long)(ex[j] >= 0 ? ex[j] : ex[0]) * a.D;
+    double acc[2] = {0.0, 0.0};
+#pragma unroll UNROLL
+    for (int d = lane * 4; d < a.D; d += kWave * 4) {
+      float xv[4], wv[2][4];
+      load4(a.x, a.act_dtype, xo + d, xv);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) load4(a.w_router, a.router_dtype, wo[j] + d, wv[j]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[j] = fma((double)xv[q], (double)wv[j][q], acc[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (ex[j] < 0) continue;
+      const double s64 = wave_sum_f64(acc[j]);
       double q64 = s64;
-      if (sig) q64 = 1.0 / (1.0 + exp(-s64)) + (a.sel_bias ? (double)a.sel_bias[e] : 0.0);
-      if (lane == l) m64[i] = q64;
+      if (sig) q64 = 1.0 / (1.0 + exp(-s64)) + (a.sel_bias ? (double)a.sel_bias[ex[j]] : 0.0);
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (lane + kWave * i == ex[j]) m64[i] = q64;
     }
   }
   bool tk[EPL];
@@ -239,28 +305,34 @@ __device__ __forceinline__ void refine_token(const RouteArgs& a, int t, int lane
 #pragma unroll
     for (int i = 0; i < EPL; ++i)
       if (!tk[i] && (be == INT_MAX || m64[i] > bv)) { bv = m64[i]; be = lane + kWave * i; }
-    wave_argmax(bv, be);
+    wave_argmax_f64(bv, be);
 #pragma unroll
     for (int i = 0; i < EPL; ++i)
       if (lane + kWave * i == be) tk[i] = true;
     if (lane == r) my_e = be;
   }
-  write_selection(a, t, lane, st, my_e);
+  write_selection(a, t, lane, st, my_e, smax, z);
 }
 
-// Pass 2 (more than 128 experts): one wavefront per flagged token, all other
-// waves exit at once.
+// Pass 2: one wavefront per flagged token (the float32 state recomputed), all
+// other waves exit at once.  The loads of the dot products run far ahead.
 template <int EPL>
 __global__ __launch_bounds__(256) void route_refine_kernel(const RouteArgs a, const int32_t* __restrict__ flags) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= a.T || flags[t] == 0) return;       // uniform per wave
-  refine_token<EPL>(a, t, lane);
+  TokenSel<EPL> st;
+  select_f32(a, t, lane, st);
+  float smax = 0.0f, z = 1.0f;
+  if (a.scoring == SOFTMAX_TOPK) softmax_stats(st, lane, a.E, smax, z);
+  refine_token<EPL, 8>(a, t, lane, st, close_mask(st, lane), smax, z);
 }
 
-// Pass 1: float32 selection of every token, the per-token probabilities, and
-// either the refinement of the tokens that need float64 in the same wave
-// (FUSED, up to 128 experts) or a flag for pass 2.
+// Pass 1: float32 selection of every token and its probabilities.  FUSED
+// (up to 128 experts): the float64 refinement of the tokens that need it in
+// the same wavefront, with a lean loop (at most two iterations of loads in
+// flight) that keeps the kernel's register footprint small; otherwise a flag
+// for pass 2.
 template <int EPL, bool FUSED>
 __global__ __launch_bounds__(256) void route_select_kernel(const RouteArgs a, int32_t* __restrict__ flags) {
   const int lane = threadIdx.x & 63;
@@ -270,39 +342,33 @@ __global__ __launch_bounds__(256) void route_select_kernel(const RouteArgs a, in
   TokenSel<EPL> st;
   select_f32(a, t, lane, st);
   const unsigned long long cm = close_mask(st, lane);
+  const bool soft = a.scoring != SIGMOID_BIAS;
+  float smax = 0.0f, z = 1.0f;
+  if (soft && (a.scoring == SOFTMAX_TOPK || a.probs != nullptr)) softmax_stats(st, lane, E, smax, z);
   if (!FUSED && lane == 0) flags[t] = cm != 0;
-  write_selection(a, t, lane, st, st.my_e);
+  if (FUSED && cm != 0) refine_token<EPL, 2>(a, t, lane, st, cm, smax, z);   // writes the selection
+  else write_selection(a, t, lane, st, st.my_e, smax, z);
 
   if (a.probs != nullptr) {
     float* prow = a.probs + (long long)t * E;
-    if (a.scoring == SIGMOID_BIAS) {
+    if (!soft) {
       float av[EPL], as = 0.0f;
 #pragma unroll
       for (int i = 0; i < EPL; ++i) {
         av[i] = (lane + kWave * i < E) ? sigmoid_f32(st.s[i]) : 0.0f;
         as += av[i];
       }
-      as = wave_sum_f32(as);
+      as = wave_sum_u(as);
 #pragma unroll
       for (int i = 0; i < EPL; ++i)
         if (lane + kWave * i < E) prow[lane + kWave * i] = av[i] / as;
     } else {
-      float m = -INFINITY;
+      const float rz = 1.0f / z;
 #pragma unroll
       for (int i = 0; i < EPL; ++i)
-        if (lane + kWave * i < E) m = fmaxf(m, st.s[i]);
-      const float smax = wave_max_f32(m);
-      float zz = 0.0f;
-#pragma unroll
-      for (int i = 0; i < EPL; ++i)
-        if (lane + kWave * i < E) zz += expf(st.s[i] - smax);
-      const float z = wave_sum_f32(zz);
-#pragma unroll
-      for (int i = 0; i < EPL; ++i)
-        if (lane + kWave * i < E) prow[lane + kWave * i] = expf(st.s[i] - smax) / z;
+        if (lane + kWave * i < E) prow[lane + kWave * i] = expf(st.s[i] - smax) * rz;
     }
   }
-  if (FUSED && cm != 0) refine_token<EPL>(a, t, lane);   // rewrites the selection
 }
 
 template <int EPL>
@@ -314,8 +380,7 @@ hipError_t launch_epl(const RouteArgs& a, int32_t* flags, hipStream_t s) {
   hipLaunchKernelGGL((route_select_kernel<EPL, false>), dim3(ceil_div(a.T, 4)), dim3(256), 0, s, a, flags);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(route_refine_kernel<EPL>, dim3(ceil_div(a.T, 4)), dim3(256), 0, s, a,
-                     (const int32_t*)flags);
+  hipLaunchKernelGGL(route_refine_kernel<EPL>, dim3(ceil_div(a.T, 4)), dim3(256), 0, s, a, (const int32_t*)flags);
   return hipGetLastError();
 }
 
