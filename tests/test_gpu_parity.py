@@ -379,8 +379,15 @@ def test_weight_streaming_many_tiles(cfg, gemm_cfg, monkeypatch):
 
 
 ROUTER_SHAPES = [
-    # the router kernel's range (65 <= E <= 256, D % 64 == 0): float32 and bf16
-    # weights, a ragged expert count, a row count that is not a multiple of 32
+    # the router kernels' range (E <= 256, D % 64 == 0): float32 and bf16
+    # weights, ragged expert counts, row counts that are not multiples of 16 or 32;
+    # E <= 64 goes to the kernel that splits the contraction over waves
+    W.MoEConfig("router_e8_bf16w", 333, 4096, 8, 2, 64, scoring=W.TOPK_SOFTMAX, zipf_s=1.0),
+    W.MoEConfig("router_e40_f32w", 250, 320, 40, 3, 64, scoring=W.SOFTMAX_TOPK, renormalize=1,
+                router_dtype=W.F32),
+    W.MoEConfig("router_e64_bf16w", 517, 2048, 64, 6, 64, scoring=W.SOFTMAX_TOPK, renormalize=1),
+    W.MoEConfig("router_e16_f32w", 64, 128, 16, 1, 64, scoring=W.SOFTMAX_TOPK, renormalize=0,
+                router_dtype=W.F32),
     W.MoEConfig("router_e128_f32w", 300, 256, 128, 2, 64, scoring=W.SOFTMAX_TOPK, renormalize=1,
                 router_dtype=W.F32),
     W.MoEConfig("router_e200_bf16w", 257, 192, 200, 4, 64, scoring=W.SIGMOID_BIAS, zipf_s=1.2),

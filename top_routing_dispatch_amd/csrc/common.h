@@ -241,7 +241,7 @@ constexpr int kF32GemmBM = 64;
 // Router logits for bf16 tokens and bf16 weights [E, planes, D] (planes = 1,
 // or 3 for the exact plane split of float32 weights): logits [T, E] float32.
 // router_kernel_fits tells whether the shape is one it handles (D % 64 == 0,
-// 65 <= E <= 256 for one plane, <= 128 for three).
+// E <= 256 for one plane, <= 128 for three).
 bool router_kernel_fits(int T, int E, int D, int planes);
 hipError_t launch_router_logits(const bf16_t* x, const bf16_t* w, int planes, float* logits, int T, int E, int D,
                                 hipStream_t s);

@@ -1,15 +1,22 @@
 // Router logits s[t, e] = sum_d x[t, d] w[e, d] for bf16 tokens and bf16
 // weights given as NP planes (NP = 1: the weights; NP = 3: the exact split of
 // float32 weights into hi + mid + lo made by launch_split_bf16x3), for
-// 65 <= E <= 256 and D a multiple of 64 ("Top-k 路由" page, step 1 of the
-// gate: one bias-free linear layer).
+// E <= 256 and D a multiple of 64 ("Top-k 路由" page, step 1 of the gate: one
+// bias-free linear layer).
 //
-// One workgroup owns 32 tokens and every expert, so each token row is read
-// once and each token fragment feeds NP MFMAs.  Operands stream through an
-// LDS ring (up to 4 deep) of 64-deep K slices (buffer loads with the LDS bit).
-// Every slice's MFMA sums are added into float64 accumulators, which keeps the
-// logits within a small multiple of float32 rounding of the exact sum, as the
-// selection's near-tie refinement requires.
+// 65 <= E <= 256: one workgroup owns 32 tokens and every expert, so each
+// token row is read once and each token fragment feeds NP MFMAs.  Operands
+// stream through an LDS ring (up to 4 deep) of 64-deep K slices (buffer loads
+// with the LDS bit).
+// E <= 64: the weights are small and the work is reading the tokens.  One
+// workgroup owns 16 tokens; its eight waves split the contraction (wave w
+// takes the 32-deep steps w, w + 8, ...), load their operands straight into
+// registers for 16x16x32 MFMAs, and add their partial sums in LDS at the end
+// in a fixed order.
+// Either way the MFMA sums of at most 64 products per plane are added into
+// float64 accumulators, which keeps the logits within a small multiple of
+// float32 rounding of the exact sum, as the selection's near-tie refinement
+// requires.
 #include "common.h"
 
 namespace moe {
@@ -153,15 +160,109 @@ hipError_t launch_router_cfg(const bf16_t* x, const bf16_t* w, float* logits, in
   return hipGetLastError();
 }
 
+template <int NB, int NP, int U>
+__global__ __launch_bounds__(512) void router_small_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ w,
+                                                           float* __restrict__ logits, int T, int E, int D) {
+  constexpr int NW = 8;                             // waves
+  __shared__ double part[NW / 2][16][NB * 16 + 1];  // [wave % 4][token][expert] partial sums
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row0 = blockIdx.x * 16;
+  const int tok = min(row0 + (lane & 15), T - 1);   // rows past the end read the last row
+  const int kg = (lane >> 4) * 8;                   // this lane's 8 of a 32-deep step
+  const bf16_t* xr = x + (long long)tok * D + kg;
+  const bf16_t* wr[NB][NP];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+      wr[b][p] = w + ((long long)min(b * 16 + (lane & 15), E - 1) * NP + p) * D + kg;
+
+  floatx4_t acc[NB];
+  double dacc[NB][4];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) { acc[b][r] = 0.0f; dacc[b][r] = 0.0; }
+  // U steps of this wave per iteration, their loads issued together; each
+  // step's MFMA sums (32 products per plane) go to float64 at once
+  const int nsteps = D / 32;
+  for (int s0 = wave; s0 < nsteps; s0 += NW * U) {
+    bf16x8_t a[U], bv[U][NB][NP];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int st = min(s0 + NW * u, nsteps - 1);  // steps past the end are loaded but not used
+      a[u] = *reinterpret_cast<const bf16x8_t*>(xr + st * 32);
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int p = 0; p < NP; ++p) bv[u][b][p] = *reinterpret_cast<const bf16x8_t*>(wr[b][p] + st * 32);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (s0 + NW * u >= nsteps) break;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+#pragma unroll
+        for (int p = 0; p < NP; ++p) acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], bv[u][b][p], acc[b], 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) { dacc[b][r] += (double)acc[b][r]; acc[b][r] = 0.0f; }
+      }
+    }
+  }
+  // lane holds expert column (lane & 15) of block b and token rows 4 (lane >> 4) + r;
+  // waves 4..7 hand their sums to waves 0..3, which then write theirs
+  const int w4 = wave & 3;
+  if (wave >= 4) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part[w4][4 * (lane >> 4) + r][b * 16 + (lane & 15)] = dacc[b][r];
+  }
+  __syncthreads();
+  if (wave < 4) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        double& slot = part[w4][4 * (lane >> 4) + r][b * 16 + (lane & 15)];
+        slot = dacc[b][r] + slot;
+      }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 16 * E; i += 512) {
+    const int tr = i / E, e = i % E;
+    if (row0 + tr < T)
+      logits[(long long)(row0 + tr) * E + e] = (float)(((part[0][tr][e] + part[1][tr][e]) + part[2][tr][e]) + part[3][tr][e]);
+  }
+}
+
+template <int NB, int NP>
+hipError_t launch_router_small(const bf16_t* x, const bf16_t* w, float* logits, int T, int E, int D, hipStream_t s) {
+  constexpr int U = NP == 1 ? (NB <= 2 ? 8 : 4) : 2;
+  hipLaunchKernelGGL((router_small_kernel<NB, NP, U>), dim3(ceil_div(T, 16)), dim3(512), 0, s, x, w, logits, T, E, D);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 bool router_kernel_fits(int T, int E, int D, int planes) {
-  return T > 0 && D > 0 && D % 64 == 0 && E > 64 && (planes == 1 ? E <= 256 : planes == 3 && E <= 128);
+  return T > 0 && E > 0 && D > 0 && D % 64 == 0 && (planes == 1 ? E <= 256 : planes == 3 && E <= 128);
 }
 
 hipError_t launch_router_logits(const bf16_t* x, const bf16_t* w, int planes, float* logits, int T, int E, int D,
                                 hipStream_t s) {
   if (!router_kernel_fits(T, E, D, planes)) return hipErrorInvalidValue;
+  if (E <= 64) {
+    if (planes == 3) {
+      if (E <= 16) return launch_router_small<1, 3>(x, w, logits, T, E, D, s);
+      if (E <= 32) return launch_router_small<2, 3>(x, w, logits, T, E, D, s);
+      return launch_router_small<4, 3>(x, w, logits, T, E, D, s);
+    }
+    if (E <= 16) return launch_router_small<1, 1>(x, w, logits, T, E, D, s);
+    if (E <= 32) return launch_router_small<2, 1>(x, w, logits, T, E, D, s);
+    return launch_router_small<4, 1>(x, w, logits, T, E, D, s);
+  }
   if (planes == 3) return launch_router_cfg<128, 3>(x, w, logits, T, E, D, s);
   if (E <= 128) return launch_router_cfg<128, 1>(x, w, logits, T, E, D, s);
   return launch_router_cfg<256, 1>(x, w, logits, T, E, D, s);
