@@ -351,6 +351,31 @@ def test_shallow_group_split(cfg, split, monkeypatch):
     print(f"  max rel err {err:.3e}")
 
 
+TAIL_SHAPES = [
+    # down projections with K >= 4096 and fewer 256x256 tiles than CUs, so
+    # that every tile runs as four quarter tiles (the case with full rounds
+    # before the tail is the full-size Mixtral-shaped layer); ragged N and
+    # ragged groups
+    W.MoEConfig("tail_split_deep", 800, 512, 8, 2, 4096, zipf_s=0.5),
+    W.MoEConfig("tail_split_ragged", 900, 448, 6, 2, 4160, zipf_s=1.0),
+]
+
+
+@pytest.mark.parametrize("tail", ["0", "1"])
+@pytest.mark.parametrize("cfg", TAIL_SHAPES, ids=lambda c: c.name)
+def test_down_tail_split(cfg, tail, monkeypatch):
+    """The down projection on 256x256 tiles with its last, partial round run as
+    quarter tiles (1) and without (0), against the oracle."""
+    monkeypatch.setenv("MOE_GEMM_CFG", "10")
+    monkeypatch.setenv("MOE_GEMM_TAIL", tail)
+    print(f"[tail {tail}] {cfg.name}", flush=True)
+    inp = W.make_inputs(cfg)
+    ref = oracle_forward(cfg, inp)
+    got = DeviceLayer(cfg, inp).layer()
+    diff, err = check_layer(cfg, inp, ref, got)
+    print(f"  max rel err {err:.3e}")
+
+
 WS_SHAPES = [
     # more tiles than workgroups of the persistent weight-streaming kernel, so
     # that its ring crosses tile boundaries: a 512-deep GELU contraction with

@@ -123,6 +123,17 @@ struct GroupedGemm {
   const int32_t* tile_prefix; // [G+1] m-tile prefix for the kernel's BM (grouped case)
   int epilogue;
   int a_kwrap;                // 0, or: A column k is read at k % a_kwrap (a multiple of 64)
+  // Last-round split of a tiled launch (non-persistent kernels, map_tile):
+  // 0: every tile;
+  // 1: only the tiles of the full rounds, the first (total / round) * round
+  //    tiles of the order (round = workgroups that run at once);
+  // 2: the remaining tiles of a tiling twice as tall and wide (BM_parent =
+  //    2 BM, tail_pn of its n-tiles, tile_prefix for BM_parent), each as four
+  //    quarter tiles of this kernel, so that the last, partial round has four
+  //    times as many (four times shorter) workgroups.
+  int tail_mode;
+  int round;
+  int tail_pn;
 };
 
 // Exact split of a float32 matrix into three bfloat16 planes, hi + mid + lo = w:
@@ -196,9 +207,25 @@ __device__ __forceinline__ void decode_tile(const GroupedGemm& p, int n_tiles, i
 template <int BM>
 __device__ __forceinline__ bool map_tile(const GroupedGemm& p, int n_tiles, int& g, int& row0, int& rows,
                                          int& nt) {
-  const int total = tile_count<BM>(p, n_tiles);
-  if ((int)blockIdx.x >= total) return false;
-  decode_tile<BM>(p, n_tiles, xcd_remap(blockIdx.x, total), g, row0, rows, nt);
+  const int bid = blockIdx.x;
+  if (p.tail_mode == 2) {
+    const int total = tile_count<2 * BM>(p, p.tail_pn);
+    const int main = total / p.round * p.round;
+    const int q = 4 * (total - main);                    // quarter tiles
+    if (bid >= q) return false;
+    const int L = xcd_remap(bid, q);
+    const int sub = L & 3;
+    int prow0, prows, pnt;
+    decode_tile<2 * BM>(p, p.tail_pn, main + (L >> 2), g, prow0, prows, pnt);
+    row0 = prow0 + (sub >> 1) * BM;
+    rows = min(BM, prows - (sub >> 1) * BM);
+    nt = 2 * pnt + (sub & 1);
+    return rows > 0 && nt < n_tiles;
+  }
+  int total = tile_count<BM>(p, n_tiles);
+  if (p.tail_mode == 1) total = total / p.round * p.round;
+  if (bid >= total) return false;
+  decode_tile<BM>(p, n_tiles, xcd_remap(bid, total), g, row0, rows, nt);
   return true;
 }
 

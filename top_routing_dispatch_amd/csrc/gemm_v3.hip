@@ -387,7 +387,12 @@ hipError_t launch_cfg3(const GroupedGemm& p, hipStream_t s) {
   if (m_tiles == 0 || n_tiles == 0) return hipSuccess;
   long long blocks = (long long)m_tiles * n_tiles;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (PERS && p.tail_mode != 0) return hipErrorInvalidValue;
   if (PERS) blocks = std::min<long long>(blocks, (long long)num_cus() * OCC);
+  if (p.tail_mode == 2) {
+    if (p.round <= 0 || p.tail_pn <= 0) return hipErrorInvalidValue;
+    blocks = 4LL * p.round;            // the partial round holds fewer than `round` parent tiles
+  }
   // dynamic LDS above 64 KB has to be allowed explicitly, once per device
   static bool allowed[64] = {};
   int dev = 0;
