@@ -33,8 +33,9 @@ VALU_F32_TFLOPS = 78.6       # FMA without packed-FP32 instructions: 256 CU x 64
 
 # Files whose change invalidates HBM-traffic counters taken earlier: the GEMM
 # kernels, their launch planning and the synthetic workload recipe.
-TRAFFIC_SOURCES = ("top_routing_dispatch_amd/csrc/common.h", "top_routing_dispatch_amd/csrc/gemm_v2.hip",
-                   "top_routing_dispatch_amd/csrc/gemm.hip", "top_routing_dispatch_amd/csrc/api.hip",
+TRAFFIC_SOURCES = ("top_routing_dispatch_amd/csrc/common.h", "top_routing_dispatch_amd/csrc/gemm.hip",
+                   "top_routing_dispatch_amd/csrc/gemm_v2.hip", "top_routing_dispatch_amd/csrc/gemm_v3.hip",
+                   "top_routing_dispatch_amd/csrc/gemm_ws.hip", "top_routing_dispatch_amd/csrc/api.hip",
                    "workloads/__init__.py")
 
 DEFAULT_CPU_SAMPLE = {"tiny": 64, "switch": 8192, "mixtral": 1024, "deepseekmoe": 4096, "deepseekv3": 256}
