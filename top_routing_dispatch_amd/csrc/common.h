@@ -156,6 +156,9 @@ __device__ __forceinline__ int tile_count(const GroupedGemm& p, int n_tiles) {
 // (uniform) reads become scalar loads, which a kernel with vector loads in
 // flight can wait for without waiting for those.
 typedef const __attribute__((address_space(4))) int32_t const_i32;
+#ifndef MOE_TILE_GM
+#define MOE_TILE_GM 8          // m-tiles per run that sweeps the n-tiles
+#endif
 template <bool SCALAR>
 __device__ __forceinline__ int ld_table(const int32_t* t, int i) {
   if constexpr (SCALAR) return ((const_i32*)t)[i];
@@ -165,7 +168,7 @@ __device__ __forceinline__ int ld_table(const int32_t* t, int i) {
 template <int BM, bool SCALAR = false>
 __device__ __forceinline__ void decode_tile(const GroupedGemm& p, int n_tiles, int L, int& g, int& row0, int& rows,
                                             int& nt) {
-  constexpr int GM = 8;
+  constexpr int GM = MOE_TILE_GM;
   if (p.offsets == nullptr) {
     const int mt_all = ceil_div(p.M_max, BM);
     const int sub = L / (GM * n_tiles);

@@ -19,6 +19,8 @@
 //              expert-local rank is below C.
 #include "common.h"
 
+#include <algorithm>
+
 namespace moe {
 namespace {
 
@@ -154,6 +156,11 @@ template <typename T>
 struct Chunk;
 template <> struct Chunk<float> {
   static constexpr int N = 4;
+  // 16 bytes as loaded, widened only where they are used
+  static __device__ __forceinline__ uint4 raw(const float* p) { return *reinterpret_cast<const uint4*>(p); }
+  static __device__ __forceinline__ float elem(const uint4& q, int i) {
+    return __uint_as_float(i == 0 ? q.x : i == 1 ? q.y : i == 2 ? q.z : q.w);
+  }
   static __device__ __forceinline__ void load(const float* p, float v[4]) {
     const float4 q = *reinterpret_cast<const float4*>(p);
     v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
@@ -164,6 +171,11 @@ template <> struct Chunk<float> {
 };
 template <> struct Chunk<bf16_t> {
   static constexpr int N = 8;
+  static __device__ __forceinline__ uint4 raw(const bf16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+  static __device__ __forceinline__ float elem(const uint4& q, int i) {
+    const uint32_t w = (i >> 1) == 0 ? q.x : (i >> 1) == 1 ? q.y : (i >> 1) == 2 ? q.z : q.w;
+    return __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
+  }
   static __device__ __forceinline__ void load(const bf16_t* p, float v[8]) {
     const uint4 q = *reinterpret_cast<const uint4*>(p);
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
@@ -182,53 +194,86 @@ template <> struct Chunk<bf16_t> {
   }
 };
 
-// One workgroup per token.  The token's row indices and weights go to LDS
-// once; each chunk then issues the loads of up to 8 rows before the first
-// multiply-add, so they are in flight together.  The sum runs over the slots
-// in order, as a chain of fused multiply-adds.
-template <typename T>
+// A workgroup covers TPB consecutive tokens (TPB * D / N chunk items of N
+// elements); their row indices and weights go to LDS once.  Each thread takes
+// U items (item i, i + 256, ...) and issues the loads of every item's rows
+// (G at a time, U * G = 8) and shared-expert chunk before the first
+// multiply-add, so that many loads are in flight whatever k and D are.  Per
+// item the sum runs over the slots in order, as a chain of fused
+// multiply-adds, and the shared-expert chunk is added last.
+constexpr int kCombineSlots = 1024;           // row indices / weights of a workgroup's tokens in LDS
+
+template <typename T, int G>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ yp, const int32_t* __restrict__ row_of,
                                                       const float* __restrict__ tw, const T* ys, T* y,
-                                                      int k, int D) {
+                                                      int ntok, int k, int D, int tpb) {
   constexpr int N = Chunk<T>::N;
-  constexpr int G = 8;                         // rows in flight per chunk
-  __shared__ int srow[kMaxTopK];
-  __shared__ float sw[kMaxTopK];
-  const int t = blockIdx.x;
-  if ((int)threadIdx.x < k) {
-    srow[threadIdx.x] = row_of[(long long)t * k + threadIdx.x];
-    sw[threadIdx.x] = tw[(long long)t * k + threadIdx.x];
+  constexpr int U = 8 / G;                     // items per thread
+  __shared__ int srow[kCombineSlots];
+  __shared__ float sw[kCombineSlots];
+  const int t0 = blockIdx.x * tpb;
+  const int nt = min(tpb, ntok - t0);
+  for (int i = threadIdx.x; i < nt * k; i += 256) {
+    srow[i] = row_of[(long long)t0 * k + i];
+    sw[i] = tw[(long long)t0 * k + i];
   }
   __syncthreads();
   const int chunks = D / N;
-  for (int c = threadIdx.x; c < chunks; c += blockDim.x) {
-    float acc[N];
+  const int items = nt * chunks;
+  for (int base = 0; base < items; base += 256 * U) {
+    int tl[U], cc[U];
+    bool ok[U];
 #pragma unroll
-    for (int q = 0; q < N; ++q) acc[q] = 0.0f;
+    for (int u = 0; u < U; ++u) {
+      const int it = base + (int)threadIdx.x + 256 * u;
+      ok[u] = it < items;
+      tl[u] = ok[u] ? it / chunks : 0;
+      cc[u] = ok[u] ? it % chunks : 0;
+    }
+    float acc[U][N];
+    uint4 vs[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      vs[u] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (int q = 0; q < N; ++q) acc[u][q] = 0.0f;
+    }
     for (int j0 = 0; j0 < k; j0 += G) {
-      float v[G][N];
+      uint4 v[U][G];
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const int j = j0 + g;
-        if (j < k && srow[j] >= 0) Chunk<T>::load(yp + (long long)srow[j] * D + c * N, v[g]);
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const int j = j0 + g;
+          const int r = (ok[u] && j < k) ? srow[tl[u] * k + j] : -1;
+          if (r >= 0) v[u][g] = Chunk<T>::raw(yp + (long long)r * D + cc[u] * N);
+        }
+        // the shared-expert chunk is loaded with the first rows, added last
+        if (ys != nullptr && j0 == 0 && ok[u]) vs[u] = Chunk<T>::raw(ys + (long long)(t0 + tl[u]) * D + cc[u] * N);
       }
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const int j = j0 + g;
-        if (j < k && srow[j] >= 0) {
-          const float w = sw[j];
+      for (int u = 0; u < U; ++u) {
 #pragma unroll
-          for (int q = 0; q < N; ++q) acc[q] = fmaf(w, v[g][q], acc[q]);
+        for (int g = 0; g < G; ++g) {
+          const int j = j0 + g;
+          const int r = (ok[u] && j < k) ? srow[tl[u] * k + j] : -1;
+          if (r >= 0) {
+            const float w = sw[tl[u] * k + j];
+#pragma unroll
+            for (int q = 0; q < N; ++q) acc[u][q] = fmaf(w, Chunk<T>::elem(v[u][g], q), acc[u][q]);
+          }
         }
       }
     }
     if (ys != nullptr) {
-      float v[N];
-      Chunk<T>::load(ys + (long long)t * D + c * N, v);
 #pragma unroll
-      for (int q = 0; q < N; ++q) acc[q] += v[q];
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int q = 0; q < N; ++q) acc[u][q] += Chunk<T>::elem(vs[u], q);
     }
-    Chunk<T>::store(y + (long long)t * D + c * N, acc);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (ok[u]) Chunk<T>::store(y + (long long)(t0 + tl[u]) * D + cc[u] * N, acc[u]);
   }
 }
 
@@ -340,24 +385,34 @@ hipError_t launch_gather_rows(const void* x, const int32_t* token_of_row, const 
   return hipGetLastError();
 }
 
+template <typename E>
+hipError_t launch_combine_t(const void* y_perm, const int32_t* row_of, const float* topk_w, const void* y_shared,
+                            void* y, int ntok, int k, int D, hipStream_t s) {
+  const int chunks = D / Chunk<E>::N;
+  const int G = k >= 5 ? 8 : k >= 3 ? 4 : k;   // rows loaded together per item
+  const int U = 8 / G;
+  // tokens per workgroup: enough items for every thread's U, within the LDS slots
+  int tpb = (256 * U + chunks - 1) / chunks;
+  tpb = std::max(1, std::min(tpb, kCombineSlots / k));
+  const dim3 grid((unsigned)ceil_div(ntok, tpb));
+  const E* yp = static_cast<const E*>(y_perm);
+  const E* ys = static_cast<const E*>(y_shared);
+  E* yo = static_cast<E*>(y);
+  switch (G) {
+    case 1: hipLaunchKernelGGL((combine_kernel<E, 1>), grid, dim3(256), 0, s, yp, row_of, topk_w, ys, yo, ntok, k, D, tpb); break;
+    case 2: hipLaunchKernelGGL((combine_kernel<E, 2>), grid, dim3(256), 0, s, yp, row_of, topk_w, ys, yo, ntok, k, D, tpb); break;
+    case 4: hipLaunchKernelGGL((combine_kernel<E, 4>), grid, dim3(256), 0, s, yp, row_of, topk_w, ys, yo, ntok, k, D, tpb); break;
+    default: hipLaunchKernelGGL((combine_kernel<E, 8>), grid, dim3(256), 0, s, yp, row_of, topk_w, ys, yo, ntok, k, D, tpb); break;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_combine(const void* y_perm, const int32_t* row_of, const float* topk_w,
                           const void* y_shared, void* y, int T, int k, int D, int act_dtype,
                           hipStream_t s) {
   if (T == 0) return hipSuccess;
-  if (act_dtype == BF16) {
-    const int chunks = D / 8;
-    const int threads = chunks >= 256 ? 256 : ((chunks + 63) / 64) * 64;
-    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(T), dim3(threads), 0, s,
-                       static_cast<const bf16_t*>(y_perm), row_of, topk_w,
-                       static_cast<const bf16_t*>(y_shared), static_cast<bf16_t*>(y), k, D);
-  } else {
-    const int chunks = D / 4;
-    const int threads = chunks >= 256 ? 256 : ((chunks + 63) / 64) * 64;
-    hipLaunchKernelGGL(combine_kernel<float>, dim3(T), dim3(threads), 0, s,
-                       static_cast<const float*>(y_perm), row_of, topk_w,
-                       static_cast<const float*>(y_shared), static_cast<float*>(y), k, D);
-  }
-  return hipGetLastError();
+  if (act_dtype == BF16) return launch_combine_t<bf16_t>(y_perm, row_of, topk_w, y_shared, y, T, k, D, s);
+  return launch_combine_t<float>(y_perm, row_of, topk_w, y_shared, y, T, k, D, s);
 }
 
 hipError_t launch_load_stats(const StatsArgs& a, hipStream_t s) {
