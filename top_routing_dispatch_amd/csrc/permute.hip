@@ -197,8 +197,9 @@ template <> struct Chunk<bf16_t> {
 // A workgroup covers TPB consecutive tokens (TPB * D / N chunk items of N
 // elements); their row indices and weights go to LDS once.  Each thread takes
 // U items (item i, i + 256, ...) and issues the loads of every item's rows
-// (G at a time, U * G = 8) and shared-expert chunk before the first
-// multiply-add, so that many loads are in flight whatever k and D are.  Per
+// (G at a time; U * G = 8, or 4 for k <= 2, where more workgroups do better)
+// and shared-expert chunk before the first multiply-add, so that many loads
+// are in flight whatever k and D are.  Per
 // item the sum runs over the slots in order, as a chain of fused
 // multiply-adds, and the shared-expert chunk is added last.
 constexpr int kCombineSlots = 1024;           // row indices / weights of a workgroup's tokens in LDS
@@ -208,7 +209,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ yp, 
                                                       const float* __restrict__ tw, const T* ys, T* y,
                                                       int ntok, int k, int D, int tpb) {
   constexpr int N = Chunk<T>::N;
-  constexpr int U = 8 / G;                     // items per thread
+  constexpr int U = G >= 4 ? 8 / G : 4 / G;     // items per thread
   __shared__ int srow[kCombineSlots];
   __shared__ float sw[kCombineSlots];
   const int t0 = blockIdx.x * tpb;
@@ -390,7 +391,7 @@ hipError_t launch_combine_t(const void* y_perm, const int32_t* row_of, const flo
                             void* y, int ntok, int k, int D, hipStream_t s) {
   const int chunks = D / Chunk<E>::N;
   const int G = k >= 5 ? 8 : k >= 3 ? 4 : k;   // rows loaded together per item
-  const int U = 8 / G;
+  const int U = G >= 4 ? 8 / G : 4 / G;
   // tokens per workgroup: enough items for every thread's U, within the LDS slots
   int tpb = (256 * U + chunks - 1) / chunks;
   tpb = std::max(1, std::min(tpb, kCombineSlots / k));
