@@ -129,6 +129,21 @@ def test_permute_every_token_on_one_expert_with_capacity():
     assert (row_of[:C, 0] == np.arange(C)).all() and (row_of[C:, 0] == -1).all()
 
 
+def test_permute_skips_repeated_and_out_of_range_ids():
+    """Slots whose expert id is outside [0, E) or repeats an earlier slot of the
+    same token are not dispatched (row -1, not counted); the other slots keep
+    the order of the valid ones.  (Library behaviour for inputs moe_route never
+    produces; the pages do not define them.)"""
+    idx = np.array([[1, 1], [0, 4], [-1, 2], [2, 0], [3, 3]])
+    cfg = W.MoEConfig("bad_ids", 5, 8, 4, 2, 8, act_dtype=W.F32, router_dtype=W.F32)
+    counts, offsets, row_of, tor, _ = _permute_gpu(cfg, idx, None)
+    # valid slots in (token, slot) order: (0,0)->1 (1,0)->0 (2,1)->2 (3,0)->2 (3,1)->0 (4,0)->3
+    assert counts.tolist() == [2, 1, 2, 1]
+    assert offsets.tolist() == [0, 2, 3, 5, 6]
+    assert tor.tolist() == [1, 3, 0, 2, 3, 4, -1, -1, -1, -1]
+    assert row_of.tolist() == [[2, -1], [0, -1], [-1, 3], [4, 1], [5, -1]]
+
+
 @pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
 def test_expert_ffn_matches_oracle(cfg):
     """Grouped expert FFN on the oracle's expert batches (x_perm, offsets)."""
