@@ -463,3 +463,52 @@ def test_router_logits_and_selection(cfg, kernel, monkeypatch):
     diff = route_differences(cfg, ref, gi, inp.sel_bias)
     same = np.setdiff1d(np.arange(T), diff)
     assert rel_err(to_numpy(tw)[same], ref["w"][same]) <= W_TOL
+
+
+GRAPH_SHAPES = [
+    # Switch-like (capacity, GELU, weight-streaming GEMM) and one with shared
+    # experts on the auxiliary stream and the deep-tile GEMM
+    W.MoEConfig("graph_gelu_capacity", 900, 192, 16, 1, 384, scoring=W.SOFTMAX_TOPK, renormalize=0,
+                activation=W.GELU, router_dtype=W.F32, capacity_factor=1.25),
+    W.MoEConfig("graph_swiglu_shared", 700, 256, 8, 2, 320, num_shared=1, d_ff_shared=128),
+]
+
+
+@pytest.mark.parametrize("cfg", GRAPH_SHAPES, ids=lambda c: c.name)
+def test_layer_forward_graph_replay(cfg):
+    """The layer forward captured in a HIP graph (its auxiliary-stream work
+    joins the capture through the fork / join events) and replayed several
+    times, with eager calls of the same layer in between: every replay equals
+    the eager result bit for bit."""
+    print(f"[graph replay] {cfg.name}", flush=True)
+    inp = W.make_inputs(cfg)
+    dl = DeviceLayer(cfg, inp)
+    T, k, E = cfg.num_tokens, cfg.top_k, cfg.num_experts
+    dev = "cuda"
+    y = torch.empty((T, cfg.d_model), dtype=act_torch_dtype(cfg), device=dev)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    stats = torch.empty(2 * E + 2, dtype=torch.float32, device=dev)
+    dropped = torch.empty(1, dtype=torch.int32, device=dev)
+    ws = M.workspace(cfg, M.MOE_OP_LAYER, dev)
+
+    def call():
+        M.moe_layer_forward(cfg, dl.weights, dl.x, y, idx, w, counts, cfg.alpha, stats, dropped, ws)
+
+    call()                                  # eager: reference, and one-time set-up outside the capture
+    torch.cuda.synchronize()
+    ref = [to_numpy(t).copy() for t in (y, idx, w, counts, stats)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        y.fill_(0); idx.fill_(-9); w.fill_(0); counts.fill_(-9); stats.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        got = [to_numpy(t) for t in (y, idx, w, counts, stats)]
+        for r, a in zip(ref, got):
+            np.testing.assert_array_equal(a, r)
+        call()                              # eager work between the replays
+        torch.cuda.synchronize()
