@@ -350,12 +350,15 @@ SPLIT_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("split", ["0", "1"])
+@pytest.mark.parametrize("split", ["0", "1", "1-pers19"])
 @pytest.mark.parametrize("cfg", SPLIT_SHAPES + V2_SHAPES, ids=lambda c: c.name)
 def test_shallow_group_split(cfg, split, monkeypatch):
     """Expert FFN with shallow groups split off to the persistent
-    weight-streaming kernel (and without), against the oracle."""
-    monkeypatch.setenv("MOE_GEMM_SPLIT", split)
+    weight-streaming kernel (1), to the persistent configuration 19 of the
+    deep-tile kernel (1-pers19), and without the split (0), against the oracle."""
+    monkeypatch.setenv("MOE_GEMM_SPLIT", split[0])
+    if split == "1-pers19":
+        monkeypatch.setenv("MOE_GEMM_SHCFG", "19")
     print(f"[split {split}] {cfg.name}", flush=True)
     inp = W.make_inputs(cfg)
     ref = oracle_forward(cfg, inp)

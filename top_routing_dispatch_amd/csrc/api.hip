@@ -267,7 +267,10 @@ FfnPlan plan_ffn(int act, int D, int F, int max_rows, int G, bool grouped) {
   pl.cfg_dn = pick_cfg(act, F, max_rows, G, true);
   pl.bm_up = cfg_bm(act, pl.cfg_up);
   pl.bm_dn = cfg_bm(act, pl.cfg_dn);
-  pl.cfg_sh = kGemmV2Configs + 9;
+  // shallow groups: the persistent weight-streaming kernel with 64x128 tiles
+  // and a 5-deep ring (measured ~1% per DeepSeek-V3-shaped layer ahead of the
+  // 64x256 persistent configuration of the deep-tile kernel)
+  pl.cfg_sh = kGemmV2Configs + kGemmV3Configs + 3;
   const char* sh_env = getenv("MOE_GEMM_SHCFG");       // tuning aid: a configuration index >= kGemmV2Configs
   if (sh_env != nullptr && *sh_env != '\0' && atoi(sh_env) >= kGemmV2Configs && atoi(sh_env) < kGemmConfigs)
     pl.cfg_sh = atoi(sh_env);
