@@ -172,7 +172,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="switch", choices=sorted(W.CONFIGS))
+    ap.add_argument("--config", default="switch", choices=sorted(W.CONFIGS) + sorted(W.DECODE_CONFIGS),
+                    help="workload; <model>_decode_t<T>: the first T tokens on that model's full-size weights")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=None)
     ap.add_argument("--copy-calibration", type=int, default=None, metavar="MIB",
@@ -191,7 +192,7 @@ def main():
     import top_routing_dispatch_amd as M
     from workloads.torch_io import act_torch_dtype, to_torch, upload_experts
 
-    cfg = W.CONFIGS[args.config]
+    cfg = W.CONFIGS.get(args.config) or W.DECODE_CONFIGS[args.config]
     dev = "cuda"
     torch.cuda.set_device(0)
     t_setup = time.perf_counter()

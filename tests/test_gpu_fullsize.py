@@ -25,16 +25,43 @@ from parity import W_TOL, out_tol, refinement_margin, rel_err, route_differences
 pytestmark = pytest.mark.gpu
 
 SAMPLE = {"switch": 32, "mixtral": 12, "deepseekmoe": 24, "deepseekv3": 8}
+DECODE_SAMPLE = 32
+
+_EXPERTS = {}
+
+
+def _experts(name):
+    """Routed expert weights of a full-size workload on the device (and their
+    host bytes), generated once per module run; other models are dropped."""
+    if name not in _EXPERTS:
+        _EXPERTS.clear()
+        torch.cuda.empty_cache()
+        _EXPERTS[name] = upload_experts(W.CONFIGS[name], "cuda", keep_host=True)
+    return _EXPERTS[name]
 
 
 @pytest.mark.parametrize("name", ["switch", "mixtral", "deepseekmoe", "deepseekv3"])
 def test_full_size_layer(name):
-    cfg = W.CONFIGS[name]
-    T, E, k, D = cfg.num_tokens, cfg.num_experts, cfg.top_k, cfg.d_model
     print(f"[full-size parity] {name}", flush=True)
+    _check_full_weights(W.CONFIGS[name], SAMPLE[name])
+
+
+@pytest.mark.parametrize("T", W.DECODE_TOKENS)
+@pytest.mark.parametrize("name", ["deepseekv3", "mixtral"])
+def test_decode_full_size(name, T):
+    """Decode-sized batches (the first T tokens of the workload) on the
+    full-size Mixtral- and DeepSeek-V3-shaped weights, as bench.py times them:
+    every routing decision, and the outputs of up to 32 tokens."""
+    cfg = W.decode_config(W.CONFIGS[name], T)
+    print(f"[decode full-size parity] {cfg.name}", flush=True)
+    _check_full_weights(cfg, min(T, DECODE_SAMPLE))
+
+
+def _check_full_weights(cfg, n_sample):
+    T, E, k, D = cfg.num_tokens, cfg.num_experts, cfg.top_k, cfg.d_model
     dev = "cuda"
     inp = W.make_inputs(cfg, with_experts=False)
-    w13, w2, host = upload_experts(cfg, dev, keep_host=True)
+    w13, w2, host = _experts(W.base_name(cfg))
     weights = dict(w_router=to_torch(inp.w_router, dev), sel_bias=to_torch(inp.sel_bias, dev), w13=w13, w2=w2,
                    ws13=to_torch(inp.ws13, dev), ws2=to_torch(inp.ws2, dev))
     x = to_torch(inp.x, dev)
@@ -100,7 +127,7 @@ def test_full_size_layer(name):
     # --- sampled outputs, oracle expert by expert
     rng = np.random.default_rng(1234)
     cand = same if cfg.capacity_factor <= 0 or len(diff) == 0 else np.array([], dtype=np.int64)
-    sample = np.sort(rng.choice(cand, size=min(SAMPLE[name], len(cand)), replace=False))
+    sample = np.sort(rng.choice(cand, size=min(n_sample, len(cand)), replace=False))
     X = O.widen(inp.x[sample])
     y_ref = np.zeros((len(sample), D))
     users = {}

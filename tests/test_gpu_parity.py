@@ -421,6 +421,63 @@ def test_weight_streaming_many_tiles(cfg, gemm_cfg, monkeypatch):
     print(f"  max rel err {err:.3e}")
 
 
+KSPLIT_SHAPES = [
+    # many units per workgroup of the weight-streaming kernel, so that its ring
+    # crosses unit boundaries (other contraction offsets): a GELU layer with
+    # capacity (512- and 2048-deep contractions) and a SwiGLU one (256 / 1024)
+    W.MoEConfig("ksplit_gelu_capacity", 2048, 512, 128, 1, 2048, scoring=W.SOFTMAX_TOPK, renormalize=0,
+                activation=W.GELU, router_dtype=W.F32, capacity_factor=1.25),
+    W.MoEConfig("ksplit_swiglu_shared", 1024, 256, 48, 2, 1024, num_shared=1, d_ff_shared=512, zipf_s=1.0),
+]
+
+
+@pytest.mark.parametrize("ks", ["2", "4", "8"])
+@pytest.mark.parametrize("gemm_cfg", [str(c) for c in range(22, 30)])
+@pytest.mark.parametrize("cfg", KSPLIT_SHAPES, ids=lambda c: c.name)
+def test_contraction_split(cfg, gemm_cfg, ks, monkeypatch):
+    """Every configuration of the weight-streaming GEMM with its contraction
+    split in 2, 4 or 8 parts (float32 partial sums added by a second kernel;
+    a launch whose contraction the forced split does not divide runs unsplit)
+    against the oracle, shared expert included."""
+    monkeypatch.setenv("MOE_GEMM_CFG", gemm_cfg)
+    monkeypatch.setenv("MOE_GEMM_KSPLIT", ks)
+    print(f"[ksplit {ks} cfg {gemm_cfg}] {cfg.name}", flush=True)
+    inp = W.make_inputs(cfg)
+    ref = oracle_forward(cfg, inp)
+    got = DeviceLayer(cfg, inp).layer()
+    diff, err = check_layer(cfg, inp, ref, got)
+    print(f"  max rel err {err:.3e}")
+
+
+DECODE_SHAPES = [
+    # decode-sized batches with long contractions: every group is shallow and
+    # the tiles are few, so both projections run on the weight-streaming
+    # kernel with the contraction split (gate/up 4 and down 8 parts in the
+    # first; the shared expert split in the second; GELU in the third)
+    W.MoEConfig("decode_t1_e8", 1, 1024, 8, 2, 2048, scoring=W.TOPK_SOFTMAX, zipf_s=1.0),
+    W.MoEConfig("decode_t3_shared", 3, 512, 64, 8, 512, num_shared=1, d_ff_shared=1024,
+                scoring=W.SIGMOID_BIAS, zipf_s=1.2),
+    W.MoEConfig("decode_t2_gelu", 2, 768, 16, 1, 3072, scoring=W.SOFTMAX_TOPK, renormalize=0,
+                activation=W.GELU, router_dtype=W.F32),
+    W.MoEConfig("decode_t8_e64", 8, 1024, 64, 6, 1024, num_shared=2, d_ff_shared=512, renormalize=1),
+]
+
+
+@pytest.mark.parametrize("ks", ["auto", "1"])
+@pytest.mark.parametrize("cfg", DECODE_SHAPES, ids=lambda c: c.name)
+def test_decode_shapes(cfg, ks, monkeypatch):
+    """Decode-sized layers (1 to 8 tokens) against the oracle, with the
+    automatic contraction split and without it."""
+    if ks != "auto":
+        monkeypatch.setenv("MOE_GEMM_KSPLIT", ks)
+    print(f"[decode ksplit {ks}] {cfg.name}", flush=True)
+    inp = W.make_inputs(cfg)
+    ref = oracle_forward(cfg, inp)
+    got = DeviceLayer(cfg, inp).layer()
+    diff, err = check_layer(cfg, inp, ref, got)
+    print(f"  max rel err {err:.3e}")
+
+
 ROUTER_SHAPES = [
     # the router kernels' range (E <= 256, D % 64 == 0): float32 and bf16
     # weights, ragged expert counts, row counts that are not multiples of 16 or 32;
@@ -435,16 +492,27 @@ ROUTER_SHAPES = [
                 router_dtype=W.F32),
     W.MoEConfig("router_e200_bf16w", 257, 192, 200, 4, 64, scoring=W.SIGMOID_BIAS, zipf_s=1.2),
     W.MoEConfig("router_e256_f32w", 129, 512, 256, 8, 64, scoring=W.TOPK_SOFTMAX, router_dtype=W.F32),
+    # few tokens, many experts: the experts split over workgroups by default
+    W.MoEConfig("router_t1_e256_bf16w", 1, 7168, 256, 8, 64, scoring=W.SIGMOID_BIAS, zipf_s=1.2),
+    W.MoEConfig("router_t5_e160_f32w", 5, 384, 160, 4, 64, scoring=W.SOFTMAX_TOPK, renormalize=1,
+                router_dtype=W.F32),
+    # more tokens than the expert split takes by default
+    W.MoEConfig("router_t600_e256_bf16w", 600, 256, 256, 8, 64, scoring=W.SIGMOID_BIAS, zipf_s=1.2),
 ]
 
 
-@pytest.mark.parametrize("kernel", ["1", "0"])
+@pytest.mark.parametrize("kernel", ["1", "1-tiled", "1-split", "0"])
 @pytest.mark.parametrize("cfg", ROUTER_SHAPES, ids=lambda c: c.name)
 def test_router_logits_and_selection(cfg, kernel, monkeypatch):
     """Router logits within the refinement margin of the float64 logits and the
-    selection equal to the oracle's, with the router kernel (1) and the general
-    GEMM path (0)."""
-    monkeypatch.setenv("MOE_ROUTER_KERNEL", kernel)
+    selection equal to the oracle's, with the router kernels (1: the default
+    choice; 1-tiled / 1-split: for E > 64, every expert per workgroup / the
+    experts split over workgroups) and the general GEMM path (0)."""
+    monkeypatch.setenv("MOE_ROUTER_KERNEL", kernel[0])
+    if kernel == "1-tiled":
+        monkeypatch.setenv("MOE_ROUTER_SPLIT", "0")
+    if kernel == "1-split":
+        monkeypatch.setenv("MOE_ROUTER_SPLIT", "1")
     print(f"[router {kernel}] {cfg.name}", flush=True)
     T, E, k = cfg.num_tokens, cfg.num_experts, cfg.top_k
     inp = W.make_inputs(cfg, with_experts=False)

@@ -96,16 +96,22 @@ size_t ws_route(const moe_config* c) {
 size_t ws_permute(const moe_config* c) {
   return carve((size_t)ceil_div(c->num_tokens, kPermuteTile) * c->num_experts * 4);
 }
-size_t ws_ffn(const moe_config*, int G, int F, int max_rows, int act) {
-  return carve((size_t)max_rows * F * esize(act)) + 4 * carve((size_t)(G + 1) * 4);
+size_t ffn_partial_bytes_any(int act, int D, int F, int max_rows, int G);
+// expert FFN workspace: h [max_rows, F] | 4 tile prefixes of G+1 | float32
+// partial sums of contraction splits
+size_t ws_ffn(const moe_config* c, int G, int F, int max_rows, int act) {
+  return carve((size_t)max_rows * F * esize(act)) + 4 * carve((size_t)(G + 1) * 4) +
+         carve(ffn_partial_bytes_any(act, c->d_model, F, max_rows, G));
 }
 size_t ws_stats(const moe_config* c) {
   return carve((size_t)ceil_div(c->num_tokens, kStatsChunk) * c->num_experts * 4);
 }
 
+size_t ffn_partial_bytes(int act, int activation, int D, int F, int max_rows, int G, bool grouped);
+
 struct Layout {
   size_t logits, flags, wsplit, probs, idx, w, tile_counts, counts, offsets, tile_prefix, tile_prefix2, row_of, tor, h,
-      h_shared, yperm, partial, total;
+      h_shared, yperm, partial, kpart, kpart_shared, total;
 };
 
 Layout layer_layout(const moe_config* c, const Derived& d) {
@@ -132,6 +138,12 @@ Layout layer_layout(const moe_config* c, const Derived& d) {
   L.h_shared = take((size_t)T * c->num_shared * c->d_ff_shared * es);
   L.yperm = take((size_t)d.rows_cap * c->d_model * es);
   L.partial = take((size_t)ceil_div(c->num_tokens, kStatsChunk) * E * 4);
+  // float32 partial sums of contraction splits: routed and shared experts
+  // run on different streams, each with its own
+  L.kpart = take(ffn_partial_bytes(c->act_dtype, c->activation, c->d_model, c->d_ff, d.rows_cap, c->num_experts, true));
+  L.kpart_shared = take(c->num_shared > 0 ? ffn_partial_bytes(c->act_dtype, SWIGLU, c->d_model,
+                                                              c->num_shared * c->d_ff_shared, c->num_tokens, 1, false)
+                                          : 0);
   L.total = o;
   return L;
 }
@@ -256,17 +268,47 @@ struct FfnPlan {
   // configuration cfg_sh (one m-tile each), deeper groups to cfg_up / cfg_dn
   bool split;
   int cfg_sh, sh_rows;
+  // contraction splits (1 = none) of the four launches: gate/up, down, and
+  // the gate/up and down of the shallow groups of a split
+  int ks_up, ks_dn, ks_sh_up, ks_sh_dn;
 };
+
+// Contraction split of a weight-streaming launch whose tiles are too few to
+// give every CU a weight stream of its own (decode-sized batches: a few rows
+// per expert, and the down projection has only D / 128 column tiles per
+// expert): the largest power of two KS <= 8 with tiles * KS <= 256 (one unit
+// per CU), K / 64 divisible by KS and at least 4 slices of 64 per part.  The
+// tile count is bounded on the host from the row and group counts (the
+// routing is known on the device only).  MOE_GEMM_KSPLIT=<n> forces n where
+// it divides the contraction (tuning aid and test hook).
+constexpr int kSplitUnits = 256;
+int pick_ksplit(int act, int cfg, int epi, int N, int K, int G, int max_rows, bool grouped) {
+  if (act != BF16 || cfg < kGemmV2Configs + kGemmV3Configs || K % 64 != 0 || max_rows <= 0) return 1;
+  const int nk = K / 64;
+  const char* env = getenv("MOE_GEMM_KSPLIT");
+  if (env != nullptr && *env != '\0') {
+    const int f = atoi(env);
+    if (f == 1 || ((f == 2 || f == 4 || f == 8) && nk % f == 0)) return f;
+  }
+  const int c = cfg - kGemmV2Configs - kGemmV3Configs;
+  const int cols = epi == EPI_SWIGLU ? gemm_ws_bn(c) / 2 : gemm_ws_bn(c);
+  const int bm = gemm_ws_bm(c);
+  const long long m_tiles = grouped ? max_rows / bm + (G < max_rows ? G : max_rows) : ceil_div(max_rows, bm);
+  const long long tiles = m_tiles * ceil_div(N, cols);
+  int ks = 1;
+  while (ks < 8 && tiles * ks * 2 <= kSplitUnits && nk % (ks * 2) == 0 && nk / (ks * 2) >= 4) ks *= 2;
+  return ks;
+}
 
 // Shallow groups are split off when both contractions are long (the
 // weight stream of a tile then dwarfs its start-up) and groups are shallow on
-// average.  MOE_GEMM_SPLIT=0 / 1 overrides the choice (tuning aid).
-FfnPlan plan_ffn(int act, int D, int F, int max_rows, int G, bool grouped) {
+// average.  MOE_GEMM_SPLIT=0 / 1 overrides the choice (tuning aid).  When
+// every group is shallow (at most sh_rows rows in all: a decode-sized
+// batch) both projections run on the shallow-group configuration alone.
+FfnPlan plan_ffn(int act, int activation, int D, int F, int max_rows, int G, bool grouped) {
   FfnPlan pl;
   pl.cfg_up = pick_cfg(act, D, max_rows, G, false);
   pl.cfg_dn = pick_cfg(act, F, max_rows, G, true);
-  pl.bm_up = cfg_bm(act, pl.cfg_up);
-  pl.bm_dn = cfg_bm(act, pl.cfg_dn);
   // shallow groups: the persistent weight-streaming kernel with 64x128 tiles
   // and a 5-deep ring (measured ~1% per DeepSeek-V3-shaped layer ahead of the
   // 64x256 persistent configuration of the deep-tile kernel)
@@ -275,12 +317,48 @@ FfnPlan plan_ffn(int act, int D, int F, int max_rows, int G, bool grouped) {
   if (sh_env != nullptr && *sh_env != '\0' && atoi(sh_env) >= kGemmV2Configs && atoi(sh_env) < kGemmConfigs)
     pl.cfg_sh = atoi(sh_env);
   pl.sh_rows = cfg_bm(act, pl.cfg_sh);
+  const char* cfg_env = getenv("MOE_GEMM_CFG");
+  const bool forced = cfg_env != nullptr && *cfg_env != '\0';
+  if (!forced && pl.cfg_up >= 0 && pl.cfg_dn >= 0 && D % 64 == 0 && F % 64 == 0 && max_rows <= pl.sh_rows) {
+    pl.cfg_up = pl.cfg_sh;
+    pl.cfg_dn = pl.cfg_sh;
+  }
+  pl.bm_up = cfg_bm(act, pl.cfg_up);
+  pl.bm_dn = cfg_bm(act, pl.cfg_dn);
   const bool able = grouped && pl.cfg_up >= 0 && pl.cfg_dn >= 0 && D % 64 == 0 && F % 64 == 0;
   const int avg = G > 0 ? max_rows / G : max_rows;
-  pl.split = able && D >= 1024 && F >= 1024 && avg < 320;
+  pl.split = able && D >= 1024 && F >= 1024 && avg < 320 && max_rows > pl.sh_rows;
   const char* env = getenv("MOE_GEMM_SPLIT");
   if (able && env != nullptr && *env != '\0') pl.split = atoi(env) != 0;
+  const int epi_up = activation == SWIGLU ? EPI_SWIGLU : EPI_GELU;
+  pl.ks_up = pick_ksplit(act, pl.cfg_up, epi_up, F, D, G, max_rows, grouped);
+  pl.ks_dn = pick_ksplit(act, pl.cfg_dn, EPI_STORE_ACT, D, F, G, max_rows, grouped);
+  pl.ks_sh_up = pl.split ? pick_ksplit(act, pl.cfg_sh, epi_up, F, D, G, max_rows, grouped) : 1;
+  pl.ks_sh_dn = pl.split ? pick_ksplit(act, pl.cfg_sh, EPI_STORE_ACT, D, F, G, max_rows, grouped) : 1;
   return pl;
+}
+
+// Bytes of float32 partial sums that the contraction splits of one expert FFN
+// need (the launches run one after another and share them).
+size_t ffn_partial_bytes(int act, int activation, int D, int F, int max_rows, int G, bool grouped) {
+  const FfnPlan pl = plan_ffn(act, activation, D, F, max_rows, G, grouped);
+  const size_t ldp_up = (size_t)(activation == SWIGLU ? 2 : 1) * F;
+  const int ks_up = pl.ks_up > pl.ks_sh_up ? pl.ks_up : pl.ks_sh_up;
+  const int ks_dn = pl.ks_dn > pl.ks_sh_dn ? pl.ks_dn : pl.ks_sh_dn;
+  size_t b = 0;
+  if (ks_up > 1) b = (size_t)ks_up * max_rows * ldp_up * 4;
+  if (ks_dn > 1) b = b > (size_t)ks_dn * max_rows * D * 4 ? b : (size_t)ks_dn * max_rows * D * 4;
+  return b;
+}
+// ... for either activation, grouped or not (moe_expert_ffn's workspace)
+size_t ffn_partial_bytes_any(int act, int D, int F, int max_rows, int G) {
+  size_t b = 0;
+  for (int a : {SWIGLU, GELU})
+    for (bool gr : {false, true}) {
+      const size_t v = ffn_partial_bytes(act, a, D, F, max_rows, G, gr);
+      b = v > b ? v : b;
+    }
+  return b;
 }
 
 // The last round of a 256x256-tile launch with a long contraction (a round
@@ -315,6 +393,7 @@ hipError_t launch_gemm_tail_split(int act, int cfg, const GroupedGemm& g, hipStr
 }
 
 hipError_t launch_gemm(int act, int cfg, const GroupedGemm& g, hipStream_t s) {
+  if (g.ksplit > 1 && (act != BF16 || cfg < kGemmV2Configs + kGemmV3Configs)) return hipErrorInvalidValue;
   if (act != BF16) return launch_gemm_f32(g, F32, F32, s);
   if (cfg >= kGemmV2Configs + kGemmV3Configs) return launch_gemm_ws(g, cfg - kGemmV2Configs - kGemmV3Configs, s);
   if (cfg >= kGemmV2Configs) return launch_gemm_v3(g, cfg - kGemmV2Configs, s);
@@ -329,9 +408,9 @@ hipError_t launch_gemm(int act, int cfg, const GroupedGemm& g, hipStream_t s) {
 // class prefixes of a split).
 moe_status run_ffn(int act, int activation, int G, int D, int F, int max_rows, const void* x_in,
                    const int32_t* gather, const int32_t* offsets, const int32_t* prefix_up,
-                   int32_t* prefix_ws, const void* w13, const void* w2, void* h, void* y_out, hipStream_t s,
-                   void* const* ev = nullptr, int stage_up = 0, int stage_down = 0) {
-  const FfnPlan pl = plan_ffn(act, D, F, max_rows, G, offsets != nullptr);
+                   int32_t* prefix_ws, const void* w13, const void* w2, void* h, void* y_out, float* part,
+                   hipStream_t s, void* const* ev = nullptr, int stage_up = 0, int stage_down = 0) {
+  const FfnPlan pl = plan_ffn(act, activation, D, F, max_rows, G, offsets != nullptr);
   const int n_mat = activation == SWIGLU ? 2 : 1;
   GroupedGemm g1{};
   g1.A = x_in; g1.a_rows = gather; g1.lda = D;
@@ -347,7 +426,11 @@ moe_status run_ffn(int act, int activation, int G, int D, int F, int max_rows, c
   g2.M_max = max_rows; g2.N = D; g2.K = F;
   g2.G = G; g2.offsets = offsets; g2.tile_prefix = prefix_up;
   g2.epilogue = EPI_STORE_ACT;
+  g1.partial = part; g1.ldp = n_mat * F; g1.ksplit = pl.ks_up;
+  g2.partial = part; g2.ldp = D; g2.ksplit = pl.ks_dn;
   GroupedGemm g1s = g1, g2s = g2;       // shallow groups of a split
+  g1s.ksplit = pl.ks_sh_up;
+  g2s.ksplit = pl.ks_sh_dn;
   if (pl.split) {
     int32_t* deep_up = prefix_ws;
     int32_t* deep_dn = pl.bm_dn != pl.bm_up ? prefix_ws + (G + 1) : deep_up;
@@ -378,9 +461,13 @@ moe_status run_ffn(int act, int activation, int G, int D, int F, int max_rows, c
 // One projection of an ungrouped (shared-expert) FFN over `rows` rows:
 // gate/up with SwiGLU into h (up == true), or down from h into y_out.
 moe_status run_ffn_part(int act, int activation, int G, int D, int F, int rows, const void* x_in, const void* w13,
-                        const void* w2, void* h, void* y_out, hipStream_t s, void* const* ev, int stage, bool up) {
-  const FfnPlan pl = plan_ffn(act, D, F, rows, G, false);
+                        const void* w2, void* h, void* y_out, float* part, hipStream_t s, void* const* ev, int stage,
+                        bool up) {
+  const FfnPlan pl = plan_ffn(act, activation, D, F, rows, G, false);
   GroupedGemm g{};
+  g.partial = part;
+  g.ldp = up ? (activation == SWIGLU ? 2 : 1) * F : D;
+  g.ksplit = up ? pl.ks_up : pl.ks_dn;
   if (up) {
     g.A = x_in; g.lda = D; g.B = w13; g.b_group_stride = (long long)(activation == SWIGLU ? 2 : 1) * F * D;
     g.C = h; g.ldc = F; g.N = F; g.K = D;
@@ -555,15 +642,16 @@ moe_status moe_expert_ffn(const moe_config* cfg, int32_t num_groups, int32_t d_f
   void* h = ws;
   int32_t* prefix_up = nullptr;
   int32_t* prefix_dn = nullptr;
+  const size_t hb = carve((size_t)max_rows * d_ff * esize(cfg->act_dtype));
+  float* part = at<float>(ws, hb + 4 * carve((size_t)(num_groups + 1) * 4));
   if (offsets != nullptr) {
-    const size_t hb = carve((size_t)max_rows * d_ff * esize(cfg->act_dtype));
     prefix_up = at<int32_t>(ws, hb);
     prefix_dn = at<int32_t>(ws, hb + carve((size_t)(num_groups + 1) * 4));
-    const FfnPlan pl = plan_ffn(cfg->act_dtype, cfg->d_model, d_ff, max_rows, num_groups, true);
+    const FfnPlan pl = plan_ffn(cfg->act_dtype, activation, cfg->d_model, d_ff, max_rows, num_groups, true);
     if (!pl.split) MOE_TRY_HIP("tile prefix", launch_tile_prefix(offsets, num_groups, pl.bm_up, prefix_up, s));
   }
   return run_ffn(cfg->act_dtype, activation, num_groups, cfg->d_model, d_ff, max_rows, x_in, gather_rows,
-                 offsets, prefix_up, prefix_dn, w13, w2, h, y_out, s);
+                 offsets, prefix_up, prefix_dn, w13, w2, h, y_out, part, s);
 }
 
 moe_status moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* row_of,
@@ -660,10 +748,10 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const moe_weights* wt,
     MOE_TRY_HIP("fork", hipEventRecord(aux->fork, s));
     MOE_TRY_HIP("fork", hipStreamWaitEvent(aux->s, aux->fork, 0));
     MOE_TRY(run_ffn_part(cfg->act_dtype, SWIGLU, 1, D, SF, T, x, wt->ws13, wt->ws2, at<void>(ws, L.h_shared), y,
-                         aux->s, ev, MOE_STAGE_SHARED_GATE_UP, true));
+                         at<float>(ws, L.kpart_shared), aux->s, ev, MOE_STAGE_SHARED_GATE_UP, true));
     if (overlap == 2)
       MOE_TRY(run_ffn_part(cfg->act_dtype, SWIGLU, 1, D, SF, T, x, wt->ws13, wt->ws2, at<void>(ws, L.h_shared), y,
-                           aux->s, ev, MOE_STAGE_SHARED_DOWN, false));
+                           at<float>(ws, L.kpart_shared), aux->s, ev, MOE_STAGE_SHARED_DOWN, false));
     MOE_TRY_HIP("join", hipEventRecord(aux->join, aux->s));
   }
 
@@ -683,7 +771,7 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const moe_weights* wt,
   pa.tile_counts = at<int32_t>(ws, L.tile_counts);
   pa.counts = cnt; pa.offsets = off; pa.row_of = row_of; pa.token_of_row = tor;
   pa.tile_prefix = tp;
-  pa.bm = plan_ffn(cfg->act_dtype, D, cfg->d_ff, d.rows_cap, E, true).bm_up;
+  pa.bm = plan_ffn(cfg->act_dtype, cfg->activation, D, cfg->d_ff, d.rows_cap, E, true).bm_up;
   MOE_TRY(mark(ev, MOE_STAGE_PERMUTE, 0, s));
   MOE_TRY_HIP("permute", launch_permute(pa, s));
   MOE_TRY(mark(ev, MOE_STAGE_PERMUTE, 1, s));
@@ -711,14 +799,14 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const moe_weights* wt,
     void* yperm = at<void>(ws, L.yperm);
     if (d.rows_cap > 0)
       MOE_TRY(run_ffn(cfg->act_dtype, cfg->activation, E, D, cfg->d_ff, d.rows_cap, x, tor, off, tp,
-                      at<int32_t>(ws, L.tile_prefix2), wt->w13, wt->w2, h, yperm, s, ev, MOE_STAGE_EXPERT_GATE_UP,
-                      MOE_STAGE_EXPERT_DOWN));
+                      at<int32_t>(ws, L.tile_prefix2), wt->w13, wt->w2, h, yperm, at<float>(ws, L.kpart), s, ev,
+                      MOE_STAGE_EXPERT_GATE_UP, MOE_STAGE_EXPERT_DOWN));
     if (shared && overlap == 0)
       MOE_TRY(run_ffn_part(cfg->act_dtype, SWIGLU, 1, D, SF, T, x, wt->ws13, wt->ws2, at<void>(ws, L.h_shared), y,
-                           s, ev, MOE_STAGE_SHARED_GATE_UP, true));
+                           at<float>(ws, L.kpart_shared), s, ev, MOE_STAGE_SHARED_GATE_UP, true));
     if (shared && overlap != 2)
       MOE_TRY(run_ffn_part(cfg->act_dtype, SWIGLU, 1, D, SF, T, x, wt->ws13, wt->ws2, at<void>(ws, L.h_shared), y,
-                           s, ev, MOE_STAGE_SHARED_DOWN, false));
+                           at<float>(ws, L.kpart_shared), s, ev, MOE_STAGE_SHARED_DOWN, false));
     if (overlap == 2) MOE_TRY_HIP("join", hipStreamWaitEvent(s, aux->join, 0));
     const void* y_shared = shared ? y : nullptr;
     MOE_TRY(mark(ev, MOE_STAGE_COMBINE, 0, s));

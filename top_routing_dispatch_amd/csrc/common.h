@@ -134,6 +134,15 @@ struct GroupedGemm {
   int tail_mode;
   int round;
   int tail_pn;
+  // Split of the contraction (weight-streaming kernel only): with ksplit > 1
+  // every tile runs as ksplit units over consecutive K / ksplit slices; each
+  // unit writes its float32 sums to partial[(ks * M_max + row) * ldp + col]
+  // (SwiGLU: gate column h at col h, up column h at col N + h; ldp >= 2N,
+  // else ldp >= N), and a second kernel adds the ksplit parts in a fixed
+  // order and applies the epilogue.  0 or 1: no split.
+  int ksplit;
+  float* partial;
+  int ldp;
 };
 
 // Exact split of a float32 matrix into three bfloat16 planes, hi + mid + lo = w:
@@ -263,6 +272,7 @@ int gemm_v3_bm(int cfg);
 constexpr int kGemmWsConfigs = 8;
 hipError_t launch_gemm_ws(const GroupedGemm& g, int cfg, hipStream_t s);
 int gemm_ws_bm(int cfg);
+int gemm_ws_bn(int cfg);
 constexpr int kGemmConfigs = kGemmV2Configs + kGemmV3Configs + kGemmWsConfigs;
 // float32 SIMT grouped GEMM.  a_dtype / b_dtype select float32 or bf16 operands.
 hipError_t launch_gemm_f32(const GroupedGemm& g, int a_dtype, int b_dtype, hipStream_t s);

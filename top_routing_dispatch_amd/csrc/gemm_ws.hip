@@ -18,7 +18,12 @@
 //   * the output block of a compute wave is staged in an LDS area of its own
 //     (16 rows at a time), apart from the ring, for 16-byte row stores;
 //   * the workgroups of one XCD take consecutive tiles of the order, so the
-//     n-tiles of a group (which share its activation rows) run in one L2.
+//     n-tiles of a group (which share its activation rows) run in one L2;
+//   * when the tiles are too few to keep every CU streaming (a handful of
+//     token rows, as in decoding), the contraction of each tile can be split
+//     into ksplit units of K / ksplit: the units write float32 partial sums,
+//     and splitk_reduce_kernel adds them in a fixed order and applies the
+//     epilogue.
 // LDS rows are BK*2 bytes; the 16-byte chunk c of row r sits in slot
 // c ^ ((r / (16 / CPR)) % CPR) (CPR chunks per row), so that the 16 rows read
 // by one pass of a fragment load cover all 64 banks once.
@@ -92,7 +97,9 @@ __device__ __forceinline__ int swz_w(int r, int c) {
   return r * (CPR * 16) + ((c ^ ((r / (16 / CPR)) & (CPR - 1))) << 4);
 }
 
-template <int BM, int BN, int WGM, int WGN, int BK, int NST, int OCC, int EPI>
+// SPLIT: the launch splits the contraction (p.ksplit > 1) and the kernel
+// writes float32 partial sums instead of the epilogue's output.
+template <int BM, int BN, int WGM, int WGN, int BK, int NST, int OCC, int EPI, bool SPLIT>
 __global__ __launch_bounds__(64 * (WGM * WGN + 4))
 __attribute__((amdgpu_waves_per_eu((WGM * WGN + 4) / 4 * OCC, (WGM * WGN + 4) / 4 * OCC)))
 void gemm_ws_kernel(const GroupedGemm p, int n_tiles) {
@@ -109,10 +116,13 @@ void gemm_ws_kernel(const GroupedGemm p, int n_tiles) {
   // slot v: the workgroups of one XCD (i % 8) hold consecutive slots
   const int S = gridDim.x;
   const int v = (S % kNumXcd == 0) ? (blockIdx.x % kNumXcd) * (S / kNumXcd) + blockIdx.x / kNumXcd : blockIdx.x;
-  const int total = (p.offsets == nullptr ? ceil_div(p.M_max, BM) : ld_table<true>(p.tile_prefix, p.G)) * n_tiles;
+  // units: tiles, each split into KS runs over K / KS (unit u: tile u / KS,
+  // part u % KS)
+  const int KS = SPLIT ? p.ksplit : 1;
+  const int total = (p.offsets == nullptr ? ceil_div(p.M_max, BM) : ld_table<true>(p.tile_prefix, p.G)) * n_tiles * KS;
   if (v >= total) return;
-  const int my_tiles = (total - 1 - v) / S + 1;     // tiles v, v + S, ...
-  const int nk = p.K / BK;
+  const int my_tiles = (total - 1 - v) / S + 1;     // units v, v + S, ...
+  const int nk = p.K / BK / KS;                      // slices per unit
   const int nsl = my_tiles * nk;                     // slices of the whole stream
 
   const bf16_t* __restrict__ A = static_cast<const bf16_t*>(p.A);
@@ -124,14 +134,18 @@ void gemm_ws_kernel(const GroupedGemm p, int n_tiles) {
   const int lrow = lane / C::CPR;
   const int lslot = lane % C::CPR;
 
-  // ---- loader: the tile and slice that the next refill reads ----
+  // ---- loader: the unit and slice that the next refill reads ----
   int ld_t = -1, ld_k = nk;
+  unsigned ld_kb = 0;                               // byte offset of the unit's first slice
   unsigned a_off[C::A_INS], b_off[C::B_INS];
   __amdgpu_buffer_rsrc_t b_rsrc = a_rsrc;
   auto ld_setup = [&](int t) __attribute__((always_inline)) {
     // scalar loads only: the ring's loads in flight are not waited for here
     int g, row0, rows, nt;
-    decode_tile<BM, true>(p, n_tiles, v + t * S, g, row0, rows, nt);
+    const int u = v + t * S;
+    const int tile = u / KS;
+    ld_kb = (unsigned)((u - tile * KS) * nk) * C::RB;
+    decode_tile<BM, true>(p, n_tiles, tile, g, row0, rows, nt);
     const bf16_t* B = static_cast<const bf16_t*>(p.B) + (long long)g * p.b_group_stride;
     b_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(B), 0, (int)kRangeEnd, 0x00020000);
     // instruction q of the wave reads rows r0 .. r0 + RPI - 1, lane row
@@ -178,7 +192,7 @@ void gemm_ws_kernel(const GroupedGemm p, int n_tiles) {
       ld_setup(ld_t);
     }
     char* st = smem + slot * C::STAGE;
-    const unsigned koff = (unsigned)ld_k * C::RB;
+    const unsigned koff = ld_kb + (unsigned)ld_k * C::RB;
 #pragma unroll
     for (int q = 0; q < C::A_INS; ++q) dma16_w(a_rsrc, a_off[q] + koff, st + (lw * C::A_INS + q) * 1024);
 #pragma unroll
@@ -187,10 +201,13 @@ void gemm_ws_kernel(const GroupedGemm p, int n_tiles) {
     ++ld_k;
   };
 
-  // ---- consumer: the tile being multiplied ----
-  int c_g, c_row0, c_rows, c_nt, act_i;
+  // ---- consumer: the unit being multiplied ----
+  int c_g, c_row0, c_rows, c_nt, c_ks, act_i;
   auto cp_setup = [&](int t) __attribute__((always_inline)) {
-    decode_tile<BM, true>(p, n_tiles, v + t * S, c_g, c_row0, c_rows, c_nt);
+    const int u = v + t * S;
+    const int tile = u / KS;
+    c_ks = u - tile * KS;
+    decode_tile<BM, true>(p, n_tiles, tile, c_g, c_row0, c_rows, c_nt);
     // 32-row blocks of this wave that hold at least one row of the tile
     act_i = min(C::TM, max(0, ceil_div(c_rows - wm * C::WM, 32)));
   };
@@ -265,7 +282,34 @@ void gemm_ws_kernel(const GroupedGemm p, int n_tiles) {
     }
   };
 
-  // ---- the stream: slice j of the workgroup's tiles sits in ring slot j % NST ----
+  // split contraction: the unit's float32 sums straight from the accumulators
+  // (lane: column fr of each 32x32 block, rows 8 (r / 4) + 4 (lane / 32) + r % 4)
+  auto epilogue_partial = [&]() __attribute__((always_inline)) {
+    float* __restrict__ P = p.partial + (size_t)c_ks * p.M_max * p.ldp;
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) {
+      if (i >= act_i) continue;
+#pragma unroll
+      for (int jj = 0; jj < C::TN; ++jj) {
+        int col;
+        if constexpr (EPI == EPI_SWIGLU) {
+          const int h = c_nt * (BN / 2) + (wn * (C::TN / 2) + (jj >> 1)) * 32 + fr;
+          if (h >= p.N) continue;
+          col = (jj & 1) ? p.N + h : h;
+        } else {
+          col = c_nt * BN + wn * C::WN + jj * 32 + fr;
+          if (col >= p.N) continue;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rl = wm * C::WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          if (rl < c_rows) P[(size_t)(c_row0 + rl) * p.ldp + col] = acc[i][jj][r];
+        }
+      }
+    }
+  };
+
+  // ---- the stream: slice j of the workgroup's units sits in ring slot j % NST ----
   if (loader) {
     for (int s = 0; s < NST - 1 && s < nsl; ++s) load_next(s);
     int slot_l = NST - 1;
@@ -351,7 +395,8 @@ void gemm_ws_kernel(const GroupedGemm p, int n_tiles) {
     slot_c = slot_c + 1 == NST ? 0 : slot_c + 1;
 
     if (++kt == nk) {
-      epilogue();
+      if constexpr (SPLIT) epilogue_partial();
+      else epilogue();
 #pragma unroll
       for (int i = 0; i < C::TM; ++i)
 #pragma unroll
@@ -360,6 +405,48 @@ void gemm_ws_kernel(const GroupedGemm p, int n_tiles) {
           for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.0f;
       kt = 0;
       if (++ct < my_tiles) cp_setup(ct);
+    }
+  }
+}
+
+// Sum of the ksplit partial results of each tile (part 0 first, then 1, ...)
+// and the epilogue, over the same tiles as the GEMM launch; four columns per
+// thread.
+template <int BM, int COLS, int EPI>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const GroupedGemm p, int n_tiles) {
+  const int total = (p.offsets == nullptr ? ceil_div(p.M_max, BM) : p.tile_prefix[p.G]) * n_tiles;
+  const int KS = p.ksplit;
+  const size_t part = (size_t)p.M_max * p.ldp;
+  bf16_t* __restrict__ Cout = static_cast<bf16_t*>(p.C);
+  constexpr int C4 = COLS / 4;
+  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+    int g, row0, rows, nt;
+    decode_tile<BM>(p, n_tiles, tile, g, row0, rows, nt);
+    const int c0 = nt * COLS;
+    const int ncols = min(COLS, p.N - c0);
+    for (int i = threadIdx.x; i < rows * C4; i += blockDim.x) {
+      const int r = i / C4, c = (i % C4) * 4;
+      if (c >= ncols) continue;
+      const float* __restrict__ P = p.partial + (size_t)(row0 + r) * p.ldp + c0 + c;
+      float a[4] = {0.0f, 0.0f, 0.0f, 0.0f}, b[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (c + e < ncols) {
+            a[e] += P[ks * part + e];
+            if constexpr (EPI == EPI_SWIGLU) b[e] += P[ks * part + p.N + e];
+          }
+        }
+      }
+      bf16_t* dst = Cout + (size_t)(row0 + r) * p.ldc + c0 + c;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (c + e >= ncols) continue;
+        float v = a[e];
+        if constexpr (EPI == EPI_SWIGLU) v = silu_f32(a[e]) * b[e];
+        if constexpr (EPI == EPI_GELU) v = gelu_bf16out(a[e]);
+        dst[e] = f32_to_bf16_rn(v);
+      }
     }
   }
 }
@@ -376,11 +463,16 @@ hipError_t launch_ws(const GroupedGemm& p, hipStream_t s) {
   const long long b_group_bytes = (long long)((EPI == EPI_SWIGLU) ? 2 * p.N : p.N) * p.K * 2;
   if (b_group_bytes >= (long long)kRangeEnd || (long long)p.lda * 2 * p.M_max >= (long long)kRangeEnd)
     return hipErrorInvalidValue;
-  const int cols = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
+  constexpr int cols = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
   const int n_tiles = ceil_div(p.N, cols);
   if (n_tiles == 0 || p.M_max == 0) return hipSuccess;
-  const long long bound = (long long)(p.offsets == nullptr ? ceil_div(p.M_max, BM)
+  const long long tiles = (long long)(p.offsets == nullptr ? ceil_div(p.M_max, BM)
                                                            : p.M_max / BM + std::min(p.G, p.M_max)) * n_tiles;
+  const int KS = p.ksplit > 1 ? p.ksplit : 1;
+  if (KS > 1 && (p.partial == nullptr || (p.K / BK) % KS != 0 ||
+                 p.ldp < ((EPI == EPI_SWIGLU) ? 2 * p.N : p.N)))
+    return hipErrorInvalidValue;
+  const long long bound = tiles * KS;
   if (bound > 0x7fffffffLL) return hipErrorInvalidValue;
   const int blocks = (int)std::min<long long>(bound, (long long)num_cus() * OCC);
   static bool allowed[64] = {};
@@ -388,13 +480,25 @@ hipError_t launch_ws(const GroupedGemm& p, hipStream_t s) {
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64 || !allowed[dev]) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_ws_kernel<BM, BN, WGM, WGN, BK, NST, OCC, EPI>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_ws_kernel<BM, BN, WGM, WGN, BK, NST, OCC, EPI, false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_ws_kernel<BM, BN, WGM, WGN, BK, NST, OCC, EPI, true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
     if (e != hipSuccess) return e;
     if (dev >= 0 && dev < 64) allowed[dev] = true;
   }
-  hipLaunchKernelGGL((gemm_ws_kernel<BM, BN, WGM, WGN, BK, NST, OCC, EPI>), dim3((unsigned)blocks),
+  if (KS == 1) {
+    hipLaunchKernelGGL((gemm_ws_kernel<BM, BN, WGM, WGN, BK, NST, OCC, EPI, false>), dim3((unsigned)blocks),
+                       dim3(C::THREADS), LDS, s, p, n_tiles);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((gemm_ws_kernel<BM, BN, WGM, WGN, BK, NST, OCC, EPI, true>), dim3((unsigned)blocks),
                      dim3(C::THREADS), LDS, s, p, n_tiles);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((splitk_reduce_kernel<BM, cols, EPI>), dim3((unsigned)std::min<long long>(tiles, 4096)),
+                     dim3(256), 0, s, p, n_tiles);
   return hipGetLastError();
 }
 
@@ -423,6 +527,11 @@ hipError_t launch_ws_epi(const GroupedGemm& p, int cfg, hipStream_t s) {
 int gemm_ws_bm(int cfg) {
   static const int bm[] = {128, 128, 64, 64, 128, 128, 128, 128};
   return (cfg >= 0 && cfg < kGemmWsConfigs) ? bm[cfg] : 0;
+}
+
+int gemm_ws_bn(int cfg) {
+  static const int bn[] = {128, 128, 256, 128, 128, 128, 128, 128};
+  return (cfg >= 0 && cfg < kGemmWsConfigs) ? bn[cfg] : 0;
 }
 
 hipError_t launch_gemm_ws(const GroupedGemm& p, int cfg, hipStream_t s) {

@@ -4,20 +4,23 @@
 // E <= 256 and D a multiple of 64 ("Top-k 路由" page, step 1 of the gate: one
 // bias-free linear layer).
 //
-// 65 <= E <= 256: one workgroup owns 32 tokens and every expert, so each
-// token row is read once and each token fragment feeds NP MFMAs.  Operands
-// stream through an LDS ring (up to 4 deep) of 64-deep K slices (buffer loads
-// with the LDS bit).
-// E <= 64: the weights are small and the work is reading the tokens.  One
-// workgroup owns 16 tokens; its eight waves split the contraction (wave w
-// takes the 32-deep steps w, w + 8, ...), load their operands straight into
-// registers for 16x16x32 MFMAs, and add their partial sums in LDS at the end
-// in a fixed order.
+// 65 <= E <= 256 and many tokens: one workgroup owns 32 tokens and every
+// expert, so each token row is read once and each token fragment feeds NP
+// MFMAs.  Operands stream through an LDS ring (up to 4 deep) of 64-deep K
+// slices (buffer loads with the LDS bit).
+// E <= 64, or few tokens: one workgroup owns 16 tokens and up to 64 experts
+// (every expert when E <= 64; blocks of 16 experts side by side in the grid
+// when the tokens are few and the experts many); its eight waves split the
+// contraction (wave w takes the 32-deep steps w, w + 8, ...), load their
+// operands straight into registers for 16x16x32 MFMAs, and add their partial
+// sums in LDS at the end in a fixed order.
 // Either way the MFMA sums of at most 64 products per plane are added into
 // float64 accumulators, which keeps the logits within a small multiple of
 // float32 rounding of the exact sum, as the selection's near-tie refinement
 // requires.
 #include "common.h"
+
+#include <cstdlib>
 
 namespace moe {
 namespace {
@@ -168,6 +171,7 @@ __global__ __launch_bounds__(512) void router_small_kernel(const bf16_t* __restr
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row0 = blockIdx.x * 16;
+  const int e0 = blockIdx.y * (NB * 16);            // this workgroup's experts e0 .. e0 + 16 NB - 1
   const int tok = min(row0 + (lane & 15), T - 1);   // rows past the end read the last row
   const int kg = (lane >> 4) * 8;                   // this lane's 8 of a 32-deep step
   const bf16_t* xr = x + (long long)tok * D + kg;
@@ -176,7 +180,7 @@ __global__ __launch_bounds__(512) void router_small_kernel(const bf16_t* __restr
   for (int b = 0; b < NB; ++b)
 #pragma unroll
     for (int p = 0; p < NP; ++p)
-      wr[b][p] = w + ((long long)min(b * 16 + (lane & 15), E - 1) * NP + p) * D + kg;
+      wr[b][p] = w + ((long long)min(e0 + b * 16 + (lane & 15), E - 1) * NP + p) * D + kg;
 
   floatx4_t acc[NB];
   double dacc[NB][4];
@@ -230,18 +234,34 @@ __global__ __launch_bounds__(512) void router_small_kernel(const bf16_t* __restr
       }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < 16 * E; i += 512) {
-    const int tr = i / E, e = i % E;
+  const int ne = min(NB * 16, E - e0);
+  for (int i = threadIdx.x; i < 16 * ne; i += 512) {
+    const int tr = i / ne, e = i % ne;
     if (row0 + tr < T)
-      logits[(long long)(row0 + tr) * E + e] = (float)(((part[0][tr][e] + part[1][tr][e]) + part[2][tr][e]) + part[3][tr][e]);
+      logits[(long long)(row0 + tr) * E + e0 + e] =
+          (float)(((part[0][tr][e] + part[1][tr][e]) + part[2][tr][e]) + part[3][tr][e]);
   }
 }
 
+// Grid: 16-token blocks x blocks of 16 NB experts (one expert block when
+// E <= 16 NB).
 template <int NB, int NP>
 hipError_t launch_router_small(const bf16_t* x, const bf16_t* w, float* logits, int T, int E, int D, hipStream_t s) {
   constexpr int U = NP == 1 ? (NB <= 2 ? 8 : 4) : 2;
-  hipLaunchKernelGGL((router_small_kernel<NB, NP, U>), dim3(ceil_div(T, 16)), dim3(512), 0, s, x, w, logits, T, E, D);
+  hipLaunchKernelGGL((router_small_kernel<NB, NP, U>), dim3(ceil_div(T, 16), ceil_div(E, NB * 16)), dim3(512), 0, s,
+                     x, w, logits, T, E, D);
   return hipGetLastError();
+}
+
+// Few tokens and many experts: the tiled kernel would run ceil(T / 32)
+// workgroups, each reading every expert's weights; splitting the experts over
+// workgroups of the small-E kernel spreads that weight read over the chip.
+// Measured on MI355X at E = 256, D = 7168: 79 us for one token on the tiled
+// kernel.  MOE_ROUTER_SPLIT=0 / 1 forces the choice (tuning aid).
+bool router_split_experts(int T, int E) {
+  const char* env = getenv("MOE_ROUTER_SPLIT");
+  if (env != nullptr && *env != '\0') return atoi(env) != 0;
+  return E > 64 && T <= 512;
 }
 
 }  // namespace
@@ -262,6 +282,10 @@ hipError_t launch_router_logits(const bf16_t* x, const bf16_t* w, int planes, fl
     if (E <= 16) return launch_router_small<1, 1>(x, w, logits, T, E, D, s);
     if (E <= 32) return launch_router_small<2, 1>(x, w, logits, T, E, D, s);
     return launch_router_small<4, 1>(x, w, logits, T, E, D, s);
+  }
+  if (router_split_experts(T, E)) {
+    if (planes == 3) return launch_router_small<1, 3>(x, w, logits, T, E, D, s);
+    return launch_router_small<1, 1>(x, w, logits, T, E, D, s);
   }
   if (planes == 3) return launch_router_cfg<128, 3>(x, w, logits, T, E, D, s);
   if (E <= 128) return launch_router_cfg<128, 1>(x, w, logits, T, E, D, s);

@@ -84,6 +84,25 @@ DEEPSEEKV3 = MoEConfig("deepseekv3", 8192, 7168, 256, 8, 2048, num_shared=1,
 
 CONFIGS = {c.name: c for c in (TINY, SWITCH, MIXTRAL, DEEPSEEKMOE, DEEPSEEKV3)}
 
+# Decode-shaped batches: the first T tokens of a workload with its full-size
+# weights (token generation runs the layer on a handful of tokens per step,
+# where the expert matrices are read for very few rows each).
+DECODE_TOKENS = (1, 8, 64, 256)
+DECODE_SEP = "_decode_t"
+
+
+def decode_config(cfg: MoEConfig, tokens: int) -> MoEConfig:
+    return cfg.replace(name=f"{cfg.name}{DECODE_SEP}{tokens}", num_tokens=tokens)
+
+
+def base_name(cfg: MoEConfig) -> str:
+    """The workload whose weights a (decode-shaped) configuration uses."""
+    return cfg.name.split(DECODE_SEP)[0]
+
+
+DECODE_CONFIGS = {d.name: d for d in (decode_config(CONFIGS[n], t) for n in ("mixtral", "deepseekv3")
+                                      for t in DECODE_TOKENS)}
+
 
 # --------------------------------------------------------------------------
 # bfloat16 encoding (input preparation only)
