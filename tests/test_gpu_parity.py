@@ -460,6 +460,11 @@ DECODE_SHAPES = [
     W.MoEConfig("decode_t2_gelu", 2, 768, 16, 1, 3072, scoring=W.SOFTMAX_TOPK, renormalize=0,
                 activation=W.GELU, router_dtype=W.F32),
     W.MoEConfig("decode_t8_e64", 8, 1024, 64, 6, 1024, num_shared=2, d_ff_shared=512, renormalize=1),
+    # long rows: the combine spreads one token's row over two workgroups
+    # (bf16 with a shared expert, bf16 top-1, float32)
+    W.MoEConfig("decode_t5_wide", 5, 8192, 16, 4, 128, num_shared=1, d_ff_shared=128, renormalize=1),
+    W.MoEConfig("decode_t3_wide_k1", 3, 9216, 8, 1, 128, renormalize=0),
+    W.MoEConfig("decode_t2_f32_wide", 2, 4096, 4, 2, 64, act_dtype=W.F32, router_dtype=W.F32),
 ]
 
 
@@ -496,23 +501,26 @@ ROUTER_SHAPES = [
     W.MoEConfig("router_t1_e256_bf16w", 1, 7168, 256, 8, 64, scoring=W.SIGMOID_BIAS, zipf_s=1.2),
     W.MoEConfig("router_t5_e160_f32w", 5, 384, 160, 4, 64, scoring=W.SOFTMAX_TOPK, renormalize=1,
                 router_dtype=W.F32),
+    W.MoEConfig("router_t16_e8_bf16w", 16, 4096, 8, 2, 64, scoring=W.TOPK_SOFTMAX, zipf_s=1.0),
+    W.MoEConfig("router_t3_e64_bf16w", 3, 2048, 64, 6, 64, scoring=W.SOFTMAX_TOPK, renormalize=1),
+    W.MoEConfig("router_t9_e128_f32w", 9, 768, 128, 1, 64, scoring=W.SOFTMAX_TOPK, renormalize=0,
+                router_dtype=W.F32),
     # more tokens than the expert split takes by default
     W.MoEConfig("router_t600_e256_bf16w", 600, 256, 256, 8, 64, scoring=W.SIGMOID_BIAS, zipf_s=1.2),
 ]
 
 
-@pytest.mark.parametrize("kernel", ["1", "1-tiled", "1-split", "0"])
+@pytest.mark.parametrize("kernel", ["1", "1-tiled", "1-split", "1-gemv", "0"])
 @pytest.mark.parametrize("cfg", ROUTER_SHAPES, ids=lambda c: c.name)
 def test_router_logits_and_selection(cfg, kernel, monkeypatch):
     """Router logits within the refinement margin of the float64 logits and the
     selection equal to the oracle's, with the router kernels (1: the default
     choice; 1-tiled / 1-split: for E > 64, every expert per workgroup / the
-    experts split over workgroups) and the general GEMM path (0)."""
+    experts split over workgroups; 1-gemv: one wave per expert, where the
+    tokens fit) and the general GEMM path (0)."""
     monkeypatch.setenv("MOE_ROUTER_KERNEL", kernel[0])
-    if kernel == "1-tiled":
-        monkeypatch.setenv("MOE_ROUTER_SPLIT", "0")
-    if kernel == "1-split":
-        monkeypatch.setenv("MOE_ROUTER_SPLIT", "1")
+    if kernel != "1" and kernel[0] == "1":
+        monkeypatch.setenv("MOE_ROUTER_PATH", kernel[2:])
     print(f"[router {kernel}] {cfg.name}", flush=True)
     T, E, k = cfg.num_tokens, cfg.num_experts, cfg.top_k
     inp = W.make_inputs(cfg, with_experts=False)

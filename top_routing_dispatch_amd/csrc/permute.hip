@@ -7,8 +7,8 @@
 // expert keeps its first C assignments in that order; the rest are dropped
 // and the residual path carries them ("别只比较 Top-k" mechanism table).
 //
-// Three small kernels, all deterministic (integer atomics only, whose result
-// does not depend on their order):
+// Three small kernels (one, when the batch fits one tile), all deterministic
+// (integer atomics only, whose result does not depend on their order):
 //   histogram  per 256-token tile, per expert: a bit mask of the tile's tokens
 //              that chose the expert (LDS atomicOr), popcounted;
 //   scan       per expert over tiles -> tile bases and nominal counts; kept =
@@ -137,6 +137,73 @@ __global__ __launch_bounds__(kPermuteTile) void scatter_kernel(const PermuteArgs
   }
 }
 
+// All three steps in one workgroup when the batch is a single tile (at most
+// kPermuteTile tokens, as in decoding): thread i owns experts 4i .. 4i+3 for
+// the counts and the scans, and token i for the scatter.
+__global__ __launch_bounds__(kPermuteTile) void permute_one_tile_kernel(const PermuteArgs a) {
+  static_assert(kMaxExperts <= 4 * kPermuteTile, "four experts per thread");
+  __shared__ uint32_t mask[kMaxExperts * kWordsPerTile];
+  __shared__ int s_off[kMaxExperts + 1];
+  __shared__ int s_scan[kPermuteTile];
+  __shared__ int s_total;
+  const uint32_t skip = build_masks(a, mask);
+  const int tid = threadIdx.x;
+  int kept[4], mt[4], sum_k = 0, sum_m = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = tid * 4 + q;
+    int c = 0;
+    if (e < a.E) {
+#pragma unroll
+      for (int w = 0; w < kWordsPerTile; ++w) c += __popc(mask[e * kWordsPerTile + w]);
+      a.counts[e] = c;
+    }
+    kept[q] = min(c, a.capacity);
+    mt[q] = ceil_div(kept[q], a.bm);
+    sum_k += kept[q];
+    sum_m += mt[q];
+  }
+  int off = block_exclusive_scan(sum_k, s_scan);
+  int mo = block_exclusive_scan(sum_m, s_scan);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = tid * 4 + q;
+    if (e < a.E) {
+      a.offsets[e] = off;
+      s_off[e] = off;
+      if (a.tile_prefix != nullptr) a.tile_prefix[e] = mo;
+    }
+    off += kept[q];
+    mo += mt[q];
+    if (e == a.E - 1) {
+      a.offsets[a.E] = off;
+      s_off[a.E] = off;
+      s_total = off;
+      if (a.tile_prefix != nullptr) a.tile_prefix[a.E] = mo;
+    }
+  }
+  __syncthreads();
+  for (int r = s_total + tid; r < a.rows_cap; r += blockDim.x) a.token_of_row[r] = -1;
+  const int t = tid;
+  if (t >= a.T) return;
+  const int word = tid >> 5;
+  const uint32_t below = (1u << (tid & 31)) - 1u;
+  for (int j = 0; j < a.k; ++j) {
+    int row = -1;
+    if (!((skip >> j) & 1u)) {
+      const int e = a.topk_idx[(long long)t * a.k + j];
+      const uint32_t* m = mask + e * kWordsPerTile;
+      int rank = __popc(m[word] & below);
+      for (int w = 0; w < word; ++w) rank += __popc(m[w]);
+      if (rank < s_off[e + 1] - s_off[e]) {
+        row = s_off[e] + rank;
+        a.token_of_row[row] = t;
+      }
+    }
+    a.row_of[(long long)t * a.k + j] = row;
+  }
+}
+
 // x_perm[r] = x[token_of_row[r]] for rows with a token; 16-byte chunks.
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restrict__ x,
                                                           const int32_t* __restrict__ tor,
@@ -207,7 +274,7 @@ constexpr int kCombineSlots = 1024;           // row indices / weights of a work
 template <typename T, int G>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ yp, const int32_t* __restrict__ row_of,
                                                       const float* __restrict__ tw, const T* ys, T* y,
-                                                      int ntok, int k, int D, int tpb) {
+                                                      int ntok, int k, int D, int tpb, int cseg) {
   constexpr int N = Chunk<T>::N;
   constexpr int U = G >= 4 ? 8 / G : 4 / G;     // items per thread
   __shared__ int srow[kCombineSlots];
@@ -219,8 +286,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ yp, 
     sw[i] = tw[(long long)t0 * k + i];
   }
   __syncthreads();
-  const int chunks = D / N;
-  const int items = nt * chunks;
+  // this workgroup's chunks of each of its tokens: [c0, c0 + cn)
+  const int c0 = blockIdx.y * cseg;
+  const int cn = min(cseg, D / N - c0);
+  const int items = nt * cn;
   for (int base = 0; base < items; base += 256 * U) {
     int tl[U], cc[U];
     bool ok[U];
@@ -228,8 +297,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ yp, 
     for (int u = 0; u < U; ++u) {
       const int it = base + (int)threadIdx.x + 256 * u;
       ok[u] = it < items;
-      tl[u] = ok[u] ? it / chunks : 0;
-      cc[u] = ok[u] ? it % chunks : 0;
+      tl[u] = ok[u] ? it / cn : 0;
+      cc[u] = ok[u] ? c0 + it % cn : 0;
     }
     float acc[U][N];
     uint4 vs[U];
@@ -364,6 +433,10 @@ __global__ __launch_bounds__(kMaxExperts) void stats_final_kernel(const StatsArg
 
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
   const int ntiles = ceil_div(a.T, kPermuteTile);
+  if (ntiles == 1) {
+    hipLaunchKernelGGL(permute_one_tile_kernel, dim3(1), dim3(kPermuteTile), 0, s, a);
+    return hipGetLastError();
+  }
   if (ntiles > 0) {
     hipLaunchKernelGGL(hist_kernel, dim3(ntiles), dim3(kPermuteTile), 0, s, a);
     hipError_t err = hipGetLastError();
@@ -395,15 +468,20 @@ hipError_t launch_combine_t(const void* y_perm, const int32_t* row_of, const flo
   // tokens per workgroup: enough items for every thread's U, within the LDS slots
   int tpb = (256 * U + chunks - 1) / chunks;
   tpb = std::max(1, std::min(tpb, kCombineSlots / k));
-  const dim3 grid((unsigned)ceil_div(ntok, tpb));
+  // few tokens with long rows (decode-sized batches): a token's chunks are
+  // spread over several workgroups of one pass each, instead of one
+  // workgroup taking several dependent passes
+  int cseg = chunks;
+  if (tpb == 1 && ntok < 1024) cseg = 256 * U;
+  const dim3 grid((unsigned)ceil_div(ntok, tpb), (unsigned)ceil_div(chunks, cseg));
   const E* yp = static_cast<const E*>(y_perm);
   const E* ys = static_cast<const E*>(y_shared);
   E* yo = static_cast<E*>(y);
   switch (G) {
-    case 1: hipLaunchKernelGGL((combine_kernel<E, 1>), grid, dim3(256), 0, s, yp, row_of, topk_w, ys, yo, ntok, k, D, tpb); break;
-    case 2: hipLaunchKernelGGL((combine_kernel<E, 2>), grid, dim3(256), 0, s, yp, row_of, topk_w, ys, yo, ntok, k, D, tpb); break;
-    case 4: hipLaunchKernelGGL((combine_kernel<E, 4>), grid, dim3(256), 0, s, yp, row_of, topk_w, ys, yo, ntok, k, D, tpb); break;
-    default: hipLaunchKernelGGL((combine_kernel<E, 8>), grid, dim3(256), 0, s, yp, row_of, topk_w, ys, yo, ntok, k, D, tpb); break;
+    case 1: hipLaunchKernelGGL((combine_kernel<E, 1>), grid, dim3(256), 0, s, yp, row_of, topk_w, ys, yo, ntok, k, D, tpb, cseg); break;
+    case 2: hipLaunchKernelGGL((combine_kernel<E, 2>), grid, dim3(256), 0, s, yp, row_of, topk_w, ys, yo, ntok, k, D, tpb, cseg); break;
+    case 4: hipLaunchKernelGGL((combine_kernel<E, 4>), grid, dim3(256), 0, s, yp, row_of, topk_w, ys, yo, ntok, k, D, tpb, cseg); break;
+    default: hipLaunchKernelGGL((combine_kernel<E, 8>), grid, dim3(256), 0, s, yp, row_of, topk_w, ys, yo, ntok, k, D, tpb, cseg); break;
   }
   return hipGetLastError();
 }

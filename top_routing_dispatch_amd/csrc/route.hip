@@ -71,17 +71,42 @@ __device__ __forceinline__ void wave_argmax_f64(double& v, int& e) {
   }
 }
 
-// Four consecutive elements (D is a multiple of 4) widened to float.
-__device__ __forceinline__ void load4(const void* p, int dt, long long i, float v[4]) {
-  if (dt == BF16) {
-    const uint2 q = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(p) + i);
-    v[0] = __uint_as_float(q.x << 16); v[1] = __uint_as_float(q.x & 0xffff0000u);
-    v[2] = __uint_as_float(q.y << 16); v[3] = __uint_as_float(q.y & 0xffff0000u);
-  } else {
-    const float4 q = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
-    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+// EL consecutive elements, bf16 (BF) or float32, as raw 16-byte words, and
+// widened to float.  The type is a template parameter, and the loads of a
+// batch are issued before any is widened, so that they are in flight
+// together.
+template <bool BF, int EL>
+struct RawEl {
+  static_assert(EL == 4 || EL == 8, "elements per load");
+  static constexpr int NQ = BF ? EL / 8 + (EL % 8 != 0) : EL / 4;
+  uint4 q[NQ];
+  __device__ __forceinline__ void load(const void* p, long long i) {
+    if constexpr (BF) {
+      const bf16_t* b = static_cast<const bf16_t*>(p) + i;
+      if constexpr (EL == 8) {
+        q[0] = *reinterpret_cast<const uint4*>(b);
+      } else {
+        const uint2 h = *reinterpret_cast<const uint2*>(b);
+        q[0] = make_uint4(h.x, h.y, 0u, 0u);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NQ; ++j) q[j] = *reinterpret_cast<const uint4*>(static_cast<const float*>(p) + i + 4 * j);
+    }
   }
-}
+  __device__ __forceinline__ float get(int e) const {
+    if constexpr (BF) {
+      const unsigned u = (&q[0].x)[e >> 1];
+      return __uint_as_float((e & 1) ? (u & 0xffff0000u) : (u << 16));
+    } else {
+      return __uint_as_float((&q[e >> 2].x)[e & 3]);
+    }
+  }
+};
+
+// Input types of the refinement's dot products: 0 = float32 tokens and
+// router weight, 1 = bf16 tokens and float32 weight, 2 = both bf16.
+constexpr int kDtF32 = 0, kDtBf16F32 = 1, kDtBf16 = 2;
 
 __device__ __forceinline__ float sigmoid_f32(float s) { return 1.0f / (1.0f + expf(-s)); }
 
@@ -209,10 +234,11 @@ __device__ __forceinline__ void write_selection(const RouteArgs& a, int t, int l
 
 // Refinement of one token on its wavefront, from the float32 state st and its
 // close mask cm: float64 logits for the experts that need them (D-long dot
-// products of the stored inputs, two experts per pass over the token's row,
-// UNROLL iterations of loads in flight), then the candidates ranked and the
-// token's selection written.
-template <int EPL, int UNROLL>
+// products of the stored inputs of types DT, two experts per pass over the
+// token's row, 8 (bf16 tokens) or 4 elements per lane and step, UNROLL steps
+// of loads in flight), then the candidates ranked and the token's selection
+// written.
+template <int EPL, int UNROLL, int DT>
 __device__ __forceinline__ void refine_token(const RouteArgs& a, int t, int lane, const TokenSel<EPL>& st,
                                           unsigned long long cm, float smax, float z) {
   const bool sig = a.scoring == SIGMOID_BIAS;
@@ -273,16 +299,31 @@ __device__ __forceinline__ void refine_token(const RouteArgs& a, int t, int lane
 #pragma unroll
     for (int j = 0; j < 2; ++j) wo[j] = (long long)(ex[j] >= 0 ? ex[j] : ex[0]) * a.D;
     double acc[2] = {0.0, 0.0};
-#pragma unroll UNROLL
-    for (int d = lane * 4; d < a.D; d += kWave * 4) {
-      float xv[4], wv[2][4];
-      load4(a.x, a.act_dtype, xo + d, xv);
+    constexpr int EL = DT == kDtF32 ? 4 : 8;
+    constexpr int STEP = kWave * EL;
+    for (int d0 = 0; d0 < a.D; d0 += STEP * UNROLL) {
+      // UNROLL steps: every load first (lanes past the row's end re-read its
+      // last EL elements and add nothing), then the products
+      RawEl<DT != kDtF32, EL> xr[UNROLL];
+      RawEl<DT == kDtBf16, EL> wr[UNROLL][2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) load4(a.w_router, a.router_dtype, wo[j] + d, wv[j]);
+      for (int u = 0; u < UNROLL; ++u) {
+        const int d = min(d0 + u * STEP + lane * EL, a.D - EL);
+        xr[u].load(a.x, xo + d);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 2; ++j) wr[u][j].load(a.w_router, wo[j] + d);
+      }
+      __builtin_amdgcn_sched_barrier(0);     // keep the batch's loads ahead of every product
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[j] = fma((double)xv[q], (double)wv[j][q], acc[j]);
+      for (int u = 0; u < UNROLL; ++u) {
+        const bool in = d0 + u * STEP + lane * EL < a.D;    // a re-read step adds zeros (finite inputs)
+#pragma unroll
+        for (int q = 0; q < EL; ++q) {
+          const double xq = in ? (double)xr[u].get(q) : 0.0;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) acc[j] = fma(xq, (double)wr[u][j].get(q), acc[j]);
+        }
+      }
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -316,7 +357,7 @@ __device__ __forceinline__ void refine_token(const RouteArgs& a, int t, int lane
 
 // Pass 2: one wavefront per flagged token (the float32 state recomputed), all
 // other waves exit at once.  The loads of the dot products run far ahead.
-template <int EPL>
+template <int EPL, int DT>
 __global__ __launch_bounds__(256) void route_refine_kernel(const RouteArgs a, const int32_t* __restrict__ flags) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -325,7 +366,7 @@ __global__ __launch_bounds__(256) void route_refine_kernel(const RouteArgs a, co
   select_f32(a, t, lane, st);
   float smax = 0.0f, z = 1.0f;
   if (a.scoring == SOFTMAX_TOPK) softmax_stats(st, lane, a.E, smax, z);
-  refine_token<EPL, 8>(a, t, lane, st, close_mask(st, lane), smax, z);
+  refine_token<EPL, 8, DT>(a, t, lane, st, close_mask(st, lane), smax, z);
 }
 
 // Pass 1: float32 selection of every token and its probabilities.  FUSED
@@ -333,7 +374,7 @@ __global__ __launch_bounds__(256) void route_refine_kernel(const RouteArgs a, co
 // the same wavefront, with a lean loop (at most two iterations of loads in
 // flight) that keeps the kernel's register footprint small; otherwise a flag
 // for pass 2.
-template <int EPL, bool FUSED>
+template <int EPL, bool FUSED, int DT>
 __global__ __launch_bounds__(256) void route_select_kernel(const RouteArgs a, int32_t* __restrict__ flags) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -346,7 +387,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(const RouteArgs a, in
   float smax = 0.0f, z = 1.0f;
   if (soft && (a.scoring == SOFTMAX_TOPK || a.probs != nullptr)) softmax_stats(st, lane, E, smax, z);
   if (!FUSED && lane == 0) flags[t] = cm != 0;
-  if (FUSED && cm != 0) refine_token<EPL, 2>(a, t, lane, st, cm, smax, z);   // writes the selection
+  if (FUSED && cm != 0) refine_token<EPL, 2, DT>(a, t, lane, st, cm, smax, z);   // writes the selection
   else write_selection(a, t, lane, st, st.my_e, smax, z);
 
   if (a.probs != nullptr) {
@@ -371,17 +412,25 @@ __global__ __launch_bounds__(256) void route_select_kernel(const RouteArgs a, in
   }
 }
 
-template <int EPL>
-hipError_t launch_epl(const RouteArgs& a, int32_t* flags, hipStream_t s) {
+template <int EPL, int DT>
+hipError_t launch_epl_dt(const RouteArgs& a, int32_t* flags, hipStream_t s) {
   if constexpr (EPL <= 2) {
-    hipLaunchKernelGGL((route_select_kernel<EPL, true>), dim3(ceil_div(a.T, 4)), dim3(256), 0, s, a, flags);
+    hipLaunchKernelGGL((route_select_kernel<EPL, true, DT>), dim3(ceil_div(a.T, 4)), dim3(256), 0, s, a, flags);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((route_select_kernel<EPL, false>), dim3(ceil_div(a.T, 4)), dim3(256), 0, s, a, flags);
+  hipLaunchKernelGGL((route_select_kernel<EPL, false, DT>), dim3(ceil_div(a.T, 4)), dim3(256), 0, s, a, flags);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(route_refine_kernel<EPL>, dim3(ceil_div(a.T, 4)), dim3(256), 0, s, a, (const int32_t*)flags);
+  hipLaunchKernelGGL((route_refine_kernel<EPL, DT>), dim3(ceil_div(a.T, 4)), dim3(256), 0, s, a,
+                     (const int32_t*)flags);
   return hipGetLastError();
+}
+
+template <int EPL>
+hipError_t launch_epl(const RouteArgs& a, int32_t* flags, hipStream_t s) {
+  if (a.act_dtype != BF16) return launch_epl_dt<EPL, kDtF32>(a, flags, s);   // float32 tokens: float32 weight
+  if (a.router_dtype != BF16) return launch_epl_dt<EPL, kDtBf16F32>(a, flags, s);
+  return launch_epl_dt<EPL, kDtBf16>(a, flags, s);
 }
 
 }  // namespace

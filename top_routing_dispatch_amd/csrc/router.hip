@@ -8,6 +8,8 @@
 // expert, so each token row is read once and each token fragment feeds NP
 // MFMAs.  Operands stream through an LDS ring (up to 4 deep) of 64-deep K
 // slices (buffer loads with the LDS bit).
+// At most 16 tokens (rows fitting in LDS): one wave per expert
+// (router_gemv_kernel below).
 // E <= 64, or few tokens: one workgroup owns 16 tokens and up to 64 experts
 // (every expert when E <= 64; blocks of 16 experts side by side in the grid
 // when the tokens are few and the experts many); its eight waves split the
@@ -21,6 +23,7 @@
 #include "common.h"
 
 #include <cstdlib>
+#include <cstring>
 
 namespace moe {
 namespace {
@@ -253,15 +256,127 @@ hipError_t launch_router_small(const bf16_t* x, const bf16_t* w, float* logits, 
   return hipGetLastError();
 }
 
-// Few tokens and many experts: the tiled kernel would run ceil(T / 32)
-// workgroups, each reading every expert's weights; splitting the experts over
-// workgroups of the small-E kernel spreads that weight read over the chip.
-// Measured on MI355X at E = 256, D = 7168: 79 us for one token on the tiled
-// kernel.  MOE_ROUTER_SPLIT=0 / 1 forces the choice (tuning aid).
-bool router_split_experts(int T, int E) {
-  const char* env = getenv("MOE_ROUTER_SPLIT");
-  if (env != nullptr && *env != '\0') return atoi(env) != 0;
-  return E > 64 && T <= 512;
+// A handful of tokens (decode-sized batches): one wave per expert.  The
+// token rows are staged in LDS; the wave streams its expert's weight row (NP
+// planes) into registers with the loads of up to 16 steps of 512 columns in
+// flight at once, and each lane adds the 8 (x NP) products of a step in
+// float32 (every bf16 x bf16 product is exact in float32) before adding that
+// into a float64 accumulator per token; the lanes' sums are then added in a
+// fixed butterfly order.
+constexpr int kGemvMaxTokens = 16;
+constexpr int kGemvLds = 128 * 1024;
+
+__device__ __forceinline__ double wave_sum_f64_r(double v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+__device__ __forceinline__ float dot8_bf16(const uint4 a, const uint4 b, float s) {
+  const unsigned av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s = fmaf(__uint_as_float(av[i] << 16), __uint_as_float(bv[i] << 16), s);
+    s = fmaf(__uint_as_float(av[i] & 0xffff0000u), __uint_as_float(bv[i] & 0xffff0000u), s);
+  }
+  return s;
+}
+
+template <int NP>
+__global__ __launch_bounds__(256) void router_gemv_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ w,
+                                                          float* __restrict__ logits, int T, int E, int D) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];   // x [T][D]
+  constexpr int U = 16 / NP;                                    // steps per batch of loads
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int n16 = T * D / 8;                                    // 16-byte chunks of x
+  // staged 8 chunks per thread at a time, all 8 loads in flight together
+  for (int i0 = threadIdx.x; i0 < n16; i0 += 8 * 256) {
+    uint4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (i0 + 256 * u < n16) v[u] = reinterpret_cast<const uint4*>(x)[i0 + 256 * u];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (i0 + 256 * u < n16) reinterpret_cast<uint4*>(smem)[i0 + 256 * u] = v[u];
+  }
+  __syncthreads();
+  const int e = blockIdx.x * 4 + wave;
+  if (e >= E) return;
+  const bf16_t* wr = w + (long long)e * NP * D;
+  double acc[kGemvMaxTokens];
+#pragma unroll
+  for (int t = 0; t < kGemvMaxTokens; ++t) acc[t] = 0.0;
+  for (int k0 = 0; k0 < D; k0 += 512 * U) {
+    uint4 wv[U][NP];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = k0 + u * 512 + lane * 8;
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+        wv[u][p] = k < D ? *reinterpret_cast<const uint4*>(wr + (long long)p * D + k) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = k0 + u * 512 + lane * 8;
+      if (k < D) {
+#pragma unroll
+        for (int t = 0; t < kGemvMaxTokens; ++t) {
+          if (t < T) {
+            const uint4 xv = *reinterpret_cast<const uint4*>(smem + ((size_t)t * D + k) * 2);
+            float s = 0.0f;
+#pragma unroll
+            for (int p = 0; p < NP; ++p) s = dot8_bf16(xv, wv[u][p], s);
+            acc[t] += (double)s;
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kGemvMaxTokens; ++t) {
+    if (t < T) {
+      const double v = wave_sum_f64_r(acc[t]);
+      if (lane == 0) logits[(long long)t * E + e] = (float)v;
+    }
+  }
+}
+
+template <int NP>
+hipError_t launch_router_gemv(const bf16_t* x, const bf16_t* w, float* logits, int T, int E, int D, hipStream_t s) {
+  const int lds = T * D * 2;
+  static bool allowed[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64 || !allowed[dev]) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&router_gemv_kernel<NP>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kGemvLds);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < 64) allowed[dev] = true;
+  }
+  hipLaunchKernelGGL((router_gemv_kernel<NP>), dim3(ceil_div(E, 4)), dim3(256), lds, s, x, w, logits, T, E, D);
+  static_assert(kGemvLds <= 160 * 1024, "LDS");
+  return hipGetLastError();
+}
+
+// Which router kernel: 2 = one wave per expert (a handful of tokens whose
+// rows fit in LDS); 1 = the small-E kernel, with the experts split over
+// workgroups when E > 64 (few tokens: the tiled kernel would run ceil(T / 32)
+// workgroups, each reading every expert's weights; measured on MI355X at
+// E = 256, D = 7168: 79 us for one token on the tiled kernel); 0 = the tiled
+// kernel.  MOE_ROUTER_PATH=gemv / split / tiled forces a kernel where it
+// applies (tuning aid and test hook).
+int router_path(int T, int E, int D) {
+  const bool gemv = T <= kGemvMaxTokens && (long long)T * D * 2 <= kGemvLds;
+  const char* env = getenv("MOE_ROUTER_PATH");
+  if (env != nullptr && *env != '\0') {
+    if (strcmp(env, "gemv") == 0 && gemv) return 2;
+    if (strcmp(env, "split") == 0) return 1;
+    if (strcmp(env, "tiled") == 0) return E <= 64 ? 1 : 0;
+  }
+  if (gemv) return 2;
+  return (E <= 64 || T <= 512) ? 1 : 0;
 }
 
 }  // namespace
@@ -273,6 +388,11 @@ bool router_kernel_fits(int T, int E, int D, int planes) {
 hipError_t launch_router_logits(const bf16_t* x, const bf16_t* w, int planes, float* logits, int T, int E, int D,
                                 hipStream_t s) {
   if (!router_kernel_fits(T, E, D, planes)) return hipErrorInvalidValue;
+  const int path = router_path(T, E, D);
+  if (path == 2) {
+    if (planes == 3) return launch_router_gemv<3>(x, w, logits, T, E, D, s);
+    return launch_router_gemv<1>(x, w, logits, T, E, D, s);
+  }
   if (E <= 64) {
     if (planes == 3) {
       if (E <= 16) return launch_router_small<1, 3>(x, w, logits, T, E, D, s);
@@ -283,7 +403,7 @@ hipError_t launch_router_logits(const bf16_t* x, const bf16_t* w, int planes, fl
     if (E <= 32) return launch_router_small<2, 1>(x, w, logits, T, E, D, s);
     return launch_router_small<4, 1>(x, w, logits, T, E, D, s);
   }
-  if (router_split_experts(T, E)) {
+  if (path == 1) {
     if (planes == 3) return launch_router_small<1, 3>(x, w, logits, T, E, D, s);
     return launch_router_small<1, 1>(x, w, logits, T, E, D, s);
   }
