@@ -273,15 +273,19 @@ struct FfnPlan {
   int ks_up, ks_dn, ks_sh_up, ks_sh_dn;
 };
 
-// Contraction split of a weight-streaming launch whose tiles are too few to
-// give every CU a weight stream of its own (decode-sized batches: a few rows
-// per expert, and the down projection has only D / 128 column tiles per
-// expert): the largest power of two KS <= 8 with tiles * KS <= 256 (one unit
-// per CU), K / 64 divisible by KS and at least 4 slices of 64 per part.  The
-// tile count is bounded on the host from the row and group counts (the
-// routing is known on the device only).  MOE_GEMM_KSPLIT=<n> forces n where
-// it divides the contraction (tuning aid and test hook).
+// Contraction split of a weight-streaming launch whose tiles do not spread
+// evenly over the CUs (decode-sized batches: a few rows per expert, and the
+// down projection has only D / 128 column tiles per expert): units of K / KS
+// for KS in {1, 2, 4, 8}, with K / 64 divisible by KS and at least 4 slices
+// of 64 per unit; a launch of U units takes about ceil(U / 256) / KS tile
+// times on 256 CUs (the persistent grid deals units round-robin), and the
+// smallest KS within 10% of the best estimate is taken (the partial sums
+// cost an extra pass; at most 256 MB of them).  The tile count is bounded on
+// the host from the row and group counts (the routing is known on the device
+// only).  MOE_GEMM_KSPLIT=<n> forces n where it divides the contraction
+// (tuning aid and test hook).
 constexpr int kSplitUnits = 256;
+constexpr long long kMaxPartialBytes = 256LL << 20;
 int pick_ksplit(int act, int cfg, int epi, int N, int K, int G, int max_rows, bool grouped) {
   if (act != BF16 || cfg < kGemmV2Configs + kGemmV3Configs || K % 64 != 0 || max_rows <= 0) return 1;
   const int nk = K / 64;
@@ -295,9 +299,17 @@ int pick_ksplit(int act, int cfg, int epi, int N, int K, int G, int max_rows, bo
   const int bm = gemm_ws_bm(c);
   const long long m_tiles = grouped ? max_rows / bm + (G < max_rows ? G : max_rows) : ceil_div(max_rows, bm);
   const long long tiles = m_tiles * ceil_div(N, cols);
-  int ks = 1;
-  while (ks < 8 && tiles * ks * 2 <= kSplitUnits && nk % (ks * 2) == 0 && nk / (ks * 2) >= 4) ks *= 2;
-  return ks;
+  const long long row_bytes = (long long)(epi == EPI_SWIGLU ? 2 : 1) * N * 4;
+  double est[4];
+  double best = 1e300;
+  for (int i = 0, ks = 1; i < 4; ++i, ks *= 2) {
+    const bool ok = ks == 1 || (nk % ks == 0 && nk / ks >= 4 && ks * max_rows * row_bytes <= kMaxPartialBytes);
+    est[i] = ok ? (double)((tiles * ks + kSplitUnits - 1) / kSplitUnits) / ks : 1e300;
+    best = est[i] < best ? est[i] : best;
+  }
+  for (int i = 0, ks = 1; i < 4; ++i, ks *= 2)
+    if (est[i] <= 1.1 * best) return ks;
+  return 1;
 }
 
 // Shallow groups are split off when both contractions are long (the

@@ -290,15 +290,15 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const bf16_t* __restri
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int n16 = T * D / 8;                                    // 16-byte chunks of x
-  // staged 8 chunks per thread at a time, all 8 loads in flight together
+  // staged 8 chunks per thread at a time, with no branch between the 8 loads
+  // so that they are in flight together: indexes past the end are clamped to
+  // the last chunk (which is then written again with its own value)
   for (int i0 = threadIdx.x; i0 < n16; i0 += 8 * 256) {
     uint4 v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (i0 + 256 * u < n16) v[u] = reinterpret_cast<const uint4*>(x)[i0 + 256 * u];
+    for (int u = 0; u < 8; ++u) v[u] = reinterpret_cast<const uint4*>(x)[min(i0 + 256 * u, n16 - 1)];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (i0 + 256 * u < n16) reinterpret_cast<uint4*>(smem)[i0 + 256 * u] = v[u];
+    for (int u = 0; u < 8; ++u) reinterpret_cast<uint4*>(smem)[min(i0 + 256 * u, n16 - 1)] = v[u];
   }
   __syncthreads();
   const int e = blockIdx.x * 4 + wave;
@@ -308,27 +308,31 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const bf16_t* __restri
 #pragma unroll
   for (int t = 0; t < kGemvMaxTokens; ++t) acc[t] = 0.0;
   for (int k0 = 0; k0 < D; k0 += 512 * U) {
+    // the batch's weight loads, all in flight together (columns past the row
+    // end re-read its last 8 and add nothing)
     uint4 wv[U][NP];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int k = k0 + u * 512 + lane * 8;
+      const int k = min(k0 + u * 512 + lane * 8, D - 8);
 #pragma unroll
-      for (int p = 0; p < NP; ++p)
-        wv[u][p] = k < D ? *reinterpret_cast<const uint4*>(wr + (long long)p * D + k) : make_uint4(0, 0, 0, 0);
+      for (int p = 0; p < NP; ++p) wv[u][p] = *reinterpret_cast<const uint4*>(wr + (long long)p * D + k);
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int k = k0 + u * 512 + lane * 8;
-      if (k < D) {
+    for (int t = 0; t < kGemvMaxTokens; ++t) {
+      if (t < T) {                                              // uniform
+        uint4 xv[U];
 #pragma unroll
-        for (int t = 0; t < kGemvMaxTokens; ++t) {
-          if (t < T) {
-            const uint4 xv = *reinterpret_cast<const uint4*>(smem + ((size_t)t * D + k) * 2);
-            float s = 0.0f;
+        for (int u = 0; u < U; ++u) {
+          const int k = min(k0 + u * 512 + lane * 8, D - 8);
+          xv[u] = *reinterpret_cast<const uint4*>(smem + ((size_t)t * D + k) * 2);
+        }
 #pragma unroll
-            for (int p = 0; p < NP; ++p) s = dot8_bf16(xv, wv[u][p], s);
-            acc[t] += (double)s;
-          }
+        for (int u = 0; u < U; ++u) {
+          float s = 0.0f;
+#pragma unroll
+          for (int p = 0; p < NP; ++p) s = dot8_bf16(xv[u], wv[u][p], s);
+          acc[t] += (k0 + u * 512 + lane * 8 < D) ? (double)s : 0.0;
         }
       }
     }
@@ -368,10 +372,13 @@ hipError_t launch_router_gemv(const bf16_t* x, const bf16_t* w, float* logits, i
 // kernel.  MOE_ROUTER_PATH=gemv / split / tiled forces a kernel where it
 // applies (tuning aid and test hook).
 int router_path(int T, int E, int D) {
-  const bool gemv = T <= kGemvMaxTokens && (long long)T * D * 2 <= kGemvLds;
+  // with few experts the one-wave-per-expert kernel has few waves: measured
+  // on MI355X at E = 8, D = 4096: 8.6 us for one token (small-E kernel 13),
+  // 17 us for eight (small-E kernel 14)
+  const bool gemv = T <= (E > 64 ? kGemvMaxTokens : 2) && (long long)T * D * 2 <= kGemvLds;
   const char* env = getenv("MOE_ROUTER_PATH");
   if (env != nullptr && *env != '\0') {
-    if (strcmp(env, "gemv") == 0 && gemv) return 2;
+    if (strcmp(env, "gemv") == 0 && T <= kGemvMaxTokens && (long long)T * D * 2 <= kGemvLds) return 2;
     if (strcmp(env, "split") == 0) return 1;
     if (strcmp(env, "tiled") == 0) return E <= 64 ? 1 : 0;
   }
