@@ -25,6 +25,9 @@ step; the steps and their sources:
   combine      index_add of weighted outputs        Tiny-MoE §6; "Top-k 路由" Step 3
   statistics   importance, load, alpha*E*sum f*P    "Top-k 路由" 負載均衡 section; Tiny-MoE §8;
                                                     "别只比较 Top-k" [9,4,2,1] assignment example
+  EP layouts   rows per destination rank, received "Top-k 路由" 通訊拓撲：All-to-All figure;
+               rows in expert-major order           "别只比较 Top-k" 按目标专家发送 / two-All-to-All
+                                                    dispatcher section
 
 Readings taken where the pages are silent (each is also listed with its reason
 in the design notes):
@@ -320,6 +323,60 @@ def num_parameters_swiglu(d_model: int, d_ff: int) -> int:
     """Parameters of one bias-free SwiGLU expert: gate [F,D] + up [F,D] + down [D,F]."""
     shapes = [(d_ff, d_model), (d_ff, d_model), (d_model, d_ff)]
     return sum(a * b for a, b in shapes)
+
+
+# --------------------------------------------------------------------------
+# Expert parallelism: the layouts around the two all-to-all exchanges
+# --------------------------------------------------------------------------
+def ep_send_layout(kept: np.ndarray, num_ranks: int) -> Dict[str, np.ndarray]:
+    """Rows each rank sends in the dispatch all-to-all ("Top-k 路由" page,
+    通訊拓撲：All-to-All figure: experts 0-3 on one device, 4-7 on the other;
+    "别只比较 Top-k" page, 按目标专家发送: an assignment goes to the rank that
+    owns its expert).  Experts sit on ranks in contiguous blocks of E / R, so
+    rank r receives the kept rows of experts r*E/R .. (r+1)*E/R - 1; with the
+    rows laid out expert after expert those are one contiguous run.
+    Returns send_counts [R] and send_offsets [R+1] (exclusive prefix)."""
+    E = len(kept)
+    assert E % num_ranks == 0
+    per = E // num_ranks
+    counts = np.zeros(num_ranks, dtype=np.int64)
+    for e in range(E):
+        counts[e // per] += int(kept[e])
+    offsets = np.zeros(num_ranks + 1, dtype=np.int64)
+    for r in range(num_ranks):
+        offsets[r + 1] = offsets[r] + counts[r]
+    return dict(send_counts=counts, send_offsets=offsets)
+
+
+def ep_recv_layout(recv_counts: np.ndarray) -> Dict[str, np.ndarray]:
+    """Where the local experts' rows sit after the dispatch all-to-all, and the
+    expert-major view the local grouped FFN reads.  recv_counts[r][e] = rows
+    that source rank r sends for local expert e.  The received buffer holds
+    the sources one after another, each source's rows expert after expert
+    (the order of its own expert-major rows).  The local FFN takes the rows
+    of local expert 0 first (from source 0, then source 1, ...), then those
+    of expert 1, and so on.  Returns local_offsets [E_local+1] and gather
+    [rows]: gather[j] = position in the received buffer of expert-major row j."""
+    recv_counts = np.asarray(recv_counts, dtype=np.int64)
+    R, El = recv_counts.shape
+    # received position of the first row of each (source, expert) run
+    src_start = np.zeros((R, El), dtype=np.int64)
+    pos = 0
+    for r in range(R):
+        for e in range(El):
+            src_start[r, e] = pos
+            pos += recv_counts[r, e]
+    local_offsets = np.zeros(El + 1, dtype=np.int64)
+    gather = np.zeros(pos, dtype=np.int64)
+    j = 0
+    for e in range(El):
+        local_offsets[e] = j
+        for r in range(R):
+            for i in range(int(recv_counts[r, e])):
+                gather[j] = src_start[r, e] + i
+                j += 1
+    local_offsets[El] = j
+    return dict(local_offsets=local_offsets, gather=gather)
 
 
 # --------------------------------------------------------------------------
