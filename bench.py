@@ -172,8 +172,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="switch", choices=sorted(W.CONFIGS) + sorted(W.DECODE_CONFIGS),
-                    help="workload; <model>_decode_t<T>: the first T tokens on that model's full-size weights")
+    ap.add_argument("--config", default="switch",
+                    choices=sorted(W.CONFIGS) + sorted(W.DECODE_CONFIGS) + sorted(W.EP_CONFIGS),
+                    help="workload; <model>_decode_t<T>: the first T tokens on that model's full-size weights; "
+                         "<model>_ep8_local: one GPU's share of an 8-rank expert-parallel layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=None)
     ap.add_argument("--copy-calibration", type=int, default=None, metavar="MIB",
@@ -186,6 +188,10 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, args.steps)
+        return
+
+    if args.config in W.EP_CONFIGS:
+        run_ep_share(args, W.EP_CONFIGS[args.config])
         return
 
     import torch
@@ -312,6 +318,93 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "stages": stage_info,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def run_ep_share(args, ep):
+    """One GPU's share of an expert-parallel layer: a step is the receive
+    layout of the rows the dispatch all-to-all delivered plus the local grouped
+    expert FFN reading them in place (the exchanges are not part of one GPU).
+    Throughput is received rows per second."""
+    import torch
+    import top_routing_dispatch_amd as M
+    from workloads.torch_io import to_torch
+
+    cfg = W.CONFIGS[ep.base]
+    El, D, F = ep.local_experts, cfg.d_model, cfg.d_ff
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    rc_host = W.ep_recv_counts(ep)
+    total = int(rc_host.sum())
+    xr_host = W.make_received_rows(ep, total)
+    xr = to_torch(xr_host, dev)
+    rc = to_torch(rc_host, dev)
+    first = ep.rank * El
+    w13 = torch.empty((El, cfg.n_mat * F, D), dtype=torch.bfloat16, device=dev)
+    w2 = torch.empty((El, D, F), dtype=torch.bfloat16, device=dev)
+    host = {}
+    for e, a, b in W.iter_experts(cfg, experts=range(first, first + El), workers=16):
+        w13[e - first].copy_(to_torch(a, "cpu"))
+        w2[e - first].copy_(to_torch(b, "cpu"))
+        host[e - first] = (a, b)
+    lcfg = cfg.replace(num_experts=El, num_tokens=total, top_k=1, num_shared=0, d_ff_shared=0)
+    lo = torch.empty(El + 1, dtype=torch.int32, device=dev)
+    g = torch.empty(total, dtype=torch.int32, device=dev)
+    y = torch.empty((total, D), dtype=torch.bfloat16, device=dev)
+    ws = M.workspace(lcfg, M.MOE_OP_EXPERT_FFN, dev)
+
+    def step():
+        M.moe_ep_recv_layout(rc, total, lo, g)
+        M.moe_expert_ffn(lcfg, El, F, cfg.activation, total, xr, g, lo, w13, w2, y, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record()
+        step()
+        b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    ev_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    flops = 2.0 * total * D * F * (cfg.n_mat + 1)
+    roof = dict(bound="mfma", achieved=round(flops / (ev_ms * 1e-3) / 1e12, 2), peak=MFMA_BF16_TFLOPS,
+                unit="TFLOP/s", frac=round(flops / (ev_ms * 1e-3) / 1e12 / MFMA_BF16_TFLOPS, 4),
+                kernel="local expert FFN (gate/up + down)", ms=round(ev_ms, 4), traffic=None)
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import moe_oracle as O
+        lay = O.ep_recv_layout(rc_host)
+        n = args.cpu_sample_tokens or 128
+        rows = lay["gather"][:n]                       # the first rows of local expert 0
+        passes, t1 = 0, time.perf_counter()
+        while True:
+            O.expert_apply(O.widen(xr_host[rows]), host[0][0], host[0][1], cfg.activation, F)
+            passes += 1
+            if time.perf_counter() - t1 >= CPU_MIN_SECONDS:
+                break
+        dt = time.perf_counter() - t1
+        try:
+            import threadpoolctl
+            info = threadpoolctl.threadpool_info()
+            cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+        except Exception:
+            cores = 1
+        cpu = dict(value=round(n * passes / dt, 2), unit="rows/s", cores=int(cores), kind="oracle",
+                   sample=f"{n} received rows of local expert 0; {passes} pass(es) in {dt:.1f} s")
+    line = {
+        "metric": "MoE-layer tokens/sec at 1 GPU; % HBM roofline (route/permute) and % MFMA peak",
+        "value": round(total / (ms_per_step * 1e-3), 1), "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": ep.name, "base": ep.base, "ranks": ep.ranks, "rank": ep.rank, "local_experts": El,
+                   "received_rows": total, "d_model": D, "d_ff": F},
+        "roofline": roof,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 

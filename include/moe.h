@@ -263,6 +263,38 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const moe_weights* wei
                                    void* ws, size_t ws_bytes, void* stream,
                                    void* const* stage_events);
 
+/* Expert parallelism, the part one GPU holds ("Top-k 路由" page, 通訊拓撲：
+ * All-to-All figure; "别只比较 Top-k" page, two-All-to-All dispatcher and
+ * 按目标专家发送 sections).  Experts sit on ranks in contiguous blocks of
+ * E / R; the exchanges themselves (all-to-all over the interconnect) are the
+ * caller's.
+ *
+ * Send layout: with the rows of moe_permute (expert-major), the rows bound for
+ * rank r are the contiguous run send_offsets[r] .. send_offsets[r+1]:
+ *   offsets      [E+1] int32 device in (moe_permute's)
+ *   send_counts  [R] int32 device out: kept rows of rank r's experts
+ *   send_offsets [R+1] int32 device out: exclusive prefix of send_counts
+ * num_experts % num_ranks == 0, 1 <= num_ranks <= num_experts. */
+moe_status moe_ep_send_layout(int32_t num_experts, int32_t num_ranks, const int32_t* offsets,
+                              int32_t* send_counts, int32_t* send_offsets, void* stream);
+
+/* Receive layout: the exchange delivers the sources one after another, each
+ * source's rows expert after expert.  The local grouped FFN reads them expert
+ * after expert (sources in rank order inside an expert) through a gather map,
+ * with no copy: moe_expert_ffn(num_groups = local_experts, x_in = received
+ * rows, gather_rows = gather, offsets = local_offsets).
+ *   recv_counts   [R, E_local] int32 device in: rows source r sends for local
+ *                 expert e (what the count exchange delivers)
+ *   rows_cap      capacity of gather (>= the received total, which the
+ *                 caller knows after the count exchange; rows past rows_cap
+ *                 are not described and local_offsets are clamped to it)
+ *   local_offsets [E_local+1] int32 device out
+ *   gather        [rows_cap] int32 device out: received position of
+ *                 expert-major row j; -1 past the received total
+ * Bit-exact and deterministic. */
+moe_status moe_ep_recv_layout(int32_t num_ranks, int32_t local_experts, const int32_t* recv_counts,
+                              int32_t rows_cap, int32_t* local_offsets, int32_t* gather, void* stream);
+
 /* Static text of a status code; the last HIP error text of this thread. */
 const char* moe_status_string(moe_status status);
 const char* moe_last_error(void);

@@ -118,6 +118,23 @@ def test_null_and_misaligned_pointers_rejected_before_launch():
     assert _raw("moe_combine", None, p, p, p, None, p, None) == M.MOE_ERR_INVALID_ARGUMENT
 
 
+def test_ep_layout_arguments_rejected_before_launch():
+    p = ctypes.c_void_p(0x100000)           # never dereferenced: validation fails first
+    bad = M.MOE_ERR_INVALID_ARGUMENT
+    # experts not divisible by ranks, zero ranks, more ranks than experts, null outputs
+    assert _raw("moe_ep_send_layout", 10, 4, p, p, p, None) == bad
+    assert _raw("moe_ep_send_layout", 8, 0, p, p, p, None) == bad
+    assert _raw("moe_ep_send_layout", 4, 8, p, p, p, None) == bad
+    assert _raw("moe_ep_send_layout", 8, 2, p, None, p, None) == bad
+    assert _raw("moe_ep_send_layout", 2048, 2, p, p, p, None) == M.MOE_ERR_UNSUPPORTED
+    # receive layout: zero ranks / experts, negative capacity, missing gather
+    assert _raw("moe_ep_recv_layout", 0, 4, p, 16, p, p, None) == bad
+    assert _raw("moe_ep_recv_layout", 2, 0, p, 16, p, p, None) == bad
+    assert _raw("moe_ep_recv_layout", 2, 4, p, -1, p, p, None) == bad
+    assert _raw("moe_ep_recv_layout", 2, 4, p, 16, p, None, None) == bad
+    assert _raw("moe_ep_recv_layout", 2, 4, None, 16, p, p, None) == bad
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(B, "_lib", None)

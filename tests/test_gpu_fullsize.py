@@ -145,3 +145,47 @@ def _check_full_weights(cfg, n_sample):
     err = row_rel_err(to_numpy(y)[sample], y_ref)
     print(f"  sampled {len(sample)} tokens over {len(users)} experts: max rel err {err:.3e}")
     assert err <= out_tol(cfg)
+
+
+@pytest.mark.parametrize("name", sorted(W.EP_CONFIGS))
+def test_ep_local_share_full_size(name):
+    """One GPU's share of the DeepSeek-V3-shaped layer on 8 ranks, as bench.py
+    times it: the receive layout of 65,536 rows for 32 local experts
+    (bit-exact against the oracle) and the local grouped FFN over the received
+    rows in place, sampled rows against the oracle."""
+    ep = W.EP_CONFIGS[name]
+    cfg = W.CONFIGS[ep.base]
+    El, D, F = ep.local_experts, cfg.d_model, cfg.d_ff
+    print(f"[ep local share] {name}", flush=True)
+    rc = W.ep_recv_counts(ep)
+    total = int(rc.sum())
+    xr = W.make_received_rows(ep, total)
+    experts = {}
+    w13 = torch.empty((El, 2 * F, D), dtype=torch.bfloat16, device="cuda")
+    w2 = torch.empty((El, D, F), dtype=torch.bfloat16, device="cuda")
+    for e, a, b in W.iter_experts(cfg, experts=range(ep.rank * El, (ep.rank + 1) * El), workers=16):
+        w13[e - ep.rank * El].copy_(to_torch(a, "cpu"))
+        w2[e - ep.rank * El].copy_(to_torch(b, "cpu"))
+        experts[e - ep.rank * El] = (a, b)
+    lo = torch.empty(El + 1, dtype=torch.int32, device="cuda")
+    g = torch.empty(total, dtype=torch.int32, device="cuda")
+    M.moe_ep_recv_layout(to_torch(rc, "cuda"), total, lo, g)
+    y = torch.empty((total, D), dtype=torch.bfloat16, device="cuda")
+    lcfg = cfg.replace(num_experts=El, num_tokens=total, top_k=1, num_shared=0, d_ff_shared=0)
+    ws = M.workspace(lcfg, M.MOE_OP_EXPERT_FFN, "cuda")
+    M.moe_expert_ffn(lcfg, El, F, cfg.activation, total, to_torch(xr, "cuda"), g, lo, w13, w2, y, ws)
+    torch.cuda.synchronize()
+    lay = O.ep_recv_layout(rc)
+    np.testing.assert_array_equal(to_numpy(lo), lay["local_offsets"])
+    np.testing.assert_array_equal(to_numpy(g), lay["gather"])
+    rng = np.random.default_rng(4321)
+    sample = np.sort(rng.choice(total, size=16, replace=False))
+    got = to_numpy(y)[sample]
+    ref = np.zeros((len(sample), D))
+    for i, j in enumerate(sample):
+        e = int(np.searchsorted(lay["local_offsets"], j, side="right") - 1)
+        X = O.widen(xr[lay["gather"][j:j + 1]])
+        ref[i] = O.expert_apply(X, experts[e][0], experts[e][1], cfg.activation, F)[0]
+    err = row_rel_err(got, ref)
+    print(f"  sampled {len(sample)} rows: max rel err {err:.3e}")
+    assert err <= out_tol(cfg)

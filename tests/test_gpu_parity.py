@@ -591,3 +591,99 @@ def test_layer_forward_graph_replay(cfg):
             np.testing.assert_array_equal(a, r)
         call()                              # eager work between the replays
         torch.cuda.synchronize()
+
+
+# --------------------------------------------------------------------------
+# expert-parallel layouts and the local expert FFN over received rows
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("R,E,T,k", [(2, 8, 300, 2), (4, 64, 777, 6), (8, 256, 513, 8), (1, 16, 50, 3)])
+def test_ep_send_layout(R, E, T, k):
+    """Per-rank send counts and offsets of the GPU permutation against the
+    oracle's (sums of kept rows over each rank's experts), bit-exact."""
+    print(f"[ep send] R={R} E={E} T={T} k={k}", flush=True)
+    cfg = W.MoEConfig("ep_send", T, 64, E, k, 64, scoring=W.SIGMOID_BIAS, zipf_s=1.2)
+    inp = W.make_inputs(cfg, with_experts=False)
+    ref = O.route(inp.x, inp.w_router, inp.sel_bias, k, cfg.scoring, cfg.renormalize)
+    idx = to_torch(ref["idx"].astype(np.int32), "cuda")
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    row_of = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    tor = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    M.moe_permute(cfg, idx, None, counts, off, row_of, tor, None, M.workspace(cfg, M.MOE_OP_PERMUTE, "cuda"))
+    sc = torch.empty(R, dtype=torch.int32, device="cuda")
+    so = torch.empty(R + 1, dtype=torch.int32, device="cuda")
+    M.moe_ep_send_layout(E, R, off, sc, so)
+    torch.cuda.synchronize()
+    want = O.ep_send_layout(O.dispatch(ref["idx"], E, None)["kept"], R)
+    np.testing.assert_array_equal(to_numpy(sc), want["send_counts"])
+    np.testing.assert_array_equal(to_numpy(so), want["send_offsets"])
+
+
+def _recv_counts(R, El, seed, empty_frac=0.2, hi=40):
+    rng = np.random.default_rng(seed)
+    rc = rng.integers(0, hi, size=(R, El)).astype(np.int32)
+    rc[rng.random((R, El)) < empty_frac] = 0
+    return rc
+
+
+@pytest.mark.parametrize("R,El,seed,extra", [(8, 32, 1, 0), (3, 5, 2, 17), (1, 1, 3, 0), (16, 64, 4, 5),
+                                             (4, 4, 5, -1)])
+def test_ep_recv_layout(R, El, seed, extra):
+    """Local offsets and the gather map against the oracle, bit-exact; entries
+    past the received total are -1 (extra > 0: spare capacity), and a
+    capacity one short of the total (extra = -1) clamps the offsets and
+    leaves the last row undescribed."""
+    print(f"[ep recv] R={R} El={El} seed={seed} extra={extra}", flush=True)
+    rc = _recv_counts(R, El, seed)
+    if rc.sum() == 0:
+        rc[0, 0] = 3
+    want = O.ep_recv_layout(rc)
+    total = int(rc.sum())
+    cap = total + extra
+    lo = torch.empty(El + 1, dtype=torch.int32, device="cuda")
+    g = torch.full((max(cap, 1),), -7, dtype=torch.int32, device="cuda")
+    M.moe_ep_recv_layout(to_torch(rc, "cuda"), cap, lo, g)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_numpy(lo), np.minimum(want["local_offsets"], cap))
+    got = to_numpy(g)[:cap]
+    n = min(cap, total)
+    np.testing.assert_array_equal(got[:n], want["gather"][:n])
+    assert (got[n:] == -1).all()
+
+
+@pytest.mark.parametrize("activation", [W.SWIGLU, W.GELU])
+def test_ep_local_ffn_over_received_rows(activation):
+    """The local grouped FFN reading the received rows in place through the
+    gather map (ragged counts, empty pairs) against the oracle, expert by
+    expert on the oracle's expert-major rows."""
+    print(f"[ep local ffn] activation={activation}", flush=True)
+    R, El, D, F = 4, 6, 256, 320
+    cfg = W.MoEConfig("ep_local", 64, D, El, 2, F, activation=activation)
+    rc = _recv_counts(R, El, 11, hi=90)
+    total = int(rc.sum())
+    rng = np.random.default_rng(12)
+    xr = W.f32_to_bf16_bits(rng.standard_normal((total, D), dtype=np.float32))
+    experts = [W.make_expert(cfg, e) for e in range(El)]
+    w13 = to_torch(np.stack([a for a, _ in experts]), "cuda")
+    w2 = to_torch(np.stack([b for _, b in experts]), "cuda")
+    lo = torch.empty(El + 1, dtype=torch.int32, device="cuda")
+    g = torch.empty(total, dtype=torch.int32, device="cuda")
+    M.moe_ep_recv_layout(to_torch(rc, "cuda"), total, lo, g)
+    y = torch.empty((total, D), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(M.moe_workspace_size(cfg.replace(num_tokens=total, top_k=1), M.MOE_OP_EXPERT_FFN) + 256,
+                     dtype=torch.uint8, device="cuda")
+    M.moe_expert_ffn(cfg, El, F, activation, total, to_torch(xr, "cuda"), g, lo, w13, w2, y, ws)
+    torch.cuda.synchronize()
+    lay = O.ep_recv_layout(rc)
+    got = to_numpy(y)
+    errs = []
+    for e in range(El):
+        a, b = lay["local_offsets"][e], lay["local_offsets"][e + 1]
+        if a == b:
+            continue
+        X = O.widen(xr[lay["gather"][a:b]])
+        ref = O.expert_apply(X, experts[e][0], experts[e][1], activation, F)
+        errs.append(row_rel_err(got[a:b], ref))
+    err = max(errs)
+    print(f"  max rel err {err:.3e}")
+    assert err <= BF16_TOL

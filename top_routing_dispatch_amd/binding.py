@@ -25,7 +25,7 @@ MOE_SWIGLU, MOE_GELU = 0, 1
 
 EXPORTED = ("moe_capacity", "moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn",
             "moe_combine", "moe_load_stats", "moe_layer_forward", "moe_layer_forward_timed",
-            "moe_status_string", "moe_last_error")
+            "moe_ep_send_layout", "moe_ep_recv_layout", "moe_status_string", "moe_last_error")
 STAGES = ("router_logits", "route_select", "permute", "expert_gate_up", "expert_down", "shared_gate_up",
           "shared_down", "combine", "load_stats")
 
@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
             "moe_layer_forward": [cfgp, ctypes.POINTER(moe_weights), vp, vp, vp, vp, vp, f32, vp, vp, vp, sz, vp],
             "moe_layer_forward_timed": [cfgp, ctypes.POINTER(moe_weights), vp, vp, vp, vp, vp, f32, vp, vp, vp, sz,
                                         vp, ctypes.POINTER(vp)],
+            "moe_ep_send_layout": [i32, i32, vp, vp, vp, vp],
+            "moe_ep_recv_layout": [i32, i32, vp, i32, vp, vp, vp],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -197,3 +199,15 @@ def moe_layer_forward_timed(cfg, weights: dict, x, y, topk_idx=None, topk_w=None
         ctypes.byref(c), ctypes.byref(w), _ptr(x), _ptr(y), _ptr(topk_idx), _ptr(topk_w), _ptr(counts),
         float(alpha), _ptr(stats), _ptr(dropped), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream),
         arr))
+
+
+def moe_ep_send_layout(num_experts, num_ranks, offsets, send_counts, send_offsets, stream=None):
+    _check("moe_ep_send_layout", lib().moe_ep_send_layout(num_experts, num_ranks, _ptr(offsets), _ptr(send_counts),
+                                                          _ptr(send_offsets), _stream(stream)))
+
+
+def moe_ep_recv_layout(recv_counts, rows_cap, local_offsets, gather, stream=None):
+    """recv_counts: [R, E_local] int32 device tensor."""
+    R, El = recv_counts.shape
+    _check("moe_ep_recv_layout", lib().moe_ep_recv_layout(R, El, _ptr(recv_counts), rows_cap, _ptr(local_offsets),
+                                                          _ptr(gather), _stream(stream)))

@@ -836,4 +836,26 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const moe_weights* wt,
   return MOE_OK;
 }
 
+moe_status moe_ep_send_layout(int32_t num_experts, int32_t num_ranks, const int32_t* offsets,
+                              int32_t* send_counts, int32_t* send_offsets, void* stream) {
+  if (num_experts <= 0 || num_ranks <= 0 || num_ranks > num_experts || num_experts % num_ranks != 0)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (num_experts > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if (offsets == nullptr || send_counts == nullptr || send_offsets == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+  MOE_TRY_HIP("ep send layout", launch_ep_send_layout(offsets, num_experts, num_ranks, send_counts, send_offsets,
+                                                      static_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
+moe_status moe_ep_recv_layout(int32_t num_ranks, int32_t local_experts, const int32_t* recv_counts,
+                              int32_t rows_cap, int32_t* local_offsets, int32_t* gather, void* stream) {
+  if (num_ranks <= 0 || local_experts <= 0 || rows_cap < 0) return MOE_ERR_INVALID_ARGUMENT;
+  if ((long long)num_ranks * local_experts > 65536 || local_experts > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if (recv_counts == nullptr || local_offsets == nullptr || (rows_cap > 0 && gather == nullptr))
+    return MOE_ERR_INVALID_ARGUMENT;
+  MOE_TRY_HIP("ep receive layout", launch_ep_recv_layout(recv_counts, num_ranks, local_experts, rows_cap,
+                                                         local_offsets, gather, static_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
 }  // extern "C"

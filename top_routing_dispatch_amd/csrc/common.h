@@ -315,6 +315,11 @@ struct PermuteArgs {
 };
 constexpr int kPermuteTile = 256;   // tokens per histogram / scatter block
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
+// Expert-parallel send / receive layouts (ep.hip).
+hipError_t launch_ep_send_layout(const int32_t* offsets, int E, int R, int32_t* send_counts, int32_t* send_offsets,
+                                 hipStream_t s);
+hipError_t launch_ep_recv_layout(const int32_t* recv_counts, int R, int El, int rows_cap, int32_t* local_offsets,
+                                 int32_t* gather, hipStream_t s);
 hipError_t launch_gather_rows(const void* x, const int32_t* token_of_row, const int32_t* offsets,
                               int E, int rows_cap, int D, int elem_bytes, void* x_perm,
                               hipStream_t s);

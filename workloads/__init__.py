@@ -104,6 +104,41 @@ DECODE_CONFIGS = {d.name: d for d in (decode_config(CONFIGS[n], t) for n in ("mi
                                       for t in DECODE_TOKENS)}
 
 
+@dataclasses.dataclass(frozen=True)
+class EpShare:
+    """One GPU's share of an expert-parallel layer: the experts of `rank` out
+    of `ranks` contiguous blocks of the base workload's routed experts, and
+    the rows the dispatch all-to-all delivers to it."""
+    name: str
+    base: str              # workload whose shapes and expert weights are used
+    ranks: int
+    rank: int
+    rows_per_pair: int     # rows each source rank sends for each local expert
+
+    @property
+    def local_experts(self) -> int:
+        return CONFIGS[self.base].num_experts // self.ranks
+
+
+# DeepSeek-V3-shaped layer on 8 GPUs: 32 local experts; 8 ranks x 8192 tokens
+# x top-8 assignments spread evenly give 2,048 rows per expert, 256 from each
+# source rank (65,536 received rows).
+EP_CONFIGS = {e.name: e for e in (EpShare("deepseekv3_ep8_local", "deepseekv3", 8, 0, 256),)}
+
+
+def ep_recv_counts(ep: EpShare) -> np.ndarray:
+    """Rows per (source rank, local expert): the even split of the recipe."""
+    return np.full((ep.ranks, ep.local_experts), ep.rows_per_pair, dtype=np.int32)
+
+
+def make_received_rows(ep: EpShare, n_rows: int) -> np.ndarray:
+    """Received activation rows [n_rows, D] ~ N(0, 1) in bf16, from a stream
+    of their own (the child after the base workload's expert streams)."""
+    cfg = CONFIGS[ep.base]
+    ss = np.random.SeedSequence(cfg.seed).spawn(4 + cfg.num_experts + cfg.num_shared + 1)[-1]
+    return _encode(_normal(ss, (n_rows, cfg.d_model)), cfg.act_dtype)
+
+
 # --------------------------------------------------------------------------
 # bfloat16 encoding (input preparation only)
 # --------------------------------------------------------------------------
