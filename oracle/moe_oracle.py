@@ -25,6 +25,8 @@ step; the steps and their sources:
   combine      index_add of weighted outputs        Tiny-MoE §6; "Top-k 路由" Step 3
   statistics   importance, load, alpha*E*sum f*P    "Top-k 路由" 負載均衡 section; Tiny-MoE §8;
                                                     "别只比较 Top-k" [9,4,2,1] assignment example
+  expert       each expert takes its top-C tokens   "Top-k 路由" Token-Choice vs Expert-Choice table;
+   choice                                           "MoE 路由算法" page, 数学机理 (2)
   EP layouts   rows per destination rank, received "Top-k 路由" 通訊拓撲：All-to-All figure;
                rows in expert-major order           "别只比较 Top-k" 按目标专家发送 / two-All-to-All
                                                     dispatcher section
@@ -323,6 +325,67 @@ def num_parameters_swiglu(d_model: int, d_ff: int) -> int:
     """Parameters of one bias-free SwiGLU expert: gate [F,D] + up [F,D] + down [D,F]."""
     shapes = [(d_ff, d_model), (d_ff, d_model), (d_model, d_ff)]
     return sum(a * b for a, b in shapes)
+
+
+# --------------------------------------------------------------------------
+# Expert-choice routing
+# --------------------------------------------------------------------------
+def expert_choice_capacity(capacity_factor: float, num_tokens: int, top_k: int, num_experts: int) -> int:
+    """Tokens each expert takes: the buffer formula of the "Top-k 路由" page
+    (容量因子: CF * tokens / N * k) with k the average number of experts per
+    token and CF = 1 when none is given, rounded up, at most T."""
+    cf = float(np.float32(capacity_factor)) if capacity_factor > 0 else 1.0
+    c = math.ceil(cf * num_tokens * top_k / num_experts) if num_tokens > 0 else 0
+    return min(c, num_tokens)
+
+
+def expert_choice_route(x, w_router, capacity: int) -> Dict[str, np.ndarray]:
+    """Expert choice ("Top-k 路由" page, Token-Choice vs Expert-Choice table:
+    each expert picks its top-C tokens; "MoE 路由算法" page, 数学机理 (2)): the
+    routing probabilities p = softmax(W_g x) over experts, then for every
+    expert the C tokens with the largest p[:, e] (equal values: lower token
+    index first).  The gate of a chosen (token, expert) is p[t, e].  Rows are
+    laid out expert after expert, tokens ascending inside an expert (as the
+    token-choice dispatch); every expert has exactly C rows."""
+    s = router_logits(x, w_router)
+    p = softmax(s)
+    T, E = p.shape
+    chosen = topk(p.T, capacity) if capacity > 0 else np.zeros((E, 0), dtype=np.int64)   # [E, C], by score
+    token_of_row = np.concatenate([np.sort(chosen[e]) for e in range(E)]) if E else np.zeros(0, np.int64)
+    expert_of_row = np.repeat(np.arange(E), capacity)
+    row_w = p[token_of_row, expert_of_row] if token_of_row.size else np.zeros(0)
+    offsets = np.arange(E + 1, dtype=np.int64) * capacity
+    return dict(logits=s, probs=p, chosen=chosen, token_of_row=token_of_row.astype(np.int64),
+                row_w=row_w, offsets=offsets)
+
+
+def expert_choice_combine(Y: np.ndarray, token_of_row: np.ndarray, row_w: np.ndarray, num_tokens: int,
+                          y_shared=None) -> np.ndarray:
+    """y_t = sum over the rows of token t of row_w * Y[row] (+ shared): the
+    index_add accumulation of the Tiny-MoE §6 combine.  A token no expert
+    chose gets nothing from the routed experts (the residual path carries it:
+    "MoE 路由算法" page, 深度剖析 ②)."""
+    D = Y.shape[1] if Y.size else (y_shared.shape[1] if y_shared is not None else 0)
+    y = np.zeros((num_tokens, D))
+    if token_of_row.size:
+        np.add.at(y, token_of_row, row_w[:, None] * Y)
+    if y_shared is not None:
+        y += y_shared
+    return y
+
+
+def expert_choice_forward(cfg, x, w_router, expert_weights: Callable[[int], tuple],
+                          shared: Sequence = ()) -> Dict[str, np.ndarray]:
+    """Expert-choice layer: route, the selected experts' FFN on their rows,
+    shared experts, combine.  Returns the routing and y."""
+    C = expert_choice_capacity(cfg.capacity_factor, cfg.num_tokens, cfg.top_k, cfg.num_experts)
+    r = expert_choice_route(x, w_router, C)
+    disp = dict(offsets=r["offsets"], token_of_row=r["token_of_row"])
+    Y = expert_outputs(x, disp, expert_weights, cfg.activation, cfg.d_ff, cfg.num_experts)
+    ys = shared_experts(x, shared) if len(shared) else None
+    y = expert_choice_combine(Y, r["token_of_row"], r["row_w"], cfg.num_tokens, ys)
+    unselected = int(cfg.num_tokens - np.unique(r["token_of_row"]).size)
+    return dict(route=r, capacity=C, Y=Y, y=y, unselected=unselected)
 
 
 # --------------------------------------------------------------------------

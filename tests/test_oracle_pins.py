@@ -534,3 +534,93 @@ def test_ep_dispatch_payload_worked_example():
     remote = int(lay["send_counts"][1])
     assert lay["send_counts"][0] == 0
     assert remote * D * 2 == 131072
+
+
+# --------------------------------------------------------------------------
+# expert-choice routing
+# --------------------------------------------------------------------------
+def test_expert_choice_capacity_is_the_buffer_formula():
+    """C is the "Top-k 路由" 容量因子 buffer (the same worked cases as the
+    token-choice capacity), CF = 1 when none is given, at most T."""
+    for c in gold("capacity_examples.json")["cases"]:
+        want = min(c["capacity"], c["num_tokens"])
+        assert O.expert_choice_capacity(c["capacity_factor"], c["num_tokens"], c["top_k"], c["num_experts"]) == want
+    assert O.expert_choice_capacity(0.0, 4096, 6, 64) == 384          # T k / E
+    assert O.expert_choice_capacity(0.0, 3, 8, 2) == 3                # at most T
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_expert_choice_selection_brute_force(seed):
+    """Every expert's chosen set is the C-subset of tokens with the largest
+    total probability, equal totals going to the lexicographically smallest
+    token set (enumerated over all subsets), with ties built in."""
+    rng = np.random.default_rng(40 + seed)
+    T, E, D = int(rng.integers(3, 8)), int(rng.integers(1, 5)), 6
+    x = rng.standard_normal((T, D))
+    wr = rng.standard_normal((E, D))
+    if seed % 2 == 0 and T > 2:
+        x[1] = x[0]                                                 # equal probabilities of tokens 0 and 1
+    C = int(rng.integers(1, T + 1))
+    r = O.expert_choice_route(x, wr, C)
+    p = O.softmax(x @ wr.T)
+    for e in range(E):
+        best = None
+        for sub in itertools.combinations(range(T), C):
+            v = sum(p[t, e] for t in sub)
+            if best is None or v > best[0] + 1e-15:
+                best = (v, sub)
+        assert tuple(sorted(r["chosen"][e])) == best[1]
+        rows = r["token_of_row"][e * C:(e + 1) * C]
+        assert list(rows) == sorted(rows)
+        np.testing.assert_array_equal(r["row_w"][e * C:(e + 1) * C], p[rows, e])
+    np.testing.assert_array_equal(r["offsets"], np.arange(E + 1) * C)
+
+
+def test_expert_choice_single_expert_takes_the_first_tokens():
+    """One expert: every probability is 1, all tied, so the expert takes
+    tokens 0 .. C-1 with gate 1."""
+    rng = np.random.default_rng(50)
+    x = rng.standard_normal((9, 4))
+    r = O.expert_choice_route(x, rng.standard_normal((1, 4)), 4)
+    np.testing.assert_array_equal(r["token_of_row"], [0, 1, 2, 3])
+    np.testing.assert_array_equal(r["row_w"], np.ones(4))
+
+
+def test_expert_choice_every_token_is_dense_soft_routing():
+    """C = T: every expert takes every token, so the layer is the dense
+    probability-weighted sum over all experts (the soft-routing formula)."""
+    rng = np.random.default_rng(51)
+    T, D, F, E = 7, 8, 6, 4
+    x = rng.standard_normal((T, D))
+    wr = rng.standard_normal((E, D))
+    ex = _rand_experts(rng, E, D, F)
+    cfg = W.MoEConfig("ec_dense", T, D, E, E, F, act_dtype=W.F32, router_dtype=W.F32)
+    out = O.expert_choice_forward(cfg, x, wr, lambda e: ex[e])
+    assert out["capacity"] == T and out["unselected"] == 0
+    p = torch.softmax(torch.from_numpy(x @ wr.T), -1).numpy()
+    dense = np.zeros((T, D))
+    for e in range(E):
+        dense += p[:, e:e + 1] * O.expert_apply(x, *ex[e], O.SWIGLU, F)
+    np.testing.assert_allclose(out["y"], dense, rtol=1e-12, atol=1e-14)
+
+
+def test_expert_choice_unchosen_token_gets_only_the_shared_path():
+    """Two experts that both prefer tokens 0 and 1 (C = 1): token 2 is chosen
+    by neither, so its routed output is zero and only the shared expert
+    reaches it; the chosen tokens get p * E(x)."""
+    rng = np.random.default_rng(52)
+    D, F = 4, 3
+    wr = np.array([[1.0, 0, 0, 0], [0, 1.0, 0, 0]])
+    x = np.array([[4.0, 0, 0, 0], [0, 4.0, 0, 0], [0.1, 0.1, 0, 0]])
+    ex = _rand_experts(rng, 2, D, F)
+    sh = [tuple(rng.standard_normal(s) for s in ((F, D), (F, D), (D, F)))]
+    cfg = W.MoEConfig("ec_unchosen", 3, D, 2, 1, F, act_dtype=W.F32, router_dtype=W.F32, capacity_factor=0.5)
+    out = O.expert_choice_forward(cfg, x, wr, lambda e: ex[e], sh)
+    assert out["capacity"] == 1 and out["unselected"] == 1
+    np.testing.assert_array_equal(out["route"]["token_of_row"], [0, 1])
+    ys = O.shared_experts(x, sh)
+    np.testing.assert_allclose(out["y"][2], ys[2], rtol=1e-13)
+    p = O.softmax(x @ wr.T)
+    for t, e in ((0, 0), (1, 1)):
+        want = p[t, e] * O.expert_apply(x[t:t + 1], *ex[e], O.SWIGLU, F)[0] + ys[t]
+        np.testing.assert_allclose(out["y"][t], want, rtol=1e-12)
