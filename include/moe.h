@@ -103,7 +103,8 @@ typedef enum {
   MOE_OP_EXPERT_FFN = 2,      /* routed experts: max_rows = A_cap, d_ff = F */
   MOE_OP_SHARED_FFN = 3,      /* shared experts: max_rows = T, d_ff = S*F_s */
   MOE_OP_LOAD_STATS = 4,
-  MOE_OP_LAYER = 5
+  MOE_OP_LAYER = 5,
+  MOE_OP_EXPERT_CHOICE = 6    /* moe_expert_choice_forward */
 } moe_op;
 
 /* Workspace bytes that entry point `op` needs for `cfg` (host output).  A
@@ -262,6 +263,37 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const moe_weights* wei
                                    int32_t* counts, float alpha, float* stats, int32_t* dropped,
                                    void* ws, size_t ws_bytes, void* stream,
                                    void* const* stage_events);
+
+/* Expert-choice routing ("Top-k 路由" page, Token-Choice vs Expert-Choice
+ * table: each expert picks its top-C tokens; "MoE 路由算法" page, 数学机理
+ * (2), and 深度剖析 ② on tokens no expert picks).  The layer forward with the
+ * routing reversed:
+ *   p = softmax(W_g x) over the experts (float32, from the router logits);
+ *   expert e takes the C tokens with the largest p[:, e] (equal values: the
+ *   lower token index first), gate p[t, e];
+ *   C = ceil(CF * T * k / E) (the buffer formula of the 容量因子 section; k =
+ *   cfg->top_k read as the average experts per token, CF =
+ *   cfg->capacity_factor, or 1 when <= 0), at most T: moe_expert_choice_capacity;
+ *   rows expert after expert, tokens ascending inside an expert (E * C rows);
+ *   the grouped expert FFN of cfg->activation on the rows, the shared experts
+ *   (weight 1, every token) as in moe_layer_forward;
+ *   y[t] = sum over the experts that took t, ascending, of p[t, e] *
+ *   FFN_e(x[t]) (+ shared); a token no expert took gets only the shared
+ *   output (0 without shared experts): the caller's residual carries it.
+ * cfg->scoring and cfg->renormalize are not used.  Limits: E <= 256,
+ * T <= 8192 (MOE_ERR_UNSUPPORTED beyond).
+ *   x, y           [T, D] act_dtype device
+ *   token_of_row   [E * C] int32 out or NULL; row_w [E * C] float32 out or NULL
+ *   unselected     [1] int32 out or NULL: tokens no expert took
+ *   ws             moe_workspace_size(MOE_OP_EXPERT_CHOICE) bytes
+ *   stage_events   NULL, or 2 * MOE_NUM_STAGES hipEvent_t as for
+ *                  moe_layer_forward_timed (route: ROUTER_LOGITS and
+ *                  ROUTE_SELECT; PERMUTE and LOAD_STATS are not used)
+ * Bit-exact choices (outside near ties of p) and deterministic outputs. */
+moe_status moe_expert_choice_capacity(const moe_config* cfg, int32_t* capacity);
+moe_status moe_expert_choice_forward(const moe_config* cfg, const moe_weights* weights, const void* x, void* y,
+                                     int32_t* token_of_row, float* row_w, int32_t* unselected,
+                                     void* ws, size_t ws_bytes, void* stream, void* const* stage_events);
 
 /* Expert parallelism, the part one GPU holds ("Top-k 路由" page, 通訊拓撲：
  * All-to-All figure; "别只比较 Top-k" page, two-All-to-All dispatcher and

@@ -145,3 +145,53 @@ def check_layer(cfg, inp, ref, got, sel_bias=None):
         err = row_rel_err(got["y"][same], ref["y"][same]) if cfg.capacity_factor <= 0 else 0.0
     assert err <= out_tol(cfg), f"max relative error {err:.3e} > {out_tol(cfg)}"
     return diff, err
+
+
+def ec_check_selection(ref, tor_gpu: np.ndarray, capacity: int) -> int:
+    """Expert-choice choices of the GPU against the oracle's: per expert the
+    same token set, except tokens whose probability is within 1e-6 relative
+    of the expert's C-th largest (either choice is correct there); rows of an
+    expert ascending.  Returns the number of experts with a near-tie exchange."""
+    p = ref["probs"]
+    T, E = p.shape
+    C = capacity
+    ties = 0
+    for e in range(E):
+        got = tor_gpu[e * C:(e + 1) * C]
+        assert (np.diff(got) > 0).all(), f"expert {e}: rows not ascending"
+        want = ref["token_of_row"][e * C:(e + 1) * C]
+        if np.array_equal(got, want):
+            continue
+        col = p[:, e]
+        v = np.sort(col)[::-1][C - 1]
+        band = np.abs(col - v) <= 1e-6 * abs(v)
+        sg, sw = set(got.tolist()), set(want.tolist())
+        for t in sg ^ sw:
+            assert band[t], f"expert {e}: token {t} chosen differently and not a near tie"
+        ties += 1
+    return ties
+
+
+def ec_oracle_output(cfg, inp, tor: np.ndarray, capacity: int, expert_weights=None, rows=None):
+    """Oracle layer output for a given expert-choice selection (the GPU's, so
+    that near-tie exchanges do not matter): float64 probabilities as gates.
+    rows: optional token subset to evaluate."""
+    p = O.softmax(O.router_logits(inp.x, inp.w_router))
+    T = cfg.num_tokens
+    C = capacity
+    ew = expert_weights or (lambda e: (inp.w13[e], inp.w2[e]))
+    X = O.widen(inp.x)
+    toks = np.arange(T) if rows is None else np.asarray(rows)
+    pos = {int(t): i for i, t in enumerate(toks)}
+    y = np.zeros((len(toks), X.shape[1]))
+    for e in range(cfg.num_experts):
+        sel = [int(t) for t in tor[e * C:(e + 1) * C] if int(t) in pos]
+        if not sel:
+            continue
+        w13, w2 = ew(e)
+        out = O.expert_apply(X[sel], w13, w2, cfg.activation, cfg.d_ff)
+        for t, o in zip(sel, out):
+            y[pos[t]] += p[t, e] * o
+    if cfg.num_shared:
+        y += O.shared_experts(inp.x[toks], inp.shared)
+    return y

@@ -10,8 +10,8 @@ import workloads as W
 from oracle import moe_oracle as O
 from workloads.torch_io import act_torch_dtype, to_numpy, to_torch
 
-from parity import (BF16_TOL, W_TOL, DeviceLayer, check_layer, oracle_forward, out_tol, refinement_margin, rel_err,
-                    route_differences, row_rel_err)
+from parity import (BF16_TOL, W_TOL, DeviceLayer, check_layer, ec_check_selection, ec_oracle_output, oracle_forward,
+                    out_tol, refinement_margin, rel_err, route_differences, row_rel_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -687,3 +687,76 @@ def test_ep_local_ffn_over_received_rows(activation):
     err = max(errs)
     print(f"  max rel err {err:.3e}")
     assert err <= BF16_TOL
+
+
+# --------------------------------------------------------------------------
+# expert-choice routing
+# --------------------------------------------------------------------------
+EC_SHAPES = [
+    W.MoEConfig("ec_swiglu", 700, 256, 8, 2, 320, zipf_s=1.0),
+    W.MoEConfig("ec_many_experts_shared", 333, 128, 64, 6, 128, num_shared=2, d_ff_shared=64),
+    W.MoEConfig("ec_gelu_f32_router", 500, 192, 16, 1, 256, activation=W.GELU, router_dtype=W.F32),
+    W.MoEConfig("ec_fp32_shared", 150, 96, 12, 3, 100, num_shared=3, d_ff_shared=20, act_dtype=W.F32,
+                router_dtype=W.F32),
+    W.MoEConfig("ec_capacity_factor", 257, 64, 5, 2, 48, capacity_factor=1.5),
+    W.MoEConfig("ec_every_token", 40, 64, 4, 4, 64),
+    W.MoEConfig("ec_256_experts", 600, 64, 256, 8, 64, scoring=W.SIGMOID_BIAS, zipf_s=1.2),
+    W.MoEConfig("ec_max_tokens", 8192, 64, 4, 1, 32),
+    W.MoEConfig("ec_one_token", 1, 64, 8, 2, 64),
+]
+
+
+@pytest.mark.parametrize("cfg", EC_SHAPES, ids=lambda c: c.name)
+def test_expert_choice_matches_oracle(cfg):
+    """Expert-choice layer: every expert's chosen tokens bit-exact against
+    the oracle (near ties of the C-th probability exempt), gates within 1e-5
+    of the float64 probabilities, unchosen-token count, and the outputs against
+    the oracle evaluated on the GPU's choices."""
+    print(f"[expert choice] {cfg.name}", flush=True)
+    T, E, D = cfg.num_tokens, cfg.num_experts, cfg.d_model
+    C = M.moe_expert_choice_capacity(cfg)
+    assert C == O.expert_choice_capacity(cfg.capacity_factor, T, cfg.top_k, E)
+    inp = W.make_inputs(cfg)
+    ref = O.expert_choice_route(inp.x, inp.w_router, C)
+    dev = "cuda"
+    weights = dict(w_router=to_torch(inp.w_router, dev), w13=to_torch(inp.w13, dev), w2=to_torch(inp.w2, dev),
+                   ws13=to_torch(inp.ws13, dev), ws2=to_torch(inp.ws2, dev))
+    x = to_torch(inp.x, dev)
+    y = torch.empty((T, D), dtype=act_torch_dtype(cfg), device=dev)
+    tor = torch.empty(E * C, dtype=torch.int32, device=dev)
+    rw = torch.empty(E * C, dtype=torch.float32, device=dev)
+    uns = torch.empty(1, dtype=torch.int32, device=dev)
+    ws = M.workspace(cfg, M.MOE_OP_EXPERT_CHOICE, dev)
+    M.moe_expert_choice_forward(cfg, weights, x, y, tor, rw, uns, ws)
+    torch.cuda.synchronize()
+    tg = to_numpy(tor).astype(np.int64)
+    ties = ec_check_selection(ref, tg, C)
+    print(f"  C={C}, experts with a near-tie exchange: {ties}")
+    p = ref["probs"]
+    gates = p[tg, np.repeat(np.arange(E), C)]
+    assert rel_err(to_numpy(rw), gates) <= W_TOL
+    assert int(to_numpy(uns)[0]) == T - np.unique(tg).size
+    if ties == 0:
+        assert int(to_numpy(uns)[0]) == O.expert_choice_forward(
+            cfg, inp.x, inp.w_router, lambda e: (inp.w13[e], inp.w2[e]), inp.shared)["unselected"]
+    y_ref = ec_oracle_output(cfg, inp, tg, C)
+    err = row_rel_err(to_numpy(y), y_ref)
+    print(f"  max rel err {err:.3e}")
+    assert err <= out_tol(cfg)
+
+
+def test_expert_choice_deterministic():
+    cfg = EC_SHAPES[1]
+    inp = W.make_inputs(cfg)
+    dev = "cuda"
+    weights = dict(w_router=to_torch(inp.w_router, dev), w13=to_torch(inp.w13, dev), w2=to_torch(inp.w2, dev),
+                   ws13=to_torch(inp.ws13, dev), ws2=to_torch(inp.ws2, dev))
+    x = to_torch(inp.x, dev)
+    ws = M.workspace(cfg, M.MOE_OP_EXPERT_CHOICE, dev)
+    outs = []
+    for _ in range(3):
+        y = torch.empty((cfg.num_tokens, cfg.d_model), dtype=torch.bfloat16, device=dev)
+        M.moe_expert_choice_forward(cfg, weights, x, y, ws=ws)
+        torch.cuda.synchronize()
+        outs.append(to_numpy(y))
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])

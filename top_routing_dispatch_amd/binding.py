@@ -21,11 +21,12 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_SOFTMAX_TOPK, MOE_TOPK_SOFTMAX, MOE_SIGMOID_BIAS = 0, 1, 2
 MOE_SWIGLU, MOE_GELU = 0, 1
 (MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_EXPERT_FFN, MOE_OP_SHARED_FFN,
- MOE_OP_LOAD_STATS, MOE_OP_LAYER) = range(6)
+ MOE_OP_LOAD_STATS, MOE_OP_LAYER, MOE_OP_EXPERT_CHOICE) = range(7)
 
 EXPORTED = ("moe_capacity", "moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn",
             "moe_combine", "moe_load_stats", "moe_layer_forward", "moe_layer_forward_timed",
-            "moe_ep_send_layout", "moe_ep_recv_layout", "moe_status_string", "moe_last_error")
+            "moe_expert_choice_capacity", "moe_expert_choice_forward", "moe_ep_send_layout", "moe_ep_recv_layout",
+            "moe_status_string", "moe_last_error")
 STAGES = ("router_logits", "route_select", "permute", "expert_gate_up", "expert_down", "shared_gate_up",
           "shared_down", "combine", "load_stats")
 
@@ -77,6 +78,9 @@ def lib() -> ctypes.CDLL:
             "moe_layer_forward": [cfgp, ctypes.POINTER(moe_weights), vp, vp, vp, vp, vp, f32, vp, vp, vp, sz, vp],
             "moe_layer_forward_timed": [cfgp, ctypes.POINTER(moe_weights), vp, vp, vp, vp, vp, f32, vp, vp, vp, sz,
                                         vp, ctypes.POINTER(vp)],
+            "moe_expert_choice_capacity": [cfgp, ctypes.POINTER(i32)],
+            "moe_expert_choice_forward": [cfgp, ctypes.POINTER(moe_weights), vp, vp, vp, vp, vp, vp, sz, vp,
+                                          ctypes.POINTER(vp)],
             "moe_ep_send_layout": [i32, i32, vp, vp, vp, vp],
             "moe_ep_recv_layout": [i32, i32, vp, i32, vp, vp, vp],
         }
@@ -199,6 +203,31 @@ def moe_layer_forward_timed(cfg, weights: dict, x, y, topk_idx=None, topk_w=None
         ctypes.byref(c), ctypes.byref(w), _ptr(x), _ptr(y), _ptr(topk_idx), _ptr(topk_w), _ptr(counts),
         float(alpha), _ptr(stats), _ptr(dropped), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream),
         arr))
+
+
+def moe_expert_choice_capacity(cfg) -> int:
+    c = make_config(cfg)
+    cap = ctypes.c_int32()
+    _check("moe_expert_choice_capacity", lib().moe_expert_choice_capacity(ctypes.byref(c), ctypes.byref(cap)))
+    return cap.value
+
+
+def moe_expert_choice_forward(cfg, weights: dict, x, y, token_of_row=None, row_w=None, unselected=None, ws=None,
+                              stage_events=None, stream=None):
+    """Expert-choice layer forward; stage_events as for moe_layer_forward_timed."""
+    c = make_config(cfg)
+    w = moe_weights()
+    for name, _ in moe_weights._fields_:
+        t = weights.get(name)
+        setattr(w, name, None if t is None else t.data_ptr())
+    arr = None
+    if stage_events is not None:
+        arr = (ctypes.c_void_p * (2 * len(STAGES)))()
+        for i, ev in enumerate(stage_events):
+            arr[i] = None if ev is None else ev.cuda_event
+    _check("moe_expert_choice_forward", lib().moe_expert_choice_forward(
+        ctypes.byref(c), ctypes.byref(w), _ptr(x), _ptr(y), _ptr(token_of_row), _ptr(row_w), _ptr(unselected),
+        _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream), arr))
 
 
 def moe_ep_send_layout(num_experts, num_ranks, offsets, send_counts, send_offsets, stream=None):

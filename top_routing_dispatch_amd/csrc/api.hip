@@ -537,6 +537,53 @@ moe_status aux_stream(AuxStream** out) {
   return MOE_OK;
 }
 
+// Expert choice --------------------------------------------------------------
+int ec_capacity(const moe_config* c) {
+  if (c->num_tokens <= 0) return 0;
+  const double cf = c->capacity_factor > 0.0f ? (double)c->capacity_factor : 1.0;
+  const double v = ceil(cf * (double)c->num_tokens * (double)c->top_k / (double)c->num_experts);
+  return v >= (double)c->num_tokens ? c->num_tokens : (int)v;
+}
+
+struct EcLayout {
+  size_t logits, wsplit, pT, tor, roww, offsets, prefixes, selbits, selpre, h, yperm, h_shared, kpart, kpart_shared,
+      total;
+};
+
+EcLayout ec_layout(const moe_config* c) {
+  EcLayout L{};
+  const size_t T = c->num_tokens, E = c->num_experts, C = ec_capacity(c);
+  const size_t es = esize(c->act_dtype);
+  const size_t W = (T + 31) / 32;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o += carve(bytes); return at; };
+  L.logits = take(T * E * 4);
+  L.wsplit = take(router_split_bytes(c));
+  L.pT = take(T * E * 4);
+  L.tor = take(E * C * 4);
+  L.roww = take(E * C * 4);
+  L.offsets = take((E + 1) * 4);
+  L.prefixes = take(4 * (E + 1) * 4);
+  L.selbits = take(E * W * 4);
+  L.selpre = take(E * W * 4);
+  L.h = take(E * C * c->d_ff * es);
+  L.yperm = take(E * C * c->d_model * es);
+  L.h_shared = take(T * c->num_shared * c->d_ff_shared * es);
+  L.kpart = take(ffn_partial_bytes(c->act_dtype, c->activation, c->d_model, c->d_ff, (int)(E * C), (int)E, true));
+  L.kpart_shared = take(c->num_shared > 0 ? ffn_partial_bytes(c->act_dtype, SWIGLU, c->d_model,
+                                                              c->num_shared * c->d_ff_shared, (int)T, 1, false)
+                                          : 0);
+  L.total = o;
+  return L;
+}
+
+moe_status validate_ec(const moe_config* c) {
+  MOE_TRY(validate_config(c));
+  if (c->num_experts > kEcMaxExperts || c->num_tokens > kEcMaxTokens) return MOE_ERR_UNSUPPORTED;
+  if ((long long)c->num_experts * ec_capacity(c) > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -579,6 +626,10 @@ moe_status moe_workspace_size(const moe_config* cfg, int32_t op, size_t* bytes) 
       break;
     case MOE_OP_LOAD_STATS: *bytes = ws_stats(cfg); break;
     case MOE_OP_LAYER: *bytes = layer_layout(cfg, d).total; break;
+    case MOE_OP_EXPERT_CHOICE:
+      MOE_TRY(validate_ec(cfg));
+      *bytes = ec_layout(cfg).total;
+      break;
     default: return MOE_ERR_INVALID_ARGUMENT;
   }
   return MOE_OK;
@@ -833,6 +884,68 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const moe_weights* wt,
     MOE_TRY_HIP("load stats", launch_load_stats(sa, s));
     MOE_TRY(mark(ev, MOE_STAGE_LOAD_STATS, 1, s));
   }
+  return MOE_OK;
+}
+
+moe_status moe_expert_choice_capacity(const moe_config* cfg, int32_t* capacity) {
+  MOE_TRY(validate_ec(cfg));
+  if (capacity == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+  *capacity = ec_capacity(cfg);
+  return MOE_OK;
+}
+
+moe_status moe_expert_choice_forward(const moe_config* cfg, const moe_weights* wt, const void* x, void* y,
+                                     int32_t* token_of_row, float* row_w, int32_t* unselected,
+                                     void* ws, size_t ws_bytes, void* stream, void* const* ev) {
+  MOE_TRY(validate_ec(cfg));
+  if (wt == nullptr || wt->w_router == nullptr || wt->w13 == nullptr || wt->w2 == nullptr)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (cfg->num_shared > 0 && (wt->ws13 == nullptr || wt->ws2 == nullptr)) return MOE_ERR_INVALID_ARGUMENT;
+  const bool any = cfg->num_tokens > 0;
+  if (any && (x == nullptr || y == nullptr || ws == nullptr)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!opt_aligned(x) || !opt_aligned(y) || !opt_aligned(token_of_row) || !opt_aligned(row_w) ||
+      !opt_aligned(unselected) || !opt_aligned(ws) || !aligned16(wt->w_router) || !aligned16(wt->w13) ||
+      !aligned16(wt->w2) || !opt_aligned(wt->ws13) || !opt_aligned(wt->ws2))
+    return MOE_ERR_INVALID_ARGUMENT;
+  const EcLayout L = ec_layout(cfg);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (!any) return MOE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int T = cfg->num_tokens, E = cfg->num_experts, D = cfg->d_model, F = cfg->d_ff;
+  const int C = ec_capacity(cfg);
+  const int SF = cfg->num_shared * cfg->d_ff_shared;
+  int32_t* tor = token_of_row ? token_of_row : at<int32_t>(ws, L.tor);
+  float* roww = row_w ? row_w : at<float>(ws, L.roww);
+  int32_t* off = at<int32_t>(ws, L.offsets);
+  int32_t* prefix_up = at<int32_t>(ws, L.prefixes);
+  float* pT = at<float>(ws, L.pT);
+  uint32_t* selbits = at<uint32_t>(ws, L.selbits);
+  int32_t* selpre = at<int32_t>(ws, L.selpre);
+  float* logits = at<float>(ws, L.logits);
+
+  MOE_TRY(mark(ev, MOE_STAGE_ROUTER_LOGITS, 0, s));
+  MOE_TRY(run_router_logits(cfg, x, wt->w_router, logits, at<void>(ws, L.wsplit), s));
+  MOE_TRY(mark(ev, MOE_STAGE_ROUTER_LOGITS, 1, s));
+  MOE_TRY(mark(ev, MOE_STAGE_ROUTE_SELECT, 0, s));
+  MOE_TRY_HIP("expert-choice route", launch_ec_route(logits, T, E, C, pT, off, tor, roww, selbits, selpre,
+                                                     unselected, s));
+  MOE_TRY(mark(ev, MOE_STAGE_ROUTE_SELECT, 1, s));
+  const FfnPlan pl = plan_ffn(cfg->act_dtype, cfg->activation, D, F, E * C, E, true);
+  if (!pl.split) MOE_TRY_HIP("tile prefix", launch_tile_prefix(off, E, pl.bm_up, prefix_up, s));
+  MOE_TRY(run_ffn(cfg->act_dtype, cfg->activation, E, D, F, E * C, x, tor, off, prefix_up, prefix_up + (E + 1),
+                  wt->w13, wt->w2, at<void>(ws, L.h), at<void>(ws, L.yperm), at<float>(ws, L.kpart), s, ev,
+                  MOE_STAGE_EXPERT_GATE_UP, MOE_STAGE_EXPERT_DOWN));
+  if (cfg->num_shared > 0) {
+    MOE_TRY(run_ffn_part(cfg->act_dtype, SWIGLU, 1, D, SF, T, x, wt->ws13, wt->ws2, at<void>(ws, L.h_shared), y,
+                         at<float>(ws, L.kpart_shared), s, ev, MOE_STAGE_SHARED_GATE_UP, true));
+    MOE_TRY(run_ffn_part(cfg->act_dtype, SWIGLU, 1, D, SF, T, x, wt->ws13, wt->ws2, at<void>(ws, L.h_shared), y,
+                         at<float>(ws, L.kpart_shared), s, ev, MOE_STAGE_SHARED_DOWN, false));
+  }
+  MOE_TRY(mark(ev, MOE_STAGE_COMBINE, 0, s));
+  MOE_TRY_HIP("expert-choice combine", launch_ec_combine(at<void>(ws, L.yperm), pT, selbits, selpre,
+                                                         cfg->num_shared > 0 ? y : nullptr, y, T, E, C, D,
+                                                         cfg->act_dtype, unselected, s));
+  MOE_TRY(mark(ev, MOE_STAGE_COMBINE, 1, s));
   return MOE_OK;
 }
 

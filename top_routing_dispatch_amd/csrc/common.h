@@ -315,6 +315,16 @@ struct PermuteArgs {
 };
 constexpr int kPermuteTile = 256;   // tokens per histogram / scatter block
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
+// Expert-choice routing and combine (expert_choice.hip): E <= 256 experts,
+// T <= 8192 tokens (the sort keys of one expert's column sit in LDS).
+constexpr int kEcMaxExperts = 256;
+constexpr int kEcMaxTokens = 8192;
+hipError_t launch_ec_route(const float* logits, int T, int E, int C, float* pT, int32_t* offsets,
+                           int32_t* token_of_row, float* row_w, uint32_t* selbits, int32_t* selpre,
+                           int32_t* unselected, hipStream_t s);
+hipError_t launch_ec_combine(const void* y_perm, const float* pT, const uint32_t* selbits, const int32_t* selpre,
+                             const void* y_shared, void* y, int T, int E, int C, int D, int act_dtype,
+                             int32_t* unselected, hipStream_t s);
 // Expert-parallel send / receive layouts (ep.hip).
 hipError_t launch_ep_send_layout(const int32_t* offsets, int E, int R, int32_t* send_counts, int32_t* send_offsets,
                                  hipStream_t s);

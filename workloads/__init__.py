@@ -96,12 +96,22 @@ def decode_config(cfg: MoEConfig, tokens: int) -> MoEConfig:
 
 
 def base_name(cfg: MoEConfig) -> str:
-    """The workload whose weights a (decode-shaped) configuration uses."""
-    return cfg.name.split(DECODE_SEP)[0]
+    """The workload whose weights a (decode-shaped or expert-choice)
+    configuration uses."""
+    name = cfg.name.split(DECODE_SEP)[0]
+    return name[:-len("_ec")] if name.endswith("_ec") else name
 
 
 DECODE_CONFIGS = {d.name: d for d in (decode_config(CONFIGS[n], t) for n in ("mixtral", "deepseekv3")
                                       for t in DECODE_TOKENS)}
+
+
+# Expert-choice routing at the shapes of three workloads: the same tokens,
+# weights and expert FFNs; each expert takes C = T k / E tokens (k read as the
+# average experts per token; the scoring mode of the workload is not used).
+EC_SUFFIX = "_ec"
+EC_CONFIGS = {c.name + EC_SUFFIX: c.replace(name=c.name + EC_SUFFIX, capacity_factor=0.0)
+              for c in (MIXTRAL, DEEPSEEKMOE, DEEPSEEKV3)}
 
 
 @dataclasses.dataclass(frozen=True)
