@@ -141,8 +141,9 @@ def copy_calibration(mib, reps):
                       "bytes_written": 4 * n, "launches": reps}), flush=True)
 
 
-def cpu_baseline(cfg, inp, sample_tokens):
-    """The oracle as it stands, on the first `sample_tokens` tokens."""
+def cpu_baseline(cfg, inp, sample_tokens, expert_choice=False):
+    """The oracle as it stands, on the first `sample_tokens` tokens (expert
+    choice: those tokens as a batch of their own, C recomputed for it)."""
     from oracle import moe_oracle as O
     try:
         import threadpoolctl
@@ -156,14 +157,17 @@ def cpu_baseline(cfg, inp, sample_tokens):
     passes = 0
     t0 = time.perf_counter()
     while True:
-        O.forward(scfg, x, inp.w_router, inp.sel_bias, lambda e: (inp.w13[e], inp.w2[e]), inp.shared)
+        if expert_choice:
+            O.expert_choice_forward(scfg, x, inp.w_router, lambda e: (inp.w13[e], inp.w2[e]), inp.shared)
+        else:
+            O.forward(scfg, x, inp.w_router, inp.sel_bias, lambda e: (inp.w13[e], inp.w2[e]), inp.shared)
         passes += 1
         dt = time.perf_counter() - t0
         if dt >= CPU_MIN_SECONDS:
             break
     return dict(value=round(Ts * passes / dt, 2), unit="tokens/s", cores=int(cores), kind="oracle",
                 sample=f"first {Ts} of {cfg.num_tokens} tokens, all {cfg.num_experts} experts"
-                       + (", capacity recomputed for the sample" if cfg.capacity_factor > 0 else "")
+                       + (", capacity recomputed for the sample" if cfg.capacity_factor > 0 or expert_choice else "")
                        + f"; {passes} pass(es) in {dt:.1f} s")
 
 
@@ -173,9 +177,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="switch",
-                    choices=sorted(W.CONFIGS) + sorted(W.DECODE_CONFIGS) + sorted(W.EP_CONFIGS),
+                    choices=sorted(W.CONFIGS) + sorted(W.DECODE_CONFIGS) + sorted(W.EP_CONFIGS) + sorted(W.EC_CONFIGS),
                     help="workload; <model>_decode_t<T>: the first T tokens on that model's full-size weights; "
-                         "<model>_ep8_local: one GPU's share of an 8-rank expert-parallel layer")
+                         "<model>_ep8_local: one GPU's share of an 8-rank expert-parallel layer; "
+                         "<model>_ec: the model's layer with expert-choice routing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=None)
     ap.add_argument("--copy-calibration", type=int, default=None, metavar="MIB",
@@ -198,7 +203,8 @@ def main():
     import top_routing_dispatch_amd as M
     from workloads.torch_io import act_torch_dtype, to_torch, upload_experts
 
-    cfg = W.CONFIGS.get(args.config) or W.DECODE_CONFIGS[args.config]
+    cfg = W.CONFIGS.get(args.config) or W.DECODE_CONFIGS.get(args.config) or W.EC_CONFIGS[args.config]
+    ec = args.config in W.EC_CONFIGS
     dev = "cuda"
     torch.cuda.set_device(0)
     t_setup = time.perf_counter()
@@ -218,7 +224,12 @@ def main():
     counts = torch.empty(E, dtype=torch.int32, device=dev)
     stats = torch.empty(2 * E + 2, dtype=torch.float32, device=dev)
     dropped = torch.empty(1, dtype=torch.int32, device=dev)
-    ws = M.workspace(cfg, M.MOE_OP_LAYER, dev)
+    ws = M.workspace(cfg, M.MOE_OP_EXPERT_CHOICE if ec else M.MOE_OP_LAYER, dev)
+    if ec:
+        C_ec = M.moe_expert_choice_capacity(cfg)
+        tor_ec = torch.empty(E * C_ec, dtype=torch.int32, device=dev)
+        rw_ec = torch.empty(E * C_ec, dtype=torch.float32, device=dev)
+        uns_ec = torch.empty(1, dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
     log(f"[bench] {cfg.name}: setup {time.perf_counter() - t_setup:.1f} s, workspace {ws.numel() / 1e6:.1f} MB")
 
@@ -235,6 +246,9 @@ def main():
         return evs
 
     def step(evs=None):
+        if ec:
+            M.moe_expert_choice_forward(cfg, weights, x, y, tor_ec, rw_ec, uns_ec, ws, stage_events=evs)
+            return
         M.moe_layer_forward_timed(cfg, weights, x, y, idx, tw, counts, cfg.alpha, stats, dropped, ws,
                                   stage_events=evs)
 
@@ -244,6 +258,8 @@ def main():
             name = M.STAGES[si]
             if name.startswith("shared") and cfg.num_shared == 0:
                 continue        # no kernels: the events only hold their creation-time records
+            if ec and name in ("permute", "load_stats"):
+                continue        # not stages of the expert-choice layer
             vals = [evs[2 * si].elapsed_time(evs[2 * si + 1]) for evs in events]
             if vals and max(vals) > 0:
                 out[name] = float(np.mean(vals))
@@ -282,9 +298,12 @@ def main():
     # the dominant stage's time over the timed steps (HIP events on the library's stream)
     dom_ms = stage_times(events, [dom_i])[dominant]
 
-    c_host = counts.cpu().numpy()
-    cap, rows_cap = M.moe_capacity(cfg)
-    kept = np.minimum(c_host, cap)
+    if ec:
+        kept = np.full(E, C_ec)                         # every expert takes exactly C tokens
+    else:
+        c_host = counts.cpu().numpy()
+        cap, rows_cap = M.moe_capacity(cfg)
+        kept = np.minimum(c_host, cap)
     A = int(kept.sum())
     E_act = int((kept > 0).sum())
     stage_info = {}
@@ -301,7 +320,7 @@ def main():
     if not args.no_cpu_baseline:
         n = args.cpu_sample_tokens or DEFAULT_CPU_SAMPLE.get(cfg.name, 64)
         log(f"[bench] timing the CPU oracle on {n} tokens")
-        cpu = cpu_baseline(cfg, inp, n)
+        cpu = cpu_baseline(cfg, inp, n, expert_choice=ec)
 
     value = T / (ms_per_step * 1e-3)
     line = {
@@ -314,7 +333,8 @@ def main():
                    "d_ff": cfg.d_ff, "shared": cfg.num_shared, "d_ff_shared": cfg.d_ff_shared,
                    "scoring": ["softmax_topk", "topk_softmax", "sigmoid_bias"][cfg.scoring],
                    "activation": ["swiglu", "gelu"][cfg.activation], "capacity_factor": cfg.capacity_factor,
-                   "kept_rows": A, "active_experts": E_act, "max_expert_rows": int(kept.max())},
+                   "kept_rows": A, "active_experts": E_act, "max_expert_rows": int(kept.max()),
+                   "routing": "expert_choice" if ec else "token_choice"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "stages": stage_info,

@@ -20,7 +20,8 @@ import workloads as W
 from oracle import moe_oracle as O
 from workloads.torch_io import act_torch_dtype, to_numpy, to_torch, upload_experts
 
-from parity import W_TOL, out_tol, refinement_margin, rel_err, route_differences, row_rel_err
+from parity import (W_TOL, ec_check_selection, ec_oracle_output, out_tol, refinement_margin, rel_err,
+                    route_differences, row_rel_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -188,4 +189,41 @@ def test_ep_local_share_full_size(name):
         ref[i] = O.expert_apply(X, experts[e][0], experts[e][1], cfg.activation, F)[0]
     err = row_rel_err(got, ref)
     print(f"  sampled {len(sample)} rows: max rel err {err:.3e}")
+    assert err <= out_tol(cfg)
+
+
+@pytest.mark.parametrize("name", ["deepseekv3_ec", "mixtral_ec", "deepseekmoe_ec"])
+def test_expert_choice_full_size(name):
+    """Expert-choice routing on the full-size workloads, as bench.py times it:
+    every expert's chosen tokens against the float64 oracle (near ties of the
+    C-th probability exempt), the gates, and 24 tokens' outputs."""
+    cfg = W.EC_CONFIGS[name]
+    T, E, D = cfg.num_tokens, cfg.num_experts, cfg.d_model
+    print(f"[expert choice full-size] {name}", flush=True)
+    C = M.moe_expert_choice_capacity(cfg)
+    inp = W.make_inputs(cfg, with_experts=False)
+    w13, w2, host = _experts(W.base_name(cfg))
+    dev = "cuda"
+    weights = dict(w_router=to_torch(inp.w_router, dev), w13=w13, w2=w2, ws13=to_torch(inp.ws13, dev),
+                   ws2=to_torch(inp.ws2, dev))
+    y = torch.empty((T, D), dtype=act_torch_dtype(cfg), device=dev)
+    tor = torch.empty(E * C, dtype=torch.int32, device=dev)
+    rw = torch.empty(E * C, dtype=torch.float32, device=dev)
+    uns = torch.empty(1, dtype=torch.int32, device=dev)
+    ws = M.workspace(cfg, M.MOE_OP_EXPERT_CHOICE, dev)
+    M.moe_expert_choice_forward(cfg, weights, to_torch(inp.x, dev), y, tor, rw, uns, ws)
+    torch.cuda.synchronize()
+    ref = O.expert_choice_route(inp.x, inp.w_router, C)
+    tg = to_numpy(tor).astype(np.int64)
+    ties = ec_check_selection(ref, tg, C)
+    gates = ref["probs"][tg, np.repeat(np.arange(E), C)]
+    assert rel_err(to_numpy(rw), gates) <= W_TOL
+    unsel = int(to_numpy(uns)[0])
+    assert unsel == T - np.unique(tg).size
+    print(f"  C={C}, experts with a near-tie exchange {ties}, tokens no expert took {unsel}")
+    rng = np.random.default_rng(99)
+    sample = np.sort(rng.choice(T, size=24, replace=False))
+    y_ref = ec_oracle_output(cfg, inp, tg, C, expert_weights=lambda e: host[e], rows=sample)
+    err = row_rel_err(to_numpy(y)[sample], y_ref)
+    print(f"  sampled {len(sample)} tokens: max rel err {err:.3e}")
     assert err <= out_tol(cfg)
