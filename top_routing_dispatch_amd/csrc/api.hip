@@ -282,7 +282,10 @@ struct FfnPlan {
 // smallest KS within 10% of the best estimate is taken (the partial sums
 // cost an extra pass; at most 256 MB of them).  The tile count is bounded on
 // the host from the row and group counts (the routing is known on the device
-// only).  MOE_GEMM_KSPLIT=<n> forces n where it divides the contraction
+// only); the bound is loose when there are many groups, so launches bounded
+// at 512 tiles or more are not split (measured: the Switch-shaped down
+// projection, bound 1,152 tiles for 768 real ones, ran 132 -> 176 us split
+// in two).  MOE_GEMM_KSPLIT=<n> forces n where it divides the contraction
 // (tuning aid and test hook).
 constexpr int kSplitUnits = 256;
 constexpr long long kMaxPartialBytes = 256LL << 20;
@@ -299,6 +302,7 @@ int pick_ksplit(int act, int cfg, int epi, int N, int K, int G, int max_rows, bo
   const int bm = gemm_ws_bm(c);
   const long long m_tiles = grouped ? max_rows / bm + (G < max_rows ? G : max_rows) : ceil_div(max_rows, bm);
   const long long tiles = m_tiles * ceil_div(N, cols);
+  if (tiles >= 2 * kSplitUnits) return 1;
   const long long row_bytes = (long long)(epi == EPI_SWIGLU ? 2 : 1) * N * 4;
   double est[4];
   double best = 1e300;
