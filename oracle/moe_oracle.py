@@ -27,6 +27,8 @@ step; the steps and their sources:
                                                     "别只比较 Top-k" [9,4,2,1] assignment example
   expert       each expert takes its top-C tokens   "Top-k 路由" Token-Choice vs Expert-Choice table;
    choice                                           "MoE 路由算法" page, 数学机理 (2)
+  backward     gradients with the routing held fixed  "Top-k 路由" 門控網路的梯度流 (note 3, 反向 line);
+                                                    Tiny-MoE §9
   EP layouts   rows per destination rank, received "Top-k 路由" 通訊拓撲：All-to-All figure;
                rows in expert-major order           "别只比较 Top-k" 按目标专家发送 / two-All-to-All
                                                     dispatcher section
@@ -325,6 +327,144 @@ def num_parameters_swiglu(d_model: int, d_ff: int) -> int:
     """Parameters of one bias-free SwiGLU expert: gate [F,D] + up [F,D] + down [D,F]."""
     shapes = [(d_ff, d_model), (d_ff, d_model), (d_model, d_ff)]
     return sum(a * b for a, b in shapes)
+
+
+# --------------------------------------------------------------------------
+# Backward pass
+# --------------------------------------------------------------------------
+def silu_grad(z: np.ndarray) -> np.ndarray:
+    """d silu / dz = sigmoid(z) (1 + z (1 - sigmoid(z)))."""
+    sg = sigmoid(z)
+    return sg * (1.0 + z * (1.0 - sg))
+
+
+def gelu_grad(z: np.ndarray) -> np.ndarray:
+    """d gelu / dz for the erf GELU: Phi(z) + z phi(z)."""
+    return 0.5 * (1.0 + erf(z / math.sqrt(2.0))) + z * np.exp(-0.5 * z * z) / math.sqrt(2.0 * math.pi)
+
+
+def gate_grad(s: np.ndarray, idx: np.ndarray, dw: np.ndarray, scoring: int, renormalize: int) -> np.ndarray:
+    """d loss / d s from d loss / d w through the combine weights of the
+    selected experts only (the selection itself is a constant: "Top-k 路由"
+    page, 門控網路的梯度流, note 3 and the 反向 line; Tiny-MoE §9).  For each
+    token, with g the weights' gradient on the selected experts:
+      raw probability  (w = p_sel):        ds = p * (g~ - <g~, p>), g~ = g on selected, 0 elsewhere
+      renormalised / k-way softmax:        ds_sel = w * (g - <g, w>), 0 elsewhere
+      sigmoid, renormalised:               ds_sel = a(1-a) * (g - <g, w>) / sum_sel a
+      sigmoid, raw:                        ds_sel = a(1-a) * g"""
+    T, E = s.shape
+    ds = np.zeros((T, E))
+    for t in range(T):
+        sel = idx[t]
+        g = dw[t]
+        if scoring == SOFTMAX_TOPK and not renormalize:
+            p = softmax(s[t])
+            gt = np.zeros(E)
+            np.add.at(gt, sel, g)
+            ds[t] = p * (gt - np.dot(gt, p))
+        elif scoring in (SOFTMAX_TOPK, TOPK_SOFTMAX):
+            w = gate_weights(s[t:t + 1], sel[None, :], scoring, 1)[0]
+            np.add.at(ds[t], sel, w * (g - np.dot(g, w)))
+        else:
+            a = sigmoid(s[t, sel])
+            if renormalize:
+                w = a / a.sum()
+                np.add.at(ds[t], sel, a * (1.0 - a) * (g - np.dot(g, w)) / a.sum())
+            else:
+                np.add.at(ds[t], sel, a * (1.0 - a) * g)
+    return ds
+
+
+def aux_loss_grad(s: np.ndarray, counts: np.ndarray, top_k: int, alpha: float, scoring: int) -> np.ndarray:
+    """d L_aux / d s for L_aux = alpha E sum_e f_e P_e with the assignment
+    shares f constant (they come from the discrete routing) and P_e the token
+    mean of the soft probabilities ("Top-k 路由" 負載均衡; Tiny-MoE §8-§9:
+    the soft importance carries the balance loss's gradient)."""
+    T, E = s.shape
+    f = np.asarray(counts, dtype=np.float64) / (T * top_k)
+    c = alpha * E * f / T                      # d L_aux / d p_hat[t, e], every token
+    if scoring == SIGMOID_BIAS:
+        a = sigmoid(s)
+        S = a.sum(axis=1, keepdims=True)
+        inner = (c[None, :] - (a * c[None, :]).sum(axis=1, keepdims=True) / S) / S
+        return inner * a * (1.0 - a)
+    p = softmax(s)
+    return p * (c[None, :] - (p * c[None, :]).sum(axis=1, keepdims=True))
+
+
+def backward(cfg, x, w_router, sel_bias, expert_weights: Callable[[int], tuple], shared: Sequence,
+             dy: np.ndarray, alpha: Optional[float] = None) -> Dict[str, np.ndarray]:
+    """Gradients of  <dy, y> + L_aux  (dy: the gradient of the loss with
+    respect to the layer output; L_aux the balance loss with coefficient
+    alpha) with respect to x, the router weight, every routed expert's w13 /
+    w2 and the shared experts' weights, the routing decisions held fixed
+    (Tiny-MoE §9: selected experts get the task gradient, the router gets it
+    through the selected weights and the balance-loss gradient through the
+    soft importance; indices, counts and capacity drops are constants).
+    Returns float64 dx [T, D], dw_router [E, D], dw13 {e: [n_mat F, D]},
+    dw2 {e: [D, F]}, dshared [(d_gate, d_up, d_down)], and the intermediates
+    dlogits [T, E], dw [T, k]."""
+    T, E, k, F = cfg.num_tokens, cfg.num_experts, cfg.top_k, cfg.d_ff
+    al = cfg.alpha if alpha is None else alpha
+    fw = forward(cfg, x, w_router, sel_bias, expert_weights, shared, alpha=al)
+    X = widen(x)
+    dY = widen(dy) if dy.dtype == np.uint16 else np.asarray(dy, dtype=np.float64)
+    dx = np.zeros_like(X)
+    row_of, tor, off = fw["row_of"], fw["token_of_row"], fw["offsets"]
+    # combine: y_t = sum_j w[t, j] Y[row(t, j)]
+    dw = np.zeros((T, k))
+    dYp = np.zeros_like(fw["y_perm"])
+    for t in range(T):
+        for j in range(k):
+            r = row_of[t, j]
+            if r >= 0:
+                dw[t, j] = np.dot(dY[t], fw["y_perm"][r])
+                dYp[r] = fw["w"][t, j] * dY[t]
+    dw13, dw2 = {}, {}
+    for e in range(E):
+        a_, b_ = int(off[e]), int(off[e + 1])
+        if b_ == a_:
+            continue
+        w13, w2 = expert_weights(e)
+        W13, W2 = widen(w13), widen(w2)
+        Xe = X[tor[a_:b_]]
+        dYe = dYp[a_:b_]
+        if cfg.activation == SWIGLU:
+            G, U = Xe @ W13[:F].T, Xe @ W13[F:].T
+            S = silu(G)
+            H = S * U
+            dH = dYe @ W2
+            dG = dH * U * silu_grad(G)
+            dU = dH * S
+            dw13[e] = np.concatenate([dG.T @ Xe, dU.T @ Xe], axis=0)
+            dXe = dG @ W13[:F] + dU @ W13[F:]
+        else:
+            Z = Xe @ W13.T
+            H = gelu(Z)
+            dH = dYe @ W2
+            dZ = dH * gelu_grad(Z)
+            dw13[e] = dZ.T @ Xe
+            dXe = dZ @ W13
+        dw2[e] = dYe.T @ H
+        np.add.at(dx, tor[a_:b_], dXe)
+    dsh = []
+    for g, u, d in shared:
+        Wg, Wu, Wd = widen(g), widen(u), widen(d)
+        G, U = X @ Wg.T, X @ Wu.T
+        S = silu(G)
+        H = S * U
+        dH = dY @ Wd
+        dG = dH * U * silu_grad(G)
+        dU = dH * S
+        dsh.append((dG.T @ X, dU.T @ X, dY.T @ H))
+        dx += dG @ Wg + dU @ Wu
+    s = fw["logits"]
+    dlogits = gate_grad(s, fw["idx"], dw, cfg.scoring, cfg.renormalize)
+    dlogits += aux_loss_grad(s, fw["counts"], k, al, cfg.scoring)
+    Wr = widen(w_router)
+    dx += dlogits @ Wr
+    return dict(dx=dx, dw_router=dlogits.T @ X, dw13=dw13, dw2=dw2, dshared=dsh, dlogits=dlogits, dw=dw,
+                forward=fw)
 
 
 # --------------------------------------------------------------------------

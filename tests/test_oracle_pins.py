@@ -624,3 +624,135 @@ def test_expert_choice_unchosen_token_gets_only_the_shared_path():
     for t, e in ((0, 0), (1, 1)):
         want = p[t, e] * O.expert_apply(x[t:t + 1], *ex[e], O.SWIGLU, F)[0] + ys[t]
         np.testing.assert_allclose(out["y"][t], want, rtol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# backward pass
+# --------------------------------------------------------------------------
+def _bw_case(name, T, D, E, k, F, **kw):
+    return W.MoEConfig(name, T, D, E, k, F, act_dtype=W.F32, router_dtype=W.F32, **kw)
+
+
+BW_CASES = [
+    _bw_case("bw_switch_like", 24, 12, 6, 1, 10, scoring=O.SOFTMAX_TOPK, renormalize=0, activation=O.GELU,
+             capacity_factor=1.0),
+    _bw_case("bw_softmax_renorm_shared", 20, 10, 5, 2, 8, scoring=O.SOFTMAX_TOPK, renormalize=1, num_shared=2,
+             d_ff_shared=6),
+    _bw_case("bw_topk_softmax", 18, 8, 4, 2, 7, scoring=O.TOPK_SOFTMAX),
+    _bw_case("bw_sigmoid_bias", 22, 9, 8, 3, 6, scoring=O.SIGMOID_BIAS, renormalize=1, num_shared=1, d_ff_shared=5),
+    _bw_case("bw_sigmoid_raw_capacity", 16, 8, 4, 2, 6, scoring=O.SIGMOID_BIAS, renormalize=0, capacity_factor=0.75),
+]
+
+
+def _bw_inputs(cfg, seed):
+    rng = np.random.default_rng(seed)
+    T, D, E, F = cfg.num_tokens, cfg.d_model, cfg.num_experts, cfg.d_ff
+    x = rng.standard_normal((T, D))
+    wr = rng.standard_normal((E, D)) * 0.5
+    b = rng.uniform(-0.1, 0.1, E) if cfg.scoring == O.SIGMOID_BIAS else None
+    ex = [(rng.standard_normal((cfg.n_mat * F, D)) * 0.3, rng.standard_normal((D, F)) * 0.3) for _ in range(E)]
+    sh = [tuple(rng.standard_normal(s) * 0.3 for s in ((cfg.d_ff_shared, D), (cfg.d_ff_shared, D),
+                                                        (D, cfg.d_ff_shared))) for _ in range(cfg.num_shared)]
+    dy = rng.standard_normal((T, D))
+    return x, wr, b, ex, sh, dy
+
+
+def _torch_grads(cfg, x, wr, ex, sh, dy, alpha, fw):
+    """The same loss written with torch float64 operations, the routing
+    decisions (indices, kept rows, counts) taken from the oracle's forward."""
+    import torch.nn.functional as Fn
+    tt = lambda a: torch.tensor(a, dtype=torch.float64, requires_grad=True)
+    X, Wr = tt(x), tt(wr)
+    W13 = [tt(a) for a, _ in ex]
+    W2 = [tt(b) for _, b in ex]
+    SH = [tuple(tt(m) for m in trip) for trip in sh]
+    T, E, k, F = cfg.num_tokens, cfg.num_experts, cfg.top_k, cfg.d_ff
+    s = X @ Wr.T
+    idx = torch.tensor(fw["idx"])
+    if cfg.scoring == O.SOFTMAX_TOPK:
+        g = torch.softmax(s, -1).gather(1, idx)
+        if cfg.renormalize:
+            g = g / g.sum(1, keepdim=True)
+    elif cfg.scoring == O.TOPK_SOFTMAX:
+        g = torch.softmax(s.gather(1, idx), -1)
+    else:
+        a = torch.sigmoid(s).gather(1, idx)
+        g = a / a.sum(1, keepdim=True) if cfg.renormalize else a
+    y = torch.zeros((T, cfg.d_model), dtype=torch.float64)
+    for t in range(T):
+        for j in range(k):
+            if fw["row_of"][t, j] < 0:
+                continue
+            e = int(fw["idx"][t, j])
+            xt = X[t:t + 1]
+            if cfg.activation == O.SWIGLU:
+                h = Fn.silu(xt @ W13[e][:F].T) * (xt @ W13[e][F:].T)
+            else:
+                h = Fn.gelu(xt @ W13[e].T)
+            y[t] = y[t] + g[t, j] * (h @ W2[e].T)[0]
+    for Wg, Wu, Wd in SH:
+        y = y + (Fn.silu(X @ Wg.T) * (X @ Wu.T)) @ Wd.T
+    if cfg.scoring == O.SIGMOID_BIAS:
+        a = torch.sigmoid(s)
+        ph = a / a.sum(1, keepdim=True)
+    else:
+        ph = torch.softmax(s, -1)
+    f = torch.tensor(fw["counts"], dtype=torch.float64) / (T * k)
+    loss = (torch.tensor(dy) * y).sum() + alpha * E * (f * ph.mean(0)).sum()
+    loss.backward()
+    return X.grad.numpy(), Wr.grad.numpy(), [w.grad for w in W13], [w.grad for w in W2], \
+        [tuple(m.grad for m in trip) for trip in SH]
+
+
+@pytest.mark.parametrize("cfg", BW_CASES, ids=lambda c: c.name)
+def test_backward_matches_torch_autograd(cfg):
+    """Every gradient of the oracle's backward against CPU torch autograd of
+    the same loss (float64), the routing held fixed."""
+    x, wr, b, ex, sh, dy = _bw_inputs(cfg, 7)
+    alpha = 0.05
+    g = O.backward(cfg, x, wr, b, lambda e: ex[e], sh, dy, alpha=alpha)
+    gx, gwr, g13, g2, gsh = _torch_grads(cfg, x, wr, ex, sh, dy, alpha, g["forward"])
+    np.testing.assert_allclose(g["dx"], gx, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(g["dw_router"], gwr, rtol=1e-10, atol=1e-12)
+    for e in range(cfg.num_experts):
+        want13 = g13[e].numpy() if g13[e] is not None else np.zeros_like(ex[e][0])
+        want2 = g2[e].numpy() if g2[e] is not None else np.zeros_like(ex[e][1])
+        np.testing.assert_allclose(g["dw13"].get(e, np.zeros_like(ex[e][0])), want13, rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(g["dw2"].get(e, np.zeros_like(ex[e][1])), want2, rtol=1e-10, atol=1e-12)
+    for got, want in zip(g["dshared"], gsh):
+        for a, b_ in zip(got, want):
+            np.testing.assert_allclose(a, b_.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_backward_finite_differences():
+    """Central differences of the scalar loss <dy, y> + L_aux, computed with
+    the oracle's forward, along random coordinates of x, the router weight and
+    one expert's matrices (steps small enough that no routing decision moves)."""
+    cfg = BW_CASES[1]
+    x, wr, b, ex, sh, dy = _bw_inputs(cfg, 8)
+    alpha = 0.05
+    g = O.backward(cfg, x, wr, b, lambda e: ex[e], sh, dy, alpha=alpha)
+
+    def loss(x_, wr_, ex_):
+        fw = O.forward(cfg, x_, wr_, b, lambda e: ex_[e], sh, alpha=alpha)
+        return float((dy * fw["y"]).sum() + fw["aux_loss"]), fw["idx"]
+
+    base_idx = g["forward"]["idx"]
+    rng = np.random.default_rng(3)
+    h = 1e-6
+    e0 = int(base_idx[0, 0])
+    checks = [("x", tuple(rng.integers(0, s) for s in x.shape)), ("wr", tuple(rng.integers(0, s) for s in wr.shape)),
+              ("w13", tuple(rng.integers(0, s) for s in ex[e0][0].shape)),
+              ("w2", tuple(rng.integers(0, s) for s in ex[e0][1].shape))]
+    for what, pos in checks:
+        vals = []
+        for sgn in (1, -1):
+            x_, wr_, ex_ = x.copy(), wr.copy(), [(a.copy(), c.copy()) for a, c in ex]
+            tgt = {"x": x_, "wr": wr_, "w13": ex_[e0][0], "w2": ex_[e0][1]}[what]
+            tgt[pos] += sgn * h
+            v, idx = loss(x_, wr_, ex_)
+            assert np.array_equal(idx, base_idx)
+            vals.append(v)
+        fd = (vals[0] - vals[1]) / (2 * h)
+        an = {"x": g["dx"], "wr": g["dw_router"], "w13": g["dw13"][e0], "w2": g["dw2"][e0]}[what][pos]
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (what, pos, fd, an)
