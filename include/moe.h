@@ -104,7 +104,8 @@ typedef enum {
   MOE_OP_SHARED_FFN = 3,      /* shared experts: max_rows = T, d_ff = S*F_s */
   MOE_OP_LOAD_STATS = 4,
   MOE_OP_LAYER = 5,
-  MOE_OP_EXPERT_CHOICE = 6    /* moe_expert_choice_forward */
+  MOE_OP_EXPERT_CHOICE = 6,   /* moe_expert_choice_forward */
+  MOE_OP_LAYER_BACKWARD = 7   /* moe_layer_backward */
 } moe_op;
 
 /* Workspace bytes that entry point `op` needs for `cfg` (host output).  A
@@ -263,6 +264,29 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const moe_weights* wei
                                    int32_t* counts, float alpha, float* stats, int32_t* dropped,
                                    void* ws, size_t ws_bytes, void* stream,
                                    void* const* stage_events);
+
+/* Backward pass of moe_layer_forward ("Top-k 路由" page, 門控網路的梯度流:
+ * the gradient flows through the selected experts' gate scores, unselected
+ * experts get none; "从 Dense FFN 到 MoE" §9: selected experts get the task
+ * gradient, the router gets it through the selected route weights and the
+ * balance loss's gradient through the soft importance).  The loss is
+ *   <dy, y> + L_aux,   L_aux = alpha * E * sum_e f_e P_e
+ * with the routing decisions (expert ids, capacity drops, the counts behind
+ * f) held fixed.  The call recomputes the forward (routing, permutation and
+ * the expert activations, in its workspace) and returns:
+ *   dx        [T, D] act_dtype out
+ *   dw_router [E, D] float32 out
+ *   dw13      [E, n_mat F, D] float32 out (rows as w13: SwiGLU gate then up)
+ *   dw2       [E, D, F] float32 out
+ *   dws13     [2 S F_s, D] float32 out, dws2 [D, S F_s] float32 out (NULL
+ *             iff S = 0)
+ * Experts without rows get zero gradients.  act_dtype must be MOE_BF16
+ * (MOE_ERR_UNSUPPORTED otherwise); intermediates are bf16 with float32
+ * accumulation.  ws: moe_workspace_size(MOE_OP_LAYER_BACKWARD) bytes (it holds
+ * transposed copies of the expert weights).  Deterministic. */
+moe_status moe_layer_backward(const moe_config* cfg, const moe_weights* weights, const void* x, const void* dy,
+                              float alpha, void* dx, float* dw_router, float* dw13, float* dw2, float* dws13,
+                              float* dws2, void* ws, size_t ws_bytes, void* stream);
 
 /* Expert-choice routing ("Top-k 路由" page, Token-Choice vs Expert-Choice
  * table: each expert picks its top-C tokens; "MoE 路由算法" page, 数学机理

@@ -760,3 +760,89 @@ def test_expert_choice_deterministic():
         torch.cuda.synchronize()
         outs.append(to_numpy(y))
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
+
+
+# --------------------------------------------------------------------------
+# backward pass
+# --------------------------------------------------------------------------
+BW_SHAPES = [
+    W.MoEConfig("bw_switch", 300, 128, 16, 1, 192, scoring=W.SOFTMAX_TOPK, renormalize=0, activation=W.GELU,
+                router_dtype=W.F32, capacity_factor=1.25),
+    W.MoEConfig("bw_mixtral", 256, 256, 8, 2, 320, scoring=W.TOPK_SOFTMAX, zipf_s=1.0),
+    W.MoEConfig("bw_deepseekmoe", 200, 128, 32, 6, 128, num_shared=2, d_ff_shared=64, scoring=W.SOFTMAX_TOPK,
+                renormalize=1),
+    W.MoEConfig("bw_deepseekv3", 333, 192, 64, 8, 128, num_shared=1, d_ff_shared=128, scoring=W.SIGMOID_BIAS,
+                renormalize=1, zipf_s=1.2),
+    W.MoEConfig("bw_sigmoid_raw_capacity", 150, 64, 8, 2, 96, scoring=W.SIGMOID_BIAS, renormalize=0,
+                capacity_factor=0.8),
+]
+# Gradient tolerance (none is stated for the backward): the forward's 2e-2
+# covers a chain of three bf16 roundings (H, y_perm, y); the input gradient
+# passes six (dy_perm, the recomputed G and U, dH, dG / dU, dx_perm, dx) and the
+# weight gradients up to five, so the bar scales to 4e-2.
+BW_TOL = 4e-2
+
+
+def tensor_rel_err(g: np.ndarray, r: np.ndarray) -> float:
+    """|gpu - ref| over max(|ref|, rms of the whole reference tensor): a
+    weight gradient of an expert with few rows is (near) rank-one, so one of
+    its rows can be a cancelling dot product whose own scale says nothing
+    about the tensor's."""
+    if r.size == 0:
+        return 0.0
+    rms = float(np.sqrt((r ** 2).mean()))
+    den = np.maximum(np.abs(r), rms if rms > 0 else 1.0)
+    return float((np.abs(g.astype(np.float64) - r) / den).max())
+
+
+@pytest.mark.parametrize("cfg", BW_SHAPES, ids=lambda c: c.name)
+def test_layer_backward_matches_oracle(cfg):
+    """Every gradient of moe_layer_backward (input, router, routed and shared
+    expert weights) against the float64 oracle backward on the same routing:
+    the input gradient row by row (each row is a token), each weight gradient
+    against the scale of its whole tensor (bf16 intermediates, float32
+    accumulation)."""
+    print(f"[backward] {cfg.name}", flush=True)
+    T, E, D, F, k = cfg.num_tokens, cfg.num_experts, cfg.d_model, cfg.d_ff, cfg.top_k
+    alpha = 0.05
+    inp = W.make_inputs(cfg)
+    rng = np.random.default_rng(5)
+    dy_h = W.f32_to_bf16_bits(rng.standard_normal((T, D), dtype=np.float32))
+    ref = O.backward(cfg, inp.x, inp.w_router, inp.sel_bias, lambda e: (inp.w13[e], inp.w2[e]), inp.shared, dy_h,
+                     alpha=alpha)
+    dl = DeviceLayer(cfg, inp)
+    got_route = dl.layer()
+    assert np.array_equal(got_route["idx"], ref["forward"]["idx"]), "routing differs (near tie): pick another seed"
+    dev = "cuda"
+    nF = cfg.n_mat * F
+    SF = cfg.num_shared * cfg.d_ff_shared
+    dx = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    dwr = torch.empty((E, D), dtype=torch.float32, device=dev)
+    dw13 = torch.empty((E, nF, D), dtype=torch.float32, device=dev)
+    dw2 = torch.empty((E, D, F), dtype=torch.float32, device=dev)
+    dws13 = torch.empty((2 * SF, D), dtype=torch.float32, device=dev) if SF else None
+    dws2 = torch.empty((D, SF), dtype=torch.float32, device=dev) if SF else None
+    ws = M.workspace(cfg, M.MOE_OP_LAYER_BACKWARD, dev)
+    M.moe_layer_backward(cfg, dl.weights, dl.x, to_torch(dy_h, dev), alpha, dx, dwr, dw13, dw2, dws13, dws2, ws)
+    torch.cuda.synchronize()
+    errs = {"dx": row_rel_err(to_numpy(dx), ref["dx"]), "dw_router": tensor_rel_err(to_numpy(dwr), ref["dw_router"])}
+    g13, g2 = to_numpy(dw13), to_numpy(dw2)
+    e13 = e2 = 0.0
+    for e in range(E):
+        r13 = ref["dw13"].get(e, np.zeros((nF, D)))
+        r2 = ref["dw2"].get(e, np.zeros((D, F)))
+        if e in ref["dw13"]:
+            e13 = max(e13, tensor_rel_err(g13[e], r13))
+            e2 = max(e2, tensor_rel_err(g2[e], r2))
+        else:
+            assert (g13[e] == 0).all() and (g2[e] == 0).all(), f"expert {e} without rows has a gradient"
+    errs["dw13"], errs["dw2"] = e13, e2
+    if SF:
+        rg = np.concatenate([np.concatenate([a for a, _, _ in ref["dshared"]], axis=0),
+                             np.concatenate([b for _, b, _ in ref["dshared"]], axis=0)], axis=0)
+        rd = np.concatenate([c for _, _, c in ref["dshared"]], axis=1)
+        errs["dws13"] = tensor_rel_err(to_numpy(dws13), rg)
+        errs["dws2"] = tensor_rel_err(to_numpy(dws2), rd)
+    print("  " + ", ".join(f"{n} {v:.2e}" for n, v in errs.items()))
+    for n, v in errs.items():
+        assert v <= BW_TOL, f"{n}: {v:.3e}"

@@ -21,11 +21,12 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_SOFTMAX_TOPK, MOE_TOPK_SOFTMAX, MOE_SIGMOID_BIAS = 0, 1, 2
 MOE_SWIGLU, MOE_GELU = 0, 1
 (MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_EXPERT_FFN, MOE_OP_SHARED_FFN,
- MOE_OP_LOAD_STATS, MOE_OP_LAYER, MOE_OP_EXPERT_CHOICE) = range(7)
+ MOE_OP_LOAD_STATS, MOE_OP_LAYER, MOE_OP_EXPERT_CHOICE, MOE_OP_LAYER_BACKWARD) = range(8)
 
 EXPORTED = ("moe_capacity", "moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn",
             "moe_combine", "moe_load_stats", "moe_layer_forward", "moe_layer_forward_timed",
-            "moe_expert_choice_capacity", "moe_expert_choice_forward", "moe_ep_send_layout", "moe_ep_recv_layout",
+            "moe_layer_backward", "moe_expert_choice_capacity", "moe_expert_choice_forward", "moe_ep_send_layout",
+            "moe_ep_recv_layout",
             "moe_status_string", "moe_last_error")
 STAGES = ("router_logits", "route_select", "permute", "expert_gate_up", "expert_down", "shared_gate_up",
           "shared_down", "combine", "load_stats")
@@ -78,6 +79,8 @@ def lib() -> ctypes.CDLL:
             "moe_layer_forward": [cfgp, ctypes.POINTER(moe_weights), vp, vp, vp, vp, vp, f32, vp, vp, vp, sz, vp],
             "moe_layer_forward_timed": [cfgp, ctypes.POINTER(moe_weights), vp, vp, vp, vp, vp, f32, vp, vp, vp, sz,
                                         vp, ctypes.POINTER(vp)],
+            "moe_layer_backward": [cfgp, ctypes.POINTER(moe_weights), vp, vp, f32, vp, vp, vp, vp, vp, vp, vp, sz,
+                                   vp],
             "moe_expert_choice_capacity": [cfgp, ctypes.POINTER(i32)],
             "moe_expert_choice_forward": [cfgp, ctypes.POINTER(moe_weights), vp, vp, vp, vp, vp, vp, sz, vp,
                                           ctypes.POINTER(vp)],
@@ -203,6 +206,19 @@ def moe_layer_forward_timed(cfg, weights: dict, x, y, topk_idx=None, topk_w=None
         ctypes.byref(c), ctypes.byref(w), _ptr(x), _ptr(y), _ptr(topk_idx), _ptr(topk_w), _ptr(counts),
         float(alpha), _ptr(stats), _ptr(dropped), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream),
         arr))
+
+
+def moe_layer_backward(cfg, weights: dict, x, dy, alpha, dx, dw_router, dw13, dw2, dws13=None, dws2=None, ws=None,
+                       stream=None):
+    """Gradients of <dy, y> + alpha-weighted balance loss, the routing fixed."""
+    c = make_config(cfg)
+    w = moe_weights()
+    for name, _ in moe_weights._fields_:
+        t = weights.get(name)
+        setattr(w, name, None if t is None else t.data_ptr())
+    _check("moe_layer_backward", lib().moe_layer_backward(
+        ctypes.byref(c), ctypes.byref(w), _ptr(x), _ptr(dy), float(alpha), _ptr(dx), _ptr(dw_router), _ptr(dw13),
+        _ptr(dw2), _ptr(dws13), _ptr(dws2), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
 
 
 def moe_expert_choice_capacity(cfg) -> int:

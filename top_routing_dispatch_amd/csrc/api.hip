@@ -541,6 +541,65 @@ moe_status aux_stream(AuxStream** out) {
   return MOE_OK;
 }
 
+// Backward -----------------------------------------------------------------
+struct BwLayout {
+  size_t fwd, y, dyp, gu, dh, dgu, dxp, w13t, w2t, ones, dw, dlogits, dxr, pre, gus, dhs, dgus, dxs, ws13t, ws2t,
+      total;
+};
+
+BwLayout bw_layout(const moe_config* c, const Derived& d) {
+  BwLayout B{};
+  const size_t T = c->num_tokens, E = c->num_experts, k = c->top_k, D = c->d_model, F = c->d_ff;
+  const size_t A = d.rows_cap, nF = (c->activation == SWIGLU ? 2 : 1) * F;
+  const size_t SF = (size_t)c->num_shared * c->d_ff_shared;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o += carve(bytes); return at; };
+  B.fwd = take(layer_layout(c, d).total);
+  B.y = take(T * D * 2);
+  B.dyp = take(A * D * 2);
+  B.gu = take(A * nF * 2);
+  B.dh = take(A * F * 2);
+  B.dgu = take(A * nF * 2);
+  B.dxp = take(A * D * 2);
+  B.w13t = take(E * D * nF * 2);
+  B.w2t = take(E * F * D * 2);
+  B.ones = take(T * k * 4);
+  B.dw = take(T * k * 4);
+  B.dlogits = take(T * E * 4);
+  B.dxr = take(T * D * 4);
+  B.pre = take(2 * (E + 1) * 4);
+  B.gus = take(T * 2 * SF * 2);
+  B.dhs = take(T * SF * 2);
+  B.dgus = take(T * 2 * SF * 2);
+  B.dxs = take(T * D * 2);
+  B.ws13t = take(2 * SF * D * 2);
+  B.ws2t = take(SF * D * 2);
+  B.total = o;
+  return B;
+}
+
+// One bf16 product C [rows, N] = A [rows, K] B_g^T for groups given by
+// offsets (or one group of `rows` rows), store epilogue, on the kernel the
+// forward would pick for this contraction.
+moe_status bw_gemm(const char* what, const void* A, const int32_t* a_rows, int lda, const void* B, long long bstride,
+                   void* C, int ldc, int rows, int N, int K, int G, const int32_t* offsets, int32_t* prefix,
+                   hipStream_t s) {
+  const int cfg = pick_cfg(BF16, K, rows, G, false);
+  GroupedGemm g{};
+  g.A = A; g.a_rows = a_rows; g.lda = lda;
+  g.B = B; g.b_group_stride = bstride;
+  g.C = C; g.ldc = ldc;
+  g.M_max = rows; g.N = N; g.K = K;
+  g.G = G; g.offsets = offsets; g.tile_prefix = nullptr;
+  g.epilogue = EPI_STORE_ACT;
+  if (offsets != nullptr) {
+    MOE_TRY_HIP("tile prefix", launch_tile_prefix(offsets, G, cfg_bm(BF16, cfg), prefix, s));
+    g.tile_prefix = prefix;
+  }
+  MOE_TRY_HIP(what, launch_gemm(BF16, cfg, g, s));
+  return MOE_OK;
+}
+
 // Expert choice --------------------------------------------------------------
 int ec_capacity(const moe_config* c) {
   if (c->num_tokens <= 0) return 0;
@@ -634,6 +693,7 @@ moe_status moe_workspace_size(const moe_config* cfg, int32_t op, size_t* bytes) 
       MOE_TRY(validate_ec(cfg));
       *bytes = ec_layout(cfg).total;
       break;
+    case MOE_OP_LAYER_BACKWARD: *bytes = bw_layout(cfg, d).total; break;
     default: return MOE_ERR_INVALID_ARGUMENT;
   }
   return MOE_OK;
@@ -888,6 +948,122 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const moe_weights* wt,
     MOE_TRY_HIP("load stats", launch_load_stats(sa, s));
     MOE_TRY(mark(ev, MOE_STAGE_LOAD_STATS, 1, s));
   }
+  return MOE_OK;
+}
+
+moe_status moe_layer_backward(const moe_config* cfg, const moe_weights* wt, const void* x, const void* dy,
+                              float alpha, void* dx, float* dw_router, float* dw13, float* dw2, float* dws13,
+                              float* dws2, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(validate_config(cfg));
+  if (cfg->act_dtype != BF16) return MOE_ERR_UNSUPPORTED;
+  if (wt == nullptr || wt->w_router == nullptr || wt->w13 == nullptr || wt->w2 == nullptr)
+    return MOE_ERR_INVALID_ARGUMENT;
+  const bool shared = cfg->num_shared > 0;
+  if (shared && (wt->ws13 == nullptr || wt->ws2 == nullptr || dws13 == nullptr || dws2 == nullptr))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (dw_router == nullptr || dw13 == nullptr || dw2 == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+  const bool any = cfg->num_tokens > 0;
+  if (any && (x == nullptr || dy == nullptr || dx == nullptr || ws == nullptr)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!opt_aligned(x) || !opt_aligned(dy) || !opt_aligned(dx) || !aligned16(dw_router) || !aligned16(dw13) ||
+      !aligned16(dw2) || !opt_aligned(dws13) || !opt_aligned(dws2) || !opt_aligned(ws) ||
+      !aligned16(wt->w_router) || !aligned16(wt->w13) || !aligned16(wt->w2) || !opt_aligned(wt->ws13) ||
+      !opt_aligned(wt->ws2))
+    return MOE_ERR_INVALID_ARGUMENT;
+  Derived d;
+  derive(cfg, &d);
+  const BwLayout B = bw_layout(cfg, d);
+  if (ws_bytes < B.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int T = cfg->num_tokens, E = cfg->num_experts, k = cfg->top_k, D = cfg->d_model, F = cfg->d_ff;
+  const int A = d.rows_cap;
+  const bool swiglu = cfg->activation == SWIGLU;
+  const int nF = (swiglu ? 2 : 1) * F;
+  const int SF = cfg->num_shared * cfg->d_ff_shared;
+  if (!any) {
+    // no tokens: every gradient is zero
+    MOE_TRY_HIP("zero", launch_fill_f32(dw_router, 0.0f, (long long)E * D, s));
+    MOE_TRY_HIP("zero", launch_fill_f32(dw13, 0.0f, (long long)E * nF * D, s));
+    MOE_TRY_HIP("zero", launch_fill_f32(dw2, 0.0f, (long long)E * D * F, s));
+    if (shared) {
+      MOE_TRY_HIP("zero", launch_fill_f32(dws13, 0.0f, 2LL * SF * D, s));
+      MOE_TRY_HIP("zero", launch_fill_f32(dws2, 0.0f, (long long)D * SF, s));
+    }
+    return MOE_OK;
+  }
+  // forward recomputation: routing, permutation, expert activations
+  void* fws = at<void>(ws, B.fwd);
+  const Layout L = layer_layout(cfg, d);
+  MOE_TRY(moe_layer_forward_timed(cfg, wt, x, at<void>(ws, B.y), nullptr, nullptr, nullptr, alpha, nullptr, nullptr,
+                                  fws, L.total, stream, nullptr));
+  const int32_t* idx = at<int32_t>(fws, L.idx);
+  const float* tw = at<float>(fws, L.w);
+  const int32_t* counts = at<int32_t>(fws, L.counts);
+  const int32_t* off = at<int32_t>(fws, L.offsets);
+  const int32_t* row_of = at<int32_t>(fws, L.row_of);
+  const int32_t* tor = at<int32_t>(fws, L.tor);
+  const bf16_t* h = at<bf16_t>(fws, L.h);
+  const bf16_t* yperm = at<bf16_t>(fws, L.yperm);
+  const float* logits = at<float>(fws, L.logits);
+  bf16_t* dyp = at<bf16_t>(ws, B.dyp);
+  bf16_t* gu = at<bf16_t>(ws, B.gu);
+  bf16_t* dh = at<bf16_t>(ws, B.dh);
+  bf16_t* dgu = at<bf16_t>(ws, B.dgu);
+  bf16_t* dxp = at<bf16_t>(ws, B.dxp);
+  bf16_t* w13t = at<bf16_t>(ws, B.w13t);
+  bf16_t* w2t = at<bf16_t>(ws, B.w2t);
+  float* dwt = at<float>(ws, B.dw);
+  float* dlog = at<float>(ws, B.dlogits);
+  int32_t* pre = at<int32_t>(ws, B.pre);
+  const bf16_t* xb = static_cast<const bf16_t*>(x);
+  const bf16_t* dyb = static_cast<const bf16_t*>(dy);
+
+  // combine: dw[t, j] = <dy[t], y_perm[row]>, dy_perm[row] = w[t, j] dy[t]
+  MOE_TRY_HIP("combine backward", launch_bw_combine(dyb, yperm, row_of, tw, T, k, D, dwt, dyp, s));
+  // routed experts: weights transposed for the data-gradient products
+  MOE_TRY_HIP("transpose w2", launch_transpose_bf16(static_cast<const bf16_t*>(wt->w2), w2t, E, D, F, s));
+  MOE_TRY_HIP("transpose w13", launch_transpose_bf16(static_cast<const bf16_t*>(wt->w13), w13t, E, nF, D, s));
+  if (A > 0) {
+    MOE_TRY(bw_gemm("expert gate/up (recomputed)", x, tor, D, wt->w13, (long long)nF * D, gu, nF, A, nF, D, E, off,
+                    pre, s));
+    MOE_TRY(bw_gemm("expert dH", dyp, nullptr, D, w2t, (long long)F * D, dh, F, A, F, D, E, off, pre, s));
+    MOE_TRY_HIP("activation backward", launch_bw_act(gu, dh, dgu, off + E, A, F, swiglu, s));
+    MOE_TRY(bw_gemm("expert dX", dgu, nullptr, nF, w13t, (long long)D * nF, dxp, D, A, D, nF, E, off, pre + (E + 1),
+                    s));
+  }
+  MOE_TRY_HIP("expert dW2", launch_wgrad(dyp, D, h, F, nullptr, off, E, A, D, F, dw2, s));
+  MOE_TRY_HIP("expert dW13", launch_wgrad(dgu, nF, xb, D, tor, off, E, A, nF, D, dw13, s));
+  // shared experts (weight 1, every token)
+  bf16_t* dxs = nullptr;
+  if (shared) {
+    bf16_t* gus = at<bf16_t>(ws, B.gus);
+    bf16_t* dhs = at<bf16_t>(ws, B.dhs);
+    bf16_t* dgus = at<bf16_t>(ws, B.dgus);
+    bf16_t* ws13t = at<bf16_t>(ws, B.ws13t);
+    bf16_t* ws2t = at<bf16_t>(ws, B.ws2t);
+    dxs = at<bf16_t>(ws, B.dxs);
+    const bf16_t* hs = at<bf16_t>(fws, L.h_shared);
+    MOE_TRY_HIP("transpose ws2", launch_transpose_bf16(static_cast<const bf16_t*>(wt->ws2), ws2t, 1, D, SF, s));
+    MOE_TRY_HIP("transpose ws13", launch_transpose_bf16(static_cast<const bf16_t*>(wt->ws13), ws13t, 1, 2 * SF, D, s));
+    MOE_TRY(bw_gemm("shared gate/up (recomputed)", x, nullptr, D, wt->ws13, 0, gus, 2 * SF, T, 2 * SF, D, 1, nullptr,
+                    nullptr, s));
+    MOE_TRY(bw_gemm("shared dH", dy, nullptr, D, ws2t, 0, dhs, SF, T, SF, D, 1, nullptr, nullptr, s));
+    MOE_TRY_HIP("shared activation backward", launch_bw_act(gus, dhs, dgus, nullptr, T, SF, true, s));
+    MOE_TRY(bw_gemm("shared dX", dgus, nullptr, 2 * SF, ws13t, 0, dxs, D, T, D, 2 * SF, 1, nullptr, nullptr, s));
+    MOE_TRY_HIP("shared dW2", launch_wgrad(dyb, D, hs, SF, nullptr, nullptr, 1, T, D, SF, dws2, s));
+    MOE_TRY_HIP("shared dW13", launch_wgrad(dgus, 2 * SF, xb, D, nullptr, nullptr, 1, T, 2 * SF, D, dws13, s));
+  }
+  // router: d loss / d logits, then its weight and input gradients
+  MOE_TRY_HIP("router backward", launch_router_grad(logits, idx, tw, dwt, counts, T, E, k, cfg->scoring,
+                                                    cfg->renormalize, alpha, dlog, s));
+  MOE_TRY_HIP("router dW", launch_gemm_f32_strided(dlog, 1, E, x, true, D, 1, E, D, T, dw_router, s));
+  float* dxr = at<float>(ws, B.dxr);
+  MOE_TRY_HIP("router dx", launch_gemm_f32_strided(dlog, E, 1, wt->w_router, cfg->router_dtype == BF16, D, 1, T, D,
+                                                   E, dxr, s));
+  // dx = sum of the token's expert rows (weight 1) + shared + router
+  float* ones = at<float>(ws, B.ones);
+  MOE_TRY_HIP("ones", launch_fill_f32(ones, 1.0f, (long long)T * k, s));
+  MOE_TRY_HIP("dx rows", launch_combine(dxp, row_of, ones, dxs, dx, T, k, D, BF16, s));
+  MOE_TRY_HIP("dx router", launch_add_f32_to_bf16(static_cast<bf16_t*>(dx), dxr, (long long)T * D, s));
   return MOE_OK;
 }
 

@@ -325,6 +325,21 @@ hipError_t launch_ec_route(const float* logits, int T, int E, int C, float* pT, 
 hipError_t launch_ec_combine(const void* y_perm, const float* pT, const uint32_t* selbits, const int32_t* selpre,
                              const void* y_shared, void* y, int T, int E, int C, int D, int act_dtype,
                              int32_t* unselected, hipStream_t s);
+// Backward pass kernels (backward.hip).
+hipError_t launch_transpose_bf16(const bf16_t* in, bf16_t* out, int G, int R, int C, hipStream_t s);
+hipError_t launch_bw_combine(const bf16_t* dy, const bf16_t* yp, const int32_t* row_of, const float* tw, int T, int k,
+                             int D, float* dw, bf16_t* dyp, hipStream_t s);
+hipError_t launch_bw_act(const bf16_t* gu, const bf16_t* dh, bf16_t* dgu, const int32_t* rows_valid, int rows_max,
+                         int F, bool swiglu, hipStream_t s);
+hipError_t launch_wgrad(const bf16_t* A, int lda, const bf16_t* B, int ldb, const int32_t* b_rows,
+                        const int32_t* offsets, int G, int rows_max, int M, int N, float* C, hipStream_t s);
+hipError_t launch_router_grad(const float* logits, const int32_t* idx, const float* tw, const float* dw,
+                              const int32_t* counts, int T, int E, int k, int scoring, int renormalize, float alpha,
+                              float* dlogits, hipStream_t s);
+hipError_t launch_gemm_f32_strided(const float* A, long long am, long long ak, const void* B, bool b_bf16,
+                                   long long bk, long long bn, int M, int N, int K, float* C, hipStream_t s);
+hipError_t launch_add_f32_to_bf16(bf16_t* y, const float* add, long long n, hipStream_t s);
+hipError_t launch_fill_f32(float* p, float v, long long n, hipStream_t s);
 // Expert-parallel send / receive layouts (ep.hip).
 hipError_t launch_ep_send_layout(const int32_t* offsets, int E, int R, int32_t* send_counts, int32_t* send_offsets,
                                  hipStream_t s);
