@@ -182,6 +182,8 @@ def main():
                          "<model>_ep8_local: one GPU's share of an 8-rank expert-parallel layer; "
                          "<model>_ec: the model's layer with expert-choice routing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time moe_layer_backward (forward recomputed inside) instead of the forward")
     ap.add_argument("--cpu-sample-tokens", type=int, default=None)
     ap.add_argument("--copy-calibration", type=int, default=None, metavar="MIB",
                     help="only run a plain copy of MIB MiB --steps times (counter calibration)")
@@ -197,6 +199,9 @@ def main():
 
     if args.config in W.EP_CONFIGS:
         run_ep_share(args, W.EP_CONFIGS[args.config])
+        return
+    if args.backward:
+        run_backward(args, W.CONFIGS.get(args.config) or W.DECODE_CONFIGS[args.config])
         return
 
     import torch
@@ -425,6 +430,71 @@ def run_ep_share(args, ep):
                    "received_rows": total, "d_model": D, "d_ff": F},
         "roofline": roof,
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def run_backward(args, cfg):
+    """One step = moe_layer_backward over the batch: the forward recomputed in
+    its workspace, then the gradients of x, the router and every expert weight."""
+    import torch
+    import top_routing_dispatch_amd as M
+    from workloads.torch_io import to_torch, upload_experts
+
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    inp = W.make_inputs(cfg, with_experts=False)
+    x = to_torch(inp.x, dev)
+    w13, w2, _ = upload_experts(cfg, dev)
+    weights = dict(w_router=to_torch(inp.w_router, dev), sel_bias=to_torch(inp.sel_bias, dev), w13=w13, w2=w2,
+                   ws13=to_torch(inp.ws13, dev), ws2=to_torch(inp.ws2, dev))
+    T, E, D, F, k = cfg.num_tokens, cfg.num_experts, cfg.d_model, cfg.d_ff, cfg.top_k
+    nF, SF = cfg.n_mat * F, cfg.num_shared * cfg.d_ff_shared
+    g = torch.Generator(device="cpu").manual_seed(1)
+    dy = torch.randn((T, D), generator=g).to(torch.bfloat16).to(dev)
+    dx = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    dwr = torch.empty((E, D), dtype=torch.float32, device=dev)
+    dw13 = torch.empty((E, nF, D), dtype=torch.float32, device=dev)
+    dw2 = torch.empty((E, D, F), dtype=torch.float32, device=dev)
+    dws13 = torch.empty((2 * SF, D), dtype=torch.float32, device=dev) if SF else None
+    dws2 = torch.empty((D, SF), dtype=torch.float32, device=dev) if SF else None
+    ws = M.workspace(cfg, M.MOE_OP_LAYER_BACKWARD, dev)
+
+    def step():
+        M.moe_layer_backward(cfg, weights, x, dy, cfg.alpha, dx, dwr, dw13, dw2, dws13, dws2, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a_ev.record()
+    for _ in range(args.steps):
+        step()
+    b_ev.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = wall * 1e3 / args.steps
+    A = T * k if cfg.capacity_factor <= 0 else M.moe_capacity(cfg)[1]
+    # expert GEMM work of the call (forward recomputation included): forward
+    # (n_mat + 1) products, gate/up recomputed (n_mat), dH (1), dX (n_mat),
+    # dW2 (1), dW13 (n_mat); shared experts the same over T rows
+    flops = 2.0 * A * D * F * (4 * cfg.n_mat + 3) + 2.0 * T * D * SF * (4 * 2 + 3)
+    ev_ms = a_ev.elapsed_time(b_ev) / args.steps
+    roof = dict(bound="mfma", achieved=round(flops / (ev_ms * 1e-3) / 1e12, 2), peak=MFMA_BF16_TFLOPS,
+                unit="TFLOP/s", frac=round(flops / (ev_ms * 1e-3) / 1e12 / MFMA_BF16_TFLOPS, 4),
+                kernel="layer backward (expert GEMM work, forward recomputation included)", ms=round(ev_ms, 4),
+                traffic=None)
+    line = {
+        "metric": "MoE-layer tokens/sec at 1 GPU; % HBM roofline (route/permute) and % MFMA peak",
+        "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name + "_backward", "tokens": T, "d_model": D, "experts": E, "top_k": k,
+                   "d_ff": F, "shared": cfg.num_shared, "d_ff_shared": cfg.d_ff_shared,
+                   "expert_gemm_flops_per_step": flops},
+        "roofline": roof,
+        "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
 

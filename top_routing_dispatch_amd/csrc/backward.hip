@@ -105,90 +105,122 @@ __global__ __launch_bounds__(256) void bw_act_kernel(const bf16_t* __restrict__ 
   }
 }
 
-// Eight bf16 values from p, the first `valid` of them read (valid may be <= 0).
-__device__ __forceinline__ uint4 load8_masked(const bf16_t* p, int valid) {
-  uint32_t w[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint32_t lo = 2 * q < valid ? p[2 * q] : 0u;
-    const uint32_t hi = 2 * q + 1 < valid ? p[2 * q + 1] : 0u;
-    w[q] = lo | (hi << 16);
-  }
-  return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
 // ---------------------------------------------------------------------------
 // C_g[m, n] = sum over rows r of group g of A[r, m] * B[b_row(r), n]
-// (float32 out, [G][M][N]); A [rows][lda] and B [*][ldb] bf16.  b_rows (or
-// NULL) maps a row to the B row it reads.  offsets [G+1] (NULL: one group of
-// rows_max rows).  64x64 tile per workgroup, 32 rows per slice; each slice is
-// stored transposed in LDS ([m][r], [n][r]) so that the MFMA operands (8
-// consecutive rows of one column) are 16-byte reads.  Four waves, 32x32 each
-// (2x2 blocks of v_mfma_f32_16x16x32_bf16).  Empty groups write zeros.
+// (float32 out, [G][M][N]); A [rows][lda] and B [*][ldb] bf16 (lda, ldb,
+// M, N multiples of 4).  b_rows (or NULL) maps a row to the B row it reads.
+// offsets [G+1] (NULL: one group of rows_max rows).  128x128 tile per
+// workgroup, 32 rows per slice.  A slice is staged transposed in LDS ([m][r],
+// [n][r]) so that the MFMA operands (8 consecutive rows of one column) are
+// 16-byte reads: each thread loads an 8-row x 4-column block of A or B (8-byte
+// loads), transposes it in registers and stores four 16-byte columns.  The
+// next slice's loads are in flight while the current one is multiplied (two
+// LDS buffers, one barrier per slice).  Four waves of 64x64 (4x4 blocks of
+// v_mfma_f32_16x16x32_bf16).  Empty groups write zeros.
+constexpr int kWgP = 40;                 // LDS row pitch in bf16 (32 rows + pad)
+
+struct WgStage {
+  uint2 v[8];
+};
+
+// thread -> operand (0: A, 1: B), 8-row group, 4-column group of the slice
+__device__ __forceinline__ void wg_load(WgStage& st, const bf16_t* __restrict__ P, int ld,
+                                        const int32_t* __restrict__ rows_map, int r_base, int r_hi, int c_base, int C) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = r_base + i;
+    uint2 q = make_uint2(0u, 0u);
+    if (r < r_hi && c_base < C) {
+      const long long pr = rows_map ? (long long)rows_map[r] : (long long)r;
+      q = *reinterpret_cast<const uint2*>(P + pr * ld + c_base);
+    }
+    st.v[i] = q;
+  }
+}
+
+__device__ __forceinline__ void wg_store(const WgStage& st, bf16_t* lds_cols, int r_off) {
+  // column c of the block gets rows 0..7: dword j = row 2j | row 2j+1 << 16
+  uint4 o[4];
+  uint32_t* w = reinterpret_cast<uint32_t*>(o);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint2 a = st.v[2 * j], b = st.v[2 * j + 1];
+    w[0 * 4 + j] = (a.x & 0xffffu) | (b.x << 16);
+    w[1 * 4 + j] = (a.x >> 16) | (b.x & 0xffff0000u);
+    w[2 * 4 + j] = (a.y & 0xffffu) | (b.y << 16);
+    w[3 * 4 + j] = (a.y >> 16) | (b.y & 0xffff0000u);
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) *reinterpret_cast<uint4*>(lds_cols + c * kWgP + r_off) = o[c];
+}
+
 __global__ __launch_bounds__(256) void wgrad_kernel(const bf16_t* __restrict__ A, int lda,
                                                     const bf16_t* __restrict__ B, int ldb,
                                                     const int32_t* __restrict__ b_rows,
                                                     const int32_t* __restrict__ offsets, int rows_max, int M, int N,
                                                     float* __restrict__ C) {
-  __shared__ __attribute__((aligned(16))) bf16_t As[64][40];   // [m][r], 32 rows + pad
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[64][40];
+  __shared__ __attribute__((aligned(16))) bf16_t S[2][2][128 * kWgP];   // [buffer][A / B][col][row]
   const int g = blockIdx.z;
-  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  const int m0 = blockIdx.y * 128, n0 = blockIdx.x * 128;
   const int r_lo = offsets ? offsets[g] : 0;
   const int r_hi = offsets ? offsets[g + 1] : rows_max;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  floatx4_t acc[2][2];
+  // staging role: threads 0..127 load A, 128..255 load B; (row group, column group)
+  const int op = threadIdx.x >> 7;
+  const int sid = threadIdx.x & 127;
+  const int rg = sid >> 5;                 // 4 groups of 8 rows
+  const int cg = (sid & 31) * 4;           // 32 groups of 4 columns
+  const bf16_t* P = op ? B : A;
+  const int ld = op ? ldb : lda;
+  const int32_t* rmap = op ? b_rows : nullptr;
+  const int c_base = (op ? n0 : m0) + cg;
+  const int C_lim = op ? N : M;
+
+  floatx4_t acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) acc[i][j][q] = 0.0f;
-  // loader: thread -> (row lr, 8 columns at lc)
-  const int lr = threadIdx.x >> 3, lc = (threadIdx.x & 7) * 8;
+
+  WgStage st;
+  int buf = 0;
+  if (r_lo < r_hi) {
+    wg_load(st, P, ld, rmap, r_lo + rg * 8, r_hi, c_base, C_lim);
+    wg_store(st, &S[0][op][cg * kWgP], rg * 8);
+  }
+  __syncthreads();
+  const int fc = lane & 15, fk = (lane >> 4) * 8;
   for (int r0 = r_lo; r0 < r_hi; r0 += 32) {
-    const int r = r0 + lr;
-    uint4 av = make_uint4(0u, 0u, 0u, 0u), bv = make_uint4(0u, 0u, 0u, 0u);
-    if (r < r_hi) {
-      if (m0 + lc + 8 <= M) av = *reinterpret_cast<const uint4*>(A + (long long)r * lda + m0 + lc);
-      else av = load8_masked(A + (long long)r * lda + m0 + lc, M - (m0 + lc));
-      const long long br = b_rows ? (long long)b_rows[r] : (long long)r;
-      if (n0 + lc + 8 <= N) bv = *reinterpret_cast<const uint4*>(B + br * ldb + n0 + lc);
-      else bv = load8_masked(B + br * ldb + n0 + lc, N - (n0 + lc));
-    }
-    __syncthreads();                                   // the previous slice's reads are done
-    const uint32_t aw[4] = {av.x, av.y, av.z, av.w}, bw4[4] = {bv.x, bv.y, bv.z, bv.w};
+    const bool more = r0 + 32 < r_hi;
+    if (more) wg_load(st, P, ld, rmap, r0 + 32 + rg * 8, r_hi, c_base, C_lim);   // next slice in flight
+    const bf16_t* As = S[buf][0];
+    const bf16_t* Bs = S[buf][1];
+    bf16x8_t fa[4], fb[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      As[lc + 2 * q][lr] = (bf16_t)(aw[q] & 0xffffu);
-      As[lc + 2 * q + 1][lr] = (bf16_t)(aw[q] >> 16);
-      Bs[lc + 2 * q][lr] = (bf16_t)(bw4[q] & 0xffffu);
-      Bs[lc + 2 * q + 1][lr] = (bf16_t)(bw4[q] >> 16);
-    }
-    __syncthreads();
-    // lane: column (lane & 15) of a 16-block, rows (lane >> 4) * 8 .. + 7 of the slice
-    const int fc = lane & 15, fk = (lane >> 4) * 8;
-    bf16x8_t fa[2], fb[2];
+    for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const bf16x8_t*>(As + (wm * 64 + i * 16 + fc) * kWgP + fk);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) fa[i] = *reinterpret_cast<const bf16x8_t*>(&As[wm * 32 + i * 16 + fc][fk]);
+    for (int j = 0; j < 4; ++j) fb[j] = *reinterpret_cast<const bf16x8_t*>(Bs + (wn * 64 + j * 16 + fc) * kWgP + fk);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) fb[j] = *reinterpret_cast<const bf16x8_t*>(&Bs[wn * 32 + j * 16 + fc][fk]);
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    if (more) wg_store(st, &S[buf ^ 1][op][cg * kWgP], rg * 8);
+    __syncthreads();                       // the next slice is stored; this one's reads are done
+    buf ^= 1;
   }
   // C block (i, j): lane holds column n = lane & 15, rows m = 4 (lane >> 4) + q
   float* Cg = C + (long long)g * M * N;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int m = m0 + wm * 32 + i * 16 + 4 * (lane >> 4) + q;
-        const int n = n0 + wn * 32 + j * 16 + (lane & 15);
+        const int m = m0 + wm * 64 + i * 16 + 4 * (lane >> 4) + q;
+        const int n = n0 + wn * 64 + j * 16 + (lane & 15);
         if (m < M && n < N) Cg[(long long)m * N + n] = acc[i][j][q];
       }
 }
@@ -387,9 +419,9 @@ hipError_t launch_bw_act(const bf16_t* gu, const bf16_t* dh, bf16_t* dgu, const 
 hipError_t launch_wgrad(const bf16_t* A, int lda, const bf16_t* B, int ldb, const int32_t* b_rows,
                         const int32_t* offsets, int G, int rows_max, int M, int N, float* C, hipStream_t s) {
   if (G <= 0 || M <= 0 || N <= 0) return hipSuccess;
-  if (lda % 8 != 0 || ldb % 8 != 0) return hipErrorInvalidValue;   // 16-byte row chunks
-  hipLaunchKernelGGL(wgrad_kernel, dim3(ceil_div(N, 64), ceil_div(M, 64), G), dim3(256), 0, s, A, lda, B, ldb, b_rows,
-                     offsets, rows_max, M, N, C);
+  if (lda % 4 != 0 || ldb % 4 != 0 || M % 4 != 0 || N % 4 != 0) return hipErrorInvalidValue;   // 8-byte column groups
+  hipLaunchKernelGGL(wgrad_kernel, dim3(ceil_div(N, 128), ceil_div(M, 128), G), dim3(256), 0, s, A, lda, B, ldb,
+                     b_rows, offsets, rows_max, M, N, C);
   return hipGetLastError();
 }
 
