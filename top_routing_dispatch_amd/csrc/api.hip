@@ -543,8 +543,8 @@ moe_status aux_stream(AuxStream** out) {
 
 // Backward -----------------------------------------------------------------
 struct BwLayout {
-  size_t fwd, y, dyp, gu, dh, dgu, dxp, w13t, w2t, ones, dw, dlogits, dxr, pre, gus, dhs, dgus, dxs, ws13t, ws2t,
-      total;
+  size_t fwd, y, dyp, gu, dh, dgu, dxp, w13t, w2t, ones, dw, dlogits, dxr, rpart, pre, gus, dhs, dgus, dxs, ws13t,
+      ws2t, total;
 };
 
 BwLayout bw_layout(const moe_config* c, const Derived& d) {
@@ -567,6 +567,7 @@ BwLayout bw_layout(const moe_config* c, const Derived& d) {
   B.dw = take(T * k * 4);
   B.dlogits = take(T * E * 4);
   B.dxr = take(T * D * 4);
+  B.rpart = take((size_t)kF32MaxSplit * E * D * 4);
   B.pre = take(2 * (E + 1) * 4);
   B.gus = take(T * 2 * SF * 2);
   B.dhs = take(T * SF * 2);
@@ -1055,10 +1056,11 @@ moe_status moe_layer_backward(const moe_config* cfg, const moe_weights* wt, cons
   // router: d loss / d logits, then its weight and input gradients
   MOE_TRY_HIP("router backward", launch_router_grad(logits, idx, tw, dwt, counts, T, E, k, cfg->scoring,
                                                     cfg->renormalize, alpha, dlog, s));
-  MOE_TRY_HIP("router dW", launch_gemm_f32_strided(dlog, 1, E, x, true, D, 1, E, D, T, dw_router, s));
+  MOE_TRY_HIP("router dW", launch_gemm_f32_strided(dlog, 1, E, x, true, D, 1, E, D, T, dw_router,
+                                                   at<float>(ws, B.rpart), s));
   float* dxr = at<float>(ws, B.dxr);
   MOE_TRY_HIP("router dx", launch_gemm_f32_strided(dlog, E, 1, wt->w_router, cfg->router_dtype == BF16, D, 1, T, D,
-                                                   E, dxr, s));
+                                                   E, dxr, nullptr, s));
   // dx = sum of the token's expert rows (weight 1) + shared + router
   float* ones = at<float>(ws, B.ones);
   MOE_TRY_HIP("ones", launch_fill_f32(ones, 1.0f, (long long)T * k, s));

@@ -338,27 +338,31 @@ __global__ __launch_bounds__(256) void router_grad_kernel(const float* __restric
 // C[m, n] = sum_k A(m, k) B(k, n), A(m, k) = A[m am + k ak] (float32),
 // B(k, n) = B[k bk + n bn] (BT), float32 out [M][N] (+ C when accumulate).
 // 64x64 tile, 4x4 per thread, 16-deep slices through LDS.
+// With gridDim.z = S > 1 the contraction is split into S consecutive ranges
+// of kc and part z writes C + z M N (added in order by sum_parts_kernel).
 template <typename BT>
 __global__ __launch_bounds__(256) void gemm_f32_strided_kernel(const float* __restrict__ A, long long am,
                                                                long long ak, const BT* __restrict__ B, long long bk,
-                                                               long long bn, int M, int N, int K,
+                                                               long long bn, int M, int N, int K, int kc,
                                                                float* __restrict__ C) {
   __shared__ float As[16][65], Bs[16][65];
   const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
   const int tm = (threadIdx.x >> 4) * 4, tn = (threadIdx.x & 15) * 4;
+  const int k_lo = blockIdx.z * kc, k_hi = min(K, k_lo + kc);
+  C += (long long)blockIdx.z * M * N;
   float acc[4][4] = {};
-  for (int k0 = 0; k0 < K; k0 += 16) {
+  for (int k0 = k_lo; k0 < k_hi; k0 += 16) {
     for (int i = threadIdx.x; i < 16 * 64; i += 256) {
       // consecutive threads walk the stride-1 index of each operand
       int kk, mm;
       if (am == 1) { mm = i & 63; kk = i >> 6; } else { kk = i & 15; mm = i >> 4; }
       const int m = m0 + mm, kq = k0 + kk;
-      As[kk][mm] = (m < M && kq < K) ? A[m * am + kq * ak] : 0.0f;
+      As[kk][mm] = (m < M && kq < k_hi) ? A[m * am + kq * ak] : 0.0f;
       int kb, nn;
       if (bn == 1) { nn = i & 63; kb = i >> 6; } else { kb = i & 15; nn = i >> 4; }
       const int n = n0 + nn, kr = k0 + kb;
       float bvv = 0.0f;
-      if (n < N && kr < K) {
+      if (n < N && kr < k_hi) {
         if constexpr (sizeof(BT) == 2) bvv = bf(B[kr * bk + n * bn]);
         else bvv = B[kr * bk + n * bn];
       }
@@ -378,6 +382,16 @@ __global__ __launch_bounds__(256) void gemm_f32_strided_kernel(const float* __re
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       if (m0 + tm + i < M && n0 + tn + j < N) C[(long long)(m0 + tm + i) * N + n0 + tn + j] = acc[i][j];
+}
+
+// C[i] = sum over parts z (in order) of P[z n + i]
+__global__ __launch_bounds__(256) void sum_parts_kernel(const float* __restrict__ P, int S, long long n,
+                                                        float* __restrict__ C) {
+  for (long long i = blockIdx.x * 256LL + threadIdx.x; i < n; i += (long long)gridDim.x * 256) {
+    float v = 0.0f;
+    for (int z = 0; z < S; ++z) v += P[z * n + i];
+    C[i] = v;
+  }
 }
 
 // y[i] = bf16(y[i] + add[i])
@@ -444,16 +458,31 @@ hipError_t launch_router_grad(const float* logits, const int32_t* idx, const flo
   return hipGetLastError();
 }
 
+int gemm_f32_split(int M, int N, int K) {
+  const long long tiles = (long long)ceil_div(M, 64) * ceil_div(N, 64);
+  int sp = 1;
+  while (sp < kF32MaxSplit && tiles * sp * 2 <= 512 && K / (sp * 2) >= 256) sp *= 2;
+  return sp;
+}
+
 hipError_t launch_gemm_f32_strided(const float* A, long long am, long long ak, const void* B, bool b_bf16,
-                                   long long bk, long long bn, int M, int N, int K, float* C, hipStream_t s) {
+                                   long long bk, long long bn, int M, int N, int K, float* C, float* partial,
+                                   hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
-  const dim3 grid((unsigned)ceil_div(N, 64), (unsigned)ceil_div(M, 64));
+  const int sp = partial != nullptr ? gemm_f32_split(M, N, K) : 1;
+  const int kc = sp > 1 ? ceil_div(ceil_div(K, sp), 16) * 16 : K;
+  const dim3 grid((unsigned)ceil_div(N, 64), (unsigned)ceil_div(M, 64), (unsigned)sp);
+  float* out = sp > 1 ? partial : C;
   if (b_bf16)
     hipLaunchKernelGGL(gemm_f32_strided_kernel<bf16_t>, grid, dim3(256), 0, s, A, am, ak,
-                       static_cast<const bf16_t*>(B), bk, bn, M, N, K, C);
+                       static_cast<const bf16_t*>(B), bk, bn, M, N, K, kc, out);
   else
     hipLaunchKernelGGL(gemm_f32_strided_kernel<float>, grid, dim3(256), 0, s, A, am, ak,
-                       static_cast<const float*>(B), bk, bn, M, N, K, C);
+                       static_cast<const float*>(B), bk, bn, M, N, K, kc, out);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || sp == 1) return e;
+  const long long n = (long long)M * N;
+  hipLaunchKernelGGL(sum_parts_kernel, dim3(grid_for(n)), dim3(256), 0, s, partial, sp, n, C);
   return hipGetLastError();
 }
 

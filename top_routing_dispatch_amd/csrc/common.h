@@ -336,8 +336,12 @@ hipError_t launch_wgrad(const bf16_t* A, int lda, const bf16_t* B, int ldb, cons
 hipError_t launch_router_grad(const float* logits, const int32_t* idx, const float* tw, const float* dw,
                               const int32_t* counts, int T, int E, int k, int scoring, int renormalize, float alpha,
                               float* dlogits, hipStream_t s);
+// partial: NULL, or room for kF32MaxSplit * M * N floats (the contraction is
+// then split over up to that many parts when the output tiles are few).
+constexpr int kF32MaxSplit = 32;
 hipError_t launch_gemm_f32_strided(const float* A, long long am, long long ak, const void* B, bool b_bf16,
-                                   long long bk, long long bn, int M, int N, int K, float* C, hipStream_t s);
+                                   long long bk, long long bn, int M, int N, int K, float* C, float* partial,
+                                   hipStream_t s);
 hipError_t launch_add_f32_to_bf16(bf16_t* y, const float* add, long long n, hipStream_t s);
 hipError_t launch_fill_f32(float* p, float v, long long n, hipStream_t s);
 // Expert-parallel send / receive layouts (ep.hip).
