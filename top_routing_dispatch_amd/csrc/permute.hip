@@ -442,7 +442,11 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kMaxExperts), 0, s, a, ntiles);
+  // one thread per expert (a power of two, at least a wave): the scans take
+  // log2(threads) steps
+  int threads = 64;
+  while (threads < a.E) threads <<= 1;
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(threads), 0, s, a, ntiles);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || ntiles == 0) return err;
   hipLaunchKernelGGL(scatter_kernel, dim3(ntiles), dim3(kPermuteTile), 0, s, a);
