@@ -485,6 +485,29 @@ def run_backward(args, cfg):
                 unit="TFLOP/s", frac=round(flops / (ev_ms * 1e-3) / 1e12 / MFMA_BF16_TFLOPS, 4),
                 kernel="layer backward (expert GEMM work, forward recomputation included)", ms=round(ev_ms, 4),
                 traffic=None)
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import moe_oracle as O
+        Ts = min(args.cpu_sample_tokens or 64, T)
+        scfg = cfg.replace(num_tokens=Ts)
+        dy_h = dy[:Ts].float().cpu().numpy()
+        expert = lambda e: W.make_expert(cfg, e)
+        passes, t1 = 0, time.perf_counter()
+        while True:
+            O.backward(scfg, inp.x[:Ts], inp.w_router, inp.sel_bias, expert, inp.shared, dy_h, alpha=cfg.alpha)
+            passes += 1
+            if time.perf_counter() - t1 >= CPU_MIN_SECONDS:
+                break
+        dt = time.perf_counter() - t1
+        try:
+            import threadpoolctl
+            info = threadpoolctl.threadpool_info()
+            cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+        except Exception:
+            cores = 1
+        cpu = dict(value=round(Ts * passes / dt, 2), unit="tokens/s", cores=int(cores), kind="oracle",
+                   sample=f"backward of the first {Ts} of {T} tokens (forward recomputed, experts regenerated); "
+                          f"{passes} pass(es) in {dt:.1f} s")
     line = {
         "metric": "MoE-layer tokens/sec at 1 GPU; % HBM roofline (route/permute) and % MFMA peak",
         "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -494,7 +517,7 @@ def run_backward(args, cfg):
                    "d_ff": F, "shared": cfg.num_shared, "d_ff_shared": cfg.d_ff_shared,
                    "expert_gemm_flops_per_step": flops},
         "roofline": roof,
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 
