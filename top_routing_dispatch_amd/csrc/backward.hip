@@ -36,8 +36,14 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16_t* __res
   bf16_t* dst = out + g * (long long)R * C;
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += 4)
-    if (r0 + i < R && c0 + tx < C) tile[i][tx] = src[(long long)(r0 + i) * C + c0 + tx];
+  // the 16 loads of a thread without branches between them (indices clamped;
+  // the clamped copies land in tile entries that are never written out)
+  bf16_t v[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q)
+    v[q] = src[(long long)min(r0 + ty + 4 * q, R - 1) * C + min(c0 + tx, C - 1)];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) tile[ty + 4 * q][tx] = v[q];
   __syncthreads();
   for (int i = ty; i < 64; i += 4)
     if (c0 + i < C && r0 + tx < R) dst[(long long)(c0 + i) * R + r0 + tx] = tile[tx][i];
@@ -81,27 +87,49 @@ __global__ __launch_bounds__(256) void bw_combine_kernel(const bf16_t* __restric
 //   dG = dh * U * silu'(G), dU = dh * silu(G), silu'(g) = s(g) (1 + g (1 - s(g))).
 // GELU: gu = Z (F columns); dZ = dh * (Phi(z) + z phi(z)).
 // Rows from rows_valid on (a device count) are skipped.
+// Eight consecutive columns per item (F % 8 == 0): 16-byte loads and stores.
 __global__ __launch_bounds__(256) void bw_act_kernel(const bf16_t* __restrict__ gu, const bf16_t* __restrict__ dh,
                                                      bf16_t* __restrict__ dgu, const int32_t* __restrict__ rows_valid,
                                                      int rows_max, int F, int swiglu) {
   const int rows = rows_valid ? min(*rows_valid, rows_max) : rows_max;
-  const long long n = (long long)rows * F;
+  const int F8 = F / 8;
+  const long long n = (long long)rows * F8;
   const int ldg = swiglu ? 2 * F : F;
   for (long long i = blockIdx.x * 256LL + threadIdx.x; i < n; i += (long long)gridDim.x * 256) {
-    const long long r = i / F;
-    const int f = (int)(i % F);
-    const float g = bf(gu[r * ldg + f]);
-    const float d = bf(dh[r * F + f]);
-    if (swiglu) {
-      const float u = bf(gu[r * ldg + F + f]);
-      const float sg = 1.0f / (1.0f + expf(-g));
-      dgu[r * ldg + f] = f32_to_bf16_rn(d * u * sg * (1.0f + g * (1.0f - sg)));
-      dgu[r * ldg + F + f] = f32_to_bf16_rn(d * g * sg);
-    } else {
-      const float cdf = 0.5f * (1.0f + erff(g * 0.70710678118654752f));
-      const float pdf = 0.39894228040143268f * expf(-0.5f * g * g);
-      dgu[r * ldg + f] = f32_to_bf16_rn(d * (cdf + g * pdf));
+    const long long r = i / F8;
+    const int f = (int)(i % F8) * 8;
+    const uint4 gq = *reinterpret_cast<const uint4*>(gu + r * ldg + f);
+    const uint4 dq = *reinterpret_cast<const uint4*>(dh + r * F + f);
+    const uint4 uq = swiglu ? *reinterpret_cast<const uint4*>(gu + r * ldg + F + f) : make_uint4(0u, 0u, 0u, 0u);
+    const uint32_t gw[4] = {gq.x, gq.y, gq.z, gq.w}, dw4[4] = {dq.x, dq.y, dq.z, dq.w},
+                   uw[4] = {uq.x, uq.y, uq.z, uq.w};
+    uint32_t o1[4], o2[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t a1 = 0, a2 = 0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float g = __uint_as_float(h ? (gw[q] & 0xffff0000u) : (gw[q] << 16));
+        const float d = __uint_as_float(h ? (dw4[q] & 0xffff0000u) : (dw4[q] << 16));
+        uint32_t r1, r2 = 0;
+        if (swiglu) {
+          const float u = __uint_as_float(h ? (uw[q] & 0xffff0000u) : (uw[q] << 16));
+          const float sg = 1.0f / (1.0f + expf(-g));
+          r1 = f32_to_bf16_rn(d * u * sg * (1.0f + g * (1.0f - sg)));
+          r2 = f32_to_bf16_rn(d * g * sg);
+        } else {
+          const float cdf = 0.5f * (1.0f + erff(g * 0.70710678118654752f));
+          const float pdf = 0.39894228040143268f * expf(-0.5f * g * g);
+          r1 = f32_to_bf16_rn(d * (cdf + g * pdf));
+        }
+        a1 |= r1 << (16 * h);
+        a2 |= r2 << (16 * h);
+      }
+      o1[q] = a1;
+      o2[q] = a2;
     }
+    *reinterpret_cast<uint4*>(dgu + r * ldg + f) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
+    if (swiglu) *reinterpret_cast<uint4*>(dgu + r * ldg + F + f) = make_uint4(o2[0], o2[1], o2[2], o2[3]);
   }
 }
 
@@ -109,14 +137,14 @@ __global__ __launch_bounds__(256) void bw_act_kernel(const bf16_t* __restrict__ 
 // C_g[m, n] = sum over rows r of group g of A[r, m] * B[b_row(r), n]
 // (float32 out, [G][M][N]); A [rows][lda] and B [*][ldb] bf16 (lda, ldb,
 // M, N multiples of 4).  b_rows (or NULL) maps a row to the B row it reads.
-// offsets [G+1] (NULL: one group of rows_max rows).  128x128 tile per
-// workgroup, 32 rows per slice.  A slice is staged transposed in LDS ([m][r],
+// offsets [G+1] (NULL: one group of rows_max rows).  BMxBN tile per
+// workgroup (128x128 on four waves, or 256x256 on eight), 32 rows per slice.  A slice is staged transposed in LDS ([m][r],
 // [n][r]) so that the MFMA operands (8 consecutive rows of one column) are
 // 16-byte reads: each thread loads an 8-row x 4-column block of A or B (8-byte
 // loads), transposes it in registers and stores four 16-byte columns.  The
 // next slice's loads are in flight while the current one is multiplied (two
-// LDS buffers, one barrier per slice).  Four waves of 64x64 (4x4 blocks of
-// v_mfma_f32_16x16x32_bf16).  Empty groups write zeros.
+// LDS buffers, one barrier per slice).  Wave tiles of 64x64 or 128x64 (blocks
+// of v_mfma_f32_16x16x32_bf16).  Empty groups write zeros.
 constexpr int kWgP = 40;                 // LDS row pitch in bf16 (32 rows + pad)
 
 struct WgStage {
@@ -124,18 +152,24 @@ struct WgStage {
 };
 
 // thread -> operand (0: A, 1: B), 8-row group, 4-column group of the slice
+// No branch between the loads (a load behind a branch is issued and waited
+// for alone): rows past the group's end and column groups past C read a
+// valid element and are zeroed afterwards.
 __device__ __forceinline__ void wg_load(WgStage& st, const bf16_t* __restrict__ P, int ld,
                                         const int32_t* __restrict__ rows_map, int r_base, int r_hi, int c_base, int C) {
+  const bool col_ok = c_base < C;
+  const int cc = col_ok ? c_base : 0;
+  long long pr[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int r = r_base + i;
-    uint2 q = make_uint2(0u, 0u);
-    if (r < r_hi && c_base < C) {
-      const long long pr = rows_map ? (long long)rows_map[r] : (long long)r;
-      q = *reinterpret_cast<const uint2*>(P + pr * ld + c_base);
-    }
-    st.v[i] = q;
+    const int r = min(r_base + i, r_hi - 1);
+    pr[i] = rows_map ? (long long)rows_map[r] : (long long)r;
   }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) st.v[i] = *reinterpret_cast<const uint2*>(P + pr[i] * ld + cc);
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (!(col_ok && r_base + i < r_hi)) st.v[i] = make_uint2(0u, 0u);
 }
 
 __device__ __forceinline__ void wg_store(const WgStage& st, bf16_t* lds_cols, int r_off) {
@@ -154,73 +188,88 @@ __device__ __forceinline__ void wg_store(const WgStage& st, bf16_t* lds_cols, in
   for (int c = 0; c < 4; ++c) *reinterpret_cast<uint4*>(lds_cols + c * kWgP + r_off) = o[c];
 }
 
-__global__ __launch_bounds__(256) void wgrad_kernel(const bf16_t* __restrict__ A, int lda,
-                                                    const bf16_t* __restrict__ B, int ldb,
-                                                    const int32_t* __restrict__ b_rows,
-                                                    const int32_t* __restrict__ offsets, int rows_max, int M, int N,
-                                                    float* __restrict__ C) {
-  __shared__ __attribute__((aligned(16))) bf16_t S[2][2][128 * kWgP];   // [buffer][A / B][col][row]
+template <int BM, int BN, int WGM, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN) void wgrad_kernel(const bf16_t* __restrict__ A, int lda,
+                                                               const bf16_t* __restrict__ B, int ldb,
+                                                               const int32_t* __restrict__ b_rows,
+                                                               const int32_t* __restrict__ offsets, int rows_max,
+                                                               int M, int N, float* __restrict__ C) {
+  static_assert(BM + BN == 64 * WGM * WGN, "one 8x4 staging block per thread");
+  constexpr int WM = BM / WGM, WN = BN / WGN;        // wave tile
+  constexpr int TM = WM / 16, TN = WN / 16;           // 16x16 blocks per wave
+  __shared__ __attribute__((aligned(16))) bf16_t S[2][(BM + BN) * kWgP];   // [buffer][A cols, then B cols][row]
   const int g = blockIdx.z;
-  const int m0 = blockIdx.y * 128, n0 = blockIdx.x * 128;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
   const int r_lo = offsets ? offsets[g] : 0;
   const int r_hi = offsets ? offsets[g + 1] : rows_max;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  // staging role: threads 0..127 load A, 128..255 load B; (row group, column group)
-  const int op = threadIdx.x >> 7;
-  const int sid = threadIdx.x & 127;
-  const int rg = sid >> 5;                 // 4 groups of 8 rows
-  const int cg = (sid & 31) * 4;           // 32 groups of 4 columns
-  const bf16_t* P = op ? B : A;
-  const int ld = op ? ldb : lda;
-  const int32_t* rmap = op ? b_rows : nullptr;
-  const int c_base = (op ? n0 : m0) + cg;
-  const int C_lim = op ? N : M;
+  const int wm = wave / WGN, wn = wave % WGN;
+  // staging role: threads 0..BM-1 load A, BM..BM+BN-1 load B; (8-row group, 4-column group)
+  const bool isb = (int)threadIdx.x >= BM;
+  const int sid = isb ? threadIdx.x - BM : threadIdx.x;
+  const int ncg = (isb ? BN : BM) / 4;
+  const int rg = sid / ncg;
+  const int cg = (sid % ncg) * 4;
+  const bf16_t* P = isb ? B : A;
+  const int ld = isb ? ldb : lda;
+  const int32_t* rmap = isb ? b_rows : nullptr;
+  const int c_base = (isb ? n0 : m0) + cg;
+  const int C_lim = isb ? N : M;
+  const int lds_col = (isb ? BM : 0) + cg;
 
-  floatx4_t acc[4][4];
+  floatx4_t acc[TM][TN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) acc[i][j][q] = 0.0f;
 
-  WgStage st;
-  int buf = 0;
-  if (r_lo < r_hi) {
-    wg_load(st, P, ld, rmap, r_lo + rg * 8, r_hi, c_base, C_lim);
-    wg_store(st, &S[0][op][cg * kWgP], rg * 8);
-  }
+  // Slices j = 0, 1, ... of the group's rows: slice j is multiplied from
+  // LDS buffer j % 2; its registers were loaded two slices earlier (three
+  // register stages), so a load has two slices of MFMA work to arrive in.
+  const int nsl = (r_hi - r_lo + 31) / 32;
+  WgStage st[3];
+  if (nsl > 0) wg_load(st[0], P, ld, rmap, r_lo + rg * 8, r_hi, c_base, C_lim);
+  if (nsl > 1) wg_load(st[1], P, ld, rmap, r_lo + 32 + rg * 8, r_hi, c_base, C_lim);
+  if (nsl > 0) wg_store(st[0], &S[0][lds_col * kWgP], rg * 8);
   __syncthreads();
   const int fc = lane & 15, fk = (lane >> 4) * 8;
-  for (int r0 = r_lo; r0 < r_hi; r0 += 32) {
-    const bool more = r0 + 32 < r_hi;
-    if (more) wg_load(st, P, ld, rmap, r0 + 32 + rg * 8, r_hi, c_base, C_lim);   // next slice in flight
-    const bf16_t* As = S[buf][0];
-    const bf16_t* Bs = S[buf][1];
-    bf16x8_t fa[4], fb[4];
+  // one slice with compile-time register stages: L loads slice j + 2, W
+  // stores slice j + 1
+  auto slice = [&](int j, WgStage& ld_st, WgStage& wr_st) __attribute__((always_inline)) {
+    if (j + 2 < nsl) wg_load(ld_st, P, ld, rmap, r_lo + (j + 2) * 32 + rg * 8, r_hi, c_base, C_lim);
+    const bf16_t* As = S[j & 1];
+    const bf16_t* Bs = S[j & 1] + BM * kWgP;
+    bf16x8_t fb[TN];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const bf16x8_t*>(As + (wm * 64 + i * 16 + fc) * kWgP + fk);
+    for (int jj = 0; jj < TN; ++jj)
+      fb[jj] = *reinterpret_cast<const bf16x8_t*>(Bs + (wn * WN + jj * 16 + fc) * kWgP + fk);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) fb[j] = *reinterpret_cast<const bf16x8_t*>(Bs + (wn * 64 + j * 16 + fc) * kWgP + fk);
+    for (int i = 0; i < TM; ++i) {
+      const bf16x8_t fa = *reinterpret_cast<const bf16x8_t*>(As + (wm * WM + i * 16 + fc) * kWgP + fk);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    if (more) wg_store(st, &S[buf ^ 1][op][cg * kWgP], rg * 8);
-    __syncthreads();                       // the next slice is stored; this one's reads are done
-    buf ^= 1;
+      for (int jj = 0; jj < TN; ++jj)
+        acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb[jj], acc[i][jj], 0, 0, 0);
+    }
+    if (j + 1 < nsl) wg_store(wr_st, &S[(j + 1) & 1][lds_col * kWgP], rg * 8);
+    __syncthreads();                       // slice j + 1 is stored; slice j's reads are done
+  };
+  for (int j = 0; j < nsl; j += 3) {
+    slice(j, st[2], st[1]);
+    if (j + 1 < nsl) slice(j + 1, st[0], st[2]);
+    if (j + 2 < nsl) slice(j + 2, st[1], st[0]);
   }
   // C block (i, j): lane holds column n = lane & 15, rows m = 4 (lane >> 4) + q
   float* Cg = C + (long long)g * M * N;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int m = m0 + wm * 64 + i * 16 + 4 * (lane >> 4) + q;
-        const int n = n0 + wn * 64 + j * 16 + (lane & 15);
+        const int m = m0 + wm * WM + i * 16 + 4 * (lane >> 4) + q;
+        const int n = n0 + wn * WN + j * 16 + (lane & 15);
         if (m < M && n < N) Cg[(long long)m * N + n] = acc[i][j][q];
       }
 }
@@ -425,8 +474,9 @@ hipError_t launch_bw_combine(const bf16_t* dy, const bf16_t* yp, const int32_t* 
 hipError_t launch_bw_act(const bf16_t* gu, const bf16_t* dh, bf16_t* dgu, const int32_t* rows_valid, int rows_max,
                          int F, bool swiglu, hipStream_t s) {
   if (rows_max <= 0) return hipSuccess;
-  hipLaunchKernelGGL(bw_act_kernel, dim3(grid_for((long long)rows_max * F)), dim3(256), 0, s, gu, dh, dgu, rows_valid,
-                     rows_max, F, swiglu ? 1 : 0);
+  if (F % 8 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(bw_act_kernel, dim3(grid_for((long long)rows_max * (F / 8))), dim3(256), 0, s, gu, dh, dgu,
+                     rows_valid, rows_max, F, swiglu ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -434,8 +484,14 @@ hipError_t launch_wgrad(const bf16_t* A, int lda, const bf16_t* B, int ldb, cons
                         const int32_t* offsets, int G, int rows_max, int M, int N, float* C, hipStream_t s) {
   if (G <= 0 || M <= 0 || N <= 0) return hipSuccess;
   if (lda % 4 != 0 || ldb % 4 != 0 || M % 4 != 0 || N % 4 != 0) return hipErrorInvalidValue;   // 8-byte column groups
-  hipLaunchKernelGGL(wgrad_kernel, dim3(ceil_div(N, 128), ceil_div(M, 128), G), dim3(256), 0, s, A, lda, B, ldb,
-                     b_rows, offsets, rows_max, M, N, C);
+  // 256x256 tiles (eight waves) for large outputs: each operand row slice is
+  // re-read by half as many workgroups as with 128x128
+  if (M >= 256 && N >= 256)
+    hipLaunchKernelGGL((wgrad_kernel<256, 256, 2, 4>), dim3(ceil_div(N, 256), ceil_div(M, 256), G), dim3(512), 0, s,
+                       A, lda, B, ldb, b_rows, offsets, rows_max, M, N, C);
+  else
+    hipLaunchKernelGGL((wgrad_kernel<128, 128, 2, 2>), dim3(ceil_div(N, 128), ceil_div(M, 128), G), dim3(256), 0, s,
+                       A, lda, B, ldb, b_rows, offsets, rows_max, M, N, C);
   return hipGetLastError();
 }
 
