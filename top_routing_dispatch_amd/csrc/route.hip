@@ -145,14 +145,26 @@ __device__ __forceinline__ void select_f32(const RouteArgs& a, int t, int lane, 
   const int E = a.E, k = a.k;
   const bool sig = a.scoring == SIGMOID_BIAS;
   const float* srow = a.logits + (long long)t * E;
+  // every load first, with no branch between them (indices clamped, values
+  // of lanes past E dropped afterwards): behind a per-slot branch the
+  // compiler issued one load at a time
+  float sv[EPL], bv[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) sv[i] = srow[min(lane + kWave * i, E - 1)];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) bv[i] = 0.0f;
+  if (sig && a.sel_bias != nullptr) {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) bv[i] = a.sel_bias[min(lane + kWave * i, E - 1)];
+  }
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     const int e = lane + kWave * i;
     const bool valid = e < E;
-    st.s[i] = valid ? srow[e] : 0.0f;
+    st.s[i] = valid ? sv[i] : 0.0f;
     float q = -INFINITY;
-    if (valid) q = sig ? sigmoid_f32(st.s[i]) + (a.sel_bias ? a.sel_bias[e] : 0.0f) : st.s[i];
+    if (valid) q = sig ? sigmoid_f32(st.s[i]) + bv[i] : st.s[i];
     st.key[i] = q;
     st.taken[i] = !valid;
     amax = fmaxf(amax, fabsf(st.s[i]));
