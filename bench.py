@@ -6,8 +6,11 @@ expert FFN (routed and shared), combine and the load statistics.
 
 Prints ONE JSON line: MoE-layer tokens/s, the roofline of the dominant stage
 (timed live with HIP events on the library's stream over the timed steps), the
-per-stage breakdown of an untimed pass with every stage bracketed by events,
-and the CPU oracle timed on a bounded sample of the same workload.
+per-stage breakdown of an untimed pass with every stage bracketed by events
+(and of a second one with the MALL and L2 evicted before each pass), the
+median / p10 / p90 of single steps' HIP-event times (an untimed run of the
+same length), and the CPU oracle
+timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -312,6 +315,20 @@ def main():
     main_ms = {k: v for k, v in stage_ms.items() if k not in AUX_STAGES}
     dominant = max(main_ms or stage_ms, key=(main_ms or stage_ms).get)
     dom_i = M.STAGES.index(dominant)
+    # The same stages with the caches cold: a 512 MB scratch read before each
+    # pass evicts the 256 MB MALL and the L2s, so no stage reads what the
+    # previous pass left there (a read, so that no dirty lines are left whose
+    # write-back would fall on the first stage).
+    n_cold = 5
+    cold_events = [new_events() for _ in range(n_cold)]
+    scratch = torch.ones(64 << 20, dtype=torch.int64, device=dev)
+    torch.cuda.synchronize()
+    for i in range(n_cold):
+        scratch.sum()
+        step(cold_events[i])
+    torch.cuda.synchronize()
+    stage_cold_ms = stage_times(cold_events, range(nst))
+    del scratch
     events = [new_events([dom_i]) for _ in range(args.steps)]
     torch.cuda.synchronize()
 
@@ -324,6 +341,16 @@ def main():
     log(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step")
     # the dominant stage's time over the timed steps (HIP events on the library's stream)
     dom_ms = stage_times(events, [dom_i])[dominant]
+    # the spread of single steps, from HIP events around each step of an
+    # untimed run of the same length (kept out of the timed region above)
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+    for i in range(args.steps):
+        step_ev[i][0].record()
+        step()
+        step_ev[i][1].record()
+    torch.cuda.synchronize()
+    per_step = np.array([a.elapsed_time(b) for a, b in step_ev])
 
     if ec:
         kept = np.full(E, C_ec)                         # every expert takes exactly C tokens
@@ -368,7 +395,10 @@ def main():
                    "routing": "expert_choice" if ec else "token_choice"},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "step_ms": {q: round(float(np.percentile(per_step, p)), 4)
+                    for q, p in (("median", 50), ("p10", 10), ("p90", 90))},
         "stages": stage_info,
+        "stages_cold_ms": {name: round(ms, 4) for name, ms in stage_cold_ms.items()},
     }
     print(json.dumps(line), flush=True)
 
