@@ -149,36 +149,68 @@ constexpr int kWgP = 40;                 // LDS row pitch in bf16 (32 rows + pad
 
 struct WgStage {
   uint2 v[8];
+  uint32_t ok;     // bit i: row i of the block exists and the column group is inside C
 };
 
-// thread -> operand (0: A, 1: B), 8-row group, 4-column group of the slice
-// No branch between the loads (a load behind a branch is issued and waited
-// for alone): rows past the group's end and column groups past C read a
-// valid element and are zeroed afterwards.
+// thread -> operand (0: A, 1: B), 8-row group, 4-column group of the slice.
+// Nothing here waits for a load: rows past the group's end and column groups
+// past C read a valid element, and wg_store zeroes them from the `ok` bits
+// when the values are consumed (slices later).  The row map is read with
+// scalar loads: the rows of one wave's threads are the RGW (1 or 2) row
+// groups starting at lane 0's, a wave-uniform range, and a scalar load's wait
+// does not also wait for the data loads of the slices in flight.
+template <int RGW>
 __device__ __forceinline__ void wg_load(WgStage& st, const bf16_t* __restrict__ P, int ld,
                                         const int32_t* __restrict__ rows_map, int r_base, int r_hi, int c_base, int C) {
   const bool col_ok = c_base < C;
   const int cc = col_ok ? c_base : 0;
   long long pr[8];
+  if (rows_map != nullptr) {                 // uniform per wave (B operand waves)
+    const int rb0 = __builtin_amdgcn_readfirstlane(r_base);
+    const int rh = __builtin_amdgcn_readfirstlane(r_hi);
+    const_i32* rm = (const_i32*)rows_map;
+    int sidx[RGW][8];
+    if (rb0 + 8 * RGW <= rh) {               // whole range inside the group: one wide scalar load
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = min(r_base + i, r_hi - 1);
-    pr[i] = rows_map ? (long long)rows_map[r] : (long long)r;
+      for (int q = 0; q < RGW; ++q)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sidx[q][i] = rm[rb0 + q * 8 + i];
+    } else {
+#pragma unroll
+      for (int q = 0; q < RGW; ++q)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sidx[q][i] = rm[min(rb0 + q * 8 + i, rh - 1)];
+    }
+    const int q_l = (r_base - rb0) >> 3;     // 0 .. RGW-1
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      int v = sidx[0][i];
+#pragma unroll
+      for (int q = 1; q < RGW; ++q) v = q_l == q ? sidx[q][i] : v;
+      pr[i] = (long long)v;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pr[i] = (long long)min(r_base + i, r_hi - 1);
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) st.v[i] = *reinterpret_cast<const uint2*>(P + pr[i] * ld + cc);
+  uint32_t ok = 0u;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    if (!(col_ok && r_base + i < r_hi)) st.v[i] = make_uint2(0u, 0u);
+  for (int i = 0; i < 8; ++i) ok |= (col_ok && r_base + i < r_hi) ? (1u << i) : 0u;
+  st.ok = ok;
 }
 
 __device__ __forceinline__ void wg_store(const WgStage& st, bf16_t* lds_cols, int r_off) {
+  uint2 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = ((st.ok >> i) & 1u) ? st.v[i] : make_uint2(0u, 0u);
   // column c of the block gets rows 0..7: dword j = row 2j | row 2j+1 << 16
   uint4 o[4];
   uint32_t* w = reinterpret_cast<uint32_t*>(o);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const uint2 a = st.v[2 * j], b = st.v[2 * j + 1];
+    const uint2 a = v[2 * j], b = v[2 * j + 1];
     w[0 * 4 + j] = (a.x & 0xffffu) | (b.x << 16);
     w[1 * 4 + j] = (a.x >> 16) | (b.x & 0xffff0000u);
     w[2 * 4 + j] = (a.y & 0xffffu) | (b.y << 16);
@@ -197,6 +229,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void wgrad_kernel(const bf16_t* __r
   static_assert(BM + BN == 64 * WGM * WGN, "one 8x4 staging block per thread");
   constexpr int WM = BM / WGM, WN = BN / WGN;        // wave tile
   constexpr int TM = WM / 16, TN = WN / 16;           // 16x16 blocks per wave
+  constexpr int RGW = 256 / BN;                       // row groups per B wave
+  static_assert(BN == 128 || BN == 256, "B waves cover 1 or 2 row groups");
+  static_assert(BM % 64 == 0, "A and B threads in separate waves");
   __shared__ __attribute__((aligned(16))) bf16_t S[2][(BM + BN) * kWgP];   // [buffer][A cols, then B cols][row]
   const int g = blockIdx.z;
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
@@ -205,7 +240,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void wgrad_kernel(const bf16_t* __r
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
   // staging role: threads 0..BM-1 load A, BM..BM+BN-1 load B; (8-row group, 4-column group)
-  const bool isb = (int)threadIdx.x >= BM;
+  // wave-uniform (BM is a multiple of 64): the operand pointers below are
+  // scalar values, so the row map is read with scalar loads
+  const bool isb = __builtin_amdgcn_readfirstlane((int)threadIdx.x / 64) * 64 >= BM;
   const int sid = isb ? threadIdx.x - BM : threadIdx.x;
   const int ncg = (isb ? BN : BM) / 4;
   const int rg = sid / ncg;
@@ -226,39 +263,48 @@ __global__ __launch_bounds__(64 * WGM * WGN) void wgrad_kernel(const bf16_t* __r
       for (int q = 0; q < 4; ++q) acc[i][j][q] = 0.0f;
 
   // Slices j = 0, 1, ... of the group's rows: slice j is multiplied from
-  // LDS buffer j % 2; its registers were loaded two slices earlier (three
-  // register stages), so a load has two slices of MFMA work to arrive in.
+  // LDS buffer j % 2; its registers were loaded three slices earlier (four
+  // register stages, slice s in stage s % 4), so a load has three slices of
+  // MFMA work to arrive in.  The loads and stores run unconditionally (slices
+  // past the group's end read clamped rows and store zeros); only the MFMA
+  // part is skipped there.  A load guarded by a condition is moved by the
+  // compiler down to its use, which would leave nothing in flight.
   const int nsl = (r_hi - r_lo + 31) / 32;
-  WgStage st[3];
-  if (nsl > 0) wg_load(st[0], P, ld, rmap, r_lo + rg * 8, r_hi, c_base, C_lim);
-  if (nsl > 1) wg_load(st[1], P, ld, rmap, r_lo + 32 + rg * 8, r_hi, c_base, C_lim);
-  if (nsl > 0) wg_store(st[0], &S[0][lds_col * kWgP], rg * 8);
+  WgStage st[4];
+  if (nsl > 0) {
+#pragma unroll
+    for (int q = 0; q < 3; ++q) wg_load<RGW>(st[q], P, ld, rmap, r_lo + q * 32 + rg * 8, r_hi, c_base, C_lim);
+    wg_store(st[0], &S[0][lds_col * kWgP], rg * 8);
+  }
   __syncthreads();
   const int fc = lane & 15, fk = (lane >> 4) * 8;
-  // one slice with compile-time register stages: L loads slice j + 2, W
+  // one slice with compile-time register stages: L loads slice j + 3, W
   // stores slice j + 1
   auto slice = [&](int j, WgStage& ld_st, WgStage& wr_st) __attribute__((always_inline)) {
-    if (j + 2 < nsl) wg_load(ld_st, P, ld, rmap, r_lo + (j + 2) * 32 + rg * 8, r_hi, c_base, C_lim);
-    const bf16_t* As = S[j & 1];
-    const bf16_t* Bs = S[j & 1] + BM * kWgP;
-    bf16x8_t fb[TN];
-#pragma unroll
-    for (int jj = 0; jj < TN; ++jj)
-      fb[jj] = *reinterpret_cast<const bf16x8_t*>(Bs + (wn * WN + jj * 16 + fc) * kWgP + fk);
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const bf16x8_t fa = *reinterpret_cast<const bf16x8_t*>(As + (wm * WM + i * 16 + fc) * kWgP + fk);
+    wg_load<RGW>(ld_st, P, ld, rmap, r_lo + (j + 3) * 32 + rg * 8, r_hi, c_base, C_lim);
+    if (j < nsl) {                         // uniform
+      const bf16_t* As = S[j & 1];
+      const bf16_t* Bs = S[j & 1] + BM * kWgP;
+      bf16x8_t fb[TN];
 #pragma unroll
       for (int jj = 0; jj < TN; ++jj)
-        acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb[jj], acc[i][jj], 0, 0, 0);
+        fb[jj] = *reinterpret_cast<const bf16x8_t*>(Bs + (wn * WN + jj * 16 + fc) * kWgP + fk);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const bf16x8_t fa = *reinterpret_cast<const bf16x8_t*>(As + (wm * WM + i * 16 + fc) * kWgP + fk);
+#pragma unroll
+        for (int jj = 0; jj < TN; ++jj)
+          acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb[jj], acc[i][jj], 0, 0, 0);
+      }
     }
-    if (j + 1 < nsl) wg_store(wr_st, &S[(j + 1) & 1][lds_col * kWgP], rg * 8);
+    wg_store(wr_st, &S[(j + 1) & 1][lds_col * kWgP], rg * 8);
     __syncthreads();                       // slice j + 1 is stored; slice j's reads are done
   };
-  for (int j = 0; j < nsl; j += 3) {
-    slice(j, st[2], st[1]);
-    if (j + 1 < nsl) slice(j + 1, st[0], st[2]);
-    if (j + 2 < nsl) slice(j + 2, st[1], st[0]);
+  for (int j = 0; j < nsl; j += 4) {
+    slice(j, st[3], st[1]);
+    slice(j + 1, st[0], st[2]);
+    slice(j + 2, st[1], st[3]);
+    slice(j + 3, st[2], st[0]);
   }
   // C block (i, j): lane holds column n = lane & 15, rows m = 4 (lane >> 4) + q
   float* Cg = C + (long long)g * M * N;
