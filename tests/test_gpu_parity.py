@@ -1,6 +1,8 @@
 """GPU parity: the HIP path through the C ABI against the CPU oracle, on seeded
 inputs at sizes the oracle finishes in seconds (several tiles, ragged tails).
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -846,3 +848,50 @@ def test_layer_backward_matches_oracle(cfg):
     print("  " + ", ".join(f"{n} {v:.2e}" for n, v in errs.items()))
     for n, v in errs.items():
         assert v <= BW_TOL, f"{n}: {v:.3e}"
+
+
+@pytest.mark.parametrize("cfg", [BW_SHAPES[1], BW_SHAPES[3]], ids=lambda c: c.name)
+def test_weight_gradient_variants_identical(cfg):
+    """The weight-gradient kernel's tile size (256x256 on eight waves or
+    128x128 on four) and its LDS chunk permutation change where partial
+    products are staged, not the order in which any output adds its rows:
+    every gradient must be bit-identical across the variants (the narrow
+    DeepSeek-V3-shaped case runs 128x128 by default, so forcing 256x256
+    also covers partial tiles)."""
+    print(f"[backward variants] {cfg.name}", flush=True)
+    T, E, D, F = cfg.num_tokens, cfg.num_experts, cfg.d_model, cfg.d_ff
+    inp = W.make_inputs(cfg)
+    rng = np.random.default_rng(9)
+    dy = to_torch(W.f32_to_bf16_bits(rng.standard_normal((T, D), dtype=np.float32)), "cuda")
+    dl = DeviceLayer(cfg, inp)
+    nF = cfg.n_mat * F
+    SF = cfg.num_shared * cfg.d_ff_shared
+    ws = M.workspace(cfg, M.MOE_OP_LAYER_BACKWARD, "cuda")
+
+    def run(env):
+        old = {k: os.environ.get(k) for k in env}
+        os.environ.update(env)
+        try:
+            out = dict(dx=torch.empty((T, D), dtype=torch.bfloat16, device="cuda"),
+                       dwr=torch.empty((E, D), dtype=torch.float32, device="cuda"),
+                       dw13=torch.empty((E, nF, D), dtype=torch.float32, device="cuda"),
+                       dw2=torch.empty((E, D, F), dtype=torch.float32, device="cuda"),
+                       dws13=torch.empty((2 * SF, D), dtype=torch.float32, device="cuda") if SF else None,
+                       dws2=torch.empty((D, SF), dtype=torch.float32, device="cuda") if SF else None)
+            M.moe_layer_backward(cfg, dl.weights, dl.x, dy, 0.05, out["dx"], out["dwr"], out["dw13"], out["dw2"],
+                                 out["dws13"], out["dws2"], ws)
+            torch.cuda.synchronize()
+            return {n: to_numpy(t) for n, t in out.items() if t is not None}
+        finally:
+            for k, v in old.items():
+                if v is None:
+                    os.environ.pop(k, None)
+                else:
+                    os.environ[k] = v
+
+    base = run({})
+    for env in ({"MOE_WGRAD_SWZ": "0"}, {"MOE_WGRAD_SWZ": "1"}, {"MOE_WGRAD_TILE": "128"},
+                {"MOE_WGRAD_TILE": "256"}):
+        got = run(env)
+        for n in base:
+            assert np.array_equal(got[n].view(np.uint8), base[n].view(np.uint8)), f"{env}: {n} differs"
