@@ -1021,8 +1021,8 @@ moe_status moe_layer_backward(const moe_config* cfg, const moe_weights* wt, cons
   // combine: dw[t, j] = <dy[t], y_perm[row]>, dy_perm[row] = w[t, j] dy[t]
   MOE_TRY_HIP("combine backward", launch_bw_combine(dyb, yperm, row_of, tw, T, k, D, dwt, dyp, s));
   // routed experts: weights transposed for the data-gradient products
-  MOE_TRY_HIP("transpose w2", launch_transpose_bf16(static_cast<const bf16_t*>(wt->w2), w2t, E, D, F, s));
-  MOE_TRY_HIP("transpose w13", launch_transpose_bf16(static_cast<const bf16_t*>(wt->w13), w13t, E, nF, D, s));
+  MOE_TRY_HIP("transpose w2", launch_transpose_bf16(static_cast<const bf16_t*>(wt->w2), w2t, E, D, F, off, s));
+  MOE_TRY_HIP("transpose w13", launch_transpose_bf16(static_cast<const bf16_t*>(wt->w13), w13t, E, nF, D, off, s));
   if (A > 0) {
     MOE_TRY(bw_gemm("expert gate/up (recomputed)", x, tor, D, wt->w13, (long long)nF * D, gu, nF, A, nF, D, E, off,
                     pre, s));
@@ -1043,8 +1043,8 @@ moe_status moe_layer_backward(const moe_config* cfg, const moe_weights* wt, cons
     bf16_t* ws2t = at<bf16_t>(ws, B.ws2t);
     dxs = at<bf16_t>(ws, B.dxs);
     const bf16_t* hs = at<bf16_t>(fws, L.h_shared);
-    MOE_TRY_HIP("transpose ws2", launch_transpose_bf16(static_cast<const bf16_t*>(wt->ws2), ws2t, 1, D, SF, s));
-    MOE_TRY_HIP("transpose ws13", launch_transpose_bf16(static_cast<const bf16_t*>(wt->ws13), ws13t, 1, 2 * SF, D, s));
+    MOE_TRY_HIP("transpose ws2", launch_transpose_bf16(static_cast<const bf16_t*>(wt->ws2), ws2t, 1, D, SF, nullptr, s));
+    MOE_TRY_HIP("transpose ws13", launch_transpose_bf16(static_cast<const bf16_t*>(wt->ws13), ws13t, 1, 2 * SF, D, nullptr, s));
     MOE_TRY(bw_gemm("shared gate/up (recomputed)", x, nullptr, D, wt->ws13, 0, gus, 2 * SF, T, 2 * SF, D, 1, nullptr,
                     nullptr, s));
     MOE_TRY(bw_gemm("shared dH", dy, nullptr, D, ws2t, 0, dhs, SF, T, SF, D, 1, nullptr, nullptr, s));

@@ -31,9 +31,12 @@ __device__ __forceinline__ float bf(bf16_t v) { return __uint_as_float((uint32_t
 
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16_t* __restrict__ in, bf16_t* __restrict__ out,
-                                                             int R, int C) {
+                                                             int R, int C, const int32_t* __restrict__ offsets) {
   __shared__ bf16_t tile[64][66];
   const long long g = blockIdx.z;
+  // a group without rows is never read transposed (the grouped products
+  // make no tiles for it): skip it (uniform per workgroup)
+  if (offsets != nullptr && offsets[g + 1] == offsets[g]) return;
   const bf16_t* src = in + g * (long long)R * C;
   bf16_t* dst = out + g * (long long)R * C;
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
@@ -525,9 +528,10 @@ inline unsigned grid_for(long long n) { return (unsigned)std::min<long long>((n 
 
 }  // namespace
 
-hipError_t launch_transpose_bf16(const bf16_t* in, bf16_t* out, int G, int R, int C, hipStream_t s) {
+hipError_t launch_transpose_bf16(const bf16_t* in, bf16_t* out, int G, int R, int C, const int32_t* offsets,
+                                 hipStream_t s) {
   if (G <= 0 || R <= 0 || C <= 0) return hipSuccess;
-  hipLaunchKernelGGL(transpose_bf16_kernel, dim3(ceil_div(C, 64), ceil_div(R, 64), G), dim3(256), 0, s, in, out, R, C);
+  hipLaunchKernelGGL(transpose_bf16_kernel, dim3(ceil_div(C, 64), ceil_div(R, 64), G), dim3(256), 0, s, in, out, R, C, offsets);
   return hipGetLastError();
 }
 

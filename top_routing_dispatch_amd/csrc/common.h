@@ -326,7 +326,8 @@ hipError_t launch_ec_combine(const void* y_perm, const float* pT, const uint32_t
                              const void* y_shared, void* y, int T, int E, int C, int D, int act_dtype,
                              int32_t* unselected, hipStream_t s);
 // Backward pass kernels (backward.hip).
-hipError_t launch_transpose_bf16(const bf16_t* in, bf16_t* out, int G, int R, int C, hipStream_t s);
+hipError_t launch_transpose_bf16(const bf16_t* in, bf16_t* out, int G, int R, int C, const int32_t* offsets,
+                                 hipStream_t s);
 hipError_t launch_bw_combine(const bf16_t* dy, const bf16_t* yp, const int32_t* row_of, const float* tw, int T, int k,
                              int D, float* dw, bf16_t* dyp, hipStream_t s);
 hipError_t launch_bw_act(const bf16_t* gu, const bf16_t* dh, bf16_t* dgu, const int32_t* rows_valid, int rows_max,
