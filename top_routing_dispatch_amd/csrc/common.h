@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stddef.h>
+#include <atomic>
 
 namespace moe {
 
@@ -59,7 +60,8 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
 
 // Compute units of the current device (cached after the first call).
 inline int num_cus() {
-  static int n = 0;
+  static std::atomic<int> cached{0};     // host threads may race to fill it: same value
+  int n = cached.load(std::memory_order_relaxed);
   if (n == 0) {
     int dev = 0, v = 0;
     if (hipGetDevice(&dev) == hipSuccess &&
@@ -67,6 +69,7 @@ inline int num_cus() {
       n = v;
     else
       n = 256;
+    cached.store(n, std::memory_order_relaxed);
   }
   return n;
 }

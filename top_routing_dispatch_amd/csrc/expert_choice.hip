@@ -253,15 +253,15 @@ hipError_t launch_ec_route(const float* logits, int T, int E, int C, float* pT, 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t lds = ec_select_lds(T);
-  static bool allowed[64] = {};
+  static std::atomic<bool> allowed[64];   // per device: attribute set (host threads may race)
   int dev = 0;
   e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64 || !allowed[dev]) {
+  if (dev < 0 || dev >= 64 || !allowed[dev].load(std::memory_order_relaxed)) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&ec_select_kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)ec_select_lds(kEcMaxTokens));
     if (e != hipSuccess) return e;
-    if (dev >= 0 && dev < 64) allowed[dev] = true;
+    if (dev >= 0 && dev < 64) allowed[dev].store(true, std::memory_order_relaxed);
   }
   hipLaunchKernelGGL(ec_select_kernel, dim3((unsigned)E), dim3(1024), lds, s, pT, T, C, ec_sort_keys(T),
                      token_of_row, row_w, selbits, selpre);

@@ -238,15 +238,15 @@ hipError_t launch_cfg(const GroupedGemm& p, hipStream_t s) {
   const long long blocks = (long long)m_tiles * n_tiles;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   // dynamic LDS above 64 KB has to be allowed explicitly, once per device
-  static bool allowed[64] = {};
+  static std::atomic<bool> allowed[64];   // per device: attribute set (host threads may race)
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64 || !allowed[dev]) {
+  if (dev < 0 || dev >= 64 || !allowed[dev].load(std::memory_order_relaxed)) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_v2_kernel<BM, BN, WGM, WGN, NST, EPI, bf16_t>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, C::STAGE * NST);
     if (e != hipSuccess) return e;
-    if (dev >= 0 && dev < 64) allowed[dev] = true;
+    if (dev >= 0 && dev < 64) allowed[dev].store(true, std::memory_order_relaxed);
   }
   hipLaunchKernelGGL((gemm_v2_kernel<BM, BN, WGM, WGN, NST, EPI, bf16_t>), dim3((unsigned)blocks),
                      dim3(C::THREADS), C::STAGE * NST, s, p, n_tiles);

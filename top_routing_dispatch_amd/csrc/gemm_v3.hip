@@ -394,15 +394,15 @@ hipError_t launch_cfg3(const GroupedGemm& p, hipStream_t s) {
     blocks = 4LL * p.round;            // the partial round holds fewer than `round` parent tiles
   }
   // dynamic LDS above 64 KB has to be allowed explicitly, once per device
-  static bool allowed[64] = {};
+  static std::atomic<bool> allowed[64];   // per device: attribute set (host threads may race)
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64 || !allowed[dev]) {
+  if (dev < 0 || dev >= 64 || !allowed[dev].load(std::memory_order_relaxed)) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_v3_kernel<BM, BN, WGM, WGN, BK, NST, NSTB, OCC, PERS, EPI, bf16_t>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
     if (e != hipSuccess) return e;
-    if (dev >= 0 && dev < 64) allowed[dev] = true;
+    if (dev >= 0 && dev < 64) allowed[dev].store(true, std::memory_order_relaxed);
   }
   hipLaunchKernelGGL((gemm_v3_kernel<BM, BN, WGM, WGN, BK, NST, NSTB, OCC, PERS, EPI, bf16_t>), dim3((unsigned)blocks),
                      dim3(C::THREADS), C::LDS, s, p, n_tiles);

@@ -475,18 +475,18 @@ hipError_t launch_ws(const GroupedGemm& p, hipStream_t s) {
   const long long bound = tiles * KS;
   if (bound > 0x7fffffffLL) return hipErrorInvalidValue;
   const int blocks = (int)std::min<long long>(bound, (long long)num_cus() * OCC);
-  static bool allowed[64] = {};
+  static std::atomic<bool> allowed[64];   // per device: attribute set (host threads may race)
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64 || !allowed[dev]) {
+  if (dev < 0 || dev >= 64 || !allowed[dev].load(std::memory_order_relaxed)) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_ws_kernel<BM, BN, WGM, WGN, BK, NST, OCC, EPI, false>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
     if (e != hipSuccess) return e;
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_ws_kernel<BM, BN, WGM, WGN, BK, NST, OCC, EPI, true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
     if (e != hipSuccess) return e;
-    if (dev >= 0 && dev < 64) allowed[dev] = true;
+    if (dev >= 0 && dev < 64) allowed[dev].store(true, std::memory_order_relaxed);
   }
   if (KS == 1) {
     hipLaunchKernelGGL((gemm_ws_kernel<BM, BN, WGM, WGN, BK, NST, OCC, EPI, false>), dim3((unsigned)blocks),

@@ -151,15 +151,15 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const bf16_t* __rest
 template <int BN, int NP>
 hipError_t launch_router_cfg(const bf16_t* x, const bf16_t* w, float* logits, int T, int E, int D, hipStream_t s) {
   using C = RCfg<BN, NP>;
-  static bool allowed[64] = {};
+  static std::atomic<bool> allowed[64];   // per device: attribute set (host threads may race)
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64 || !allowed[dev]) {
+  if (dev < 0 || dev >= 64 || !allowed[dev].load(std::memory_order_relaxed)) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&router_logits_kernel<BN, NP>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, C::STAGE * C::NST);
     if (e != hipSuccess) return e;
-    if (dev >= 0 && dev < 64) allowed[dev] = true;
+    if (dev >= 0 && dev < 64) allowed[dev].store(true, std::memory_order_relaxed);
   }
   hipLaunchKernelGGL((router_logits_kernel<BN, NP>), dim3(ceil_div(T, C::BM)), dim3(256), C::STAGE * C::NST, s, x, w,
                      logits, T, E, D);
@@ -349,15 +349,15 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const bf16_t* __restri
 template <int NP>
 hipError_t launch_router_gemv(const bf16_t* x, const bf16_t* w, float* logits, int T, int E, int D, hipStream_t s) {
   const int lds = T * D * 2;
-  static bool allowed[64] = {};
+  static std::atomic<bool> allowed[64];   // per device: attribute set (host threads may race)
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64 || !allowed[dev]) {
+  if (dev < 0 || dev >= 64 || !allowed[dev].load(std::memory_order_relaxed)) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&router_gemv_kernel<NP>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kGemvLds);
     if (e != hipSuccess) return e;
-    if (dev >= 0 && dev < 64) allowed[dev] = true;
+    if (dev >= 0 && dev < 64) allowed[dev].store(true, std::memory_order_relaxed);
   }
   hipLaunchKernelGGL((router_gemv_kernel<NP>), dim3(ceil_div(E, 4)), dim3(256), lds, s, x, w, logits, T, E, D);
   static_assert(kGemvLds <= 160 * 1024, "LDS");
