@@ -544,7 +544,7 @@ moe_status aux_stream(AuxStream** out) {
 // Backward -----------------------------------------------------------------
 struct BwLayout {
   size_t fwd, y, dyp, gu, dh, dgu, dxp, w13t, w2t, ones, dw, dlogits, dxr, rpart, pre, gus, dhs, dgus, dxs, ws13t,
-      ws2t, total;
+      ws2t, rplanes, rplanes_t, raux, total;
 };
 
 BwLayout bw_layout(const moe_config* c, const Derived& d) {
@@ -567,7 +567,7 @@ BwLayout bw_layout(const moe_config* c, const Derived& d) {
   B.dw = take(T * k * 4);
   B.dlogits = take(T * E * 4);
   B.dxr = take(T * D * 4);
-  B.rpart = take((size_t)kF32MaxSplit * E * D * 4);
+  B.rpart = take((size_t)std::max(kF32MaxSplit, 3 * kRouterMfmaSplit) * E * D * 4);
   B.pre = take(2 * (E + 1) * 4);
   B.gus = take(T * 2 * SF * 2);
   B.dhs = take(T * SF * 2);
@@ -575,6 +575,9 @@ BwLayout bw_layout(const moe_config* c, const Derived& d) {
   B.dxs = take(T * D * 2);
   B.ws13t = take(2 * SF * D * 2);
   B.ws2t = take(SF * D * 2);
+  B.rplanes = take(T * 3 * E * 2);
+  B.rplanes_t = take(T * 3 * E * 2);
+  B.raux = take((kRouterMfmaSplit + 1 + 3 * E) * 4);
   B.total = o;
   return B;
 }
@@ -1056,11 +1059,23 @@ moe_status moe_layer_backward(const moe_config* cfg, const moe_weights* wt, cons
   // router: d loss / d logits, then its weight and input gradients
   MOE_TRY_HIP("router backward", launch_router_grad(logits, idx, tw, dwt, counts, T, E, k, cfg->scoring,
                                                     cfg->renormalize, alpha, dlog, s));
-  MOE_TRY_HIP("router dW", launch_gemm_f32_strided(dlog, 1, E, x, true, D, 1, E, D, T, dw_router,
-                                                   at<float>(ws, B.rpart), s));
+  // on the matrix cores where the shapes allow (the exact three-plane split
+  // of the logit gradients keeps every product exact), else float32 FMA
   float* dxr = at<float>(ws, B.dxr);
-  MOE_TRY_HIP("router dx", launch_gemm_f32_strided(dlog, E, 1, wt->w_router, cfg->router_dtype == BF16, D, 1, T, D,
-                                                   E, dxr, nullptr, s));
+  const bool mfma_dw = E % 4 == 0 && D % 4 == 0;
+  const bool mfma_dx = mfma_dw && T % 4 == 0 && cfg->router_dtype == BF16;
+  if (mfma_dw) {
+    MOE_TRY_HIP("router gradients", launch_router_grad_mfma(dlog, xb, static_cast<const bf16_t*>(wt->w_router), T, E,
+                                                            D, dw_router, mfma_dx ? dxr : nullptr,
+                                                            at<bf16_t>(ws, B.rplanes), at<bf16_t>(ws, B.rplanes_t),
+                                                            at<int32_t>(ws, B.raux), at<float>(ws, B.rpart), s));
+  } else {
+    MOE_TRY_HIP("router dW", launch_gemm_f32_strided(dlog, 1, E, x, true, D, 1, E, D, T, dw_router,
+                                                     at<float>(ws, B.rpart), s));
+  }
+  if (!mfma_dx)
+    MOE_TRY_HIP("router dx", launch_gemm_f32_strided(dlog, E, 1, wt->w_router, cfg->router_dtype == BF16, D, 1, T,
+                                                     D, E, dxr, nullptr, s));
   // dx = sum of the token's expert rows (weight 1) + shared + router
   float* ones = at<float>(ws, B.ones);
   MOE_TRY_HIP("ones", launch_fill_f32(ones, 1.0f, (long long)T * k, s));

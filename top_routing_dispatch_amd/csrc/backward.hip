@@ -624,6 +624,51 @@ hipError_t launch_gemm_f32_strided(const float* A, long long am, long long ak, c
   return hipGetLastError();
 }
 
+// Chunk bounds of a split contraction (offsets[g] = min(g * chunk, T)) and
+// the plane row map r -> r mod E of the router's input gradient.
+__global__ __launch_bounds__(256) void router_mfma_aux_kernel(int32_t* __restrict__ offsets, int G, int chunk, int T,
+                                                              int32_t* __restrict__ rmap, int E3, int E) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i <= G + E3; i += gridDim.x * 256) {
+    if (i <= G) offsets[i] = min(i * chunk, T);
+    else rmap[i - G - 1] = (i - G - 1) % E;
+  }
+}
+
+hipError_t launch_router_grad_mfma(const float* dlog, const bf16_t* x, const bf16_t* w_router, int T, int E, int D,
+                                   float* dw_router, float* dx_router, bf16_t* planes, bf16_t* planes_t,
+                                   int32_t* aux, float* partial, hipStream_t s) {
+  if (T <= 0 || E <= 0 || D <= 0) return hipSuccess;
+  const int E3 = 3 * E;
+  if (E3 % 4 != 0 || D % 4 != 0 || (dx_router != nullptr && (T % 4 != 0 || w_router == nullptr)))
+    return hipErrorInvalidValue;
+  hipError_t e = launch_split_bf16x3(dlog, T, E, planes, s);      // [T][3][E]: plane p of logit e at column p E + e
+  if (e != hipSuccess) return e;
+  // token chunks, so that the output tiles times the chunks fill the chip
+  const int bt = (E3 >= 256 && D >= 256) ? 256 : 128;
+  const int tiles = ceil_div(E3, bt) * ceil_div(D, bt);
+  int G = std::min(kRouterMfmaSplit, std::max(1, ceil_div(2 * num_cus(), tiles)));
+  G = std::min(G, std::max(1, T / 256));
+  const int chunk = ceil_div(ceil_div(T, G), 32) * 32;
+  G = ceil_div(T, chunk);
+  int32_t* offsets = aux;
+  int32_t* rmap = aux + kRouterMfmaSplit + 1;
+  hipLaunchKernelGGL(router_mfma_aux_kernel, dim3(ceil_div(G + 1 + E3, 256)), dim3(256), 0, s, offsets, G, chunk, T,
+                     rmap, E3, E);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // dW_router: parts [G][3][E][D] over the token chunks and planes, added in that order
+  e = launch_wgrad(planes, E3, x, D, nullptr, offsets, G, T, E3, D, partial, s);
+  if (e != hipSuccess) return e;
+  const long long n = (long long)E * D;
+  hipLaunchKernelGGL(sum_parts_kernel, dim3(grid_for(n)), dim3(256), 0, s, partial, 3 * G, n, dw_router);
+  e = hipGetLastError();
+  if (e != hipSuccess || dx_router == nullptr) return e;
+  // dx_router [T][D] = sum over the 3E plane rows r of planes_t[r][t] w_router[r mod E][d]
+  e = launch_transpose_bf16(planes, planes_t, 1, T, E3, nullptr, s);
+  if (e != hipSuccess) return e;
+  return launch_wgrad(planes_t, T, w_router, D, rmap, nullptr, 1, E3, T, D, dx_router, s);
+}
+
 hipError_t launch_add_f32_to_bf16(bf16_t* y, const float* add, long long n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(add_f32_to_bf16_kernel, dim3(grid_for(n)), dim3(256), 0, s, y, add, n);

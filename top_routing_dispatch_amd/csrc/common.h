@@ -346,6 +346,16 @@ constexpr int kF32MaxSplit = 32;
 hipError_t launch_gemm_f32_strided(const float* A, long long am, long long ak, const void* B, bool b_bf16,
                                    long long bk, long long bn, int M, int N, int K, float* C, float* partial,
                                    hipStream_t s);
+// Router gradients on the matrix cores: dlogits [T, E] (float32) split
+// exactly into three bf16 planes; dW_router [E, D] = dlogits^T x over up to
+// kRouterMfmaSplit token chunks (partial: room for 3 kRouterMfmaSplit E D
+// floats), and, when dx_router is given (T % 4 == 0, bf16 w_router [E, D]),
+// dx_router [T, D] = dlogits w_router.  planes [T][3E], planes_t [3E][T],
+// aux: kRouterMfmaSplit + 1 + 3E ints.  E % 4 == 0 and D % 4 == 0.
+constexpr int kRouterMfmaSplit = 10;
+hipError_t launch_router_grad_mfma(const float* dlog, const bf16_t* x, const bf16_t* w_router, int T, int E, int D,
+                                   float* dw_router, float* dx_router, bf16_t* planes, bf16_t* planes_t,
+                                   int32_t* aux, float* partial, hipStream_t s);
 hipError_t launch_add_f32_to_bf16(bf16_t* y, const float* add, long long n, hipStream_t s);
 hipError_t launch_fill_f32(float* p, float v, long long n, hipStream_t s);
 // Expert-parallel send / receive layouts (ep.hip).
