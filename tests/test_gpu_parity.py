@@ -777,6 +777,8 @@ BW_SHAPES = [
                 renormalize=1, zipf_s=1.2),
     W.MoEConfig("bw_sigmoid_raw_capacity", 150, 64, 8, 2, 96, scoring=W.SIGMOID_BIAS, renormalize=0,
                 capacity_factor=0.8),
+    # E not a multiple of 4: the router gradients take the float32 path
+    W.MoEConfig("bw_six_experts", 96, 64, 6, 2, 64, scoring=W.SOFTMAX_TOPK, renormalize=1),
 ]
 # Gradient tolerance (none is stated for the backward): the forward's 2e-2
 # covers a chain of three bf16 roundings (H, y_perm, y); the input gradient
