@@ -827,10 +827,13 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* wt, const
                                  stream, nullptr);
 }
 
-moe_status moe_layer_forward_timed(const moe_config* cfg, const moe_weights* wt, const void* x, void* y,
-                                   int32_t* topk_idx, float* topk_w, int32_t* counts, float alpha, float* stats,
-                                   int32_t* dropped, void* ws, size_t ws_bytes, void* stream,
-                                   void* const* ev) {
+// The layer forward; routing_only: stop after the permutation (routing,
+// selection and dispatch tables in the workspace, no expert or shared work:
+// the backward runs the expert products itself).
+static moe_status layer_forward_impl(const moe_config* cfg, const moe_weights* wt, const void* x, void* y,
+                                     int32_t* topk_idx, float* topk_w, int32_t* counts, float alpha, float* stats,
+                              int32_t* dropped, void* ws, size_t ws_bytes, void* stream, void* const* ev,
+                              bool routing_only) {
   MOE_TRY(validate_config(cfg));
   if (wt == nullptr || wt->w_router == nullptr || wt->w13 == nullptr || wt->w2 == nullptr)
     return MOE_ERR_INVALID_ARGUMENT;
@@ -863,7 +866,7 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const moe_weights* wt,
   // auxiliary stream while routing and permutation (short, latency-bound
   // kernels that leave most of the chip idle) run here, and is joined before
   // the routed experts, which need the whole chip.
-  const bool shared = any && cfg->num_shared > 0;
+  const bool shared = !routing_only && any && cfg->num_shared > 0;
   const int SF = cfg->num_shared * cfg->d_ff_shared;
   const int overlap = shared ? shared_overlap() : 0;
   // The load statistics need only the probabilities and the counts: they run
@@ -906,6 +909,7 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const moe_weights* wt,
   MOE_TRY(mark(ev, MOE_STAGE_PERMUTE, 0, s));
   MOE_TRY_HIP("permute", launch_permute(pa, s));
   MOE_TRY(mark(ev, MOE_STAGE_PERMUTE, 1, s));
+  if (routing_only) return MOE_OK;
 
   StatsArgs sa{};
   if (want_stats) {
@@ -955,6 +959,15 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const moe_weights* wt,
   return MOE_OK;
 }
 
+
+moe_status moe_layer_forward_timed(const moe_config* cfg, const moe_weights* wt, const void* x, void* y,
+                                   int32_t* topk_idx, float* topk_w, int32_t* counts, float alpha, float* stats,
+                                   int32_t* dropped, void* ws, size_t ws_bytes, void* stream,
+                                   void* const* ev) {
+  return layer_forward_impl(cfg, wt, x, y, topk_idx, topk_w, counts, alpha, stats, dropped, ws, ws_bytes, stream,
+                            ev, false);
+}
+
 moe_status moe_layer_backward(const moe_config* cfg, const moe_weights* wt, const void* x, const void* dy,
                               float alpha, void* dx, float* dw_router, float* dw13, float* dw2, float* dws13,
                               float* dws2, void* ws, size_t ws_bytes, void* stream) {
@@ -994,19 +1007,21 @@ moe_status moe_layer_backward(const moe_config* cfg, const moe_weights* wt, cons
     }
     return MOE_OK;
   }
-  // forward recomputation: routing, permutation, expert activations
+  // forward recomputation: routing and permutation, then the expert products
+  // below (the gate/up product is stored before the activation, which the
+  // backward needs, and the activation is applied to it elementwise)
   void* fws = at<void>(ws, B.fwd);
   const Layout L = layer_layout(cfg, d);
-  MOE_TRY(moe_layer_forward_timed(cfg, wt, x, at<void>(ws, B.y), nullptr, nullptr, nullptr, alpha, nullptr, nullptr,
-                                  fws, L.total, stream, nullptr));
+  MOE_TRY(layer_forward_impl(cfg, wt, x, at<void>(ws, B.y), nullptr, nullptr, nullptr, alpha, nullptr, nullptr, fws,
+                             L.total, stream, nullptr, true));
   const int32_t* idx = at<int32_t>(fws, L.idx);
   const float* tw = at<float>(fws, L.w);
   const int32_t* counts = at<int32_t>(fws, L.counts);
   const int32_t* off = at<int32_t>(fws, L.offsets);
   const int32_t* row_of = at<int32_t>(fws, L.row_of);
   const int32_t* tor = at<int32_t>(fws, L.tor);
-  const bf16_t* h = at<bf16_t>(fws, L.h);
-  const bf16_t* yperm = at<bf16_t>(fws, L.yperm);
+  bf16_t* h = at<bf16_t>(fws, L.h);
+  bf16_t* yperm = at<bf16_t>(fws, L.yperm);
   const float* logits = at<float>(fws, L.logits);
   bf16_t* dyp = at<bf16_t>(ws, B.dyp);
   bf16_t* gu = at<bf16_t>(ws, B.gu);
@@ -1021,14 +1036,19 @@ moe_status moe_layer_backward(const moe_config* cfg, const moe_weights* wt, cons
   const bf16_t* xb = static_cast<const bf16_t*>(x);
   const bf16_t* dyb = static_cast<const bf16_t*>(dy);
 
+  if (A > 0) {
+    MOE_TRY(bw_gemm("expert gate/up (recomputed)", x, tor, D, wt->w13, (long long)nF * D, gu, nF, A, nF, D, E, off,
+                    pre, s));
+    MOE_TRY_HIP("expert activation (recomputed)", launch_act_fwd(gu, h, off + E, A, F, swiglu, s));
+    MOE_TRY(bw_gemm("expert down (recomputed)", h, nullptr, F, wt->w2, (long long)D * F, yperm, D, A, D, F, E, off,
+                    pre, s));
+  }
   // combine: dw[t, j] = <dy[t], y_perm[row]>, dy_perm[row] = w[t, j] dy[t]
   MOE_TRY_HIP("combine backward", launch_bw_combine(dyb, yperm, row_of, tw, T, k, D, dwt, dyp, s));
   // routed experts: weights transposed for the data-gradient products
   MOE_TRY_HIP("transpose w2", launch_transpose_bf16(static_cast<const bf16_t*>(wt->w2), w2t, E, D, F, off, s));
   MOE_TRY_HIP("transpose w13", launch_transpose_bf16(static_cast<const bf16_t*>(wt->w13), w13t, E, nF, D, off, s));
   if (A > 0) {
-    MOE_TRY(bw_gemm("expert gate/up (recomputed)", x, tor, D, wt->w13, (long long)nF * D, gu, nF, A, nF, D, E, off,
-                    pre, s));
     MOE_TRY(bw_gemm("expert dH", dyp, nullptr, D, w2t, (long long)F * D, dh, F, A, F, D, E, off, pre, s));
     MOE_TRY_HIP("activation backward", launch_bw_act(gu, dh, dgu, off + E, A, F, swiglu, s));
     MOE_TRY(bw_gemm("expert dX", dgu, nullptr, nF, w13t, (long long)D * nF, dxp, D, A, D, nF, E, off, pre + (E + 1),
@@ -1045,11 +1065,12 @@ moe_status moe_layer_backward(const moe_config* cfg, const moe_weights* wt, cons
     bf16_t* ws13t = at<bf16_t>(ws, B.ws13t);
     bf16_t* ws2t = at<bf16_t>(ws, B.ws2t);
     dxs = at<bf16_t>(ws, B.dxs);
-    const bf16_t* hs = at<bf16_t>(fws, L.h_shared);
+    bf16_t* hs = at<bf16_t>(fws, L.h_shared);
     MOE_TRY_HIP("transpose ws2", launch_transpose_bf16(static_cast<const bf16_t*>(wt->ws2), ws2t, 1, D, SF, nullptr, s));
     MOE_TRY_HIP("transpose ws13", launch_transpose_bf16(static_cast<const bf16_t*>(wt->ws13), ws13t, 1, 2 * SF, D, nullptr, s));
     MOE_TRY(bw_gemm("shared gate/up (recomputed)", x, nullptr, D, wt->ws13, 0, gus, 2 * SF, T, 2 * SF, D, 1, nullptr,
                     nullptr, s));
+    MOE_TRY_HIP("shared activation (recomputed)", launch_act_fwd(gus, hs, nullptr, T, SF, true, s));
     MOE_TRY(bw_gemm("shared dH", dy, nullptr, D, ws2t, 0, dhs, SF, T, SF, D, 1, nullptr, nullptr, s));
     MOE_TRY_HIP("shared activation backward", launch_bw_act(gus, dhs, dgus, nullptr, T, SF, true, s));
     MOE_TRY(bw_gemm("shared dX", dgus, nullptr, 2 * SF, ws13t, 0, dxs, D, T, D, 2 * SF, 1, nullptr, nullptr, s));

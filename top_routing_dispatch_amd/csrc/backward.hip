@@ -542,6 +542,49 @@ hipError_t launch_bw_combine(const bf16_t* dy, const bf16_t* yp, const int32_t* 
   return hipGetLastError();
 }
 
+// h [rows, F] from the stored pre-activations gu [rows, nF]: SwiGLU
+// silu(g) * u, GELU gelu(g), in float32, rounded to bf16 (the functions of
+// the forward's GEMM epilogues); rows = *rows_valid (or rows_max).
+__global__ __launch_bounds__(256) void act_fwd_kernel(const bf16_t* __restrict__ gu, bf16_t* __restrict__ h,
+                                                      const int32_t* __restrict__ rows_valid, int rows_max, int F,
+                                                      int swiglu) {
+  const int rows = rows_valid ? min(*rows_valid, rows_max) : rows_max;
+  const int F8 = F / 8;
+  const long long n = (long long)rows * F8;
+  const int ldg = swiglu ? 2 * F : F;
+  for (long long i = blockIdx.x * 256LL + threadIdx.x; i < n; i += (long long)gridDim.x * 256) {
+    const long long r = i / F8;
+    const int f = (int)(i % F8) * 8;
+    const uint4 gq = *reinterpret_cast<const uint4*>(gu + r * ldg + f);
+    const uint4 uq = swiglu ? *reinterpret_cast<const uint4*>(gu + r * ldg + F + f) : make_uint4(0u, 0u, 0u, 0u);
+    const uint32_t gw[4] = {gq.x, gq.y, gq.z, gq.w}, uw[4] = {uq.x, uq.y, uq.z, uq.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t a = 0;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float g = __uint_as_float(e ? (gw[q] & 0xffff0000u) : (gw[q] << 16));
+        float v;
+        if (swiglu) v = silu_f32(g) * __uint_as_float(e ? (uw[q] & 0xffff0000u) : (uw[q] << 16));
+        else v = gelu_bf16out(g);
+        a |= (uint32_t)f32_to_bf16_rn(v) << (16 * e);
+      }
+      o[q] = a;
+    }
+    *reinterpret_cast<uint4*>(h + r * F + f) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+hipError_t launch_act_fwd(const bf16_t* gu, bf16_t* h, const int32_t* rows_valid, int rows_max, int F, bool swiglu,
+                          hipStream_t s) {
+  if (rows_max <= 0) return hipSuccess;
+  if (F % 8 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(act_fwd_kernel, dim3(grid_for((long long)rows_max * (F / 8))), dim3(256), 0, s, gu, h,
+                     rows_valid, rows_max, F, swiglu ? 1 : 0);
+  return hipGetLastError();
+}
+
 hipError_t launch_bw_act(const bf16_t* gu, const bf16_t* dh, bf16_t* dgu, const int32_t* rows_valid, int rows_max,
                          int F, bool swiglu, hipStream_t s) {
   if (rows_max <= 0) return hipSuccess;

@@ -333,6 +333,8 @@ hipError_t launch_transpose_bf16(const bf16_t* in, bf16_t* out, int G, int R, in
                                  hipStream_t s);
 hipError_t launch_bw_combine(const bf16_t* dy, const bf16_t* yp, const int32_t* row_of, const float* tw, int T, int k,
                              int D, float* dw, bf16_t* dyp, hipStream_t s);
+hipError_t launch_act_fwd(const bf16_t* gu, bf16_t* h, const int32_t* rows_valid, int rows_max, int F, bool swiglu,
+                          hipStream_t s);
 hipError_t launch_bw_act(const bf16_t* gu, const bf16_t* dh, bf16_t* dgu, const int32_t* rows_valid, int rows_max,
                          int F, bool swiglu, hipStream_t s);
 hipError_t launch_wgrad(const bf16_t* A, int lda, const bf16_t* B, int ldb, const int32_t* b_rows,
