@@ -166,6 +166,20 @@ def copy_rate(mib=1024, reps=5):
     return dict(kernel="torch.neg float32, 1 GiB read + 1 GiB written", gbps=round(8 * n / (ms * 1e-3) / 1e9, 1))
 
 
+def gpu_clocks():
+    """The GPU's current clocks as rocm-smi reports them (card 0), or None when
+    the tool is missing or fails: context for the roofline fractions, which
+    use the published peaks."""
+    import subprocess
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=15)
+        data = json.loads(out.stdout)
+        card = data.get("card0") or next(iter(data.values()))
+        return {k.strip(" :"): v for k, v in card.items() if "clock" in k.lower() or "clk" in k.lower()}
+    except Exception:
+        return None
+
+
 def cpu_baseline(cfg, inp, sample_tokens, expert_choice=False):
     """The oracle as it stands, on the first `sample_tokens` tokens (expert
     choice: those tokens as a batch of their own, C recomputed for it)."""
@@ -373,6 +387,7 @@ def main():
         ref = copy_rate()
         ref["achieved_over_copy"] = round(roof["achieved"] / ref["gbps"], 4)
         roof["copy_ref"] = ref
+    roof["clocks"] = gpu_clocks()
 
     cpu = None
     if not args.no_cpu_baseline:
