@@ -35,6 +35,16 @@
  *   - Size limits: 1 <= E <= 1024, 1 <= k <= min(E, 32), D and F multiples of
  *     8 (of 4 for MOE_F32 activations), T >= 0.  Outside: MOE_ERR_UNSUPPORTED
  *     (or MOE_ERR_INVALID_ARGUMENT for values that are meaningless).
+ *   - Operand spans: the kernels address each matrix operand with 32-bit
+ *     byte offsets, so every one of them must span at most 0xFFE00000 bytes
+ *     (4 GiB - 2 MiB): x [T, D]; the permuted rows [A_cap, D] and the
+ *     activations [A_cap, F]; one expert's w13 [n_mat F, D] and w2 [D, F];
+ *     the router weight as [E, 3 D] float32; the shared experts' [T, S F_s],
+ *     [2 S F_s, D] and [D, S F_s]; for the backward also [A_cap, n_mat F]
+ *     and [T, 2 S F_s] bfloat16.  A configuration past any of them is
+ *     rejected with MOE_ERR_UNSUPPORTED by every call that takes it
+ *     (moe_capacity and moe_workspace_size included), before any launch.
+ *     Example: at D = 7168, k = 8 (bf16, dropless) T may be at most 37,430.
  */
 #ifndef MOE_H
 #define MOE_H

@@ -140,3 +140,74 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         B.lib()
+
+
+def _tiny_layer_args(cfg, dev="cpu"):
+    import torch
+    T, D, E, k, F = cfg.num_tokens, cfg.d_model, cfg.num_experts, cfg.top_k, cfg.d_ff
+    act = torch.bfloat16
+    w = dict(w_router=torch.zeros(E, D, dtype=act), sel_bias=None, w13=torch.zeros(E, 2 * F, D, dtype=act),
+             w2=torch.zeros(E, D, F, dtype=act), ws13=None, ws2=None)
+    x = torch.zeros(T, D, dtype=act)
+    y = torch.zeros(T, D, dtype=act)
+    ws = torch.zeros(M.moe_workspace_size(cfg, M.MOE_OP_LAYER), dtype=torch.uint8)
+    return w, x, y, ws
+
+
+def test_binding_rejects_host_tensors_before_the_call():
+    cfg = W.MoEConfig("v", 16, 64, 4, 2, 32)
+    w, x, y, ws = _tiny_layer_args(cfg)
+    with pytest.raises(ValueError, match="must be on the GPU"):
+        M.moe_layer_forward(cfg, w, x, y, ws=ws)
+
+
+@pytest.mark.parametrize("bad", ["dtype", "short", "transposed", "missing_weight", "short_ws", "idx_dtype"])
+def test_binding_checks_types_and_sizes(monkeypatch, bad):
+    """With the device check stubbed out (no GPU here), every other host check
+    must still reject a bad argument before the library is called."""
+    import torch
+    monkeypatch.setattr(B, "_on_device", lambda t: True)
+    called = []
+    monkeypatch.setattr(B, "_check", lambda fn, st: called.append(fn))
+    cfg = W.MoEConfig("v", 16, 64, 4, 2, 32)
+    w, x, y, ws = _tiny_layer_args(cfg)
+    idx = torch.zeros(16, 2, dtype=torch.int32)
+    if bad == "dtype":
+        x = x.float()
+    elif bad == "short":
+        y = y[:-1]
+    elif bad == "transposed":
+        x = torch.zeros(64, 16, dtype=torch.bfloat16).t()
+    elif bad == "missing_weight":
+        w["w2"] = None
+    elif bad == "short_ws":
+        ws = ws[:-256]
+    elif bad == "idx_dtype":
+        idx = idx.long()
+    with pytest.raises(ValueError):
+        M.moe_layer_forward(cfg, w, x, y, topk_idx=idx, ws=ws)
+    assert set(called) <= {"moe_workspace_size", "moe_capacity"}      # host-side size queries only
+
+
+def test_oversized_operands_rejected_before_launch():
+    """A DeepSeek-V3-shaped layer at T = 131,072: the permuted rows
+    [T k, D] bf16 alone are 15 GB, past the 32-bit byte offsets the kernels
+    address operands with, so every call rejects the configuration up front
+    (the largest T that fits at this shape is 37,430)."""
+    big = W.DEEPSEEKV3.replace(num_tokens=131072)
+    for op in (M.MOE_OP_ROUTE, M.MOE_OP_LAYER, M.MOE_OP_EXPERT_FFN, M.MOE_OP_LAYER_BACKWARD):
+        with pytest.raises(M.MoEError) as ei:
+            M.moe_workspace_size(big, op)
+        assert ei.value.status == M.MOE_ERR_UNSUPPORTED
+    c = B.make_config(big)
+    p = ctypes.c_void_p(0x100000)           # never dereferenced: validation fails first
+    w = B.moe_weights(p.value, p.value, p.value, p.value, p.value, p.value)
+    assert _raw("moe_layer_forward", ctypes.byref(c), ctypes.byref(w), p, p, None, None, None, ctypes.c_float(0.01),
+                None, None, p, 1 << 62, None) == M.MOE_ERR_UNSUPPORTED
+    assert M.moe_capacity(W.DEEPSEEKV3.replace(num_tokens=37430))[1] == 37430 * 8
+    with pytest.raises(M.MoEError):
+        M.moe_capacity(W.DEEPSEEKV3.replace(num_tokens=37431))
+    # x alone past the limit: a wide token matrix with top-1
+    wide = W.MoEConfig("wide", 300000, 7168, 8, 1, 64)
+    with pytest.raises(M.MoEError):
+        M.moe_workspace_size(wide, M.MOE_OP_ROUTE)

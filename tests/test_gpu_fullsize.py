@@ -3,13 +3,20 @@ DeepSeek-V3 shapes), in the launch configuration bench.py times
 (moe_layer_forward on the whole batch):
 
   * expert selection of every token against the float64 oracle (near-tie
-    exemption only), counts, and the full permutation of the oracle's own
-    selection, bit-exact;
+    exemption only; at an exempt token the oracle's later steps are re-run
+    on the GPU's choice): weights, counts, drops and the load statistics of
+    every token, and the full permutation of the oracle's own selection,
+    bit-exact;
   * the float32 router logits the selection starts from, against float64:
     the error must sit far inside the margin that triggers the float64
     near-tie refinement;
-  * layer outputs on a seeded sample of tokens, each computed by the oracle
-    expert by expert (only the experts the sample uses are widened).
+  * layer outputs of the tokens of the first and last row of every active
+    expert (so every expert and every tile class of the grouped GEMM
+    launches is covered) plus a seeded random sample, each computed by the
+    oracle expert by expert (only the experts the sample uses are widened).
+
+The oracle widens every active expert's weights once (about 0.2 s each at
+the DeepSeek-V3 shape), so these tests carry their own time limit.
 """
 import numpy as np
 import pytest
@@ -20,8 +27,8 @@ import workloads as W
 from oracle import moe_oracle as O
 from workloads.torch_io import act_torch_dtype, to_numpy, to_torch, upload_experts
 
-from parity import (W_TOL, ec_check_selection, ec_oracle_output, out_tol, refinement_margin, rel_err,
-                    route_differences, row_rel_err)
+from parity import (W_TOL, check_stats, ec_check_selection, ec_oracle_output, out_tol, refinement_margin, rel_err,
+                    rerun_on_choice, route_differences, row_rel_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -41,12 +48,14 @@ def _experts(name):
     return _EXPERTS[name]
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("name", ["switch", "mixtral", "deepseekmoe", "deepseekv3"])
 def test_full_size_layer(name):
     print(f"[full-size parity] {name}", flush=True)
     _check_full_weights(W.CONFIGS[name], SAMPLE[name])
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("T", W.DECODE_TOKENS)
 @pytest.mark.parametrize("name", ["deepseekv3", "mixtral"])
 def test_decode_full_size(name, T):
@@ -94,22 +103,13 @@ def _check_full_weights(cfg, n_sample):
     gi, gw = to_numpy(idx), to_numpy(tw)
     np.testing.assert_array_equal(gi, to_numpy(idx2))
     diff = route_differences(cfg, ref, gi, inp.sel_bias)
-    same = np.setdiff1d(np.arange(T), diff)
-    assert rel_err(gw[same], ref["w"][same]) <= W_TOL
     print(f"  near-tie tokens {len(diff)}")
-
-    cap = O.capacity(cfg.capacity_factor, T, k, E)
-    disp = O.dispatch(ref["idx"], E, cap)
-    ref_counts = disp["counts"].copy()
-    for t in diff:
-        np.subtract.at(ref_counts, ref["idx"][t], 1)
-        np.add.at(ref_counts, gi[t], 1)
-    np.testing.assert_array_equal(to_numpy(counts), ref_counts)
-    if len(diff) == 0:
-        st = O.load_stats(disp["counts"], ref["probs"], k, cfg.alpha, disp["kept"])
-        g = to_numpy(stats)
-        assert rel_err(g[:E], st["f"]) <= W_TOL and rel_err(g[E:2 * E], st["P"]) <= W_TOL
-        assert int(to_numpy(dropped)[0]) == st["dropped"]
+    # the oracle's steps after the selection, re-run on the GPU's choice at the exempt tokens
+    ch = rerun_on_choice(cfg, ref, gi, diff)
+    disp = ch["disp"]
+    assert rel_err(gw, ch["w"]) <= W_TOL
+    np.testing.assert_array_equal(to_numpy(counts), disp["counts"])
+    check_stats(cfg, ch["stats"], to_numpy(stats), int(to_numpy(dropped)[0]))
 
     # --- permutation of the oracle's selection, bit-exact at full size
     cap_c, rows_cap = M.moe_capacity(cfg)
@@ -120,32 +120,56 @@ def _check_full_weights(cfg, n_sample):
     M.moe_permute(cfg, to_torch(ref["idx"].astype(np.int32), dev), None, c2, off, row_of, tor, None,
                   M.workspace(cfg, M.MOE_OP_PERMUTE, dev))
     torch.cuda.synchronize()
-    A = int(disp["offsets"][-1])
-    np.testing.assert_array_equal(to_numpy(off), disp["offsets"])
-    np.testing.assert_array_equal(to_numpy(row_of), disp["row_of"])
-    np.testing.assert_array_equal(to_numpy(tor)[:A], disp["token_of_row"])
+    own = O.dispatch(ref["idx"], E, O.capacity(cfg.capacity_factor, T, k, E))
+    A = int(own["offsets"][-1])
+    np.testing.assert_array_equal(to_numpy(off), own["offsets"])
+    np.testing.assert_array_equal(to_numpy(row_of), own["row_of"])
+    np.testing.assert_array_equal(to_numpy(tor)[:A], own["token_of_row"])
 
-    # --- sampled outputs, oracle expert by expert
-    rng = np.random.default_rng(1234)
-    cand = same if cfg.capacity_factor <= 0 or len(diff) == 0 else np.array([], dtype=np.int64)
-    sample = np.sort(rng.choice(cand, size=min(n_sample, len(cand)), replace=False))
+    # --- sampled outputs, oracle expert by expert, on the re-run choice
+    sample, why = coverage_sample(cfg, disp, n_sample)
     X = O.widen(inp.x[sample])
     y_ref = np.zeros((len(sample), D))
     users = {}
     for i, t in enumerate(sample):
         for j in range(k):
             if disp["row_of"][t, j] >= 0:
-                users.setdefault(int(ref["idx"][t, j]), []).append((i, j))
+                users.setdefault(int(ch["idx"][t, j]), []).append((i, j))
     for e, lst in users.items():
         rows = [i for i, _ in lst]
         out = O.expert_apply(X[rows], host[e][0], host[e][1], cfg.activation, cfg.d_ff)
         for (i, j), o in zip(lst, out):
-            y_ref[i] += ref["w"][sample[i], j] * o
+            y_ref[i] += ch["w"][sample[i], j] * o
     if cfg.num_shared:
         y_ref += O.shared_experts(inp.x[sample], inp.shared)
+    active = int((disp["kept"] > 0).sum())
+    print(f"  sampled {len(sample)} tokens over {len(users)} of {active} active experts ({why})")
+    assert len(users) == active, "every active expert must have a sampled token"
     err = row_rel_err(to_numpy(y)[sample], y_ref)
-    print(f"  sampled {len(sample)} tokens over {len(users)} experts: max rel err {err:.3e}")
+    print(f"  max rel err {err:.3e}")
     assert err <= out_tol(cfg)
+
+
+def coverage_sample(cfg, disp, n_extra, seed=1234):
+    """Tokens whose outputs are checked: for every expert with kept rows, the
+    token of its first and of its last row (the first and last m-tile of
+    every group, so every tile class of the grouped GEMM launches is hit:
+    deep tiles, shallow weight-streaming groups and the partial tiles at a
+    group's end, where the last-round quarter tiles fall), plus `n_extra`
+    tokens drawn at random."""
+    off, tor = disp["offsets"], disp["token_of_row"]
+    must = set()
+    for e in range(cfg.num_experts):
+        a, b = int(off[e]), int(off[e + 1])
+        if b > a:
+            must.add(int(tor[a]))
+            must.add(int(tor[b - 1]))
+    rng = np.random.default_rng(seed)
+    rest = np.setdiff1d(np.arange(cfg.num_tokens), np.fromiter(must, dtype=np.int64, count=len(must)))
+    extra = rng.choice(rest, size=min(n_extra, len(rest)), replace=False) if len(rest) else []
+    sample = np.sort(np.concatenate([np.fromiter(must, dtype=np.int64, count=len(must)),
+                                     np.asarray(extra, dtype=np.int64)]))
+    return sample, f"first and last row of every expert: {len(must)} tokens, {len(extra)} random"
 
 
 @pytest.mark.parametrize("name", sorted(W.EP_CONFIGS))

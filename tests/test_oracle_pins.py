@@ -155,6 +155,118 @@ def test_near_tie_mask():
 
 
 # --------------------------------------------------------------------------
+# exact widening of stored inputs
+# --------------------------------------------------------------------------
+def test_widen_every_bfloat16_pattern_matches_torch():
+    """All 65,536 bfloat16 bit patterns against torch's own bfloat16 -> float64
+    conversion (NaN patterns stay NaN, signed zeros and infinities keep their
+    sign)."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = O.widen(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert nan.sum() == 2 * 127                      # exponent all ones, mantissa non-zero, both signs
+    np.testing.assert_array_equal(np.isnan(got), nan)
+    np.testing.assert_array_equal(got[~nan], ref[~nan])
+    np.testing.assert_array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_widen_hand_values():
+    """bfloat16 = sign, 8 exponent bits (bias 127), 7 mantissa bits."""
+    cases = {0x3F80: 1.0, 0xC049: -3.140625, 0x0001: 2.0 ** -133, 0x0080: 2.0 ** -126,
+             0x7F7F: (2 - 2.0 ** -7) * 2.0 ** 127, 0x8000: -0.0, 0x7F80: math.inf, 0xFF80: -math.inf,
+             0x3E80: 0.25, 0x4120: 10.0}
+    bits = np.array(list(cases), dtype=np.uint16)
+    got = O.widen(bits)
+    for b, v, g in zip(cases, cases.values(), got):
+        assert g == v and math.copysign(1.0, g) == math.copysign(1.0, v), hex(b)
+    # float32 storage widens to the same value (no bit reinterpretation)
+    f = np.array([1.5, -2.25e-30, 3.0e38], dtype=np.float32)
+    np.testing.assert_array_equal(O.widen(f), torch.from_numpy(f).double().numpy())
+    # a bfloat16 pattern is the upper half of the float32 it stands for
+    f32 = np.array([1.0, -3.140625, 0.25], dtype=np.float32)
+    np.testing.assert_array_equal(O.widen((f32.view(np.uint32) >> 16).astype(np.uint16)), f32.astype(np.float64))
+
+
+# --------------------------------------------------------------------------
+# near-tie exemption key
+# --------------------------------------------------------------------------
+def test_exemption_key_per_mode_matches_library_routines():
+    """The score the 1e-6 exemption is measured on: the routing probability
+    softmax(s) for both softmax modes, the biased affinity sigmoid(s) + b for
+    sigmoid scoring (torch's float64 softmax / sigmoid as independent
+    routines)."""
+    rng = np.random.default_rng(31)
+    s = rng.standard_normal((40, 16)) * 2
+    b = rng.uniform(-0.1, 0.1, 16)
+    p = torch.softmax(torch.from_numpy(s), -1).numpy()
+    for scoring in (O.SOFTMAX_TOPK, O.TOPK_SOFTMAX):
+        np.testing.assert_allclose(O.exemption_key(s, scoring, None), p, rtol=1e-13, atol=0)
+    a = torch.sigmoid(torch.from_numpy(s)).numpy()
+    np.testing.assert_allclose(O.exemption_key(s, O.SIGMOID_BIAS, b), a + b[None, :], rtol=1e-14, atol=0)
+    np.testing.assert_allclose(O.exemption_key(s, O.SIGMOID_BIAS, None), a, rtol=1e-14, atol=0)
+
+
+def test_exemption_key_orders_like_the_selection_key():
+    """The exemption key ranks the experts exactly as the key top-k selects on
+    (p is monotone in s), so exempt tokens are those whose selection boundary
+    is close, in every mode."""
+    rng = np.random.default_rng(32)
+    s = rng.standard_normal((200, 24)) * 3
+    b = rng.uniform(-0.1, 0.1, 24)
+    for scoring in (O.SOFTMAX_TOPK, O.TOPK_SOFTMAX, O.SIGMOID_BIAS):
+        bias = b if scoring == O.SIGMOID_BIAS else None
+        np.testing.assert_array_equal(O.topk(O.exemption_key(s, scoring, bias), 6),
+                                      O.topk(O.selection_key(s, scoring, bias), 6))
+
+
+def test_topk_softmax_exemption_gap_is_the_logit_difference():
+    """For top-k-then-softmax the ranking is on the logits, whose relative gap
+    depends on where zero is; the exemption uses p instead, whose relative gap
+    (p_i - p_j) / p_i = 1 - exp(-(s_i - s_j)) depends only on the logit
+    difference (closed form), like the k-way softmax weights themselves."""
+    rng = np.random.default_rng(33)
+    s = rng.standard_normal((50, 8))
+    key = O.exemption_key(s, O.TOPK_SOFTMAX, None)
+    srt = -np.sort(-key, axis=1)
+    ss = -np.sort(-s, axis=1)
+    np.testing.assert_allclose((srt[:, 0] - srt[:, 1]) / srt[:, 0], -np.expm1(-(ss[:, 0] - ss[:, 1])), rtol=1e-9)
+    # shifting every logit of a token leaves the exemption decision unchanged
+    for c in (-50.0, 1e-3, 75.0):
+        np.testing.assert_allclose(O.exemption_key(s + c, O.TOPK_SOFTMAX, None), key, rtol=1e-12)
+
+
+@pytest.mark.parametrize("scoring", [O.SOFTMAX_TOPK, O.TOPK_SOFTMAX])
+def test_softmax_modes_exempt_hand_built_near_ties(scoring):
+    """k = 2; experts 1 and 2 straddle the boundary.  A logit gap of 4e-7 is a
+    relative gap of about 4e-7 in p (exempt), 3e-6 is not; a gap of 4e-7
+    between slots 1 and 2 only lets the slots swap.  Logits near zero show why
+    the gap is not measured on s: 1e-9 against -1e-9 is a relative gap of 2 in
+    s but a near tie in p."""
+    s = np.array([[1.0, 0.5, 0.5 - 4e-7, 0.0],
+                  [1.0, 0.5, 0.5 - 3e-6, 0.0],
+                  [0.7, 0.7 - 4e-7, 0.2, 0.0],
+                  [0.9, 1e-9, -1e-9, -0.5]])
+    bnd, swp = O.near_tie_mask(O.exemption_key(s, scoring, None), 2)
+    assert bnd.tolist() == [True, False, False, True]
+    assert swp[:, 0].tolist() == [False, False, True, False]
+
+
+def test_sigmoid_mode_exempts_near_ties_of_the_biased_affinity():
+    """The sigmoid exemption is measured on a + b, the key that selects: two
+    experts whose logits are far apart can tie once the bias is added, and the
+    same logits with no bias are not a near tie."""
+    a1, b1, b2 = 0.6, 0.0, -0.05
+    a2 = a1 + b1 - b2 + 2e-7                          # a2 + b2 = a1 + b1 + 2e-7
+    s = np.array([[3.0, math.log(a1 / (1 - a1)), math.log(a2 / (1 - a2)), -2.0]])
+    b = np.array([0.0, b1, b2, 0.0])
+    bnd, _ = O.near_tie_mask(O.exemption_key(s, O.SIGMOID_BIAS, b), 2)
+    assert bnd.tolist() == [True]
+    bnd0, _ = O.near_tie_mask(O.exemption_key(s, O.SIGMOID_BIAS, np.zeros(4)), 2)
+    assert bnd0.tolist() == [False]
+
+
+# --------------------------------------------------------------------------
 # dispatch and capacity
 # --------------------------------------------------------------------------
 def test_dispatch_worked_example():

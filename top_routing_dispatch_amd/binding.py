@@ -111,6 +111,70 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+_I32, _F32, _BYTES = "int32", "float32", "bytes"
+
+
+def _elem(cfg, kind):
+    """torch dtype an argument of `kind` must have: "act" / "router" follow the
+    configuration's activation and router types."""
+    if kind == "act":
+        return torch.bfloat16 if cfg.act_dtype == MOE_BF16 else torch.float32
+    if kind == "router":
+        return torch.bfloat16 if cfg.router_dtype == MOE_BF16 else torch.float32
+    return {_I32: torch.int32, _F32: torch.float32}[kind]
+
+
+def _on_device(t: torch.Tensor) -> bool:
+    return t.is_cuda
+
+
+def _arg(fn: str, name: str, t, kind, numel: int, cfg=None, required: bool = False):
+    """Host-side check of one tensor argument before its pointer crosses the C
+    ABI (which cannot see sizes or types): a device tensor, dense, of the
+    expected element type, holding at least `numel` elements (bytes for a
+    workspace).  Raises ValueError instead of letting a kernel read or write
+    past a buffer."""
+    if t is None:
+        if required:
+            raise ValueError(f"{fn}: {name} is required")
+        return
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{fn}: {name} must be a torch.Tensor")
+    if not _on_device(t):
+        raise ValueError(f"{fn}: {name} must be on the GPU (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{fn}: {name} must be contiguous")
+    if kind == _BYTES:
+        have = t.numel() * t.element_size()
+    else:
+        want = _elem(cfg, kind)
+        if t.dtype != want:
+            raise ValueError(f"{fn}: {name} must be {want} (got {t.dtype})")
+        have = t.numel()
+    if have < numel:
+        raise ValueError(f"{fn}: {name} holds {have} {'bytes' if kind == _BYTES else 'elements'}, needs {numel}")
+
+
+def _ws_bytes(ws) -> int:
+    return 0 if ws is None else ws.numel() * ws.element_size()
+
+
+def _rows_cap(cfg) -> int:
+    return moe_capacity(cfg)[1]
+
+
+def _check_weights(fn, cfg, weights: dict, need_experts: bool = True):
+    T, D, E, F = cfg.num_tokens, cfg.d_model, cfg.num_experts, cfg.d_ff
+    nF = (2 if cfg.activation == MOE_SWIGLU else 1) * F
+    SF = cfg.num_shared * cfg.d_ff_shared
+    _arg(fn, "w_router", weights.get("w_router"), "router", E * D, cfg, required=True)
+    _arg(fn, "sel_bias", weights.get("sel_bias"), _F32, E, cfg)
+    _arg(fn, "w13", weights.get("w13"), "act", E * nF * D, cfg, required=need_experts)
+    _arg(fn, "w2", weights.get("w2"), "act", E * D * F, cfg, required=need_experts)
+    _arg(fn, "ws13", weights.get("ws13"), "act", 2 * SF * D, cfg, required=SF > 0)
+    _arg(fn, "ws2", weights.get("ws2"), "act", D * SF, cfg, required=SF > 0)
+
+
 def _stream(stream=None):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -142,42 +206,104 @@ def workspace(cfg, op: int, device="cuda") -> torch.Tensor:
 
 
 def moe_route(cfg, x, w_router, sel_bias, topk_idx, topk_w, probs, ws, stream=None):
+    T, D, E, k = cfg.num_tokens, cfg.d_model, cfg.num_experts, cfg.top_k
+    fn = "moe_route"
+    _arg(fn, "x", x, "act", T * D, cfg, required=T > 0)
+    _arg(fn, "w_router", w_router, "router", E * D, cfg, required=True)
+    _arg(fn, "sel_bias", sel_bias, _F32, E, cfg)
+    _arg(fn, "topk_idx", topk_idx, _I32, T * k, cfg, required=T > 0)
+    _arg(fn, "topk_w", topk_w, _F32, T * k, cfg, required=T > 0)
+    _arg(fn, "probs", probs, _F32, T * E, cfg)
+    _arg(fn, "ws", ws, _BYTES, moe_workspace_size(cfg, MOE_OP_ROUTE), cfg, required=T > 0)
     c = make_config(cfg)
     _check("moe_route", lib().moe_route(ctypes.byref(c), _ptr(x), _ptr(w_router), _ptr(sel_bias), _ptr(topk_idx),
-                                        _ptr(topk_w), _ptr(probs), _ptr(ws), ws.numel() if ws is not None else 0,
+                                        _ptr(topk_w), _ptr(probs), _ptr(ws), _ws_bytes(ws),
                                         _stream(stream)))
 
 
 def moe_permute(cfg, topk_idx, x, counts, offsets, row_of, token_of_row, x_perm, ws, stream=None):
+    T, D, E, k = cfg.num_tokens, cfg.d_model, cfg.num_experts, cfg.top_k
+    A = _rows_cap(cfg)
+    fn = "moe_permute"
+    _arg(fn, "topk_idx", topk_idx, _I32, T * k, cfg, required=T > 0)
+    _arg(fn, "x", x, "act", T * D, cfg)
+    _arg(fn, "counts", counts, _I32, E, cfg, required=True)
+    _arg(fn, "offsets", offsets, _I32, E + 1, cfg, required=True)
+    _arg(fn, "row_of", row_of, _I32, T * k, cfg, required=T > 0)
+    _arg(fn, "token_of_row", token_of_row, _I32, A, cfg, required=A > 0)
+    _arg(fn, "x_perm", x_perm, "act", A * D, cfg)
+    _arg(fn, "ws", ws, _BYTES, moe_workspace_size(cfg, MOE_OP_PERMUTE), cfg, required=T > 0)
     c = make_config(cfg)
     _check("moe_permute", lib().moe_permute(ctypes.byref(c), _ptr(topk_idx), _ptr(x), _ptr(counts), _ptr(offsets),
                                             _ptr(row_of), _ptr(token_of_row), _ptr(x_perm), _ptr(ws),
-                                            ws.numel() if ws is not None else 0, _stream(stream)))
+                                            _ws_bytes(ws), _stream(stream)))
 
 
 def moe_expert_ffn(cfg, num_groups, d_ff, activation, max_rows, x_in, gather_rows, offsets, w13, w2, y_out, ws,
                    stream=None):
+    D = cfg.d_model
+    nF = (2 if activation == MOE_SWIGLU else 1) * d_ff
+    fn = "moe_expert_ffn"
+    need = max_rows > 0
+    # with a gather map the rows of x_in it names are the caller's to bound
+    _arg(fn, "x_in", x_in, "act", D if gather_rows is not None else max_rows * D, cfg, required=need)
+    if x_in is not None and x_in.numel() % D:
+        raise ValueError(f"{fn}: x_in must hold whole rows of {D}")
+    _arg(fn, "gather_rows", gather_rows, _I32, max_rows, cfg)
+    _arg(fn, "offsets", offsets, _I32, num_groups + 1, cfg)
+    _arg(fn, "w13", w13, "act", num_groups * nF * D, cfg, required=need)
+    _arg(fn, "w2", w2, "act", num_groups * D * d_ff, cfg, required=need)
+    _arg(fn, "y_out", y_out, "act", max_rows * D, cfg, required=need)
     c = make_config(cfg)
     _check("moe_expert_ffn", lib().moe_expert_ffn(ctypes.byref(c), num_groups, d_ff, activation, max_rows, _ptr(x_in),
                                                   _ptr(gather_rows), _ptr(offsets), _ptr(w13), _ptr(w2), _ptr(y_out),
-                                                  _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
+                                                  _ptr(ws), _ws_bytes(ws), _stream(stream)))
 
 
 def moe_combine(cfg, y_perm, row_of, topk_w, y_shared, y, stream=None):
+    T, D, k = cfg.num_tokens, cfg.d_model, cfg.top_k
+    fn = "moe_combine"
+    _arg(fn, "y_perm", y_perm, "act", _rows_cap(cfg) * D, cfg)
+    _arg(fn, "row_of", row_of, _I32, T * k, cfg, required=T > 0)
+    _arg(fn, "topk_w", topk_w, _F32, T * k, cfg, required=T > 0)
+    _arg(fn, "y_shared", y_shared, "act", T * D, cfg)
+    _arg(fn, "y", y, "act", T * D, cfg, required=T > 0)
     c = make_config(cfg)
     _check("moe_combine", lib().moe_combine(ctypes.byref(c), _ptr(y_perm), _ptr(row_of), _ptr(topk_w),
                                             _ptr(y_shared), _ptr(y), _stream(stream)))
 
 
 def moe_load_stats(cfg, counts, probs, alpha, f, P, aux_loss, imbalance, dropped, ws, stream=None):
+    T, E = cfg.num_tokens, cfg.num_experts
+    fn = "moe_load_stats"
+    _arg(fn, "counts", counts, _I32, E, cfg, required=True)
+    _arg(fn, "probs", probs, _F32, T * E, cfg, required=T > 0)
+    for name, t, n in (("f", f, E), ("P", P, E), ("aux_loss", aux_loss, 1), ("imbalance", imbalance, 1)):
+        _arg(fn, name, t, _F32, n, cfg)
+    _arg(fn, "dropped", dropped, _I32, 1, cfg)
+    _arg(fn, "ws", ws, _BYTES, moe_workspace_size(cfg, MOE_OP_LOAD_STATS), cfg, required=T > 0)
     c = make_config(cfg)
     _check("moe_load_stats", lib().moe_load_stats(ctypes.byref(c), _ptr(counts), _ptr(probs), float(alpha), _ptr(f),
                                                   _ptr(P), _ptr(aux_loss), _ptr(imbalance), _ptr(dropped), _ptr(ws),
-                                                  ws.numel() if ws is not None else 0, _stream(stream)))
+                                                  _ws_bytes(ws), _stream(stream)))
+
+
+def _check_layer_args(fn, cfg, weights, x, y, topk_idx, topk_w, counts, stats, dropped, ws):
+    T, D, E, k = cfg.num_tokens, cfg.d_model, cfg.num_experts, cfg.top_k
+    _check_weights(fn, cfg, weights)
+    _arg(fn, "x", x, "act", T * D, cfg, required=T > 0)
+    _arg(fn, "y", y, "act", T * D, cfg, required=T > 0)
+    _arg(fn, "topk_idx", topk_idx, _I32, T * k, cfg)
+    _arg(fn, "topk_w", topk_w, _F32, T * k, cfg)
+    _arg(fn, "counts", counts, _I32, E, cfg)
+    _arg(fn, "stats", stats, _F32, 2 * E + 2, cfg)
+    _arg(fn, "dropped", dropped, _I32, 1, cfg)
+    _arg(fn, "ws", ws, _BYTES, moe_workspace_size(cfg, MOE_OP_LAYER), cfg, required=T > 0)
 
 
 def moe_layer_forward(cfg, weights: dict, x, y, topk_idx=None, topk_w=None, counts=None, alpha=0.01, stats=None,
                       dropped=None, ws=None, stream=None):
+    _check_layer_args("moe_layer_forward", cfg, weights, x, y, topk_idx, topk_w, counts, stats, dropped, ws)
     c = make_config(cfg)
     w = moe_weights()
     for name, _ in moe_weights._fields_:
@@ -185,13 +311,14 @@ def moe_layer_forward(cfg, weights: dict, x, y, topk_idx=None, topk_w=None, coun
         setattr(w, name, None if t is None else t.data_ptr())
     _check("moe_layer_forward", lib().moe_layer_forward(
         ctypes.byref(c), ctypes.byref(w), _ptr(x), _ptr(y), _ptr(topk_idx), _ptr(topk_w), _ptr(counts),
-        float(alpha), _ptr(stats), _ptr(dropped), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
+        float(alpha), _ptr(stats), _ptr(dropped), _ptr(ws), _ws_bytes(ws), _stream(stream)))
 
 
 def moe_layer_forward_timed(cfg, weights: dict, x, y, topk_idx=None, topk_w=None, counts=None, alpha=0.01,
                             stats=None, dropped=None, ws=None, stage_events=None, stream=None):
     """stage_events: list of 2 * len(STAGES) torch.cuda.Event (enable_timing=True)
     already recorded once (so that their HIP handles exist), or None entries."""
+    _check_layer_args("moe_layer_forward_timed", cfg, weights, x, y, topk_idx, topk_w, counts, stats, dropped, ws)
     c = make_config(cfg)
     w = moe_weights()
     for name, _ in moe_weights._fields_:
@@ -204,13 +331,25 @@ def moe_layer_forward_timed(cfg, weights: dict, x, y, topk_idx=None, topk_w=None
             arr[i] = None if ev is None else ev.cuda_event
     _check("moe_layer_forward_timed", lib().moe_layer_forward_timed(
         ctypes.byref(c), ctypes.byref(w), _ptr(x), _ptr(y), _ptr(topk_idx), _ptr(topk_w), _ptr(counts),
-        float(alpha), _ptr(stats), _ptr(dropped), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream),
-        arr))
+        float(alpha), _ptr(stats), _ptr(dropped), _ptr(ws), _ws_bytes(ws), _stream(stream), arr))
 
 
 def moe_layer_backward(cfg, weights: dict, x, dy, alpha, dx, dw_router, dw13, dw2, dws13=None, dws2=None, ws=None,
                        stream=None):
     """Gradients of <dy, y> + alpha-weighted balance loss, the routing fixed."""
+    T, D, E, F = cfg.num_tokens, cfg.d_model, cfg.num_experts, cfg.d_ff
+    nF = (2 if cfg.activation == MOE_SWIGLU else 1) * F
+    SF = cfg.num_shared * cfg.d_ff_shared
+    fn = "moe_layer_backward"
+    _check_weights(fn, cfg, weights)
+    for name, t in (("x", x), ("dy", dy), ("dx", dx)):
+        _arg(fn, name, t, "act", T * D, cfg, required=T > 0)
+    _arg(fn, "dw_router", dw_router, _F32, E * D, cfg, required=True)
+    _arg(fn, "dw13", dw13, _F32, E * nF * D, cfg, required=True)
+    _arg(fn, "dw2", dw2, _F32, E * D * F, cfg, required=True)
+    _arg(fn, "dws13", dws13, _F32, 2 * SF * D, cfg, required=SF > 0)
+    _arg(fn, "dws2", dws2, _F32, D * SF, cfg, required=SF > 0)
+    _arg(fn, "ws", ws, _BYTES, moe_workspace_size(cfg, MOE_OP_LAYER_BACKWARD), cfg, required=T > 0)
     c = make_config(cfg)
     w = moe_weights()
     for name, _ in moe_weights._fields_:
@@ -218,7 +357,7 @@ def moe_layer_backward(cfg, weights: dict, x, dy, alpha, dx, dw_router, dw13, dw
         setattr(w, name, None if t is None else t.data_ptr())
     _check("moe_layer_backward", lib().moe_layer_backward(
         ctypes.byref(c), ctypes.byref(w), _ptr(x), _ptr(dy), float(alpha), _ptr(dx), _ptr(dw_router), _ptr(dw13),
-        _ptr(dw2), _ptr(dws13), _ptr(dws2), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
+        _ptr(dw2), _ptr(dws13), _ptr(dws2), _ptr(ws), _ws_bytes(ws), _stream(stream)))
 
 
 def moe_expert_choice_capacity(cfg) -> int:
@@ -231,6 +370,16 @@ def moe_expert_choice_capacity(cfg) -> int:
 def moe_expert_choice_forward(cfg, weights: dict, x, y, token_of_row=None, row_w=None, unselected=None, ws=None,
                               stage_events=None, stream=None):
     """Expert-choice layer forward; stage_events as for moe_layer_forward_timed."""
+    T, D = cfg.num_tokens, cfg.d_model
+    fn = "moe_expert_choice_forward"
+    rows = cfg.num_experts * moe_expert_choice_capacity(cfg)
+    _check_weights(fn, cfg, weights)
+    _arg(fn, "x", x, "act", T * D, cfg, required=T > 0)
+    _arg(fn, "y", y, "act", T * D, cfg, required=T > 0)
+    _arg(fn, "token_of_row", token_of_row, _I32, rows, cfg)
+    _arg(fn, "row_w", row_w, _F32, rows, cfg)
+    _arg(fn, "unselected", unselected, _I32, 1, cfg)
+    _arg(fn, "ws", ws, _BYTES, moe_workspace_size(cfg, MOE_OP_EXPERT_CHOICE), cfg, required=T > 0)
     c = make_config(cfg)
     w = moe_weights()
     for name, _ in moe_weights._fields_:
@@ -243,16 +392,28 @@ def moe_expert_choice_forward(cfg, weights: dict, x, y, token_of_row=None, row_w
             arr[i] = None if ev is None else ev.cuda_event
     _check("moe_expert_choice_forward", lib().moe_expert_choice_forward(
         ctypes.byref(c), ctypes.byref(w), _ptr(x), _ptr(y), _ptr(token_of_row), _ptr(row_w), _ptr(unselected),
-        _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream), arr))
+        _ptr(ws), _ws_bytes(ws), _stream(stream), arr))
+
+
+class _Int32Only:
+    act_dtype = router_dtype = MOE_F32
 
 
 def moe_ep_send_layout(num_experts, num_ranks, offsets, send_counts, send_offsets, stream=None):
+    fn = "moe_ep_send_layout"
+    _arg(fn, "offsets", offsets, _I32, num_experts + 1, _Int32Only, required=True)
+    _arg(fn, "send_counts", send_counts, _I32, max(num_ranks, 0), _Int32Only, required=True)
+    _arg(fn, "send_offsets", send_offsets, _I32, max(num_ranks, 0) + 1, _Int32Only, required=True)
     _check("moe_ep_send_layout", lib().moe_ep_send_layout(num_experts, num_ranks, _ptr(offsets), _ptr(send_counts),
                                                           _ptr(send_offsets), _stream(stream)))
 
 
 def moe_ep_recv_layout(recv_counts, rows_cap, local_offsets, gather, stream=None):
     """recv_counts: [R, E_local] int32 device tensor."""
+    fn = "moe_ep_recv_layout"
+    _arg(fn, "recv_counts", recv_counts, _I32, 1, _Int32Only, required=True)
     R, El = recv_counts.shape
+    _arg(fn, "local_offsets", local_offsets, _I32, El + 1, _Int32Only, required=True)
+    _arg(fn, "gather", gather, _I32, rows_cap, _Int32Only, required=rows_cap > 0)
     _check("moe_ep_recv_layout", lib().moe_ep_recv_layout(R, El, _ptr(recv_counts), rows_cap, _ptr(local_offsets),
                                                           _ptr(gather), _stream(stream)))

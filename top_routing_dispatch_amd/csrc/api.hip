@@ -64,6 +64,34 @@ moe_status derive(const moe_config* c, Derived* d) {
   return MOE_OK;
 }
 
+// The kernels address their matrix operands with 32-bit byte offsets from one
+// buffer descriptor per operand.  Every operand such a descriptor covers must
+// span at most kMaxOperandBytes (4 GiB minus the 2 MiB the weight-streaming
+// kernel keeps above its range for rows that return zeros); larger shapes are
+// rejected before anything is launched instead of wrapping.
+constexpr long long kMaxOperandBytes = 0xffe00000LL;
+inline bool span_ok(long long rows, long long cols, long long elem) {
+  return rows * cols * elem <= kMaxOperandBytes;
+}
+
+moe_status validate_spans(const moe_config* c) {
+  const long long es = c->act_dtype == BF16 ? 2 : 4;
+  const long long T = c->num_tokens, D = c->d_model, E = c->num_experts, k = c->top_k, F = c->d_ff;
+  const long long nF = (c->activation == SWIGLU ? 2 : 1) * F;
+  const long long SF = (long long)c->num_shared * c->d_ff_shared;
+  long long A = T * k;                                   // rows of the permuted operands (upper bound)
+  if (c->capacity_factor > 0.0f) {
+    const double cap = ceil((double)c->capacity_factor * (double)A / (double)E);
+    if (cap * (double)E < (double)A) A = (long long)cap * E;
+  }
+  const bool ok = span_ok(T, D, es) &&                  // x (router, gate/up, shared)
+                  span_ok(A, D, es) && span_ok(A, F, es) &&   // x_perm / y_perm, H
+                  span_ok(nF, D, es) && span_ok(D, F, es) &&  // one expert's weights
+                  span_ok(E, 3 * D, 4) &&                      // router weight (float32, or its bf16 planes)
+                  span_ok(T, SF, es) && span_ok(2 * SF, D, es) && span_ok(D, SF, es);   // shared experts
+  return ok ? MOE_OK : MOE_ERR_UNSUPPORTED;
+}
+
 moe_status validate_config(const moe_config* c) {
   if (c == nullptr) return MOE_ERR_INVALID_ARGUMENT;
   if (c->num_tokens < 0 || c->d_model <= 0 || c->num_experts <= 0 || c->top_k <= 0 || c->d_ff <= 0)
@@ -83,7 +111,7 @@ moe_status validate_config(const moe_config* c) {
   const long long T = c->num_tokens;
   if (T * c->num_experts > INT32_MAX / 2 || T * c->top_k > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
   if ((long long)c->num_shared * c->d_ff_shared > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
-  return MOE_OK;
+  return validate_spans(c);
 }
 
 // Workspace pieces ---------------------------------------------------------
@@ -542,6 +570,19 @@ moe_status aux_stream(AuxStream** out) {
 }
 
 // Backward -----------------------------------------------------------------
+// The backward's extra operands: the gate/up products and their gradients
+// [A, n_mat F] of the routed and [T, 2 S F_s] of the shared experts, and the
+// transposed expert weights [D, n_mat F].
+moe_status validate_backward_spans(const moe_config* c) {
+  Derived d;
+  derive(c, &d);
+  const long long nF = (c->activation == SWIGLU ? 2LL : 1LL) * c->d_ff;
+  const long long SF = (long long)c->num_shared * c->d_ff_shared;
+  if (!span_ok(d.rows_cap, nF, 2) || !span_ok(c->num_tokens, 2 * SF, 2) || !span_ok(c->d_model, nF, 2))
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
 struct BwLayout {
   size_t fwd, y, dyp, gu, dh, dgu, dxp, w13t, w2t, ones, dw, dlogits, dxr, rpart, pre, gus, dhs, dgus, dxs, ws13t,
       ws2t, rplanes, rplanes_t, raux, total;
@@ -648,6 +689,9 @@ moe_status validate_ec(const moe_config* c) {
   MOE_TRY(validate_config(c));
   if (c->num_experts > kEcMaxExperts || c->num_tokens > kEcMaxTokens) return MOE_ERR_UNSUPPORTED;
   if ((long long)c->num_experts * ec_capacity(c) > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
+  const long long rows = (long long)c->num_experts * ec_capacity(c);
+  if (!span_ok(rows, c->d_model, esize(c->act_dtype)) || !span_ok(rows, c->d_ff, esize(c->act_dtype)))
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -697,7 +741,10 @@ moe_status moe_workspace_size(const moe_config* cfg, int32_t op, size_t* bytes) 
       MOE_TRY(validate_ec(cfg));
       *bytes = ec_layout(cfg).total;
       break;
-    case MOE_OP_LAYER_BACKWARD: *bytes = bw_layout(cfg, d).total; break;
+    case MOE_OP_LAYER_BACKWARD:
+      MOE_TRY(validate_backward_spans(cfg));
+      *bytes = bw_layout(cfg, d).total;
+      break;
     default: return MOE_ERR_INVALID_ARGUMENT;
   }
   return MOE_OK;
@@ -762,6 +809,14 @@ moe_status moe_expert_ffn(const moe_config* cfg, int32_t num_groups, int32_t d_f
   if (num_groups > kMaxExperts) return MOE_ERR_UNSUPPORTED;
   const int vec = cfg->act_dtype == BF16 ? 8 : 4;
   if (d_ff % vec) return MOE_ERR_UNSUPPORTED;
+  {
+    const long long es = esize(cfg->act_dtype), nF = (activation == SWIGLU ? 2LL : 1LL) * d_ff;
+    // x_in rows (without a gather map; with one, the caller keeps the rows it
+    // names within the same bound), H, y_out and one group's weights
+    if (!span_ok(max_rows, cfg->d_model, es) || !span_ok(max_rows, d_ff, es) || !span_ok(nF, cfg->d_model, es) ||
+        !span_ok(cfg->d_model, d_ff, es))
+      return MOE_ERR_UNSUPPORTED;
+  }
   if (max_rows > 0 && (x_in == nullptr || w13 == nullptr || w2 == nullptr || y_out == nullptr || ws == nullptr))
     return MOE_ERR_INVALID_ARGUMENT;
   if (!opt_aligned(x_in) || !opt_aligned(gather_rows) || !opt_aligned(offsets) || !opt_aligned(w13) ||
@@ -986,6 +1041,7 @@ moe_status moe_layer_backward(const moe_config* cfg, const moe_weights* wt, cons
       !aligned16(wt->w_router) || !aligned16(wt->w13) || !aligned16(wt->w2) || !opt_aligned(wt->ws13) ||
       !opt_aligned(wt->ws2))
     return MOE_ERR_INVALID_ARGUMENT;
+  MOE_TRY(validate_backward_spans(cfg));
   Derived d;
   derive(cfg, &d);
   const BwLayout B = bw_layout(cfg, d);

@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const bf16_t* __rest
   const int nk = D / 64;
 
   const __amdgpu_buffer_rsrc_t x_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(x), 0, 0x7fffffff, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(x), 0, (int)0xffffffffu, 0x00020000);
   const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<bf16_t*>(w), 0, (int)((unsigned)E * NP * (unsigned)D * 2u), 0x00020000);
   // byte offsets of this wave's loads at slice 0 (rows past the end clamped);
