@@ -32,7 +32,7 @@ import workloads as W  # noqa: E402
 # MI355X published peaks
 HBM_GBPS = 8000.0
 MFMA_BF16_TFLOPS = 2500.0
-VALU_F32_TFLOPS = 78.6       # FMA without packed-FP32 instructions: 256 CU x 64 lanes x 2 x 2.4 GHz
+VALU_F32_TFLOPS = 157.3      # published float32 vector peak (packed FP32; the kernels use half of it, unpacked)
 
 # Files whose change invalidates HBM-traffic counters taken earlier: the GEMM
 # kernels, their launch planning and the synthetic workload recipe.
@@ -50,27 +50,39 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def router_planes(cfg):
+    """bf16 planes the router GEMM runs over: a float32 router weight with bf16
+    tokens is split exactly into three bf16 planes (hi + mid + lo), each
+    multiplied on the matrix cores."""
+    return 3 if (cfg.router_dtype == W.F32 and cfg.act_dtype == W.BF16) else 1
+
+
 def stage_work(cfg, stage, A, E_act, T):
-    """Algorithmic (flops, bytes) of one launch of a stage; A = kept rows."""
+    """Algorithmic (flops, bytes) of one launch of a stage; A = kept rows.
+    The grouped GEMMs count the expert weights once, the rows they read and
+    the rows they write back to token order (x in, y_perm out); the
+    activation H between the two projections is an intermediate of the
+    implementation, not of the method, and is left out (stage_h_bytes gives
+    it)."""
     b = 2 if cfg.act_dtype == W.BF16 else 4
     br = 2 if cfg.router_dtype == W.BF16 else 4
     D, F, E, k = cfg.d_model, cfg.d_ff, cfg.num_experts, cfg.top_k
     nm = cfg.n_mat
     SF = cfg.num_shared * cfg.d_ff_shared
     if stage == "router_logits":
-        return 2.0 * T * D * E, T * D * b + E * D * br + T * E * 4
+        return 2.0 * T * D * E * router_planes(cfg), T * D * b + E * D * br + T * E * 4
     if stage == "route_select":
         return 0.0, T * E * 4 * 2 + T * k * 8
     if stage == "permute":
         return 0.0, T * k * 4 * 3 + A * 4 + (E + 1) * 8
     if stage == "expert_gate_up":
-        return 2.0 * A * D * F * nm, E_act * nm * F * D * b + A * D * b + A * F * b
+        return 2.0 * A * D * F * nm, E_act * nm * F * D * b + A * D * b
     if stage == "expert_down":
-        return 2.0 * A * F * D, E_act * D * F * b + A * F * b + A * D * b
+        return 2.0 * A * F * D, E_act * D * F * b + A * D * b
     if stage == "shared_gate_up":
-        return 2.0 * T * D * 2 * SF, 2 * SF * D * b + T * D * b + T * SF * b
+        return 2.0 * T * D * 2 * SF, 2 * SF * D * b + T * D * b
     if stage == "shared_down":
-        return 2.0 * T * SF * D, D * SF * b + T * SF * b + T * D * b
+        return 2.0 * T * SF * D, D * SF * b + T * D * b
     if stage == "combine":
         return 0.0, A * D * b + T * k * 8 + (T * D * b if SF else 0) + T * D * b
     if stage == "load_stats":
@@ -78,11 +90,25 @@ def stage_work(cfg, stage, A, E_act, T):
     raise KeyError(stage)
 
 
+def stage_h_bytes(cfg, stage, A, T):
+    """Bytes of the activation H that a projection writes (gate/up) or reads
+    (down) on top of stage_work's."""
+    b = 2 if cfg.act_dtype == W.BF16 else 4
+    SF = cfg.num_shared * cfg.d_ff_shared
+    if stage in ("expert_gate_up", "expert_down"):
+        return A * cfg.d_ff * b
+    if stage in ("shared_gate_up", "shared_down"):
+        return T * SF * b
+    return 0
+
+
 def roofline_of(cfg, stage, flops, nbytes, ms):
+    """The stage against its roof: the larger of its time at the compute peak
+    (bf16 matrix cores; float32 vector units for the all-float32 layer) and
+    its time at the HBM peak decides the bound."""
     t = ms * 1e-3
     gemm = flops > 0
-    f32 = (cfg.act_dtype == W.F32) or (stage == "router_logits" and cfg.router_dtype == W.F32)
-    if gemm and f32:
+    if gemm and cfg.act_dtype == W.F32:
         peak_f, unit_bound = VALU_F32_TFLOPS, "alu"
     else:
         peak_f, unit_bound = MFMA_BF16_TFLOPS, "mfma"
@@ -93,6 +119,23 @@ def roofline_of(cfg, stage, flops, nbytes, ms):
     achieved = nbytes / t / 1e9
     return dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_GBPS, unit="GB/s",
                 frac=round(achieved / HBM_GBPS, 4))
+
+
+def targets_of(cfg, stage_ms, A, E_act, T):
+    """The layer's stated targets at the measured stage times: router,
+    selection, permutation and combine against the HBM peak, the routed
+    expert GEMMs (gate/up + down) against the bf16 matrix-core peak."""
+    out = {}
+    for st in ("router_logits", "route_select", "permute", "combine"):
+        if st in stage_ms:
+            _, by = stage_work(cfg, st, A, E_act, T)
+            out[st + "_hbm_frac"] = round(by / (stage_ms[st] * 1e-3) / 1e9 / HBM_GBPS, 4)
+    if "expert_gate_up" in stage_ms and "expert_down" in stage_ms:
+        fl = sum(stage_work(cfg, st, A, E_act, T)[0] for st in ("expert_gate_up", "expert_down"))
+        ms = stage_ms["expert_gate_up"] + stage_ms["expert_down"]
+        out["expert_gemm_ms"] = round(ms, 4)
+        out["expert_gemm_mfma_frac"] = round(fl / (ms * 1e-3) / 1e12 / MFMA_BF16_TFLOPS, 4)
+    return out
 
 
 def sources_digest():
@@ -180,16 +223,36 @@ def gpu_clocks():
         return None
 
 
+def host_info():
+    """Threads the oracle's BLAS uses, the BLAS library and the host CPU model
+    (for the CPU baseline's record)."""
+    cores, blas = 1, None
+    try:
+        import threadpoolctl
+        info = [i for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            cores = max(i.get("num_threads", 1) for i in info)
+            blas = ", ".join(f"{i.get('internal_api')} {i.get('version')} ({i.get('threading_layer')} threads)"
+                             for i in info)
+    except Exception:
+        pass
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.lower().startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return dict(cores=int(cores), cpu_model=model, blas=blas, host_cpus=os.cpu_count())
+
+
 def cpu_baseline(cfg, inp, sample_tokens, expert_choice=False):
     """The oracle as it stands, on the first `sample_tokens` tokens (expert
     choice: those tokens as a batch of their own, C recomputed for it)."""
     from oracle import moe_oracle as O
-    try:
-        import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
-    except Exception:
-        cores = 1
+    hi = host_info()
     Ts = min(sample_tokens, cfg.num_tokens)
     scfg = cfg.replace(num_tokens=Ts)
     x = inp.x[:Ts]
@@ -204,10 +267,11 @@ def cpu_baseline(cfg, inp, sample_tokens, expert_choice=False):
         dt = time.perf_counter() - t0
         if dt >= CPU_MIN_SECONDS:
             break
-    return dict(value=round(Ts * passes / dt, 2), unit="tokens/s", cores=int(cores), kind="oracle",
+    return dict(value=round(Ts * passes / dt, 2), unit="tokens/s", cores=hi["cores"], kind="oracle",
                 sample=f"first {Ts} of {cfg.num_tokens} tokens, all {cfg.num_experts} experts"
                        + (", capacity recomputed for the sample" if cfg.capacity_factor > 0 or expert_choice else "")
-                       + f"; {passes} pass(es) in {dt:.1f} s")
+                       + f"; {passes} pass(es) in {dt:.1f} s",
+                cpu_model=hi["cpu_model"], blas=hi["blas"], host_cpus=hi["host_cpus"])
 
 
 def main():
@@ -215,7 +279,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="switch",
+    ap.add_argument("--config", default="deepseekv3",
                     choices=sorted(W.CONFIGS) + sorted(W.DECODE_CONFIGS) + sorted(W.EP_CONFIGS) + sorted(W.EC_CONFIGS),
                     help="workload; <model>_decode_t<T>: the first T tokens on that model's full-size weights; "
                          "<model>_ep8_local: one GPU's share of an 8-rank expert-parallel layer; "
@@ -382,6 +446,15 @@ def main():
     roof = roofline_of(cfg, dominant, fl, by, dom_ms)
     roof["kernel"] = dominant
     roof["ms"] = round(dom_ms, 4)
+    hb = stage_h_bytes(cfg, dominant, A, T)
+    if hb:
+        # the same stage with the activation H between the projections counted as traffic
+        roof["with_h"] = dict(bytes=int(by + hb), gbps=round((by + hb) / (dom_ms * 1e-3) / 1e9, 1),
+                              hbm_frac=round((by + hb) / (dom_ms * 1e-3) / 1e9 / HBM_GBPS, 4))
+    if fl > 0:
+        roof["mfma_frac" if cfg.act_dtype == W.BF16 else "alu_frac"] = round(
+            fl / (dom_ms * 1e-3) / 1e12 / (MFMA_BF16_TFLOPS if cfg.act_dtype == W.BF16 else VALU_F32_TFLOPS), 4)
+        roof["hbm_frac"] = round(by / (dom_ms * 1e-3) / 1e9 / HBM_GBPS, 4)
     roof["traffic"] = measured_traffic(cfg.name, dominant)
     if roof["bound"] == "hbm":
         ref = copy_rate()
@@ -412,6 +485,7 @@ def main():
         "cpu_baseline": cpu,
         "step_ms": {q: round(float(np.percentile(per_step, p)), 4)
                     for q, p in (("median", 50), ("p10", 10), ("p90", 90))},
+        "targets": targets_of(cfg, stage_ms, A, E_act, T),
         "stages": stage_info,
         "stages_cold_ms": {name: round(ms, 4) for name, ms in stage_cold_ms.items()},
     }
@@ -484,14 +558,10 @@ def run_ep_share(args, ep):
             if time.perf_counter() - t1 >= CPU_MIN_SECONDS:
                 break
         dt = time.perf_counter() - t1
-        try:
-            import threadpoolctl
-            info = threadpoolctl.threadpool_info()
-            cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
-        except Exception:
-            cores = 1
-        cpu = dict(value=round(n * passes / dt, 2), unit="rows/s", cores=int(cores), kind="oracle",
-                   sample=f"{n} received rows of local expert 0; {passes} pass(es) in {dt:.1f} s")
+        hi = host_info()
+        cpu = dict(value=round(n * passes / dt, 2), unit="rows/s", cores=hi["cores"], kind="oracle",
+                   sample=f"{n} received rows of local expert 0; {passes} pass(es) in {dt:.1f} s",
+                   cpu_model=hi["cpu_model"], blas=hi["blas"], host_cpus=hi["host_cpus"])
     line = {
         "metric": "MoE-layer tokens/sec at 1 GPU; % HBM roofline (route/permute) and % MFMA peak",
         "value": round(total / (ms_per_step * 1e-3), 1), "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
@@ -570,15 +640,11 @@ def run_backward(args, cfg):
             if time.perf_counter() - t1 >= CPU_MIN_SECONDS:
                 break
         dt = time.perf_counter() - t1
-        try:
-            import threadpoolctl
-            info = threadpoolctl.threadpool_info()
-            cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
-        except Exception:
-            cores = 1
-        cpu = dict(value=round(Ts * passes / dt, 2), unit="tokens/s", cores=int(cores), kind="oracle",
+        hi = host_info()
+        cpu = dict(value=round(Ts * passes / dt, 2), unit="tokens/s", cores=hi["cores"], kind="oracle",
                    sample=f"backward of the first {Ts} of {T} tokens (forward recomputed, experts regenerated); "
-                          f"{passes} pass(es) in {dt:.1f} s")
+                          f"{passes} pass(es) in {dt:.1f} s",
+                   cpu_model=hi["cpu_model"], blas=hi["blas"], host_cpus=hi["host_cpus"])
     line = {
         "metric": "MoE-layer tokens/sec at 1 GPU; % HBM roofline (route/permute) and % MFMA peak",
         "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
