@@ -248,6 +248,13 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* weights,
                              int32_t* counts, float alpha, float* stats, int32_t* dropped,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* Re-reads the MOE_* tuning variables of the environment (tuning aids that
+ * force a kernel choice: MOE_GEMM_CFG, MOE_GEMM_SPLIT, MOE_ROUTER_PATH, ...).
+ * The library reads them once, at its first launch, and otherwise only here:
+ * no launch path calls getenv.  For tuning tools and tests; not thread-safe
+ * with respect to launches running on other host threads. */
+moe_status moe_reload_tuning(void);
+
 /* Kernel stages of moe_layer_forward, in launch order. */
 typedef enum {
   MOE_STAGE_ROUTER_LOGITS = 0,   /* x W_g^T on the matrix cores / float32 ALUs */

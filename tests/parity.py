@@ -31,6 +31,13 @@ W_TOL = 1e-5
 REL_TIE = 1e-6     # near-tie band of the selection, relative to the k-th best key
 
 
+def set_env(monkeypatch, name: str, value: str):
+    """Set a MOE_* tuning variable for one test and make the library read it
+    (it reads them once otherwise); conftest re-reads them after the test."""
+    monkeypatch.setenv(name, value)
+    M.moe_reload_tuning()
+
+
 def out_tol(cfg) -> float:
     return BF16_TOL if cfg.act_dtype == W.BF16 else F32_TOL
 

@@ -13,7 +13,7 @@ from oracle import moe_oracle as O
 from workloads.torch_io import act_torch_dtype, to_numpy, to_torch
 
 from parity import (BF16_TOL, W_TOL, DeviceLayer, check_layer, ec_check_selection, ec_oracle_output, oracle_forward,
-                    out_tol, refinement_margin, rel_err, rerun_on_choice, route_differences, row_rel_err)
+                    out_tol, refinement_margin, rel_err, rerun_on_choice, route_differences, row_rel_err, set_env)
 
 pytestmark = pytest.mark.gpu
 
@@ -334,7 +334,7 @@ GEMM_TILE_CONFIGS = range(-1, 30)
 def test_every_gemm_tile_config(cfg, gemm_cfg, monkeypatch):
     """Each tile configuration of the pipelined expert GEMM (K a multiple of 64)
     against the oracle, through the whole layer; -1 is the general kernel."""
-    monkeypatch.setenv("MOE_GEMM_CFG", gemm_cfg)
+    set_env(monkeypatch, "MOE_GEMM_CFG", gemm_cfg)
     print(f"[tile config {gemm_cfg}] {cfg.name}", flush=True)
     inp = W.make_inputs(cfg)
     ref = oracle_forward(cfg, inp)
@@ -357,9 +357,9 @@ def test_shallow_group_split(cfg, split, monkeypatch):
     """Expert FFN with shallow groups split off to the persistent
     weight-streaming kernel (1), to the persistent configuration 19 of the
     deep-tile kernel (1-pers19), and without the split (0), against the oracle."""
-    monkeypatch.setenv("MOE_GEMM_SPLIT", split[0])
+    set_env(monkeypatch, "MOE_GEMM_SPLIT", split[0])
     if split == "1-pers19":
-        monkeypatch.setenv("MOE_GEMM_SHCFG", "19")
+        set_env(monkeypatch, "MOE_GEMM_SHCFG", "19")
     print(f"[split {split}] {cfg.name}", flush=True)
     inp = W.make_inputs(cfg)
     ref = oracle_forward(cfg, inp)
@@ -385,8 +385,8 @@ TAIL_SHAPES = [
 def test_down_tail_split(cfg, tail, monkeypatch):
     """The down projection on 256x256 tiles with its last, partial round run as
     quarter tiles (1) and without (0), against the oracle."""
-    monkeypatch.setenv("MOE_GEMM_CFG", "10")
-    monkeypatch.setenv("MOE_GEMM_TAIL", tail)
+    set_env(monkeypatch, "MOE_GEMM_CFG", "10")
+    set_env(monkeypatch, "MOE_GEMM_TAIL", tail)
     print(f"[tail {tail}] {cfg.name}", flush=True)
     inp = W.make_inputs(cfg)
     ref = oracle_forward(cfg, inp)
@@ -413,7 +413,7 @@ def test_weight_streaming_many_tiles(cfg, gemm_cfg, monkeypatch):
     default choice for these shallow groups) against the oracle with several
     tiles per workgroup."""
     if gemm_cfg != "default":
-        monkeypatch.setenv("MOE_GEMM_CFG", gemm_cfg)
+        set_env(monkeypatch, "MOE_GEMM_CFG", gemm_cfg)
     print(f"[ws {gemm_cfg}] {cfg.name}", flush=True)
     inp = W.make_inputs(cfg)
     ref = oracle_forward(cfg, inp)
@@ -440,8 +440,8 @@ def test_contraction_split(cfg, gemm_cfg, ks, monkeypatch):
     split in 2, 4 or 8 parts (float32 partial sums added by a second kernel;
     a launch whose contraction the forced split does not divide runs unsplit)
     against the oracle, shared expert included."""
-    monkeypatch.setenv("MOE_GEMM_CFG", gemm_cfg)
-    monkeypatch.setenv("MOE_GEMM_KSPLIT", ks)
+    set_env(monkeypatch, "MOE_GEMM_CFG", gemm_cfg)
+    set_env(monkeypatch, "MOE_GEMM_KSPLIT", ks)
     print(f"[ksplit {ks} cfg {gemm_cfg}] {cfg.name}", flush=True)
     inp = W.make_inputs(cfg)
     ref = oracle_forward(cfg, inp)
@@ -475,7 +475,7 @@ def test_decode_shapes(cfg, ks, monkeypatch):
     """Decode-sized layers (1 to 8 tokens) against the oracle, with the
     automatic contraction split and without it."""
     if ks != "auto":
-        monkeypatch.setenv("MOE_GEMM_KSPLIT", ks)
+        set_env(monkeypatch, "MOE_GEMM_KSPLIT", ks)
     print(f"[decode ksplit {ks}] {cfg.name}", flush=True)
     inp = W.make_inputs(cfg)
     ref = oracle_forward(cfg, inp)
@@ -519,9 +519,9 @@ def test_router_logits_and_selection(cfg, kernel, monkeypatch):
     choice; 1-tiled / 1-split: for E > 64, every expert per workgroup / the
     experts split over workgroups; 1-gemv: one wave per expert, where the
     tokens fit) and the general GEMM path (0)."""
-    monkeypatch.setenv("MOE_ROUTER_KERNEL", kernel[0])
+    set_env(monkeypatch, "MOE_ROUTER_KERNEL", kernel[0])
     if kernel != "1" and kernel[0] == "1":
-        monkeypatch.setenv("MOE_ROUTER_PATH", kernel[2:])
+        set_env(monkeypatch, "MOE_ROUTER_PATH", kernel[2:])
     print(f"[router {kernel}] {cfg.name}", flush=True)
     T, E, k = cfg.num_tokens, cfg.num_experts, cfg.top_k
     inp = W.make_inputs(cfg, with_experts=False)
@@ -871,6 +871,7 @@ def test_weight_gradient_variants_identical(cfg):
     def run(env):
         old = {k: os.environ.get(k) for k in env}
         os.environ.update(env)
+        M.moe_reload_tuning()
         try:
             out = dict(dx=torch.empty((T, D), dtype=torch.bfloat16, device="cuda"),
                        dwr=torch.empty((E, D), dtype=torch.float32, device="cuda"),
@@ -888,6 +889,7 @@ def test_weight_gradient_variants_identical(cfg):
                     os.environ.pop(k, None)
                 else:
                     os.environ[k] = v
+            M.moe_reload_tuning()
 
     base = run({})
     for env in ({"MOE_WGRAD_SWZ": "0"}, {"MOE_WGRAD_SWZ": "1"}, {"MOE_WGRAD_TILE": "128"},

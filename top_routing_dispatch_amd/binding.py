@@ -27,7 +27,7 @@ EXPORTED = ("moe_capacity", "moe_workspace_size", "moe_route", "moe_permute", "m
             "moe_combine", "moe_load_stats", "moe_layer_forward", "moe_layer_forward_timed",
             "moe_layer_backward", "moe_expert_choice_capacity", "moe_expert_choice_forward", "moe_ep_send_layout",
             "moe_ep_recv_layout",
-            "moe_status_string", "moe_last_error")
+            "moe_reload_tuning", "moe_status_string", "moe_last_error")
 STAGES = ("router_logits", "route_select", "permute", "expert_gate_up", "expert_down", "shared_gate_up",
           "shared_down", "combine", "load_stats")
 
@@ -91,12 +91,19 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = ctypes.c_int
+        L.moe_reload_tuning.argtypes = []
+        L.moe_reload_tuning.restype = ctypes.c_int
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_last_error.argtypes = []
         L.moe_last_error.restype = ctypes.c_char_p
         _lib = L
     return _lib
+
+
+def moe_reload_tuning():
+    """Re-read the MOE_* tuning variables (the library reads them once)."""
+    _check("moe_reload_tuning", lib().moe_reload_tuning())
 
 
 def make_config(cfg) -> moe_config:
@@ -140,6 +147,8 @@ def _arg(fn: str, name: str, t, kind, numel: int, cfg=None, required: bool = Fal
         return
     if not isinstance(t, torch.Tensor):
         raise ValueError(f"{fn}: {name} must be a torch.Tensor")
+    if numel == 0 and t.numel() == 0:
+        return                           # nothing is read or written through it
     if not _on_device(t):
         raise ValueError(f"{fn}: {name} must be on the GPU (got {t.device})")
     if not t.is_contiguous():
@@ -263,7 +272,11 @@ def moe_expert_ffn(cfg, num_groups, d_ff, activation, max_rows, x_in, gather_row
 def moe_combine(cfg, y_perm, row_of, topk_w, y_shared, y, stream=None):
     T, D, k = cfg.num_tokens, cfg.d_model, cfg.top_k
     fn = "moe_combine"
-    _arg(fn, "y_perm", y_perm, "act", _rows_cap(cfg) * D, cfg)
+    # row_of (device data) names the rows of y_perm that are read: they are
+    # the caller's to provide; here only whole rows are required
+    _arg(fn, "y_perm", y_perm, "act", D if T > 0 and _rows_cap(cfg) > 0 else 0, cfg)
+    if y_perm is not None and y_perm.numel() % D:
+        raise ValueError(f"{fn}: y_perm must hold whole rows of {D}")
     _arg(fn, "row_of", row_of, _I32, T * k, cfg, required=T > 0)
     _arg(fn, "topk_w", topk_w, _F32, T * k, cfg, required=T > 0)
     _arg(fn, "y_shared", y_shared, "act", T * D, cfg)

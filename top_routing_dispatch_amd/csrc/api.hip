@@ -192,8 +192,8 @@ size_t router_split_bytes(const moe_config* c) {
 
 // MOE_ROUTER_KERNEL=0 keeps the router on the general GEMM (tuning aid).
 bool router_kernel_enabled() {
-  const char* env = getenv("MOE_ROUTER_KERNEL");
-  return env == nullptr || *env == '\0' || atoi(env) != 0;
+  const int v = tuning().router_kernel;
+  return v == kUnset || v != 0;
 }
 
 moe_status run_router_logits(const moe_config* c, const void* x, const void* w_router, float* logits,
@@ -262,11 +262,9 @@ moe_status mark(void* const* ev, int stage, int which, hipStream_t s) {
 // that of the down projection alone.
 int pick_cfg(int act, int K, int max_rows, int G, bool down) {
   if (act != BF16 || K % 64 != 0) return -1;
-  const char* env = down && getenv("MOE_GEMM_CFG_DOWN") != nullptr ? getenv("MOE_GEMM_CFG_DOWN") : getenv("MOE_GEMM_CFG");
-  if (env != nullptr && *env != '\0') {
-    const int c = atoi(env);
-    return (c >= -1 && c < kGemmConfigs) ? c : -1;
-  }
+  const Tuning t = tuning();
+  const int forced = down && t.gemm_cfg_down != kUnset ? t.gemm_cfg_down : t.gemm_cfg;
+  if (forced != kUnset) return (forced >= -1 && forced < kGemmConfigs) ? forced : -1;
   // measured on MI355X at the Switch / Mixtral / DeepSeekMoE / DeepSeek-V3
   // shapes: 256x256 tiles on 8 waves (64-deep slices, interleaved schedule,
   // weights fetched two slices ahead) once groups are a few hundred rows
@@ -320,11 +318,8 @@ constexpr long long kMaxPartialBytes = 256LL << 20;
 int pick_ksplit(int act, int cfg, int epi, int N, int K, int G, int max_rows, bool grouped) {
   if (act != BF16 || cfg < kGemmV2Configs + kGemmV3Configs || K % 64 != 0 || max_rows <= 0) return 1;
   const int nk = K / 64;
-  const char* env = getenv("MOE_GEMM_KSPLIT");
-  if (env != nullptr && *env != '\0') {
-    const int f = atoi(env);
-    if (f == 1 || ((f == 2 || f == 4 || f == 8) && nk % f == 0)) return f;
-  }
+  const int f = tuning().gemm_ksplit;
+  if (f != kUnset && (f == 1 || ((f == 2 || f == 4 || f == 8) && nk % f == 0))) return f;
   const int c = cfg - kGemmV2Configs - kGemmV3Configs;
   const int cols = epi == EPI_SWIGLU ? gemm_ws_bn(c) / 2 : gemm_ws_bn(c);
   const int bm = gemm_ws_bm(c);
@@ -357,12 +352,11 @@ FfnPlan plan_ffn(int act, int activation, int D, int F, int max_rows, int G, boo
   // and a 5-deep ring (measured ~1% per DeepSeek-V3-shaped layer ahead of the
   // 64x256 persistent configuration of the deep-tile kernel)
   pl.cfg_sh = kGemmV2Configs + kGemmV3Configs + 3;
-  const char* sh_env = getenv("MOE_GEMM_SHCFG");       // tuning aid: a configuration index >= kGemmV2Configs
-  if (sh_env != nullptr && *sh_env != '\0' && atoi(sh_env) >= kGemmV2Configs && atoi(sh_env) < kGemmConfigs)
-    pl.cfg_sh = atoi(sh_env);
+  const Tuning t = tuning();
+  if (t.gemm_shcfg != kUnset && t.gemm_shcfg >= kGemmV2Configs && t.gemm_shcfg < kGemmConfigs)
+    pl.cfg_sh = t.gemm_shcfg;       // tuning aid: a configuration index >= kGemmV2Configs
   pl.sh_rows = cfg_bm(act, pl.cfg_sh);
-  const char* cfg_env = getenv("MOE_GEMM_CFG");
-  const bool forced = cfg_env != nullptr && *cfg_env != '\0';
+  const bool forced = t.gemm_cfg != kUnset;
   if (!forced && pl.cfg_up >= 0 && pl.cfg_dn >= 0 && D % 64 == 0 && F % 64 == 0 && max_rows <= pl.sh_rows) {
     pl.cfg_up = pl.cfg_sh;
     pl.cfg_dn = pl.cfg_sh;
@@ -372,8 +366,7 @@ FfnPlan plan_ffn(int act, int activation, int D, int F, int max_rows, int G, boo
   const bool able = grouped && pl.cfg_up >= 0 && pl.cfg_dn >= 0 && D % 64 == 0 && F % 64 == 0;
   const int avg = G > 0 ? max_rows / G : max_rows;
   pl.split = able && D >= 1024 && F >= 1024 && avg < 320 && max_rows > pl.sh_rows;
-  const char* env = getenv("MOE_GEMM_SPLIT");
-  if (able && env != nullptr && *env != '\0') pl.split = atoi(env) != 0;
+  if (able && t.gemm_split != kUnset) pl.split = t.gemm_split != 0;
   const int epi_up = activation == SWIGLU ? EPI_SWIGLU : EPI_GELU;
   pl.ks_up = pick_ksplit(act, pl.cfg_up, epi_up, F, D, G, max_rows, grouped);
   pl.ks_dn = pick_ksplit(act, pl.cfg_dn, EPI_STORE_ACT, D, F, G, max_rows, grouped);
@@ -413,8 +406,8 @@ size_t ffn_partial_bytes_any(int act, int D, int F, int max_rows, int G) {
 // at K = 1408 or 2048, where it is not used.  MOE_GEMM_TAIL=0 turns it off
 // (tuning aid).
 bool tail_split_enabled() {
-  const char* env = getenv("MOE_GEMM_TAIL");
-  return env == nullptr || *env == '\0' || atoi(env) != 0;
+  const int v = tuning().gemm_tail;
+  return v == kUnset || v != 0;
 }
 constexpr int kTailParentCfg = kGemmV2Configs + 0;   // 256x256 tiles, one workgroup per CU
 constexpr int kTailChildCfg = kGemmV2Configs + 6;    // 128x128 tiles, 64-deep slices
@@ -450,10 +443,32 @@ hipError_t launch_gemm(int act, int cfg, const GroupedGemm& g, hipStream_t s) {
 // caller when offsets are given); prefix_ws has room for three more prefixes
 // of G+1 entries (the down projection's when it tiles differently, or the
 // class prefixes of a split).
+// A second stream for the shallow groups of a split: their persistent
+// weight-streaming launches take `cus` CUs (their HBM stream needs few) while
+// the deep-tile launches, which are bound by the matrix cores, run on the
+// caller's stream on the remaining CUs, and on all of them once the shallow
+// groups are done.
+struct SideStream {
+  hipStream_t s;
+  hipEvent_t fork, join;
+  int cus;
+};
+
+// CUs of the concurrent shallow-group launch (MOE_SHALLOW_CUS overrides;
+// 0 runs the shallow groups in line after the deep ones).  Measured on
+// MI355X at the DeepSeek-V3 shape (routed FFN, deep + shallow): in line
+// 7.01 ms; beside the deep tiles on 64 CUs 6.71, 96 6.85, 128 6.96, 160 6.95.
+int shallow_cus() {
+  const int v = tuning().shallow_cus;
+  if (v != kUnset) return v < 0 ? 0 : v;
+  return 64;
+}
+
 moe_status run_ffn(int act, int activation, int G, int D, int F, int max_rows, const void* x_in,
                    const int32_t* gather, const int32_t* offsets, const int32_t* prefix_up,
                    int32_t* prefix_ws, const void* w13, const void* w2, void* h, void* y_out, float* part,
-                   hipStream_t s, void* const* ev = nullptr, int stage_up = 0, int stage_down = 0) {
+                   hipStream_t s, void* const* ev = nullptr, int stage_up = 0, int stage_down = 0,
+                   const SideStream* side = nullptr) {
   const FfnPlan pl = plan_ffn(act, activation, D, F, max_rows, G, offsets != nullptr);
   const int n_mat = activation == SWIGLU ? 2 : 1;
   GroupedGemm g1{};
@@ -491,13 +506,32 @@ moe_status run_ffn(int act, int activation, int G, int D, int F, int max_rows, c
     MOE_TRY_HIP("tile prefix", launch_tile_prefix(offsets, G, pl.bm_dn, prefix_ws, s));
     g2.tile_prefix = prefix_ws;
   }
+  // Concurrent shallow groups: both of their projections on the side stream
+  // (the gate/up of a group before its down, in stream order), issued before
+  // the deep launches so that they hold their CUs from the start; the two
+  // classes write disjoint rows of h and y_out.  The stage events then span
+  // the deep launches (gate/up) and the rest up to the join (down).
+  // (only the shallow launches may use the contraction split's partial sums,
+  // which the two launches of the side stream use one after the other)
+  const bool concurrent = pl.split && side != nullptr && side->cus > 0 &&
+                          pl.cfg_sh >= kGemmV2Configs + kGemmV3Configs && pl.ks_up <= 1 && pl.ks_dn <= 1;
   MOE_TRY(mark(ev, stage_up, 0, s));
+  if (concurrent) {
+    g1s.cus = side->cus;
+    g2s.cus = side->cus;
+    MOE_TRY_HIP("fork", hipEventRecord(side->fork, s));
+    MOE_TRY_HIP("fork", hipStreamWaitEvent(side->s, side->fork, 0));
+    MOE_TRY_HIP("expert gate/up (shallow groups)", launch_gemm(act, pl.cfg_sh, g1s, side->s));
+    MOE_TRY_HIP("expert down (shallow groups)", launch_gemm(act, pl.cfg_sh, g2s, side->s));
+    MOE_TRY_HIP("join", hipEventRecord(side->join, side->s));
+  }
   MOE_TRY_HIP("expert gate/up", launch_gemm(act, pl.cfg_up, g1, s));
-  if (pl.split) MOE_TRY_HIP("expert gate/up (shallow groups)", launch_gemm(act, pl.cfg_sh, g1s, s));
+  if (pl.split && !concurrent) MOE_TRY_HIP("expert gate/up (shallow groups)", launch_gemm(act, pl.cfg_sh, g1s, s));
   MOE_TRY(mark(ev, stage_up, 1, s));
   MOE_TRY(mark(ev, stage_down, 0, s));
   MOE_TRY_HIP("expert down", launch_gemm_tail_split(act, pl.cfg_dn, g2, s));
-  if (pl.split) MOE_TRY_HIP("expert down (shallow groups)", launch_gemm(act, pl.cfg_sh, g2s, s));
+  if (pl.split && !concurrent) MOE_TRY_HIP("expert down (shallow groups)", launch_gemm(act, pl.cfg_sh, g2s, s));
+  if (concurrent) MOE_TRY_HIP("join", hipStreamWaitEvent(s, side->join, 0));
   MOE_TRY(mark(ev, stage_down, 1, s));
   return MOE_OK;
 }
@@ -534,9 +568,8 @@ moe_status run_ffn_part(int act, int activation, int G, int D, int F, int rows, 
 // auxiliary stream, joined before the combine.  MOE_SHARED_OVERLAP overrides
 // (tuning aid).
 int shared_overlap() {
-  const char* env = getenv("MOE_SHARED_OVERLAP");
-  if (env != nullptr && *env != '\0' && atoi(env) >= 0 && atoi(env) <= 2) return atoi(env);
-  return 2;
+  const int v = tuning().shared_overlap;
+  return (v != kUnset && v >= 0 && v <= 2) ? v : 2;
 }
 
 // A library-owned stream per device for the layer's work that does not depend
@@ -548,6 +581,8 @@ struct AuxStream {
   hipStream_t s = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
   hipEvent_t stats_fork = nullptr, stats_join = nullptr;   // load statistics beside the experts
+  hipStream_t s2 = nullptr;                                 // shallow expert groups beside the deep ones
+  hipEvent_t side_fork = nullptr, side_join = nullptr;
 };
 constexpr int kMaxDevices = 64;
 AuxStream g_aux[kMaxDevices];
@@ -564,6 +599,9 @@ moe_status aux_stream(AuxStream** out) {
     MOE_TRY_HIP("join event", hipEventCreateWithFlags(&a.join, hipEventDisableTiming));
     MOE_TRY_HIP("fork event", hipEventCreateWithFlags(&a.stats_fork, hipEventDisableTiming));
     MOE_TRY_HIP("join event", hipEventCreateWithFlags(&a.stats_join, hipEventDisableTiming));
+    MOE_TRY_HIP("side stream", hipStreamCreateWithFlags(&a.s2, hipStreamNonBlocking));
+    MOE_TRY_HIP("fork event", hipEventCreateWithFlags(&a.side_fork, hipEventDisableTiming));
+    MOE_TRY_HIP("join event", hipEventCreateWithFlags(&a.side_join, hipEventDisableTiming));
   }
   *out = &a;
   return MOE_OK;
@@ -887,8 +925,8 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* wt, const
 // the backward runs the expert products itself).
 static moe_status layer_forward_impl(const moe_config* cfg, const moe_weights* wt, const void* x, void* y,
                                      int32_t* topk_idx, float* topk_w, int32_t* counts, float alpha, float* stats,
-                              int32_t* dropped, void* ws, size_t ws_bytes, void* stream, void* const* ev,
-                              bool routing_only) {
+                                     int32_t* dropped, void* ws, size_t ws_bytes, void* stream, void* const* ev,
+                                     bool routing_only) {
   MOE_TRY(validate_config(cfg));
   if (wt == nullptr || wt->w_router == nullptr || wt->w13 == nullptr || wt->w2 == nullptr)
     return MOE_ERR_INVALID_ARGUMENT;
@@ -927,9 +965,13 @@ static moe_status layer_forward_impl(const moe_config* cfg, const moe_weights* w
   // The load statistics need only the probabilities and the counts: they run
   // on the auxiliary stream beside the expert GEMMs, joined at the end.
   const bool stats_aside = any && want_stats;
+  // The shallow expert groups (when the plan splits them off) run on a second
+  // auxiliary stream beside the deep ones.
+  const bool side_ffn = !routing_only && any && d.rows_cap > 0 && shallow_cus() > 0 &&
+                        plan_ffn(cfg->act_dtype, cfg->activation, D, cfg->d_ff, d.rows_cap, E, true).split;
   std::unique_lock<std::mutex> aux_lock(g_aux_mu, std::defer_lock);
   AuxStream* aux = nullptr;
-  if (overlap > 0 || stats_aside) {
+  if (overlap > 0 || stats_aside || side_ffn) {
     aux_lock.lock();
     MOE_TRY(aux_stream(&aux));
   }
@@ -987,10 +1029,12 @@ static moe_status layer_forward_impl(const moe_config* cfg, const moe_weights* w
   if (any) {
     void* h = at<void>(ws, L.h);
     void* yperm = at<void>(ws, L.yperm);
+    SideStream side{};
+    if (side_ffn) side = SideStream{aux->s2, aux->side_fork, aux->side_join, shallow_cus()};
     if (d.rows_cap > 0)
       MOE_TRY(run_ffn(cfg->act_dtype, cfg->activation, E, D, cfg->d_ff, d.rows_cap, x, tor, off, tp,
                       at<int32_t>(ws, L.tile_prefix2), wt->w13, wt->w2, h, yperm, at<float>(ws, L.kpart), s, ev,
-                      MOE_STAGE_EXPERT_GATE_UP, MOE_STAGE_EXPERT_DOWN));
+                      MOE_STAGE_EXPERT_GATE_UP, MOE_STAGE_EXPERT_DOWN, side_ffn ? &side : nullptr));
     if (shared && overlap == 0)
       MOE_TRY(run_ffn_part(cfg->act_dtype, SWIGLU, 1, D, SF, T, x, wt->ws13, wt->ws2, at<void>(ws, L.h_shared), y,
                            at<float>(ws, L.kpart_shared), s, ev, MOE_STAGE_SHARED_GATE_UP, true));

@@ -600,10 +600,9 @@ hipError_t launch_wgrad(const bf16_t* A, int lda, const bf16_t* B, int ldb, cons
   if (lda % 4 != 0 || ldb % 4 != 0 || M % 4 != 0 || N % 4 != 0) return hipErrorInvalidValue;   // 8-byte column groups
   // 256x256 tiles (eight waves) for large outputs: each operand row slice is
   // re-read by half as many workgroups as with 128x128
-  const char* env = getenv("MOE_WGRAD_TILE");      // 128 or 256 forces a tile (tuning aid)
-  const int forced = env != nullptr ? atoi(env) : 0;
-  const char* senv = getenv("MOE_WGRAD_SWZ");      // LDS chunk permutation 0 / 1 / 2 (tuning aid)
-  const int swz = senv != nullptr ? atoi(senv) : 2;
+  const Tuning t = tuning();
+  const int forced = t.wgrad_tile != kUnset ? t.wgrad_tile : 0;   // 128 or 256 forces a tile (tuning aid)
+  const int swz = t.wgrad_swz != kUnset ? t.wgrad_swz : 2;         // LDS chunk permutation 0 / 1 / 2 (tuning aid)
 #define MOE_WG(BM_, BN_, WGM_, WGN_, SWZ_)                                                                   \
   hipLaunchKernelGGL((wgrad_kernel<BM_, BN_, WGM_, WGN_, SWZ_>), dim3(ceil_div(N, BN_), ceil_div(M, BM_), G), \
                      dim3(64 * WGM_ * WGN_), 0, s, A, lda, B, ldb, b_rows, offsets, rows_max, M, N, C)

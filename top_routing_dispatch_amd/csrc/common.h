@@ -59,6 +59,26 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
 }
 
 // Compute units of the current device (cached after the first call).
+// Tuning aids (MOE_* environment variables forcing a kernel choice), read
+// once per process; kUnset where a variable is not set.  Launch paths take a
+// copy from tuning() and never call getenv.
+constexpr int kUnset = -2147483647 - 1;
+struct Tuning {
+  int router_kernel = kUnset;    // MOE_ROUTER_KERNEL: 0 keeps the router on the general GEMM
+  int router_path = kUnset;      // MOE_ROUTER_PATH: tiled (0) / split (1) / gemv (2)
+  int gemm_cfg = kUnset;         // MOE_GEMM_CFG: tile configuration of the grouped GEMMs
+  int gemm_cfg_down = kUnset;    // MOE_GEMM_CFG_DOWN: ... of the down projection alone
+  int gemm_ksplit = kUnset;      // MOE_GEMM_KSPLIT: contraction split of weight-streaming launches
+  int gemm_shcfg = kUnset;       // MOE_GEMM_SHCFG: configuration of the shallow groups
+  int gemm_split = kUnset;       // MOE_GEMM_SPLIT: 0 / 1 shallow-group split off / on
+  int gemm_tail = kUnset;        // MOE_GEMM_TAIL: 0 turns the last-round split off
+  int shared_overlap = kUnset;   // MOE_SHARED_OVERLAP: 0 / 1 / 2
+  int shallow_cus = kUnset;      // MOE_SHALLOW_CUS: CUs of the concurrent shallow-group launch (0 = in line)
+  int wgrad_tile = kUnset;       // MOE_WGRAD_TILE: 128 / 256
+  int wgrad_swz = kUnset;        // MOE_WGRAD_SWZ: 0 / 1 / 2
+};
+Tuning tuning();
+
 inline int num_cus() {
   static std::atomic<int> cached{0};     // host threads may race to fill it: same value
   int n = cached.load(std::memory_order_relaxed);
@@ -137,6 +157,9 @@ struct GroupedGemm {
   int tail_mode;
   int round;
   int tail_pn;
+  // Persistent launches: CUs the grid may occupy (0 = all of them), so that
+  // a launch can run beside another one on the remaining CUs.
+  int cus;
   // Split of the contraction (weight-streaming kernel only): with ksplit > 1
   // every tile runs as ksplit units over consecutive K / ksplit slices; each
   // unit writes its float32 sums to partial[(ks * M_max + row) * ldp + col]

@@ -474,7 +474,8 @@ hipError_t launch_ws(const GroupedGemm& p, hipStream_t s) {
     return hipErrorInvalidValue;
   const long long bound = tiles * KS;
   if (bound > 0x7fffffffLL) return hipErrorInvalidValue;
-  const int blocks = (int)std::min<long long>(bound, (long long)num_cus() * OCC);
+  const int cus = p.cus > 0 ? std::min(p.cus, num_cus()) : num_cus();
+  const int blocks = (int)std::min<long long>(bound, (long long)cus * OCC);
   static std::atomic<bool> allowed[64];   // per device: attribute set (host threads may race)
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);

@@ -376,12 +376,10 @@ int router_path(int T, int E, int D) {
   // on MI355X at E = 8, D = 4096: 8.6 us for one token (small-E kernel 13),
   // 17 us for eight (small-E kernel 14)
   const bool gemv = T <= (E > 64 ? kGemvMaxTokens : 2) && (long long)T * D * 2 <= kGemvLds;
-  const char* env = getenv("MOE_ROUTER_PATH");
-  if (env != nullptr && *env != '\0') {
-    if (strcmp(env, "gemv") == 0 && T <= kGemvMaxTokens && (long long)T * D * 2 <= kGemvLds) return 2;
-    if (strcmp(env, "split") == 0) return 1;
-    if (strcmp(env, "tiled") == 0) return E <= 64 ? 1 : 0;
-  }
+  const int forced = tuning().router_path;
+  if (forced == 2 && T <= kGemvMaxTokens && (long long)T * D * 2 <= kGemvLds) return 2;
+  if (forced == 1) return 1;
+  if (forced == 0) return E <= 64 ? 1 : 0;
   if (gemv) return 2;
   return (E <= 64 || T <= 512) ? 1 : 0;
 }
