@@ -248,6 +248,26 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* weights,
                              int32_t* counts, float alpha, float* stats, int32_t* dropped,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* moe_layer_forward for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * arguments minus the workspace: the call runs in a scratch array that the
+ * library holds in device memory, MOE_STATIC_SCRATCH_BYTES per GPU, kept
+ * from the first call on a GPU until the process ends.  It allocates
+ * nothing, creates no stream or event, and runs every kernel on `stream`
+ * (the shared experts and the load statistics too, so nothing is forked).
+ * A configuration whose moe_workspace_size(MOE_OP_LAYER) exceeds the scratch
+ * is rejected with MOE_ERR_WORKSPACE_TOO_SMALL before any launch
+ * (moe_last_error() names both sizes): 64 MiB holds decode-sized batches,
+ * e.g. 256 tokens at the Mixtral- or DeepSeek-V3-shaped widths.  Every call
+ * on one GPU uses the same scratch: calls that overlap on one GPU (two
+ * streams, two host threads without ordering) race and must be serialised
+ * by the caller.  Results equal moe_layer_forward's. */
+#define MOE_STATIC_SCRATCH_BYTES (64u << 20)
+moe_status moe_layer_forward_static(const moe_config* cfg, const moe_weights* weights,
+                                    const void* x, void* y, int32_t* topk_idx, float* topk_w,
+                                    int32_t* counts, float alpha, float* stats, int32_t* dropped,
+                                    void* stream);
+
 /* Re-reads the MOE_* tuning variables of the environment (tuning aids that
  * force a kernel choice: MOE_GEMM_CFG, MOE_GEMM_SPLIT, MOE_ROUTER_PATH, ...).
  * The library reads them once, at its first launch, and otherwise only here:

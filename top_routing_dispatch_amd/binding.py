@@ -24,7 +24,7 @@ MOE_SWIGLU, MOE_GELU = 0, 1
  MOE_OP_LOAD_STATS, MOE_OP_LAYER, MOE_OP_EXPERT_CHOICE, MOE_OP_LAYER_BACKWARD) = range(8)
 
 EXPORTED = ("moe_capacity", "moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn",
-            "moe_combine", "moe_load_stats", "moe_layer_forward", "moe_layer_forward_timed",
+            "moe_combine", "moe_load_stats", "moe_layer_forward", "moe_layer_forward_timed", "moe_layer_forward_static",
             "moe_layer_backward", "moe_expert_choice_capacity", "moe_expert_choice_forward", "moe_ep_send_layout",
             "moe_ep_recv_layout",
             "moe_reload_tuning", "moe_status_string", "moe_last_error")
@@ -79,6 +79,7 @@ def lib() -> ctypes.CDLL:
             "moe_layer_forward": [cfgp, ctypes.POINTER(moe_weights), vp, vp, vp, vp, vp, f32, vp, vp, vp, sz, vp],
             "moe_layer_forward_timed": [cfgp, ctypes.POINTER(moe_weights), vp, vp, vp, vp, vp, f32, vp, vp, vp, sz,
                                         vp, ctypes.POINTER(vp)],
+            "moe_layer_forward_static": [cfgp, ctypes.POINTER(moe_weights), vp, vp, vp, vp, vp, f32, vp, vp, vp],
             "moe_layer_backward": [cfgp, ctypes.POINTER(moe_weights), vp, vp, f32, vp, vp, vp, vp, vp, vp, vp, sz,
                                    vp],
             "moe_expert_choice_capacity": [cfgp, ctypes.POINTER(i32)],
@@ -192,7 +193,7 @@ def _stream(stream=None):
 
 def _check(fn: str, st: int):
     if st != MOE_OK:
-        detail = lib().moe_last_error().decode() if st == MOE_ERR_HIP else ""
+        detail = lib().moe_last_error().decode() if st in (MOE_ERR_HIP, MOE_ERR_WORKSPACE_TOO_SMALL) else ""
         raise MoEError(fn, st, detail)
 
 
@@ -311,7 +312,8 @@ def _check_layer_args(fn, cfg, weights, x, y, topk_idx, topk_w, counts, stats, d
     _arg(fn, "counts", counts, _I32, E, cfg)
     _arg(fn, "stats", stats, _F32, 2 * E + 2, cfg)
     _arg(fn, "dropped", dropped, _I32, 1, cfg)
-    _arg(fn, "ws", ws, _BYTES, moe_workspace_size(cfg, MOE_OP_LAYER), cfg, required=T > 0)
+    if fn != "moe_layer_forward_static":
+        _arg(fn, "ws", ws, _BYTES, moe_workspace_size(cfg, MOE_OP_LAYER), cfg, required=T > 0)
 
 
 def moe_layer_forward(cfg, weights: dict, x, y, topk_idx=None, topk_w=None, counts=None, alpha=0.01, stats=None,
@@ -325,6 +327,24 @@ def moe_layer_forward(cfg, weights: dict, x, y, topk_idx=None, topk_w=None, coun
     _check("moe_layer_forward", lib().moe_layer_forward(
         ctypes.byref(c), ctypes.byref(w), _ptr(x), _ptr(y), _ptr(topk_idx), _ptr(topk_w), _ptr(counts),
         float(alpha), _ptr(stats), _ptr(dropped), _ptr(ws), _ws_bytes(ws), _stream(stream)))
+
+
+MOE_STATIC_SCRATCH_BYTES = 64 << 20
+
+
+def moe_layer_forward_static(cfg, weights: dict, x, y, topk_idx=None, topk_w=None, counts=None, alpha=0.01,
+                             stats=None, dropped=None, stream=None):
+    """moe_layer_forward in the library's static device scratch: no workspace
+    argument, nothing allocated (for callers that cannot allocate)."""
+    _check_layer_args("moe_layer_forward_static", cfg, weights, x, y, topk_idx, topk_w, counts, stats, dropped, None)
+    c = make_config(cfg)
+    w = moe_weights()
+    for name, _ in moe_weights._fields_:
+        t = weights.get(name)
+        setattr(w, name, None if t is None else t.data_ptr())
+    _check("moe_layer_forward_static", lib().moe_layer_forward_static(
+        ctypes.byref(c), ctypes.byref(w), _ptr(x), _ptr(y), _ptr(topk_idx), _ptr(topk_w), _ptr(counts),
+        float(alpha), _ptr(stats), _ptr(dropped), _stream(stream)))
 
 
 def moe_layer_forward_timed(cfg, weights: dict, x, y, topk_idx=None, topk_w=None, counts=None, alpha=0.01,

@@ -7,6 +7,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "common.h"
@@ -922,11 +923,13 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* wt, const
 
 // The layer forward; routing_only: stop after the permutation (routing,
 // selection and dispatch tables in the workspace, no expert or shared work:
-// the backward runs the expert products itself).
+// the backward runs the expert products itself); single_stream: every kernel
+// on the caller's stream (no auxiliary stream, so nothing is created on first
+// use).
 static moe_status layer_forward_impl(const moe_config* cfg, const moe_weights* wt, const void* x, void* y,
                                      int32_t* topk_idx, float* topk_w, int32_t* counts, float alpha, float* stats,
                                      int32_t* dropped, void* ws, size_t ws_bytes, void* stream, void* const* ev,
-                                     bool routing_only) {
+                                     bool routing_only, bool single_stream = false) {
   MOE_TRY(validate_config(cfg));
   if (wt == nullptr || wt->w_router == nullptr || wt->w13 == nullptr || wt->w2 == nullptr)
     return MOE_ERR_INVALID_ARGUMENT;
@@ -961,13 +964,13 @@ static moe_status layer_forward_impl(const moe_config* cfg, const moe_weights* w
   // the routed experts, which need the whole chip.
   const bool shared = !routing_only && any && cfg->num_shared > 0;
   const int SF = cfg->num_shared * cfg->d_ff_shared;
-  const int overlap = shared ? shared_overlap() : 0;
+  const int overlap = shared && !single_stream ? shared_overlap() : 0;
   // The load statistics need only the probabilities and the counts: they run
   // on the auxiliary stream beside the expert GEMMs, joined at the end.
-  const bool stats_aside = any && want_stats;
+  const bool stats_aside = any && want_stats && !single_stream;
   // The shallow expert groups (when the plan splits them off) run on a second
   // auxiliary stream beside the deep ones.
-  const bool side_ffn = !routing_only && any && d.rows_cap > 0 && shallow_cus() > 0 &&
+  const bool side_ffn = !routing_only && any && d.rows_cap > 0 && !single_stream && shallow_cus() > 0 &&
                         plan_ffn(cfg->act_dtype, cfg->activation, D, cfg->d_ff, d.rows_cap, E, true).split;
   std::unique_lock<std::mutex> aux_lock(g_aux_mu, std::defer_lock);
   AuxStream* aux = nullptr;
@@ -1065,6 +1068,62 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const moe_weights* wt,
                                    void* const* ev) {
   return layer_forward_impl(cfg, wt, x, y, topk_idx, topk_w, counts, alpha, stats, dropped, ws, ws_bytes, stream,
                             ev, false);
+}
+
+}  // extern "C"
+
+// Scratch of the allocation-free layer forward: one array per GPU, in the
+// library's device code, alive until the process ends.  Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in for
+// the symbol); it uses the device address hipGetSymbolAddress returns, looked
+// up once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[MOE_STATIC_SCRATCH_BYTES];
+
+namespace {
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+moe_status static_scratch(void** out) {
+  int dev = 0;
+  MOE_TRY_HIP("hipGetDevice", hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      MOE_TRY_HIP("scratch address", hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+      if (p == nullptr || (reinterpret_cast<uintptr_t>(p) & 255u) != 0) {
+        snprintf(g_last_error, sizeof(g_last_error), "static scratch: unusable device address");
+        return MOE_ERR_HIP;
+      }
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return MOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+moe_status moe_layer_forward_static(const moe_config* cfg, const moe_weights* wt, const void* x, void* y,
+                                    int32_t* topk_idx, float* topk_w, int32_t* counts, float alpha, float* stats,
+                                    int32_t* dropped, void* stream) {
+  MOE_TRY(validate_config(cfg));
+  Derived d;
+  derive(cfg, &d);
+  const size_t need = layer_layout(cfg, d).total;
+  if (need > (size_t)MOE_STATIC_SCRATCH_BYTES) {
+    snprintf(g_last_error, sizeof(g_last_error),
+             "moe_layer_forward_static: this configuration needs %zu bytes of scratch, the static scratch holds %zu",
+             need, (size_t)MOE_STATIC_SCRATCH_BYTES);
+    return MOE_ERR_WORKSPACE_TOO_SMALL;
+  }
+  void* ws = nullptr;
+  MOE_TRY(static_scratch(&ws));
+  return layer_forward_impl(cfg, wt, x, y, topk_idx, topk_w, counts, alpha, stats, dropped, ws,
+                            (size_t)MOE_STATIC_SCRATCH_BYTES, stream, nullptr, false, true);
 }
 
 moe_status moe_layer_backward(const moe_config* cfg, const moe_weights* wt, const void* x, const void* dy,
