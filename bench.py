@@ -37,7 +37,7 @@ VALU_F32_TFLOPS = 157.3      # published float32 vector peak (packed FP32; the k
 # Files whose change invalidates HBM-traffic counters taken earlier: the GEMM
 # kernels, their launch planning and the synthetic workload recipe.
 TRAFFIC_SOURCES = ("top_routing_dispatch_amd/csrc/common.h", "top_routing_dispatch_amd/csrc/gemm.hip",
-                   "top_routing_dispatch_amd/csrc/gemm_v2.hip", "top_routing_dispatch_amd/csrc/gemm_v3.hip",
+                   "top_routing_dispatch_amd/csrc/gemm_v3.hip",
                    "top_routing_dispatch_amd/csrc/gemm_ws.hip", "top_routing_dispatch_amd/csrc/api.hip",
                    "workloads/__init__.py")
 

@@ -324,9 +324,9 @@ V2_SHAPES = [
 ]
 
 
-# -1: general kernel; 0-9: pipelined 8-wave kernel; 10-21: kernel with 32- or 64-deep slices
-# (19, 20: persistent tiles); 22-29: persistent weight-streaming kernel
-GEMM_TILE_CONFIGS = range(-1, 30)
+# -1: general kernel; 0-11: deep-tile kernel with 32- or 64-deep slices (9, 10:
+# persistent tiles); 12-19: persistent weight-streaming kernel
+GEMM_TILE_CONFIGS = range(-1, 20)
 
 
 @pytest.mark.parametrize("gemm_cfg", [str(c) for c in GEMM_TILE_CONFIGS])
@@ -351,15 +351,15 @@ SPLIT_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("split", ["0", "1", "1-pers19"])
+@pytest.mark.parametrize("split", ["0", "1", "1-pers9"])
 @pytest.mark.parametrize("cfg", SPLIT_SHAPES + V2_SHAPES, ids=lambda c: c.name)
 def test_shallow_group_split(cfg, split, monkeypatch):
     """Expert FFN with shallow groups split off to the persistent
     weight-streaming kernel (1), to the persistent configuration 19 of the
-    deep-tile kernel (1-pers19), and without the split (0), against the oracle."""
+    deep-tile kernel (1-pers9), and without the split (0), against the oracle."""
     set_env(monkeypatch, "MOE_GEMM_SPLIT", split[0])
-    if split == "1-pers19":
-        set_env(monkeypatch, "MOE_GEMM_SHCFG", "19")
+    if split == "1-pers9":
+        set_env(monkeypatch, "MOE_GEMM_SHCFG", "9")
     print(f"[split {split}] {cfg.name}", flush=True)
     inp = W.make_inputs(cfg)
     ref = oracle_forward(cfg, inp)
@@ -385,7 +385,7 @@ TAIL_SHAPES = [
 def test_down_tail_split(cfg, tail, monkeypatch):
     """The down projection on 256x256 tiles with its last, partial round run as
     quarter tiles (1) and without (0), against the oracle."""
-    set_env(monkeypatch, "MOE_GEMM_CFG", "10")
+    set_env(monkeypatch, "MOE_GEMM_CFG", "0")
     set_env(monkeypatch, "MOE_GEMM_TAIL", tail)
     print(f"[tail {tail}] {cfg.name}", flush=True)
     inp = W.make_inputs(cfg)
@@ -406,10 +406,10 @@ WS_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("gemm_cfg", ["default"] + [str(c) for c in range(22, 30)])
+@pytest.mark.parametrize("gemm_cfg", ["default"] + [str(c) for c in range(12, 20)])
 @pytest.mark.parametrize("cfg", WS_SHAPES, ids=lambda c: c.name)
 def test_weight_streaming_many_tiles(cfg, gemm_cfg, monkeypatch):
-    """The persistent weight-streaming GEMM (its configurations 22-29, and the
+    """The persistent weight-streaming GEMM (its configurations 12-19, and the
     default choice for these shallow groups) against the oracle with several
     tiles per workgroup."""
     if gemm_cfg != "default":
@@ -433,7 +433,7 @@ KSPLIT_SHAPES = [
 
 
 @pytest.mark.parametrize("ks", ["2", "4", "8"])
-@pytest.mark.parametrize("gemm_cfg", [str(c) for c in range(22, 30)])
+@pytest.mark.parametrize("gemm_cfg", [str(c) for c in range(12, 20)])
 @pytest.mark.parametrize("cfg", KSPLIT_SHAPES, ids=lambda c: c.name)
 def test_contraction_split(cfg, gemm_cfg, ks, monkeypatch):
     """Every configuration of the weight-streaming GEMM with its contraction

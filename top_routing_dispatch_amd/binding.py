@@ -14,7 +14,9 @@ from typing import Optional
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmoe_hip.so")
+# the in-tree build; MOE_LIB_PATH names another build of the same sources
+# (a tuning variant)
+LIB_PATH = os.environ.get("MOE_LIB_PATH") or os.path.join(_PKG, "libmoe_hip.so")
 
 MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1

@@ -39,27 +39,31 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, jobs: int = 8, out: str = LIB_PATH, defines=(), build_dir: str = BUILD_DIR) -> str:
+    """Compile every source and link `out` (the in-tree library by default;
+    `defines` and another `out` / `build_dir` give a variant build for
+    kernel-tuning experiments, loaded through MOE_LIB_PATH)."""
+    os.makedirs(build_dir, exist_ok=True)
     sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     if not sources:
         raise RuntimeError("no HIP sources found")
+    dflags = [f"-D{d}" for d in defines]
 
     def compile_one(src):
-        obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-        out = _run([HIPCC, *FLAGS, "-c", src, "-o", obj])
-        if verbose and out.strip():
-            print(out)
+        obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+        log = _run([HIPCC, *FLAGS, *dflags, "-c", src, "-o", obj])
+        if verbose and log.strip():
+            print(log)
         return obj
 
     with ThreadPoolExecutor(max(1, jobs)) as ex:
         objs = list(ex.map(compile_one, sources))
-    tmp = LIB_PATH + ".tmp"
+    tmp = out + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB_PATH}")
-    return LIB_PATH
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":

@@ -274,8 +274,8 @@ int pick_cfg(int act, int K, int max_rows, int G, bool down) {
   // workgroups per CU, so that one's activation epilogue overlaps the
   // other's weight stream; down: one workgroup per CU, four slices deep)
   const int avg = G > 0 ? max_rows / G : max_rows;
-  if (avg >= 160) return kGemmV2Configs;
-  return kGemmV2Configs + kGemmV3Configs + (down ? 5 : 6);
+  if (avg >= 160) return 0;
+  return kGemmV3Configs + (down ? 5 : 6);
 }
 
 int cfg_bm(int act, int cfg) {
@@ -284,9 +284,8 @@ int cfg_bm(int act, int cfg) {
     GroupedGemm dummy{};
     return gemm_bf16_bm(dummy);
   }
-  if (cfg < kGemmV2Configs) return gemm_v2_bm(cfg);
-  if (cfg < kGemmV2Configs + kGemmV3Configs) return gemm_v3_bm(cfg - kGemmV2Configs);
-  return gemm_ws_bm(cfg - kGemmV2Configs - kGemmV3Configs);
+  if (cfg < kGemmV3Configs) return gemm_v3_bm(cfg);
+  return gemm_ws_bm(cfg - kGemmV3Configs);
 }
 
 struct FfnPlan {
@@ -317,11 +316,11 @@ struct FfnPlan {
 constexpr int kSplitUnits = 256;
 constexpr long long kMaxPartialBytes = 256LL << 20;
 int pick_ksplit(int act, int cfg, int epi, int N, int K, int G, int max_rows, bool grouped) {
-  if (act != BF16 || cfg < kGemmV2Configs + kGemmV3Configs || K % 64 != 0 || max_rows <= 0) return 1;
+  if (act != BF16 || cfg < kGemmV3Configs || K % 64 != 0 || max_rows <= 0) return 1;
   const int nk = K / 64;
   const int f = tuning().gemm_ksplit;
   if (f != kUnset && (f == 1 || ((f == 2 || f == 4 || f == 8) && nk % f == 0))) return f;
-  const int c = cfg - kGemmV2Configs - kGemmV3Configs;
+  const int c = cfg - kGemmV3Configs;
   const int cols = epi == EPI_SWIGLU ? gemm_ws_bn(c) / 2 : gemm_ws_bn(c);
   const int bm = gemm_ws_bm(c);
   const long long m_tiles = grouped ? max_rows / bm + (G < max_rows ? G : max_rows) : ceil_div(max_rows, bm);
@@ -352,10 +351,10 @@ FfnPlan plan_ffn(int act, int activation, int D, int F, int max_rows, int G, boo
   // shallow groups: the persistent weight-streaming kernel with 64x128 tiles
   // and a 5-deep ring (measured ~1% per DeepSeek-V3-shaped layer ahead of the
   // 64x256 persistent configuration of the deep-tile kernel)
-  pl.cfg_sh = kGemmV2Configs + kGemmV3Configs + 3;
+  pl.cfg_sh = kGemmV3Configs + 3;
   const Tuning t = tuning();
-  if (t.gemm_shcfg != kUnset && t.gemm_shcfg >= kGemmV2Configs && t.gemm_shcfg < kGemmConfigs)
-    pl.cfg_sh = t.gemm_shcfg;       // tuning aid: a configuration index >= kGemmV2Configs
+  if (t.gemm_shcfg != kUnset && t.gemm_shcfg >= 0 && t.gemm_shcfg < kGemmConfigs)
+    pl.cfg_sh = t.gemm_shcfg;       // tuning aid: a configuration index >= 0
   pl.sh_rows = cfg_bm(act, pl.cfg_sh);
   const bool forced = t.gemm_cfg != kUnset;
   if (!forced && pl.cfg_up >= 0 && pl.cfg_dn >= 0 && D % 64 == 0 && F % 64 == 0 && max_rows <= pl.sh_rows) {
@@ -410,8 +409,8 @@ bool tail_split_enabled() {
   const int v = tuning().gemm_tail;
   return v == kUnset || v != 0;
 }
-constexpr int kTailParentCfg = kGemmV2Configs + 0;   // 256x256 tiles, one workgroup per CU
-constexpr int kTailChildCfg = kGemmV2Configs + 6;    // 128x128 tiles, 64-deep slices
+constexpr int kTailParentCfg = 0;   // 256x256 tiles, one workgroup per CU
+constexpr int kTailChildCfg = 6;    // 128x128 tiles, 64-deep slices
 
 hipError_t launch_gemm(int act, int cfg, const GroupedGemm& g, hipStream_t s);
 
@@ -431,11 +430,10 @@ hipError_t launch_gemm_tail_split(int act, int cfg, const GroupedGemm& g, hipStr
 }
 
 hipError_t launch_gemm(int act, int cfg, const GroupedGemm& g, hipStream_t s) {
-  if (g.ksplit > 1 && (act != BF16 || cfg < kGemmV2Configs + kGemmV3Configs)) return hipErrorInvalidValue;
+  if (g.ksplit > 1 && (act != BF16 || cfg < kGemmV3Configs)) return hipErrorInvalidValue;
   if (act != BF16) return launch_gemm_f32(g, F32, F32, s);
-  if (cfg >= kGemmV2Configs + kGemmV3Configs) return launch_gemm_ws(g, cfg - kGemmV2Configs - kGemmV3Configs, s);
-  if (cfg >= kGemmV2Configs) return launch_gemm_v3(g, cfg - kGemmV2Configs, s);
-  if (cfg >= 0) return launch_gemm_v2(g, cfg, s);
+  if (cfg >= kGemmV3Configs) return launch_gemm_ws(g, cfg - kGemmV3Configs, s);
+  if (cfg >= 0) return launch_gemm_v3(g, cfg, s);
   return launch_gemm_bf16(g, s);
 }
 
@@ -488,6 +486,10 @@ moe_status run_ffn(int act, int activation, int G, int D, int F, int max_rows, c
   g2.epilogue = EPI_STORE_ACT;
   g1.partial = part; g1.ldp = n_mat * F; g1.ksplit = pl.ks_up;
   g2.partial = part; g2.ldp = D; g2.ksplit = pl.ks_dn;
+  {
+    const int gm = tuning().tile_gm;
+    g1.tile_gm = g2.tile_gm = (gm != kUnset && gm > 0 && gm <= 64) ? gm : 0;
+  }
   GroupedGemm g1s = g1, g2s = g2;       // shallow groups of a split
   g1s.ksplit = pl.ks_sh_up;
   g2s.ksplit = pl.ks_sh_dn;
@@ -515,7 +517,7 @@ moe_status run_ffn(int act, int activation, int G, int D, int F, int max_rows, c
   // (only the shallow launches may use the contraction split's partial sums,
   // which the two launches of the side stream use one after the other)
   const bool concurrent = pl.split && side != nullptr && side->cus > 0 &&
-                          pl.cfg_sh >= kGemmV2Configs + kGemmV3Configs && pl.ks_up <= 1 && pl.ks_dn <= 1;
+                          pl.cfg_sh >= kGemmV3Configs && pl.ks_up <= 1 && pl.ks_dn <= 1;
   MOE_TRY(mark(ev, stage_up, 0, s));
   if (concurrent) {
     g1s.cus = side->cus;
@@ -566,11 +568,13 @@ moe_status run_ffn_part(int act, int activation, int G, int D, int F, int rows, 
 // How the shared experts run beside the routed path: 0 = after the routed
 // experts on the caller's stream; 1 = gate/up on the auxiliary stream during
 // routing, joined before the routed experts; 2 = both projections on the
-// auxiliary stream, joined before the combine.  MOE_SHARED_OVERLAP overrides
-// (tuning aid).
+// auxiliary stream from the start, joined before the combine; 3 = both on
+// the auxiliary stream from the end of the permutation (beside the routed
+// experts, leaving the routing kernels the whole chip), joined before the
+// combine.  MOE_SHARED_OVERLAP overrides (tuning aid).
 int shared_overlap() {
   const int v = tuning().shared_overlap;
-  return (v != kUnset && v >= 0 && v <= 2) ? v : 2;
+  return (v != kUnset && v >= 0 && v <= 3) ? v : 2;
 }
 
 // A library-owned stream per device for the layer's work that does not depend
@@ -978,7 +982,17 @@ static moe_status layer_forward_impl(const moe_config* cfg, const moe_weights* w
     aux_lock.lock();
     MOE_TRY(aux_stream(&aux));
   }
-  if (overlap > 0) {
+  auto fork_shared = [&]() -> moe_status {
+    MOE_TRY_HIP("fork", hipEventRecord(aux->fork, s));
+    MOE_TRY_HIP("fork", hipStreamWaitEvent(aux->s, aux->fork, 0));
+    MOE_TRY(run_ffn_part(cfg->act_dtype, SWIGLU, 1, D, SF, T, x, wt->ws13, wt->ws2, at<void>(ws, L.h_shared), y,
+                         at<float>(ws, L.kpart_shared), aux->s, ev, MOE_STAGE_SHARED_GATE_UP, true));
+    MOE_TRY(run_ffn_part(cfg->act_dtype, SWIGLU, 1, D, SF, T, x, wt->ws13, wt->ws2, at<void>(ws, L.h_shared), y,
+                         at<float>(ws, L.kpart_shared), aux->s, ev, MOE_STAGE_SHARED_DOWN, false));
+    MOE_TRY_HIP("join", hipEventRecord(aux->join, aux->s));
+    return MOE_OK;
+  };
+  if (overlap == 1 || overlap == 2) {
     MOE_TRY_HIP("fork", hipEventRecord(aux->fork, s));
     MOE_TRY_HIP("fork", hipStreamWaitEvent(aux->s, aux->fork, 0));
     MOE_TRY(run_ffn_part(cfg->act_dtype, SWIGLU, 1, D, SF, T, x, wt->ws13, wt->ws2, at<void>(ws, L.h_shared), y,
@@ -1028,6 +1042,7 @@ static moe_status layer_forward_impl(const moe_config* cfg, const moe_weights* w
   }
 
   if (overlap == 1) MOE_TRY_HIP("join", hipStreamWaitEvent(s, aux->join, 0));
+  if (overlap == 3) MOE_TRY(fork_shared());
 
   if (any) {
     void* h = at<void>(ws, L.h);
@@ -1041,10 +1056,10 @@ static moe_status layer_forward_impl(const moe_config* cfg, const moe_weights* w
     if (shared && overlap == 0)
       MOE_TRY(run_ffn_part(cfg->act_dtype, SWIGLU, 1, D, SF, T, x, wt->ws13, wt->ws2, at<void>(ws, L.h_shared), y,
                            at<float>(ws, L.kpart_shared), s, ev, MOE_STAGE_SHARED_GATE_UP, true));
-    if (shared && overlap != 2)
+    if (shared && overlap < 2)
       MOE_TRY(run_ffn_part(cfg->act_dtype, SWIGLU, 1, D, SF, T, x, wt->ws13, wt->ws2, at<void>(ws, L.h_shared), y,
                            at<float>(ws, L.kpart_shared), s, ev, MOE_STAGE_SHARED_DOWN, false));
-    if (overlap == 2) MOE_TRY_HIP("join", hipStreamWaitEvent(s, aux->join, 0));
+    if (overlap >= 2) MOE_TRY_HIP("join", hipStreamWaitEvent(s, aux->join, 0));
     const void* y_shared = shared ? y : nullptr;
     MOE_TRY(mark(ev, MOE_STAGE_COMBINE, 0, s));
     MOE_TRY_HIP("combine", launch_combine(yperm, row_of, w, y_shared, y, T, cfg->top_k, D, cfg->act_dtype, s));

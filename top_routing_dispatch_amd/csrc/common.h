@@ -74,6 +74,7 @@ struct Tuning {
   int gemm_tail = kUnset;        // MOE_GEMM_TAIL: 0 turns the last-round split off
   int shared_overlap = kUnset;   // MOE_SHARED_OVERLAP: 0 / 1 / 2
   int shallow_cus = kUnset;      // MOE_SHALLOW_CUS: CUs of the concurrent shallow-group launch (0 = in line)
+  int tile_gm = kUnset;          // MOE_TILE_GM: m-tiles per run of the grouped GEMMs' tile order
   int wgrad_tile = kUnset;       // MOE_WGRAD_TILE: 128 / 256
   int wgrad_swz = kUnset;        // MOE_WGRAD_SWZ: 0 / 1 / 2
 };
@@ -160,6 +161,8 @@ struct GroupedGemm {
   // Persistent launches: CUs the grid may occupy (0 = all of them), so that
   // a launch can run beside another one on the remaining CUs.
   int cus;
+  // m-tiles per run of the tile order that sweeps a group's n-tiles (0 = 8)
+  int tile_gm;
   // Split of the contraction (weight-streaming kernel only): with ksplit > 1
   // every tile runs as ksplit units over consecutive K / ksplit slices; each
   // unit writes its float32 sums to partial[(ks * M_max + row) * ldp + col]
@@ -203,7 +206,7 @@ __device__ __forceinline__ int ld_table(const int32_t* t, int i) {
 template <int BM, bool SCALAR = false>
 __device__ __forceinline__ void decode_tile(const GroupedGemm& p, int n_tiles, int L, int& g, int& row0, int& rows,
                                             int& nt) {
-  constexpr int GM = MOE_TILE_GM;
+  const int GM = p.tile_gm > 0 ? p.tile_gm : MOE_TILE_GM;
   if (p.offsets == nullptr) {
     const int mt_all = ceil_div(p.M_max, BM);
     const int sub = L / (GM * n_tiles);
@@ -282,24 +285,19 @@ hipError_t launch_tile_prefix_classes(const int32_t* offsets, int G, TilePrefixR
 // bf16 MFMA grouped GEMM; returns the BM its tiles use via bm_out when non-null.
 hipError_t launch_gemm_bf16(const GroupedGemm& g, hipStream_t s);
 int gemm_bf16_bm(const GroupedGemm& g);
-// Pipelined bf16 grouped GEMM (K % 64 == 0), tile configuration `cfg`.
-constexpr int kGemmV2Configs = 10;
-hipError_t launch_gemm_v2(const GroupedGemm& g, int cfg, hipStream_t s);
-int gemm_v2_bm(int cfg);
-// bf16 grouped GEMM with 128x128 wave tiles, one wave per SIMD (K % 32 == 0,
-// K % 64 == 0 for the 64-deep configuration).  Its tile configurations follow
-// the pipelined kernel's in one numbering: kGemmV2Configs + cfg.
+// bf16 grouped GEMM for deep groups (K % 64 == 0, or % 32 for the 32-deep
+// configurations): tile configurations 0 .. kGemmV3Configs-1.
 constexpr int kGemmV3Configs = 12;
 hipError_t launch_gemm_v3(const GroupedGemm& g, int cfg, hipStream_t s);
 int gemm_v3_bm(int cfg);
 // Persistent weight-streaming bf16 grouped GEMM for shallow groups (K % 64 ==
-// 0); its tile configurations follow in the same numbering:
-// kGemmV2Configs + kGemmV3Configs + cfg.
+// 0); its tile configurations follow in the same numbering: kGemmV3Configs +
+// cfg.
 constexpr int kGemmWsConfigs = 8;
 hipError_t launch_gemm_ws(const GroupedGemm& g, int cfg, hipStream_t s);
 int gemm_ws_bm(int cfg);
 int gemm_ws_bn(int cfg);
-constexpr int kGemmConfigs = kGemmV2Configs + kGemmV3Configs + kGemmWsConfigs;
+constexpr int kGemmConfigs = kGemmV3Configs + kGemmWsConfigs;
 // float32 SIMT grouped GEMM.  a_dtype / b_dtype select float32 or bf16 operands.
 hipError_t launch_gemm_f32(const GroupedGemm& g, int a_dtype, int b_dtype, hipStream_t s);
 constexpr int kF32GemmBM = 64;

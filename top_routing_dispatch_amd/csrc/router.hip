@@ -4,10 +4,10 @@
 // E <= 256 and D a multiple of 64 ("Top-k 路由" page, step 1 of the gate: one
 // bias-free linear layer).
 //
-// 65 <= E <= 256 and many tokens: one workgroup owns 32 tokens and every
-// expert, so each token row is read once and each token fragment feeds NP
-// MFMAs.  Operands stream through an LDS ring (up to 4 deep) of 64-deep K
-// slices (buffer loads with the LDS bit).
+// 65 <= E <= 256 and many tokens: one workgroup owns a block of BM tokens and
+// BN experts (router_shape picks the block that moves the fewest bytes per
+// CU; every token fragment feeds NP MFMAs).  Operands stream through an LDS
+// ring (up to 4 deep) of 64-deep K slices (buffer loads with the LDS bit).
 // At most 16 tokens (rows fitting in LDS): one wave per expert
 // (router_gemv_kernel below).
 // E <= 64, or few tokens: one workgroup owns 16 tokens and up to 64 experts
@@ -43,30 +43,37 @@ __device__ __forceinline__ void wait_vm_r() {
 // 128-byte rows (64 bf16), chunk c of row r in slot c ^ ((r >> 1) & 7).
 __device__ __forceinline__ int swz_r(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
 
-template <int BN, int NP>
+// A workgroup owns BM tokens and BN experts (the grid's y dimension runs over
+// blocks of BN experts); its four waves are laid out WGM x WGN over them, each
+// owning 32 tokens and BN / WGN experts.
+template <int BM, int BN, int NP>
 struct RCfg {
-  static constexpr int BM = 32;                       // tokens per workgroup
+  static constexpr int WGM = BM / 32, WGN = 4 / WGM;  // wave layout
   static constexpr int XB = BM * 128, WB = NP * BN * 128;  // bytes per slice
   static constexpr int STAGE = XB + WB;
   static constexpr int NST = (160 * 1024) / STAGE < 4 ? (160 * 1024) / STAGE : 4;
   static constexpr int X_INS = XB / 1024 / 4, W_INS = WB / 1024 / 4;   // per wave per slice
   static constexpr int INS = X_INS + W_INS;
-  static constexpr int TN = BN / 4 / 32;              // 32-column blocks per wave
+  static constexpr int WN = BN / WGN;                 // experts per wave
+  static constexpr int TN = WN / 32;                  // 32-column blocks per wave
+  static_assert(WGM >= 1 && WGM * WGN == 4 && BM == 32 * WGM, "wave layout");
   static_assert(XB % 4096 == 0 && WB % 4096 == 0, "load split");
-  static_assert(TN >= 1, "wave tile");
+  static_assert(TN >= 1 && WN % 32 == 0, "wave tile");
   static_assert(NST >= 2 && STAGE * NST <= 160 * 1024, "LDS");
   static_assert(INS * (NST - 2) <= 63, "vmcnt range");
 };
 
-template <int BN, int NP>
+template <int BM, int BN, int NP>
 __global__ __launch_bounds__(256) void router_logits_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ w,
                                                             float* __restrict__ logits, int T, int E, int D) {
-  using C = RCfg<BN, NP>;
+  using C = RCfg<BM, BN, NP>;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int row0 = blockIdx.x * C::BM;
-  const int rows = min(C::BM, T - row0);
+  const int wm = wave / C::WGN, wn = wave % C::WGN;
+  const int row0 = blockIdx.x * BM;
+  const int rows = min(BM, T - row0);
+  const int e0 = blockIdx.y * BN;
   const int nk = D / 64;
 
   const __amdgpu_buffer_rsrc_t x_rsrc =
@@ -86,7 +93,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const bf16_t* __rest
   for (int q = 0; q < C::W_INS; ++q) {
     const int r = (wave * C::W_INS + q) * 8 + (lane >> 3);     // LDS row: plane r / BN, expert r % BN
     const int c = (lane & 7) ^ ((r >> 1) & 7);
-    const unsigned e = (unsigned)min(r % BN, E - 1), pl = (unsigned)(r / BN);
+    const unsigned e = (unsigned)min(e0 + r % BN, E - 1), pl = (unsigned)(r / BN);
     w_off[q] = ((e * NP + pl) * (unsigned)D + c * 8) * 2u;
   }
   auto issue = [&](int kt) __attribute__((always_inline)) {
@@ -118,10 +125,10 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const bf16_t* __rest
     const char* sw = sx + C::XB;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(sx + swz_r(fr, kk * 2 + fh));
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(sx + swz_r(wm * 32 + fr, kk * 2 + fh));
 #pragma unroll
       for (int j = 0; j < C::TN; ++j) {
-        const int r = wave * (BN / 4) + j * 32 + fr;
+        const int r = wn * C::WN + j * 32 + fr;
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
           const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(sw + swz_r(p * BN + r, kk * 2 + fh));
@@ -138,32 +145,77 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const bf16_t* __rest
   // lane holds column (lane & 31) and rows 8*(r/4) + 4*(lane/32) + (r%4)
 #pragma unroll
   for (int j = 0; j < C::TN; ++j) {
-    const int e = wave * (BN / 4) + j * 32 + fr;
+    const int e = e0 + wn * C::WN + j * 32 + fr;
     if (e >= E) continue;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int rl = 8 * (r >> 2) + 4 * fh + (r & 3);
+      const int rl = wm * 32 + 8 * (r >> 2) + 4 * fh + (r & 3);
       if (rl < rows) logits[(long long)(row0 + rl) * E + e] = (float)dacc[j][r];
     }
   }
 }
 
-template <int BN, int NP>
+template <int BM, int BN, int NP>
 hipError_t launch_router_cfg(const bf16_t* x, const bf16_t* w, float* logits, int T, int E, int D, hipStream_t s) {
-  using C = RCfg<BN, NP>;
+  using C = RCfg<BM, BN, NP>;
   static std::atomic<bool> allowed[64];   // per device: attribute set (host threads may race)
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64 || !allowed[dev].load(std::memory_order_relaxed)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&router_logits_kernel<BN, NP>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&router_logits_kernel<BM, BN, NP>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, C::STAGE * C::NST);
     if (e != hipSuccess) return e;
     if (dev >= 0 && dev < 64) allowed[dev].store(true, std::memory_order_relaxed);
   }
-  hipLaunchKernelGGL((router_logits_kernel<BN, NP>), dim3(ceil_div(T, C::BM)), dim3(256), C::STAGE * C::NST, s, x, w,
-                     logits, T, E, D);
+  hipLaunchKernelGGL((router_logits_kernel<BM, BN, NP>), dim3(ceil_div(T, BM), ceil_div(E, BN)), dim3(256),
+                     C::STAGE * C::NST, s, x, w, logits, T, E, D);
   return hipGetLastError();
+}
+
+// Block shape of the tiled router kernel.  Every workgroup streams its BM
+// token rows and its BN experts' weight rows (NP planes) through LDS once;
+// with one workgroup per CU in flight, the time goes with the rounds of
+// workgroups times the bytes one workgroup moves from L2, so the shape with
+// the fewest (rounds x (BM + NP BN)) is taken (ties: more workgroups).
+// Measured on MI355X at the DeepSeek-V3 shape (8192 tokens, 256 experts,
+// D = 7168): 32 x 256 blocks (every workgroup re-reading all of W_g)
+// 89-116 us.
+struct RouterShape { int bm, bn; };
+RouterShape router_shape(int T, int E, int NP) {
+  static const RouterShape cand1[] = {{32, 256}, {32, 128}, {64, 128}, {64, 64}, {128, 64}};
+  static const RouterShape cand3[] = {{32, 128}, {64, 64}};
+  const RouterShape* c = NP == 1 ? cand1 : cand3;
+  const int n = NP == 1 ? 5 : 2;
+  const int cus = num_cus();
+  RouterShape best{0, 0};
+  long long best_cost = 0, best_wgs = 0;
+  for (int i = 0; i < n; ++i) {
+    if (NP == 1 && c[i].bn > 128 && E <= 128) continue;      // blocks wider than the experts
+    const long long wgs = (long long)ceil_div(T, c[i].bm) * ceil_div(E, c[i].bn);
+    const long long cost = ((wgs + cus - 1) / cus) * (c[i].bm + (long long)NP * c[i].bn);
+    if (best.bm == 0 || cost < best_cost || (cost == best_cost && wgs > best_wgs)) {
+      best = c[i];
+      best_cost = cost;
+      best_wgs = wgs;
+    }
+  }
+  return best;
+}
+
+template <int NP>
+hipError_t launch_router_tiled(const bf16_t* x, const bf16_t* w, float* logits, int T, int E, int D, hipStream_t s) {
+  const RouterShape sh = router_shape(T, E, NP);
+  if constexpr (NP == 1) {
+    if (sh.bm == 32 && sh.bn == 256) return launch_router_cfg<32, 256, 1>(x, w, logits, T, E, D, s);
+    if (sh.bm == 32 && sh.bn == 128) return launch_router_cfg<32, 128, 1>(x, w, logits, T, E, D, s);
+    if (sh.bm == 64 && sh.bn == 128) return launch_router_cfg<64, 128, 1>(x, w, logits, T, E, D, s);
+    if (sh.bm == 64 && sh.bn == 64) return launch_router_cfg<64, 64, 1>(x, w, logits, T, E, D, s);
+    return launch_router_cfg<128, 64, 1>(x, w, logits, T, E, D, s);
+  } else {
+    if (sh.bm == 32) return launch_router_cfg<32, 128, 3>(x, w, logits, T, E, D, s);
+    return launch_router_cfg<64, 64, 3>(x, w, logits, T, E, D, s);
+  }
 }
 
 template <int NB, int NP, int U>
@@ -412,9 +464,8 @@ hipError_t launch_router_logits(const bf16_t* x, const bf16_t* w, int planes, fl
     if (planes == 3) return launch_router_small<1, 3>(x, w, logits, T, E, D, s);
     return launch_router_small<1, 1>(x, w, logits, T, E, D, s);
   }
-  if (planes == 3) return launch_router_cfg<128, 3>(x, w, logits, T, E, D, s);
-  if (E <= 128) return launch_router_cfg<128, 1>(x, w, logits, T, E, D, s);
-  return launch_router_cfg<256, 1>(x, w, logits, T, E, D, s);
+  if (planes == 3) return launch_router_tiled<3>(x, w, logits, T, E, D, s);
+  return launch_router_tiled<1>(x, w, logits, T, E, D, s);
 }
 
 }  // namespace moe

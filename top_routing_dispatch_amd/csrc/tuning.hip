@@ -41,6 +41,7 @@ void read_env() {
   t.gemm_tail = env_int("MOE_GEMM_TAIL");
   t.shared_overlap = env_int("MOE_SHARED_OVERLAP");
   t.shallow_cus = env_int("MOE_SHALLOW_CUS");
+  t.tile_gm = env_int("MOE_TILE_GM");
   t.wgrad_tile = env_int("MOE_WGRAD_TILE");
   t.wgrad_swz = env_int("MOE_WGRAD_SWZ");
   std::lock_guard<std::mutex> lock(g_tuning_mu);
