@@ -91,6 +91,14 @@ def stage_work(cfg, stage, A, E_act, T):
         return 0.0, A * D * b + T * k * 8 + (T * D * b if SF else 0) + T * D * b
     if stage == "load_stats":
         return 0.0, T * E * 4 + E * 4
+    if stage == "fused_layer":
+        # x and the weights read once (routed experts with rows only), y and
+        # the routing outputs written: what the one-workgroup layer must move
+        parts = ("router_logits", "expert_ffn") + (("shared_gate_up", "shared_down") if SF else ())
+        fl = sum(stage_work(cfg, p, A, E_act, T)[0] for p in parts)
+        by = (T * D * b + E * D * br + E_act * (nm + 1) * F * D * b + 3 * SF * D * b + T * D * b
+              + T * k * 8 + E * 4 + (2 * E + 2) * 4)
+        return fl, by
     raise KeyError(stage)
 
 
@@ -141,6 +149,8 @@ def targets_of(cfg, stage_ms, A, E_act, T):
         ms = stage_ms["expert_ffn"]
         out["expert_gemm_ms"] = round(ms, 4)
         out["expert_gemm_mfma_frac"] = round(fl / (ms * 1e-3) / 1e12 / MFMA_BF16_TFLOPS, 4)
+    if "fused_layer" in stage_ms:
+        out["fused_layer_us"] = round(stage_ms["fused_layer"] * 1e3, 2)
     return out
 
 
@@ -377,14 +387,18 @@ def main():
         M.moe_layer_forward_timed(cfg, weights, x, y, idx, tw, counts, cfg.alpha, stats, dropped, ws,
                                   stage_events=evs)
 
+    # stages that run (the others' events only hold their creation-time records)
+    ran = set(M.STAGES) - {"permute", "load_stats", "fused_layer"} if ec else set(M.moe_layer_stages(cfg))
+    if ec and cfg.num_shared == 0:
+        ran -= {"shared_gate_up", "shared_down"}
+    log(f"[bench] stages: {' '.join(s for s in M.STAGES if s in ran)}")
+
     def stage_times(events, stages):
         out = {}
         for si in stages:
             name = M.STAGES[si]
-            if name.startswith("shared") and cfg.num_shared == 0:
-                continue        # no kernels: the events only hold their creation-time records
-            if ec and name in ("permute", "load_stats"):
-                continue        # not stages of the expert-choice layer
+            if name not in ran:
+                continue
             vals = [evs[2 * si].elapsed_time(evs[2 * si + 1]) for evs in events]
             if vals and max(vals) > 0:
                 out[name] = float(np.mean(vals))

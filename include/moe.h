@@ -286,8 +286,26 @@ typedef enum {
   MOE_STAGE_SHARED_DOWN = 6,
   MOE_STAGE_COMBINE = 7,
   MOE_STAGE_LOAD_STATS = 8,
-  MOE_NUM_STAGES = 9
+  MOE_STAGE_FUSED_LAYER = 9,     /* every step above in one kernel (small batches) */
+  MOE_NUM_STAGES = 10
 } moe_stage;
+
+/* Which stages moe_layer_forward runs for `cfg` in a call that asks for
+ * every output: runs[s] = 1 or 0 for s < MOE_NUM_STAGES (host array).
+ * Host-side only: no device is touched.  A small batch runs
+ * MOE_STAGE_FUSED_LAYER alone: route, dispatch, experts, combine and
+ * statistics in one launch of one workgroup per token, in which every
+ * workgroup routes the whole batch and then runs its own token through its
+ * experts.  Each step is defined as on the staged path (the logits and the
+ * selection in double precision, the expert sums in float32 from the stored
+ * values, the activations kept in float32 between the two projections).  It
+ * runs when the batch fits (T <= 256, E <= 64, k <= 8; x, W_g, the float64
+ * logits and the token's buffers within 63 KB of LDS) and the work of one
+ * workgroup is small: T*E*D <= 262144 router multiply-adds and at most
+ * 1048576 for the token's routed and shared experts.  The environment variable MOE_FUSED, read like the
+ * other tuning variables (moe_reload_tuning), overrides the choice: 1 fuses
+ * every batch that fits, 0 none. */
+moe_status moe_layer_stages(const moe_config* cfg, int32_t* runs);
 
 /* moe_layer_forward with stage timing: identical work, and for every stage s
  * that runs, hipEventRecord(stage_events[2s], <its stream>) before its kernels

@@ -211,3 +211,34 @@ def test_oversized_operands_rejected_before_launch():
     wide = W.MoEConfig("wide", 300000, 7168, 8, 1, 64)
     with pytest.raises(M.MoEError):
         M.moe_workspace_size(wide, M.MOE_OP_ROUTE)
+
+
+def test_layer_stages_pick_the_one_workgroup_kernel_for_small_batches(monkeypatch):
+    """moe_layer_stages is host-side: the fused kernel for batches with little
+    work, the staged kernels otherwise, MOE_FUSED overriding the choice where
+    the batch fits one workgroup."""
+    staged = ["router_logits", "route_select", "permute", "expert_gate_up", "expert_down", "combine",
+              "load_stats"]
+    assert M.moe_layer_stages(W.TINY) == ["fused_layer"]
+    assert M.moe_layer_stages(W.MIXTRAL) == staged
+    assert M.moe_layer_stages(W.DEEPSEEKV3) == staged[:5] + ["shared_gate_up", "shared_down"] + staged[5:]
+    assert M.moe_layer_stages(W.TINY.replace(num_tokens=0)) == ["permute", "load_stats"]
+    wide = W.MoEConfig("wide", 16, 512, 8, 2, 512)
+    assert "fused_layer" not in M.moe_layer_stages(wide)            # fits, but too much work for one CU
+    too_big = [W.TINY.replace(num_tokens=257), W.TINY.replace(num_experts=65, top_k=2),
+               W.MoEConfig("k9", 16, 32, 16, 9, 16), W.TINY.replace(d_ff=8192),
+               W.TINY.replace(num_tokens=256, num_experts=64)]   # the last two past the LDS
+    try:
+        monkeypatch.setenv("MOE_FUSED", "1")
+        M.moe_reload_tuning()
+        assert M.moe_layer_stages(wide) == ["fused_layer"]
+        for c in too_big:
+            assert "fused_layer" not in M.moe_layer_stages(c), c
+        monkeypatch.setenv("MOE_FUSED", "0")
+        M.moe_reload_tuning()
+        assert M.moe_layer_stages(W.TINY) == staged
+    finally:
+        monkeypatch.delenv("MOE_FUSED")
+        M.moe_reload_tuning()
+    with pytest.raises(M.MoEError):
+        M.moe_layer_stages(W.TINY.replace(top_k=5))

@@ -41,15 +41,70 @@ EDGE = [
 ]
 
 
+@pytest.mark.parametrize("path", ["default", "staged"])
 @pytest.mark.parametrize("cfg", SMALL + EDGE, ids=lambda c: c.name)
-def test_layer_forward_matches_oracle(cfg):
-    print(f"[layer parity] {cfg.name}", flush=True)
+def test_layer_forward_matches_oracle(cfg, path, monkeypatch):
+    """Every configuration on the path the library picks (the one-workgroup
+    kernel for the smallest batches) and on the staged kernels."""
+    if path == "staged":
+        set_env(monkeypatch, "MOE_FUSED", "0")
+    stages = M.moe_layer_stages(cfg)
+    print(f"[layer parity] {cfg.name} {path}: {' '.join(stages)}", flush=True)
+    assert ("fused_layer" in stages) == (path == "default" and cfg.name in FUSED_BY_DEFAULT)
     inp = W.make_inputs(cfg)
     ref = oracle_forward(cfg, inp)
     dl = DeviceLayer(cfg, inp)
     got = dl.layer()
     diff, err = check_layer(cfg, inp, ref, got)
     print(f"  max rel err {err:.3e}, near-tie tokens {len(diff)}")
+
+
+# Batches that fit one workgroup, over the scoring rules, both activations,
+# both element types, capacity drops and shared experts, up to the largest
+# batch the fused kernel takes.
+FUSED_SHAPES = [
+    W.MoEConfig("fused_sigmoid_bias_shared", 64, 128, 16, 4, 64, num_shared=2, d_ff_shared=32,
+                scoring=W.SIGMOID_BIAS, renormalize=1, zipf_s=1.2),
+    W.MoEConfig("fused_topk_softmax_capacity", 96, 64, 8, 2, 80, scoring=W.TOPK_SOFTMAX, capacity_factor=0.75,
+                zipf_s=1.0),
+    W.MoEConfig("fused_f32_gelu_shared_capacity", 48, 96, 12, 3, 64, num_shared=3, d_ff_shared=16,
+                activation=W.GELU, act_dtype=W.F32, router_dtype=W.F32, capacity_factor=0.8),
+    W.MoEConfig("fused_switch_top1", 128, 64, 16, 1, 96, renormalize=0, activation=W.GELU, router_dtype=W.F32,
+                capacity_factor=1.25),
+    W.MoEConfig("fused_sigmoid_unnormalised_f32", 33, 40, 64, 6, 24, scoring=W.SIGMOID_BIAS, renormalize=0,
+                act_dtype=W.F32, router_dtype=W.F32),
+    W.MoEConfig("fused_k_equals_e", 40, 32, 4, 4, 16, act_dtype=W.F32, router_dtype=W.F32),
+    W.MoEConfig("fused_most_tokens", 256, 32, 8, 2, 48, num_shared=1, d_ff_shared=32, capacity_factor=1.0),
+    W.MoEConfig("fused_most_experts", 64, 32, 64, 6, 32, scoring=W.SIGMOID_BIAS, renormalize=1, zipf_s=1.2),
+]
+FUSED_BY_DEFAULT = {"tiny", "one_token", "one_expert", "k_equals_e_soft", "mostly_empty_experts"}
+
+
+@pytest.mark.parametrize("cfg", FUSED_SHAPES, ids=lambda c: c.name)
+def test_fused_layer_matches_oracle_and_staged_path(cfg, monkeypatch):
+    """The one-workgroup layer against the oracle, and its routing decisions
+    and statistics against the staged path's (selections equal away from
+    near ties, counts and drops equal where the selections are).  MOE_FUSED=1
+    takes the one-workgroup kernel for every batch that fits, also where the
+    staged path is faster."""
+    set_env(monkeypatch, "MOE_FUSED", "1")
+    assert M.moe_layer_stages(cfg) == ["fused_layer"]
+    print(f"[fused layer] {cfg.name}", flush=True)
+    inp = W.make_inputs(cfg)
+    ref = oracle_forward(cfg, inp)
+    dl = DeviceLayer(cfg, inp)
+    fused = dl.layer()
+    diff, err = check_layer(cfg, inp, ref, fused)
+    print(f"  fused: max rel err {err:.3e}, near-tie tokens {len(diff)}")
+    set_env(monkeypatch, "MOE_FUSED", "0")
+    assert "fused_layer" not in M.moe_layer_stages(cfg)
+    staged = dl.layer()
+    check_layer(cfg, inp, ref, staged)
+    if (fused["idx"] == staged["idx"]).all():
+        np.testing.assert_array_equal(fused["counts"], staged["counts"])
+        assert fused["dropped"] == staged["dropped"]
+        assert rel_err(fused["w"], staged["w"]) <= W_TOL
+        assert row_rel_err(fused["y"], O.widen(staged["y"])) <= 2 * out_tol(cfg)
 
 
 @pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
@@ -550,6 +605,8 @@ GRAPH_SHAPES = [
     W.MoEConfig("graph_gelu_capacity", 900, 192, 16, 1, 384, scoring=W.SOFTMAX_TOPK, renormalize=0,
                 activation=W.GELU, router_dtype=W.F32, capacity_factor=1.25),
     W.MoEConfig("graph_swiglu_shared", 700, 256, 8, 2, 320, num_shared=1, d_ff_shared=128),
+    # the one-workgroup kernel
+    W.TINY,
 ]
 
 

@@ -28,10 +28,10 @@ MOE_SWIGLU, MOE_GELU = 0, 1
 EXPORTED = ("moe_capacity", "moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn",
             "moe_combine", "moe_load_stats", "moe_layer_forward", "moe_layer_forward_timed", "moe_layer_forward_static",
             "moe_layer_backward", "moe_expert_choice_capacity", "moe_expert_choice_forward", "moe_ep_send_layout",
-            "moe_ep_recv_layout",
+            "moe_ep_recv_layout", "moe_layer_stages",
             "moe_reload_tuning", "moe_status_string", "moe_last_error")
 STAGES = ("router_logits", "route_select", "permute", "expert_gate_up", "expert_down", "shared_gate_up",
-          "shared_down", "combine", "load_stats")
+          "shared_down", "combine", "load_stats", "fused_layer")
 
 
 class moe_config(ctypes.Structure):
@@ -89,6 +89,7 @@ def lib() -> ctypes.CDLL:
                                           ctypes.POINTER(vp)],
             "moe_ep_send_layout": [i32, i32, vp, vp, vp, vp],
             "moe_ep_recv_layout": [i32, i32, vp, i32, vp, vp, vp],
+            "moe_layer_stages": [cfgp, ctypes.POINTER(i32)],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -204,6 +205,15 @@ def moe_capacity(cfg):
     cap, rows = ctypes.c_int32(), ctypes.c_int32()
     _check("moe_capacity", lib().moe_capacity(ctypes.byref(c), ctypes.byref(cap), ctypes.byref(rows)))
     return cap.value, rows.value
+
+
+def moe_layer_stages(cfg):
+    """Names of the stages moe_layer_forward runs for `cfg` (every output asked
+    for): the staged kernels, or "fused_layer" alone for small batches."""
+    c = make_config(cfg)
+    runs = (ctypes.c_int32 * len(STAGES))()
+    _check("moe_layer_stages", lib().moe_layer_stages(ctypes.byref(c), runs))
+    return [name for name, r in zip(STAGES, runs) if r]
 
 
 def moe_workspace_size(cfg, op: int) -> int:

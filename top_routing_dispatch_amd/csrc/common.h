@@ -77,6 +77,7 @@ struct Tuning {
   int tile_gm = kUnset;          // MOE_TILE_GM: m-tiles per run of the grouped GEMMs' tile order
   int wgrad_tile = kUnset;       // MOE_WGRAD_TILE: 128 / 256
   int wgrad_swz = kUnset;        // MOE_WGRAD_SWZ: 0 / 1 / 2
+  int fused = kUnset;            // MOE_FUSED: 1 / 0 one-workgroup layer for every / no batch that fits
 };
 Tuning tuning();
 
@@ -404,5 +405,28 @@ struct StatsArgs {
 };
 constexpr int kStatsChunk = 64;     // tokens per partial-sum block (multiple of 4)
 hipError_t launch_load_stats(const StatsArgs& a, hipStream_t s);
+
+// Whole layer forward in one workgroup for small batches (fused.hip).
+struct FusedArgs {
+  const void* x;              // [T, D] act dtype
+  const void* w_router;       // [E, D] router dtype
+  const float* sel_bias;      // [E] or nullptr
+  const void* w13;            // [E, 2F or F, D]
+  const void* w2;             // [E, D, F]
+  const void* ws13;           // [2 SF, D] or nullptr
+  const void* ws2;            // [D, SF]
+  void* y;                    // [T, D] act dtype out
+  int32_t* topk_idx;          // [T, k] or nullptr
+  float* topk_w;              // [T, k] or nullptr
+  int32_t* counts;            // [E] or nullptr
+  float* stats;               // [2E + 2] or nullptr
+  int32_t* dropped;           // [1] or nullptr
+  int T, D, E, k, F, SF;      // SF = S * F_s (0 = no shared experts)
+  int scoring, renormalize, activation, capacity;
+  float alpha;
+};
+constexpr int kFusedMaxTokens = 256;
+bool fused_layer_fits(int act_dtype, int T, int D, int E, int k, int F, int SF);
+hipError_t launch_fused_layer(const FusedArgs& a, int act_dtype, int router_dtype, hipStream_t s);
 
 }  // namespace moe

@@ -44,6 +44,7 @@ void read_env() {
   t.tile_gm = env_int("MOE_TILE_GM");
   t.wgrad_tile = env_int("MOE_WGRAD_TILE");
   t.wgrad_swz = env_int("MOE_WGRAD_SWZ");
+  t.fused = env_int("MOE_FUSED");
   std::lock_guard<std::mutex> lock(g_tuning_mu);
   g_tuning = t;
 }
