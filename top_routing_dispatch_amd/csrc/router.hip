@@ -22,6 +22,7 @@
 // requires.
 #include "common.h"
 
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 
@@ -174,13 +175,14 @@ hipError_t launch_router_cfg(const bf16_t* x, const bf16_t* w, float* logits, in
 }
 
 // Block shape of the tiled router kernel.  Every workgroup streams its BM
-// token rows and its BN experts' weight rows (NP planes) through LDS once;
-// with one workgroup per CU in flight, the time goes with the rounds of
-// workgroups times the bytes one workgroup moves from L2, so the shape with
-// the fewest (rounds x (BM + NP BN)) is taken (ties: more workgroups).
-// Measured on MI355X at the DeepSeek-V3 shape (8192 tokens, 256 experts,
-// D = 7168): 32 x 256 blocks (every workgroup re-reading all of W_g)
-// 89-116 us.
+// token rows and its BN experts' weight rows (NP planes) through LDS once.
+// A shape whose LDS ring leaves room for a second workgroup on the CU runs
+// two at a time, one's float64 additions and waits beside the other's
+// MFMAs, so the time goes with the rounds of workgroups per CU slot times
+// the bytes one workgroup moves (ties: more workgroups).  Measured on
+// MI355X at the DeepSeek-V3 shape (8192 tokens, 256 experts, D = 7168):
+// 64 x 64 blocks, two per CU, 58-62 us; 64 x 128 and 128 x 64, one per CU,
+// 74-82 us; 32 x 256 (every workgroup re-reading all of W_g) 80-116 us.
 struct RouterShape { int bm, bn; };
 RouterShape router_shape(int T, int E, int NP) {
   static const RouterShape cand1[] = {{32, 256}, {32, 128}, {64, 128}, {64, 64}, {128, 64}};
@@ -192,8 +194,12 @@ RouterShape router_shape(int T, int E, int NP) {
   long long best_cost = 0, best_wgs = 0;
   for (int i = 0; i < n; ++i) {
     if (NP == 1 && c[i].bn > 128 && E <= 128) continue;      // blocks wider than the experts
+    const int stage = (c[i].bm + NP * c[i].bn) * 128;        // the ring of RCfg
+    const int nst = std::min(4, (160 * 1024) / stage);
+    const int slots = std::min(2, (160 * 1024) / (stage * nst));
     const long long wgs = (long long)ceil_div(T, c[i].bm) * ceil_div(E, c[i].bn);
-    const long long cost = ((wgs + cus - 1) / cus) * (c[i].bm + (long long)NP * c[i].bn);
+    const long long cost = ((wgs + (long long)cus * slots - 1) / ((long long)cus * slots)) *
+                           (c[i].bm + (long long)NP * c[i].bn);
     if (best.bm == 0 || cost < best_cost || (cost == best_cost && wgs > best_wgs)) {
       best = c[i];
       best_cost = cost;
