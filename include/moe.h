@@ -61,7 +61,8 @@ typedef enum {
   MOE_ERR_INVALID_ARGUMENT = 1,   /* null required pointer, bad size, misalignment */
   MOE_ERR_UNSUPPORTED = 2,        /* valid but not implemented combination */
   MOE_ERR_WORKSPACE_TOO_SMALL = 3,
-  MOE_ERR_HIP = 4                 /* a HIP launch or API call failed */
+  MOE_ERR_HIP = 4,                /* a HIP launch or API call failed */
+  MOE_ERR_DEBUG_CHECK = 5         /* MOE_DEBUG=1: a table failed its host-side check */
 } moe_status;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
@@ -267,6 +268,27 @@ moe_status moe_layer_forward_static(const moe_config* cfg, const moe_weights* we
                                     const void* x, void* y, int32_t* topk_idx, float* topk_w,
                                     int32_t* counts, float alpha, float* stats, int32_t* dropped,
                                     void* stream);
+
+/* Debug checks.  With the environment variable MOE_DEBUG=1 (read like the
+ * tuning variables) the library copies the integer tables an entry point
+ * reads or writes to the host, synchronising `stream`, and checks them
+ * before it goes on; a table that breaks its definition fails the call with
+ * MOE_ERR_DEBUG_CHECK and moe_last_error() names the first bad entry:
+ *   moe_expert_ffn: offsets non-decreasing from >= 0 to <= max_rows, and
+ *                   gather_rows[r] >= 0 for the rows the groups cover (before
+ *                   any launch);
+ *   moe_combine:    row_of in [-1, A_cap) (before any launch);
+ *   moe_permute and the staged moe_layer_forward: counts, offsets, row_of
+ *                   and token_of_row against the dispatch of topk_idx
+ *                   ("从 Dense FFN 到 MoE" §5 batches, "Top-k 路由" 容量因子),
+ *                   after the permutation.
+ * Calls that synchronise cannot be captured in a HIP graph.
+ *
+ * moe_check_dispatch runs that dispatch check on HOST arrays (shapes as in
+ * moe_permute): MOE_OK, or MOE_ERR_DEBUG_CHECK with the first difference in
+ * moe_last_error().  For tools and tests; touches no device. */
+moe_status moe_check_dispatch(const moe_config* cfg, const int32_t* topk_idx, const int32_t* counts,
+                              const int32_t* offsets, const int32_t* row_of, const int32_t* token_of_row);
 
 /* Re-reads the MOE_* tuning variables of the environment (tuning aids that
  * force a kernel choice: MOE_GEMM_CFG, MOE_GEMM_SPLIT, MOE_ROUTER_PATH, ...).

@@ -954,3 +954,68 @@ def test_weight_gradient_variants_identical(cfg):
         got = run(env)
         for n in base:
             assert np.array_equal(got[n].view(np.uint8), base[n].view(np.uint8)), f"{env}: {n} differs"
+
+
+# --------------------------------------------------------------------------
+# MOE_DEBUG: host-side checks of the dispatch tables
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg", [SMALL[1], SMALL[3], SMALL[5], EDGE[5]], ids=lambda c: c.name)
+def test_debug_checks_pass_on_the_staged_path(cfg, monkeypatch):
+    """With MOE_DEBUG=1 the staged layer and moe_permute check their tables
+    on the host and still return the oracle's results."""
+    set_env(monkeypatch, "MOE_DEBUG", "1")
+    set_env(monkeypatch, "MOE_FUSED", "0")
+    print(f"[debug checks] {cfg.name}", flush=True)
+    inp = W.make_inputs(cfg)
+    ref = oracle_forward(cfg, inp)
+    dl = DeviceLayer(cfg, inp)
+    check_layer(cfg, inp, ref, dl.layer())
+    T, k, E = cfg.num_tokens, cfg.top_k, cfg.num_experts
+    cap, rows_cap = M.moe_capacity(cfg)
+    idx = to_torch(ref["idx"].astype(np.int32), "cuda")
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    row_of = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    tor = torch.empty(rows_cap, dtype=torch.int32, device="cuda")
+    ws = M.workspace(cfg, M.MOE_OP_PERMUTE, "cuda")
+    M.moe_permute(cfg, idx, None, counts, offsets, row_of, tor, None, ws)
+    torch.cuda.synchronize()
+
+
+def test_debug_checks_reject_bad_tables_before_launch(monkeypatch):
+    """MOE_DEBUG=1 turns caller tables out of range into MOE_ERR_DEBUG_CHECK
+    before any launch.  Every buffer has room for the bad rows as well, so
+    the call stays within its memory even if a check did not fire."""
+    set_env(monkeypatch, "MOE_DEBUG", "1")
+    cfg = W.MoEConfig("debug_tables", 64, 64, 4, 2, 32)
+    dev = "cuda"
+    G, F, D, rows, slack = 4, 32, 64, 128, 64
+    x = torch.zeros(((rows + slack) * D,), dtype=torch.bfloat16, device=dev)
+    y = torch.zeros(((rows + slack) * D,), dtype=torch.bfloat16, device=dev)
+    w13 = torch.zeros((G * 2 * F * D,), dtype=torch.bfloat16, device=dev)
+    w2 = torch.zeros((G * D * F,), dtype=torch.bfloat16, device=dev)
+    need = M.moe_workspace_size(cfg.replace(num_tokens=(rows + slack) * 2), M.MOE_OP_EXPERT_FFN)
+    ws = torch.empty(4 * need + (1 << 20), dtype=torch.uint8, device=dev)
+    good = torch.tensor([0, 32, 64, 96, rows], dtype=torch.int32, device=dev)
+    M.moe_expert_ffn(cfg, G, F, M.MOE_SWIGLU, rows, x, None, good, w13, w2, y, ws)
+    torch.cuda.synchronize()
+    past = torch.tensor([0, 32, 64, 96, rows + 16], dtype=torch.int32, device=dev)
+    with pytest.raises(M.MoEError, match="exceeds max_rows") as e:
+        M.moe_expert_ffn(cfg, G, F, M.MOE_SWIGLU, rows, x, None, past, w13, w2, y, ws)
+    assert e.value.status == M.MOE_ERR_DEBUG_CHECK
+    gather = torch.zeros(rows + slack, dtype=torch.int32, device=dev)
+    gather[5] = -1
+    x_after_one_row = x.view(rows + slack, D)[1:].reshape(-1)   # row -1 of it is still x's first row
+    with pytest.raises(M.MoEError, match=r"gather_rows\[5\]"):
+        M.moe_expert_ffn(cfg, G, F, M.MOE_SWIGLU, rows, x_after_one_row, gather, good, w13, w2, y, ws)
+    T, k = cfg.num_tokens, cfg.top_k
+    _, rows_cap = M.moe_capacity(cfg)
+    y_perm = torch.zeros(((rows_cap + slack) * D,), dtype=torch.bfloat16, device=dev)
+    row_of = torch.arange(T * k, dtype=torch.int32, device=dev).reshape(T, k)
+    row_of[7, 1] = rows_cap + 3
+    tw = torch.full((T, k), 0.5, dtype=torch.float32, device=dev)
+    out = torch.zeros((T, D), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(M.MoEError, match=r"row_of\[15\]") as e:
+        M.moe_combine(cfg, y_perm, row_of, tw, None, out)
+    assert e.value.status == M.MOE_ERR_DEBUG_CHECK
+    torch.cuda.synchronize()

@@ -18,7 +18,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 # (a tuning variant)
 LIB_PATH = os.environ.get("MOE_LIB_PATH") or os.path.join(_PKG, "libmoe_hip.so")
 
-MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP = range(5)
+(MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP,
+ MOE_ERR_DEBUG_CHECK) = range(6)
 MOE_F32, MOE_BF16 = 0, 1
 MOE_SOFTMAX_TOPK, MOE_TOPK_SOFTMAX, MOE_SIGMOID_BIAS = 0, 1, 2
 MOE_SWIGLU, MOE_GELU = 0, 1
@@ -28,7 +29,7 @@ MOE_SWIGLU, MOE_GELU = 0, 1
 EXPORTED = ("moe_capacity", "moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn",
             "moe_combine", "moe_load_stats", "moe_layer_forward", "moe_layer_forward_timed", "moe_layer_forward_static",
             "moe_layer_backward", "moe_expert_choice_capacity", "moe_expert_choice_forward", "moe_ep_send_layout",
-            "moe_ep_recv_layout", "moe_layer_stages",
+            "moe_ep_recv_layout", "moe_layer_stages", "moe_check_dispatch",
             "moe_reload_tuning", "moe_status_string", "moe_last_error")
 STAGES = ("router_logits", "route_select", "permute", "expert_gate_up", "expert_down", "shared_gate_up",
           "shared_down", "combine", "load_stats", "fused_layer")
@@ -90,6 +91,7 @@ def lib() -> ctypes.CDLL:
             "moe_ep_send_layout": [i32, i32, vp, vp, vp, vp],
             "moe_ep_recv_layout": [i32, i32, vp, i32, vp, vp, vp],
             "moe_layer_stages": [cfgp, ctypes.POINTER(i32)],
+            "moe_check_dispatch": [cfgp, vp, vp, vp, vp, vp],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -196,7 +198,8 @@ def _stream(stream=None):
 
 def _check(fn: str, st: int):
     if st != MOE_OK:
-        detail = lib().moe_last_error().decode() if st in (MOE_ERR_HIP, MOE_ERR_WORKSPACE_TOO_SMALL) else ""
+        detail = (lib().moe_last_error().decode()
+                  if st in (MOE_ERR_HIP, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_DEBUG_CHECK) else "")
         raise MoEError(fn, st, detail)
 
 
@@ -214,6 +217,17 @@ def moe_layer_stages(cfg):
     runs = (ctypes.c_int32 * len(STAGES))()
     _check("moe_layer_stages", lib().moe_layer_stages(ctypes.byref(c), runs))
     return [name for name, r in zip(STAGES, runs) if r]
+
+
+def moe_check_dispatch(cfg, topk_idx, counts, offsets, row_of, token_of_row):
+    """The host-side dispatch check on numpy int32 arrays (shapes as in
+    moe_permute); raises MoEError(MOE_ERR_DEBUG_CHECK) naming the first bad
+    entry."""
+    import numpy as np
+    arrs = [np.ascontiguousarray(a, dtype=np.int32) for a in (topk_idx, counts, offsets, row_of, token_of_row)]
+    ptrs = [a.ctypes.data_as(ctypes.c_void_p) if a.size else None for a in arrs]
+    c = make_config(cfg)
+    _check("moe_check_dispatch", lib().moe_check_dispatch(ctypes.byref(c), *ptrs))
 
 
 def moe_workspace_size(cfg, op: int) -> int:

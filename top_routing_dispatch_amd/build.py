@@ -66,6 +66,69 @@ def build(verbose: bool = False, jobs: int = 8, out: str = LIB_PATH, defines=(),
     return out
 
 
+# Host code under AddressSanitizer and UndefinedBehaviorSanitizer: the
+# sanitizer flags go to the host pass only (device code is built as usual),
+# and the objects are linked by the host compiler against the shared
+# sanitizer runtime, which the process must preload
+# (LD_PRELOAD=sanitizer_runtime()).
+SAN_DIR = os.path.join(BUILD_DIR, "san")
+SAN_LIB = os.path.join(SAN_DIR, "libmoe_hip_san.so")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+CLANGXX = os.path.join(os.path.dirname(os.path.realpath(HIPCC)), "..", "llvm", "bin", "clang++")
+
+
+def sanitizer_runtime() -> str:
+    """The shared AddressSanitizer runtime of the ROCm compiler (it carries
+    the UndefinedBehaviorSanitizer handlers too)."""
+    found = glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so")
+    if not found:
+        raise RuntimeError("no AddressSanitizer runtime under /opt/rocm/llvm")
+    return sorted(found)[-1]
+
+
+def sources_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for src in sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.h")) +
+                      [os.path.join(INCLUDE, "moe.h")]):
+        with open(src, "rb") as f:
+            h.update(os.path.basename(src).encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def build_sanitized(verbose: bool = False, jobs: int = 8) -> str:
+    """The library with its host code under ASan + UBSan (-O1 -g), in
+    _build/san; rebuilt only when a source changed since the last build."""
+    os.makedirs(SAN_DIR, exist_ok=True)
+    stamp = os.path.join(SAN_DIR, "sources_digest")
+    digest = sources_digest()
+    if os.path.exists(SAN_LIB) and os.path.exists(stamp) and open(stamp).read().strip() == digest:
+        return SAN_LIB
+    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    flags = [f if f != "-O3" else "-O1" for f in FLAGS] + ["-g"] + SAN_FLAGS
+
+    def compile_one(src):
+        obj = os.path.join(SAN_DIR, os.path.basename(src) + ".o")
+        _run([HIPCC, *flags, "-c", src, "-o", obj])
+        return obj
+
+    with ThreadPoolExecutor(max(1, jobs)) as ex:
+        objs = list(ex.map(compile_one, sources))
+    tmp = SAN_LIB + ".tmp"
+    _run([CLANGXX, "-shared", "-fsanitize=address,undefined", "-shared-libsan", *objs,
+          "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib", "-o", tmp])
+    os.replace(tmp, SAN_LIB)
+    with open(stamp, "w") as f:
+        f.write(digest + "\n")
+    if verbose:
+        print(f"built {SAN_LIB}")
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    if "--sanitize" in sys.argv[1:]:
+        build_sanitized(verbose=True)
+    else:
+        build(verbose=True)
     sys.exit(0)

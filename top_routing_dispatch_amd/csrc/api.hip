@@ -9,6 +9,7 @@
 
 #include <atomic>
 #include <mutex>
+#include <vector>
 
 #include "common.h"
 #include "moe.h"
@@ -30,6 +31,8 @@ moe_status hip_status(const char* where, hipError_t e) {
   return MOE_ERR_HIP;
 }
 
+bool debug_on() { return tuning().debug > 0; }
+
 #define MOE_TRY_HIP(where, expr)                        \
   do {                                                  \
     const moe_status _st = hip_status(where, (expr));   \
@@ -40,6 +43,38 @@ moe_status hip_status(const char* where, hipError_t e) {
     const moe_status _st = (expr);                      \
     if (_st != MOE_OK) return _st;                      \
   } while (0)
+
+// MOE_DEBUG=1: device tables copied to the host and checked before going on.
+template <typename T>
+moe_status to_host(const T* dev, size_t n, std::vector<T>* out, hipStream_t s) {
+  out->assign(n, T());
+  if (n == 0) return MOE_OK;
+  MOE_TRY_HIP("debug copy", hipMemcpyAsync(out->data(), dev, n * sizeof(T), hipMemcpyDeviceToHost, s));
+  MOE_TRY_HIP("debug copy", hipStreamSynchronize(s));
+  return MOE_OK;
+}
+
+moe_status debug_fail(const char* where, const char* msg) {
+  debug_message(where, msg);
+  return MOE_ERR_DEBUG_CHECK;
+}
+
+moe_status debug_check_dispatch(const char* where, const moe_config* c, int capacity, int rows_cap,
+                                const int32_t* idx, const int32_t* counts, const int32_t* offsets,
+                                const int32_t* row_of, const int32_t* tor, hipStream_t s) {
+  const int T = c->num_tokens, k = c->top_k, E = c->num_experts;
+  std::vector<int32_t> hi, hc, ho, hr, ht;
+  MOE_TRY(to_host(idx, (size_t)T * k, &hi, s));
+  MOE_TRY(to_host(counts, (size_t)E, &hc, s));
+  MOE_TRY(to_host(offsets, (size_t)E + 1, &ho, s));
+  MOE_TRY(to_host(row_of, (size_t)T * k, &hr, s));
+  MOE_TRY(to_host(tor, (size_t)rows_cap, &ht, s));
+  char msg[200];
+  if (!check_dispatch(hi.data(), hc.data(), ho.data(), hr.data(), ht.data(), T, k, E, capacity, rows_cap, msg,
+                      sizeof(msg)))
+    return debug_fail(where, msg);
+  return MOE_OK;
+}
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool opt_aligned(const void* p) { return p == nullptr || aligned16(p); }
@@ -740,6 +775,12 @@ moe_status validate_ec(const moe_config* c) {
 
 }  // namespace
 
+namespace moe {
+void debug_message(const char* where, const char* msg) {
+  snprintf(g_last_error, sizeof(g_last_error), "%s: %s", where, msg);
+}
+}  // namespace moe
+
 extern "C" {
 
 const char* moe_status_string(moe_status st) {
@@ -749,6 +790,7 @@ const char* moe_status_string(moe_status st) {
     case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
     case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
     case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    case MOE_ERR_DEBUG_CHECK: return "MOE_ERR_DEBUG_CHECK";
   }
   return "unknown moe_status";
 }
@@ -836,6 +878,9 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* topk_idx, const voi
   a.counts = counts; a.offsets = offsets; a.row_of = row_of; a.token_of_row = token_of_row;
   a.tile_prefix = nullptr; a.bm = 1;
   MOE_TRY_HIP("permute", launch_permute(a, s));
+  if (debug_on() && any)
+    MOE_TRY(debug_check_dispatch("moe_permute", cfg, d.capacity, d.rows_cap, topk_idx, counts, offsets, row_of,
+                                 token_of_row, s));
   if (x != nullptr)
     MOE_TRY_HIP("gather rows", launch_gather_rows(x, token_of_row, offsets, cfg->num_experts, d.rows_cap,
                                                   cfg->d_model, (int)esize(cfg->act_dtype), x_perm, s));
@@ -868,6 +913,22 @@ moe_status moe_expert_ffn(const moe_config* cfg, int32_t num_groups, int32_t d_f
   if (ws_bytes < ws_ffn(cfg, num_groups, d_ff, max_rows, cfg->act_dtype)) return MOE_ERR_WORKSPACE_TOO_SMALL;
   if (max_rows == 0) return MOE_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (debug_on()) {
+    int rows = max_rows;
+    char msg[200];
+    if (offsets != nullptr) {
+      std::vector<int32_t> ho;
+      MOE_TRY(to_host(offsets, (size_t)num_groups + 1, &ho, s));
+      if (!check_group_offsets(ho.data(), num_groups, max_rows, msg, sizeof(msg)))
+        return debug_fail("moe_expert_ffn", msg);
+      rows = ho[num_groups];
+    }
+    if (gather_rows != nullptr) {
+      std::vector<int32_t> hg;
+      MOE_TRY(to_host(gather_rows, (size_t)rows, &hg, s));
+      if (!check_gather_rows(hg.data(), rows, msg, sizeof(msg))) return debug_fail("moe_expert_ffn", msg);
+    }
+  }
   void* h = ws;
   int32_t* prefix_up = nullptr;
   int32_t* prefix_dn = nullptr;
@@ -895,6 +956,13 @@ moe_status moe_combine(const moe_config* cfg, const void* y_perm, const int32_t*
       !opt_aligned(y))
     return MOE_ERR_INVALID_ARGUMENT;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (debug_on() && cfg->num_tokens > 0) {
+    std::vector<int32_t> hr;
+    MOE_TRY(to_host(row_of, (size_t)cfg->num_tokens * cfg->top_k, &hr, s));
+    char msg[200];
+    if (!check_row_map(hr.data(), cfg->num_tokens, cfg->top_k, d.rows_cap, msg, sizeof(msg)))
+      return debug_fail("moe_combine", msg);
+  }
   MOE_TRY_HIP("combine", launch_combine(y_perm, row_of, topk_w, y_shared, y, cfg->num_tokens, cfg->top_k,
                                         cfg->d_model, cfg->act_dtype, s));
   return MOE_OK;
@@ -1064,6 +1132,8 @@ static moe_status layer_forward_impl(const moe_config* cfg, const moe_weights* w
   MOE_TRY(mark(ev, MOE_STAGE_PERMUTE, 0, s));
   MOE_TRY_HIP("permute", launch_permute(pa, s));
   MOE_TRY(mark(ev, MOE_STAGE_PERMUTE, 1, s));
+  if (debug_on() && any)
+    MOE_TRY(debug_check_dispatch("moe_layer_forward", cfg, d.capacity, d.rows_cap, idx, cnt, off, row_of, tor, s));
   if (routing_only) return MOE_OK;
 
   StatsArgs sa{};

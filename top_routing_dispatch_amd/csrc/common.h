@@ -78,6 +78,7 @@ struct Tuning {
   int wgrad_tile = kUnset;       // MOE_WGRAD_TILE: 128 / 256
   int wgrad_swz = kUnset;        // MOE_WGRAD_SWZ: 0 / 1 / 2
   int fused = kUnset;            // MOE_FUSED: 1 / 0 one-workgroup layer for every / no batch that fits
+  int debug = kUnset;            // MOE_DEBUG: 1 checks the dispatch tables on the host (synchronises)
 };
 Tuning tuning();
 
@@ -426,6 +427,16 @@ struct FusedArgs {
   float alpha;
 };
 constexpr int kFusedMaxTokens = 256;
+
+// Host-side checks of dispatch tables in host memory (checks.hip); false
+// with a message in msg when a table breaks its definition.
+bool check_group_offsets(const int32_t* off, int G, int max_rows, char* msg, size_t n);
+bool check_gather_rows(const int32_t* rows, int n_rows, char* msg, size_t n);
+bool check_row_map(const int32_t* row_of, int T, int k, int rows_cap, char* msg, size_t n);
+bool check_dispatch(const int32_t* idx, const int32_t* counts, const int32_t* offsets, const int32_t* row_of,
+                    const int32_t* tor, int T, int k, int E, int capacity, int rows_cap, char* msg, size_t n);
+// Sets the library's last error message (api.hip).
+void debug_message(const char* where, const char* msg);
 bool fused_layer_fits(int act_dtype, int T, int D, int E, int k, int F, int SF);
 hipError_t launch_fused_layer(const FusedArgs& a, int act_dtype, int router_dtype, hipStream_t s);
 

@@ -45,6 +45,7 @@ void read_env() {
   t.wgrad_tile = env_int("MOE_WGRAD_TILE");
   t.wgrad_swz = env_int("MOE_WGRAD_SWZ");
   t.fused = env_int("MOE_FUSED");
+  t.debug = env_int("MOE_DEBUG");
   std::lock_guard<std::mutex> lock(g_tuning_mu);
   g_tuning = t;
 }
