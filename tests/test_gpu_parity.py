@@ -382,6 +382,7 @@ V2_SHAPES = [
 # -1: general kernel; 0-11: deep-tile kernel with 32- or 64-deep slices (9, 10:
 # persistent tiles); 12-19: persistent weight-streaming kernel
 GEMM_TILE_CONFIGS = range(-1, 20)
+WS_CONFIGS = range(12, 20)
 
 
 @pytest.mark.parametrize("gemm_cfg", [str(c) for c in GEMM_TILE_CONFIGS])
@@ -406,15 +407,21 @@ SPLIT_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("split", ["0", "1", "1-pers9"])
+@pytest.mark.parametrize("split", ["0", "1", "1-pers9", "1-rows128", "1-sh14-rows192"])
 @pytest.mark.parametrize("cfg", SPLIT_SHAPES + V2_SHAPES, ids=lambda c: c.name)
 def test_shallow_group_split(cfg, split, monkeypatch):
     """Expert FFN with shallow groups split off to the persistent
-    weight-streaming kernel (1), to the persistent configuration 19 of the
+    weight-streaming kernel (1; rowsN: groups of up to N rows count as
+    shallow, so that they take several of its 64-row tiles; 1-sh14: its
+    64 x 256 configuration), to the persistent configuration 9 of the
     deep-tile kernel (1-pers9), and without the split (0), against the oracle."""
     set_env(monkeypatch, "MOE_GEMM_SPLIT", split[0])
     if split == "1-pers9":
         set_env(monkeypatch, "MOE_GEMM_SHCFG", "9")
+    if split.startswith("1-sh"):
+        set_env(monkeypatch, "MOE_GEMM_SHCFG", split[4:6])
+    if "-rows" in split:
+        set_env(monkeypatch, "MOE_SHALLOW_ROWS", split.split("-rows")[1])
     print(f"[split {split}] {cfg.name}", flush=True)
     inp = W.make_inputs(cfg)
     ref = oracle_forward(cfg, inp)
@@ -461,7 +468,7 @@ WS_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("gemm_cfg", ["default"] + [str(c) for c in range(12, 20)])
+@pytest.mark.parametrize("gemm_cfg", ["default"] + [str(c) for c in WS_CONFIGS])
 @pytest.mark.parametrize("cfg", WS_SHAPES, ids=lambda c: c.name)
 def test_weight_streaming_many_tiles(cfg, gemm_cfg, monkeypatch):
     """The persistent weight-streaming GEMM (its configurations 12-19, and the
@@ -488,7 +495,7 @@ KSPLIT_SHAPES = [
 
 
 @pytest.mark.parametrize("ks", ["2", "4", "8"])
-@pytest.mark.parametrize("gemm_cfg", [str(c) for c in range(12, 20)])
+@pytest.mark.parametrize("gemm_cfg", [str(c) for c in WS_CONFIGS])
 @pytest.mark.parametrize("cfg", KSPLIT_SHAPES, ids=lambda c: c.name)
 def test_contraction_split(cfg, gemm_cfg, ks, monkeypatch):
     """Every configuration of the weight-streaming GEMM with its contraction

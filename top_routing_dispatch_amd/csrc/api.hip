@@ -326,9 +326,9 @@ int cfg_bm(int act, int cfg) {
 struct FfnPlan {
   int cfg_up, cfg_dn, bm_up, bm_dn;
   // split: groups of at most sh_rows rows go to the persistent weight-streaming
-  // configuration cfg_sh (one m-tile each), deeper groups to cfg_up / cfg_dn
+  // configuration cfg_sh (m-tiles of sh_bm rows), deeper groups to cfg_up / cfg_dn
   bool split;
-  int cfg_sh, sh_rows;
+  int cfg_sh, sh_rows, sh_bm;
   // contraction splits (1 = none) of the four launches: gate/up, down, and
   // the gate/up and down of the shallow groups of a split
   int ks_up, ks_dn, ks_sh_up, ks_sh_dn;
@@ -379,6 +379,8 @@ int pick_ksplit(int act, int cfg, int epi, int N, int K, int G, int max_rows, bo
 // average.  MOE_GEMM_SPLIT=0 / 1 overrides the choice (tuning aid).  When
 // every group is shallow (at most sh_rows rows in all: a decode-sized
 // batch) both projections run on the shallow-group configuration alone.
+constexpr int kShallowRows = 64;
+
 FfnPlan plan_ffn(int act, int activation, int D, int F, int max_rows, int G, bool grouped) {
   FfnPlan pl;
   pl.cfg_up = pick_cfg(act, D, max_rows, G, false);
@@ -390,7 +392,12 @@ FfnPlan plan_ffn(int act, int activation, int D, int F, int max_rows, int G, boo
   const Tuning t = tuning();
   if (t.gemm_shcfg != kUnset && t.gemm_shcfg >= 0 && t.gemm_shcfg < kGemmConfigs)
     pl.cfg_sh = t.gemm_shcfg;       // tuning aid: a configuration index >= 0
-  pl.sh_rows = cfg_bm(act, pl.cfg_sh);
+  // groups of at most sh_rows rows are shallow (64 by default; the tiles of
+  // the weight-streaming configuration may be shorter, a group then takes
+  // several of them)
+  pl.sh_bm = cfg_bm(act, pl.cfg_sh);
+  pl.sh_rows = pl.sh_bm > kShallowRows ? pl.sh_bm : kShallowRows;
+  if (t.shallow_rows != kUnset && t.shallow_rows >= pl.sh_bm && t.shallow_rows <= 4096) pl.sh_rows = t.shallow_rows;
   const bool forced = t.gemm_cfg != kUnset;
   if (!forced && pl.cfg_up >= 0 && pl.cfg_dn >= 0 && D % 64 == 0 && F % 64 == 0 && max_rows <= pl.sh_rows) {
     pl.cfg_up = pl.cfg_sh;
@@ -534,7 +541,7 @@ moe_status run_ffn(int act, int activation, int G, int D, int F, int max_rows, c
     int32_t* shallow = prefix_ws + 2 * (G + 1);
     const TilePrefixReq r0{deep_up, pl.bm_up, pl.sh_rows, INT_MAX};
     const TilePrefixReq r1{deep_dn != deep_up ? deep_dn : nullptr, pl.bm_dn, pl.sh_rows, INT_MAX};
-    const TilePrefixReq r2{shallow, pl.sh_rows, 0, pl.sh_rows};
+    const TilePrefixReq r2{shallow, pl.sh_bm, 0, pl.sh_rows};
     MOE_TRY_HIP("tile prefix", launch_tile_prefix_classes(offsets, G, r0, r1, r2, s));
     g1.tile_prefix = deep_up;
     g2.tile_prefix = deep_dn;

@@ -79,6 +79,7 @@ struct Tuning {
   int wgrad_swz = kUnset;        // MOE_WGRAD_SWZ: 0 / 1 / 2
   int fused = kUnset;            // MOE_FUSED: 1 / 0 one-workgroup layer for every / no batch that fits
   int debug = kUnset;            // MOE_DEBUG: 1 checks the dispatch tables on the host (synchronises)
+  int shallow_rows = kUnset;     // MOE_SHALLOW_ROWS: groups of at most this many rows count as shallow
 };
 Tuning tuning();
 

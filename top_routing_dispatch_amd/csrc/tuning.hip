@@ -46,6 +46,7 @@ void read_env() {
   t.wgrad_swz = env_int("MOE_WGRAD_SWZ");
   t.fused = env_int("MOE_FUSED");
   t.debug = env_int("MOE_DEBUG");
+  t.shallow_rows = env_int("MOE_SHALLOW_ROWS");
   std::lock_guard<std::mutex> lock(g_tuning_mu);
   g_tuning = t;
 }
