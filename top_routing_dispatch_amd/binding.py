@@ -8,6 +8,7 @@ if the library is missing, loading fails loudly.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 from typing import Optional
 
@@ -108,20 +109,39 @@ def lib() -> ctypes.CDLL:
 
 
 def moe_reload_tuning():
-    """Re-read the MOE_* tuning variables (the library reads them once)."""
+    """Re-read the MOE_* tuning variables (the library reads them once); the
+    workspace sizes cached here depend on them."""
     _check("moe_reload_tuning", lib().moe_reload_tuning())
+    _workspace_size_cached.cache_clear()
+    _layer_specs.cache_clear()
 
 
-def make_config(cfg) -> moe_config:
-    """moe_config from any object carrying the same field names."""
+def _new_config(cfg) -> moe_config:
     c = moe_config()
     for name, _ in moe_config._fields_:
         setattr(c, name, getattr(cfg, name))
     return c
 
 
+@functools.lru_cache(maxsize=512)
+def _config_cached(cfg) -> moe_config:
+    return _new_config(cfg)
+
+
+def make_config(cfg) -> moe_config:
+    """moe_config from any object carrying the same field names (one shared,
+    read-only structure per hashable configuration: the library only reads
+    it)."""
+    try:
+        return _config_cached(cfg)
+    except TypeError:                    # not hashable
+        return _new_config(cfg)
+
+
 def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    """Device address of a tensor as a plain integer (ctypes converts it for
+    the c_void_p parameters), or None."""
+    return None if t is None else t.data_ptr()
 
 
 _I32, _F32, _BYTES = "int32", "float32", "bytes"
@@ -230,11 +250,23 @@ def moe_check_dispatch(cfg, topk_idx, counts, offsets, row_of, token_of_row):
     _check("moe_check_dispatch", lib().moe_check_dispatch(ctypes.byref(c), *ptrs))
 
 
-def moe_workspace_size(cfg, op: int) -> int:
+def _workspace_size(cfg, op: int) -> int:
     c = make_config(cfg)
     n = ctypes.c_size_t()
     _check("moe_workspace_size", lib().moe_workspace_size(ctypes.byref(c), op, ctypes.byref(n)))
     return n.value
+
+
+@functools.lru_cache(maxsize=1024)
+def _workspace_size_cached(cfg, op: int) -> int:
+    return _workspace_size(cfg, op)
+
+
+def moe_workspace_size(cfg, op: int) -> int:
+    try:
+        return _workspace_size_cached(cfg, op)
+    except TypeError:                    # not hashable
+        return _workspace_size(cfg, op)
 
 
 def workspace(cfg, op: int, device="cuda") -> torch.Tensor:
@@ -328,18 +360,56 @@ def moe_load_stats(cfg, counts, probs, alpha, f, P, aux_loss, imbalance, dropped
                                                   _ws_bytes(ws), _stream(stream)))
 
 
+def _layer_specs_of(cfg, with_ws: bool):
+    """(name, kind, numel, required) of every tensor argument of the layer
+    forward, weights first."""
+    T, D, E, k, F = cfg.num_tokens, cfg.d_model, cfg.num_experts, cfg.top_k, cfg.d_ff
+    nF = (2 if cfg.activation == MOE_SWIGLU else 1) * F
+    SF = cfg.num_shared * cfg.d_ff_shared
+    specs = [("w_router", "router", E * D, True), ("sel_bias", _F32, E, False),
+             ("w13", "act", E * nF * D, True), ("w2", "act", E * D * F, True),
+             ("ws13", "act", 2 * SF * D, SF > 0), ("ws2", "act", D * SF, SF > 0),
+             ("x", "act", T * D, T > 0), ("y", "act", T * D, T > 0),
+             ("topk_idx", _I32, T * k, False), ("topk_w", _F32, T * k, False), ("counts", _I32, E, False),
+             ("stats", _F32, 2 * E + 2, False), ("dropped", _I32, 1, False)]
+    if with_ws:
+        specs.append(("ws", _BYTES, moe_workspace_size(cfg, MOE_OP_LAYER), T > 0))
+    return tuple((name, None if kind == _BYTES else _elem(cfg, kind), kind, n, req) for name, kind, n, req in specs)
+
+
+@functools.lru_cache(maxsize=512)
+def _layer_specs(cfg, with_ws: bool):
+    return _layer_specs_of(cfg, with_ws)
+
+
 def _check_layer_args(fn, cfg, weights, x, y, topk_idx, topk_w, counts, stats, dropped, ws):
-    T, D, E, k = cfg.num_tokens, cfg.d_model, cfg.num_experts, cfg.top_k
-    _check_weights(fn, cfg, weights)
-    _arg(fn, "x", x, "act", T * D, cfg, required=T > 0)
-    _arg(fn, "y", y, "act", T * D, cfg, required=T > 0)
-    _arg(fn, "topk_idx", topk_idx, _I32, T * k, cfg)
-    _arg(fn, "topk_w", topk_w, _F32, T * k, cfg)
-    _arg(fn, "counts", counts, _I32, E, cfg)
-    _arg(fn, "stats", stats, _F32, 2 * E + 2, cfg)
-    _arg(fn, "dropped", dropped, _I32, 1, cfg)
-    if fn != "moe_layer_forward_static":
-        _arg(fn, "ws", ws, _BYTES, moe_workspace_size(cfg, MOE_OP_LAYER), cfg, required=T > 0)
+    """The per-tensor checks of _arg on every argument of the layer forward,
+    in one pass; the first argument that fails is re-checked by _arg for its
+    message.  The specs (element types and sizes) are cached per hashable
+    configuration."""
+    with_ws = fn != "moe_layer_forward_static"
+    try:
+        specs = _layer_specs(cfg, with_ws)
+    except TypeError:                    # not hashable
+        specs = _layer_specs_of(cfg, with_ws)
+    g = weights.get
+    tensors = (g("w_router"), g("sel_bias"), g("w13"), g("w2"), g("ws13"), g("ws2"),
+               x, y, topk_idx, topk_w, counts, stats, dropped, ws)
+    on_device = _on_device
+    for (name, dt, kind, numel, req), t in zip(specs, tensors):
+        if t is None:
+            if req:
+                raise ValueError(f"{fn}: {name} is required")
+            continue
+        if isinstance(t, torch.Tensor):
+            n_t = t.numel()
+            if numel == 0 and n_t == 0:
+                continue                 # nothing is read or written through it
+            if (on_device(t) and t.is_contiguous() and
+                    (n_t * t.element_size() >= numel if dt is None else (t.dtype is dt and n_t >= numel))):
+                continue
+        _arg(fn, name, t, kind, numel, cfg, required=req)
+        raise ValueError(f"{fn}: {name} failed its check")
 
 
 def moe_layer_forward(cfg, weights: dict, x, y, topk_idx=None, topk_w=None, counts=None, alpha=0.01, stats=None,
@@ -383,9 +453,9 @@ def moe_layer_forward_timed(cfg, weights: dict, x, y, topk_idx=None, topk_w=None
     for name, _ in moe_weights._fields_:
         t = weights.get(name)
         setattr(w, name, None if t is None else t.data_ptr())
-    n = 2 * len(STAGES)
-    arr = (ctypes.c_void_p * n)()
+    arr = None
     if stage_events is not None:
+        arr = (ctypes.c_void_p * (2 * len(STAGES)))()
         for i, ev in enumerate(stage_events):
             arr[i] = None if ev is None else ev.cuda_event
     _check("moe_layer_forward_timed", lib().moe_layer_forward_timed(
