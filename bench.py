@@ -430,7 +430,7 @@ def main():
     # the time they wait for the chip
     main_ms = {k: v for k, v in stage_ms.items() if k not in AUX_STAGES}
     if "expert_ffn" in main_ms:
-        # the routed expert FFN is judged as one grouped-GEMM stage
+        # the routed expert FFN is timed as one grouped-GEMM stage
         main_ms.pop("expert_gate_up")
         main_ms.pop("expert_down")
     dominant = max(main_ms or stage_ms, key=(main_ms or stage_ms).get)
