@@ -379,10 +379,11 @@ V2_SHAPES = [
 ]
 
 
-# -1: general kernel; 0-11: deep-tile kernel with 32- or 64-deep slices (9, 10:
-# persistent tiles); 12-19: persistent weight-streaming kernel
-GEMM_TILE_CONFIGS = range(-1, 20)
-WS_CONFIGS = range(12, 20)
+# -1: general kernel; 0-13: deep-tile kernel with 32- or 64-deep slices (9, 10:
+# persistent tiles; 12, 13: slices staged in registers); 14-21: persistent
+# weight-streaming kernel
+GEMM_TILE_CONFIGS = range(-1, 22)
+WS_CONFIGS = range(14, 22)
 
 
 @pytest.mark.parametrize("gemm_cfg", [str(c) for c in GEMM_TILE_CONFIGS])
@@ -407,12 +408,12 @@ SPLIT_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("split", ["0", "1", "1-pers9", "1-rows128", "1-sh14-rows192"])
+@pytest.mark.parametrize("split", ["0", "1", "1-pers9", "1-rows128", "1-sh16-rows192"])
 @pytest.mark.parametrize("cfg", SPLIT_SHAPES + V2_SHAPES, ids=lambda c: c.name)
 def test_shallow_group_split(cfg, split, monkeypatch):
     """Expert FFN with shallow groups split off to the persistent
     weight-streaming kernel (1; rowsN: groups of up to N rows count as
-    shallow, so that they take several of its 64-row tiles; 1-sh14: its
+    shallow, so that they take several of its 64-row tiles; 1-sh16: its
     64 x 256 configuration), to the persistent configuration 9 of the
     deep-tile kernel (1-pers9), and without the split (0), against the oracle."""
     set_env(monkeypatch, "MOE_GEMM_SPLIT", split[0])
@@ -471,7 +472,7 @@ WS_SHAPES = [
 @pytest.mark.parametrize("gemm_cfg", ["default"] + [str(c) for c in WS_CONFIGS])
 @pytest.mark.parametrize("cfg", WS_SHAPES, ids=lambda c: c.name)
 def test_weight_streaming_many_tiles(cfg, gemm_cfg, monkeypatch):
-    """The persistent weight-streaming GEMM (its configurations 12-19, and the
+    """The persistent weight-streaming GEMM (its configurations 14-21, and the
     default choice for these shallow groups) against the oracle with several
     tiles per workgroup."""
     if gemm_cfg != "default":

@@ -290,7 +290,7 @@ hipError_t launch_gemm_bf16(const GroupedGemm& g, hipStream_t s);
 int gemm_bf16_bm(const GroupedGemm& g);
 // bf16 grouped GEMM for deep groups (K % 64 == 0, or % 32 for the 32-deep
 // configurations): tile configurations 0 .. kGemmV3Configs-1.
-constexpr int kGemmV3Configs = 12;
+constexpr int kGemmV3Configs = 14;
 hipError_t launch_gemm_v3(const GroupedGemm& g, int cfg, hipStream_t s);
 int gemm_v3_bm(int cfg);
 // Persistent weight-streaming bf16 grouped GEMM for shallow groups (K % 64 ==

@@ -25,7 +25,7 @@
 namespace moe {
 namespace {
 
-template <int BM, int BN, int WGM, int WGN, int BK, int NST, int NSTB>
+template <int BM, int BN, int WGM, int WGN, int BK, int NST, int NSTB, int RSD = 0>
 struct Cfg3 {
   static constexpr int THREADS = 64 * WGM * WGN;
   static constexpr int NWAVES = WGM * WGN;
@@ -37,7 +37,10 @@ struct Cfg3 {
   static constexpr int KK = BK / 16;                     // MFMA k-steps per slice
   static constexpr int A_BYTES = BM * RB, B_BYTES = BN * RB;
   static constexpr int B_RING = NST * A_BYTES;           // the B ring follows the A ring
-  static constexpr int LDS = NST * A_BYTES + NSTB * B_BYTES;
+  // RSD > 0: slices staged in registers (RSD slices in flight per thread) and
+  // written to two LDS stages of A_BYTES + B_BYTES; otherwise the DMA rings
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int LDS = RSD > 0 ? 2 * STAGE : NST * A_BYTES + NSTB * B_BYTES;
   static constexpr int A_INS = BM / RPI / NWAVES;        // load instructions per wave per slice
   static constexpr int B_INS = BN / RPI / NWAVES;
   static constexpr int INS = A_INS + B_INS;
@@ -79,11 +82,12 @@ __device__ __forceinline__ int swz3(int r, int c) {
   return r * (CPR * 16) + ((c ^ ((r / (16 / CPR)) & (CPR - 1))) << 4);
 }
 
-template <int BM, int BN, int WGM, int WGN, int BK, int NST, int NSTB, int OCC, bool PERS, int EPI, typename OutT>
+template <int BM, int BN, int WGM, int WGN, int BK, int NST, int NSTB, int RSD, int OCC, bool PERS, int EPI,
+          typename OutT>
 __global__ __launch_bounds__(64 * WGM * WGN)
 __attribute__((amdgpu_waves_per_eu(WGM * WGN / 4 * OCC, WGM * WGN / 4 * OCC)))
 void gemm_v3_kernel(const GroupedGemm p, int n_tiles) {
-  using C = Cfg3<BM, BN, WGM, WGN, BK, NST, NSTB>;
+  using C = Cfg3<BM, BN, WGM, WGN, BK, NST, NSTB, RSD>;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
   const int lane = threadIdx.x & 63;
@@ -178,6 +182,42 @@ void gemm_v3_kernel(const GroupedGemm p, int n_tiles) {
 
   constexpr int MF = C::TM * C::TN;
 
+  // Fragment read r (0 <= r < TM + TN) of 16-deep step kk of the slice at sa
+  // (A) / sb (B), numbered in the order of first use by the MFMAs (block row
+  // i, then column j): A0, B0..B(TN-1), A1, ..., A(TM-1).
+  // act_c: the number of 32-row blocks of the wave that hold rows of the
+  // tile when known at compile time, else -1 (act_i at run time).
+  auto frag_read1 = [&](auto act_c, int buf, const char* sa, const char* sb, int kk, int r)
+                        __attribute__((always_inline)) {
+    constexpr int ACT = decltype(act_c)::value;
+    const int act = ACT >= 0 ? ACT : act_i;
+    const int ch = kk * 2 + fc;
+    if (r >= 1 && r <= C::TN) {
+      bfv[buf][r - 1] = *reinterpret_cast<const bf16x8_t*>(sb + swz3<C::CPR>(wn * C::WN + (r - 1) * 32 + fr, ch));
+    } else {
+      const int i = r == 0 ? 0 : r - C::TN;
+      if (i == 0 || i < act)
+        af[buf][i] = *reinterpret_cast<const bf16x8_t*>(sa + swz3<C::CPR>(wm * C::WM + i * 32 + fr, ch));
+    }
+  };
+  auto frag_reads = [&](auto act_c, int buf, const char* sa, const char* sb, int kk) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < C::TM + C::TN; ++r) frag_read1(act_c, buf, sa, sb, kk, r);
+  };
+  // MFMAs of one 16-deep step on fragment buffer `buf`.
+  auto mfma_all = [&](auto act_c, int buf) __attribute__((always_inline)) {
+    constexpr int ACT = decltype(act_c)::value;
+    const int act = ACT >= 0 ? ACT : act_i;
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) {
+      if (i < act) {
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][i], bfv[buf][j], acc[i][j], 0, 0, 0);
+      }
+    }
+  };
+
   // FULL: every 32-row block of the wave holds rows of the tile.  Its steps
   // are straight-line code, and each step's fragment reads for the next step
   // (and its refill loads) are placed one after each MFMA, so that they issue
@@ -217,33 +257,11 @@ void gemm_v3_kernel(const GroupedGemm p, int n_tiles) {
       else wait_vm<0>();
       __builtin_amdgcn_s_barrier();
     };
-    // Fragment reads in the order of first use by the MFMAs (block row i,
-    // then column j): A0, B0..B(TN-1), A1, ..., A(TM-1).
+    using act_t = std::integral_constant<int, FULL ? C::TM : -1>;
     auto load_frags = [&](int buf, int kt, int kk) __attribute__((always_inline)) {
-      const char* sa = smem + (kt % NST) * C::A_BYTES;
-      const char* sb = smem + C::B_RING + (kt % NSTB) * C::B_BYTES;
-      const int ch = kk * 2 + fc;
-      af[buf][0] = *reinterpret_cast<const bf16x8_t*>(sa + swz3<C::CPR>(wm * C::WM + fr, ch));
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j)
-        bfv[buf][j] = *reinterpret_cast<const bf16x8_t*>(sb + swz3<C::CPR>(wn * C::WN + j * 32 + fr, ch));
-#pragma unroll
-      for (int i = 1; i < C::TM; ++i)
-        if (FULL || i < act_i)
-          af[buf][i] = *reinterpret_cast<const bf16x8_t*>(sa + swz3<C::CPR>(wm * C::WM + i * 32 + fr, ch));
+      frag_reads(act_t{}, buf, smem + (kt % NST) * C::A_BYTES, smem + C::B_RING + (kt % NSTB) * C::B_BYTES, kk);
     };
-    // MFMAs of one 16-deep step on fragment buffer `buf`, with the refill
-    // loads that belong to step kk.
-    auto mfma_step = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i) {
-        if (FULL || i < act_i) {
-#pragma unroll
-          for (int j = 0; j < C::TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][i], bfv[buf][j], acc[i][j], 0, 0, 0);
-        }
-      }
-    };
+    auto mfma_step = [&](int buf) __attribute__((always_inline)) { mfma_all(act_t{}, buf); };
     // Instruction order of one straight-line step: MFMA m is followed by the
     // reads r with r * MF / NR == m and the loads d with d * MF / ND == m.
     auto interleave = [&](bool reads, bool refill_here) __attribute__((always_inline)) {
@@ -297,12 +315,162 @@ void gemm_v3_kernel(const GroupedGemm p, int n_tiles) {
     for (; kt < nk - 1; ++kt) slice(kt, false, false);
     slice(nk - 1, false, true);
   };
-  if (act_i == C::TM) {
-    if (a_live) k_loop(std::true_type{}, std::true_type{});
-    else k_loop(std::true_type{}, std::false_type{});
+  // Register-staged slices (RSD > 0): each thread loads its 16-byte chunks of
+  // slice j (the same chunks the DMA rings move, so the LDS layout and the
+  // fragment reads are those above) into register set j % RSD, and writes
+  // them to LDS stage j % 2 during the iteration before slice j is
+  // multiplied; the loads of slice j + RSD then reuse those registers.  Slice
+  // j's loads are thus issued RSD iterations before they are awaited, and
+  // one barrier per iteration hands the stages over.
+  // act_c: the wave's count of 32-row blocks holding rows of the tile (a
+  // compile-time constant here, so that partial tiles get the interleaved
+  // schedule too, with their own MFMA count).
+  auto k_loop_rs = [&](auto act_c, auto al_c) __attribute__((always_inline)) {
+    constexpr int ACT = decltype(act_c)::value;
+    constexpr bool AL = decltype(al_c)::value;
+    constexpr int MFR = ACT * C::TN;                     // MFMAs per step
+    constexpr int RS = RSD > 0 ? RSD : 1;
+    static_assert(RS <= 2, "register sets");
+    constexpr int WL = (AL ? C::A_INS : 0) + C::B_INS;   // loads (and LDS writes) per slice of this wave
+    u32x4_t R[RS][C::INS];
+    // Load / LDS write w (0 <= w < WL) of this wave's share of a slice: the A
+    // chunks first (when the wave loads A), then the B chunks.
+    auto gload1 = [&](auto set_c, int j, int w) __attribute__((always_inline)) {
+      constexpr int S = decltype(set_c)::value;
+      const int q = AL ? w : C::A_INS + w;
+      if (q < C::A_INS) R[S][q] = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_off[q] + j * (unsigned)C::RB, 0, 0);
+      else R[S][q] = __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, b_off[q - C::A_INS] + j * (unsigned)C::RB, 0, 0);
+    };
+    auto lwrite1 = [&](auto set_c, int j, int w) __attribute__((always_inline)) {
+      constexpr int S = decltype(set_c)::value;
+      const int q = AL ? w : C::A_INS + w;
+      char* st = smem + (j & 1) * C::STAGE +
+                 (q < C::A_INS ? (wave * C::A_INS + q) * 1024 : C::A_BYTES + (wave * C::B_INS + q - C::A_INS) * 1024);
+      *reinterpret_cast<u32x4_t*>(st + lane * 16) = R[S][q];
+    };
+    auto gload = [&](auto set_c, int j) __attribute__((always_inline)) {
+#pragma unroll
+      for (int w = 0; w < WL; ++w) gload1(set_c, j, w);
+    };
+    auto lwrite = [&](auto set_c, int j) __attribute__((always_inline)) {
+#pragma unroll
+      for (int w = 0; w < WL; ++w) lwrite1(set_c, j, w);
+    };
+    // the writes and loads of one slice are spread over the first KK - 1
+    // steps: step kk takes w in [w_lo(kk), w_lo(kk + 1))
+    auto w_lo = [](int kk) { return kk * WL / (C::KK - 1); };
+    auto load_frags = [&](int buf, int kt, int kk) __attribute__((always_inline)) {
+      const char* sa = smem + (kt & 1) * C::STAGE;
+      frag_reads(act_c, buf, sa, sa + C::A_BYTES, kk);
+    };
+    // fragment reads of a step: A0 and the B blocks always, A1.. as active
+    constexpr int NR = (ACT > 1 ? ACT : 1) + C::TN;
+    // one MFMA, then the fragment reads, LDS writes and loads that follow it
+    auto interleave = [&](bool reads, int nw) __attribute__((always_inline)) {
+      if constexpr (MFR > 0) {
+#pragma unroll
+        for (int m = 0; m < MFR; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
+          if (reads) {
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+              if (r * MFR / NR == m) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+          }
+#pragma unroll
+          for (int d = 0; d < C::INS; ++d)
+            if (d < nw && d * MFR / nw == m) {
+              __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // one LDS write
+              __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one load
+            }
+        }
+      }
+    };
+    // Iteration kt multiplies slice kt (stage kt % 2); wr: slice kt + 1 exists
+    // and goes from its registers to the other stage; ld: slice kt + 1 + RS
+    // exists and is loaded into the registers just written; last: no next slice.
+    auto slice = [&](int kt, auto set_c, bool wr, bool ld, bool last) __attribute__((always_inline)) {
+#pragma unroll
+      for (int kk = 0; kk < C::KK - 1; ++kk) {
+        // The reads of this stage and the writes to the other one go out in
+        // the order the schedule below interleaves them (the compiler keeps
+        // LDS reads and writes in source order, as it cannot tell the two
+        // stages apart).
+        const char* sa = smem + (kt & 1) * C::STAGE;
+        const int nw = w_lo(kk + 1) - w_lo(kk);
+        constexpr int SLOTS = MFR > 0 ? MFR : 1;
+#pragma unroll
+        for (int m = 0; m < SLOTS; ++m) {
+#pragma unroll
+          for (int r = 0; r < NR; ++r)
+            if (r * SLOTS / NR == m) frag_read1(act_c, (kk + 1) & 1, sa, sa + C::A_BYTES, kk + 1, r);
+#pragma unroll
+          for (int d = 0; d < C::INS; ++d)
+            if (d < nw && d * SLOTS / nw == m) {
+              if (wr) lwrite1(set_c, kt + 1, w_lo(kk) + d);
+              if (ld) gload1(set_c, kt + 1 + RS, w_lo(kk) + d);
+            }
+        }
+        mfma_all(act_c, kk & 1);
+        interleave(true, wr && ld ? nw : 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // this wave's reads of slice kt and writes of slice kt + 1 are done
+      // before the barrier; after it every wave's writes are visible and the
+      // stage of slice kt may be refilled
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (!last) {
+        __builtin_amdgcn_s_barrier();
+        load_frags(0, kt + 1, 0);
+      }
+      mfma_all(act_c, 1);
+      interleave(!last, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // register set of the slice written in iteration kt: (kt + 1) % RS
+    auto slice_any = [&](int kt, bool wr, bool ld, bool last) __attribute__((always_inline)) {
+      if (RS == 1 || (kt + 1) % RS == 0) slice(kt, std::integral_constant<int, 0>{}, wr, ld, last);
+      else slice(kt, std::integral_constant<int, RS - 1>{}, wr, ld, last);
+    };
+    gload(std::integral_constant<int, 0>{}, 0);
+    lwrite(std::integral_constant<int, 0>{}, 0);
+    if (1 < nk) gload(std::integral_constant<int, 1 % RS>{}, 1);
+    if (RS == 2 && 2 < nk) gload(std::integral_constant<int, 0>{}, 2);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    load_frags(0, 0, 0);
+    const int n_full = max(0, nk - 1 - RS);   // iterations that write and load
+    int kt = 0;
+    for (; kt + RS <= n_full; kt += RS) {
+      slice(kt, std::integral_constant<int, 1 % RS>{}, true, true, false);
+      if constexpr (RS == 2) slice(kt + 1, std::integral_constant<int, 0>{}, true, true, false);
+    }
+    for (; kt < n_full; ++kt) slice_any(kt, true, true, false);
+    for (; kt < nk - 1; ++kt) slice_any(kt, true, false, false);
+    slice_any(nk - 1, false, false, true);
+  };
+  if constexpr (RSD > 0) {
+    // one instance per count of active 32-row blocks (a wave with none
+    // still loads and writes its share of the slices)
+    auto by_act = [&](auto act_c) __attribute__((always_inline)) {
+      if (a_live) k_loop_rs(act_c, std::true_type{});
+      else k_loop_rs(act_c, std::false_type{});
+    };
+    static_assert(C::TM <= 4, "active block counts");
+    switch (act_i) {
+      case 0: by_act(std::integral_constant<int, 0>{}); break;
+      case 1: by_act(std::integral_constant<int, 1>{}); break;
+      case 2: if constexpr (C::TM >= 2) by_act(std::integral_constant<int, 2>{}); break;
+      case 3: if constexpr (C::TM >= 3) by_act(std::integral_constant<int, 3>{}); break;
+      default: if constexpr (C::TM >= 4) by_act(std::integral_constant<int, 4>{}); break;
+    }
   } else {
-    if (a_live) k_loop(std::false_type{}, std::true_type{});
-    else k_loop(std::false_type{}, std::false_type{});
+    if (act_i == C::TM) {
+      if (a_live) k_loop(std::true_type{}, std::true_type{});
+      else k_loop(std::true_type{}, std::false_type{});
+    } else {
+      if (a_live) k_loop(std::false_type{}, std::true_type{});
+      else k_loop(std::false_type{}, std::false_type{});
+    }
   }
   wait_vm<0>();   // nothing is in flight into LDS when the staging below reuses it
 
@@ -377,9 +545,9 @@ inline int m_bound3(const GroupedGemm& p, int bm) {
   return p.M_max / bm + (p.G < p.M_max ? p.G : p.M_max);
 }
 
-template <int BM, int BN, int WGM, int WGN, int BK, int NST, int NSTB, int OCC, bool PERS, int EPI>
+template <int BM, int BN, int WGM, int WGN, int BK, int NST, int NSTB, int RSD, int OCC, bool PERS, int EPI>
 hipError_t launch_cfg3(const GroupedGemm& p, hipStream_t s) {
-  using C = Cfg3<BM, BN, WGM, WGN, BK, NST, NSTB>;
+  using C = Cfg3<BM, BN, WGM, WGN, BK, NST, NSTB, RSD>;
   if (p.K % BK != 0) return hipErrorInvalidValue;
   const int cols = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
   const int n_tiles = ceil_div(p.N, cols);
@@ -399,12 +567,12 @@ hipError_t launch_cfg3(const GroupedGemm& p, hipStream_t s) {
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64 || !allowed[dev].load(std::memory_order_relaxed)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_v3_kernel<BM, BN, WGM, WGN, BK, NST, NSTB, OCC, PERS, EPI, bf16_t>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_v3_kernel<BM, BN, WGM, WGN, BK, NST, NSTB, RSD, OCC, PERS, EPI, bf16_t>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
     if (e != hipSuccess) return e;
     if (dev >= 0 && dev < 64) allowed[dev].store(true, std::memory_order_relaxed);
   }
-  hipLaunchKernelGGL((gemm_v3_kernel<BM, BN, WGM, WGN, BK, NST, NSTB, OCC, PERS, EPI, bf16_t>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((gemm_v3_kernel<BM, BN, WGM, WGN, BK, NST, NSTB, RSD, OCC, PERS, EPI, bf16_t>), dim3((unsigned)blocks),
                      dim3(C::THREADS), C::LDS, s, p, n_tiles);
   return hipGetLastError();
 }
@@ -412,22 +580,25 @@ hipError_t launch_cfg3(const GroupedGemm& p, hipStream_t s) {
 template <int EPI>
 hipError_t launch_v3_epi(const GroupedGemm& p, int cfg, hipStream_t s) {
   switch (cfg) {
-    //                       BM   BN WGM WGN  BK NST NSTB OCC   PERS
+    //                       BM   BN WGM WGN  BK NST NSTB RSD OCC PERS
     // one workgroup per CU
-    case 0: return launch_cfg3<256, 256, 2, 4, 64, 2, 3, 1, false, EPI>(p, s);
-    case 1: return launch_cfg3<256, 256, 2, 4, 64, 2, 2, 1, false, EPI>(p, s);
-    case 2: return launch_cfg3<256, 256, 2, 2, 64, 2, 3, 1, false, EPI>(p, s);
-    case 3: return launch_cfg3<256, 256, 2, 2, 64, 2, 2, 1, false, EPI>(p, s);
-    case 4: return launch_cfg3<256, 256, 2, 4, 32, 4, 4, 1, false, EPI>(p, s);
-    case 11: return launch_cfg3<128, 256, 1, 4, 32, 4, 4, 1, false, EPI>(p, s);
+    case 0: return launch_cfg3<256, 256, 2, 4, 64, 2, 3, 0, 1, false, EPI>(p, s);
+    case 1: return launch_cfg3<256, 256, 2, 4, 64, 2, 2, 0, 1, false, EPI>(p, s);
+    case 2: return launch_cfg3<256, 256, 2, 2, 64, 2, 3, 0, 1, false, EPI>(p, s);
+    case 3: return launch_cfg3<256, 256, 2, 2, 64, 2, 2, 0, 1, false, EPI>(p, s);
+    case 4: return launch_cfg3<256, 256, 2, 4, 32, 4, 4, 0, 1, false, EPI>(p, s);
+    case 11: return launch_cfg3<128, 256, 1, 4, 32, 4, 4, 0, 1, false, EPI>(p, s);
     // two workgroups per CU (<= 80 KB of LDS each)
-    case 5: return launch_cfg3<128, 128, 2, 2, 32, 4, 4, 2, false, EPI>(p, s);
-    case 6: return launch_cfg3<128, 128, 2, 2, 64, 2, 2, 2, false, EPI>(p, s);
-    case 7: return launch_cfg3<128, 128, 2, 2, 64, 2, 3, 2, false, EPI>(p, s);
-    case 8: return launch_cfg3<128, 256, 2, 2, 32, 3, 3, 2, false, EPI>(p, s);
+    case 5: return launch_cfg3<128, 128, 2, 2, 32, 4, 4, 0, 2, false, EPI>(p, s);
+    case 6: return launch_cfg3<128, 128, 2, 2, 64, 2, 2, 0, 2, false, EPI>(p, s);
+    case 7: return launch_cfg3<128, 128, 2, 2, 64, 2, 3, 0, 2, false, EPI>(p, s);
+    case 8: return launch_cfg3<128, 256, 2, 2, 32, 3, 3, 0, 2, false, EPI>(p, s);
     // persistent weight streaming for shallow groups (one m-tile per group)
-    case 9: return launch_cfg3<64, 256, 1, 4, 64, 4, 4, 1, true, EPI>(p, s);
-    case 10: return launch_cfg3<64, 256, 1, 4, 32, 4, 4, 2, true, EPI>(p, s);
+    case 9: return launch_cfg3<64, 256, 1, 4, 64, 4, 4, 0, 1, true, EPI>(p, s);
+    case 10: return launch_cfg3<64, 256, 1, 4, 32, 4, 4, 0, 2, true, EPI>(p, s);
+    // register-staged slices, two LDS stages
+    case 12: return launch_cfg3<256, 256, 2, 2, 64, 2, 2, 1, 1, false, EPI>(p, s);
+    case 13: return launch_cfg3<256, 256, 2, 4, 64, 2, 2, 1, 1, false, EPI>(p, s);
   }
   return hipErrorInvalidValue;
 }
@@ -435,7 +606,7 @@ hipError_t launch_v3_epi(const GroupedGemm& p, int cfg, hipStream_t s) {
 }  // namespace
 
 int gemm_v3_bm(int cfg) {
-  static const int bm[] = {256, 256, 256, 256, 256, 128, 128, 128, 128, 64, 64, 128};
+  static const int bm[] = {256, 256, 256, 256, 256, 128, 128, 128, 128, 64, 64, 128, 256, 256};
   return (cfg >= 0 && cfg < kGemmV3Configs) ? bm[cfg] : 0;
 }
 
