@@ -443,19 +443,68 @@ TAIL_SHAPES = [
 ]
 
 
+@pytest.mark.parametrize("parent", ["0", "13"])
 @pytest.mark.parametrize("tail", ["0", "1"])
 @pytest.mark.parametrize("cfg", TAIL_SHAPES, ids=lambda c: c.name)
-def test_down_tail_split(cfg, tail, monkeypatch):
-    """The down projection on 256x256 tiles with its last, partial round run as
-    quarter tiles (1) and without (0), against the oracle."""
-    set_env(monkeypatch, "MOE_GEMM_CFG", "0")
+def test_down_tail_split(cfg, tail, parent, monkeypatch):
+    """The down projection on 256x256 tiles (DMA rings: 0; slices staged in
+    registers: 13) with its last, partial round run as quarter tiles (1) and
+    without (0), against the oracle."""
+    set_env(monkeypatch, "MOE_GEMM_CFG", parent)
     set_env(monkeypatch, "MOE_GEMM_TAIL", tail)
-    print(f"[tail {tail}] {cfg.name}", flush=True)
+    print(f"[tail {tail} parent {parent}] {cfg.name}", flush=True)
     inp = W.make_inputs(cfg)
     ref = oracle_forward(cfg, inp)
     got = DeviceLayer(cfg, inp).layer()
     diff, err = check_layer(cfg, inp, ref, got)
     print(f"  max rel err {err:.3e}")
+
+
+# Group sizes that give a 256-row tile every count of active 32-row blocks in
+# either row half of its waves (1-4), waves that load no activation rows,
+# empty groups and groups of several tiles.
+STAGED_GROUPS = [0, 1, 31, 32, 33, 64, 65, 100, 128, 129, 200, 255, 0, 256, 257, 600]
+
+
+@pytest.mark.parametrize("gather", [False, True], ids=["rows", "gathered"])
+@pytest.mark.parametrize("activation", [W.SWIGLU, W.GELU], ids=["swiglu", "gelu"])
+@pytest.mark.parametrize("D,F", [(64, 64), (128, 192), (384, 128), (256, 320)])
+def test_staged_slices_bit_identical_to_dma_rings(D, F, activation, gather, monkeypatch):
+    """The deep-tile configurations that stage slices in registers (12: four
+    waves, 13: eight) reproduce the bits of configuration 0 (DMA rings), whose
+    results the tile-configuration tests check against the oracle: each output
+    is accumulated by the same MFMAs in the same order.  Contractions of 1, 2,
+    3, 4, 5 and 6 slices of 64 cover the staged loop's prologue, steady part
+    and tail."""
+    dev = "cuda"
+    G = len(STAGED_GROUPS)
+    offs = np.concatenate([[0], np.cumsum(STAGED_GROUPS)]).astype(np.int32)
+    rows = int(offs[-1])
+    cfg = W.MoEConfig("staged_bits", rows, D, G, 1, F, activation=activation)
+    print(f"[staged bits] D={D} F={F} act={activation} gather={gather} rows={rows}", flush=True)
+    g = torch.Generator().manual_seed(7 * D + F + 1000 * activation)
+    nF = (2 if activation == W.SWIGLU else 1) * F
+    if gather:
+        src = torch.randn(rows + 37, D, generator=g).to(torch.bfloat16)
+        pick = torch.randperm(rows + 37, generator=g)[:rows].to(torch.int32)
+        x_in, rows_in = src.to(dev), pick.to(dev)
+    else:
+        x_in, rows_in = torch.randn(rows, D, generator=g).to(torch.bfloat16).to(dev), None
+    w13 = (torch.randn(G, nF, D, generator=g) * 0.05).to(torch.bfloat16).to(dev)
+    w2 = (torch.randn(G, D, F, generator=g) * 0.05).to(torch.bfloat16).to(dev)
+    off = torch.from_numpy(offs).to(dev)
+    ws = M.workspace(cfg, M.MOE_OP_EXPERT_FFN, dev)
+    outs = {}
+    for c in ("0", "12", "13"):
+        set_env(monkeypatch, "MOE_GEMM_CFG", c)
+        y = torch.full((rows, D), float("nan"), dtype=torch.bfloat16, device=dev)
+        M.moe_expert_ffn(cfg, G, F, activation, rows, x_in, rows_in, off, w13, w2, y, ws)
+        torch.cuda.synchronize()
+        outs[c] = y.cpu()
+    assert torch.isfinite(outs["0"].float()).all()
+    for c in ("12", "13"):
+        same = outs[c].view(torch.int16) == outs["0"].view(torch.int16)
+        assert bool(same.all()), f"config {c}: {int((~same).sum())} of {same.numel()} outputs differ"
 
 
 WS_SHAPES = [
