@@ -1,16 +1,14 @@
-// bf16 grouped GEMM with one wavefront per SIMD and 128x128 wave tiles, for
-// the deep expert FFN shapes (K a multiple of BK).
-//
-// C[r, n] = sum_k A[r, k] * B_g[n, k] for the rows r of group g, with the tile
-// scheduler and epilogues of gemm.hip.  Differences from the 8-wave kernel:
-//   * four waves per workgroup, each owning a 128x128 block of C (4x4 MFMA
-//     32x32x16 blocks, accumulators in the AGPR half of the register file):
-//     every fragment read from LDS feeds four MFMAs, which keeps LDS traffic
-//     (fragment reads plus the DMA writes) below what the LDS port delivers
-//     while the matrix cores run at full rate;
-//   * K-slices of BK (32 or 64) elements in an NST-deep LDS ring: with BK=32
-//     the ring holds four or five slices of a 256x256 tile, so three or four
-//     refills are in flight behind the slice being multiplied;
+// bf16 grouped GEMM on 32x32x16 MFMAs for the deep expert FFN shapes (K a
+// multiple of BK), with the tile scheduler and epilogues of gemm.hip:
+// C[r, n] = sum_k A[r, k] * B_g[n, k] for the rows r of group g.
+//   * WGM x WGN waves per workgroup, each owning a WM x WN block of C (TM x TN
+//     MFMA blocks): the default 256x256 tile runs eight waves of 128x64 (two
+//     per SIMD); the four-wave forms own 128x128 each (one per SIMD,
+//     accumulators in the AGPR half of the register file);
+//   * K-slices of BK (32 or 64) elements reach LDS either by buffer-to-LDS
+//     DMA into NST / NSTB-deep rings (RSD = 0), or through registers (RSD >
+//     0): 16-byte buffer loads one slice ahead, then LDS writes into one of
+//     two stages, spread over the MFMAs of the slice before;
 //   * a wave skips the MFMAs and fragment reads of 32-row blocks that lie past
 //     the tile's last row (groups of a few rows pay only for the weight
 //     stream, not for MFMAs on padding).
