@@ -155,7 +155,7 @@ def coverage_sample(cfg, disp, n_extra, seed=1234):
     token of its first and of its last row (the first and last m-tile of
     every group, so every tile class of the grouped GEMM launches is hit:
     deep tiles, shallow weight-streaming groups and the partial tiles at a
-    group's end, where the last-round quarter tiles fall), plus `n_extra`
+    group's end, among them the split last-round tiles), plus `n_extra`
     tokens drawn at random."""
     off, tor = disp["offsets"], disp["token_of_row"]
     must = set()

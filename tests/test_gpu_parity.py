@@ -435,9 +435,10 @@ def test_shallow_group_split(cfg, split, monkeypatch):
 
 TAIL_SHAPES = [
     # down projections with K >= 4096 and fewer 256x256 tiles than CUs, so
-    # that every tile runs as four quarter tiles (the case with full rounds
-    # before the tail is the full-size Mixtral-shaped layer); ragged N and
-    # ragged groups
+    # that every tile runs in the split tail (K = 4096: eight units of 8
+    # slices each; K = 4160 = 65 slices: one unit, as 65 has no even
+    # divisor); the case with full rounds before the tail is the full-size
+    # Mixtral-shaped layer; ragged N and ragged groups
     W.MoEConfig("tail_split_deep", 800, 512, 8, 2, 4096, zipf_s=0.5),
     W.MoEConfig("tail_split_ragged", 900, 448, 6, 2, 4160, zipf_s=1.0),
 ]
@@ -448,8 +449,8 @@ TAIL_SHAPES = [
 @pytest.mark.parametrize("cfg", TAIL_SHAPES, ids=lambda c: c.name)
 def test_down_tail_split(cfg, tail, parent, monkeypatch):
     """The down projection on 256x256 tiles (DMA rings: 0; slices staged in
-    registers: 13) with its last, partial round run as quarter tiles (1) and
-    without (0), against the oracle."""
+    registers: 13) with the tiles of its last, partial round split over the
+    contraction (1) and without (0), against the oracle."""
     set_env(monkeypatch, "MOE_GEMM_CFG", parent)
     set_env(monkeypatch, "MOE_GEMM_TAIL", tail)
     print(f"[tail {tail} parent {parent}] {cfg.name}", flush=True)

@@ -423,7 +423,7 @@ FfnPlan plan_ffn(int act, int activation, int D, int F, int max_rows, int G, boo
 
 // Bytes of float32 partial sums that the contraction splits of one expert FFN
 // need (the launches run one after another and share them).
-size_t ffn_partial_bytes(int act, int activation, int D, int F, int max_rows, int G, bool grouped) {
+size_t ffn_ksplit_bytes(int act, int activation, int D, int F, int max_rows, int G, bool grouped) {
   const FfnPlan pl = plan_ffn(act, activation, D, F, max_rows, G, grouped);
   const size_t ldp_up = (size_t)(activation == SWIGLU ? 2 : 1) * F;
   const int ks_up = pl.ks_up > pl.ks_sh_up ? pl.ks_up : pl.ks_sh_up;
@@ -432,6 +432,13 @@ size_t ffn_partial_bytes(int act, int activation, int D, int F, int max_rows, in
   if (ks_up > 1) b = (size_t)ks_up * max_rows * ldp_up * 4;
   if (ks_dn > 1) b = b > (size_t)ks_dn * max_rows * D * 4 ? b : (size_t)ks_dn * max_rows * D * 4;
   return b;
+}
+size_t ffn_tail_bytes(int act, int activation, int D, int F, int max_rows, int G, bool grouped);
+// The contraction splits' partial sums, then (from a 256-byte boundary) the
+// unit blocks of the down projection's split tail.
+size_t ffn_partial_bytes(int act, int activation, int D, int F, int max_rows, int G, bool grouped) {
+  return round_up(ffn_ksplit_bytes(act, activation, D, F, max_rows, G, grouped), 256) +
+         ffn_tail_bytes(act, activation, D, F, max_rows, G, grouped);
 }
 // ... for either activation, grouped or not (moe_expert_ffn's workspace)
 size_t ffn_partial_bytes_any(int act, int D, int F, int max_rows, int G) {
@@ -446,9 +453,13 @@ size_t ffn_partial_bytes_any(int act, int D, int F, int max_rows, int G) {
 
 // The last round of a 256x256-tile launch with a long contraction (a round
 // takes long there): when the tiles do not fill a whole number of rounds (one
-// workgroup per CU), the full rounds run as they are and the remaining tiles
-// as four 128x128 quarters each, so the partial round ends sooner.  Measured
-// on MI355X: -10% for the Mixtral-shaped down projection (K = 14336); no gain
+// workgroup per CU), the full rounds run as they are and each remaining tile
+// runs as S units over a part of the contraction each (S from tail_units:
+// S times the remaining tiles fill at most one round), whose float32 sums a
+// second kernel adds in a fixed order.  Measured on MI355X (Mixtral-shaped
+// down projection, K = 14336, 64 tiles left after two rounds, S = 4):
+// 1123 us without a split, 947-958 us with the remaining tiles as four
+// 128x128 quarters each (the form this replaces), 854-859 us split; no gain
 // at K = 1408 or 2048, where it is not used.  MOE_GEMM_TAIL=0 turns it off
 // (tuning aid).
 bool tail_split_enabled() {
@@ -458,24 +469,36 @@ bool tail_split_enabled() {
 // parents: the 256x256-tile configurations with one workgroup per CU (DMA
 // rings, or register-staged slices on 8 waves)
 constexpr int kTailParentCfg = 0, kTailParentStagedCfg = kDeepCfg;
-constexpr int kTailChildCfg = 6;    // 128x128 tiles, 64-deep slices
+constexpr int kTailBlock = 256 * 256;   // floats per unit block of the split tail
+
+size_t ffn_tail_bytes(int act, int activation, int D, int F, int max_rows, int G, bool grouped) {
+  if (act != BF16 || !grouped || F < 4096 || F % 64 != 0 || !tail_split_enabled()) return 0;
+  const FfnPlan pl = plan_ffn(act, activation, D, F, max_rows, G, grouped);
+  if (pl.cfg_dn != kTailParentCfg && pl.cfg_dn != kTailParentStagedCfg) return 0;
+  return (size_t)num_cus() * kTailBlock * 4;
+}
 
 hipError_t launch_gemm(int act, int cfg, const GroupedGemm& g, hipStream_t s);
 
 hipError_t launch_gemm_tail_split(int act, int cfg, const GroupedGemm& g, hipStream_t s) {
   const bool parent = cfg == kTailParentCfg || cfg == kTailParentStagedCfg;
-  if (act != BF16 || !parent || g.offsets == nullptr || g.K < 4096 || !tail_split_enabled())
+  const int round = num_cus();
+  // (the unit blocks are in the workspace whenever this split applies:
+  // ffn_tail_bytes follows the same conditions)
+  if (act != BF16 || !parent || g.offsets == nullptr || g.K < 4096 || !tail_split_enabled() ||
+      g.epilogue != EPI_STORE_ACT || g.tail_part == nullptr || g.tail_cap < round)
     return launch_gemm(act, cfg, g, s);
-  const int cols = g.epilogue == EPI_SWIGLU ? 128 : 256;
   GroupedGemm full = g, tail = g;
   full.tail_mode = 1;
-  full.round = num_cus();
-  tail.tail_mode = 2;
-  tail.round = full.round;
-  tail.tail_pn = ceil_div(g.N, cols);
+  full.round = round;
   hipError_t e = launch_gemm(act, cfg, full, s);
   if (e != hipSuccess) return e;
-  return launch_gemm(act, kTailChildCfg, tail, s);
+  tail.tail_mode = 2;
+  tail.round = round;
+  tail.epilogue = EPI_TAIL_PART;
+  e = launch_gemm(act, cfg, tail, s);
+  if (e != hipSuccess) return e;
+  return launch_tail_reduce(tail, s);
 }
 
 hipError_t launch_gemm(int act, int cfg, const GroupedGemm& g, hipStream_t s) {
@@ -542,6 +565,12 @@ moe_status run_ffn(int act, int activation, int G, int D, int F, int max_rows, c
   GroupedGemm g1s = g1, g2s = g2;       // shallow groups of a split
   g1s.ksplit = pl.ks_sh_up;
   g2s.ksplit = pl.ks_sh_dn;
+  // the split tail's unit blocks follow the contraction splits' sums (their
+  // own region: the shallow launches may use those on another stream)
+  if (part != nullptr && ffn_tail_bytes(act, activation, D, F, max_rows, G, offsets != nullptr) > 0) {
+    g2.tail_part = part + round_up(ffn_ksplit_bytes(act, activation, D, F, max_rows, G, offsets != nullptr), 256) / 4;
+    g2.tail_cap = num_cus();
+  }
   if (pl.split) {
     int32_t* deep_up = prefix_ws;
     int32_t* deep_dn = pl.bm_dn != pl.bm_up ? prefix_ws + (G + 1) : deep_up;

@@ -134,6 +134,7 @@ enum Epilogue {
   EPI_STORE_ACT = 1,   // C in the activation type
   EPI_SWIGLU = 2,      // B rows n and F+n are gate and up: H = silu(g) * u
   EPI_GELU = 3,        // H = gelu(C)
+  EPI_TAIL_PART = 4,   // float32 sums of one unit of the split tail (tail_mode 2)
 };
 
 struct GroupedGemm {
@@ -154,13 +155,13 @@ struct GroupedGemm {
   // 0: every tile;
   // 1: only the tiles of the full rounds, the first (total / round) * round
   //    tiles of the order (round = workgroups that run at once);
-  // 2: the remaining tiles of a tiling twice as tall and wide (BM_parent =
-  //    2 BM, tail_pn of its n-tiles, tile_prefix for BM_parent), each as four
-  //    quarter tiles of this kernel, so that the last, partial round has four
-  //    times as many (four times shorter) workgroups.
+  // 2: the remaining tiles, each as S units over consecutive K / S slices
+  //    (S from tail_units, so that S times the remaining tiles fill at most
+  //    one round): unit b writes its float32 sums as block b of BM x BN floats
+  //    at `tail_part` (epilogue EPI_TAIL_PART; the buffer holds `tail_cap`
+  //    blocks), and tail_reduce adds each tile's S blocks in order into C.
   int tail_mode;
   int round;
-  int tail_pn;
   // Persistent launches: CUs the grid may occupy (0 = all of them), so that
   // a launch can run beside another one on the remaining CUs.
   int cus;
@@ -175,6 +176,8 @@ struct GroupedGemm {
   int ksplit;
   float* partial;
   int ldp;
+  float* tail_part;   // tail_mode 2: float32 unit blocks (tail_cap of BM x BN)
+  int tail_cap;
 };
 
 // Exact split of a float32 matrix into three bfloat16 planes, hi + mid + lo = w:
@@ -252,20 +255,6 @@ template <int BM>
 __device__ __forceinline__ bool map_tile(const GroupedGemm& p, int n_tiles, int& g, int& row0, int& rows,
                                          int& nt) {
   const int bid = blockIdx.x;
-  if (p.tail_mode == 2) {
-    const int total = tile_count<2 * BM>(p, p.tail_pn);
-    const int main = total / p.round * p.round;
-    const int q = 4 * (total - main);                    // quarter tiles
-    if (bid >= q) return false;
-    const int L = xcd_remap(bid, q);
-    const int sub = L & 3;
-    int prow0, prows, pnt;
-    decode_tile<2 * BM>(p, p.tail_pn, main + (L >> 2), g, prow0, prows, pnt);
-    row0 = prow0 + (sub >> 1) * BM;
-    rows = min(BM, prows - (sub >> 1) * BM);
-    nt = 2 * pnt + (sub & 1);
-    return rows > 0 && nt < n_tiles;
-  }
   int total = tile_count<BM>(p, n_tiles);
   if (p.tail_mode == 1) total = total / p.round * p.round;
   if (bid >= total) return false;
@@ -284,6 +273,19 @@ struct TilePrefixReq {
 };
 hipError_t launch_tile_prefix_classes(const int32_t* offsets, int G, TilePrefixReq r0, TilePrefixReq r1,
                                       TilePrefixReq r2, hipStream_t s);
+
+// Units of the split tail (tail_mode 2): of `total` tiles, the first `main`
+// fill whole rounds; each of the r left over runs as S units, S the largest
+// power of two up to 8 with S * r <= round that divides the nk slices and
+// leaves at least four per unit (1 if none does).
+__host__ __device__ inline void tail_units(int total, int round, int nk, int& main, int& r, int& S) {
+  main = total / round * round;
+  r = total - main;
+  S = 1;
+  while (S < 8 && 2 * S * r <= round && nk % (2 * S) == 0 && nk / (2 * S) >= 4) S *= 2;
+}
+// The split tail's sum of units and store (tail_mode 2), after its GEMM launch.
+hipError_t launch_tail_reduce(const GroupedGemm& g, hipStream_t s);
 
 // bf16 MFMA grouped GEMM; returns the BM its tiles use via bm_out when non-null.
 hipError_t launch_gemm_bf16(const GroupedGemm& g, hipStream_t s);

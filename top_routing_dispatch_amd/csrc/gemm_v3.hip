@@ -97,7 +97,16 @@ void gemm_v3_kernel(const GroupedGemm p, int n_tiles) {
   const int total = PERS ? tile_count<BM>(p, n_tiles) : 0;
   for (int tile = blockIdx.x;; tile += gridDim.x) {
   int g, row0, rows, nt;
-  if constexpr (PERS) {
+  // split tail (EPI_TAIL_PART): this workgroup's unit covers slices
+  // [k_unit * nk, (k_unit + 1) * nk) of its tile
+  int k_unit = 0, k_units = 1;
+  if constexpr (EPI == EPI_TAIL_PART) {
+    int main, r;
+    tail_units(tile_count<BM>(p, n_tiles), p.round, p.K / BK, main, r, k_units);
+    if ((int)blockIdx.x >= k_units * r) return;
+    k_unit = (int)blockIdx.x % k_units;
+    decode_tile<BM>(p, n_tiles, main + (int)blockIdx.x / k_units, g, row0, rows, nt);
+  } else if constexpr (PERS) {
     if (tile >= total) break;
     decode_tile<BM>(p, n_tiles, tile, g, row0, rows, nt);
   } else {
@@ -148,7 +157,14 @@ void gemm_v3_kernel(const GroupedGemm p, int n_tiles) {
   // Iteration it refills A with slice it + NST - 1 and B with slice
   // it + NSTB - 1; load instruction q of an iteration belongs to the
   // shallower ring first, then to the deeper one.
-  const int nk = K / BK;
+  const int nk = K / BK / k_units;
+  if (k_unit > 0) {
+    const unsigned k_off = (unsigned)(k_unit * nk) * (unsigned)C::RB;
+#pragma unroll
+    for (int q = 0; q < C::A_INS; ++q) a_off[q] += k_off;
+#pragma unroll
+    for (int q = 0; q < C::B_INS; ++q) b_off[q] += k_off;
+  }
   auto dma_one = [&](int q, int it) __attribute__((always_inline)) {
     const int j = it + C::depth(q) - 1;
     if (C::is_a(q)) {
@@ -472,6 +488,24 @@ void gemm_v3_kernel(const GroupedGemm p, int n_tiles) {
   }
   wait_vm<0>();   // nothing is in flight into LDS when the staging below reuses it
 
+  if constexpr (EPI == EPI_TAIL_PART) {
+    // float32 sums of the unit as block blockIdx.x of BM x BN floats (row
+    // major); a lane holds column lane % 32 and rows 8 (r / 4) + 4 (lane / 32)
+    // + r % 4 of each 32x32 block, and blocks past the tile's rows stay unset
+    float* __restrict__ P = p.tail_part + (size_t)blockIdx.x * (BM * BN);
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) {
+      if (i >= act_i) continue;
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm * C::WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          P[row * BN + wn * C::WN + j * 32 + (lane & 31)] = acc[i][j][r];
+        }
+    }
+    return;
+  }
   // Epilogue: the activation is applied in registers, each wave's output
   // block goes to its own LDS region and is read back as 16-byte row chunks
   // for full-width global stores.  One LDS write instruction covers rows r and
@@ -538,6 +572,40 @@ void gemm_v3_kernel(const GroupedGemm p, int n_tiles) {
   }
 }
 
+// Sum of each split-tail tile's units (unit 0 first, then 1, ...) into C,
+// rounded to bf16: one workgroup per 16 rows of a tile, four columns per
+// thread.  The grid covers `round` tiles (an upper bound of those left over).
+template <int BM, int BN>
+__global__ __launch_bounds__(256) void tail_reduce_kernel(const GroupedGemm p, int n_tiles) {
+  int main, r, S;
+  tail_units(tile_count<BM>(p, n_tiles), p.round, p.K / 64, main, r, S);
+  const int t = blockIdx.x;
+  if (t >= r) return;
+  int g, row0, rows, nt;
+  decode_tile<BM>(p, n_tiles, main + t, g, row0, rows, nt);
+  const int rb = blockIdx.y * 16;
+  if (rb >= rows) return;
+  const float* __restrict__ P = p.tail_part + (size_t)t * S * (BM * BN);
+  bf16_t* __restrict__ Cout = static_cast<bf16_t*>(p.C);
+  constexpr int C4 = BN / 4;
+  for (int i = threadIdx.x; i < 16 * C4; i += blockDim.x) {
+    const int rr = rb + i / C4, c = (i % C4) * 4;
+    if (rr >= rows) continue;
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = P[rr * BN + c + e];
+    for (int k = 1; k < S; ++k) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] += P[(size_t)k * (BM * BN) + rr * BN + c + e];
+    }
+    const int n = nt * BN + c;
+    bf16_t* dst = Cout + (size_t)(row0 + rr) * p.ldc + n;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (n + e < p.N) dst[e] = f32_to_bf16_rn(v[e]);
+  }
+}
+
 inline int m_bound3(const GroupedGemm& p, int bm) {
   if (p.offsets == nullptr) return ceil_div(p.M_max, bm);
   return p.M_max / bm + (p.G < p.M_max ? p.G : p.M_max);
@@ -555,9 +623,12 @@ hipError_t launch_cfg3(const GroupedGemm& p, hipStream_t s) {
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   if (PERS && p.tail_mode != 0) return hipErrorInvalidValue;
   if (PERS) blocks = std::min<long long>(blocks, (long long)num_cus() * OCC);
+  if ((p.tail_mode == 2) != (EPI == EPI_TAIL_PART)) return hipErrorInvalidValue;
   if (p.tail_mode == 2) {
-    if (p.round <= 0 || p.tail_pn <= 0) return hipErrorInvalidValue;
-    blocks = 4LL * p.round;            // the partial round holds fewer than `round` parent tiles
+    // at most `round` units, each a block of the float32 buffer
+    if (p.round <= 0 || p.tail_part == nullptr || p.tail_cap < p.round || PERS || p.offsets == nullptr)
+      return hipErrorInvalidValue;
+    blocks = p.round;
   }
   // dynamic LDS above 64 KB has to be allowed explicitly, once per device
   static std::atomic<bool> allowed[64];   // per device: attribute set (host threads may race)
@@ -603,12 +674,28 @@ hipError_t launch_v3_epi(const GroupedGemm& p, int cfg, hipStream_t s) {
 
 }  // namespace
 
+hipError_t launch_tail_reduce(const GroupedGemm& g, hipStream_t s) {
+  if (g.tail_mode != 2 || g.round <= 0 || g.tail_part == nullptr || g.epilogue != EPI_TAIL_PART || g.K % 64 != 0)
+    return hipErrorInvalidValue;
+  const int n_tiles = ceil_div(g.N, 256);
+  if (n_tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL((tail_reduce_kernel<256, 256>), dim3((unsigned)g.round, 256 / 16), dim3(256), 0, s, g, n_tiles);
+  return hipGetLastError();
+}
+
 int gemm_v3_bm(int cfg) {
   static const int bm[] = {256, 256, 256, 256, 256, 128, 128, 128, 128, 64, 64, 128, 256, 256};
   return (cfg >= 0 && cfg < kGemmV3Configs) ? bm[cfg] : 0;
 }
 
 hipError_t launch_gemm_v3(const GroupedGemm& p, int cfg, hipStream_t s) {
+  if (p.epilogue == EPI_TAIL_PART) {
+    // the split tail runs on the 256x256 configurations with one workgroup
+    // per CU (DMA rings, register-staged slices)
+    if (cfg == 0) return launch_cfg3<256, 256, 2, 4, 64, 2, 3, 0, 1, false, EPI_TAIL_PART>(p, s);
+    if (cfg == 13) return launch_cfg3<256, 256, 2, 4, 64, 2, 2, 1, 1, false, EPI_TAIL_PART>(p, s);
+    return hipErrorInvalidValue;
+  }
   switch (p.epilogue) {
     case EPI_STORE_ACT: return launch_v3_epi<EPI_STORE_ACT>(p, cfg, s);
     case EPI_SWIGLU: return launch_v3_epi<EPI_SWIGLU>(p, cfg, s);
