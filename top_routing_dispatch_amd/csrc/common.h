@@ -159,7 +159,8 @@ struct GroupedGemm {
   //    (S from tail_units, so that S times the remaining tiles fill at most
   //    one round): unit b writes its float32 sums as block b of BM x BN floats
   //    at `tail_part` (epilogue EPI_TAIL_PART; the buffer holds `tail_cap`
-  //    blocks), and tail_reduce adds each tile's S blocks in order into C.
+  //    blocks), and tail_reduce adds each tile's S blocks in order into C
+  //    (with S = 1 the units store their tiles into C themselves).
   int tail_mode;
   int round;
   // Persistent launches: CUs the grid may occupy (0 = all of them), so that

@@ -488,10 +488,11 @@ void gemm_v3_kernel(const GroupedGemm p, int n_tiles) {
   }
   wait_vm<0>();   // nothing is in flight into LDS when the staging below reuses it
 
-  if constexpr (EPI == EPI_TAIL_PART) {
+  if (EPI == EPI_TAIL_PART && k_units > 1) {
     // float32 sums of the unit as block blockIdx.x of BM x BN floats (row
     // major); a lane holds column lane % 32 and rows 8 (r / 4) + 4 (lane / 32)
-    // + r % 4 of each 32x32 block, and blocks past the tile's rows stay unset
+    // + r % 4 of each 32x32 block, and blocks past the tile's rows stay unset.
+    // (One unit per tile: the whole sum, stored below like EPI_STORE_ACT.)
     float* __restrict__ P = p.tail_part + (size_t)blockIdx.x * (BM * BN);
 #pragma unroll
     for (int i = 0; i < C::TM; ++i) {
@@ -580,7 +581,7 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(const GroupedGemm p, i
   int main, r, S;
   tail_units(tile_count<BM>(p, n_tiles), p.round, p.K / 64, main, r, S);
   const int t = blockIdx.x;
-  if (t >= r) return;
+  if (t >= r || S == 1) return;      // one unit per tile: stored by the GEMM itself
   int g, row0, rows, nt;
   decode_tile<BM>(p, n_tiles, main + t, g, row0, rows, nt);
   const int rb = blockIdx.y * 16;
