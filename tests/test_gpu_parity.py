@@ -38,6 +38,9 @@ EDGE = [
     W.MoEConfig("mostly_empty_experts", 20, 72, 64, 2, 56, scoring=W.SIGMOID_BIAS),
     W.MoEConfig("max_experts_max_k", 70, 64, 1024, 32, 16, scoring=W.SOFTMAX_TOPK),
     W.MoEConfig("ragged_everything", 259, 8, 5, 3, 8, num_shared=1, d_ff_shared=8, capacity_factor=0.6),
+    # three permutation tiles with the largest masks (E * 8 words of LDS) and
+    # an expert count that is not a power of two (prefix scans over 1024 threads)
+    W.MoEConfig("experts_1000_three_tiles", 600, 64, 1000, 8, 16, scoring=W.SOFTMAX_TOPK, capacity_factor=1.0),
 ]
 
 
@@ -139,7 +142,7 @@ def _permute_gpu(cfg, idx, x_host):
             None if xp is None else to_numpy(xp)[:rows_cap])
 
 
-@pytest.mark.parametrize("cfg", SMALL + EDGE[:4], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", SMALL + EDGE[:4] + EDGE[-1:], ids=lambda c: c.name)
 def test_permute_bit_exact(cfg):
     """Dispatch of the oracle's own selection: counts, offsets, permutation, drops
     and the gathered rows are bit-exact."""
