@@ -22,7 +22,7 @@ __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __rest
   const int g = threadIdx.x;
   s[g] = (g < G) ? ceil_div(off[g + 1] - off[g], bm) : 0;
   __syncthreads();
-  for (int d = 1; d < (int)blockDim.x; d <<= 1) {
+  for (int d = 1; d < kMaxExperts; d <<= 1) {
     const int v = (g >= d) ? s[g - d] : 0;
     __syncthreads();
     s[g] += v;
@@ -45,7 +45,7 @@ __global__ __launch_bounds__(1024) void tile_prefix_classes_kernel(const int32_t
     if (r.out == nullptr) continue;     // uniform: the same request for every thread
     s[g] = (n > r.lo && n <= r.hi) ? ceil_div(n, r.bm) : 0;
     __syncthreads();
-    for (int d = 1; d < (int)blockDim.x; d <<= 1) {
+    for (int d = 1; d < kMaxExperts; d <<= 1) {
       const int v = (g >= d) ? s[g - d] : 0;
       __syncthreads();
       s[g] += v;
@@ -407,25 +407,15 @@ hipError_t launch_f32_epi(const GroupedGemm& p, hipStream_t s) {
 
 }  // namespace
 
-// One thread per group, a power of two of at least one wave (the scans take
-// log2(threads) steps): with a few hundred groups the workgroup is four
-// waves, which fit beside a resident GEMM workgroup on a CU.
-inline int prefix_threads(int G) {
-  int t = 64;
-  while (t < G) t <<= 1;
-  return t;
-}
-
 hipError_t launch_tile_prefix(const int32_t* offsets, int G, int bm, int32_t* prefix, hipStream_t s) {
-  if (G > kMaxExperts) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(prefix_threads(G)), 0, s, offsets, G, bm, prefix);
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(kMaxExperts), 0, s, offsets, G, bm, prefix);
   return hipGetLastError();
 }
 
 hipError_t launch_tile_prefix_classes(const int32_t* offsets, int G, TilePrefixReq r0, TilePrefixReq r1,
                                       TilePrefixReq r2, hipStream_t s) {
   if (G > kMaxExperts) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(tile_prefix_classes_kernel, dim3(1), dim3(prefix_threads(G)), 0, s, offsets, G, r0, r1, r2);
+  hipLaunchKernelGGL(tile_prefix_classes_kernel, dim3(1), dim3(kMaxExperts), 0, s, offsets, G, r0, r1, r2);
   return hipGetLastError();
 }
 

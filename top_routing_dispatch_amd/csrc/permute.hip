@@ -49,11 +49,8 @@ __device__ uint32_t build_masks(const PermuteArgs& a, uint32_t* mask) {
   return skip;
 }
 
-// The masks take E * kWordsPerTile words of dynamic LDS (8 KB at 256
-// experts): sized by the expert count, so that a block fits in what a
-// resident GEMM workgroup leaves of a CU's LDS.
 __global__ __launch_bounds__(kPermuteTile) void hist_kernel(const PermuteArgs a) {
-  extern __shared__ uint32_t mask[];
+  __shared__ uint32_t mask[kMaxExperts * kWordsPerTile];
   build_masks(a, mask);
   for (int e = threadIdx.x; e < a.E; e += blockDim.x) {
     int c = 0;
@@ -84,11 +81,9 @@ __global__ __launch_bounds__(kMaxExperts) void scan_kernel(const PermuteArgs a, 
   const int e = threadIdx.x;
   int total = 0;
   if (e < a.E) {
-    // the counts of 8 tiles are fetched together, then turned into the
-    // tiles' base ranks inside expert e (8, not more: the kernel stays within
-    // 32 VGPRs, so that its one workgroup fits beside a resident 256x256 GEMM
-    // workgroup on a CU instead of waiting for one to finish)
-    constexpr int B = 8;
+    // the counts of 16 tiles are fetched together, then turned into the
+    // tiles' base ranks inside expert e
+    constexpr int B = 16;
     for (int t0 = 0; t0 < ntiles; t0 += B) {
       int c[B];
 #pragma unroll
@@ -117,7 +112,7 @@ __global__ __launch_bounds__(kMaxExperts) void scan_kernel(const PermuteArgs a, 
 }
 
 __global__ __launch_bounds__(kPermuteTile) void scatter_kernel(const PermuteArgs a) {
-  extern __shared__ uint32_t mask[];   // E * kWordsPerTile words
+  __shared__ uint32_t mask[kMaxExperts * kWordsPerTile];
   const uint32_t skip = build_masks(a, mask);
   const int tid = threadIdx.x;
   const int t = blockIdx.x * kPermuteTile + tid;
@@ -442,9 +437,8 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(permute_one_tile_kernel, dim3(1), dim3(kPermuteTile), 0, s, a);
     return hipGetLastError();
   }
-  const size_t mask_bytes = (size_t)a.E * kWordsPerTile * sizeof(uint32_t);
   if (ntiles > 0) {
-    hipLaunchKernelGGL(hist_kernel, dim3(ntiles), dim3(kPermuteTile), mask_bytes, s, a);
+    hipLaunchKernelGGL(hist_kernel, dim3(ntiles), dim3(kPermuteTile), 0, s, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
@@ -455,7 +449,7 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(threads), 0, s, a, ntiles);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || ntiles == 0) return err;
-  hipLaunchKernelGGL(scatter_kernel, dim3(ntiles), dim3(kPermuteTile), mask_bytes, s, a);
+  hipLaunchKernelGGL(scatter_kernel, dim3(ntiles), dim3(kPermuteTile), 0, s, a);
   return hipGetLastError();
 }
 
