@@ -263,13 +263,19 @@ __global__ __launch_bounds__(512) void router_small_kernel(const bf16_t* __restr
 #pragma unroll
         for (int p = 0; p < NP; ++p) bv[u][b][p] = *reinterpret_cast<const bf16x8_t*>(wr[b][p] + st * 32);
     }
+    // Every load of the batch is issued before the first product: with a
+    // branch per step the compiler moved each step's loads down to its MFMA
+    // and waited for them one step at a time.  A step past the end multiplies
+    // a token fragment with its bits cleared (zeros: the sums do not change).
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (s0 + NW * u >= nsteps) break;
+      const unsigned keep = (s0 + NW * u < nsteps) ? 0xffffffffu : 0u;
+      const bf16x8_t au = __builtin_bit_cast(bf16x8_t, __builtin_bit_cast(u32x4_t, a[u]) & keep);
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
 #pragma unroll
-        for (int p = 0; p < NP; ++p) acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], bv[u][b][p], acc[b], 0, 0, 0);
+        for (int p = 0; p < NP; ++p) acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(au, bv[u][b][p], acc[b], 0, 0, 0);
 #pragma unroll
         for (int r = 0; r < 4; ++r) { dacc[b][r] += (double)acc[b][r]; acc[b][r] = 0.0f; }
       }
