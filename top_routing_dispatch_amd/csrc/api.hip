@@ -84,6 +84,7 @@ inline size_t carve(size_t bytes) { return round_up(bytes, 256); }
 struct Derived {
   int capacity;     // INT32_MAX when dropless
   int rows_cap;     // A_cap
+  int group_rows;   // bound on one expert's rows: a token gives an expert at most one row
 };
 
 moe_status derive(const moe_config* c, Derived* d) {
@@ -97,6 +98,7 @@ moe_status derive(const moe_config* c, Derived* d) {
     d->capacity = INT32_MAX;
     d->rows_cap = (int)A;
   }
+  d->group_rows = c->num_tokens < d->capacity ? c->num_tokens : d->capacity;
   return MOE_OK;
 }
 
@@ -171,7 +173,8 @@ size_t ws_stats(const moe_config* c) {
   return carve((size_t)ceil_div(c->num_tokens, kStatsChunk) * c->num_experts * 4);
 }
 
-size_t ffn_partial_bytes(int act, int activation, int D, int F, int max_rows, int G, bool grouped);
+size_t ffn_partial_bytes(int act, int activation, int D, int F, int max_rows, int G, bool grouped,
+                         int group_rows = INT_MAX);
 
 struct Layout {
   size_t logits, flags, wsplit, probs, idx, w, tile_counts, counts, offsets, tile_prefix, tile_prefix2, row_of, tor, h,
@@ -204,7 +207,8 @@ Layout layer_layout(const moe_config* c, const Derived& d) {
   L.partial = take((size_t)ceil_div(c->num_tokens, kStatsChunk) * E * 4);
   // float32 partial sums of contraction splits: routed and shared experts
   // run on different streams, each with its own
-  L.kpart = take(ffn_partial_bytes(c->act_dtype, c->activation, c->d_model, c->d_ff, d.rows_cap, c->num_experts, true));
+  L.kpart = take(ffn_partial_bytes(c->act_dtype, c->activation, c->d_model, c->d_ff, d.rows_cap, c->num_experts, true,
+                                   d.group_rows));
   L.kpart_shared = take(c->num_shared > 0 ? ffn_partial_bytes(c->act_dtype, SWIGLU, c->d_model,
                                                               c->num_shared * c->d_ff_shared, c->num_tokens, 1, false)
                                           : 0);
@@ -385,8 +389,13 @@ int pick_ksplit(int act, int cfg, int epi, int N, int K, int G, int max_rows, bo
 // batch) both projections run on the shallow-group configuration alone.
 constexpr int kShallowRows = 64;
 
-FfnPlan plan_ffn(int act, int activation, int D, int F, int max_rows, int G, bool grouped) {
+// group_rows bounds the rows of any one group (the layer knows one: a token
+// gives an expert at most one row); with every group shallow the
+// weight-streaming configuration takes both projections on all CUs.
+FfnPlan plan_ffn(int act, int activation, int D, int F, int max_rows, int G, bool grouped,
+                 int group_rows = INT_MAX) {
   FfnPlan pl;
+  const int grp = max_rows < group_rows ? max_rows : group_rows;   // rows of the largest group
   pl.cfg_up = pick_cfg(act, D, max_rows, G, false);
   pl.cfg_dn = pick_cfg(act, F, max_rows, G, true);
   // shallow groups: the persistent weight-streaming kernel with 64x128 tiles
@@ -403,7 +412,7 @@ FfnPlan plan_ffn(int act, int activation, int D, int F, int max_rows, int G, boo
   pl.sh_rows = pl.sh_bm > kShallowRows ? pl.sh_bm : kShallowRows;
   if (t.shallow_rows != kUnset && t.shallow_rows >= pl.sh_bm && t.shallow_rows <= 4096) pl.sh_rows = t.shallow_rows;
   const bool forced = t.gemm_cfg != kUnset;
-  if (!forced && pl.cfg_up >= 0 && pl.cfg_dn >= 0 && D % 64 == 0 && F % 64 == 0 && max_rows <= pl.sh_rows) {
+  if (!forced && pl.cfg_up >= 0 && pl.cfg_dn >= 0 && D % 64 == 0 && F % 64 == 0 && grp <= pl.sh_rows) {
     pl.cfg_up = pl.cfg_sh;
     pl.cfg_dn = pl.cfg_sh;
   }
@@ -411,7 +420,7 @@ FfnPlan plan_ffn(int act, int activation, int D, int F, int max_rows, int G, boo
   pl.bm_dn = cfg_bm(act, pl.cfg_dn);
   const bool able = grouped && pl.cfg_up >= 0 && pl.cfg_dn >= 0 && D % 64 == 0 && F % 64 == 0;
   const int avg = G > 0 ? max_rows / G : max_rows;
-  pl.split = able && D >= 1024 && F >= 1024 && avg < 320 && max_rows > pl.sh_rows;
+  pl.split = able && D >= 1024 && F >= 1024 && avg < 320 && grp > pl.sh_rows;
   if (able && t.gemm_split != kUnset) pl.split = t.gemm_split != 0;
   const int epi_up = activation == SWIGLU ? EPI_SWIGLU : EPI_GELU;
   pl.ks_up = pick_ksplit(act, pl.cfg_up, epi_up, F, D, G, max_rows, grouped);
@@ -423,8 +432,9 @@ FfnPlan plan_ffn(int act, int activation, int D, int F, int max_rows, int G, boo
 
 // Bytes of float32 partial sums that the contraction splits of one expert FFN
 // need (the launches run one after another and share them).
-size_t ffn_ksplit_bytes(int act, int activation, int D, int F, int max_rows, int G, bool grouped) {
-  const FfnPlan pl = plan_ffn(act, activation, D, F, max_rows, G, grouped);
+size_t ffn_ksplit_bytes(int act, int activation, int D, int F, int max_rows, int G, bool grouped,
+                        int group_rows = INT_MAX) {
+  const FfnPlan pl = plan_ffn(act, activation, D, F, max_rows, G, grouped, group_rows);
   const size_t ldp_up = (size_t)(activation == SWIGLU ? 2 : 1) * F;
   const int ks_up = pl.ks_up > pl.ks_sh_up ? pl.ks_up : pl.ks_sh_up;
   const int ks_dn = pl.ks_dn > pl.ks_sh_dn ? pl.ks_dn : pl.ks_sh_dn;
@@ -433,12 +443,14 @@ size_t ffn_ksplit_bytes(int act, int activation, int D, int F, int max_rows, int
   if (ks_dn > 1) b = b > (size_t)ks_dn * max_rows * D * 4 ? b : (size_t)ks_dn * max_rows * D * 4;
   return b;
 }
-size_t ffn_tail_bytes(int act, int activation, int D, int F, int max_rows, int G, bool grouped);
+size_t ffn_tail_bytes(int act, int activation, int D, int F, int max_rows, int G, bool grouped,
+                      int group_rows = INT_MAX);
 // The contraction splits' partial sums, then (from a 256-byte boundary) the
 // unit blocks of the down projection's split tail.
-size_t ffn_partial_bytes(int act, int activation, int D, int F, int max_rows, int G, bool grouped) {
-  return round_up(ffn_ksplit_bytes(act, activation, D, F, max_rows, G, grouped), 256) +
-         ffn_tail_bytes(act, activation, D, F, max_rows, G, grouped);
+size_t ffn_partial_bytes(int act, int activation, int D, int F, int max_rows, int G, bool grouped,
+                         int group_rows) {
+  return round_up(ffn_ksplit_bytes(act, activation, D, F, max_rows, G, grouped, group_rows), 256) +
+         ffn_tail_bytes(act, activation, D, F, max_rows, G, grouped, group_rows);
 }
 // ... for either activation, grouped or not (moe_expert_ffn's workspace)
 size_t ffn_partial_bytes_any(int act, int D, int F, int max_rows, int G) {
@@ -471,9 +483,9 @@ bool tail_split_enabled() {
 constexpr int kTailParentCfg = 0, kTailParentStagedCfg = kDeepCfg;
 constexpr int kTailBlock = 256 * 256;   // floats per unit block of the split tail
 
-size_t ffn_tail_bytes(int act, int activation, int D, int F, int max_rows, int G, bool grouped) {
+size_t ffn_tail_bytes(int act, int activation, int D, int F, int max_rows, int G, bool grouped, int group_rows) {
   if (act != BF16 || !grouped || F < 4096 || F % 64 != 0 || !tail_split_enabled()) return 0;
-  const FfnPlan pl = plan_ffn(act, activation, D, F, max_rows, G, grouped);
+  const FfnPlan pl = plan_ffn(act, activation, D, F, max_rows, G, grouped, group_rows);
   if (pl.cfg_dn != kTailParentCfg && pl.cfg_dn != kTailParentStagedCfg) return 0;
   return (size_t)num_cus() * kTailBlock * 4;
 }
@@ -526,21 +538,28 @@ struct SideStream {
 };
 
 // CUs of the concurrent shallow-group launch (MOE_SHALLOW_CUS overrides;
-// 0 runs the shallow groups in line after the deep ones).  Measured on
-// MI355X at the DeepSeek-V3 shape (routed FFN, deep + shallow): in line
-// 7.01 ms; beside the deep tiles on 64 CUs 6.71, 96 6.85, 128 6.96, 160 6.95.
-int shallow_cus() {
+// 0 runs the shallow groups in line after the deep ones), from the average
+// rows per group: where it is well above the shallow threshold the deep
+// groups carry most of the work and the shallow ones' weight stream needs
+// few CUs; near or below it most groups are shallow and their stream needs
+// most of the chip.  Measured on MI355X, routed FFN, DeepSeek-V3 shape
+// (8192 tokens, 256 rows per expert on average): in line 7.01 ms; beside the
+// deep tiles on 64 CUs 6.71, 96 6.85, 128 6.96, 160 6.95.  Its first 256
+// tokens (8 rows on average), whole layer: 64 CUs 3.23 ms, 128 2.00, 192
+// 1.71, in line 1.76.
+int shallow_cus(int max_rows, int G, int sh_rows) {
   const int v = tuning().shallow_cus;
   if (v != kUnset) return v < 0 ? 0 : v;
-  return 64;
+  const long long avg = G > 0 ? max_rows / G : max_rows;
+  return avg >= 2LL * sh_rows ? 64 : 192;
 }
 
 moe_status run_ffn(int act, int activation, int G, int D, int F, int max_rows, const void* x_in,
                    const int32_t* gather, const int32_t* offsets, const int32_t* prefix_up,
                    int32_t* prefix_ws, const void* w13, const void* w2, void* h, void* y_out, float* part,
                    hipStream_t s, void* const* ev = nullptr, int stage_up = 0, int stage_down = 0,
-                   const SideStream* side = nullptr) {
-  const FfnPlan pl = plan_ffn(act, activation, D, F, max_rows, G, offsets != nullptr);
+                   const SideStream* side = nullptr, int group_rows = INT_MAX) {
+  const FfnPlan pl = plan_ffn(act, activation, D, F, max_rows, G, offsets != nullptr, group_rows);
   const int n_mat = activation == SWIGLU ? 2 : 1;
   GroupedGemm g1{};
   g1.A = x_in; g1.a_rows = gather; g1.lda = D;
@@ -567,8 +586,9 @@ moe_status run_ffn(int act, int activation, int G, int D, int F, int max_rows, c
   g2s.ksplit = pl.ks_sh_dn;
   // the split tail's unit blocks follow the contraction splits' sums (their
   // own region: the shallow launches may use those on another stream)
-  if (part != nullptr && ffn_tail_bytes(act, activation, D, F, max_rows, G, offsets != nullptr) > 0) {
-    g2.tail_part = part + round_up(ffn_ksplit_bytes(act, activation, D, F, max_rows, G, offsets != nullptr), 256) / 4;
+  if (part != nullptr && ffn_tail_bytes(act, activation, D, F, max_rows, G, offsets != nullptr, group_rows) > 0) {
+    g2.tail_part = part + round_up(ffn_ksplit_bytes(act, activation, D, F, max_rows, G, offsets != nullptr,
+                                                    group_rows), 256) / 4;
     g2.tail_cap = num_cus();
   }
   if (pl.split) {
@@ -798,7 +818,8 @@ EcLayout ec_layout(const moe_config* c) {
   L.h = take(E * C * c->d_ff * es);
   L.yperm = take(E * C * c->d_model * es);
   L.h_shared = take(T * c->num_shared * c->d_ff_shared * es);
-  L.kpart = take(ffn_partial_bytes(c->act_dtype, c->activation, c->d_model, c->d_ff, (int)(E * C), (int)E, true));
+  L.kpart = take(ffn_partial_bytes(c->act_dtype, c->activation, c->d_model, c->d_ff, (int)(E * C), (int)E, true,
+                                   (int)C));
   L.kpart_shared = take(c->num_shared > 0 ? ffn_partial_bytes(c->act_dtype, SWIGLU, c->d_model,
                                                               c->num_shared * c->d_ff_shared, (int)T, 1, false)
                                           : 0);
@@ -1126,8 +1147,9 @@ static moe_status layer_forward_impl(const moe_config* cfg, const moe_weights* w
   const bool stats_aside = any && want_stats && !single_stream;
   // The shallow expert groups (when the plan splits them off) run on a second
   // auxiliary stream beside the deep ones.
-  const bool side_ffn = !routing_only && any && d.rows_cap > 0 && !single_stream && shallow_cus() > 0 &&
-                        plan_ffn(cfg->act_dtype, cfg->activation, D, cfg->d_ff, d.rows_cap, E, true).split;
+  const FfnPlan ffn_plan = plan_ffn(cfg->act_dtype, cfg->activation, D, cfg->d_ff, d.rows_cap, E, true, d.group_rows);
+  const int side_cus = shallow_cus(d.rows_cap, E, ffn_plan.sh_rows);
+  const bool side_ffn = !routing_only && any && d.rows_cap > 0 && !single_stream && side_cus > 0 && ffn_plan.split;
   std::unique_lock<std::mutex> aux_lock(g_aux_mu, std::defer_lock);
   AuxStream* aux = nullptr;
   if (overlap > 0 || stats_aside || side_ffn) {
@@ -1171,7 +1193,7 @@ static moe_status layer_forward_impl(const moe_config* cfg, const moe_weights* w
   pa.tile_counts = at<int32_t>(ws, L.tile_counts);
   pa.counts = cnt; pa.offsets = off; pa.row_of = row_of; pa.token_of_row = tor;
   pa.tile_prefix = tp;
-  pa.bm = plan_ffn(cfg->act_dtype, cfg->activation, D, cfg->d_ff, d.rows_cap, E, true).bm_up;
+  pa.bm = ffn_plan.bm_up;
   MOE_TRY(mark(ev, MOE_STAGE_PERMUTE, 0, s));
   MOE_TRY_HIP("permute", launch_permute(pa, s));
   MOE_TRY(mark(ev, MOE_STAGE_PERMUTE, 1, s));
@@ -1202,11 +1224,11 @@ static moe_status layer_forward_impl(const moe_config* cfg, const moe_weights* w
     void* h = at<void>(ws, L.h);
     void* yperm = at<void>(ws, L.yperm);
     SideStream side{};
-    if (side_ffn) side = SideStream{aux->s2, aux->side_fork, aux->side_join, shallow_cus()};
+    if (side_ffn) side = SideStream{aux->s2, aux->side_fork, aux->side_join, side_cus};
     if (d.rows_cap > 0)
       MOE_TRY(run_ffn(cfg->act_dtype, cfg->activation, E, D, cfg->d_ff, d.rows_cap, x, tor, off, tp,
                       at<int32_t>(ws, L.tile_prefix2), wt->w13, wt->w2, h, yperm, at<float>(ws, L.kpart), s, ev,
-                      MOE_STAGE_EXPERT_GATE_UP, MOE_STAGE_EXPERT_DOWN, side_ffn ? &side : nullptr));
+                      MOE_STAGE_EXPERT_GATE_UP, MOE_STAGE_EXPERT_DOWN, side_ffn ? &side : nullptr, d.group_rows));
     if (shared && overlap == 0)
       MOE_TRY(run_ffn_part(cfg->act_dtype, SWIGLU, 1, D, SF, T, x, wt->ws13, wt->ws2, at<void>(ws, L.h_shared), y,
                            at<float>(ws, L.kpart_shared), s, ev, MOE_STAGE_SHARED_GATE_UP, true));
@@ -1494,11 +1516,12 @@ moe_status moe_expert_choice_forward(const moe_config* cfg, const moe_weights* w
   MOE_TRY_HIP("expert-choice route", launch_ec_route(logits, T, E, C, pT, off, tor, roww, selbits, selpre,
                                                      unselected, s));
   MOE_TRY(mark(ev, MOE_STAGE_ROUTE_SELECT, 1, s));
-  const FfnPlan pl = plan_ffn(cfg->act_dtype, cfg->activation, D, F, E * C, E, true);
+  // every expert takes exactly C rows
+  const FfnPlan pl = plan_ffn(cfg->act_dtype, cfg->activation, D, F, E * C, E, true, C);
   if (!pl.split) MOE_TRY_HIP("tile prefix", launch_tile_prefix(off, E, pl.bm_up, prefix_up, s));
   MOE_TRY(run_ffn(cfg->act_dtype, cfg->activation, E, D, F, E * C, x, tor, off, prefix_up, prefix_up + (E + 1),
                   wt->w13, wt->w2, at<void>(ws, L.h), at<void>(ws, L.yperm), at<float>(ws, L.kpart), s, ev,
-                  MOE_STAGE_EXPERT_GATE_UP, MOE_STAGE_EXPERT_DOWN));
+                  MOE_STAGE_EXPERT_GATE_UP, MOE_STAGE_EXPERT_DOWN, nullptr, C));
   if (cfg->num_shared > 0) {
     MOE_TRY(run_ffn_part(cfg->act_dtype, SWIGLU, 1, D, SF, T, x, wt->ws13, wt->ws2, at<void>(ws, L.h_shared), y,
                          at<float>(ws, L.kpart_shared), s, ev, MOE_STAGE_SHARED_GATE_UP, true));
