@@ -582,6 +582,12 @@ DECODE_SHAPES = [
     W.MoEConfig("decode_t5_wide", 5, 8192, 16, 4, 128, num_shared=1, d_ff_shared=128, renormalize=1),
     W.MoEConfig("decode_t3_wide_k1", 3, 9216, 8, 1, 128, renormalize=0),
     W.MoEConfig("decode_t2_f32_wide", 2, 4096, 4, 2, 64, act_dtype=W.F32, router_dtype=W.F32),
+    # more rows than one shallow tile but no group above 48 (the token
+    # count): every group shallow, on all CUs
+    W.MoEConfig("decode_t48_rows384", 48, 1024, 32, 8, 1024, scoring=W.SIGMOID_BIAS, zipf_s=1.2),
+    # a few groups above 64 rows among many small ones (12 rows per group on
+    # average): the shallow groups beside the deep ones on 192 CUs
+    W.MoEConfig("decode_t200_skewed", 200, 1024, 128, 8, 1024, zipf_s=1.3),
 ]
 
 
