@@ -551,7 +551,8 @@ int shallow_cus(int max_rows, int G, int sh_rows) {
   const int v = tuning().shallow_cus;
   if (v != kUnset) return v < 0 ? 0 : v;
   const long long avg = G > 0 ? max_rows / G : max_rows;
-  return avg >= 2LL * sh_rows ? 64 : 192;
+  const int n = num_cus();                       // 256 on MI355X: 64 or 192
+  return avg >= 2LL * sh_rows ? (n + 3) / 4 : (3 * n + 3) / 4;
 }
 
 moe_status run_ffn(int act, int activation, int G, int D, int F, int max_rows, const void* x_in,
