@@ -546,13 +546,13 @@ struct SideStream {
 // (8192 tokens, 256 rows per expert on average): in line 7.01 ms; beside the
 // deep tiles on 64 CUs 6.71, 96 6.85, 128 6.96, 160 6.95.  Its first 256
 // tokens (8 rows on average), whole layer: 64 CUs 3.23 ms, 128 2.00, 192
-// 1.71, in line 1.76.
+// 1.71, 224 1.69, all 256 1.69, in line 1.76.
 int shallow_cus(int max_rows, int G, int sh_rows) {
   const int v = tuning().shallow_cus;
   if (v != kUnset) return v < 0 ? 0 : v;
   const long long avg = G > 0 ? max_rows / G : max_rows;
-  const int n = num_cus();                       // 256 on MI355X: 64 or 192
-  return avg >= 2LL * sh_rows ? (n + 3) / 4 : (3 * n + 3) / 4;
+  const int n = num_cus();                       // 256 on MI355X: 64, or all
+  return avg >= 2LL * sh_rows ? (n + 3) / 4 : n;
 }
 
 moe_status run_ffn(int act, int activation, int G, int D, int F, int max_rows, const void* x_in,
